@@ -1,0 +1,141 @@
+"""fp64 CPU oracle for the TTT forward scan -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The HIP library never loads it and the
+two share no code.
+
+The arithmetic lives in ``ttt_oracle.c`` (plain loops, fp64, OpenMP over the
+independent (batch, head) chains); this module only compiles it with gcc and
+marshals numpy arrays.  ``dual.py`` holds a second, independent formulation
+(the chunked matrix "dual form") used by the oracle's own tests.
+
+Parity status of each function (how it is pinned, see tests/test_oracle.py):
+  linear_forward  -- pinned: hand-derived exact d=2 examples, eta=0, autograd
+                     mini-batch GD, causal linear attention (W0=0), affine
+                     chunk map, dual form, chaining, column separability.
+  mlp_forward     -- pinned: eta=0, kernelised linear attention (W2_0=0),
+                     autograd mini-batch GD, finite differences, dual form.
+                     No exact worked example exists (SiLU is transcendental).
+  linear_decode   -- pinned: n steps equal linear_forward with b=1.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ttt_oracle.c")
+_LIB = os.path.join(_HERE, "libttt_oracle.so")
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile ttt_oracle.c into libttt_oracle.so (gcc, -O2, OpenMP)."""
+    if not force and os.path.exists(_LIB):
+        return _LIB
+    tmp = _LIB + ".tmp"
+    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+           "-Wall", "-Wextra", _SRC, "-o", tmp, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB):
+        build()
+    lib = ctypes.CDLL(_LIB)
+    P = ctypes.c_void_p
+    L = ctypes.c_long
+    I = ctypes.c_int
+    lib.ttt_oracle_linear_forward.argtypes = [P, P, P, P, I, P, L, L, L, L, L, P, P, I]
+    lib.ttt_oracle_linear_forward.restype = I
+    lib.ttt_oracle_mlp_forward.argtypes = [P, P, P, P, P, I, P, L, L, L, L, L, L, P, P, P, I]
+    lib.ttt_oracle_mlp_forward.restype = I
+    lib.ttt_oracle_linear_decode.argtypes = [P, P, P, P, P, L, L, L, P]
+    lib.ttt_oracle_linear_decode.restype = I
+    lib.ttt_oracle_max_threads.argtypes = []
+    lib.ttt_oracle_max_threads.restype = I
+    _lib = lib
+    return lib
+
+
+def _f64(x) -> np.ndarray:
+    """Exact upcast of an fp32/bf16/fp64 array (numpy or torch CPU) to fp64."""
+    try:
+        import torch
+        if isinstance(x, torch.Tensor):
+            x = x.detach().to("cpu", torch.float64).numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def max_threads() -> int:
+    return int(_load().ttt_oracle_max_threads())
+
+
+def linear_forward(Q, K, V, W0, eta, b: int, nthreads: int = 0):
+    """Primal mini-batch GD, TTT-Linear.  Q,K,V [B,H,T,d]; W0 [H,d,d] or
+    [B,H,d,d]; eta [H].  Returns (Y [B,H,T,d], W_out [B,H,d,d]) in fp64."""
+    Q, K, V, W0, eta = map(_f64, (Q, K, V, W0, eta))
+    B, H, T, d = Q.shape
+    assert K.shape == Q.shape and V.shape == Q.shape
+    per_batch = 1 if W0.ndim == 4 else 0
+    assert W0.shape == ((B, H, d, d) if per_batch else (H, d, d))
+    assert eta.shape == (H,)
+    Y = np.zeros((B, H, T, d))
+    W_out = np.zeros((B, H, d, d))
+    rc = _load().ttt_oracle_linear_forward(_ptr(Q), _ptr(K), _ptr(V), _ptr(W0), per_batch,
+                                           _ptr(eta), B, H, T, d, int(b), _ptr(Y),
+                                           _ptr(W_out), int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"oracle linear_forward failed ({rc})")
+    return Y, W_out
+
+
+def mlp_forward(Q, K, V, W1, W2, eta, b: int, nthreads: int = 0):
+    """Primal mini-batch GD, TTT-MLP f(z)=SiLU(z W1) W2.  W1 [H,d,m] or
+    [B,H,d,m]; W2 [H,m,d] or [B,H,m,d].  Returns (Y, W1_out, W2_out), fp64."""
+    Q, K, V, W1, W2, eta = map(_f64, (Q, K, V, W1, W2, eta))
+    B, H, T, d = Q.shape
+    m = W1.shape[-1]
+    per_batch = 1 if W1.ndim == 4 else 0
+    lead = (B, H) if per_batch else (H,)
+    assert W1.shape == lead + (d, m) and W2.shape == lead + (m, d)
+    assert eta.shape == (H,)
+    Y = np.zeros((B, H, T, d))
+    W1o = np.zeros((B, H, d, m))
+    W2o = np.zeros((B, H, m, d))
+    rc = _load().ttt_oracle_mlp_forward(_ptr(Q), _ptr(K), _ptr(V), _ptr(W1), _ptr(W2),
+                                        per_batch, _ptr(eta), B, H, T, d, m, int(b),
+                                        _ptr(Y), _ptr(W1o), _ptr(W2o), int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"oracle mlp_forward failed ({rc})")
+    return Y, W1o, W2o
+
+
+def linear_decode(q, k, v, W, eta):
+    """One online-GD token step for every (batch, head).  q,k,v [B,H,d];
+    W [B,H,d,d].  Returns (y [B,H,d], W_new [B,H,d,d]); W is not modified."""
+    q, k, v, eta = map(_f64, (q, k, v, eta))
+    Wn = _f64(W).copy()
+    B, H, d = q.shape
+    assert Wn.shape == (B, H, d, d) and eta.shape == (H,)
+    y = np.zeros((B, H, d))
+    rc = _load().ttt_oracle_linear_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(Wn), _ptr(eta),
+                                          B, H, d, _ptr(y))
+    if rc != 0:
+        raise RuntimeError(f"oracle linear_decode failed ({rc})")
+    return y, Wn

@@ -1,0 +1,362 @@
+/*
+ * ttt_oracle.c -- plain, slow, fp64 CPU oracle for the forward scan of a
+ * Test-Time-Training (TTT) layer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or
+ * call this file: only the test suite, the smoke check and the CPU-baseline
+ * leg of the benchmark use it.  It shares no code, header, table or helper
+ * with the HIP library; it does not include include/ttt.h.
+ *
+ * Sources (cited by page title and section; no other source is used):
+ *   [KV]  "Test-Time Training Layers: How Inner-Loop Gradient Descent Replaces
+ *         the Transformer KV Cache with Expressive Hidden Models"
+ *         (news.premlal.in), section "The Core Mechanism: The Hidden State as a
+ *         Machine Learning Model", steps 1-3 (loss with the 1/2 factor, one
+ *         gradient step, readout with the updated weights); section "Hardware
+ *         Parallelization: The Dual Form and Mini-Batch GPU Acceleration"
+ *         (mini-batches of 16 or 32 tokens, dual form equivalent to mini-batch
+ *         gradient descent).
+ *   [SEQ] "Test-Time Training (TTT) Layers for Sequence Modeling"
+ *         (dileepadev.github.io), sections "Mathematical Formulation" and
+ *         "Variants: TTT-Linear vs. TTT-MLP" (linear inner model; two-layer MLP
+ *         with a SiLU non-linearity).
+ *   [MEM] the test-time-training essay on ren-xubin.github.io, paragraph on
+ *         the dual form (gradients taken relative to the parameters at the
+ *         start of a block, their effects accumulated in causal order) and the
+ *         paragraph on fast weights being reset at the end of a sequence.
+ *   [E2]  the E2-TTT write-up on zhichai.net, section "The Curse of
+ *         Efficiency" (gradients computed at each chunk's start and applied to
+ *         the whole chunk).
+ *
+ * What is computed: mini-batch gradient descent in PRIMAL form, token by token,
+ * every intermediate fast weight W_t materialised.  This is the plain
+ * definition that the chunked dual form reaches exactly (up to rounding
+ * order), so the oracle is that definition written out.
+ *
+ * Conventions (readings where the pages leave a step open):
+ *   - row-vector form f(z;W) = z W, W[d_in][d_out] row-major.  The pages'
+ *     listings use the column form W k; the two are the same map with
+ *     W_row = W_col transposed.
+ *   - loss l(W; k, v) = 1/2 || f(k; W) - v ||^2  ([KV] step 1).
+ *   - within a mini-batch every gradient is taken at the chunk-start weights
+ *     and the gradients are SUMMED (no 1/b) in causal order ([MEM], [E2]).
+ *   - token t reads out with the weights after its own update ([KV] step 3).
+ *   - a final partial mini-batch (T mod b != 0) follows the same rules.
+ *   - eta is one value per head.
+ *   - every sequence starts from the given initial weights ([MEM]).
+ *
+ * Layouts (all dense, row-major, fp64):
+ *   Q, K, V, Y : [B][H][T][d]
+ *   W0         : [H][d][d]   (w0_per_batch == 0)  or  [B][H][d][d]  (== 1)
+ *   W_out      : [B][H][d][d]
+ *   MLP: W1 [.][d][m], W2 [.][m][d] with the same leading dims.
+ *
+ * Parallelism: the (batch, head) chains are independent; they are spread
+ * over OpenMP threads.  Inside a chain the loops are sequential and plain.
+ */
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORACLE_OK 0
+#define ORACLE_EINVAL (-1)
+#define ORACLE_ENOMEM (-2)
+
+static void set_threads(int nthreads)
+{
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+}
+
+/* Number of OpenMP threads the next parallel region will use. */
+int ttt_oracle_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* ------------------------------------------------------------------------ */
+/* TTT-Linear: inner model f(z; W) = z W ([SEQ] "TTT-Linear").               */
+/* ------------------------------------------------------------------------ */
+
+/* One (batch, head) chain of the linear scan.  q, k, v, y point at [T][d]. */
+static void linear_chain(const double* q, const double* k, const double* v,
+                         const double* w_init, double eta, long T, long d, long b,
+                         double* y, double* w_final,
+                         double* W, double* Wc, double* G, double* Wt, double* r)
+{
+    const long dd = d * d;
+    memcpy(W, w_init, (size_t)dd * sizeof(double));
+    for (long s = 0; s < T; s += b) {
+        long e = s + b < T ? s + b : T;
+        /* chunk-start weights; accumulated gradient starts at zero */
+        memcpy(Wc, W, (size_t)dd * sizeof(double));
+        memset(G, 0, (size_t)dd * sizeof(double));
+        for (long t = s; t < e; ++t) {
+            const double* kt = k + t * d;
+            const double* vt = v + t * d;
+            const double* qt = q + t * d;
+            /* residual of the reconstruction at the chunk-start weights:
+             * r = k Wc - v, so grad_W 1/2||k W - v||^2 = k^T r ([KV] step 1-2) */
+            for (long j = 0; j < d; ++j) {
+                double acc = 0.0;
+                for (long i = 0; i < d; ++i)
+                    acc += kt[i] * Wc[i * d + j];
+                r[j] = acc - vt[j];
+            }
+            /* G += k^T r  (sum over the tokens of the chunk so far) */
+            for (long i = 0; i < d; ++i)
+                for (long j = 0; j < d; ++j)
+                    G[i * d + j] += kt[i] * r[j];
+            /* W_t = Wc - eta G  ([KV] step 2, mini-batch reading) */
+            for (long x = 0; x < dd; ++x)
+                Wt[x] = Wc[x] - eta * G[x];
+            /* y_t = q_t W_t  ([KV] step 3: readout after the update) */
+            for (long j = 0; j < d; ++j) {
+                double acc = 0.0;
+                for (long i = 0; i < d; ++i)
+                    acc += qt[i] * Wt[i * d + j];
+                y[t * d + j] = acc;
+            }
+        }
+        /* the weights after the chunk are those after its last token */
+        memcpy(W, Wt, (size_t)dd * sizeof(double));
+    }
+    memcpy(w_final, W, (size_t)dd * sizeof(double));
+}
+
+int ttt_oracle_linear_forward(const double* Q, const double* K, const double* V,
+                              const double* W0, int w0_per_batch, const double* eta,
+                              long B, long H, long T, long d, long b,
+                              double* Y, double* W_out, int nthreads)
+{
+    if (B < 0 || H < 0 || T < 0 || d < 1 || b < 1)
+        return ORACLE_EINVAL;
+    if (!W0 || !eta || !W_out || (T > 0 && (!Q || !K || !V || !Y)))
+        return ORACLE_EINVAL;
+    const long dd = d * d;
+    const long units = B * H;
+    int status = ORACLE_OK;
+    set_threads(nthreads);
+#pragma omp parallel
+    {
+        double* ws = (double*)malloc((size_t)(4 * dd + d) * sizeof(double));
+        if (!ws) {
+#pragma omp atomic write
+            status = ORACLE_ENOMEM;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (long u = 0; u < units; ++u) {
+            if (!ws)
+                continue;
+            long h = u % H;
+            const double* w_init = W0 + (w0_per_batch ? u : h) * dd;
+            const long off = u * T * d;
+            linear_chain(Q + off, K + off, V + off, w_init, eta[h], T, d, b,
+                         Y + off, W_out + u * dd,
+                         ws, ws + dd, ws + 2 * dd, ws + 3 * dd, ws + 4 * dd);
+        }
+        free(ws);
+    }
+    return status;
+}
+
+/* ------------------------------------------------------------------------ */
+/* TTT-MLP: f(z; W1, W2) = SiLU(z W1) W2, d -> m -> d, no biases             */
+/* ([SEQ] "TTT-MLP": two-layer MLP with a SiLU non-linearity).                */
+/* ------------------------------------------------------------------------ */
+
+static double sigmoid(double x) { return 1.0 / (1.0 + exp(-x)); }
+static double silu(double x) { return x * sigmoid(x); }
+/* d/dx [x sigma(x)] = sigma(x) + x sigma(x) (1 - sigma(x)) */
+static double silu_grad(double x)
+{
+    double s = sigmoid(x);
+    return s * (1.0 + x * (1.0 - s));
+}
+
+struct mlp_ws {
+    double *A1, *A2, *A1c, *A2c, *G1, *G2, *W1t, *W2t;
+    double *h, *a, *e, *ga, *dh, *hq, *aq;
+};
+
+static void mlp_chain(const double* q, const double* k, const double* v,
+                      const double* w1_init, const double* w2_init, double eta,
+                      long T, long d, long m, long b,
+                      double* y, double* w1_final, double* w2_final, struct mlp_ws* w)
+{
+    const long dm = d * m;
+    memcpy(w->A1, w1_init, (size_t)dm * sizeof(double));
+    memcpy(w->A2, w2_init, (size_t)dm * sizeof(double));
+    for (long s = 0; s < T; s += b) {
+        long e = s + b < T ? s + b : T;
+        memcpy(w->A1c, w->A1, (size_t)dm * sizeof(double));
+        memcpy(w->A2c, w->A2, (size_t)dm * sizeof(double));
+        memset(w->G1, 0, (size_t)dm * sizeof(double));
+        memset(w->G2, 0, (size_t)dm * sizeof(double));
+        for (long t = s; t < e; ++t) {
+            const double* kt = k + t * d;
+            const double* vt = v + t * d;
+            const double* qt = q + t * d;
+            /* forward of the inner model on the key, at the chunk-start weights */
+            for (long p = 0; p < m; ++p) {
+                double acc = 0.0;
+                for (long i = 0; i < d; ++i)
+                    acc += kt[i] * w->A1c[i * m + p];
+                w->h[p] = acc;
+                w->a[p] = silu(acc);
+            }
+            for (long j = 0; j < d; ++j) {
+                double acc = 0.0;
+                for (long p = 0; p < m; ++p)
+                    acc += w->a[p] * w->A2c[p * d + j];
+                w->e[j] = acc - vt[j];                       /* dl/dz */
+            }
+            /* backward through the inner model (chain rule) */
+            for (long p = 0; p < m; ++p) {
+                double acc = 0.0;
+                for (long j = 0; j < d; ++j)
+                    acc += w->e[j] * w->A2c[p * d + j];
+                w->ga[p] = acc;                              /* dl/da */
+                w->dh[p] = acc * silu_grad(w->h[p]);         /* dl/dh */
+            }
+            for (long p = 0; p < m; ++p)
+                for (long j = 0; j < d; ++j)
+                    w->G2[p * d + j] += w->a[p] * w->e[j];   /* dl/dW2 = a^T e */
+            for (long i = 0; i < d; ++i)
+                for (long p = 0; p < m; ++p)
+                    w->G1[i * m + p] += kt[i] * w->dh[p];    /* dl/dW1 = k^T dh */
+            /* weights after token t, then the readout with them */
+            for (long x = 0; x < dm; ++x) {
+                w->W1t[x] = w->A1c[x] - eta * w->G1[x];
+                w->W2t[x] = w->A2c[x] - eta * w->G2[x];
+            }
+            for (long p = 0; p < m; ++p) {
+                double acc = 0.0;
+                for (long i = 0; i < d; ++i)
+                    acc += qt[i] * w->W1t[i * m + p];
+                w->hq[p] = acc;
+                w->aq[p] = silu(acc);
+            }
+            for (long j = 0; j < d; ++j) {
+                double acc = 0.0;
+                for (long p = 0; p < m; ++p)
+                    acc += w->aq[p] * w->W2t[p * d + j];
+                y[t * d + j] = acc;
+            }
+        }
+        memcpy(w->A1, w->W1t, (size_t)dm * sizeof(double));
+        memcpy(w->A2, w->W2t, (size_t)dm * sizeof(double));
+    }
+    memcpy(w1_final, w->A1, (size_t)dm * sizeof(double));
+    memcpy(w2_final, w->A2, (size_t)dm * sizeof(double));
+}
+
+int ttt_oracle_mlp_forward(const double* Q, const double* K, const double* V,
+                           const double* W1_0, const double* W2_0, int w0_per_batch,
+                           const double* eta, long B, long H, long T, long d, long m, long b,
+                           double* Y, double* W1_out, double* W2_out, int nthreads)
+{
+    if (B < 0 || H < 0 || T < 0 || d < 1 || m < 1 || b < 1)
+        return ORACLE_EINVAL;
+    if (!W1_0 || !W2_0 || !eta || !W1_out || !W2_out ||
+        (T > 0 && (!Q || !K || !V || !Y)))
+        return ORACLE_EINVAL;
+    const long dm = d * m;
+    const long units = B * H;
+    int status = ORACLE_OK;
+    set_threads(nthreads);
+#pragma omp parallel
+    {
+        double* buf = (double*)malloc((size_t)(8 * dm + 6 * m + d) * sizeof(double));
+        struct mlp_ws w;
+        memset(&w, 0, sizeof w);
+        if (!buf) {
+#pragma omp atomic write
+            status = ORACLE_ENOMEM;
+        } else {
+            w.A1 = buf;
+            w.A2 = w.A1 + dm;
+            w.A1c = w.A2 + dm;
+            w.A2c = w.A1c + dm;
+            w.G1 = w.A2c + dm;
+            w.G2 = w.G1 + dm;
+            w.W1t = w.G2 + dm;
+            w.W2t = w.W1t + dm;
+            w.h = w.W2t + dm;
+            w.a = w.h + m;
+            w.ga = w.a + m;
+            w.dh = w.ga + m;
+            w.hq = w.dh + m;
+            w.aq = w.hq + m;
+            w.e = w.aq + m;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (long u = 0; u < units; ++u) {
+            if (!buf)
+                continue;
+            long h = u % H;
+            long src = w0_per_batch ? u : h;
+            const long off = u * T * d;
+            mlp_chain(Q + off, K + off, V + off, W1_0 + src * dm, W2_0 + src * dm, eta[h],
+                      T, d, m, b, Y + off, W1_out + u * dm, W2_out + u * dm, &w);
+        }
+        free(buf);
+    }
+    return status;
+}
+
+/* ------------------------------------------------------------------------ */
+/* TTT-Linear single-token step (online gradient descent, the b = 1 case):    */
+/* r = k W - v; W <- W - eta k^T r; y = q W  ([KV] steps 1-3; the section on  */
+/* the dual form names online GD as the form used for token-by-token decode). */
+/* q, k, v, y: [B][H][d]; W: [B][H][d][d] updated in place.                   */
+/* ------------------------------------------------------------------------ */
+int ttt_oracle_linear_decode(const double* q, const double* k, const double* v,
+                             double* W, const double* eta, long B, long H, long d,
+                             double* y)
+{
+    if (B < 0 || H < 0 || d < 1)
+        return ORACLE_EINVAL;
+    if (B * H > 0 && (!q || !k || !v || !W || !eta || !y))
+        return ORACLE_EINVAL;
+    double* r = (double*)malloc((size_t)d * sizeof(double));
+    if (!r)
+        return ORACLE_ENOMEM;
+    for (long u = 0; u < B * H; ++u) {
+        long h = u % H;
+        const double* kt = k + u * d;
+        const double* vt = v + u * d;
+        const double* qt = q + u * d;
+        double* Wu = W + u * d * d;
+        for (long j = 0; j < d; ++j) {
+            double acc = 0.0;
+            for (long i = 0; i < d; ++i)
+                acc += kt[i] * Wu[i * d + j];
+            r[j] = acc - vt[j];
+        }
+        for (long i = 0; i < d; ++i)
+            for (long j = 0; j < d; ++j) {
+                double g = kt[i] * r[j];                     /* grad = k^T r */
+                Wu[i * d + j] -= eta[h] * g;
+            }
+        for (long j = 0; j < d; ++j) {
+            double acc = 0.0;
+            for (long i = 0; i < d; ++i)
+                acc += qt[i] * Wu[i * d + j];
+            y[u * d + j] = acc;
+        }
+    }
+    free(r);
+    return ORACLE_OK;
+}

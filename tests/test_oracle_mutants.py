@@ -1,0 +1,112 @@
+"""Planted mistakes in the oracle must be caught by its pins.
+
+Each case below copies ttt_oracle.c, plants one plausible mistake in the copy
+(a wrong sign, a transposed operand, a dropped factor, the readout taken
+before the update, ...), compiles it with gcc into a temporary library and
+runs the pin battery from test_oracle.py against it.  At least one pin must
+fail for every mutant; the unmodified source must pass them all.  Everything
+here runs on the CPU.
+"""
+import os
+import subprocess
+import tempfile
+
+import numpy as np
+import pytest
+
+import oracle
+import test_oracle as pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "ttt_oracle.c")
+
+MUTANTS = {
+    "residual_sign": ("r[j] = acc - vt[j];\n            }\n            /* G +=",
+                      "r[j] = vt[j] - acc;\n            }\n            /* G +="),
+    "gradient_transposed": ("G[i * d + j] += kt[i] * r[j];", "G[i * d + j] += kt[j] * r[i];"),
+    "prediction_transposed": ("acc += kt[i] * Wc[i * d + j];", "acc += kt[i] * Wc[j * d + i];"),
+    "readout_before_update": ("acc += qt[i] * Wt[i * d + j];", "acc += qt[i] * Wc[i * d + j];"),
+    "missing_half": ("Wt[x] = Wc[x] - eta * G[x];", "Wt[x] = Wc[x] - 2.0 * eta * G[x];"),
+    "gradient_not_accumulated": ("G[i * d + j] += kt[i] * r[j];", "G[i * d + j] = kt[i] * r[j];"),
+    "silu_grad_sign": ("return s * (1.0 + x * (1.0 - s));", "return s * (1.0 - x * (1.0 - s));"),
+    "silu_is_sigmoid": ("static double silu(double x) { return x * sigmoid(x); }",
+                        "static double silu(double x) { return sigmoid(x); }"),
+    "mlp_w2_grad_uses_preactivation": ("w->G2[p * d + j] += w->a[p] * w->e[j];",
+                                       "w->G2[p * d + j] += w->h[p] * w->e[j];"),
+    "mlp_w1_grad_drops_activation_grad": ("w->dh[p] = acc * silu_grad(w->h[p]);",
+                                          "w->dh[p] = acc;"),
+    "mlp_readout_old_w2": ("acc += w->aq[p] * w->W2t[p * d + j];",
+                           "acc += w->aq[p] * w->A2c[p * d + j];"),
+    "decode_sign": ("Wu[i * d + j] -= eta[h] * g;", "Wu[i * d + j] += eta[h] * g;"),
+    "decode_residual_uses_query": ("acc += kt[i] * Wu[i * d + j];", "acc += qt[i] * Wu[i * d + j];"),
+}
+
+
+def _battery():
+    """Run the pins; return the names of those that fail."""
+    failed = []
+    checks = [
+        ("worked_examples", lambda: pins.test_worked_examples_exact(oracle)),
+        ("eta_zero_linear", lambda: pins.test_eta_zero_linear(oracle)),
+        ("autograd_linear_b1", lambda: pins.test_autograd_minibatch_linear(oracle, 1)),
+        ("autograd_linear_b4", lambda: pins.test_autograd_minibatch_linear(oracle, 4)),
+        ("linear_attention", lambda: pins.test_zero_init_is_causal_linear_attention(oracle, 16, 16)),
+        ("eta_zero_mlp", lambda: pins.test_eta_zero_mlp(oracle)),
+        ("mlp_kernel_attention", lambda: pins.test_mlp_zero_second_layer_is_kernel_linear_attention(oracle)),
+        ("autograd_mlp_b4", lambda: pins.test_autograd_minibatch_mlp(oracle, 4)),
+        ("mlp_fd", lambda: pins.test_mlp_gradient_matches_finite_differences(oracle)),
+        ("decode_vs_scan", lambda: pins.test_decode_steps_equal_b1_scan(oracle)),
+        ("decode_example", lambda: pins.test_decode_worked_example(oracle)),
+    ]
+    for name, fn in checks:
+        try:
+            with np.errstate(all="ignore"):
+                fn()
+        except AssertionError:
+            failed.append(name)
+    return failed
+
+
+def _build_variant(src_text, tmpdir, tag):
+    c = os.path.join(tmpdir, f"oracle_{tag}.c")
+    so = os.path.join(tmpdir, f"liboracle_{tag}.so")
+    with open(c, "w") as f:
+        f.write(src_text)
+    subprocess.run(["gcc", "-O1", "-fopenmp", "-fPIC", "-shared", "-std=c11", c, "-o", so, "-lm"],
+                   check=True, capture_output=True)
+    return so
+
+
+def _with_library(so):
+    import ctypes
+    saved = oracle._lib
+    oracle._lib = None
+    real = oracle._LIB
+    oracle._LIB = so
+    try:
+        oracle._load()
+        return _battery()
+    finally:
+        oracle._lib = saved
+        oracle._LIB = real
+        del ctypes
+
+
+@pytest.fixture(scope="module")
+def source():
+    return open(SRC).read()
+
+
+def test_unmodified_source_passes_battery(source):
+    with tempfile.TemporaryDirectory() as td:
+        so = _build_variant(source, td, "clean")
+        assert _with_library(so) == []
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(source, name):
+    old, new = MUTANTS[name]
+    assert source.count(old) == 1, f"mutation site for {name} not unique"
+    with tempfile.TemporaryDirectory() as td:
+        so = _build_variant(source.replace(old, new), td, name)
+        failed = _with_library(so)
+    assert failed, f"mutant {name} passed every pin"
