@@ -1,0 +1,335 @@
+#!/usr/bin/env python3
+"""Throughput of the TTT forward scan on one MI355X; prints ONE JSON line.
+
+Metric: TTT forward tokens/s = B*T / (seconds per step), at d = 64, b = 16,
+plus the fraction of the MFMA or HBM roofline reached by the dominant kernel.
+
+A step is one pass of the hot path over one batch of synthetic inputs that
+are already resident in HBM:
+  - TTT-Linear workloads: ttt_linear_forward, then the workload's single-token
+    decode steps (ttt_linear_decode_step) from the final state, if any;
+  - TTT-MLP workloads: ttt_mlp_forward.
+--config picks the workload (1..5, default 2: B1 H4 d64 T2048 b16 fp32).
+Unless --quick is given, the other d = 64 workloads are measured too and
+reported under "workloads" in the same line.
+
+roofline.achieved = algorithmic bytes (HBM bound) or flops (MFMA bound) of
+one launch of the dominant kernel / its mean duration from HIP events
+recorded on the launch stream around every launch in the timed region.
+cpu_baseline = the fp64 oracle (plain loops, OpenMP over chains) timed on
+this host's cores on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "TTT forward tokens/sec (B·T/s) at d=64,b=16; % of MFMA/HBM roofline"
+PEAK_HBM = 8.0e12            # bytes/s, MI355X HBM3E
+PEAK_FLOPS = {"bf16": 2.5e15, "fp32": 157.3e12}   # dense MFMA
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = {
+    "linear_mfma_kernel": "ttt_linear_mfma.hip",
+    "linear_generic_kernel": "ttt_generic.hip",
+    "mlp_generic_kernel": "ttt_generic.hip",
+    "mlp_mfma_kernel": "ttt_mlp_mfma.hip",
+    "decode_kernel": "ttt_decode.hip",
+}
+
+
+# ---------------------------------------------------------------------------
+# algorithmic work of one launch
+# ---------------------------------------------------------------------------
+def _chunks(T, b):
+    full, rem = divmod(T, b)
+    return [b] * full + ([rem] if rem else [])
+
+
+def linear_work(w):
+    """flops and HBM bytes of one ttt_linear_forward call (dense b x b tiles)."""
+    s = 4 if w.dtype == "fp32" else 2
+    d, units = w.d, w.B * w.H
+    flops = units * sum(6 * n * d * d + 4 * n * n * d for n in _chunks(w.T, w.b))
+    nbytes = units * w.T * 4 * d * s + w.H * d * d * 4 + units * d * d * 4
+    return flops, nbytes
+
+
+def mlp_work(w):
+    s = 4 if w.dtype == "fp32" else 2
+    d, m, units = w.d, w.m, w.B * w.H
+    flops = units * sum(14 * n * d * m + 4 * n * n * d + 4 * n * n * m for n in _chunks(w.T, w.b))
+    nbytes = units * w.T * 4 * d * s + (w.H + units) * 2 * d * m * 4
+    return flops, nbytes
+
+
+def decode_work(w):
+    s = 4 if w.dtype == "fp32" else 2
+    units, d = w.B * w.H, w.d
+    return units * 6 * d * d, units * (2 * d * d * 4 + 4 * d * s)
+
+
+def kernel_name(w):
+    if w.kind == "mlp":
+        return "mlp_mfma_kernel" if (w.dtype == "bf16" and w.d == 64 and w.m == 256 and w.b == 16) \
+            else "mlp_generic_kernel"
+    return "linear_mfma_kernel" if (w.dtype == "bf16" and w.d == 64 and w.b == 16) \
+        else "linear_generic_kernel"
+
+
+def source_sha(kernel):
+    path = os.path.join(ROOT, "test_sequence_layers_linear_amd", "csrc", KERNEL_SOURCES[kernel])
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def stored_traffic(kernel, workload):
+    """HBM bytes per launch from committed rocprofv3 --pmc summaries, if they
+    were taken on the current source of the kernel; else None."""
+    path = os.path.join(PROFILES, "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(kernel, {}).get(workload)
+    except (ValueError, OSError):
+        return None
+    if not rec or rec.get("source_sha") != source_sha(kernel):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def roofline(w, flops, nbytes, seconds, kernel):
+    dt = "bf16" if w.dtype == "bf16" else "fp32"
+    ridge = PEAK_FLOPS[dt] / PEAK_HBM
+    if flops / nbytes > ridge:
+        ach, peak, unit, bound = flops / seconds / 1e12, PEAK_FLOPS[dt] / 1e12, "TFLOP/s", "mfma"
+    else:
+        ach, peak, unit, bound = nbytes / seconds / 1e9, PEAK_HBM / 1e9, "GB/s", "hbm"
+    return {"bound": bound, "achieved": round(ach, 3), "peak": peak, "unit": unit,
+            "frac": round(ach / peak, 5), "traffic": stored_traffic(kernel, w.name),
+            "kernel": kernel, "mean_launch_us": round(seconds * 1e6, 3),
+            "algorithmic_flops": flops, "algorithmic_bytes": nbytes,
+            "active_cu_ceiling": round(min(1.0, w.B * w.H / 256), 4)}
+
+
+# ---------------------------------------------------------------------------
+# GPU measurement
+# ---------------------------------------------------------------------------
+class Runner:
+    def __init__(self, w, seed):
+        import torch
+        import test_sequence_layers_linear_amd as ttt
+        from test_sequence_layers_linear_amd.inputs import make_inputs
+
+        self.torch, self.ttt, self.w = torch, ttt, w
+        self.host = make_inputs(w, seed)
+        self.g = {k: v.cuda() for k, v in self.host.items()}
+        g = self.g
+        self.Y = torch.empty_like(g["Q"])
+        if w.kind == "linear":
+            self.W = torch.empty((w.B, w.H, w.d, w.d), device="cuda")
+        else:
+            self.W1 = torch.empty((w.B, w.H, w.d, w.m), device="cuda")
+            self.W2 = torch.empty((w.B, w.H, w.m, w.d), device="cuda")
+        if w.decode_steps:
+            self.y = torch.empty_like(g["dq"][0])
+        torch.cuda.synchronize()
+
+    def forward(self):
+        g, ttt = self.g, self.ttt
+        if self.w.kind == "linear":
+            ttt.ttt_linear_forward(g["Q"], g["K"], g["V"], g["W0"], g["eta"], self.w.b,
+                                   Y=self.Y, W_out=self.W)
+        else:
+            ttt.ttt_mlp_forward(g["Q"], g["K"], g["V"], g["W1"], g["W2"], g["eta"], self.w.b,
+                                Y=self.Y, W1_out=self.W1, W2_out=self.W2)
+
+    def decode(self):
+        g, ttt = self.g, self.ttt
+        for s in range(self.w.decode_steps):
+            ttt.ttt_linear_decode_step(g["dq"][s], g["dk"][s], g["dv"][s], self.W, g["eta"],
+                                       y=self.y)
+
+    def measure(self, steps, warmup):
+        torch = self.torch
+        for _ in range(warmup):
+            self.forward()
+            self.decode()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        dv = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)] if self.w.decode_steps else []
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            ev[i][0].record()
+            self.forward()
+            ev[i][1].record()
+            if dv:
+                dv[i][0].record()
+                self.decode()
+                dv[i][1].record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        fwd = sum(a.elapsed_time(b) for a, b in ev) / steps / 1e3
+        dec = (sum(a.elapsed_time(b) for a, b in dv) / steps / 1e3) if dv else 0.0
+        return wall / steps, fwd, dec
+
+    def measure_cold(self, reps):
+        """Forward duration with the 256 MB last-level cache flushed before each launch."""
+        torch = self.torch
+        junk = torch.empty(512 * 1024 * 1024 // 4, device="cuda")
+        times = []
+        for _ in range(reps):
+            junk.fill_(1.0)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            self.forward()
+            b.record()
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b) / 1e3)
+        del junk
+        times.sort()
+        return times[len(times) // 2]
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle on a bounded sample
+# ---------------------------------------------------------------------------
+def _select(host, chains, T):
+    import torch
+    out = {k: torch.stack([host[k][b, h, :T] for b, h in chains])[None] for k in ("Q", "K", "V")}
+    out["eta"] = torch.stack([host["eta"][h] for _, h in chains])
+    for k in ("W0", "W1", "W2"):
+        if k in host:
+            out[k] = torch.stack([host[k][h] for _, h in chains])
+    return out
+
+
+def run_cpu_baseline(w, host, target_s):
+    import oracle
+    threads = max(1, oracle.max_threads())
+    units = [(b, h) for b in range(w.B) for h in range(w.H)]
+    k = min(len(units), threads)
+    chains = units[:k]
+    sub = _select(host, chains, w.T)
+
+    def once():
+        if w.kind == "linear":
+            oracle.linear_forward(sub["Q"], sub["K"], sub["V"], sub["W0"], sub["eta"], w.b,
+                                  nthreads=k)
+        else:
+            oracle.mlp_forward(sub["Q"], sub["K"], sub["V"], sub["W1"], sub["W2"], sub["eta"],
+                               w.b, nthreads=k)
+
+    t0 = time.perf_counter()
+    once()
+    first = time.perf_counter() - t0
+    reps = max(1, int(math.ceil((target_s - first) / max(first, 1e-6))))
+    reps = min(reps, 1000)
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        once()
+    el = time.perf_counter() - t0
+    tokens = k * w.T * reps / w.H      # B*T-equivalent tokens (all heads of a token)
+    return {"value": round(tokens / el, 3), "unit": "tokens/s", "cores": k, "kind": "oracle",
+            "sample": f"{k} of {len(units)} (batch, head) chains at full T={w.T}, "
+                      f"{reps} repetitions, {el:.1f} s; tokens counted as chains*T/H",
+            "host_threads_available": threads}
+
+
+# ---------------------------------------------------------------------------
+def measure_workload(cfg, steps, warmup, cold_reps):
+    from test_sequence_layers_linear_amd.inputs import CONFIGS, default_seed
+    w = CONFIGS[cfg]
+    r = Runner(w, default_seed(cfg))
+    per_step, fwd, dec = r.measure(steps, warmup)
+    flops, nbytes = (linear_work if w.kind == "linear" else mlp_work)(w)
+    kern = kernel_name(w)
+    out = {"workload": w.name, "config": cfg, "tokens_per_s": w.B * w.T / per_step,
+           "ms_per_step": per_step * 1e3, "forward_us": fwd * 1e6,
+           "forward_tokens_per_s": w.B * w.T / fwd,
+           "roofline": roofline(w, flops, nbytes, fwd, kern)}
+    if cold_reps:
+        cold = r.measure_cold(cold_reps)
+        out["forward_us_cold_llc"] = cold * 1e6
+        out["roofline_cold_llc_frac"] = roofline(w, flops, nbytes, cold, kern)["frac"]
+    if w.decode_steps:
+        df, db = decode_work(w)
+        per = dec / w.decode_steps
+        out["decode"] = {"steps": w.decode_steps, "us_per_step": per * 1e6,
+                         "GB_per_s": db / per / 1e9, "hbm_frac": db / per / PEAK_HBM,
+                         "bytes_per_step": db}
+    return w, r, out
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--quick", action="store_true", help="only the selected workload")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              f"(--gpus {args.gpus} requested). (batch, head) chains are independent, so "
+              "several GPUs would each run this same kernel on their share.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    print(f"[bench] workload config {args.config}: steps {args.steps} warmup {args.warmup}",
+          file=sys.stderr, flush=True)
+    w, runner, main_res = measure_workload(args.config, args.steps, args.warmup, cold_reps=5)
+    print(f"[bench] {w.name}: {main_res['tokens_per_s']:.4g} tokens/s", file=sys.stderr, flush=True)
+
+    extras = {}
+    if not args.quick:
+        for cfg in (3, 4, 5):
+            if cfg == args.config:
+                continue
+            st = 10 if cfg != 5 else 3
+            print(f"[bench] extra workload config {cfg}", file=sys.stderr, flush=True)
+            _, rr, res = measure_workload(cfg, st, 2, cold_reps=3)
+            extras[str(cfg)] = res
+            del rr
+            torch.cuda.empty_cache()
+            print(f"[bench]   {res['workload']}: {res['tokens_per_s']:.4g} tokens/s, "
+                  f"roofline frac {res['roofline']['frac']}", file=sys.stderr, flush=True)
+
+    cpu = None
+    if not args.no_cpu:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        cpu = run_cpu_baseline(w, runner.host, args.cpu_seconds)
+
+    line = {
+        "metric": METRIC, "value": round(main_res["tokens_per_s"], 3), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(main_res["ms_per_step"], 6), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32" if w.dtype == "fp32" else "bf16",
+        "data": "synthetic (seeded Gaussian Q/K/V, see inputs.py)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "d": w.d, "b": w.b,
+                   "m": w.m or None, "decode_steps": w.decode_steps, "global_batch": w.B,
+                   "seq_len": w.T, "parallelism": "none (one GPU; one workgroup per chain)"},
+        "roofline": main_res["roofline"],
+        "cpu_baseline": cpu,
+        "detail": {k: v for k, v in main_res.items() if k not in ("roofline",)},
+        "workloads": extras,
+        "device": torch.cuda.get_device_name(0),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

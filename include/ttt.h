@@ -1,0 +1,142 @@
+/*
+ * ttt.h -- C ABI of libttt.so: the forward scan of a Test-Time-Training (TTT)
+ * layer on one AMD Instinct MI355X (gfx950).
+ *
+ * The layer's hidden state is a per-head fast weight W.  Each mini-batch of
+ * b tokens takes one gradient step of the reconstruction loss
+ *     l(W; k, v) = 1/2 || f(k; W) - v ||^2
+ * and every token reads out y = f(q; W) with the weights after its own
+ * update.  Definitions: "Test-Time Training Layers: How Inner-Loop Gradient
+ * Descent Replaces the Transformer KV Cache with Expressive Hidden Models"
+ * (news.premlal.in), section "The Core Mechanism", steps 1-3, and section
+ * "Hardware Parallelization: The Dual Form and Mini-Batch GPU Acceleration";
+ * "Test-Time Training (TTT) Layers for Sequence Modeling"
+ * (dileepadev.github.io), sections "Mathematical Formulation" and
+ * "Variants: TTT-Linear vs. TTT-MLP".
+ *
+ * Conventions shared by every entry point:
+ *   - Row-vector form f(z; W) = z W; W[i][j] has i = input, j = output.
+ *   - Within a mini-batch every gradient is taken at the chunk-start W and
+ *     summed (no 1/b) in token order; a final partial mini-batch
+ *     (T mod b != 0) follows the same rules.
+ *   - eta is one fp32 learning rate per head.
+ *   - All arrays are dense, row-major, and live in DEVICE memory owned by the
+ *     caller.  The library allocates nothing and keeps no state between
+ *     calls.
+ *   - qkv_dtype selects the element type of Q/K/V/Y (and q/k/v/y): TTT_F32
+ *     (float) or TTT_BF16 (bfloat16 bits, round-to-nearest-even on output).
+ *     Fast-weight state is always fp32.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default
+ *     stream) and the call returns without synchronising.
+ *   - Arguments are validated before any HIP call; on an error nothing is
+ *     launched and nothing is written.  No C++ exception crosses the ABI.
+ *   - Results are deterministic run to run (no atomics, fixed reduction
+ *     order).
+ */
+#ifndef TTT_H
+#define TTT_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    TTT_F32 = 0,
+    TTT_BF16 = 1
+} ttt_dtype;
+
+typedef enum {
+    TTT_OK = 0,
+    TTT_ERR_INVALID_ARG = -1,   /* null pointer, negative size, b < 1, aliasing */
+    TTT_ERR_UNSUPPORTED = -2,   /* shape or dtype outside what the kernels cover */
+    TTT_ERR_HIP = -3            /* a HIP call or kernel launch failed */
+} ttt_status;
+
+/*
+ * TTT-Linear, chunked dual form.  Inner model f(z; W) = z W with W [d][d].
+ * Per mini-batch (rows = tokens of the chunk, W = chunk-start weights):
+ *     E      = K W - V
+ *     Y      = Q W - eta_h * tril(Q K^T) E        (diagonal kept)
+ *     W_next = W - eta_h * K^T E
+ * which is exactly mini-batch gradient descent on the loss above with the
+ * readout after each token's update (the dual form named in the section
+ * "Hardware Parallelization" of the news.premlal.in page; the dual-form
+ * paragraph of the ren-xubin.github.io essay).
+ *
+ *   Q, K, V      [B][H][T][d], qkv_dtype, read only.
+ *   W0           fp32, [H][d][d] shared over the batch (w0_per_batch = 0) or
+ *                [B][H][d][d] (w0_per_batch = 1).
+ *   eta          fp32 [H].
+ *   Y            [B][H][T][d], qkv_dtype, written.
+ *   W_out        fp32 [B][H][d][d], the weights after the last token.  It may
+ *                be the same pointer as W0 when w0_per_batch = 1 (in-place
+ *                state update); no other overlap between an output and any
+ *                argument is allowed.
+ *   B, H, T      >= 0.  B*H = 0 is a no-op.  T = 0 writes W_out = W0.
+ *   d            16, 32, 64 or 128.
+ *   b            mini-batch size, 1 <= b <= 64.  (d = 64, b = 16 runs the
+ *                MFMA kernel; other shapes run a plainer kernel.)
+ * Errors: TTT_ERR_INVALID_ARG, TTT_ERR_UNSUPPORTED (d, b, dtype, or on-chip
+ * memory the shape needs), TTT_ERR_HIP.
+ */
+int ttt_linear_forward(const void* Q, const void* K, const void* V, int qkv_dtype,
+                       const float* W0, int w0_per_batch, const float* eta,
+                       int64_t B, int64_t H, int64_t T, int d, int b,
+                       void* Y, float* W_out, void* stream);
+
+/*
+ * TTT-MLP, chunked dual form.  Inner model f(z) = SiLU(z W1) W2, W1 [d][m],
+ * W2 [m][d], no biases ("Test-Time Training (TTT) Layers for Sequence
+ * Modeling", section "Variants": a two-layer MLP with a SiLU non-linearity).
+ * Per mini-batch, all gradients at the chunk-start (W1, W2), the inner
+ * backward pass fused into the scan:
+ *     Hk = K W1, Ak = SiLU(Hk), E = Ak W2 - V
+ *     D  = (E W2^T) * SiLU'(Hk)
+ *     Hq = Q W1 - eta_h tril(Q K^T) D,   Aq = SiLU(Hq)
+ *     Y  = Aq W2 - eta_h tril(Aq Ak^T) E
+ *     W1 <- W1 - eta_h K^T D,  W2 <- W2 - eta_h Ak^T E
+ *
+ *   Q, K, V, Y   as for ttt_linear_forward.
+ *   W1_0, W2_0   fp32 [H][d][m], [H][m][d] (w0_per_batch = 0) or with a
+ *                leading [B] (w0_per_batch = 1).
+ *   W1_out, W2_out  fp32 [B][H][d][m], [B][H][m][d].  They may equal
+ *                W1_0 / W2_0 when w0_per_batch = 1.
+ *   d            16, 32 or 64;  m a multiple of 16 in [16, 512];  1 <= b <= 64.
+ *                (d = 64, m = 256, b = 16 runs the MFMA kernel.)
+ * Errors as for ttt_linear_forward.
+ */
+int ttt_mlp_forward(const void* Q, const void* K, const void* V, int qkv_dtype,
+                    const float* W1_0, const float* W2_0, int w0_per_batch,
+                    const float* eta, int64_t B, int64_t H, int64_t T, int d, int m, int b,
+                    void* Y, float* W1_out, float* W2_out, void* stream);
+
+/*
+ * TTT-Linear single-token step (online gradient descent, the b = 1 case; the
+ * "Hardware Parallelization" section of the news.premlal.in page names this
+ * sequential form as the one for token-by-token decoding):
+ *     r = k W - v;   W <- W - eta_h k^T r;   y = q W   (updated W)
+ *
+ *   q, k, v      [B][H][d], qkv_dtype, read only.
+ *   W            fp32 [B][H][d][d], updated IN PLACE.
+ *   eta          fp32 [H].
+ *   y            [B][H][d], qkv_dtype, written; must not overlap any input.
+ *   d            16, 32, 64 or 128.
+ * Errors as for ttt_linear_forward.
+ */
+int ttt_linear_decode_step(const void* q, const void* k, const void* v, int qkv_dtype,
+                           float* W, const float* eta, int64_t B, int64_t H, int d,
+                           void* y, void* stream);
+
+/* Static, human-readable text for a status code (never NULL). */
+const char* ttt_status_string(int status);
+
+/* ABI version of this header: (major << 16) | minor. */
+int ttt_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TTT_H */

@@ -1,0 +1,196 @@
+"""Python binding of libttt.so: the TTT forward scan on MI355X (gfx950).
+
+Argument marshalling only.  Every step of the scan runs in the HIP kernels
+behind the C ABI declared in include/ttt.h; this module checks tensor
+properties, allocates outputs with torch (device memory only) and passes raw
+device pointers plus the current HIP stream.  There is no CPU fallback: if
+libttt.so is missing or a call fails, an exception is raised.
+
+Functions (same names as the C ABI):
+    ttt_linear_forward(Q, K, V, W0, eta, b)           -> (Y, W_out)
+    ttt_mlp_forward(Q, K, V, W1, W2, eta, b)          -> (Y, W1_out, W2_out)
+    ttt_linear_decode_step(q, k, v, W, eta)           -> y   (W updated in place)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libttt.so")
+
+TTT_F32 = 0
+TTT_BF16 = 1
+TTT_OK = 0
+TTT_ERR_INVALID_ARG = -1
+TTT_ERR_UNSUPPORTED = -2
+TTT_ERR_HIP = -3
+
+_lib = None
+
+
+class TTTError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{message} (status {status})")
+        self.status = status
+
+
+def load_library():
+    """Load libttt.so (built in place by test_sequence_layers_linear_amd/build.py)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built: run __graft_entry__.build() "
+                           "or python test_sequence_layers_linear_amd/build.py")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, L = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+    lib.ttt_linear_forward.argtypes = [P, P, P, I, P, I, P, L, L, L, I, I, P, P, P]
+    lib.ttt_linear_forward.restype = I
+    lib.ttt_mlp_forward.argtypes = [P, P, P, I, P, P, I, P, L, L, L, I, I, I, P, P, P, P]
+    lib.ttt_mlp_forward.restype = I
+    lib.ttt_linear_decode_step.argtypes = [P, P, P, I, P, P, L, L, I, P, P]
+    lib.ttt_linear_decode_step.restype = I
+    lib.ttt_status_string.argtypes = [I]
+    lib.ttt_status_string.restype = ctypes.c_char_p
+    lib.ttt_abi_version.argtypes = []
+    lib.ttt_abi_version.restype = I
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().ttt_status_string(int(status)).decode()
+
+
+def _check(status: int):
+    if status != TTT_OK:
+        raise TTTError(status, status_string(status))
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return TTT_F32
+    if t.dtype == torch.bfloat16:
+        return TTT_BF16
+    raise TypeError(f"Q/K/V must be float32 or bfloat16, got {t.dtype}")
+
+
+def _need(t: torch.Tensor, name: str, device, dtype=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be in GPU memory (got {t.device})")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream_handle(device, stream):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def ttt_linear_forward(Q, K, V, W0, eta, b: int, Y=None, W_out=None, stream=None):
+    """TTT-Linear dual-form forward.  Q,K,V [B,H,T,d] fp32/bf16 on a GPU;
+    W0 fp32 [H,d,d] (shared over the batch) or [B,H,d,d]; eta fp32 [H].
+    Returns (Y [B,H,T,d] in Q's dtype, W_out fp32 [B,H,d,d])."""
+    lib = load_library()
+    if Q.dim() != 4:
+        raise ValueError("Q must be [B,H,T,d]")
+    dev = Q.device
+    B, H, T, d = Q.shape
+    for t, n in ((Q, "Q"), (K, "K"), (V, "V")):
+        _need(t, n, dev, Q.dtype)
+        if t.shape != Q.shape:
+            raise ValueError(f"{n} shape {tuple(t.shape)} != Q shape {tuple(Q.shape)}")
+    _need(W0, "W0", dev, torch.float32)
+    _need(eta, "eta", dev, torch.float32)
+    per_batch = W0.dim() == 4
+    if W0.shape != ((B, H, d, d) if per_batch else (H, d, d)) or eta.shape != (H,):
+        raise ValueError("W0 must be [H,d,d] or [B,H,d,d] and eta [H]")
+    if Y is None:
+        Y = torch.empty_like(Q)
+    if W_out is None:
+        W_out = torch.empty((B, H, d, d), device=dev, dtype=torch.float32)
+    _need(Y, "Y", dev, Q.dtype)
+    _need(W_out, "W_out", dev, torch.float32)
+    _check(lib.ttt_linear_forward(Q.data_ptr(), K.data_ptr(), V.data_ptr(), _dtype_code(Q),
+                                  W0.data_ptr(), int(per_batch), eta.data_ptr(),
+                                  B, H, T, d, int(b), Y.data_ptr(), W_out.data_ptr(),
+                                  _stream_handle(dev, stream)))
+    return Y, W_out
+
+
+def ttt_mlp_forward(Q, K, V, W1, W2, eta, b: int, Y=None, W1_out=None, W2_out=None,
+                    stream=None):
+    """TTT-MLP dual-form forward, f(z) = SiLU(z W1) W2.  W1 fp32 [H,d,m] or
+    [B,H,d,m]; W2 fp32 [H,m,d] or [B,H,m,d].  Returns (Y, W1_out, W2_out)."""
+    lib = load_library()
+    if Q.dim() != 4:
+        raise ValueError("Q must be [B,H,T,d]")
+    dev = Q.device
+    B, H, T, d = Q.shape
+    for t, n in ((Q, "Q"), (K, "K"), (V, "V")):
+        _need(t, n, dev, Q.dtype)
+        if t.shape != Q.shape:
+            raise ValueError(f"{n} shape {tuple(t.shape)} != Q shape {tuple(Q.shape)}")
+    _need(W1, "W1", dev, torch.float32)
+    _need(W2, "W2", dev, torch.float32)
+    _need(eta, "eta", dev, torch.float32)
+    per_batch = W1.dim() == 4
+    m = W1.shape[-1]
+    lead = (B, H) if per_batch else (H,)
+    if W1.shape != lead + (d, m) or W2.shape != lead + (m, d) or eta.shape != (H,):
+        raise ValueError("W1 must be [H,d,m] / [B,H,d,m], W2 [H,m,d] / [B,H,m,d], eta [H]")
+    if Y is None:
+        Y = torch.empty_like(Q)
+    if W1_out is None:
+        W1_out = torch.empty((B, H, d, m), device=dev, dtype=torch.float32)
+    if W2_out is None:
+        W2_out = torch.empty((B, H, m, d), device=dev, dtype=torch.float32)
+    _need(Y, "Y", dev, Q.dtype)
+    _need(W1_out, "W1_out", dev, torch.float32)
+    _need(W2_out, "W2_out", dev, torch.float32)
+    _check(lib.ttt_mlp_forward(Q.data_ptr(), K.data_ptr(), V.data_ptr(), _dtype_code(Q),
+                               W1.data_ptr(), W2.data_ptr(), int(per_batch), eta.data_ptr(),
+                               B, H, T, d, m, int(b), Y.data_ptr(), W1_out.data_ptr(),
+                               W2_out.data_ptr(), _stream_handle(dev, stream)))
+    return Y, W1_out, W2_out
+
+
+def ttt_linear_decode_step(q, k, v, W, eta, y=None, stream=None):
+    """One TTT-Linear token step: q,k,v [B,H,d] fp32/bf16; W fp32 [B,H,d,d]
+    updated in place; eta fp32 [H].  Returns y [B,H,d] in q's dtype."""
+    lib = load_library()
+    if q.dim() != 3:
+        raise ValueError("q must be [B,H,d]")
+    dev = q.device
+    B, H, d = q.shape
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, dev, q.dtype)
+        if t.shape != q.shape:
+            raise ValueError(f"{n} shape {tuple(t.shape)} != q shape {tuple(q.shape)}")
+    _need(W, "W", dev, torch.float32)
+    _need(eta, "eta", dev, torch.float32)
+    if W.shape != (B, H, d, d) or eta.shape != (H,):
+        raise ValueError("W must be [B,H,d,d] and eta [H]")
+    if y is None:
+        y = torch.empty_like(q)
+    _need(y, "y", dev, q.dtype)
+    _check(lib.ttt_linear_decode_step(q.data_ptr(), k.data_ptr(), v.data_ptr(), _dtype_code(q),
+                                      W.data_ptr(), eta.data_ptr(), B, H, d, y.data_ptr(),
+                                      _stream_handle(dev, stream)))
+    return y
+
+
+__all__ = [
+    "ttt_linear_forward", "ttt_mlp_forward", "ttt_linear_decode_step", "load_library",
+    "status_string", "TTTError", "LIB_PATH", "TTT_F32", "TTT_BF16",
+]

@@ -1,0 +1,171 @@
+// ttt_capi.hip -- the C ABI declared in include/ttt.h: argument validation,
+// kernel selection and launch on the caller's stream.  Validation happens
+// before any HIP call, so every error path is reachable without a GPU.
+#include "ttt.h"
+#include "ttt_internal.h"
+
+#include <stdint.h>
+
+namespace {
+
+using ttt::LinearArgs;
+using ttt::MlpArgs;
+using ttt::DecodeArgs;
+
+constexpr int kAbiVersion = (1 << 16) | 0;
+
+bool valid_dtype(int dt) { return dt == TTT_F32 || dt == TTT_BF16; }
+size_t elem_bytes(int dt) { return dt == TTT_F32 ? 4 : 2; }
+
+// a*b*c*... with overflow detection (all factors >= 0)
+bool mul_ok(int64_t& acc, int64_t x)
+{
+    int64_t r;
+    if (__builtin_mul_overflow(acc, x, &r)) return false;
+    acc = r;
+    return true;
+}
+
+struct Range {
+    const void* p;
+    int64_t bytes;
+};
+
+bool overlap(const Range& a, const Range& b)
+{
+    if (!a.p || !b.p || a.bytes <= 0 || b.bytes <= 0) return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+    return a0 < b0 + static_cast<uintptr_t>(b.bytes) && b0 < a0 + static_cast<uintptr_t>(a.bytes);
+}
+
+bool d_supported(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+
+// largest grid.x the launchers use
+constexpr int64_t kMaxUnits = 0x7fffffff;
+
+int hip_status(hipError_t e) { return e == hipSuccess ? TTT_OK : TTT_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int ttt_abi_version(void) { return kAbiVersion; }
+
+const char* ttt_status_string(int status)
+{
+    switch (status) {
+    case TTT_OK: return "ok";
+    case TTT_ERR_INVALID_ARG: return "invalid argument (null pointer, negative size, b < 1, bad flag or overlapping buffers)";
+    case TTT_ERR_UNSUPPORTED: return "unsupported shape or dtype (d, m, b, dtype, or on-chip memory the shape needs)";
+    case TTT_ERR_HIP: return "a HIP call or kernel launch failed";
+    default: return "unknown status";
+    }
+}
+
+int ttt_linear_forward(const void* Q, const void* K, const void* V, int qkv_dtype,
+                       const float* W0, int w0_per_batch, const float* eta,
+                       int64_t B, int64_t H, int64_t T, int d, int b,
+                       void* Y, float* W_out, void* stream)
+{
+    if (B < 0 || H < 0 || T < 0 || b < 1 || (w0_per_batch != 0 && w0_per_batch != 1))
+        return TTT_ERR_INVALID_ARG;
+    if (!valid_dtype(qkv_dtype) || !d_supported(d) || b > 64)
+        return TTT_ERR_UNSUPPORTED;
+    int64_t units = B;
+    if (!mul_ok(units, H) || units > kMaxUnits) return TTT_ERR_UNSUPPORTED;
+    if (units == 0) return TTT_OK;
+    int64_t n_qkv = units;
+    if (!mul_ok(n_qkv, T) || !mul_ok(n_qkv, d) || !mul_ok(n_qkv, 4)) return TTT_ERR_UNSUPPORTED;
+    n_qkv = n_qkv / 4 * static_cast<int64_t>(elem_bytes(qkv_dtype));
+    const int64_t n_state = static_cast<int64_t>(d) * d * 4;
+    if (!W0 || !eta || !W_out) return TTT_ERR_INVALID_ARG;
+    if (T > 0 && (!Q || !K || !V || !Y)) return TTT_ERR_INVALID_ARG;
+
+    const Range rQ{Q, T ? n_qkv : 0}, rK{K, T ? n_qkv : 0}, rV{V, T ? n_qkv : 0};
+    const Range rY{Y, T ? n_qkv : 0};
+    const Range rW0{W0, (w0_per_batch ? units : H) * n_state};
+    const Range rWo{W_out, units * n_state}, rEta{eta, H * 4};
+    for (const Range& in : {rQ, rK, rV, rW0, rEta, rWo})
+        if (overlap(rY, in)) return TTT_ERR_INVALID_ARG;
+    for (const Range& in : {rQ, rK, rV, rEta})
+        if (overlap(rWo, in)) return TTT_ERR_INVALID_ARG;
+    if (overlap(rWo, rW0) && !(w0_per_batch && static_cast<const void*>(W_out) == W0))
+        return TTT_ERR_INVALID_ARG;
+
+    LinearArgs a{Q, K, V, qkv_dtype, W0, w0_per_batch, eta, B, H, T, d, b,
+                 Y, W_out, static_cast<hipStream_t>(stream)};
+    if (ttt::linear_mfma_supports(a))
+        return hip_status(ttt::launch_linear_mfma(a));
+    if (ttt::linear_generic_lds_bytes(d, b) > static_cast<size_t>(ttt::kMaxLdsBytes))
+        return TTT_ERR_UNSUPPORTED;
+    return hip_status(ttt::launch_linear_generic(a));
+}
+
+int ttt_mlp_forward(const void* Q, const void* K, const void* V, int qkv_dtype,
+                    const float* W1_0, const float* W2_0, int w0_per_batch,
+                    const float* eta, int64_t B, int64_t H, int64_t T, int d, int m, int b,
+                    void* Y, float* W1_out, float* W2_out, void* stream)
+{
+    if (B < 0 || H < 0 || T < 0 || b < 1 || m < 1 || (w0_per_batch != 0 && w0_per_batch != 1))
+        return TTT_ERR_INVALID_ARG;
+    if (!valid_dtype(qkv_dtype) || !(d == 16 || d == 32 || d == 64) || b > 64 ||
+        m % 16 != 0 || m > 512)
+        return TTT_ERR_UNSUPPORTED;
+    int64_t units = B;
+    if (!mul_ok(units, H) || units > kMaxUnits) return TTT_ERR_UNSUPPORTED;
+    if (units == 0) return TTT_OK;
+    int64_t n_qkv = units;
+    if (!mul_ok(n_qkv, T) || !mul_ok(n_qkv, d) || !mul_ok(n_qkv, 4)) return TTT_ERR_UNSUPPORTED;
+    n_qkv = n_qkv / 4 * static_cast<int64_t>(elem_bytes(qkv_dtype));
+    const int64_t n_state = static_cast<int64_t>(d) * m * 4;
+    if (!W1_0 || !W2_0 || !eta || !W1_out || !W2_out) return TTT_ERR_INVALID_ARG;
+    if (T > 0 && (!Q || !K || !V || !Y)) return TTT_ERR_INVALID_ARG;
+
+    const int64_t n_src = (w0_per_batch ? units : H) * n_state;
+    const Range rQ{Q, T ? n_qkv : 0}, rK{K, T ? n_qkv : 0}, rV{V, T ? n_qkv : 0};
+    const Range rY{Y, T ? n_qkv : 0};
+    const Range rW1{W1_0, n_src}, rW2{W2_0, n_src};
+    const Range rW1o{W1_out, units * n_state}, rW2o{W2_out, units * n_state};
+    const Range rEta{eta, H * 4};
+    for (const Range& in : {rQ, rK, rV, rW1, rW2, rEta, rW1o, rW2o})
+        if (overlap(rY, in)) return TTT_ERR_INVALID_ARG;
+    for (const Range& in : {rQ, rK, rV, rEta, rW2, rW2o})
+        if (overlap(rW1o, in)) return TTT_ERR_INVALID_ARG;
+    for (const Range& in : {rQ, rK, rV, rEta, rW1})
+        if (overlap(rW2o, in)) return TTT_ERR_INVALID_ARG;
+    if (overlap(rW1o, rW1) && !(w0_per_batch && static_cast<const void*>(W1_out) == W1_0))
+        return TTT_ERR_INVALID_ARG;
+    if (overlap(rW2o, rW2) && !(w0_per_batch && static_cast<const void*>(W2_out) == W2_0))
+        return TTT_ERR_INVALID_ARG;
+
+    MlpArgs a{Q, K, V, qkv_dtype, W1_0, W2_0, w0_per_batch, eta, B, H, T, d, m, b,
+              Y, W1_out, W2_out, static_cast<hipStream_t>(stream)};
+    if (ttt::mlp_mfma_supports(a))
+        return hip_status(ttt::launch_mlp_mfma(a));
+    if (ttt::mlp_generic_lds_bytes(d, m, b) > static_cast<size_t>(ttt::kMaxLdsBytes))
+        return TTT_ERR_UNSUPPORTED;
+    return hip_status(ttt::launch_mlp_generic(a));
+}
+
+int ttt_linear_decode_step(const void* q, const void* k, const void* v, int qkv_dtype,
+                           float* W, const float* eta, int64_t B, int64_t H, int d,
+                           void* y, void* stream)
+{
+    if (B < 0 || H < 0) return TTT_ERR_INVALID_ARG;
+    if (!valid_dtype(qkv_dtype) || !d_supported(d)) return TTT_ERR_UNSUPPORTED;
+    int64_t units = B;
+    if (!mul_ok(units, H) || units > kMaxUnits) return TTT_ERR_UNSUPPORTED;
+    if (units == 0) return TTT_OK;
+    if (!q || !k || !v || !W || !eta || !y) return TTT_ERR_INVALID_ARG;
+    const int64_t n_vec = units * d * static_cast<int64_t>(elem_bytes(qkv_dtype));
+    const Range rq{q, n_vec}, rk{k, n_vec}, rv{v, n_vec}, ry{y, n_vec};
+    const Range rW{W, units * d * d * 4}, rEta{eta, H * 4};
+    for (const Range& in : {rq, rk, rv, rW, rEta})
+        if (overlap(ry, in)) return TTT_ERR_INVALID_ARG;
+    for (const Range& in : {rq, rk, rv, rEta})
+        if (overlap(rW, in)) return TTT_ERR_INVALID_ARG;
+    DecodeArgs a{q, k, v, qkv_dtype, W, eta, B, H, d, y, static_cast<hipStream_t>(stream)};
+    return hip_status(ttt::launch_decode(a));
+}
+
+}  // extern "C"

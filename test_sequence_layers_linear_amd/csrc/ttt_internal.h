@@ -1,0 +1,74 @@
+// ttt_internal.h -- declarations shared by the kernels and the C-ABI layer of
+// libttt.so.  Not part of the public ABI (that is include/ttt.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ttt {
+
+// Maximum LDS one workgroup may use on gfx950.
+constexpr int kMaxLdsBytes = 160 * 1024;
+
+// ---------------------------------------------------------------------------
+// element access: Q/K/V/Y are fp32 or bf16 (stored as raw 16-bit patterns)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float load_elem(const float* p, int64_t i) { return p[i]; }
+__device__ __forceinline__ float load_elem(const uint16_t* p, int64_t i)
+{
+    return __uint_as_float(static_cast<uint32_t>(p[i]) << 16);
+}
+__device__ __forceinline__ void store_elem(float* p, int64_t i, float x) { p[i] = x; }
+// fp32 -> bf16, round to nearest even (lowers to v_cvt_pk_bf16_f32 on gfx950)
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float x)
+{
+    __bf16 h = static_cast<__bf16>(x);
+    return __builtin_bit_cast(uint16_t, h);
+}
+__device__ __forceinline__ void store_elem(uint16_t* p, int64_t i, float x)
+{
+    p[i] = f32_to_bf16_bits(x);
+}
+
+__device__ __forceinline__ float silu_f(float x) { return x / (1.0f + __expf(-x)); }
+
+// ---------------------------------------------------------------------------
+// launchers (each returns hipSuccess or the launch error)
+// ---------------------------------------------------------------------------
+struct LinearArgs {
+    const void* Q; const void* K; const void* V; int dtype;
+    const float* W0; int w0_per_batch; const float* eta;
+    int64_t B, H, T; int d, b;
+    void* Y; float* W_out; hipStream_t stream;
+};
+
+struct MlpArgs {
+    const void* Q; const void* K; const void* V; int dtype;
+    const float* W1_0; const float* W2_0; int w0_per_batch; const float* eta;
+    int64_t B, H, T; int d, m, b;
+    void* Y; float* W1_out; float* W2_out; hipStream_t stream;
+};
+
+struct DecodeArgs {
+    const void* q; const void* k; const void* v; int dtype;
+    float* W; const float* eta; int64_t B, H; int d;
+    void* y; hipStream_t stream;
+};
+
+// Generic kernels: any supported d and b, fp32 arithmetic, state in LDS
+// (linear) or in the output buffers (MLP).  LDS bytes they need:
+size_t linear_generic_lds_bytes(int d, int b);
+size_t mlp_generic_lds_bytes(int d, int m, int b);
+hipError_t launch_linear_generic(const LinearArgs& a);
+hipError_t launch_mlp_generic(const MlpArgs& a);
+
+// MFMA kernels for the d = 64, b = 16 (and m = 256) shapes with bf16 inputs.
+bool linear_mfma_supports(const LinearArgs& a);
+hipError_t launch_linear_mfma(const LinearArgs& a);
+bool mlp_mfma_supports(const MlpArgs& a);
+hipError_t launch_mlp_mfma(const MlpArgs& a);
+
+// Decode step.
+hipError_t launch_decode(const DecodeArgs& a);
+
+}  // namespace ttt

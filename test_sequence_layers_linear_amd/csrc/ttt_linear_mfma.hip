@@ -1,0 +1,340 @@
+// ttt_linear_mfma.hip -- TTT-Linear dual-form scan on MFMA for bf16 Q/K/V,
+// head dim d = 64, mini-batch b = 16, fp32 fast weights.
+//
+// Per chunk of 16 tokens (W = chunk-start weights, row-vector form z W):
+//     E' = eta (V - K W)                 (= -eta E, the scaled residual)
+//     Y  = Q W + tril(Q K^T) E'          (= Q W - eta tril(Q K^T) E)
+//     W  = W + K^T E'                    (= W - eta K^T E)
+// the dual form of mini-batch gradient descent ("Test-Time Training Layers:
+// How Inner-Loop Gradient Descent Replaces the Transformer KV Cache ...",
+// section "Hardware Parallelization: The Dual Form and Mini-Batch GPU
+// Acceleration"; the dual-form paragraph of the ren-xubin.github.io essay).
+//
+// Work split.  One workgroup (4 waves) per (batch, head) chain.  The loss
+// 1/2 sum_j (k . W[:, j] - v_j)^2 separates over output columns j, so wave w
+// owns the 16 columns [16w, 16w + 16) of W outright and no partial result
+// ever moves between waves; the waves share only the staged inputs.
+//
+// Register dataflow (16x16 MFMA layouts; lane l, c = l % 16, g = l / 16):
+//   C/D tile    : lane holds rows 4g..4g+3 of column c.
+//   A operand   : lane holds row c, k-slots of group g.
+//   B operand   : lane holds column c, k-slots of group g.
+// The W slice is kept as the fp32 accumulator of the update MFMA, four 16-row
+// tiles mt = 0..3.  Row m of tile mt is input index i = rho(mt, m) with
+//     rho(mt, m) = 32 (mt / 2) + 8 (m / 4) + 4 (mt % 2) + m % 4,
+// chosen so that the accumulator registers of tiles 2s and 2s+1, rounded to
+// bf16, ARE the B operand of a 16x16x32 product over i in [32s, 32s + 32)
+// with k-slot (g, e) <-> i = 32s + 8g + e: one contiguous 16-byte segment of
+// a K or Q row per lane.  So
+//   R    = K W_J - V    : A = K rows, B = W registers; V enters transposed
+//                         through a product of its row tile with -I
+//   Y^T  = W_J^T Q^T + E'^T S^T : A = the same W registers, B = Q rows
+//   S^T  = K Q^T        : lands in exactly the B layout of E'^T S^T
+//   E'   = -eta R (C layout) is at once the B operand of the update and the
+//        A operand of E'^T S^T
+//   W   += K^T E'       : A = K^T, read from a transposed copy in LDS
+// Y^T comes out with 4 consecutive columns of one token per lane (one 8-byte
+// store).  Only R -> E' -> update -> bf16(W) is a dependent chain per chunk.
+//
+// Memory.  Q, K, V stream from HBM exactly once per chain.  A stage is two
+// chunks (32 tokens); for each stage wave w loads rows [8w, 8w + 8) of the
+// stage's K, Q and V with fully coalesced 16-byte-per-lane buffer loads (one
+// 1 KB row block per instruction) into registers, and later writes them to
+// one slot of a 3-slot LDS ring: K, Q, V row-major with the 16-byte segments
+// of row r XOR-swizzled by r % 8 (conflict-free operand reads), plus K^T with
+// a padded 40-byte row (conflict-free 8-byte reads of 4 tokens of one input
+// index).  Loads run 6 to 12 stages ahead in two fixed register sets, A and
+// B (while one set is consumed the other is in flight), so the compiler can
+// wait on exactly the set it needs.  One barrier per stage: at stage s every
+// wave writes stage s + 1 into slot (s + 1) % 3, meets the barrier, then
+// computes stage s from slot s % 3; the slot being written was last read at
+// stage s - 2, before the previous barrier.  Per-chain buffer resources are
+// sized to the chain's T tokens, so rows past the end read as zero (an
+// all-zero chunk leaves W unchanged) and stores past the end are dropped:
+// there are no tail branches.
+#include "ttt_internal.h"
+
+namespace ttt {
+namespace {
+
+constexpr int kD = 64;
+constexpr int kB = 16;
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kStageChunks = 2;
+constexpr int kStageTokens = kB * kStageChunks;
+constexpr int kSet = 6;                 // stages per register set (two sets)
+constexpr int kSlots = 3;               // LDS ring slots (kSet * 2 % kSlots == 0)
+// word 3 of a raw buffer resource on gfx9-family GPUs (32-bit data format)
+constexpr int kBufferDword3 = 0x00020000;
+
+// LDS layout of one chunk inside a stage slot (bytes)
+constexpr int kRowBytes = kD * 2;                    // 128
+constexpr int kOffK = 0;
+constexpr int kOffQ = kOffK + kB * kRowBytes;        // 2048
+constexpr int kOffV = kOffQ + kB * kRowBytes;        // 4096
+constexpr int kOffKt = kOffV + kB * kRowBytes;       // 6144
+constexpr int kKtRow = 40;                           // 16 tokens * 2 B + 8 B pad
+constexpr int kChunkBytes = kOffKt + kD * kKtRow;    // 8704
+constexpr int kSlotBytes = kChunkBytes * kStageChunks;
+constexpr int kLdsBytes = kSlotBytes * kSlots;       // 52224
+
+static_assert((2 * kSet) % kSlots == 0, "slot index must be static inside the loop");
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma16(bf16x4 a, bf16x4 b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a),
+                                                     __builtin_bit_cast(i16x4, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 pack8(f32x4 lo, f32x4 hi)
+{
+    bf16x8 r;
+    r[0] = static_cast<__bf16>(lo[0]); r[1] = static_cast<__bf16>(lo[1]);
+    r[2] = static_cast<__bf16>(lo[2]); r[3] = static_cast<__bf16>(lo[3]);
+    r[4] = static_cast<__bf16>(hi[0]); r[5] = static_cast<__bf16>(hi[1]);
+    r[6] = static_cast<__bf16>(hi[2]); r[7] = static_cast<__bf16>(hi[3]);
+    return r;
+}
+
+__device__ __forceinline__ bf16x4 pack4(f32x4 x)
+{
+    bf16x4 r;
+    r[0] = static_cast<__bf16>(x[0]); r[1] = static_cast<__bf16>(x[1]);
+    r[2] = static_cast<__bf16>(x[2]); r[3] = static_cast<__bf16>(x[3]);
+    return r;
+}
+
+__device__ __forceinline__ int rho(int mt, int m)
+{
+    return 32 * (mt >> 1) + 8 * (m >> 2) + 4 * (mt & 1) + (m & 3);
+}
+
+// byte offset of 16-byte segment `seg` of row `r` in a swizzled row-major tile
+__device__ __forceinline__ int swz(int r, int seg) { return r * kRowBytes + ((seg ^ (r & 7)) << 4); }
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t chain_rsrc(const void* base, int64_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0,
+                                             static_cast<int>(bytes), kBufferDword3);
+}
+
+// One wave's share of one stage: rows [8w, 8w + 8) of the stage's K, Q, V;
+// lane l holds row 8w + l / 8, 16-byte segment l % 8.
+struct StageRegs {
+    u32x4 k, q, v;
+};
+
+__global__ void __launch_bounds__(kThreads, 1)
+linear_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                   const uint16_t* __restrict__ V, const float* W0, int w0_per_batch,
+                   const float* __restrict__ eta, int H, int T,
+                   uint16_t* __restrict__ Y, float* W_out)
+{
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+
+    const int lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
+    const int c = lane & 15;
+    const int g = lane >> 4;
+    const int col = 16 * w + c;          // this lane's column of W
+
+    const int64_t u = blockIdx.x;
+    const int h = static_cast<int>(u % H);
+    const float et = eta[h];
+    const float* w0 = W0 + (w0_per_batch ? u : h) * kD * kD;
+
+    // fast weights: Wacc[mt][r] = W[rho(mt, 4g + r)][col]
+    f32x4 Wacc[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            Wacc[mt][r] = w0[rho(mt, 4 * g + r) * kD + col];
+
+    // -I as the B operand of a 16x16x16 product: B[k = 4g + r][n = c] = -(k == n)
+    bf16x4 neg_eye;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+        neg_eye[r] = static_cast<__bf16>(4 * g + r == c ? -1.0f : 0.0f);
+
+    const int64_t base = u * static_cast<int64_t>(T) * kD;
+    const int64_t chain_bytes = static_cast<int64_t>(T) * kD * 2;
+    const __amdgpu_buffer_rsrc_t rq = chain_rsrc(Q + base, chain_bytes);
+    const __amdgpu_buffer_rsrc_t rk = chain_rsrc(K + base, chain_bytes);
+    const __amdgpu_buffer_rsrc_t rv = chain_rsrc(V + base, chain_bytes);
+    const __amdgpu_buffer_rsrc_t ry = chain_rsrc(Y + base, chain_bytes);
+
+    const int nstages = (T + kStageTokens - 1) / kStageTokens;
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+
+    // staging: this lane's row inside the stage and its 16-byte segment
+    const int st_row = 8 * w + (lane >> 3);             // 0..31
+    const int st_seg = lane & 7;
+    auto load_stage = [&](StageRegs& o, int stage) {
+        const int off = (stage * kStageTokens + st_row) * kRowBytes + st_seg * 16;
+        o.k = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
+        o.q = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0);
+        o.v = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0);
+    };
+    auto write_stage = [&](const StageRegs& o, int slot) {
+        unsigned char* chunk = lds + slot * kSlotBytes + (st_row >> 4) * kChunkBytes;
+        const int r = st_row & 15;
+        *reinterpret_cast<u32x4*>(chunk + kOffK + swz(r, st_seg)) = o.k;
+        *reinterpret_cast<u32x4*>(chunk + kOffQ + swz(r, st_seg)) = o.q;
+        *reinterpret_cast<u32x4*>(chunk + kOffV + swz(r, st_seg)) = o.v;
+        // K^T[i][t] for the 8 input indices of this segment
+        const bf16x8 kv = __builtin_bit_cast(bf16x8, o.k);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            *reinterpret_cast<__bf16*>(chunk + kOffKt + (8 * st_seg + e) * kKtRow + 2 * r) = kv[e];
+    };
+
+    // Operands of one chunk, read from its LDS tile.
+    struct ChunkOps {
+        bf16x8 ka0, ka1, qa0, qa1;
+        bf16x4 vrow;
+        bf16x4 kt[4];
+    };
+    auto read_ops = [&](ChunkOps& o, const unsigned char* tile) {
+        o.ka0 = *reinterpret_cast<const bf16x8*>(tile + kOffK + swz(c, g));
+        o.ka1 = *reinterpret_cast<const bf16x8*>(tile + kOffK + swz(c, 4 + g));
+        o.qa0 = *reinterpret_cast<const bf16x8*>(tile + kOffQ + swz(c, g));
+        o.qa1 = *reinterpret_cast<const bf16x8*>(tile + kOffQ + swz(c, 4 + g));
+        o.vrow = *reinterpret_cast<const bf16x4*>(tile + kOffV + swz(c, 2 * w + (g >> 1)) + 8 * (g & 1));
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+            o.kt[mt] = *reinterpret_cast<const bf16x4*>(tile + kOffKt + rho(mt, c) * kKtRow + 8 * g);
+    };
+
+    // One chunk of the scan, tokens t0 onwards.
+    auto step = [&](const ChunkOps& o, int t0) {
+        const bf16x8 bw0 = pack8(Wacc[0], Wacc[1]);
+        const bf16x8 bw1 = pack8(Wacc[2], Wacc[3]);
+
+        // R = K W_J - V (C layout: rows t = 4g + r, column col)
+        f32x4 R = mfma16(o.vrow, neg_eye, zero);
+        R = mfma32(o.ka0, bw0, R);
+        R = mfma32(o.ka1, bw1, R);
+
+        // off the chain: S^T = K Q^T, Y^T partial = W_J^T Q^T
+        f32x4 St = mfma32(o.ka0, o.qa0, zero);
+        St = mfma32(o.ka1, o.qa1, St);
+        f32x4 Yt = mfma32(bw0, o.qa0, zero);
+        Yt = mfma32(bw1, o.qa1, Yt);
+
+        // E' = eta (V - K W) = -eta R
+        const bf16x4 eb = pack4(-et * R);
+
+        // W += K^T E'
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+            Wacc[mt] = mfma16(o.kt[mt], eb, Wacc[mt]);
+
+        // S^T masked: lane (c = t, g) holds S[t][t' = 4g + r]; keep t' <= t
+        f32x4 Sm;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            Sm[r] = (4 * g + r <= c) ? St[r] : 0.f;
+        Yt = mfma16(eb, pack4(Sm), Yt);
+
+        // Y[t0 + c][16w + 4g .. +3]; rows past T fall outside the buffer.
+        // The store consumes the last MFMA of the chunk, so every MFMA of
+        // the chunk has read its operands before the wave goes on.
+        const bf16x4 yb = pack4(Yt);
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, yb), ry,
+                                              ((t0 + c) * kD + 16 * w + 4 * g) * 2, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // Stage s: publish stage s + 1 (held in `next`), then compute stage s.
+    // All LDS operand reads of the stage complete before its first MFMA: an
+    // LDS read returning into a register that an MFMA issued earlier has not
+    // read yet corrupts that MFMA's operand, so reads and products are kept
+    // in separate phases (the scheduling barriers stop the compiler from
+    // interleaving them).
+    auto process = [&](const StageRegs& next, int s, int slot) {
+        write_stage(next, (slot + 1) % kSlots);
+        __syncthreads();
+        const unsigned char* sl = lds + slot * kSlotBytes;
+        ChunkOps o0, o1;
+        read_ops(o0, sl);
+        read_ops(o1, sl + kChunkBytes);
+        __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): all operands in registers
+        __builtin_amdgcn_sched_barrier(0);
+        step(o0, s * kStageTokens);
+        step(o1, s * kStageTokens + kB);
+    };
+
+    if (nstages > 0) {
+        StageRegs setA[kSet], setB[kSet];
+        {
+            StageRegs first;
+            load_stage(first, 0);
+            write_stage(first, 0);
+        }
+#pragma unroll
+        for (int p = 0; p < kSet; ++p)
+            load_stage(setA[p], 1 + p);
+        // stages s0 .. s0 + 2 kSet - 1 per iteration; setA holds s0 + 1 .. s0 + kSet
+        for (int s0 = 0; s0 < nstages; s0 += 2 * kSet) {
+#pragma unroll
+            for (int p = 0; p < kSet; ++p)
+                load_stage(setB[p], s0 + kSet + 1 + p);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int p = 0; p < kSet; ++p)
+                process(setA[p], s0 + p, p % kSlots);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int p = 0; p < kSet; ++p)
+                load_stage(setA[p], s0 + 2 * kSet + 1 + p);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int p = 0; p < kSet; ++p)
+                process(setB[p], s0 + kSet + p, (kSet + p) % kSlots);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+
+    float* wo = W_out + u * kD * kD;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            wo[rho(mt, 4 * g + r) * kD + col] = Wacc[mt][r];
+}
+
+}  // namespace
+
+bool linear_mfma_supports(const LinearArgs& a)
+{
+    // per-chain byte offsets, including the loads past the end, are 32-bit
+    const int64_t max_tokens = (int64_t{1} << 31) / (kD * 2) - kStageTokens * (3 * kSet + 2);
+    return a.dtype == 1 && a.d == kD && a.b == kB && a.T <= max_tokens;
+}
+
+hipError_t launch_linear_mfma(const LinearArgs& a)
+{
+    const dim3 grid(static_cast<unsigned>(a.B * a.H)), block(kThreads);
+    hipLaunchKernelGGL(linear_mfma_kernel, grid, block, kLdsBytes, a.stream,
+                       static_cast<const uint16_t*>(a.Q), static_cast<const uint16_t*>(a.K),
+                       static_cast<const uint16_t*>(a.V), a.W0, a.w0_per_batch, a.eta,
+                       static_cast<int>(a.H), static_cast<int>(a.T),
+                       static_cast<uint16_t*>(a.Y), a.W_out);
+    return hipGetLastError();
+}
+
+}  // namespace ttt

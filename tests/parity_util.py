@@ -1,0 +1,73 @@
+"""Helpers shared by the GPU parity tests (comparison only, no method arithmetic)."""
+import numpy as np
+import torch
+
+import oracle
+import test_sequence_layers_linear_amd as ttt
+from test_sequence_layers_linear_amd.inputs import CONFIGS, Workload, default_seed, make_inputs
+
+# relative-L2 bounds: fp32 inputs 1e-4, bf16 inputs with fp32 state 2e-2
+TOL = {"fp32": 1e-4, "bf16": 2e-2}
+
+
+def rel_l2(x, ref) -> float:
+    x = np.asarray(x.detach().to("cpu", torch.float64).numpy() if isinstance(x, torch.Tensor) else x,
+                   dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert x.shape == ref.shape, (x.shape, ref.shape)
+    n = np.linalg.norm(ref)
+    return float(np.linalg.norm(x - ref) / (n if n > 0 else 1.0))
+
+
+def to_gpu(inp: dict) -> dict:
+    return {k: v.cuda() for k, v in inp.items()}
+
+
+def select_chains(inp: dict, chains, per_batch=False) -> dict:
+    """Inputs restricted to a list of (batch, head) chains, stacked as B=1, H=len."""
+    out = {}
+    for k in ("Q", "K", "V"):
+        out[k] = torch.stack([inp[k][b, h] for b, h in chains])[None]
+    out["eta"] = torch.stack([inp["eta"][h] for _, h in chains])
+    for k in ("W0", "W1", "W2"):
+        if k in inp:
+            src = inp[k]
+            out[k] = torch.stack([src[b, h] if src.dim() == 4 else src[h] for b, h in chains])
+    return out
+
+
+def linear_oracle(inp: dict, b: int):
+    return oracle.linear_forward(inp["Q"], inp["K"], inp["V"], inp["W0"], inp["eta"], b)
+
+
+def mlp_oracle(inp: dict, b: int):
+    return oracle.mlp_forward(inp["Q"], inp["K"], inp["V"], inp["W1"], inp["W2"], inp["eta"], b)
+
+
+def linear_gpu(inp_gpu: dict, b: int):
+    Y, W = ttt.ttt_linear_forward(inp_gpu["Q"], inp_gpu["K"], inp_gpu["V"], inp_gpu["W0"],
+                                  inp_gpu["eta"], b)
+    torch.cuda.synchronize()
+    return Y, W
+
+
+def mlp_gpu(inp_gpu: dict, b: int):
+    out = ttt.ttt_mlp_forward(inp_gpu["Q"], inp_gpu["K"], inp_gpu["V"], inp_gpu["W1"],
+                              inp_gpu["W2"], inp_gpu["eta"], b)
+    torch.cuda.synchronize()
+    return out
+
+
+def sample_chains(B: int, H: int, n: int, seed: int):
+    rng = np.random.default_rng(seed)
+    idx = rng.choice(B * H, size=min(n, B * H), replace=False)
+    return [(int(i) // H, int(i) % H) for i in sorted(idx)]
+
+
+def announce(*parts):
+    print("[case]", *parts, flush=True)
+
+
+__all__ = ["TOL", "rel_l2", "to_gpu", "select_chains", "linear_oracle", "mlp_oracle",
+           "linear_gpu", "mlp_gpu", "sample_chains", "announce", "CONFIGS", "Workload",
+           "default_seed", "make_inputs"]

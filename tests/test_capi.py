@@ -1,0 +1,117 @@
+"""The C ABI of libttt.so, checked without a GPU.
+
+The library must load and export every function include/ttt.h declares, and
+every argument error must come back as its status code before any HIP call
+is made (so these run on a machine with no GPU).  Fake, never-dereferenced
+addresses stand in for device buffers.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import test_sequence_layers_linear_amd as ttt
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ttt.h")
+
+OK, INVALID, UNSUPPORTED = ttt.TTT_OK, ttt.TTT_ERR_INVALID_ARG, ttt.TTT_ERR_UNSUPPORTED
+
+# fake device addresses, far apart so only deliberate overlaps overlap
+QA, KA, VA, W0A, ETA, YA, WOA = (0x10_0000_0000 * (i + 1) for i in range(7))
+W1A, W2A, W1O, W2O = (0x90_0000_0000 + 0x10_0000_0000 * i for i in range(4))
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(ttt_\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return ttt.load_library()
+
+
+def test_exports_every_declared_function(lib):
+    names = declared_functions()
+    assert set(names) >= {"ttt_linear_forward", "ttt_mlp_forward", "ttt_linear_decode_step",
+                          "ttt_status_string", "ttt_abi_version"}
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in ttt.h but not exported"
+
+
+def test_status_strings_and_version(lib):
+    for s in (OK, INVALID, UNSUPPORTED, ttt.TTT_ERR_HIP, 12345):
+        assert isinstance(ttt.status_string(s), str) and ttt.status_string(s)
+    assert lib.ttt_abi_version() >> 16 == 1
+
+
+def lin(lib, Q=QA, K=KA, V=VA, dt=1, W0=W0A, pb=0, eta=ETA, B=2, H=3, T=64, d=64, b=16,
+        Y=YA, Wo=WOA):
+    return lib.ttt_linear_forward(Q, K, V, dt, W0, pb, eta, B, H, T, d, b, Y, Wo, None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(B=-1), INVALID), (dict(H=-2), INVALID), (dict(T=-5), INVALID),
+    (dict(b=0), INVALID), (dict(pb=2), INVALID),
+    (dict(Q=None), INVALID), (dict(K=None), INVALID), (dict(V=None), INVALID),
+    (dict(Y=None), INVALID), (dict(W0=None), INVALID), (dict(eta=None), INVALID),
+    (dict(Wo=None), INVALID),
+    (dict(d=48), UNSUPPORTED), (dict(d=256), UNSUPPORTED), (dict(b=65), UNSUPPORTED),
+    (dict(dt=7), UNSUPPORTED), (dict(d=128, b=64, dt=0), UNSUPPORTED),  # > 160 KB of LDS
+    (dict(Y=QA), INVALID), (dict(Y=KA + 64), INVALID), (dict(Y=VA), INVALID),
+    (dict(Y=WOA), INVALID), (dict(Wo=QA), INVALID), (dict(Wo=W0A), INVALID),
+    (dict(Wo=W0A + 4, pb=1), INVALID),
+    (dict(B=0), OK), (dict(H=0), OK),
+])
+def test_linear_validation(lib, kw, expect):
+    assert lin(lib, **kw) == expect
+
+
+def test_linear_no_inputs_needed_when_empty(lib):
+    # B*H == 0: a no-op, even with null pointers
+    assert lib.ttt_linear_forward(None, None, None, 1, None, 0, None, 0, 4, 8, 64, 16,
+                                  None, None, None) == OK
+
+
+def mlp(lib, dt=1, W1=W1A, W2=W2A, pb=0, B=2, H=3, T=64, d=64, m=256, b=16, Y=YA,
+        W1o=W1O, W2o=W2O, Q=QA):
+    return lib.ttt_mlp_forward(Q, KA, VA, dt, W1, W2, pb, ETA, B, H, T, d, m, b, Y, W1o, W2o,
+                               None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(B=-1), INVALID), (dict(b=0), INVALID), (dict(m=0), INVALID),
+    (dict(W1=None), INVALID), (dict(W2o=None), INVALID), (dict(Q=None), INVALID),
+    (dict(d=128), UNSUPPORTED), (dict(m=100), UNSUPPORTED), (dict(m=1024), UNSUPPORTED),
+    (dict(dt=3), UNSUPPORTED), (dict(b=80), UNSUPPORTED),
+    (dict(Y=W1A), INVALID), (dict(W1o=W2O), INVALID), (dict(W1o=W1A), INVALID),
+    (dict(B=0), OK),
+])
+def test_mlp_validation(lib, kw, expect):
+    assert mlp(lib, **kw) == expect
+
+
+def dec(lib, q=QA, W=W0A, y=YA, dt=1, B=2, H=24, d=64):
+    return lib.ttt_linear_decode_step(q, KA, VA, dt, W, ETA, B, H, d, y, None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(B=-1), INVALID), (dict(q=None), INVALID), (dict(W=None), INVALID),
+    (dict(y=None), INVALID), (dict(d=96), UNSUPPORTED), (dict(dt=9), UNSUPPORTED),
+    (dict(y=QA), INVALID), (dict(y=W0A), INVALID), (dict(W=KA), INVALID),
+    (dict(B=0), OK),
+])
+def test_decode_validation(lib, kw, expect):
+    assert dec(lib, **kw) == expect
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 1, 16, 16)
+    with pytest.raises((ValueError, TypeError, RuntimeError)):
+        ttt.ttt_linear_forward(x, x, x, torch.zeros(1, 16, 16), torch.zeros(1), 16,
+                               Y=torch.zeros(1, 1, 16, 16), W_out=torch.zeros(1, 1, 16, 16),
+                               stream=None)

@@ -1,0 +1,78 @@
+"""GPU parity of ttt_linear_decode_step against the fp64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import test_sequence_layers_linear_amd as ttt
+from parity_util import (CONFIGS, TOL, announce, default_seed, linear_gpu, make_inputs, rel_l2,
+                         sample_chains, select_chains, to_gpu)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("d", [16, 32, 64, 128])
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_decode_steps_match_online_gd(d, dtype):
+    """n decode steps from a per-(batch, head) state == the oracle's b = 1 scan."""
+    announce("decode", d, dtype)
+    w = CONFIGS[2].with_(B=2, H=3, T=9, d=d, dtype=dtype, eta=("uniform", 0.01, 0.1))
+    inp = make_inputs(w, 70 + d, w0_per_batch=True)
+    Yr, Wr = oracle.linear_forward(inp["Q"], inp["K"], inp["V"], inp["W0"], inp["eta"], 1)
+    g = to_gpu(inp)
+    W = g["W0"].clone()
+    ys = []
+    for t in range(w.T):
+        ys.append(ttt.ttt_linear_decode_step(g["Q"][:, :, t].contiguous(),
+                                             g["K"][:, :, t].contiguous(),
+                                             g["V"][:, :, t].contiguous(), W, g["eta"]))
+    torch.cuda.synchronize()
+    Y = torch.stack(ys, dim=2)
+    ey, ew = rel_l2(Y, Yr), rel_l2(W, Wr)
+    print(f"  rel-L2 y {ey:.3e}  W {ew:.3e}", flush=True)
+    assert ey <= TOL[dtype] and ew <= TOL[dtype]
+
+
+def test_config4_prefill_then_256_decode_steps():
+    """The long-context workload's tail: forward over T = 32768 tokens, then
+    256 single-token steps from the final W, on sampled chains."""
+    w = CONFIGS[4]
+    announce("decode after config 4 prefill", w.name)
+    inp = make_inputs(w, default_seed(4))
+    g = to_gpu(inp)
+    _, W = linear_gpu(g, w.b)
+    ys = []
+    for s in range(w.decode_steps):
+        ys.append(ttt.ttt_linear_decode_step(g["dq"][s], g["dk"][s], g["dv"][s], W, g["eta"]))
+    torch.cuda.synchronize()
+    y = torch.stack(ys)                           # [steps, B, H, d]
+    chains = sample_chains(w.B, w.H, 2, seed=45)
+    sub = select_chains(inp, chains)
+    _, Wr = oracle.linear_forward(sub["Q"], sub["K"], sub["V"], sub["W0"], sub["eta"], w.b)
+    dq = torch.stack([inp["dq"][:, b, h] for b, h in chains], dim=1)[:, None]
+    dk = torch.stack([inp["dk"][:, b, h] for b, h in chains], dim=1)[:, None]
+    dv = torch.stack([inp["dv"][:, b, h] for b, h in chains], dim=1)[:, None]
+    yr = []
+    for s in range(w.decode_steps):
+        ys_, Wr = oracle.linear_decode(dq[s], dk[s], dv[s], Wr, sub["eta"])
+        yr.append(ys_)
+    yr = np.stack(yr)
+    yg = torch.stack([y[:, b, h] for b, h in chains], dim=1)[:, None]
+    Wg = torch.stack([W[b, h] for b, h in chains])[None]
+    ey, ew = rel_l2(yg, yr), rel_l2(Wg, Wr)
+    print(f"  chains {chains} rel-L2 y {ey:.3e}  W {ew:.3e}", flush=True)
+    assert ey <= TOL["bf16"] and ew <= TOL["bf16"]
+
+
+def test_decode_worked_example_exact():
+    """Token 2 of the hand-derived d = 2 example as one step, embedded in d = 16."""
+    W = torch.zeros(1, 1, 16, 16)
+    W[0, 0, 0, :2] = torch.tensor([0.5, 1.0])
+    q = torch.zeros(1, 1, 16); q[0, 0, :2] = torch.tensor([1.0, 0.0])
+    k = torch.zeros(1, 1, 16); k[0, 0, :2] = torch.tensor([1.0, 1.0])
+    v = torch.zeros(1, 1, 16); v[0, 0, :2] = torch.tensor([3.0, -1.0])
+    W = W.cuda()
+    y = ttt.ttt_linear_decode_step(q.cuda(), k.cuda(), v.cuda(), W, torch.tensor([0.5]).cuda())
+    torch.cuda.synchronize()
+    assert torch.equal(y[0, 0, :2].cpu(), torch.tensor([1.75, 0.0]))
+    assert torch.equal(W[0, 0, :2, :2].cpu(), torch.tensor([[1.75, 0.0], [1.25, -1.0]]))
