@@ -38,6 +38,7 @@ PEAK_FLOPS = {"bf16": 2.5e15, "fp32": 157.3e12}   # dense MFMA
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = {
     "linear_mfma_kernel": "ttt_linear_mfma.hip",
+    "linear_mfma_f32_kernel": "ttt_linear_mfma_f32.hip",
     "linear_generic_kernel": "ttt_generic.hip",
     "mlp_generic_kernel": "ttt_generic.hip",
     "mlp_mfma_kernel": "ttt_mlp_mfma.hip",
@@ -80,8 +81,9 @@ def kernel_name(w):
     if w.kind == "mlp":
         return "mlp_mfma_kernel" if (w.dtype == "bf16" and w.d == 64 and w.m == 256 and w.b == 16) \
             else "mlp_generic_kernel"
-    return "linear_mfma_kernel" if (w.dtype == "bf16" and w.d == 64 and w.b == 16) \
-        else "linear_generic_kernel"
+    if w.d == 64 and w.b == 16:
+        return "linear_mfma_kernel" if w.dtype == "bf16" else "linear_mfma_f32_kernel"
+    return "linear_generic_kernel"
 
 
 def source_sha(kernel):

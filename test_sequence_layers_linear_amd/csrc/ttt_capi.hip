@@ -96,6 +96,8 @@ int ttt_linear_forward(const void* Q, const void* K, const void* V, int qkv_dtyp
                  Y, W_out, static_cast<hipStream_t>(stream)};
     if (ttt::linear_mfma_supports(a))
         return hip_status(ttt::launch_linear_mfma(a));
+    if (ttt::linear_mfma_f32_supports(a))
+        return hip_status(ttt::launch_linear_mfma_f32(a));
     if (ttt::linear_generic_lds_bytes(d, b) > static_cast<size_t>(ttt::kMaxLdsBytes))
         return TTT_ERR_UNSUPPORTED;
     return hip_status(ttt::launch_linear_generic(a));

@@ -62,9 +62,12 @@ size_t mlp_generic_lds_bytes(int d, int m, int b);
 hipError_t launch_linear_generic(const LinearArgs& a);
 hipError_t launch_mlp_generic(const MlpArgs& a);
 
-// MFMA kernels for the d = 64, b = 16 (and m = 256) shapes with bf16 inputs.
+// MFMA kernels for the d = 64, b = 16 (and m = 256) shapes: bf16 inputs on
+// bf16 MFMA, fp32 inputs on fp32 MFMA.
 bool linear_mfma_supports(const LinearArgs& a);
 hipError_t launch_linear_mfma(const LinearArgs& a);
+bool linear_mfma_f32_supports(const LinearArgs& a);
+hipError_t launch_linear_mfma_f32(const LinearArgs& a);
 bool mlp_mfma_supports(const MlpArgs& a);
 hipError_t launch_mlp_mfma(const MlpArgs& a);
 

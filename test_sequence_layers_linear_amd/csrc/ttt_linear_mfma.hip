@@ -221,19 +221,23 @@ linear_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
 
     // One chunk of the scan, tokens t0 onwards.
     auto step = [&](const ChunkOps& o, int t0) {
-        const bf16x8 bw0 = pack8(Wacc[0], Wacc[1]);
-        const bf16x8 bw1 = pack8(Wacc[2], Wacc[3]);
+        // bf16 copy of the W slice at the chunk start: the B operand of K W_J
+        // and the A operand of W_J^T Q^T (k-slot (g, e) of pair s <-> input
+        // index 32s + 8g + e).  (Computing it at the end of the previous chunk
+        // and carrying it across gave wrong results on gfx950; see DESIGN.)
+        const bf16x8 b0 = pack8(Wacc[0], Wacc[1]);
+        const bf16x8 b1 = pack8(Wacc[2], Wacc[3]);
 
         // R = K W_J - V (C layout: rows t = 4g + r, column col)
         f32x4 R = mfma16(o.vrow, neg_eye, zero);
-        R = mfma32(o.ka0, bw0, R);
-        R = mfma32(o.ka1, bw1, R);
+        R = mfma32(o.ka0, b0, R);
+        R = mfma32(o.ka1, b1, R);
 
         // off the chain: S^T = K Q^T, Y^T partial = W_J^T Q^T
         f32x4 St = mfma32(o.ka0, o.qa0, zero);
         St = mfma32(o.ka1, o.qa1, St);
-        f32x4 Yt = mfma32(bw0, o.qa0, zero);
-        Yt = mfma32(bw1, o.qa1, Yt);
+        f32x4 Yt = mfma32(b0, o.qa0, zero);
+        Yt = mfma32(b1, o.qa1, Yt);
 
         // E' = eta (V - K W) = -eta R
         const bf16x4 eb = pack4(-et * R);
@@ -248,14 +252,27 @@ linear_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
 #pragma unroll
         for (int r = 0; r < 4; ++r)
             Sm[r] = (4 * g + r <= c) ? St[r] : 0.f;
-        Yt = mfma16(eb, pack4(Sm), Yt);
+        const bf16x4 sb = pack4(Sm);
+        Yt = mfma16(eb, sb, Yt);
 
         // Y[t0 + c][16w + 4g .. +3]; rows past T fall outside the buffer.
-        // The store consumes the last MFMA of the chunk, so every MFMA of
-        // the chunk has read its operands before the wave goes on.
         const bf16x4 yb = pack4(Yt);
         __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, yb), ry,
                                               ((t0 + c) * kD + 16 * w + 4 * g) * 2, 0, 0);
+        // Consume the update results too: with the Y store, every MFMA result
+        // of the chunk has now reached a VALU instruction, so no MFMA of the
+        // chunk is in flight.  Only then are its operand registers released
+        // (the empty asm keeps them allocated until here): an LDS read landing
+        // in a register an issued MFMA had not read yet corrupted the product
+        // on gfx950, so operand lifetimes are pinned rather than left to the
+        // register allocator.
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+            Wacc[mt] = Wacc[mt] + zero;
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("" ::"v"(b0), "v"(b1), "v"(o.ka0), "v"(o.ka1), "v"(o.qa0), "v"(o.qa1),
+                     "v"(o.vrow), "v"(o.kt[0]), "v"(o.kt[1]), "v"(o.kt[2]), "v"(o.kt[3]),
+                     "v"(eb), "v"(sb));
         __builtin_amdgcn_sched_barrier(0);
     };
 

@@ -1,0 +1,293 @@
+// ttt_linear_mfma_f32.hip -- TTT-Linear dual-form scan on fp32 MFMA for fp32
+// Q/K/V, head dim d = 64, mini-batch b = 16, fp32 fast weights.
+//
+// Same recurrence and work split as the bf16 kernel (one workgroup of 4 waves
+// per (batch, head) chain, wave w owns the 16 output columns [16w, 16w + 16)
+// of W), with every product in fp32 on v_mfma_f32_16x16x4_f32:
+//     E' = eta (V - K W),   Y = Q W + tril(Q K^T) E',   W = W + K^T E'
+// ("Test-Time Training Layers: How Inner-Loop Gradient Descent Replaces the
+// Transformer KV Cache ...", section "Hardware Parallelization: The Dual Form
+// and Mini-Batch GPU Acceleration").
+//
+// 16x16x4 fp32 layouts (lane l, c = l % 16, g = l / 16):
+//   A: lane holds A[c][k = g];  B: lane holds B[k = g][c];
+//   C/D: lane holds rows 4g..4g+3 of column c.
+// W slice: four 16-row accumulator tiles mt; row 4g + r of tile mt is input
+// index i = 16g + 4mt + r.  A product contracting over i in 16 k-steps
+// ks = 0..15 with k-slot g <-> i = 16g + ks then takes as its W operand the
+// register Wacc[ks / 4][ks % 4] itself (no conversion, no data movement), and
+// the K or Q operand of lane (c, g) for all 16 k-steps is the 64-byte row
+// segment [16g, 16g + 16) of token c.  Products:
+//   R   = -V + K W_J   : V^T read from LDS straight into the accumulator
+//   S^T = K Q^T        : C layout = B layout of the E'^T S^T product
+//   Y^T = W_J^T Q^T + E'^T S^T (masked)
+//   W  += K^T E'       : 4 k-steps over tokens t = 4g + q; E' register q is
+//                        the B operand and K^T rows come from LDS
+// Each product over i runs as 4 independent accumulators (k-steps ks mod 4)
+// that are summed at the end, so the 16 MFMAs of a product form 4 short
+// dependency chains instead of one long one.
+//
+// Memory: as in the bf16 kernel, with a stage of one chunk: wave w loads rows
+// [4w, 4w + 4) of the chunk's K, Q and V (three 1 KB row blocks, 16 bytes per
+// lane) two register sets ahead, then writes them into a 3-slot LDS ring
+// holding K and Q row-major (16-byte segments XOR-swizzled by row) and K^T,
+// V^T (token-contiguous rows, segments swizzled by row group).  One barrier
+// per chunk.  All LDS operand reads of a chunk complete before its first MFMA
+// and every MFMA result is consumed before the chunk ends, so no LDS read is
+// in flight while an MFMA may still read its source registers.
+#include "ttt_internal.h"
+
+namespace ttt {
+namespace {
+
+constexpr int kD = 64;
+constexpr int kB = 16;
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kSet = 6;                 // chunks per register set (two sets)
+constexpr int kSlots = 3;
+constexpr int kBufferDword3 = 0x00020000;   // raw buffer resource word 3 (gfx9 family)
+
+constexpr int kRowBytes = kD * 4;                    // 256
+constexpr int kOffK = 0;
+constexpr int kOffQ = kOffK + kB * kRowBytes;        // 4096
+constexpr int kOffKt = kOffQ + kB * kRowBytes;       // 8192  [64 i][16 t] fp32
+constexpr int kOffVt = kOffKt + kD * kB * 4;         // 12288 [64 j][16 t] fp32
+constexpr int kSlotBytes = kOffVt + kD * kB * 4;     // 16384
+constexpr int kLdsBytes = kSlotBytes * kSlots;       // 49152
+
+static_assert((2 * kSet) % kSlots == 0, "slot index must be static inside the loop");
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mfma(float a, float b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// K, Q tiles: row r (token), 16-byte segment s in [0, 16)
+__device__ __forceinline__ int swz_row(int r, int s) { return r * kRowBytes + ((s ^ (r & 15)) << 4); }
+// K^T, V^T tiles: row x (input / output index), 16-byte segment s in [0, 4)
+// (4 tokens each); the segment is swizzled by the row group so that 8 lanes
+// reading segment s of 8 rows ρ hit 8 different bank groups.
+__device__ __forceinline__ int swz_kt(int i, int s) { return i * 64 + ((s ^ ((i >> 4) & 3)) << 4); }
+__device__ __forceinline__ int swz_vt(int j, int s) { return j * 64 + ((s ^ ((j >> 2) & 3)) << 4); }
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t chain_rsrc(const void* base, int64_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0,
+                                             static_cast<int>(bytes), kBufferDword3);
+}
+
+struct StageRegs {
+    u32x4 k, q, v;
+};
+
+__global__ void __launch_bounds__(kThreads, 1)
+linear_mfma_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
+                       const float* __restrict__ V, const float* W0, int w0_per_batch,
+                       const float* __restrict__ eta, int H, int T,
+                       float* __restrict__ Y, float* W_out)
+{
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+
+    const int lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
+    const int c = lane & 15;
+    const int g = lane >> 4;
+    const int col = 16 * w + c;
+
+    const int64_t u = blockIdx.x;
+    const int h = static_cast<int>(u % H);
+    const float et = eta[h];
+    const float* w0 = W0 + (w0_per_batch ? u : h) * kD * kD;
+
+    // Wacc[mt][r] = W[16g + 4mt + r][col]
+    f32x4 Wacc[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            Wacc[mt][r] = w0[(16 * g + 4 * mt + r) * kD + col];
+
+    const int64_t base = u * static_cast<int64_t>(T) * kD;
+    const int64_t chain_bytes = static_cast<int64_t>(T) * kD * 4;
+    const __amdgpu_buffer_rsrc_t rq = chain_rsrc(Q + base, chain_bytes);
+    const __amdgpu_buffer_rsrc_t rk = chain_rsrc(K + base, chain_bytes);
+    const __amdgpu_buffer_rsrc_t rv = chain_rsrc(V + base, chain_bytes);
+    const __amdgpu_buffer_rsrc_t ry = chain_rsrc(Y + base, chain_bytes);
+
+    const int nchunks = (T + kB - 1) / kB;
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+
+    // staging: lane l of wave w holds row 4w + l / 16, 16-byte segment l % 16
+    const int st_row = 4 * w + (lane >> 4);
+    const int st_seg = lane & 15;
+    auto load_stage = [&](StageRegs& o, int chunk) {
+        const int off = (chunk * kB + st_row) * kRowBytes + st_seg * 16;
+        o.k = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
+        o.q = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0);
+        o.v = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0);
+    };
+    auto write_stage = [&](const StageRegs& o, int slot) {
+        unsigned char* sl = lds + slot * kSlotBytes;
+        *reinterpret_cast<u32x4*>(sl + kOffK + swz_row(st_row, st_seg)) = o.k;
+        *reinterpret_cast<u32x4*>(sl + kOffQ + swz_row(st_row, st_seg)) = o.q;
+        // transposed copies: element e of this segment is index 4 st_seg + e;
+        // token st_row sits at position st_row % 4 of 16-byte segment st_row / 4
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int x = 4 * st_seg + e;
+            *reinterpret_cast<uint32_t*>(sl + kOffKt + swz_kt(x, st_row >> 2) + 4 * (st_row & 3)) = o.k[e];
+            *reinterpret_cast<uint32_t*>(sl + kOffVt + swz_vt(x, st_row >> 2) + 4 * (st_row & 3)) = o.v[e];
+        }
+    };
+
+    struct ChunkOps {
+        f32x4 k[4];        // K[t = c][16g + 4x .. +3], x = 0..3
+        f32x4 q[4];        // Q[t = c][16g + 4x .. +3]
+        f32x4 kt[4];       // K^T[16g... see below]: kt[mt] = K[4g .. 4g+3][i = 16(c/4) + 4mt + c%4]
+        f32x4 vt;          // V[4g .. 4g+3][col]
+    };
+    auto read_ops = [&](ChunkOps& o, const unsigned char* sl) {
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            o.k[x] = *reinterpret_cast<const f32x4*>(sl + kOffK + swz_row(c, 4 * g + x));
+            o.q[x] = *reinterpret_cast<const f32x4*>(sl + kOffQ + swz_row(c, 4 * g + x));
+        }
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+            o.kt[mt] = *reinterpret_cast<const f32x4*>(
+                sl + kOffKt + swz_kt(16 * (c >> 2) + 4 * mt + (c & 3), g));
+        o.vt = *reinterpret_cast<const f32x4*>(sl + kOffVt + swz_vt(col, g));
+    };
+
+    auto step = [&](const ChunkOps& o, int t0) {
+        // R = -V + K W_J, St = K Q^T, Yt = W_J^T Q^T: 4 accumulators each over
+        // k-steps ks = 4x + r (x = register group of the row segment)
+        f32x4 R[4], St[4], Yt[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            R[r] = (r == 0) ? -o.vt : zero;
+            St[r] = zero;
+            Yt[r] = zero;
+        }
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                // k-step ks = 4x + r: i = 16g + ks, W operand Wacc[x][r]
+                R[r] = mfma(o.k[x][r], Wacc[x][r], R[r]);
+                St[r] = mfma(o.k[x][r], o.q[x][r], St[r]);
+                Yt[r] = mfma(Wacc[x][r], o.q[x][r], Yt[r]);
+            }
+        const f32x4 Rs = (R[0] + R[1]) + (R[2] + R[3]);
+        f32x4 S = (St[0] + St[1]) + (St[2] + St[3]);
+        f32x4 Ys = (Yt[0] + Yt[1]) + (Yt[2] + Yt[3]);
+
+        // E' = -eta R: lane (c = j, g) holds E'[t = 4g + q][j]
+        const f32x4 Ep = -et * Rs;
+
+        // W += K^T E' (k-steps q over tokens t = 4g + q)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq)
+                Wacc[mt] = mfma(o.kt[mt][qq], Ep[qq], Wacc[mt]);
+
+        // S^T masked: lane (c = t, g) holds S[t][t' = 4g + q]; keep t' <= t
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq)
+            S[qq] = (4 * g + qq <= c) ? S[qq] : 0.f;
+        f32x4 Y2 = zero;
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq)
+            Y2 = mfma(Ep[qq], S[qq], Y2);
+        const f32x4 Yv = Ys + Y2;
+
+        // Y[t0 + c][16w + 4g .. +3]; rows past T fall outside the buffer
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, Yv), ry,
+                                               ((t0 + c) * kD + 16 * w + 4 * g) * 4, 0, 0);
+        // Consume the update results too: from here on no MFMA of this chunk
+        // is in flight.  Only then are the chunk's operand registers released
+        // (the empty asm keeps them allocated until now), so no LDS or VALU
+        // write can land in a register an issued MFMA has not read yet.
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+            Wacc[mt] = Wacc[mt] + zero;
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("" ::"v"(o.k[0]), "v"(o.k[1]), "v"(o.k[2]), "v"(o.k[3]), "v"(o.q[0]),
+                     "v"(o.q[1]), "v"(o.q[2]), "v"(o.q[3]), "v"(o.kt[0]), "v"(o.kt[1]),
+                     "v"(o.kt[2]), "v"(o.kt[3]), "v"(Ep), "v"(S));
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    auto process = [&](const StageRegs& next, int chunk, int slot) {
+        write_stage(next, (slot + 1) % kSlots);
+        __syncthreads();
+        ChunkOps o;
+        read_ops(o, lds + slot * kSlotBytes);
+        __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
+        __builtin_amdgcn_sched_barrier(0);
+        step(o, chunk * kB);
+    };
+
+    if (nchunks > 0) {
+        StageRegs setA[kSet], setB[kSet];
+        {
+            StageRegs first;
+            load_stage(first, 0);
+            write_stage(first, 0);
+        }
+#pragma unroll
+        for (int p = 0; p < kSet; ++p)
+            load_stage(setA[p], 1 + p);
+        for (int c0 = 0; c0 < nchunks; c0 += 2 * kSet) {
+#pragma unroll
+            for (int p = 0; p < kSet; ++p)
+                load_stage(setB[p], c0 + kSet + 1 + p);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int p = 0; p < kSet; ++p)
+                process(setA[p], c0 + p, p % kSlots);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int p = 0; p < kSet; ++p)
+                load_stage(setA[p], c0 + 2 * kSet + 1 + p);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int p = 0; p < kSet; ++p)
+                process(setB[p], c0 + kSet + p, (kSet + p) % kSlots);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+
+    float* wo = W_out + u * kD * kD;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            wo[(16 * g + 4 * mt + r) * kD + col] = Wacc[mt][r];
+}
+
+}  // namespace
+
+bool linear_mfma_f32_supports(const LinearArgs& a)
+{
+    const int64_t max_tokens = (int64_t{1} << 31) / (kD * 4) - kB * (3 * kSet + 2);
+    return a.dtype == 0 && a.d == kD && a.b == kB && a.T <= max_tokens;
+}
+
+hipError_t launch_linear_mfma_f32(const LinearArgs& a)
+{
+    const dim3 grid(static_cast<unsigned>(a.B * a.H)), block(kThreads);
+    hipLaunchKernelGGL(linear_mfma_f32_kernel, grid, block, kLdsBytes, a.stream,
+                       static_cast<const float*>(a.Q), static_cast<const float*>(a.K),
+                       static_cast<const float*>(a.V), a.W0, a.w0_per_batch, a.eta,
+                       static_cast<int>(a.H), static_cast<int>(a.T),
+                       static_cast<float*>(a.Y), a.W_out);
+    return hipGetLastError();
+}
+
+}  // namespace ttt

@@ -69,6 +69,13 @@ def test_mfma_shapes(B, H, T):
     _check(make_inputs(w, 7 + T), 16, "bf16")
 
 
+@pytest.mark.parametrize("B,H,T", [(1, 1, 1), (1, 1, 17), (2, 3, 48), (1, 7, 257), (2, 2, 1000)])
+def test_mfma_fp32_shapes(B, H, T):
+    w = CONFIGS[2].with_(B=B, H=H, T=T, eta=("uniform", 0.01, 0.1))
+    announce("linear mfma fp32", B, H, T)
+    _check(make_inputs(w, 9 + T), 16, "fp32")
+
+
 @pytest.mark.parametrize("d,b,dtype", [(16, 16, "fp32"), (32, 16, "fp32"), (64, 16, "fp32"),
                                        (128, 16, "fp32"), (64, 1, "fp32"), (16, 8, "fp32"),
                                        (32, 64, "fp32"), (128, 32, "fp32"), (16, 16, "bf16"),
@@ -120,16 +127,17 @@ def _embed(g, case, d, dtype):
     return pad(g["q"]), pad(g["k"]), pad(g["v"]), W0.cuda()
 
 
-@pytest.mark.parametrize("path", ["generic_fp32", "mfma_bf16"])
+@pytest.mark.parametrize("path", ["generic_fp32", "mfma_bf16", "mfma_fp32"])
 def test_worked_examples_bit_exact(path):
     g, cases = _worked_cases()
     eta = torch.tensor([float(Fraction(g["eta"]))]).cuda()
     for case in cases:
-        if path == "mfma_bf16":
+        if path.startswith("mfma"):
             # when b >= T one chunk covers the sequence, so b equals b = 16 there
             if case["b"] < case["T"]:
                 continue
-            d, dtype, b = 64, torch.bfloat16, 16
+            d, b = 64, 16
+            dtype = torch.bfloat16 if path == "mfma_bf16" else torch.float32
         else:
             d, dtype, b = 16, torch.float32, case["b"]
         q, k, v, W0 = _embed(g, case, d, dtype)
