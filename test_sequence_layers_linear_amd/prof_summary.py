@@ -1,0 +1,120 @@
+"""Turn rocprofv3 CSV output of prof_workload.py runs into the short text
+summaries kept under profiles/ and the per-launch HBM byte table bench.py
+reports as roofline.traffic.
+
+    python3 -m test_sequence_layers_linear_amd.prof_summary --config 2 \
+        --trace DIR_WITH_kt_kernel_stats.csv --fetch DIR_FETCH --write DIR_WRITE \
+        --command "..." --out profiles/linear_fp32_B1_H4_T2048.md
+
+FETCH_SIZE and WRITE_SIZE are in KiB per dispatch.  Each is scaled by the
+ratio of the known bytes of the plain 256 MiB device copy in the same run to
+what the same counter reads for that copy.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "test_sequence_layers_linear_amd", "csrc")
+KERNEL_FILES = {
+    "linear_mfma_kernel": "ttt_linear_mfma.hip",
+    "linear_mfma_f32_kernel": "ttt_linear_mfma_f32.hip",
+    "linear_generic_kernel": "ttt_generic.hip",
+    "mlp_generic_kernel": "ttt_generic.hip",
+    "mlp_mfma_kernel": "ttt_mlp_mfma.hip",
+    "decode_kernel": "ttt_decode.hip",
+}
+COPY_NAME = "__amd_rocclr_copyBuffer"
+
+
+def short_name(full: str) -> str:
+    for k in KERNEL_FILES:
+        if k + "(" in full or k + "<" in full:
+            return k
+    return full.split("(")[0][-60:]
+
+
+def source_sha(kernel: str) -> str:
+    path = os.path.join(CSRC, KERNEL_FILES[kernel])
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def one_csv(d: str, suffix: str) -> str:
+    hits = glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True)
+    if not hits:
+        raise FileNotFoundError(f"no *{suffix} under {d}")
+    return hits[0]
+
+
+def counter_per_kernel(d: str):
+    vals = {}
+    for r in csv.DictReader(open(one_csv(d, "counter_collection.csv"))):
+        vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return vals
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--config", type=int, required=True)
+    ap.add_argument("--trace", required=True)
+    ap.add_argument("--fetch", required=True)
+    ap.add_argument("--write", required=True)
+    ap.add_argument("--command", required=True, help="the rocprofv3 command lines that made the data")
+    ap.add_argument("--copy-mib", type=int, default=256)
+    ap.add_argument("--out", required=True)
+    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"))
+    args = ap.parse_args()
+
+    import sys
+    sys.path.insert(0, ROOT)
+    from test_sequence_layers_linear_amd.inputs import CONFIGS
+    w = CONFIGS[args.config]
+
+    stats = list(csv.DictReader(open(one_csv(args.trace, "kernel_stats.csv"))))
+    fetch = counter_per_kernel(args.fetch)
+    write = counter_per_kernel(args.write)
+    copy_bytes = args.copy_mib * 1024 * 1024
+    copy_fetch = max(v for k, vs in fetch.items() if COPY_NAME in k for v in vs) * 1024
+    copy_write = max(v for k, vs in write.items() if COPY_NAME in k for v in vs) * 1024
+    f_scale, w_scale = copy_bytes / copy_fetch, copy_bytes / copy_write
+
+    lines = [f"# rocprofv3 summary: {w.name}", "",
+             "Commands (run from /tmp on the GPU box, repo at $R):", "", "```", args.command, "```", "",
+             f"Copy calibration ({args.copy_mib} MiB device copy): FETCH_SIZE reads "
+             f"{copy_fetch / 1024:.1f} KiB (scale {f_scale:.3f}), WRITE_SIZE reads "
+             f"{copy_write / 1024:.1f} KiB (scale {w_scale:.3f}).", "",
+             "| kernel | calls | avg us | min us | max us | HBM read MB/launch | HBM write MB/launch |",
+             "|---|---|---|---|---|---|---|"]
+    table = json.load(open(args.traffic)) if os.path.exists(args.traffic) else {}
+    for r in stats:
+        name = short_name(r["Name"])
+        if name not in KERNEL_FILES:
+            continue
+        fr = [v for k, vs in fetch.items() if short_name(k) == name for v in vs]
+        wr = [v for k, vs in write.items() if short_name(k) == name for v in vs]
+        rd = sum(fr) / len(fr) * 1024 * f_scale if fr else float("nan")
+        wb = sum(wr) / len(wr) * 1024 * w_scale if wr else float("nan")
+        lines.append(f"| {name} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                     f"{rd / 1e6:.3f} | {wb / 1e6:.3f} |")
+        if fr and wr:
+            table.setdefault(name, {})[w.name] = {
+                "source_sha": source_sha(name), "bytes_per_launch": int(rd + wb),
+                "read_bytes": int(rd), "write_bytes": int(wb),
+                "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
+                "avg_us": round(float(r["AverageNs"]) / 1e3, 3)}
+    lines.append("")
+    with open(args.out, "w") as f:
+        f.write("\n".join(lines))
+    with open(args.traffic, "w") as f:
+        json.dump(table, f, indent=1, sort_keys=True)
+    print("\n".join(lines))
+
+
+if __name__ == "__main__":
+    main()

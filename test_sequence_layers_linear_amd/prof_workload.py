@@ -1,0 +1,62 @@
+"""Fixed workload for rocprofv3 runs: one benchmark configuration's hot path
+launched a few times, then one plain device copy of known size whose HBM
+counters calibrate the byte counters of the kernels above.
+
+    rocprofv3 --kernel-trace --stats -- python3 <repo>/test_sequence_layers_linear_amd/prof_workload.py --config 2
+    rocprofv3 --pmc FETCH_SIZE       -- python3 <repo>/test_sequence_layers_linear_amd/prof_workload.py --config 2
+"""
+from __future__ import annotations
+
+import argparse
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--reps", type=int, default=5)
+    ap.add_argument("--copy-mib", type=int, default=256)
+    ap.add_argument("--decode", action="store_true", help="also run the workload's decode steps")
+    args = ap.parse_args()
+
+    import torch
+    import test_sequence_layers_linear_amd as ttt
+    from test_sequence_layers_linear_amd.inputs import CONFIGS, default_seed, make_inputs
+
+    w = CONFIGS[args.config]
+    g = {k: v.cuda() for k, v in make_inputs(w, default_seed(args.config)).items()}
+    Y = torch.empty_like(g["Q"])
+    if w.kind == "linear":
+        W = torch.empty((w.B, w.H, w.d, w.d), device="cuda")
+    else:
+        W1 = torch.empty((w.B, w.H, w.d, w.m), device="cuda")
+        W2 = torch.empty((w.B, w.H, w.m, w.d), device="cuda")
+    torch.cuda.synchronize()
+    for _ in range(args.reps):
+        if w.kind == "linear":
+            ttt.ttt_linear_forward(g["Q"], g["K"], g["V"], g["W0"], g["eta"], w.b, Y=Y, W_out=W)
+            if args.decode:
+                y = torch.empty_like(g["dq"][0])
+                for s in range(w.decode_steps):
+                    ttt.ttt_linear_decode_step(g["dq"][s], g["dk"][s], g["dv"][s], W, g["eta"], y=y)
+        else:
+            ttt.ttt_mlp_forward(g["Q"], g["K"], g["V"], g["W1"], g["W2"], g["eta"], w.b,
+                                Y=Y, W1_out=W1, W2_out=W2)
+    torch.cuda.synchronize()
+    n = args.copy_mib * 1024 * 1024 // 4
+    a = torch.ones(n, device="cuda")
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    b.copy_(a)          # reads and writes exactly copy_mib MiB
+    torch.cuda.synchronize()
+    print(f"prof_workload: config {args.config} ({w.name}) x{args.reps}, copy {args.copy_mib} MiB",
+          flush=True)
+
+
+if __name__ == "__main__":
+    main()
