@@ -18,7 +18,8 @@ def _check(inp, b, dtype):
 
 
 @pytest.mark.parametrize("d,m,b,T,dtype", [(64, 256, 16, 100, "bf16"), (64, 256, 16, 16, "bf16"),
-                                           (64, 256, 16, 5, "bf16"), (64, 256, 16, 300, "fp32"),
+                                           (64, 256, 16, 5, "bf16"), (64, 256, 16, 48, "bf16"),
+                                           (64, 256, 16, 300, "fp32"),
                                            (16, 64, 4, 37, "fp32"), (32, 128, 16, 50, "fp32"),
                                            (32, 128, 8, 50, "bf16"), (64, 512, 16, 40, "bf16"),
                                            (16, 16, 1, 9, "fp32")])
@@ -26,6 +27,18 @@ def test_mlp_shapes(d, m, b, T, dtype):
     announce("mlp", d, m, b, T, dtype)
     w = CONFIGS[5].with_(B=2, H=3, T=T, d=d, m=m, b=b, dtype=dtype)
     _check(make_inputs(w, 200 + d + m + T), b, dtype)
+
+
+@pytest.mark.parametrize("T,std,eta,per_batch", [(32, 0.3, 0.3, False), (100, 0.2, 0.1, True),
+                                                  (160, 0.2, 0.1, False), (257, 0.1, 0.05, True)])
+def test_mlp_strong_state(T, std, eta, per_batch):
+    """d64 m256 b16 bf16 with a state large enough that every term of the
+    update and the readout moves the result well above the tolerance (the
+    updates change Y by 70-100 % in rel-L2 here; larger eta at T = 100 makes
+    the inner descent itself diverge)."""
+    announce("mlp strong state", T, std, eta, per_batch)
+    w = CONFIGS[5].with_(B=2, H=3, T=T, w0=("normal", std), eta=("const", eta))
+    _check(make_inputs(w, 300 + T, w0_per_batch=per_batch), 16, "bf16")
 
 
 def test_config5_sampled_chains_full_length():
