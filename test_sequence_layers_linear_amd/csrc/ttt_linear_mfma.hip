@@ -99,6 +99,23 @@ __device__ __forceinline__ f32x4 mfma16(bf16x4 a, bf16x4 b, f32x4 c)
                                                      __builtin_bit_cast(i16x4, b), c, 0, 0, 0);
 }
 
+// A 16x16x16 product whose result feeds a 16x16x32 product as the
+// accumulator (or the reverse) needs 5 wait states on gfx950 between the two,
+// more than the compiler inserts; such products are issued as 16x16x32 with
+// the upper four k-slots zero, so that every accumulation chain has one shape.
+__device__ __forceinline__ f32x4 mfma16_as32(bf16x4 a, bf16x4 b, f32x4 c)
+{
+    bf16x8 a8, b8;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        a8[e] = a[e];
+        b8[e] = b[e];
+        a8[4 + e] = static_cast<__bf16>(0.0f);
+        b8[4 + e] = static_cast<__bf16>(0.0f);
+    }
+    return mfma32(a8, b8, c);
+}
+
 __device__ __forceinline__ bf16x8 pack8(f32x4 lo, f32x4 hi)
 {
     bf16x8 r;
@@ -223,13 +240,13 @@ linear_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     auto step = [&](const ChunkOps& o, int t0) {
         // bf16 copy of the W slice at the chunk start: the B operand of K W_J
         // and the A operand of W_J^T Q^T (k-slot (g, e) of pair s <-> input
-        // index 32s + 8g + e).  (Computing it at the end of the previous chunk
-        // and carrying it across gave wrong results on gfx950; see DESIGN.)
+        // index 32s + 8g + e)
         const bf16x8 b0 = pack8(Wacc[0], Wacc[1]);
         const bf16x8 b1 = pack8(Wacc[2], Wacc[3]);
 
-        // R = K W_J - V (C layout: rows t = 4g + r, column col)
-        f32x4 R = mfma16(o.vrow, neg_eye, zero);
+        // R = K W_J - V (C layout: rows t = 4g + r, column col); the -I
+        // product is issued in the 16x16x32 shape of the chain it starts
+        f32x4 R = mfma16_as32(o.vrow, neg_eye, zero);
         R = mfma32(o.ka0, b0, R);
         R = mfma32(o.ka1, b1, R);
 
@@ -253,35 +270,15 @@ linear_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
         for (int r = 0; r < 4; ++r)
             Sm[r] = (4 * g + r <= c) ? St[r] : 0.f;
         const bf16x4 sb = pack4(Sm);
-        Yt = mfma16(eb, sb, Yt);
+        Yt = mfma16_as32(eb, sb, Yt);
 
         // Y[t0 + c][16w + 4g .. +3]; rows past T fall outside the buffer.
         const bf16x4 yb = pack4(Yt);
         __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, yb), ry,
                                               ((t0 + c) * kD + 16 * w + 4 * g) * 2, 0, 0);
-        // Consume the update results too: with the Y store, every MFMA result
-        // of the chunk has now reached a VALU instruction, so no MFMA of the
-        // chunk is in flight.  Only then are its operand registers released
-        // (the empty asm keeps them allocated until here): an LDS read landing
-        // in a register an issued MFMA had not read yet corrupted the product
-        // on gfx950, so operand lifetimes are pinned rather than left to the
-        // register allocator.
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-            Wacc[mt] = Wacc[mt] + zero;
-        __builtin_amdgcn_sched_barrier(0);
-        asm volatile("" ::"v"(b0), "v"(b1), "v"(o.ka0), "v"(o.ka1), "v"(o.qa0), "v"(o.qa1),
-                     "v"(o.vrow), "v"(o.kt[0]), "v"(o.kt[1]), "v"(o.kt[2]), "v"(o.kt[3]),
-                     "v"(eb), "v"(sb));
-        __builtin_amdgcn_sched_barrier(0);
     };
 
     // Stage s: publish stage s + 1 (held in `next`), then compute stage s.
-    // All LDS operand reads of the stage complete before its first MFMA: an
-    // LDS read returning into a register that an MFMA issued earlier has not
-    // read yet corrupts that MFMA's operand, so reads and products are kept
-    // in separate phases (the scheduling barriers stop the compiler from
-    // interleaving them).
     auto process = [&](const StageRegs& next, int s, int slot) {
         write_stage(next, (slot + 1) % kSlots);
         __syncthreads();
@@ -289,8 +286,6 @@ linear_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
         ChunkOps o0, o1;
         read_ops(o0, sl);
         read_ops(o1, sl + kChunkBytes);
-        __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): all operands in registers
-        __builtin_amdgcn_sched_barrier(0);
         step(o0, s * kStageTokens);
         step(o1, s * kStageTokens + kB);
     };

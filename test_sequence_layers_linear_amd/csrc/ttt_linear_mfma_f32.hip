@@ -32,9 +32,8 @@
 // lane) two register sets ahead, then writes them into a 3-slot LDS ring
 // holding K and Q row-major (16-byte segments XOR-swizzled by row) and K^T,
 // V^T (token-contiguous rows, segments swizzled by row group).  One barrier
-// per chunk.  All LDS operand reads of a chunk complete before its first MFMA
-// and every MFMA result is consumed before the chunk ends, so no LDS read is
-// in flight while an MFMA may still read its source registers.
+// per chunk.  Every product is a 16x16x4 fp32 MFMA, so accumulation chains
+// never mix MFMA shapes.
 #include "ttt_internal.h"
 
 namespace ttt {
@@ -209,18 +208,6 @@ linear_mfma_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
         // Y[t0 + c][16w + 4g .. +3]; rows past T fall outside the buffer
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, Yv), ry,
                                                ((t0 + c) * kD + 16 * w + 4 * g) * 4, 0, 0);
-        // Consume the update results too: from here on no MFMA of this chunk
-        // is in flight.  Only then are the chunk's operand registers released
-        // (the empty asm keeps them allocated until now), so no LDS or VALU
-        // write can land in a register an issued MFMA has not read yet.
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-            Wacc[mt] = Wacc[mt] + zero;
-        __builtin_amdgcn_sched_barrier(0);
-        asm volatile("" ::"v"(o.k[0]), "v"(o.k[1]), "v"(o.k[2]), "v"(o.k[3]), "v"(o.q[0]),
-                     "v"(o.q[1]), "v"(o.q[2]), "v"(o.q[3]), "v"(o.kt[0]), "v"(o.kt[1]),
-                     "v"(o.kt[2]), "v"(o.kt[3]), "v"(Ep), "v"(S));
-        __builtin_amdgcn_sched_barrier(0);
     };
 
     auto process = [&](const StageRegs& next, int chunk, int slot) {
@@ -228,8 +215,6 @@ linear_mfma_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
         __syncthreads();
         ChunkOps o;
         read_ops(o, lds + slot * kSlotBytes);
-        __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
-        __builtin_amdgcn_sched_barrier(0);
         step(o, chunk * kB);
     };
 
