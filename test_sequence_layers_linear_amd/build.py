@@ -1,33 +1,61 @@
-"""Build libttt.so (hipcc, gfx950) from csrc/ in place."""
+"""Build libttt.so (hipcc, gfx950) from csrc/ in place.
+
+Each source is compiled to an object under _build/ with the common flags plus
+its own, then the objects are linked into libttt.so.
+"""
 from __future__ import annotations
 
 import glob
 import os
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
+OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libttt.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU ops.
 FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
     f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}",
 ]
+
+# Per-file flags.  The TTT-Linear MFMA kernels keep every MFMA accumulator in
+# ordinary VGPRs (they fit): otherwise the compiler places the results in
+# AGPRs and copies each one back to a VGPR before its VALU use, about a
+# quarter of the instructions of a chunk.  The TTT-MLP kernel needs the AGPRs
+# for its 192 registers of fast weights.
+EXTRA = {
+    "ttt_linear_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "ttt_linear_mfma_f32.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
 
 
 def sources() -> list[str]:
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
+def _compile(src: str, verbose: bool) -> str:
+    obj = os.path.join(OBJ, os.path.basename(src) + ".o")
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(os.path.basename(src), []), "-c", src, "-o", obj]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    return obj
+
+
 def build(verbose: bool = False) -> str:
+    os.makedirs(OBJ, exist_ok=True)
+    with ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), sources()))
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, *sources(), "-o", tmp]
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

@@ -6,6 +6,12 @@
 
 #include <stdint.h>
 
+#include <stdlib.h>
+
+#include <atomic>
+#include <mutex>
+#include <vector>
+
 namespace {
 
 using ttt::LinearArgs;
@@ -44,6 +50,132 @@ bool d_supported(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 constexpr int64_t kMaxUnits = 0x7fffffff;
 
 int hip_status(hipError_t e) { return e == hipSuccess ? TTT_OK : TTT_ERR_HIP; }
+
+// Compute units of the current device (cached per device).
+int device_cus()
+{
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+    if (dev < 64) {
+        const int v = cache[dev].load(std::memory_order_relaxed);
+        if (v > 0) return v;
+    }
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
+// Segment count for a chain-parallel scan of `units` chains of T tokens:
+// minimises ceil(chunks / S) (fwd + map) + (S - 1) apply while both launches
+// fit on the device at once.
+// TTT_LINEAR_SEGMENTS=S (S >= 1) forces S segments (at least one chunk
+// each), for tests and tuning.
+ttt::SegmentPlan plan_segments(int64_t units, int64_t T, int chunk, const ttt::SegmentCosts& cost)
+{
+    ttt::SegmentPlan p;
+    p.seg_len = T;
+    const int64_t chunks = (T + chunk - 1) / chunk;
+    if (const char* env = getenv("TTT_LINEAR_SEGMENTS")) {
+        const long S = strtol(env, nullptr, 10);
+        if (S >= 1 && chunks > 0) {
+            p.seg_len = ((chunks + S - 1) / S) * chunk;
+            p.nseg = static_cast<int>((T + p.seg_len - 1) / p.seg_len);
+            return p;
+        }
+    }
+    const int64_t cap = static_cast<int64_t>(device_cus()) * ttt::kLinearBlocksPerCu;
+    if (cap <= 0 || units * 2 > cap || chunks < 4) return p;
+    double best = static_cast<double>(chunks) * cost.fwd;
+    int best_s = 1;
+    for (int S = 2; S <= 64; ++S) {
+        if (units * S > cap || units * (S - 1) * 2 > cap) break;
+        const int64_t per = (chunks + S - 1) / S;
+        if (per < 2) break;
+        const double t = per * (cost.fwd + cost.map) + (S - 1) * cost.apply;
+        if (t < best) { best = t; best_s = S; }
+    }
+    if (best_s > 1) {
+        p.seg_len = ((chunks + best_s - 1) / best_s) * chunk;
+        p.nseg = static_cast<int>((T + p.seg_len - 1) / p.seg_len);
+    }
+    return p;
+}
+
+// Workspace for the segment maps: one device buffer per (device, stream),
+// grown on demand and kept until the process ends.  Calls on one stream are
+// ordered by the stream, so they can share its buffer; calls on different
+// streams get different buffers.  Before a buffer is replaced by a larger one
+// its stream is synchronised, so no enqueued kernel still uses it.
+hipError_t workspace_get(void** ptr, size_t bytes, hipStream_t stream)
+{
+    struct Entry {
+        int dev;
+        hipStream_t stream;
+        void* p;
+        size_t bytes;
+    };
+    static std::mutex mu;
+    static std::vector<Entry> cache;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lock(mu);
+    Entry* hit = nullptr;
+    for (Entry& x : cache)
+        if (x.dev == dev && x.stream == stream) hit = &x;
+    if (hit && hit->bytes >= bytes) {
+        *ptr = hit->p;
+        return hipSuccess;
+    }
+    if (hit) {
+        e = hipStreamSynchronize(stream);
+        if (e != hipSuccess) return e;
+        e = hipFree(hit->p);
+        hit->p = nullptr;
+        hit->bytes = 0;
+        if (e != hipSuccess) return e;
+    }
+    void* p = nullptr;
+    e = hipMalloc(&p, bytes);
+    if (e != hipSuccess) return e;
+    if (hit) {
+        hit->p = p;
+        hit->bytes = bytes;
+    } else {
+        cache.push_back(Entry{dev, stream, p, bytes});
+    }
+    *ptr = p;
+    return hipSuccess;
+}
+
+// Runs a segmented MFMA linear scan: workspace for the maps (and a copy of
+// W0 when W_out overwrites it), then both launches.
+int run_linear_segmented(LinearArgs a, ttt::SegmentPlan p,
+                         hipError_t (*launch)(const LinearArgs&, const ttt::SegmentPlan&))
+{
+    if (p.nseg <= 1) return hip_status(launch(a, p));
+    const int64_t units = a.B * a.H;
+    const size_t state = static_cast<size_t>(a.d) * a.d * sizeof(float);
+    const size_t map_bytes = static_cast<size_t>(units) * (p.nseg - 1) * 2 * state;
+    const int64_t w0_units = a.w0_per_batch ? units : a.H;
+    const bool in_place = reinterpret_cast<uintptr_t>(a.W_out) < reinterpret_cast<uintptr_t>(a.W0) + w0_units * state &&
+                          reinterpret_cast<uintptr_t>(a.W0) < reinterpret_cast<uintptr_t>(a.W_out) + units * state;
+    const size_t copy_bytes = in_place ? static_cast<size_t>(w0_units) * state : 0;
+    void* ws = nullptr;
+    hipError_t e = workspace_get(&ws, map_bytes + copy_bytes, a.stream);
+    if (e != hipSuccess) return TTT_ERR_HIP;
+    p.maps = static_cast<float*>(ws);
+    if (in_place) {
+        // the last segment writes W_out while other segments may still read W0
+        float* w0c = p.maps + map_bytes / sizeof(float);
+        e = hipMemcpyAsync(w0c, a.W0, copy_bytes, hipMemcpyDeviceToDevice, a.stream);
+        a.W0 = w0c;
+    }
+    if (e == hipSuccess) e = launch(a, p);
+    return hip_status(e);
+}
 
 }  // namespace
 
@@ -95,9 +227,11 @@ int ttt_linear_forward(const void* Q, const void* K, const void* V, int qkv_dtyp
     LinearArgs a{Q, K, V, qkv_dtype, W0, w0_per_batch, eta, B, H, T, d, b,
                  Y, W_out, static_cast<hipStream_t>(stream)};
     if (ttt::linear_mfma_supports(a))
-        return hip_status(ttt::launch_linear_mfma(a));
+        return run_linear_segmented(a, plan_segments(units, T, b, ttt::kLinearBf16Costs),
+                                    ttt::launch_linear_mfma);
     if (ttt::linear_mfma_f32_supports(a))
-        return hip_status(ttt::launch_linear_mfma_f32(a));
+        return run_linear_segmented(a, plan_segments(units, T, b, ttt::kLinearF32Costs),
+                                    ttt::launch_linear_mfma_f32);
     if (ttt::linear_generic_lds_bytes(d, b) > static_cast<size_t>(ttt::kMaxLdsBytes))
         return TTT_ERR_UNSUPPORTED;
     return hip_status(ttt::launch_linear_generic(a));

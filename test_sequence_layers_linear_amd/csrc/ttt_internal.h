@@ -62,12 +62,33 @@ size_t mlp_generic_lds_bytes(int d, int m, int b);
 hipError_t launch_linear_generic(const LinearArgs& a);
 hipError_t launch_mlp_generic(const MlpArgs& a);
 
+// Sequence-segment split of the TTT-Linear scan.  Each chunk maps the state
+// affinely, W' = (I - eta K^T K) W + eta K^T V, so a run of chunks does too:
+// W_end = M W_start + N.  With nseg > 1 the tokens of a chain are cut into
+// segments of seg_len tokens (a multiple of the chunk size); one launch
+// computes (M, N) of every segment but the last into `maps`
+// ([B H][nseg - 1][2][d][d] fp32), a second one runs every segment's scan from
+// W0 carried through the maps of the segments before it.
+struct SegmentPlan {
+    int nseg = 1;
+    int64_t seg_len = 0;
+    float* maps = nullptr;
+};
+
 // MFMA kernels for the d = 64, b = 16 (and m = 256) shapes: bf16 inputs on
-// bf16 MFMA, fp32 inputs on fp32 MFMA.
+// bf16 MFMA, fp32 inputs on fp32 MFMA.  Per-chunk latencies (us) that size the
+// segment split: forward chunk, map chunk, one map application.
+struct SegmentCosts {
+    double fwd, map, apply;
+};
 bool linear_mfma_supports(const LinearArgs& a);
-hipError_t launch_linear_mfma(const LinearArgs& a);
+hipError_t launch_linear_mfma(const LinearArgs& a, const SegmentPlan& p);
 bool linear_mfma_f32_supports(const LinearArgs& a);
-hipError_t launch_linear_mfma_f32(const LinearArgs& a);
+hipError_t launch_linear_mfma_f32(const LinearArgs& a, const SegmentPlan& p);
+constexpr SegmentCosts kLinearBf16Costs{0.44, 0.30, 0.85};
+constexpr SegmentCosts kLinearF32Costs{1.60, 1.00, 0.85};
+// workgroups of one MFMA linear launch that run at once on one CU
+constexpr int kLinearBlocksPerCu = 2;
 bool mlp_mfma_supports(const MlpArgs& a);
 hipError_t launch_mlp_mfma(const MlpArgs& a);
 

@@ -154,11 +154,50 @@ struct StageRegs {
     u32x4 k, q, v;
 };
 
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// W <- M W + N for this wave's 16 columns in fp32 (M, N: 64 x 64 row-major).
+// 16 fp32 k-steps (mt, r) with k-slot g <-> W row rho(mt, 4g + r), so the B
+// operand is the accumulator register W[mt][r] itself; output tile mo is laid
+// out like W (row m of the A operand is W row rho(mo, m)).
+__device__ __forceinline__ void apply_map(f32x4 (&W)[4], const float* __restrict__ M,
+                                          const float* __restrict__ N, int col, int c, int g)
+{
+    f32x4 acc[4];
+#pragma unroll
+    for (int mo = 0; mo < 4; ++mo)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            acc[mo][r] = N[rho(mo, 4 * g + r) * kD + col];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int k = rho(mt, 4 * g + r);
+#pragma unroll
+            for (int mo = 0; mo < 4; ++mo)
+                acc[mo] = mfma_f32(M[rho(mo, c) * kD + k], W[mt][r], acc[mo]);
+        }
+#pragma unroll
+    for (int mo = 0; mo < 4; ++mo)
+        W[mo] = acc[mo];
+}
+
+// kMaps = false: the scan of segment s of a chain (Y rows of the segment; the
+//   last segment also writes W_out), started from W0 carried through the maps
+//   of segments 0 .. s-1.
+// kMaps = true: the affine map W_end = M W_start + N of segment s < nseg - 1;
+//   block half 0 runs the scan from W = I with V = 0 (giving M), half 1 from
+//   W = 0 with the segment's V (giving N).  No Q, no Y.
+template <bool kMaps>
 __global__ void __launch_bounds__(kThreads, 1)
 linear_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                    const uint16_t* __restrict__ V, const float* W0, int w0_per_batch,
-                   const float* __restrict__ eta, int H, int T,
-                   uint16_t* __restrict__ Y, float* W_out)
+                   const float* __restrict__ eta, int H, int T, int seg_len, int nseg,
+                   float* maps, uint16_t* __restrict__ Y, float* W_out)
 {
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
 
@@ -168,18 +207,42 @@ linear_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     const int g = lane >> 4;
     const int col = 16 * w + c;          // this lane's column of W
 
-    const int64_t u = blockIdx.x;
+    int64_t u;
+    int s, half = 0;
+    if (kMaps) {
+        const int per = 2 * (nseg - 1);
+        u = blockIdx.x / per;
+        s = (blockIdx.x % per) >> 1;
+        half = blockIdx.x & 1;
+    } else {
+        u = blockIdx.x / nseg;
+        s = blockIdx.x % nseg;
+    }
     const int h = static_cast<int>(u % H);
     const float et = eta[h];
-    const float* w0 = W0 + (w0_per_batch ? u : h) * kD * kD;
+    const int t_begin = s * seg_len;
+    const int t_len = min(seg_len, T - t_begin);
+    // map j of chain u: M at maps + (u (nseg - 1) + j) 2 64 64, N right after
+    auto map_ptr = [&](int j) { return maps + ((u * (nseg - 1) + j) * 2) * kD * kD; };
 
     // fast weights: Wacc[mt][r] = W[rho(mt, 4g + r)][col]
     f32x4 Wacc[4];
+    if (kMaps) {
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+        for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            Wacc[mt][r] = w0[rho(mt, 4 * g + r) * kD + col];
+            for (int r = 0; r < 4; ++r)
+                Wacc[mt][r] = (half == 0 && rho(mt, 4 * g + r) == col) ? 1.0f : 0.0f;
+    } else {
+        const float* w0 = W0 + (w0_per_batch ? u : h) * kD * kD;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                Wacc[mt][r] = w0[rho(mt, 4 * g + r) * kD + col];
+        for (int j = 0; j < s; ++j)
+            apply_map(Wacc, map_ptr(j), map_ptr(j) + kD * kD, col, c, g);
+    }
 
     // -I as the B operand of a 16x16x16 product: B[k = 4g + r][n = c] = -(k == n)
     bf16x4 neg_eye;
@@ -187,14 +250,14 @@ linear_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     for (int r = 0; r < 4; ++r)
         neg_eye[r] = static_cast<__bf16>(4 * g + r == c ? -1.0f : 0.0f);
 
-    const int64_t base = u * static_cast<int64_t>(T) * kD;
-    const int64_t chain_bytes = static_cast<int64_t>(T) * kD * 2;
-    const __amdgpu_buffer_rsrc_t rq = chain_rsrc(Q + base, chain_bytes);
-    const __amdgpu_buffer_rsrc_t rk = chain_rsrc(K + base, chain_bytes);
-    const __amdgpu_buffer_rsrc_t rv = chain_rsrc(V + base, chain_bytes);
-    const __amdgpu_buffer_rsrc_t ry = chain_rsrc(Y + base, chain_bytes);
+    const int64_t base = (u * static_cast<int64_t>(T) + t_begin) * kD;
+    const int64_t seg_bytes = static_cast<int64_t>(t_len) * kD * 2;
+    const __amdgpu_buffer_rsrc_t rq = chain_rsrc(Q + base, kMaps ? 0 : seg_bytes);
+    const __amdgpu_buffer_rsrc_t rk = chain_rsrc(K + base, seg_bytes);
+    const __amdgpu_buffer_rsrc_t rv = chain_rsrc(V + base, (kMaps && half == 0) ? 0 : seg_bytes);
+    const __amdgpu_buffer_rsrc_t ry = chain_rsrc(Y + base, kMaps ? 0 : seg_bytes);
 
-    const int nstages = (T + kStageTokens - 1) / kStageTokens;
+    const int nstages = (t_len + kStageTokens - 1) / kStageTokens;
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 
     // staging: this lane's row inside the stage and its 16-byte segment
@@ -203,14 +266,16 @@ linear_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     auto load_stage = [&](StageRegs& o, int stage) {
         const int off = (stage * kStageTokens + st_row) * kRowBytes + st_seg * 16;
         o.k = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
-        o.q = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0);
+        if (!kMaps)
+            o.q = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0);
         o.v = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0);
     };
     auto write_stage = [&](const StageRegs& o, int slot) {
         unsigned char* chunk = lds + slot * kSlotBytes + (st_row >> 4) * kChunkBytes;
         const int r = st_row & 15;
         *reinterpret_cast<u32x4*>(chunk + kOffK + swz(r, st_seg)) = o.k;
-        *reinterpret_cast<u32x4*>(chunk + kOffQ + swz(r, st_seg)) = o.q;
+        if (!kMaps)
+            *reinterpret_cast<u32x4*>(chunk + kOffQ + swz(r, st_seg)) = o.q;
         *reinterpret_cast<u32x4*>(chunk + kOffV + swz(r, st_seg)) = o.v;
         // K^T[i][t] for the 8 input indices of this segment
         const bf16x8 kv = __builtin_bit_cast(bf16x8, o.k);
@@ -228,8 +293,10 @@ linear_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     auto read_ops = [&](ChunkOps& o, const unsigned char* tile) {
         o.ka0 = *reinterpret_cast<const bf16x8*>(tile + kOffK + swz(c, g));
         o.ka1 = *reinterpret_cast<const bf16x8*>(tile + kOffK + swz(c, 4 + g));
-        o.qa0 = *reinterpret_cast<const bf16x8*>(tile + kOffQ + swz(c, g));
-        o.qa1 = *reinterpret_cast<const bf16x8*>(tile + kOffQ + swz(c, 4 + g));
+        if (!kMaps) {
+            o.qa0 = *reinterpret_cast<const bf16x8*>(tile + kOffQ + swz(c, g));
+            o.qa1 = *reinterpret_cast<const bf16x8*>(tile + kOffQ + swz(c, 4 + g));
+        }
         o.vrow = *reinterpret_cast<const bf16x4*>(tile + kOffV + swz(c, 2 * w + (g >> 1)) + 8 * (g & 1));
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
@@ -250,12 +317,6 @@ linear_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
         R = mfma32(o.ka0, b0, R);
         R = mfma32(o.ka1, b1, R);
 
-        // off the chain: S^T = K Q^T, Y^T partial = W_J^T Q^T
-        f32x4 St = mfma32(o.ka0, o.qa0, zero);
-        St = mfma32(o.ka1, o.qa1, St);
-        f32x4 Yt = mfma32(b0, o.qa0, zero);
-        Yt = mfma32(b1, o.qa1, Yt);
-
         // E' = eta (V - K W) = -eta R
         const bf16x4 eb = pack4(-et * R);
 
@@ -264,18 +325,26 @@ linear_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
         for (int mt = 0; mt < 4; ++mt)
             Wacc[mt] = mfma16(o.kt[mt], eb, Wacc[mt]);
 
-        // S^T masked: lane (c = t, g) holds S[t][t' = 4g + r]; keep t' <= t
-        f32x4 Sm;
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-            Sm[r] = (4 * g + r <= c) ? St[r] : 0.f;
-        const bf16x4 sb = pack4(Sm);
-        Yt = mfma16_as32(eb, sb, Yt);
+        if constexpr (!kMaps) {
+            // off the chain: S^T = K Q^T, Y^T partial = W_J^T Q^T
+            f32x4 St = mfma32(o.ka0, o.qa0, zero);
+            St = mfma32(o.ka1, o.qa1, St);
+            f32x4 Yt = mfma32(b0, o.qa0, zero);
+            Yt = mfma32(b1, o.qa1, Yt);
 
-        // Y[t0 + c][16w + 4g .. +3]; rows past T fall outside the buffer.
-        const bf16x4 yb = pack4(Yt);
-        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, yb), ry,
-                                              ((t0 + c) * kD + 16 * w + 4 * g) * 2, 0, 0);
+            // S^T masked: lane (c = t, g) holds S[t][t' = 4g + r]; keep t' <= t
+            f32x4 Sm;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                Sm[r] = (4 * g + r <= c) ? St[r] : 0.f;
+            const bf16x4 sb = pack4(Sm);
+            Yt = mfma16_as32(eb, sb, Yt);
+
+            // Y[t0 + c][16w + 4g .. +3]; rows past the segment fall outside the buffer.
+            const bf16x4 yb = pack4(Yt);
+            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, yb), ry,
+                                                  ((t0 + c) * kD + 16 * w + 4 * g) * 2, 0, 0);
+        }
     };
 
     // Stage s: publish stage s + 1 (held in `next`), then compute stage s.
@@ -321,7 +390,13 @@ linear_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
         }
     }
 
-    float* wo = W_out + u * kD * kD;
+    float* wo;
+    if (kMaps)
+        wo = map_ptr(s) + half * kD * kD;
+    else if (s == nseg - 1)
+        wo = W_out + u * kD * kD;
+    else
+        return;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -338,14 +413,26 @@ bool linear_mfma_supports(const LinearArgs& a)
     return a.dtype == 1 && a.d == kD && a.b == kB && a.T <= max_tokens;
 }
 
-hipError_t launch_linear_mfma(const LinearArgs& a)
+hipError_t launch_linear_mfma(const LinearArgs& a, const SegmentPlan& p)
 {
-    const dim3 grid(static_cast<unsigned>(a.B * a.H)), block(kThreads);
-    hipLaunchKernelGGL(linear_mfma_kernel, grid, block, kLdsBytes, a.stream,
-                       static_cast<const uint16_t*>(a.Q), static_cast<const uint16_t*>(a.K),
-                       static_cast<const uint16_t*>(a.V), a.W0, a.w0_per_batch, a.eta,
-                       static_cast<int>(a.H), static_cast<int>(a.T),
-                       static_cast<uint16_t*>(a.Y), a.W_out);
+    const dim3 block(kThreads);
+    const auto* q = static_cast<const uint16_t*>(a.Q);
+    const auto* k = static_cast<const uint16_t*>(a.K);
+    const auto* v = static_cast<const uint16_t*>(a.V);
+    auto* y = static_cast<uint16_t*>(a.Y);
+    const int H = static_cast<int>(a.H), T = static_cast<int>(a.T);
+    const int seg_len = static_cast<int>(p.seg_len);
+    if (p.nseg > 1) {
+        const dim3 grid(static_cast<unsigned>(a.B * a.H * (p.nseg - 1) * 2));
+        hipLaunchKernelGGL(linear_mfma_kernel<true>, grid, block, kLdsBytes, a.stream, q, k, v,
+                           a.W0, a.w0_per_batch, a.eta, H, T, seg_len, p.nseg, p.maps, y, a.W_out);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+    }
+    const dim3 grid(static_cast<unsigned>(a.B * a.H * p.nseg));
+    hipLaunchKernelGGL(linear_mfma_kernel<false>, grid, block, kLdsBytes, a.stream, q, k, v,
+                       a.W0, a.w0_per_batch, a.eta, H, T, seg_len, p.nseg, p.maps, y, a.W_out);
     return hipGetLastError();
 }
 

@@ -83,11 +83,48 @@ struct StageRegs {
     u32x4 k, q, v;
 };
 
+// Row of W held in register r of accumulator tile mt by lane group g.
+__device__ __forceinline__ int wrow(int mt, int m) { return 16 * (m >> 2) + 4 * mt + (m & 3); }
+
+// W <- M W + N for this wave's 16 columns (M, N: 64 x 64 row-major fp32).
+// 16 k-steps (mt, r) with k-slot g <-> W row wrow(mt, 4g + r), so the B
+// operand is the accumulator register W[mt][r] itself; output tile mt_out is
+// laid out like W (row m of the A operand is W row wrow(mt_out, m)).
+__device__ __forceinline__ void apply_map(f32x4 (&W)[4], const float* __restrict__ M,
+                                          const float* __restrict__ N, int col, int c, int g)
+{
+    f32x4 acc[4];
+#pragma unroll
+    for (int mo = 0; mo < 4; ++mo)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            acc[mo][r] = N[wrow(mo, 4 * g + r) * kD + col];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int k = wrow(mt, 4 * g + r);
+#pragma unroll
+            for (int mo = 0; mo < 4; ++mo)
+                acc[mo] = mfma(M[wrow(mo, c) * kD + k], W[mt][r], acc[mo]);
+        }
+#pragma unroll
+    for (int mo = 0; mo < 4; ++mo)
+        W[mo] = acc[mo];
+}
+
+// kMaps = false: the scan of segment s of a chain (Y rows of the segment; the
+//   last segment also writes W_out), started from W0 carried through the maps
+//   of segments 0 .. s-1.
+// kMaps = true: the affine map W_end = M W_start + N of segment s < nseg - 1;
+//   block half 0 runs the scan from W = I with V = 0 (giving M), half 1 from
+//   W = 0 with the segment's V (giving N).  No Y.
+template <bool kMaps>
 __global__ void __launch_bounds__(kThreads, 1)
 linear_mfma_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                        const float* __restrict__ V, const float* W0, int w0_per_batch,
-                       const float* __restrict__ eta, int H, int T,
-                       float* __restrict__ Y, float* W_out)
+                       const float* __restrict__ eta, int H, int T, int seg_len, int nseg,
+                       float* maps, float* __restrict__ Y, float* W_out)
 {
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
 
@@ -97,27 +134,51 @@ linear_mfma_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
     const int g = lane >> 4;
     const int col = 16 * w + c;
 
-    const int64_t u = blockIdx.x;
+    int64_t u;
+    int s, half = 0;
+    if (kMaps) {
+        const int per = 2 * (nseg - 1);
+        u = blockIdx.x / per;
+        s = (blockIdx.x % per) >> 1;
+        half = blockIdx.x & 1;
+    } else {
+        u = blockIdx.x / nseg;
+        s = blockIdx.x % nseg;
+    }
     const int h = static_cast<int>(u % H);
     const float et = eta[h];
-    const float* w0 = W0 + (w0_per_batch ? u : h) * kD * kD;
+    const int t_begin = s * seg_len;
+    const int t_len = min(seg_len, T - t_begin);
+    // map j of chain u: M at maps + (u (nseg - 1) + j) 2 64 64, N right after
+    auto map_ptr = [&](int j) { return maps + ((u * (nseg - 1) + j) * 2) * kD * kD; };
 
     // Wacc[mt][r] = W[16g + 4mt + r][col]
     f32x4 Wacc[4];
+    if (kMaps) {
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+        for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            Wacc[mt][r] = w0[(16 * g + 4 * mt + r) * kD + col];
+            for (int r = 0; r < 4; ++r)
+                Wacc[mt][r] = (half == 0 && wrow(mt, 4 * g + r) == col) ? 1.0f : 0.0f;
+    } else {
+        const float* w0 = W0 + (w0_per_batch ? u : h) * kD * kD;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                Wacc[mt][r] = w0[wrow(mt, 4 * g + r) * kD + col];
+        for (int j = 0; j < s; ++j)
+            apply_map(Wacc, map_ptr(j), map_ptr(j) + kD * kD, col, c, g);
+    }
 
-    const int64_t base = u * static_cast<int64_t>(T) * kD;
-    const int64_t chain_bytes = static_cast<int64_t>(T) * kD * 4;
-    const __amdgpu_buffer_rsrc_t rq = chain_rsrc(Q + base, chain_bytes);
-    const __amdgpu_buffer_rsrc_t rk = chain_rsrc(K + base, chain_bytes);
-    const __amdgpu_buffer_rsrc_t rv = chain_rsrc(V + base, chain_bytes);
-    const __amdgpu_buffer_rsrc_t ry = chain_rsrc(Y + base, chain_bytes);
+    const int64_t base = (u * static_cast<int64_t>(T) + t_begin) * kD;
+    const int64_t seg_bytes = static_cast<int64_t>(t_len) * kD * 4;
+    const __amdgpu_buffer_rsrc_t rq = chain_rsrc(Q + base, kMaps ? 0 : seg_bytes);
+    const __amdgpu_buffer_rsrc_t rk = chain_rsrc(K + base, seg_bytes);
+    const __amdgpu_buffer_rsrc_t rv = chain_rsrc(V + base, (kMaps && half == 0) ? 0 : seg_bytes);
+    const __amdgpu_buffer_rsrc_t ry = chain_rsrc(Y + base, kMaps ? 0 : seg_bytes);
 
-    const int nchunks = (T + kB - 1) / kB;
+    const int nchunks = (t_len + kB - 1) / kB;
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 
     // staging: lane l of wave w holds row 4w + l / 16, 16-byte segment l % 16
@@ -126,13 +187,15 @@ linear_mfma_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
     auto load_stage = [&](StageRegs& o, int chunk) {
         const int off = (chunk * kB + st_row) * kRowBytes + st_seg * 16;
         o.k = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
-        o.q = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0);
+        if (!kMaps)
+            o.q = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0);
         o.v = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0);
     };
     auto write_stage = [&](const StageRegs& o, int slot) {
         unsigned char* sl = lds + slot * kSlotBytes;
         *reinterpret_cast<u32x4*>(sl + kOffK + swz_row(st_row, st_seg)) = o.k;
-        *reinterpret_cast<u32x4*>(sl + kOffQ + swz_row(st_row, st_seg)) = o.q;
+        if (!kMaps)
+            *reinterpret_cast<u32x4*>(sl + kOffQ + swz_row(st_row, st_seg)) = o.q;
         // transposed copies: element e of this segment is index 4 st_seg + e;
         // token st_row sits at position st_row % 4 of 16-byte segment st_row / 4
 #pragma unroll
@@ -153,7 +216,8 @@ linear_mfma_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
             o.k[x] = *reinterpret_cast<const f32x4*>(sl + kOffK + swz_row(c, 4 * g + x));
-            o.q[x] = *reinterpret_cast<const f32x4*>(sl + kOffQ + swz_row(c, 4 * g + x));
+            if (!kMaps)
+                o.q[x] = *reinterpret_cast<const f32x4*>(sl + kOffQ + swz_row(c, 4 * g + x));
         }
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
@@ -178,12 +242,12 @@ linear_mfma_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
             for (int r = 0; r < 4; ++r) {
                 // k-step ks = 4x + r: i = 16g + ks, W operand Wacc[x][r]
                 R[r] = mfma(o.k[x][r], Wacc[x][r], R[r]);
-                St[r] = mfma(o.k[x][r], o.q[x][r], St[r]);
-                Yt[r] = mfma(Wacc[x][r], o.q[x][r], Yt[r]);
+                if constexpr (!kMaps) {
+                    St[r] = mfma(o.k[x][r], o.q[x][r], St[r]);
+                    Yt[r] = mfma(Wacc[x][r], o.q[x][r], Yt[r]);
+                }
             }
         const f32x4 Rs = (R[0] + R[1]) + (R[2] + R[3]);
-        f32x4 S = (St[0] + St[1]) + (St[2] + St[3]);
-        f32x4 Ys = (Yt[0] + Yt[1]) + (Yt[2] + Yt[3]);
 
         // E' = -eta R: lane (c = j, g) holds E'[t = 4g + q][j]
         const f32x4 Ep = -et * Rs;
@@ -195,19 +259,23 @@ linear_mfma_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
             for (int qq = 0; qq < 4; ++qq)
                 Wacc[mt] = mfma(o.kt[mt][qq], Ep[qq], Wacc[mt]);
 
-        // S^T masked: lane (c = t, g) holds S[t][t' = 4g + q]; keep t' <= t
+        if constexpr (!kMaps) {
+            f32x4 S = (St[0] + St[1]) + (St[2] + St[3]);
+            const f32x4 Ys = (Yt[0] + Yt[1]) + (Yt[2] + Yt[3]);
+            // S^T masked: lane (c = t, g) holds S[t][t' = 4g + q]; keep t' <= t
 #pragma unroll
-        for (int qq = 0; qq < 4; ++qq)
-            S[qq] = (4 * g + qq <= c) ? S[qq] : 0.f;
-        f32x4 Y2 = zero;
+            for (int qq = 0; qq < 4; ++qq)
+                S[qq] = (4 * g + qq <= c) ? S[qq] : 0.f;
+            f32x4 Y2 = zero;
 #pragma unroll
-        for (int qq = 0; qq < 4; ++qq)
-            Y2 = mfma(Ep[qq], S[qq], Y2);
-        const f32x4 Yv = Ys + Y2;
+            for (int qq = 0; qq < 4; ++qq)
+                Y2 = mfma(Ep[qq], S[qq], Y2);
+            const f32x4 Yv = Ys + Y2;
 
-        // Y[t0 + c][16w + 4g .. +3]; rows past T fall outside the buffer
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, Yv), ry,
-                                               ((t0 + c) * kD + 16 * w + 4 * g) * 4, 0, 0);
+            // Y[t0 + c][16w + 4g .. +3]; rows past the segment fall outside the buffer
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, Yv), ry,
+                                                   ((t0 + c) * kD + 16 * w + 4 * g) * 4, 0, 0);
+        }
     };
 
     auto process = [&](const StageRegs& next, int chunk, int slot) {
@@ -248,12 +316,18 @@ linear_mfma_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
         }
     }
 
-    float* wo = W_out + u * kD * kD;
+    float* wo;
+    if (kMaps)
+        wo = map_ptr(s) + half * kD * kD;
+    else if (s == nseg - 1)
+        wo = W_out + u * kD * kD;
+    else
+        return;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-            wo[(16 * g + 4 * mt + r) * kD + col] = Wacc[mt][r];
+            wo[wrow(mt, 4 * g + r) * kD + col] = Wacc[mt][r];
 }
 
 }  // namespace
@@ -264,14 +338,26 @@ bool linear_mfma_f32_supports(const LinearArgs& a)
     return a.dtype == 0 && a.d == kD && a.b == kB && a.T <= max_tokens;
 }
 
-hipError_t launch_linear_mfma_f32(const LinearArgs& a)
+hipError_t launch_linear_mfma_f32(const LinearArgs& a, const SegmentPlan& p)
 {
-    const dim3 grid(static_cast<unsigned>(a.B * a.H)), block(kThreads);
-    hipLaunchKernelGGL(linear_mfma_f32_kernel, grid, block, kLdsBytes, a.stream,
-                       static_cast<const float*>(a.Q), static_cast<const float*>(a.K),
-                       static_cast<const float*>(a.V), a.W0, a.w0_per_batch, a.eta,
-                       static_cast<int>(a.H), static_cast<int>(a.T),
-                       static_cast<float*>(a.Y), a.W_out);
+    const dim3 block(kThreads);
+    const auto* q = static_cast<const float*>(a.Q);
+    const auto* k = static_cast<const float*>(a.K);
+    const auto* v = static_cast<const float*>(a.V);
+    auto* y = static_cast<float*>(a.Y);
+    const int H = static_cast<int>(a.H), T = static_cast<int>(a.T);
+    const int seg_len = static_cast<int>(p.seg_len);
+    if (p.nseg > 1) {
+        const dim3 grid(static_cast<unsigned>(a.B * a.H * (p.nseg - 1) * 2));
+        hipLaunchKernelGGL(linear_mfma_f32_kernel<true>, grid, block, kLdsBytes, a.stream, q, k, v,
+                           a.W0, a.w0_per_batch, a.eta, H, T, seg_len, p.nseg, p.maps, y, a.W_out);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+    }
+    const dim3 grid(static_cast<unsigned>(a.B * a.H * p.nseg));
+    hipLaunchKernelGGL(linear_mfma_f32_kernel<false>, grid, block, kLdsBytes, a.stream, q, k, v,
+                       a.W0, a.w0_per_batch, a.eta, H, T, seg_len, p.nseg, p.maps, y, a.W_out);
     return hipGetLastError();
 }
 

@@ -164,9 +164,11 @@ def test_deterministic(cfg):
 
 
 @pytest.mark.parametrize("cfg", [2, 3])
-def test_chaining_through_state_is_exact(cfg):
+def test_chaining_through_state_is_exact(cfg, monkeypatch):
     """forward(T) == forward(T1) then forward(T2) from W_out (T1 mod b == 0):
-    the fp32 state is stored and reloaded exactly."""
+    the fp32 state is stored and reloaded exactly (one segment per chain: a
+    segmented scan composes the same updates in another order)."""
+    monkeypatch.setenv("TTT_LINEAR_SEGMENTS", "1")
     w = CONFIGS[cfg].with_(B=2, H=3, T=160)
     g = to_gpu(make_inputs(w, 31))
     Y, W = linear_gpu(g, 16)
@@ -218,3 +220,46 @@ def test_nan_propagates():
     Y, W = linear_gpu(to_gpu(inp), 16)
     assert torch.isfinite(Y[0, 0].float()).all() and torch.isfinite(W[0, 0]).all()
     assert torch.isnan(W[0, 1]).any()
+
+
+# ---------------------------------------------------------------------------
+# sequence-segment scan: each segment maps its start state affinely, so the
+# chain is cut into segments whose maps are composed (forced segment counts;
+# the benchmark workloads above use the library's own choice)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("cfg", [2, 3])
+@pytest.mark.parametrize("T,S,per_batch", [(100, 2, False), (333, 3, True), (1000, 7, False),
+                                           (100, 50, True), (512, 4, False), (48, 3, False)])
+def test_segmented_scan(cfg, T, S, per_batch, monkeypatch):
+    monkeypatch.setenv("TTT_LINEAR_SEGMENTS", str(S))
+    w = CONFIGS[cfg].with_(B=2, H=3, T=T, w0=("normal", 0.3), eta=("uniform", 0.01, 0.1))
+    announce("linear segmented", cfg, T, S, per_batch)
+    _check(make_inputs(w, 400 + T + S, w0_per_batch=per_batch), 16, w.dtype)
+
+
+@pytest.mark.parametrize("cfg", [2, 3])
+def test_segmented_in_place_and_deterministic(cfg, monkeypatch):
+    """W_out == W0 with several segments: the later segments still start from
+    the original W0; repeated calls agree bit for bit."""
+    monkeypatch.setenv("TTT_LINEAR_SEGMENTS", "4")
+    w = CONFIGS[cfg].with_(B=2, H=3, T=300)
+    g = to_gpu(make_inputs(w, 71, w0_per_batch=True))
+    Y_ref, W_ref = linear_gpu(g, 16)
+    Y_again, W_again = linear_gpu(g, 16)
+    assert torch.equal(Y_ref, Y_again) and torch.equal(W_ref, W_again)
+    state = g["W0"].clone()
+    Y, W = ttt.ttt_linear_forward(g["Q"], g["K"], g["V"], state, g["eta"], 16, W_out=state)
+    torch.cuda.synchronize()
+    assert torch.equal(Y, Y_ref) and torch.equal(state, W_ref)
+
+
+def test_segmented_close_to_single_segment(monkeypatch):
+    """fp32: the composed maps change only the rounding order."""
+    w = CONFIGS[2].with_(B=1, H=4, T=1024, w0=("normal", 0.3))
+    g = to_gpu(make_inputs(w, 81))
+    monkeypatch.setenv("TTT_LINEAR_SEGMENTS", "1")
+    Y1, W1 = linear_gpu(g, 16)
+    monkeypatch.setenv("TTT_LINEAR_SEGMENTS", "16")
+    Y16, W16 = linear_gpu(g, 16)
+    assert rel_l2(Y16, Y1.double().cpu().numpy()) <= 2e-6
+    assert rel_l2(W16, W1.double().cpu().numpy()) <= 2e-6
