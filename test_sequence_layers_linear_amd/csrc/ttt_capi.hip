@@ -8,6 +8,7 @@
 
 #include <stdlib.h>
 
+#include <algorithm>
 #include <atomic>
 #include <mutex>
 #include <vector>
@@ -67,33 +68,40 @@ int device_cus()
     return n;
 }
 
-// Segment count for a chain-parallel scan of `units` chains of T tokens:
-// minimises ceil(chunks / S) (fwd + map) + (S - 1) apply while both launches
-// fit on the device at once.
-// TTT_LINEAR_SEGMENTS=S (S >= 1) forces S segments (at least one chunk
-// each), for tests and tuning.
+// Segment count for a chain-parallel scan of `units` chains of T tokens.
+// Model (us): a launch of n workgroups runs them all at once when
+// n <= 2 CUs, each one slowed by max(1, n / CUs) (two workgroups share a CU);
+//   S = 1:  chunks fwd f(units)
+//   S > 1:  c (map f(2 units (S - 1)) + fwd f(units S)) + (S - 1) apply + extra
+// with c = ceil(chunks / S) and `extra` the two additional launches.
+// TTT_LINEAR_SEGMENTS=S (1 <= S <= kMaxSegments) forces S segments (at least
+// one chunk each), for tests and tuning.
 ttt::SegmentPlan plan_segments(int64_t units, int64_t T, int chunk, const ttt::SegmentCosts& cost)
 {
     ttt::SegmentPlan p;
     p.seg_len = T;
     const int64_t chunks = (T + chunk - 1) / chunk;
     if (const char* env = getenv("TTT_LINEAR_SEGMENTS")) {
-        const long S = strtol(env, nullptr, 10);
+        const long S = std::min<long>(strtol(env, nullptr, 10), ttt::kMaxSegments);
         if (S >= 1 && chunks > 0) {
             p.seg_len = ((chunks + S - 1) / S) * chunk;
             p.nseg = static_cast<int>((T + p.seg_len - 1) / p.seg_len);
             return p;
         }
     }
-    const int64_t cap = static_cast<int64_t>(device_cus()) * ttt::kLinearBlocksPerCu;
-    if (cap <= 0 || units * 2 > cap || chunks < 4) return p;
-    double best = static_cast<double>(chunks) * cost.fwd;
+    const int64_t cus = device_cus();
+    const int64_t cap = cus * ttt::kLinearBlocksPerCu;
+    if (cus <= 0 || units >= cus || chunks < 4) return p;
+    auto slow = [&](int64_t n) { return n > cus ? static_cast<double>(n) / cus : 1.0; };
+    double best = static_cast<double>(chunks) * cost.fwd * slow(units);
     int best_s = 1;
-    for (int S = 2; S <= 64; ++S) {
-        if (units * S > cap || units * (S - 1) * 2 > cap) break;
+    for (int S = 2; S <= ttt::kMaxSegments; ++S) {
+        const int64_t maps = units * (S - 1) * 2, fwd = units * S;
+        if (maps > cap || fwd > cap) break;
         const int64_t per = (chunks + S - 1) / S;
         if (per < 2) break;
-        const double t = per * (cost.fwd + cost.map) + (S - 1) * cost.apply;
+        const double t = per * (cost.map * slow(maps) + cost.fwd * slow(fwd)) +
+                         (S - 1) * cost.apply + cost.launch;
         if (t < best) { best = t; best_s = S; }
     }
     if (best_s > 1) {
@@ -150,8 +158,10 @@ hipError_t workspace_get(void** ptr, size_t bytes, hipStream_t stream)
     return hipSuccess;
 }
 
-// Runs a segmented MFMA linear scan: workspace for the maps (and a copy of
-// W0 when W_out overwrites it), then both launches.
+// Runs a segmented MFMA linear scan: workspace for the maps and the segment
+// start states, then the launches.  The start states (including the copy of
+// W0 for the first segment) are complete before any segment writes W_out, so
+// W_out may overwrite W0.
 int run_linear_segmented(LinearArgs a, ttt::SegmentPlan p,
                          hipError_t (*launch)(const LinearArgs&, const ttt::SegmentPlan&))
 {
@@ -159,22 +169,12 @@ int run_linear_segmented(LinearArgs a, ttt::SegmentPlan p,
     const int64_t units = a.B * a.H;
     const size_t state = static_cast<size_t>(a.d) * a.d * sizeof(float);
     const size_t map_bytes = static_cast<size_t>(units) * (p.nseg - 1) * 2 * state;
-    const int64_t w0_units = a.w0_per_batch ? units : a.H;
-    const bool in_place = reinterpret_cast<uintptr_t>(a.W_out) < reinterpret_cast<uintptr_t>(a.W0) + w0_units * state &&
-                          reinterpret_cast<uintptr_t>(a.W0) < reinterpret_cast<uintptr_t>(a.W_out) + units * state;
-    const size_t copy_bytes = in_place ? static_cast<size_t>(w0_units) * state : 0;
+    const size_t start_bytes = static_cast<size_t>(units) * p.nseg * state;
     void* ws = nullptr;
-    hipError_t e = workspace_get(&ws, map_bytes + copy_bytes, a.stream);
-    if (e != hipSuccess) return TTT_ERR_HIP;
+    if (workspace_get(&ws, map_bytes + start_bytes, a.stream) != hipSuccess) return TTT_ERR_HIP;
     p.maps = static_cast<float*>(ws);
-    if (in_place) {
-        // the last segment writes W_out while other segments may still read W0
-        float* w0c = p.maps + map_bytes / sizeof(float);
-        e = hipMemcpyAsync(w0c, a.W0, copy_bytes, hipMemcpyDeviceToDevice, a.stream);
-        a.W0 = w0c;
-    }
-    if (e == hipSuccess) e = launch(a, p);
-    return hip_status(e);
+    p.wstart = p.maps + map_bytes / sizeof(float);
+    return hip_status(launch(a, p));
 }
 
 }  // namespace

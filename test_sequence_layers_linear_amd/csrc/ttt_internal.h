@@ -67,26 +67,33 @@ hipError_t launch_mlp_generic(const MlpArgs& a);
 // W_end = M W_start + N.  With nseg > 1 the tokens of a chain are cut into
 // segments of seg_len tokens (a multiple of the chunk size); one launch
 // computes (M, N) of every segment but the last into `maps`
-// ([B H][nseg - 1][2][d][d] fp32), a second one runs every segment's scan from
-// W0 carried through the maps of the segments before it.
+// ([B H][nseg - 1][2][d][d] fp32), a second composes them into the start
+// state of every segment (`wstart`, [B H][nseg][d][d], wstart[.][0] = W0),
+// and a third runs every segment's scan from its start state.
 struct SegmentPlan {
     int nseg = 1;
     int64_t seg_len = 0;
     float* maps = nullptr;
+    float* wstart = nullptr;
 };
+hipError_t launch_linear_combine(const LinearArgs& a, const SegmentPlan& p);
+size_t linear_combine_lds_bytes(int nseg);
+// most segments per chain (the combine step keeps every start state in LDS)
+constexpr int kMaxSegments = 30;   // with the ring's spare slots: 36 x 4352 B of LDS
 
 // MFMA kernels for the d = 64, b = 16 (and m = 256) shapes: bf16 inputs on
-// bf16 MFMA, fp32 inputs on fp32 MFMA.  Per-chunk latencies (us) that size the
-// segment split: forward chunk, map chunk, one map application.
+// bf16 MFMA, fp32 inputs on fp32 MFMA.  Latencies (us) that size the segment
+// split: forward chunk, map chunk, one step of the start-state composition,
+// and the fixed cost of the two extra launches.
 struct SegmentCosts {
-    double fwd, map, apply;
+    double fwd, map, apply, launch;
 };
 bool linear_mfma_supports(const LinearArgs& a);
 hipError_t launch_linear_mfma(const LinearArgs& a, const SegmentPlan& p);
 bool linear_mfma_f32_supports(const LinearArgs& a);
 hipError_t launch_linear_mfma_f32(const LinearArgs& a, const SegmentPlan& p);
-constexpr SegmentCosts kLinearBf16Costs{0.44, 0.30, 0.85};
-constexpr SegmentCosts kLinearF32Costs{1.60, 1.00, 0.85};
+constexpr SegmentCosts kLinearBf16Costs{0.39, 0.30, 0.70, 11.0};
+constexpr SegmentCosts kLinearF32Costs{1.45, 1.00, 0.70, 11.0};
 // workgroups of one MFMA linear launch that run at once on one CU
 constexpr int kLinearBlocksPerCu = 2;
 bool mlp_mfma_supports(const MlpArgs& a);

@@ -154,41 +154,9 @@ struct StageRegs {
     u32x4 k, q, v;
 };
 
-__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c)
-{
-    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
-
-// W <- M W + N for this wave's 16 columns in fp32 (M, N: 64 x 64 row-major).
-// 16 fp32 k-steps (mt, r) with k-slot g <-> W row rho(mt, 4g + r), so the B
-// operand is the accumulator register W[mt][r] itself; output tile mo is laid
-// out like W (row m of the A operand is W row rho(mo, m)).
-__device__ __forceinline__ void apply_map(f32x4 (&W)[4], const float* __restrict__ M,
-                                          const float* __restrict__ N, int col, int c, int g)
-{
-    f32x4 acc[4];
-#pragma unroll
-    for (int mo = 0; mo < 4; ++mo)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-            acc[mo][r] = N[rho(mo, 4 * g + r) * kD + col];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int k = rho(mt, 4 * g + r);
-#pragma unroll
-            for (int mo = 0; mo < 4; ++mo)
-                acc[mo] = mfma_f32(M[rho(mo, c) * kD + k], W[mt][r], acc[mo]);
-        }
-#pragma unroll
-    for (int mo = 0; mo < 4; ++mo)
-        W[mo] = acc[mo];
-}
-
 // kMaps = false: the scan of segment s of a chain (Y rows of the segment; the
-//   last segment also writes W_out), started from W0 carried through the maps
-//   of segments 0 .. s-1.
+//   last segment also writes W_out), started from W0 (one segment) or from
+//   the segment's start state in wstart.
 // kMaps = true: the affine map W_end = M W_start + N of segment s < nseg - 1;
 //   block half 0 runs the scan from W = I with V = 0 (giving M), half 1 from
 //   W = 0 with the segment's V (giving N).  No Q, no Y.
@@ -197,7 +165,7 @@ __global__ void __launch_bounds__(kThreads, 1)
 linear_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                    const uint16_t* __restrict__ V, const float* W0, int w0_per_batch,
                    const float* __restrict__ eta, int H, int T, int seg_len, int nseg,
-                   float* maps, uint16_t* __restrict__ Y, float* W_out)
+                   float* maps, const float* wstart, uint16_t* __restrict__ Y, float* W_out)
 {
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
 
@@ -234,14 +202,13 @@ linear_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
             for (int r = 0; r < 4; ++r)
                 Wacc[mt][r] = (half == 0 && rho(mt, 4 * g + r) == col) ? 1.0f : 0.0f;
     } else {
-        const float* w0 = W0 + (w0_per_batch ? u : h) * kD * kD;
+        const float* w0 = nseg > 1 ? wstart + (u * nseg + s) * kD * kD
+                                   : W0 + (w0_per_batch ? u : h) * kD * kD;
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 Wacc[mt][r] = w0[rho(mt, 4 * g + r) * kD + col];
-        for (int j = 0; j < s; ++j)
-            apply_map(Wacc, map_ptr(j), map_ptr(j) + kD * kD, col, c, g);
     }
 
     // -I as the B operand of a 16x16x16 product: B[k = 4g + r][n = c] = -(k == n)
@@ -376,19 +343,26 @@ linear_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
                 load_stage(setB[p], s0 + kSet + 1 + p);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int p = 0; p < kSet; ++p)
+            for (int p = 0; p < kSet; ++p) {
+                if (s0 + p >= nstages)       // uniform: the scan is done
+                    goto done;
                 process(setA[p], s0 + p, p % kSlots);
+            }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int p = 0; p < kSet; ++p)
                 load_stage(setA[p], s0 + 2 * kSet + 1 + p);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int p = 0; p < kSet; ++p)
+            for (int p = 0; p < kSet; ++p) {
+                if (s0 + kSet + p >= nstages)
+                    goto done;
                 process(setB[p], s0 + kSet + p, (kSet + p) % kSlots);
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
     }
+done:
 
     float* wo;
     if (kMaps)
@@ -425,14 +399,18 @@ hipError_t launch_linear_mfma(const LinearArgs& a, const SegmentPlan& p)
     if (p.nseg > 1) {
         const dim3 grid(static_cast<unsigned>(a.B * a.H * (p.nseg - 1) * 2));
         hipLaunchKernelGGL(linear_mfma_kernel<true>, grid, block, kLdsBytes, a.stream, q, k, v,
-                           a.W0, a.w0_per_batch, a.eta, H, T, seg_len, p.nseg, p.maps, y, a.W_out);
-        const hipError_t e = hipGetLastError();
+                           a.W0, a.w0_per_batch, a.eta, H, T, seg_len, p.nseg, p.maps, p.wstart, y,
+                           a.W_out);
+        hipError_t e = hipGetLastError();
+        if (e == hipSuccess)
+            e = launch_linear_combine(a, p);
         if (e != hipSuccess)
             return e;
     }
     const dim3 grid(static_cast<unsigned>(a.B * a.H * p.nseg));
     hipLaunchKernelGGL(linear_mfma_kernel<false>, grid, block, kLdsBytes, a.stream, q, k, v,
-                       a.W0, a.w0_per_batch, a.eta, H, T, seg_len, p.nseg, p.maps, y, a.W_out);
+                       a.W0, a.w0_per_batch, a.eta, H, T, seg_len, p.nseg, p.maps, p.wstart, y,
+                       a.W_out);
     return hipGetLastError();
 }
 
