@@ -14,8 +14,11 @@ Unless --quick is given, the other d = 64 workloads are measured too and
 reported under "workloads" in the same line.
 
 roofline.achieved = algorithmic bytes (HBM bound) or flops (MFMA bound) of
-one launch of the dominant kernel / its mean duration from HIP events
-recorded on the launch stream around every launch in the timed region.
+one forward call / its mean duration from HIP events recorded on the launch
+stream around every call in the timed region.  A call is one kernel launch,
+except a segmented TTT-Linear scan: maps, start-state composition and
+segment scans, three launches back to back on the stream (roofline.kernel
+names them).  The decode steps of a workload run as one captured HIP graph.
 cpu_baseline = the fp64 oracle (plain loops, OpenMP over chains) timed on
 this host's cores on a bounded sample of the same workload.
 """
@@ -37,8 +40,11 @@ PEAK_HBM = 8.0e12            # bytes/s, MI355X HBM3E
 PEAK_FLOPS = {"bf16": 2.5e15, "fp32": 157.3e12}   # dense MFMA
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = {
-    "linear_mfma_kernel": "ttt_linear_mfma.hip",
-    "linear_mfma_f32_kernel": "ttt_linear_mfma_f32.hip",
+    "linear_mfma_kernel[scan]": "ttt_linear_mfma.hip",
+    "linear_mfma_kernel[maps]": "ttt_linear_mfma.hip",
+    "linear_mfma_f32_kernel[scan]": "ttt_linear_mfma_f32.hip",
+    "linear_mfma_f32_kernel[maps]": "ttt_linear_mfma_f32.hip",
+    "linear_combine_kernel": "ttt_linear_combine.hip",
     "linear_generic_kernel": "ttt_generic.hip",
     "mlp_generic_kernel": "ttt_generic.hip",
     "mlp_mfma_kernel": "ttt_mlp_mfma.hip",
@@ -77,13 +83,25 @@ def decode_work(w):
     return units * 6 * d * d, units * (2 * d * d * 4 + 4 * d * s)
 
 
-def kernel_name(w):
+def kernel_names(w, nseg):
+    """Kernels one forward call dispatches (segmented TTT-Linear: the maps
+    launch, the start-state composition and the segment scans)."""
     if w.kind == "mlp":
-        return "mlp_mfma_kernel" if (w.dtype == "bf16" and w.d == 64 and w.m == 256 and w.b == 16) \
-            else "mlp_generic_kernel"
+        return ["mlp_mfma_kernel" if (w.dtype == "bf16" and w.d == 64 and w.m == 256 and w.b == 16)
+                else "mlp_generic_kernel"]
     if w.d == 64 and w.b == 16:
-        return "linear_mfma_kernel" if w.dtype == "bf16" else "linear_mfma_f32_kernel"
-    return "linear_generic_kernel"
+        k = "linear_mfma_kernel" if w.dtype == "bf16" else "linear_mfma_f32_kernel"
+        return [k + "[maps]", "linear_combine_kernel", k + "[scan]"] if nseg > 1 else [k + "[scan]"]
+    return ["linear_generic_kernel"]
+
+
+def segments(w):
+    if w.kind != "linear":
+        return 1
+    import torch
+    import test_sequence_layers_linear_amd as ttt
+    return ttt.ttt_linear_segments(w.B, w.H, w.T, w.d, w.b,
+                                   torch.float32 if w.dtype == "fp32" else torch.bfloat16)
 
 
 def source_sha(kernel):
@@ -91,22 +109,27 @@ def source_sha(kernel):
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
 
-def stored_traffic(kernel, workload):
-    """HBM bytes per launch from committed rocprofv3 --pmc summaries, if they
-    were taken on the current source of the kernel; else None."""
+def stored_traffic(kernels, workload):
+    """HBM bytes of one forward call (summed over its kernels) from committed
+    rocprofv3 --pmc summaries, if every kernel's figure was taken on its
+    current source; else None."""
     path = os.path.join(PROFILES, "traffic.json")
     if not os.path.exists(path):
         return None
     try:
-        rec = json.load(open(path)).get(kernel, {}).get(workload)
+        table = json.load(open(path))
     except (ValueError, OSError):
         return None
-    if not rec or rec.get("source_sha") != source_sha(kernel):
-        return None
-    return rec.get("bytes_per_launch")
+    total = 0
+    for k in kernels:
+        rec = table.get(k, {}).get(workload)
+        if not rec or rec.get("source_sha") != source_sha(k):
+            return None
+        total += rec.get("bytes_per_launch", 0)
+    return total
 
 
-def roofline(w, flops, nbytes, seconds, kernel):
+def roofline(w, flops, nbytes, seconds, kernels):
     dt = "bf16" if w.dtype == "bf16" else "fp32"
     ridge = PEAK_FLOPS[dt] / PEAK_HBM
     if flops / nbytes > ridge:
@@ -114,8 +137,8 @@ def roofline(w, flops, nbytes, seconds, kernel):
     else:
         ach, peak, unit, bound = nbytes / seconds / 1e9, PEAK_HBM / 1e9, "GB/s", "hbm"
     return {"bound": bound, "achieved": round(ach, 3), "peak": peak, "unit": unit,
-            "frac": round(ach / peak, 5), "traffic": stored_traffic(kernel, w.name),
-            "kernel": kernel, "mean_launch_us": round(seconds * 1e6, 3),
+            "frac": round(ach / peak, 5), "traffic": stored_traffic(kernels, w.name),
+            "kernel": " + ".join(kernels), "mean_launch_us": round(seconds * 1e6, 3),
             "algorithmic_flops": flops, "algorithmic_bytes": nbytes,
             "active_cu_ceiling": round(min(1.0, w.B * w.H / 256), 4)}
 
@@ -152,14 +175,36 @@ class Runner:
             ttt.ttt_mlp_forward(g["Q"], g["K"], g["V"], g["W1"], g["W2"], g["eta"], self.w.b,
                                 Y=self.Y, W1_out=self.W1, W2_out=self.W2)
 
-    def decode(self):
+    def decode_eager(self):
         g, ttt = self.g, self.ttt
         for s in range(self.w.decode_steps):
             ttt.ttt_linear_decode_step(g["dq"][s], g["dk"][s], g["dv"][s], self.W, g["eta"],
                                        y=self.y)
 
+    def capture_decode(self):
+        """The decode steps as one HIP graph (one launch per token, replayed
+        as a unit), so that a token costs its kernel rather than a host call."""
+        torch = self.torch
+        self.graph = None
+        if not self.w.decode_steps:
+            return
+        self.decode_eager()                  # warm the launch path
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            self.decode_eager()
+        torch.cuda.synchronize()
+        self.graph = graph
+
+    def decode(self):
+        if getattr(self, "graph", None) is not None:
+            self.graph.replay()
+        else:
+            self.decode_eager()
+
     def measure(self, steps, warmup):
         torch = self.torch
+        self.capture_decode()
         for _ in range(warmup):
             self.forward()
             self.decode()
@@ -254,8 +299,10 @@ def measure_workload(cfg, steps, warmup, cold_reps):
     r = Runner(w, default_seed(cfg))
     per_step, fwd, dec = r.measure(steps, warmup)
     flops, nbytes = (linear_work if w.kind == "linear" else mlp_work)(w)
-    kern = kernel_name(w)
+    nseg = segments(w)
+    kern = kernel_names(w, nseg)
     out = {"workload": w.name, "config": cfg, "tokens_per_s": w.B * w.T / per_step,
+           "segments_per_chain": nseg,
            "ms_per_step": per_step * 1e3, "forward_us": fwd * 1e6,
            "forward_tokens_per_s": w.B * w.T / fwd,
            "roofline": roofline(w, flops, nbytes, fwd, kern)}
@@ -267,6 +314,7 @@ def measure_workload(cfg, steps, warmup, cold_reps):
         df, db = decode_work(w)
         per = dec / w.decode_steps
         out["decode"] = {"steps": w.decode_steps, "us_per_step": per * 1e6,
+                         "hip_graph": r.graph is not None,
                          "GB_per_s": db / per / 1e9, "hbm_frac": db / per / PEAK_HBM,
                          "bytes_per_step": db}
     return w, r, out
@@ -323,7 +371,10 @@ def main():
         "data": "synthetic (seeded Gaussian Q/K/V, see inputs.py)",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "d": w.d, "b": w.b,
                    "m": w.m or None, "decode_steps": w.decode_steps, "global_batch": w.B,
-                   "seq_len": w.T, "parallelism": "none (one GPU; one workgroup per chain)"},
+                   "seq_len": w.T,
+                   "parallelism": (f"one GPU; {main_res['segments_per_chain']} sequence segments "
+                                   "per (batch, head) chain" if main_res["segments_per_chain"] > 1
+                                   else "one GPU; one workgroup per (batch, head) chain")},
         "roofline": main_res["roofline"],
         "cpu_baseline": cpu,
         "detail": {k: v for k, v in main_res.items() if k not in ("roofline",)},

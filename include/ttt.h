@@ -21,8 +21,10 @@
  *     (T mod b != 0) follows the same rules.
  *   - eta is one fp32 learning rate per head.
  *   - All arrays are dense, row-major, and live in DEVICE memory owned by the
- *     caller.  The library allocates nothing and keeps no state between
- *     calls.
+ *     caller.  The only memory the library allocates is the workspace of a
+ *     segmented TTT-Linear scan (below): one device buffer per (device,
+ *     stream) pair, grown on demand and kept until the process exits.  No
+ *     other state is kept between calls.
  *   - qkv_dtype selects the element type of Q/K/V/Y (and q/k/v/y): TTT_F32
  *     (float) or TTT_BF16 (bfloat16 bits, round-to-nearest-even on output).
  *     Fast-weight state is always fp32.
@@ -77,9 +79,25 @@ typedef enum {
  *   B, H, T      >= 0.  B*H = 0 is a no-op.  T = 0 writes W_out = W0.
  *   d            16, 32, 64 or 128.
  *   b            mini-batch size, 1 <= b <= 64.  (d = 64, b = 16 runs the
- *                MFMA kernel; other shapes run a plainer kernel.)
+ *                MFMA kernels; other shapes run a plainer kernel.)
+ *
+ * Segmented scan (d = 64, b = 16, when the chains are too few to fill the
+ * GPU).  A mini-batch maps the weights affinely,
+ *     W_next = (I - eta_h K^T K) W + eta_h K^T V,
+ * so a run of mini-batches does too: W_end = M W_start + N.  The T tokens of
+ * each chain are then cut into segments (a whole number of mini-batches
+ * each); one launch computes (M, N) of every segment but the last, one
+ * composes them into every segment's start state, and one runs all segments'
+ * scans at once.  The result is the same mini-batch descent; only the fp32
+ * rounding order of the state differs from a single-segment scan.  The
+ * maps and start states (B*H*(3 nseg - 2)*d*d*4 bytes) live in the stream's
+ * workspace: calls on one stream share it, calls on different streams do
+ * not.  ttt_linear_segments reports the segment count a call would use; the
+ * environment variable TTT_LINEAR_SEGMENTS=S (1..30) forces S segments.
+ *
  * Errors: TTT_ERR_INVALID_ARG, TTT_ERR_UNSUPPORTED (d, b, dtype, or on-chip
- * memory the shape needs), TTT_ERR_HIP.
+ * memory the shape needs), TTT_ERR_HIP (including a failed workspace
+ * allocation).
  */
 int ttt_linear_forward(const void* Q, const void* K, const void* V, int qkv_dtype,
                        const float* W0, int w0_per_batch, const float* eta,
@@ -130,6 +148,15 @@ int ttt_linear_decode_step(const void* q, const void* k, const void* v, int qkv_
                            void* y, void* stream);
 
 /* Static, human-readable text for a status code (never NULL). */
+/*
+ * Number of sequence segments ttt_linear_forward would cut each chain into
+ * for these sizes on the current device (1 = one workgroup scans the whole
+ * chain).  Returns a negative ttt_status for arguments ttt_linear_forward
+ * would reject.  Needs no device memory; queries the device's compute-unit
+ * count.
+ */
+int ttt_linear_segments(int64_t B, int64_t H, int64_t T, int d, int b, int qkv_dtype);
+
 const char* ttt_status_string(int status);
 
 /* ABI version of this header: (major << 16) | minor. */

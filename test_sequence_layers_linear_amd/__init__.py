@@ -53,6 +53,8 @@ def load_library():
     lib.ttt_mlp_forward.restype = I
     lib.ttt_linear_decode_step.argtypes = [P, P, P, I, P, P, L, L, I, P, P]
     lib.ttt_linear_decode_step.restype = I
+    lib.ttt_linear_segments.argtypes = [L, L, L, I, I, I]
+    lib.ttt_linear_segments.restype = I
     lib.ttt_status_string.argtypes = [I]
     lib.ttt_status_string.restype = ctypes.c_char_p
     lib.ttt_abi_version.argtypes = []
@@ -190,7 +192,17 @@ def ttt_linear_decode_step(q, k, v, W, eta, y=None, stream=None):
     return y
 
 
+def ttt_linear_segments(B: int, H: int, T: int, d: int, b: int, dtype=torch.bfloat16) -> int:
+    """Sequence segments ttt_linear_forward cuts each chain into for these
+    sizes on the current device (1 = unsegmented)."""
+    code = TTT_F32 if dtype == torch.float32 else TTT_BF16
+    n = load_library().ttt_linear_segments(int(B), int(H), int(T), int(d), int(b), code)
+    _check(min(n, 0))
+    return n
+
+
 __all__ = [
-    "ttt_linear_forward", "ttt_mlp_forward", "ttt_linear_decode_step", "load_library",
+    "ttt_linear_forward", "ttt_mlp_forward", "ttt_linear_decode_step", "ttt_linear_segments",
+    "load_library",
     "status_string", "TTTError", "LIB_PATH", "TTT_F32", "TTT_BF16",
 ]

@@ -19,7 +19,7 @@ using ttt::LinearArgs;
 using ttt::MlpArgs;
 using ttt::DecodeArgs;
 
-constexpr int kAbiVersion = (1 << 16) | 0;
+constexpr int kAbiVersion = (1 << 16) | 1;
 
 bool valid_dtype(int dt) { return dt == TTT_F32 || dt == TTT_BF16; }
 size_t elem_bytes(int dt) { return dt == TTT_F32 ? 4 : 2; }
@@ -235,6 +235,20 @@ int ttt_linear_forward(const void* Q, const void* K, const void* V, int qkv_dtyp
     if (ttt::linear_generic_lds_bytes(d, b) > static_cast<size_t>(ttt::kMaxLdsBytes))
         return TTT_ERR_UNSUPPORTED;
     return hip_status(ttt::launch_linear_generic(a));
+}
+
+int ttt_linear_segments(int64_t B, int64_t H, int64_t T, int d, int b, int qkv_dtype)
+{
+    if (B < 0 || H < 0 || T < 0 || b < 1) return TTT_ERR_INVALID_ARG;
+    if (!valid_dtype(qkv_dtype) || !d_supported(d) || b > 64) return TTT_ERR_UNSUPPORTED;
+    int64_t units = B;
+    if (!mul_ok(units, H) || units > kMaxUnits) return TTT_ERR_UNSUPPORTED;
+    LinearArgs a{nullptr, nullptr, nullptr, qkv_dtype, nullptr, 0, nullptr, B, H, T, d, b,
+                 nullptr, nullptr, nullptr};
+    if (units == 0 || T == 0) return 1;
+    if (ttt::linear_mfma_supports(a)) return plan_segments(units, T, b, ttt::kLinearBf16Costs).nseg;
+    if (ttt::linear_mfma_f32_supports(a)) return plan_segments(units, T, b, ttt::kLinearF32Costs).nseg;
+    return 1;
 }
 
 int ttt_mlp_forward(const void* Q, const void* K, const void* V, int qkv_dtype,

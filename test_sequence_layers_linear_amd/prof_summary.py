@@ -22,8 +22,11 @@ import os
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "test_sequence_layers_linear_amd", "csrc")
 KERNEL_FILES = {
-    "linear_mfma_kernel": "ttt_linear_mfma.hip",
-    "linear_mfma_f32_kernel": "ttt_linear_mfma_f32.hip",
+    "linear_mfma_kernel[scan]": "ttt_linear_mfma.hip",
+    "linear_mfma_kernel[maps]": "ttt_linear_mfma.hip",
+    "linear_mfma_f32_kernel[scan]": "ttt_linear_mfma_f32.hip",
+    "linear_mfma_f32_kernel[maps]": "ttt_linear_mfma_f32.hip",
+    "linear_combine_kernel": "ttt_linear_combine.hip",
     "linear_generic_kernel": "ttt_generic.hip",
     "mlp_generic_kernel": "ttt_generic.hip",
     "mlp_mfma_kernel": "ttt_mlp_mfma.hip",
@@ -33,8 +36,15 @@ COPY_NAME = "__amd_rocclr_copyBuffer"
 
 
 def short_name(full: str) -> str:
+    """Kernel key: the function name, with [maps] / [scan] for the two
+    instantiations of the TTT-Linear MFMA kernels."""
     for k in KERNEL_FILES:
-        if k + "(" in full or k + "<" in full:
+        base = k.split("[")[0]
+        if base + "<true>" in full:
+            return base + "[maps]"
+        if base + "<false>" in full:
+            return base + "[scan]"
+        if base + "(" in full or base + "<" in full:
             return k
     return full.split("(")[0][-60:]
 

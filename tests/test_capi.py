@@ -37,7 +37,7 @@ def lib():
 def test_exports_every_declared_function(lib):
     names = declared_functions()
     assert set(names) >= {"ttt_linear_forward", "ttt_mlp_forward", "ttt_linear_decode_step",
-                          "ttt_status_string", "ttt_abi_version"}
+                          "ttt_linear_segments", "ttt_status_string", "ttt_abi_version"}
     for n in names:
         assert hasattr(lib, n), f"{n} declared in ttt.h but not exported"
 
@@ -115,3 +115,24 @@ def test_binding_rejects_cpu_tensors():
         ttt.ttt_linear_forward(x, x, x, torch.zeros(1, 16, 16), torch.zeros(1), 16,
                                Y=torch.zeros(1, 1, 16, 16), W_out=torch.zeros(1, 1, 16, 16),
                                stream=None)
+
+
+def test_segment_query_validation_and_override(lib, monkeypatch):
+    """The segment-count query validates like ttt_linear_forward; the
+    TTT_LINEAR_SEGMENTS override is applied (clamped to 30, at least one
+    mini-batch per segment) before any device query."""
+    assert lib.ttt_linear_segments(-1, 3, 64, 64, 16, 1) == INVALID
+    assert lib.ttt_linear_segments(1, 3, 64, 64, 0, 1) == INVALID
+    assert lib.ttt_linear_segments(1, 3, 64, 48, 16, 1) == UNSUPPORTED
+    assert lib.ttt_linear_segments(1, 3, 64, 64, 16, 7) == UNSUPPORTED
+    assert lib.ttt_linear_segments(0, 3, 64, 64, 16, 1) == 1
+    monkeypatch.setenv("TTT_LINEAR_SEGMENTS", "4")
+    assert lib.ttt_linear_segments(1, 4, 2048, 64, 16, 0) == 4
+    assert lib.ttt_linear_segments(1, 4, 16, 64, 16, 0) == 1       # one mini-batch
+    assert lib.ttt_linear_segments(1, 4, 40, 64, 16, 1) == 3       # 3 chunks, one each
+    monkeypatch.setenv("TTT_LINEAR_SEGMENTS", "50")
+    # clamped to 30: 128 chunks in segments of ceil(128 / 30) = 5 -> 26 segments
+    assert lib.ttt_linear_segments(1, 4, 2048, 64, 16, 0) == 26
+    assert lib.ttt_linear_segments(1, 4, 30 * 16, 64, 16, 0) == 30
+    monkeypatch.setenv("TTT_LINEAR_SEGMENTS", "3")
+    assert lib.ttt_linear_segments(1, 4, 2048, 32, 16, 0) == 1     # generic kernel: no split

@@ -76,3 +76,32 @@ def test_decode_worked_example_exact():
     torch.cuda.synchronize()
     assert torch.equal(y[0, 0, :2].cpu(), torch.tensor([1.75, 0.0]))
     assert torch.equal(W[0, 0, :2, :2].cpu(), torch.tensor([[1.75, 0.0], [1.25, -1.0]]))
+
+
+def test_decode_steps_in_a_hip_graph_match_eager():
+    """Decode steps captured once in a HIP graph and replayed several times
+    (with eager work and synchronisation between the replays) give exactly
+    the eager results each time."""
+    w = CONFIGS[4].with_(B=2, H=3, T=16, decode_steps=8)
+    g = to_gpu(make_inputs(w, 91, w0_per_batch=True))
+    W = g["W0"].clone()
+    y = torch.empty_like(g["dq"][0])
+
+    def steps():
+        for s in range(w.decode_steps):
+            ttt.ttt_linear_decode_step(g["dq"][s], g["dk"][s], g["dv"][s], W, g["eta"], y=y)
+
+    steps()
+    torch.cuda.synchronize()
+    W_ref, y_ref = W.clone(), y.clone()
+    W.copy_(g["W0"])
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        steps()
+    for _ in range(3):
+        W.copy_(g["W0"])
+        y.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(W, W_ref) and torch.equal(y, y_ref)
