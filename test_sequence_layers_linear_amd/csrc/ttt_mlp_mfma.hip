@@ -15,13 +15,14 @@
 // Gradient Descent Replaces the Transformer KV Cache ...", sections "The Core
 // Mechanism" and "Hardware Parallelization").
 //
-// Work split.  One workgroup of 4 waves per (batch, head) chain; wave w owns
-// hidden units [64w, 64w + 64) (4 hidden tiles of 16): W1[:, slice] and
-// W2[slice, :] live in its fp32 MFMA accumulators for the whole scan.  Only two
-// quantities need all hidden units: Z (needed by every wave, on the critical
-// path) and Y; both are summed across waves through LDS, each wave reducing a
-// quarter of the output columns (reduce-scatter), and E' is then shared
-// through LDS in the two orientations the products need.
+// Work split.  One workgroup of 8 waves (two per SIMD) per (batch, head)
+// chain; wave w owns hidden units [32w, 32w + 32) (2 hidden tiles of 16):
+// W1[:, slice] and W2[slice, :] live in its fp32 MFMA accumulators (ordinary
+// VGPRs) for the whole scan.  Only two quantities need all hidden units: Z
+// (needed by every wave, on the critical path) and Y; both are summed across
+// waves through LDS, waves 0-3 each reducing a quarter of the output columns
+// (reduce-scatter), and E' is then shared through LDS in the two orientations
+// the products need.  Waves 0-3 also stage the inputs.
 //
 // Layouts (16x16 MFMA; lane l, c = l % 16, g = l / 16; C: lane holds rows
 // 4g..4g+3 of column c; A: lane holds row c; B: lane holds column c):
@@ -51,7 +52,11 @@ namespace {
 constexpr int kD = 64;
 constexpr int kM = 256;
 constexpr int kB = 16;
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;                               // waves per chain
+constexpr int kHid = kM / kWaves;                       // hidden units per wave
+constexpr int kHT = kHid / 16;                          // 16-unit hidden tiles per wave
+constexpr int kHK = kHT / 2;                            // 32-unit k-blocks per wave
+constexpr int kWork = 4;                                // waves that stage and reduce
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBufferDword3 = 0x00020000;   // raw buffer resource word 3 (gfx9 family)
 
@@ -69,10 +74,10 @@ constexpr int kYRow = kD * 4 + 16;                      // fp32 [t][64 j] + pad 
 constexpr int kYWave = kB * kYRow;                      // 4352
 constexpr int kENRow = kRowBytes + 16;                  // bf16 [t][64 j] + pad = 144
 constexpr int kOffZ = 2 * kSlotBytes;                   // 18432
-constexpr int kOffY = kOffZ + kWaves * kZWave;          // 38912
-constexpr int kOffEN = kOffY + kWaves * kYWave;         // 56320
-constexpr int kOffET = kOffEN + kB * kENRow;            // 58624
-constexpr int kLdsBytes = kOffET + kD * kTrRow;         // 61184
+constexpr int kOffY = kOffZ + kWaves * kZWave;          // 59392
+constexpr int kOffEN = kOffY + kWaves * kYWave;         // 94208
+constexpr int kOffET = kOffEN + kB * kENRow;            // 96512
+constexpr int kLdsBytes = kOffET + kD * kTrRow;         // 99072
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -140,7 +145,12 @@ __device__ __forceinline__ int rho(int mt, int m)
     return 32 * (mt >> 1) + 8 * (m >> 2) + 4 * (mt & 1) + (m & 3);
 }
 __device__ __forceinline__ int swz(int r, int seg) { return r * kRowBytes + ((seg ^ (r & 7)) << 4); }
-__device__ __forceinline__ float sigmoid_f(float x) { return 1.0f / (1.0f + __expf(-x)); }
+// logistic sigmoid with the hardware exp2 and reciprocal (about 1 ulp each;
+// the products it feeds take bf16 operands)
+__device__ __forceinline__ float sigmoid_f(float x)
+{
+    return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * x));
+}
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t chain_rsrc(const void* base, int64_t bytes)
 {
@@ -148,8 +158,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t chain_rsrc(const void* base, i
                                              static_cast<int>(bytes), kBufferDword3);
 }
 
-// one wave's share of one chunk: rows [4w, 4w + 4) of K, Q, V; lane l holds
-// row 4w + l / 16, 8-byte segment l % 16 (4 bf16)
+// one staging wave's share of one chunk (w < kWork): rows [4w, 4w + 4) of
+// K, Q, V; lane l holds row 4w + l / 16, 8-byte segment l % 16 (4 bf16)
 struct StageRegs {
     u32x2 k, q, v;
 };
@@ -174,20 +184,20 @@ mlp_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const float* w1 = W1_0 + src * kD * kM;
     const float* w2 = W2_0 + src * kM * kD;
 
-    // fast weights of hidden slice [64w, 64w + 64):
-    //   W1a[it][ht][r] = W1[rho(it, 4g + r)][64w + 16ht + c]        (lane = hidden)
-    //   W2a[ht][jt][r] = W2[64w + 16ht + 4g + r][16jt + c]          (lane = output)
-    //   W2b[jt][ht][r] = W2[64w + 16ht + c][16jt + 4g + r]          (lane = hidden)
-    f32x4 W1a[4][4], W2a[4][4], W2b[4][4];
+    // fast weights of hidden slice [kHid w, kHid w + kHid):
+    //   W1a[it][ht][r] = W1[rho(it, 4g + r)][kHid w + 16ht + c]      (lane = hidden)
+    //   W2a[ht][jt][r] = W2[kHid w + 16ht + 4g + r][16jt + c]        (lane = output)
+    //   W2b[jt][ht][r] = W2[kHid w + 16ht + c][16jt + 4g + r]        (lane = hidden)
+    f32x4 W1a[4][kHT], W2a[kHT][4], W2b[4][kHT];
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
+        for (int b = 0; b < kHT; ++b)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                W1a[a][b][r] = w1[rho(a, 4 * g + r) * kM + 64 * w + 16 * b + c];
-                W2a[a][b][r] = w2[(64 * w + 16 * a + 4 * g + r) * kD + 16 * b + c];
-                W2b[a][b][r] = w2[(64 * w + 16 * b + c) * kD + 16 * a + 4 * g + r];
+                W1a[a][b][r] = w1[rho(a, 4 * g + r) * kM + kHid * w + 16 * b + c];
+                W2a[b][a][r] = w2[(kHid * w + 16 * b + 4 * g + r) * kD + 16 * a + c];
+                W2b[a][b][r] = w2[(kHid * w + 16 * b + c) * kD + 16 * a + 4 * g + r];
             }
 
     bf16x4 eye;       // identity as a B operand: B[k = 4g + r][n = c] = (k == n)
@@ -209,12 +219,16 @@ mlp_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const int st_row = 4 * w + (lane >> 4);
     const int st_seg = lane & 15;                  // 8-byte segment: columns 4 st_seg .. +3
     auto load_stage = [&](StageRegs& o, int chunk) {
+        if (w >= kWork)
+            return;
         const int off = (chunk * kB + st_row) * kRowBytes + st_seg * 8;
         o.k = __builtin_amdgcn_raw_buffer_load_b64(rk, off, 0, 0);
         o.q = __builtin_amdgcn_raw_buffer_load_b64(rq, off, 0, 0);
         o.v = __builtin_amdgcn_raw_buffer_load_b64(rv, off, 0, 0);
     };
     auto write_stage = [&](const StageRegs& o, int slot) {
+        if (w >= kWork)
+            return;
         unsigned char* sl = lds + slot * kSlotBytes;
         const int pos = swz(st_row, st_seg >> 1) + 8 * (st_seg & 1);
         *reinterpret_cast<u32x2*>(sl + kOffK + pos) = o.k;
@@ -229,9 +243,11 @@ mlp_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         }
     };
 
-    // Y of a finished chunk: sum the 4 wave partials of this lane's token c,
-    // columns 16w + 4g .. +3, and store (rows past T are dropped)
+    // Y of a finished chunk (waves w < kWork): sum the wave partials of this
+    // lane's token c, columns 16w + 4g .. +3, and store (rows past T are dropped)
     auto finish_y = [&](int t0) {
+        if (w >= kWork)
+            return;
         f32x4 acc = zero;
 #pragma unroll
         for (int ww = 0; ww < kWaves; ++ww)
@@ -256,10 +272,10 @@ mlp_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         // ---- P1: Hk, Q W1, S, Ak, Z partial ----------------------------------
         // (bf16 copies of the chunk-start weights are packed where they are
         // used; the updates come last, so every product sees chunk-start values)
-        f32x4 Hq[4], dsl[4];
-        bf16x4 AkT[4], AkH[4];
+        f32x4 Hq[kHT], dsl[kHT];
+        bf16x4 AkT[kHT], AkH[kHT];
 #pragma unroll
-        for (int ht = 0; ht < 4; ++ht) {
+        for (int ht = 0; ht < kHT; ++ht) {
             const bf16x8 b0 = pack8(W1a[0][ht], W1a[1][ht]);
             const bf16x8 b1 = pack8(W1a[2][ht], W1a[3][ht]);
             f32x4 hk = mfma32(ka0, b0, zero);
@@ -287,21 +303,26 @@ mlp_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
             sb = pack4(St);
         }
 #pragma unroll
-        for (int ht = 0; ht < 4; ++ht)
+        for (int ht = 0; ht < kHT; ++ht)
             AkH[ht] = pack4(mfma16(AkT[ht], eye, zero));
-        const bf16x8 akh0 = cat8(AkH[0], AkH[1]), akh1 = cat8(AkH[2], AkH[3]);
+        bf16x8 akh[kHK];
+#pragma unroll
+        for (int kb = 0; kb < kHK; ++kb)
+            akh[kb] = cat8(AkH[2 * kb], AkH[2 * kb + 1]);
 #pragma unroll
         for (int jt = 0; jt < 4; ++jt) {
-            f32x4 z = mfma32(akh0, pack8(W2a[0][jt], W2a[1][jt]), zero);
-            z = mfma32(akh1, pack8(W2a[2][jt], W2a[3][jt]), z);
+            f32x4 z = zero;
+#pragma unroll
+            for (int kb = 0; kb < kHK; ++kb)
+                z = mfma32(akh[kb], pack8(W2a[2 * kb][jt], W2a[2 * kb + 1][jt]), z);
             // Z partial [j = 16jt + c][t = 4g .. +3] of this wave
             *reinterpret_cast<f32x4*>(lds + kOffZ + w * kZWave + (16 * jt + c) * kZRow + 16 * g) = z;
         }
         __builtin_amdgcn_sched_barrier(0);
         __syncthreads();
 
-        // ---- P2: Z for columns 16w + c, E' -> LDS -------------------------
-        {
+        // ---- P2: Z for columns 16w + c, E' -> LDS (waves w < kWork) ---------
+        if (w < kWork) {
             f32x4 zs = zero;
 #pragma unroll
             for (int ww = 0; ww < kWaves; ++ww)
@@ -341,17 +362,17 @@ mlp_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         __builtin_amdgcn_sched_barrier(0);
 
         // D' = (E' W2^T) * SiLU'(Hk), layout T
-        bf16x4 DT[4];
+        bf16x4 DT[kHT];
 #pragma unroll
-        for (int ht = 0; ht < 4; ++ht) {
+        for (int ht = 0; ht < kHT; ++ht) {
             f32x4 gg = mfma32(eA[0], pack8(W2b[0][ht], W2b[1][ht]), zero);
             gg = mfma32(eA[1], pack8(W2b[2][ht], W2b[3][ht]), gg);
             DT[ht] = pack4(gg * dsl[ht]);
         }
         // Hq = Q W1 + S D'; Aq = SiLU(Hq) -> layout H
-        bf16x4 AqH[4];
+        bf16x4 AqH[kHT];
 #pragma unroll
-        for (int ht = 0; ht < 4; ++ht) {
+        for (int ht = 0; ht < kHT; ++ht) {
             const f32x4 hq = mfma16_as32(sb, DT[ht], Hq[ht]);
             f32x4 a;
 #pragma unroll
@@ -359,12 +380,17 @@ mlp_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 a[r] = hq[r] * sigmoid_f(hq[r]);
             AqH[ht] = pack4(mfma16(pack4(a), eye, zero));
         }
-        const bf16x8 aqh0 = cat8(AqH[0], AqH[1]), aqh1 = cat8(AqH[2], AqH[3]);
+        bf16x8 aqh[kHK];
+#pragma unroll
+        for (int kb = 0; kb < kHK; ++kb)
+            aqh[kb] = cat8(AqH[2 * kb], AqH[2 * kb + 1]);
         // Sa for the E' term: lane (c = t, g) holds Sa[t][t' = 4g + r], masked
         bf16x4 sab;
         {
-            f32x4 Sa = mfma32(akh0, aqh0, zero);
-            Sa = mfma32(akh1, aqh1, Sa);
+            f32x4 Sa = zero;
+#pragma unroll
+            for (int kb = 0; kb < kHK; ++kb)
+                Sa = mfma32(akh[kb], aqh[kb], Sa);
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 Sa[r] = (4 * g + r <= c) ? Sa[r] : 0.f;
@@ -375,10 +401,13 @@ mlp_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         // repacks them here instead of keeping the phase-1 packs alive.
 #pragma unroll
         for (int jt = 0; jt < 4; ++jt) {
-            f32x4 x0 = W2a[0][jt], x1 = W2a[1][jt], x2 = W2a[2][jt], x3 = W2a[3][jt];
-            asm volatile("" : "+v"(x0), "+v"(x1), "+v"(x2), "+v"(x3));
-            f32x4 y = mfma32(pack8(x0, x1), aqh0, zero);
-            y = mfma32(pack8(x2, x3), aqh1, y);
+            f32x4 y = zero;
+#pragma unroll
+            for (int kb = 0; kb < kHK; ++kb) {
+                f32x4 x0 = W2a[2 * kb][jt], x1 = W2a[2 * kb + 1][jt];
+                asm volatile("" : "+v"(x0), "+v"(x1));
+                y = mfma32(pack8(x0, x1), aqh[kb], y);
+            }
             y = mfma16_as32(eT[jt], sab, y);
             *reinterpret_cast<f32x4*>(lds + kOffY + w * kYWave + c * kYRow + (16 * jt + 4 * g) * 4) = y;
         }
@@ -386,10 +415,10 @@ mlp_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 #pragma unroll
         for (int it = 0; it < 4; ++it)
 #pragma unroll
-            for (int ht = 0; ht < 4; ++ht)
+            for (int ht = 0; ht < kHT; ++ht)
                 W1a[it][ht] = mfma16(kt[it], DT[ht], W1a[it][ht]);
 #pragma unroll
-        for (int ht = 0; ht < 4; ++ht)
+        for (int ht = 0; ht < kHT; ++ht)
 #pragma unroll
             for (int jt = 0; jt < 4; ++jt) {
                 W2a[ht][jt] = mfma16(AkT[ht], eT[jt], W2a[ht][jt]);
@@ -434,11 +463,11 @@ mlp_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
+        for (int b = 0; b < kHT; ++b)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                w1o[rho(a, 4 * go + r) * kM + 64 * wo + 16 * b + co] = W1a[a][b][r];
-                w2o[(64 * wo + 16 * a + 4 * go + r) * kD + 16 * b + co] = W2a[a][b][r];
+                w1o[rho(a, 4 * go + r) * kM + kHid * wo + 16 * b + co] = W1a[a][b][r];
+                w2o[(kHid * wo + 16 * b + 4 * go + r) * kD + 16 * a + co] = W2a[b][a][r];
             }
 }
 
@@ -453,6 +482,11 @@ bool mlp_mfma_supports(const MlpArgs& a)
 hipError_t launch_mlp_mfma(const MlpArgs& a)
 {
     const dim3 grid(static_cast<unsigned>(a.B * a.H)), block(kThreads);
+    static_assert(kLdsBytes <= kMaxLdsBytes, "LDS budget");
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(mlp_mfma_kernel),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+    if (e != hipSuccess)
+        return e;
     hipLaunchKernelGGL(mlp_mfma_kernel, grid, block, kLdsBytes, a.stream,
                        static_cast<const uint16_t*>(a.Q), static_cast<const uint16_t*>(a.K),
                        static_cast<const uint16_t*>(a.V), a.W1_0, a.W2_0, a.w0_per_batch, a.eta,
