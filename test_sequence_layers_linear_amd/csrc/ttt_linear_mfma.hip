@@ -73,11 +73,9 @@ constexpr int kRowBytes = kD * 2;                    // 128
 constexpr int kOffK = 0;
 constexpr int kOffQ = kOffK + kB * kRowBytes;        // 2048
 constexpr int kOffV = kOffQ + kB * kRowBytes;        // 4096
-constexpr int kOffKt = kOffV + kB * kRowBytes;       // 6144
-constexpr int kKtRow = 40;                           // 16 tokens * 2 B + 8 B pad
-constexpr int kChunkBytes = kOffKt + kD * kKtRow;    // 8704
+constexpr int kChunkBytes = kOffV + kB * kRowBytes;  // 6144
 constexpr int kSlotBytes = kChunkBytes * kStageChunks;
-constexpr int kLdsBytes = kSlotBytes * kSlots;       // 52224
+constexpr int kLdsBytes = kSlotBytes * kSlots;       // 36864
 
 static_assert((2 * kSet) % kSlots == 0, "slot index must be static inside the loop");
 
@@ -137,6 +135,17 @@ __device__ __forceinline__ bf16x4 pack4(f32x4 x)
 __device__ __forceinline__ int rho(int mt, int m)
 {
     return 32 * (mt >> 1) + 8 * (m >> 2) + 4 * (mt & 1) + (m & 3);
+}
+
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives, as
+// element k (k = 0..3), element i % 4 of the 8-byte block addressed by lane
+// 4k + i / 4 of its group (measured on gfx950 with an in-bounds probe).
+__device__ __forceinline__ bf16x4 read_tr16(const unsigned char* p)
+{
+    typedef __bf16 lds_bf16x4 __attribute__((ext_vector_type(4)));
+    const auto q = (__attribute__((address_space(3))) lds_bf16x4*)(
+        (__attribute__((address_space(3))) unsigned char*)(p));
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(q);
 }
 
 // byte offset of 16-byte segment `seg` of row `r` in a swizzled row-major tile
@@ -244,11 +253,6 @@ linear_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
         if (!kMaps)
             *reinterpret_cast<u32x4*>(chunk + kOffQ + swz(r, st_seg)) = o.q;
         *reinterpret_cast<u32x4*>(chunk + kOffV + swz(r, st_seg)) = o.v;
-        // K^T[i][t] for the 8 input indices of this segment
-        const bf16x8 kv = __builtin_bit_cast(bf16x8, o.k);
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-            *reinterpret_cast<__bf16*>(chunk + kOffKt + (8 * st_seg + e) * kKtRow + 2 * r) = kv[e];
     };
 
     // Operands of one chunk, read from its LDS tile.
@@ -265,9 +269,12 @@ linear_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
             o.qa1 = *reinterpret_cast<const bf16x8*>(tile + kOffQ + swz(c, 4 + g));
         }
         o.vrow = *reinterpret_cast<const bf16x4*>(tile + kOffV + swz(c, 2 * w + (g >> 1)) + 8 * (g & 1));
+        // K^T operand of the update, transposed on the way out of LDS: lane
+        // (c, g) addresses row 4g + c / 4, inputs rho(mt, 4 (c % 4) .. + 3) (8
+        // contiguous bytes) and receives K[4g + r][rho(mt, c)], r = 0..3
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
-            o.kt[mt] = *reinterpret_cast<const bf16x4*>(tile + kOffKt + rho(mt, c) * kKtRow + 8 * g);
+            o.kt[mt] = read_tr16(tile + kOffK + swz(4 * g + (c >> 2), 4 * (mt >> 1) + (c & 3)) + 8 * (mt & 1));
     };
 
     // One chunk of the scan, tokens t0 onwards.

@@ -62,22 +62,21 @@ constexpr int kBufferDword3 = 0x00020000;   // raw buffer resource word 3 (gfx9 
 
 // LDS layout (bytes)
 constexpr int kRowBytes = kD * 2;                       // 128: bf16 row of K/Q
-constexpr int kTrRow = 40;                              // K^T / V^T / E'^T rows: 16 tokens + pad
+constexpr int kTrRow = 40;                              // E'^T rows: 16 tokens + pad
 constexpr int kOffK = 0;
 constexpr int kOffQ = kOffK + kB * kRowBytes;           // 2048
-constexpr int kOffKt = kOffQ + kB * kRowBytes;          // 4096
-constexpr int kOffVt = kOffKt + kD * kTrRow;            // 6656
-constexpr int kSlotBytes = kOffVt + kD * kTrRow;        // 9216
+constexpr int kOffV = kOffQ + kB * kRowBytes;           // 4096
+constexpr int kSlotBytes = kOffV + kB * kRowBytes;      // 6144
 constexpr int kZRow = 80;                               // fp32 [j][16 t] + pad
 constexpr int kZWave = kD * kZRow;                      // 5120
 constexpr int kYRow = kD * 4 + 16;                      // fp32 [t][64 j] + pad = 272
 constexpr int kYWave = kB * kYRow;                      // 4352
 constexpr int kENRow = kRowBytes + 16;                  // bf16 [t][64 j] + pad = 144
-constexpr int kOffZ = 2 * kSlotBytes;                   // 18432
-constexpr int kOffY = kOffZ + kWaves * kZWave;          // 59392
-constexpr int kOffEN = kOffY + kWaves * kYWave;         // 94208
-constexpr int kOffET = kOffEN + kB * kENRow;            // 96512
-constexpr int kLdsBytes = kOffET + kD * kTrRow;         // 99072
+constexpr int kOffZ = 2 * kSlotBytes;                   // 12288
+constexpr int kOffY = kOffZ + kWaves * kZWave;          // 53248
+constexpr int kOffEN = kOffY + kWaves * kYWave;         // 88064
+constexpr int kOffET = kOffEN + kB * kENRow;            // 90368
+constexpr int kLdsBytes = kOffET + kD * kTrRow;         // 92928
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -143,6 +142,16 @@ __device__ __forceinline__ bf16x8 cat8(bf16x4 lo, bf16x4 hi)
 __device__ __forceinline__ int rho(int mt, int m)
 {
     return 32 * (mt >> 1) + 8 * (m >> 2) + 4 * (mt & 1) + (m & 3);
+}
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives, as
+// element k (k = 0..3), element i % 4 of the 8-byte block addressed by lane
+// 4k + i / 4 of its group (measured on gfx950 with an in-bounds probe).
+__device__ __forceinline__ bf16x4 read_tr16(const unsigned char* p)
+{
+    typedef __bf16 lds_bf16x4 __attribute__((ext_vector_type(4)));
+    const auto q = (__attribute__((address_space(3))) lds_bf16x4*)(
+        (__attribute__((address_space(3))) unsigned char*)(p));
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(q);
 }
 __device__ __forceinline__ int swz(int r, int seg) { return r * kRowBytes + ((seg ^ (r & 7)) << 4); }
 // logistic sigmoid with the hardware exp2 and reciprocal (about 1 ulp each;
@@ -233,14 +242,7 @@ mlp_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         const int pos = swz(st_row, st_seg >> 1) + 8 * (st_seg & 1);
         *reinterpret_cast<u32x2*>(sl + kOffK + pos) = o.k;
         *reinterpret_cast<u32x2*>(sl + kOffQ + pos) = o.q;
-        const bf16x4 kv = __builtin_bit_cast(bf16x4, o.k);
-        const bf16x4 vv = __builtin_bit_cast(bf16x4, o.v);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int x = 4 * st_seg + e;
-            *reinterpret_cast<__bf16*>(sl + kOffKt + x * kTrRow + 2 * st_row) = kv[e];
-            *reinterpret_cast<__bf16*>(sl + kOffVt + x * kTrRow + 2 * st_row) = vv[e];
-        }
+        *reinterpret_cast<u32x2*>(sl + kOffV + pos) = o.v;
     };
 
     // Y of a finished chunk (waves w < kWork): sum the wave partials of this
@@ -328,7 +330,10 @@ mlp_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
             for (int ww = 0; ww < kWaves; ++ww)
                 zs += *reinterpret_cast<const f32x4*>(lds + kOffZ + ww * kZWave +
                                                       (16 * w + c) * kZRow + 16 * g);
-            const bf16x4 vt = *reinterpret_cast<const bf16x4*>(sl + kOffVt + (16 * w + c) * kTrRow + 8 * g);
+            // V[4g + r][16w + c], transposed on the way out of LDS (lane (c, g)
+            // addresses row 4g + c / 4, columns 16w + 4 (c % 4) .. + 3)
+            const bf16x4 vt = read_tr16(sl + kOffV + swz(4 * g + (c >> 2), 2 * w + ((c & 3) >> 1)) +
+                                        8 * (c & 1));
             f32x4 e;
 #pragma unroll
             for (int r = 0; r < 4; ++r)
@@ -357,7 +362,7 @@ mlp_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
             eT[jt] = *reinterpret_cast<const bf16x4*>(lds + kOffET + (16 * jt + c) * kTrRow + 8 * g);
 #pragma unroll
         for (int it = 0; it < 4; ++it)
-            kt[it] = *reinterpret_cast<const bf16x4*>(sl + kOffKt + rho(it, c) * kTrRow + 8 * g);
+            kt[it] = read_tr16(sl + kOffK + swz(4 * g + (c >> 2), 4 * (it >> 1) + (c & 3)) + 8 * (it & 1));
         __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
         __builtin_amdgcn_sched_barrier(0);
 
