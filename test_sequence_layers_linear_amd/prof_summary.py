@@ -72,8 +72,9 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--config", type=int, required=True)
     ap.add_argument("--trace", required=True)
-    ap.add_argument("--fetch", required=True)
-    ap.add_argument("--write", required=True)
+    ap.add_argument("--fetch", help="rocprofv3 --pmc FETCH_SIZE output (omit: no byte counts)")
+    ap.add_argument("--write", help="rocprofv3 --pmc WRITE_SIZE output")
+    ap.add_argument("--title", help="heading (default: the workload name)")
     ap.add_argument("--command", required=True, help="the rocprofv3 command lines that made the data")
     ap.add_argument("--copy-mib", type=int, default=256)
     ap.add_argument("--out", required=True)
@@ -86,20 +87,22 @@ def main():
     w = CONFIGS[args.config]
 
     stats = list(csv.DictReader(open(one_csv(args.trace, "kernel_stats.csv"))))
-    fetch = counter_per_kernel(args.fetch)
-    write = counter_per_kernel(args.write)
-    copy_bytes = args.copy_mib * 1024 * 1024
-    copy_fetch = max(v for k, vs in fetch.items() if COPY_NAME in k for v in vs) * 1024
-    copy_write = max(v for k, vs in write.items() if COPY_NAME in k for v in vs) * 1024
-    f_scale, w_scale = copy_bytes / copy_fetch, copy_bytes / copy_write
-
-    lines = [f"# rocprofv3 summary: {w.name}", "",
-             "Commands (run from /tmp on the GPU box, repo at $R):", "", "```", args.command, "```", "",
-             f"Copy calibration ({args.copy_mib} MiB device copy): FETCH_SIZE reads "
-             f"{copy_fetch / 1024:.1f} KiB (scale {f_scale:.3f}), WRITE_SIZE reads "
-             f"{copy_write / 1024:.1f} KiB (scale {w_scale:.3f}).", "",
-             "| kernel | calls | avg us | min us | max us | HBM read MB/launch | HBM write MB/launch |",
-             "|---|---|---|---|---|---|---|"]
+    have_bytes = bool(args.fetch and args.write)
+    fetch = counter_per_kernel(args.fetch) if have_bytes else {}
+    write = counter_per_kernel(args.write) if have_bytes else {}
+    lines = [f"# rocprofv3 summary: {args.title or w.name}", "",
+             "Commands (run from /tmp on the GPU box, repo at $R):", "", "```", args.command, "```", ""]
+    f_scale = w_scale = 1.0
+    if have_bytes:
+        copy_bytes = args.copy_mib * 1024 * 1024
+        copy_fetch = max(v for k, vs in fetch.items() if COPY_NAME in k for v in vs) * 1024
+        copy_write = max(v for k, vs in write.items() if COPY_NAME in k for v in vs) * 1024
+        f_scale, w_scale = copy_bytes / copy_fetch, copy_bytes / copy_write
+        lines += [f"Copy calibration ({args.copy_mib} MiB device copy): FETCH_SIZE reads "
+                  f"{copy_fetch / 1024:.1f} KiB (scale {f_scale:.3f}), WRITE_SIZE reads "
+                  f"{copy_write / 1024:.1f} KiB (scale {w_scale:.3f}).", ""]
+    lines += ["| kernel | calls | avg us | min us | max us | HBM read MB/launch | HBM write MB/launch |",
+              "|---|---|---|---|---|---|---|"]
     table = json.load(open(args.traffic)) if os.path.exists(args.traffic) else {}
     for r in stats:
         name = short_name(r["Name"])
