@@ -69,11 +69,11 @@ int device_cus()
 }
 
 // Segment count for a chain-parallel scan of `units` chains of T tokens.
-// Model (us): a launch of n workgroups runs them all at once when
-// n <= 2 CUs, each one slowed by max(1, n / CUs) (two workgroups share a CU);
-//   S = 1:  chunks fwd f(units)
-//   S > 1:  c (map f(2 units (S - 1)) + fwd f(units S)) + (S - 1) apply + extra
-// with c = ceil(chunks / S) and `extra` the two additional launches.
+// Each launch of the split runs all its workgroups at once, one per CU (more
+// would queue or share CUs and stretch the slowest ones), so S is limited to
+// what fits; within that it minimises
+//   ceil(chunks / S) (map + fwd) + (S - 1) apply + launch
+// against the unsplit chunks * fwd (costs measured on MI355X).
 // TTT_LINEAR_SEGMENTS=S (1 <= S <= kMaxSegments) forces S segments (at least
 // one chunk each), for tests and tuning.
 ttt::SegmentPlan plan_segments(int64_t units, int64_t T, int chunk, const ttt::SegmentCosts& cost)
@@ -90,18 +90,14 @@ ttt::SegmentPlan plan_segments(int64_t units, int64_t T, int chunk, const ttt::S
         }
     }
     const int64_t cus = device_cus();
-    const int64_t cap = cus * ttt::kLinearBlocksPerCu;
-    if (cus <= 0 || units >= cus || chunks < 4) return p;
-    auto slow = [&](int64_t n) { return n > cus ? static_cast<double>(n) / cus : 1.0; };
-    double best = static_cast<double>(chunks) * cost.fwd * slow(units);
+    if (cus <= 0 || 2 * units > cus || chunks < 4) return p;
+    double best = static_cast<double>(chunks) * cost.fwd;
     int best_s = 1;
     for (int S = 2; S <= ttt::kMaxSegments; ++S) {
-        const int64_t maps = units * (S - 1) * 2, fwd = units * S;
-        if (maps > cap || fwd > cap) break;
+        if (units * S > cus || units * (S - 1) * cost.map_blocks_per_segment > cus) break;
         const int64_t per = (chunks + S - 1) / S;
         if (per < 2) break;
-        const double t = per * (cost.map * slow(maps) + cost.fwd * slow(fwd)) +
-                         (S - 1) * cost.apply + cost.launch;
+        const double t = per * (cost.map + cost.fwd) + (S - 1) * cost.apply + cost.launch;
         if (t < best) { best = t; best_s = S; }
     }
     if (best_s > 1) {

@@ -87,15 +87,14 @@ constexpr int kMaxSegments = 30;   // with the ring's spare slots: 36 x 4352 B o
 // and the fixed cost of the two extra launches.
 struct SegmentCosts {
     double fwd, map, apply, launch;
+    int map_blocks_per_segment;   // workgroups of the maps launch per segment
 };
 bool linear_mfma_supports(const LinearArgs& a);
 hipError_t launch_linear_mfma(const LinearArgs& a, const SegmentPlan& p);
 bool linear_mfma_f32_supports(const LinearArgs& a);
 hipError_t launch_linear_mfma_f32(const LinearArgs& a, const SegmentPlan& p);
-constexpr SegmentCosts kLinearBf16Costs{0.39, 0.30, 0.70, 11.0};
-constexpr SegmentCosts kLinearF32Costs{1.45, 1.00, 0.70, 11.0};
-// workgroups of one MFMA linear launch that run at once on one CU
-constexpr int kLinearBlocksPerCu = 2;
+constexpr SegmentCosts kLinearBf16Costs{0.35, 0.43, 0.90, 11.0, 1};
+constexpr SegmentCosts kLinearF32Costs{1.90, 1.20, 0.90, 11.0, 2};
 bool mlp_mfma_supports(const MlpArgs& a);
 hipError_t launch_mlp_mfma(const MlpArgs& a);
 

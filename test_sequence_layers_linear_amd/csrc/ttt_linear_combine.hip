@@ -13,7 +13,8 @@
 // and stores every W_j.  The segments then run their scans independently.
 //
 // Column j of W_{j+1} depends only on column j of W_j, so one chain is split
-// over 4 workgroups, one per 16-column slice J; wave I of a workgroup computes
+// over 4 workgroups, one per 16-column slice J (all on the XCD of the chain's
+// maps and scans); wave I of a workgroup computes
 // the 16 x 16 output tile (I, J) of each step in fp32 on
 // v_mfma_f32_16x16x4_f32 (16 k-steps in 4 independent accumulators).  Every
 // slice W_j stays in LDS (rows padded to 17 floats, so the four rows 16 g + s
@@ -48,8 +49,8 @@ namespace {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __global__ void __launch_bounds__(kThreads, 1)
-linear_combine_kernel(const float* W0, int w0_per_batch, int H, const float* __restrict__ maps,
-                      int nseg, float* __restrict__ wstart)
+linear_combine_kernel(const float* W0, int w0_per_batch, int H, int64_t units,
+                      const float* __restrict__ maps, int nseg, float* __restrict__ wstart)
 {
     extern __shared__ float Wl[];        // [nseg][64][kPad]: slice J of W_0 .. W_{nseg-1}
 
@@ -59,8 +60,21 @@ linear_combine_kernel(const float* W0, int w0_per_batch, int H, const float* __r
     const int c = lane & 15;
     const int g = lane >> 4;
 
-    const int64_t u = blockIdx.x >> 2;   // chain
-    const int J = blockIdx.x & 3;        // column slice
+    // chain u and column slice J; with at least 8 chains the 4 workgroups of
+    // chain u run on XCD u % 8 (workgroups go to the XCDs round robin), where
+    // its maps were written
+    int64_t u;
+    int J;
+    if (units < 8) {
+        u = blockIdx.x >> 2;
+        J = blockIdx.x & 3;
+    } else {
+        const int t = blockIdx.x >> 3;
+        u = 8 * static_cast<int64_t>(t >> 2) + (blockIdx.x & 7);
+        J = t & 3;
+    }
+    if (u >= units)
+        return;
     const int h = static_cast<int>(u % H);
     const float* w0 = W0 + (w0_per_batch ? u : h) * kD * kD;
     float* out = wstart + u * nseg * kD * kD;
@@ -145,8 +159,11 @@ hipError_t launch_linear_combine(const LinearArgs& a, const SegmentPlan& p)
         if (e != hipSuccess)
             return e;
     }
-    hipLaunchKernelGGL(linear_combine_kernel, dim3(static_cast<unsigned>(a.B * a.H * 4)), dim3(kThreads), lds,
-                       a.stream, a.W0, a.w0_per_batch, static_cast<int>(a.H), p.maps, p.nseg, p.wstart);
+    const int64_t units = a.B * a.H;
+    const int64_t blocks = units < 8 ? 4 * units : 32 * ((units + 7) / 8);
+    hipLaunchKernelGGL(linear_combine_kernel, dim3(static_cast<unsigned>(blocks)),
+                       dim3(kThreads), lds, a.stream, a.W0, a.w0_per_batch, static_cast<int>(a.H), units,
+                       p.maps, p.nseg, p.wstart);
     return hipGetLastError();
 }
 

@@ -163,37 +163,62 @@ struct StageRegs {
     u32x4 k, q, v;
 };
 
+// Block id -> (chain u, block s of the chain) for nb blocks per chain.  With
+// at least 8 chains every block of chain u gets id = u (mod 8): workgroups
+// are dispatched to the 8 XCDs round robin, so they all share XCD u % 8 and
+// its L2 (grid 8 nb ceil(units / 8); ids with u >= units do nothing).  With
+// fewer chains that would leave XCDs idle, so blocks are numbered plainly.
+__device__ __forceinline__ void xcd_block(int id, int nb, int64_t units, int64_t& u, int& s)
+{
+    if (units < 8) {
+        u = id / nb;
+        s = id % nb;
+        return;
+    }
+    const int t = id >> 3;
+    u = 8 * static_cast<int64_t>(t / nb) + (id & 7);
+    s = t % nb;
+}
+__host__ __device__ inline int64_t placed_grid(int64_t units, int nb)
+{
+    return units < 8 ? units * nb : 8 * nb * ((units + 7) / 8);
+}
+
 // kMaps = false: the scan of segment s of a chain (Y rows of the segment; the
 //   last segment also writes W_out), started from W0 (one segment) or from
 //   the segment's start state in wstart.
-// kMaps = true: the affine map W_end = M W_start + N of segment s < nseg - 1;
-//   block half 0 runs the scan from W = I with V = 0 (giving M), half 1 from
-//   W = 0 with the segment's V (giving N).  No Q, no Y.
+// kMaps = true: the affine map W_end = M W_start + N of segment s < nseg - 1,
+//   8 waves: waves 0-3 (half 0) run the scan from W = I with V = 0 (giving
+//   M), waves 4-7 (half 1) from W = 0 with the segment's V (giving N); both
+//   halves share the staged K.  No Q, no Y.
+// With nseg > 1 the blocks of chain u all run on XCD u % 8 (see xcd_block),
+// so the maps, start states and scans of a chain meet in one L2.
 template <bool kMaps>
-__global__ void __launch_bounds__(kThreads, 1)
+__global__ void __launch_bounds__(kMaps ? 2 * kThreads : kThreads, 1)
 linear_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                    const uint16_t* __restrict__ V, const float* W0, int w0_per_batch,
-                   const float* __restrict__ eta, int H, int T, int seg_len, int nseg,
-                   float* maps, const float* wstart, uint16_t* __restrict__ Y, float* W_out)
+                   const float* __restrict__ eta, int H, int T, int64_t units, int seg_len,
+                   int nseg, float* maps, const float* wstart, uint16_t* __restrict__ Y,
+                   float* W_out)
 {
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
 
     const int lane = threadIdx.x & 63;
-    const int w = threadIdx.x >> 6;
+    const int w = (threadIdx.x >> 6) & (kWaves - 1);
+    // wave-uniform role flags, made scalar so that the compiler branches on
+    // them instead of masking lanes
+    const int half = kMaps ? __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 8)) : 0;
+    const bool stager = !kMaps || __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6)) < kWaves;
     const int c = lane & 15;
     const int g = lane >> 4;
     const int col = 16 * w + c;          // this lane's column of W
 
-    int64_t u;
-    int s, half = 0;
-    if (kMaps) {
-        const int per = 2 * (nseg - 1);
-        u = blockIdx.x / per;
-        s = (blockIdx.x % per) >> 1;
-        half = blockIdx.x & 1;
-    } else {
-        u = blockIdx.x / nseg;
-        s = blockIdx.x % nseg;
+    int64_t u = blockIdx.x;
+    int s = 0;
+    if (nseg > 1) {
+        xcd_block(blockIdx.x, kMaps ? nseg - 1 : nseg, units, u, s);
+        if (u >= units)                  // padding of the XCD placement
+            return;
     }
     const int h = static_cast<int>(u % H);
     const float et = eta[h];
@@ -230,16 +255,22 @@ linear_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     const int64_t seg_bytes = static_cast<int64_t>(t_len) * kD * 2;
     const __amdgpu_buffer_rsrc_t rq = chain_rsrc(Q + base, kMaps ? 0 : seg_bytes);
     const __amdgpu_buffer_rsrc_t rk = chain_rsrc(K + base, seg_bytes);
-    const __amdgpu_buffer_rsrc_t rv = chain_rsrc(V + base, (kMaps && half == 0) ? 0 : seg_bytes);
+    const __amdgpu_buffer_rsrc_t rv = chain_rsrc(V + base, seg_bytes);
     const __amdgpu_buffer_rsrc_t ry = chain_rsrc(Y + base, kMaps ? 0 : seg_bytes);
 
     const int nstages = (t_len + kStageTokens - 1) / kStageTokens;
+    // stages per register set: the maps block runs 8 waves (half the
+    // registers per wave), so it prefetches 3-6 stages ahead instead of 6-12
+    constexpr int kSetK = kMaps ? kSet / 2 : kSet;
+    static_assert((2 * kSetK) % kSlots == 0, "slot index must be static inside the loop");
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 
     // staging: this lane's row inside the stage and its 16-byte segment
     const int st_row = 8 * w + (lane >> 3);             // 0..31
     const int st_seg = lane & 7;
     auto load_stage = [&](StageRegs& o, int stage) {
+        if (!stager)
+            return;
         const int off = (stage * kStageTokens + st_row) * kRowBytes + st_seg * 16;
         o.k = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
         if (!kMaps)
@@ -247,6 +278,8 @@ linear_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
         o.v = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0);
     };
     auto write_stage = [&](const StageRegs& o, int slot) {
+        if (!stager)
+            return;
         unsigned char* chunk = lds + slot * kSlotBytes + (st_row >> 4) * kChunkBytes;
         const int r = st_row & 15;
         *reinterpret_cast<u32x4*>(chunk + kOffK + swz(r, st_seg)) = o.k;
@@ -287,7 +320,11 @@ linear_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
 
         // R = K W_J - V (C layout: rows t = 4g + r, column col); the -I
         // product is issued in the 16x16x32 shape of the chain it starts
-        f32x4 R = mfma16_as32(o.vrow, neg_eye, zero);
+        // (the M half, half 0, of a maps block has V = 0: its V operand is
+        // zeroed rather than the product skipped, since an MFMA inside an
+        // EXEC-masked region still executes)
+        const bf16x4 vrow = (kMaps && half == 0) ? bf16x4{} : o.vrow;
+        f32x4 R = mfma16_as32(vrow, neg_eye, zero);
         R = mfma32(o.ka0, b0, R);
         R = mfma32(o.ka1, b1, R);
 
@@ -334,37 +371,37 @@ linear_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     };
 
     if (nstages > 0) {
-        StageRegs setA[kSet], setB[kSet];
+        StageRegs setA[kSetK], setB[kSetK];
         {
             StageRegs first;
             load_stage(first, 0);
             write_stage(first, 0);
         }
 #pragma unroll
-        for (int p = 0; p < kSet; ++p)
+        for (int p = 0; p < kSetK; ++p)
             load_stage(setA[p], 1 + p);
-        // stages s0 .. s0 + 2 kSet - 1 per iteration; setA holds s0 + 1 .. s0 + kSet
-        for (int s0 = 0; s0 < nstages; s0 += 2 * kSet) {
+        // stages s0 .. s0 + 2 kSetK - 1 per iteration; setA holds s0 + 1 .. s0 + kSetK
+        for (int s0 = 0; s0 < nstages; s0 += 2 * kSetK) {
 #pragma unroll
-            for (int p = 0; p < kSet; ++p)
-                load_stage(setB[p], s0 + kSet + 1 + p);
+            for (int p = 0; p < kSetK; ++p)
+                load_stage(setB[p], s0 + kSetK + 1 + p);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int p = 0; p < kSet; ++p) {
+            for (int p = 0; p < kSetK; ++p) {
                 if (s0 + p >= nstages)       // uniform: the scan is done
                     goto done;
                 process(setA[p], s0 + p, p % kSlots);
             }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int p = 0; p < kSet; ++p)
-                load_stage(setA[p], s0 + 2 * kSet + 1 + p);
+            for (int p = 0; p < kSetK; ++p)
+                load_stage(setA[p], s0 + 2 * kSetK + 1 + p);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int p = 0; p < kSet; ++p) {
-                if (s0 + kSet + p >= nstages)
+            for (int p = 0; p < kSetK; ++p) {
+                if (s0 + kSetK + p >= nstages)
                     goto done;
-                process(setB[p], s0 + kSet + p, (kSet + p) % kSlots);
+                process(setB[p], s0 + kSetK + p, (kSetK + p) % kSlots);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -396,27 +433,27 @@ bool linear_mfma_supports(const LinearArgs& a)
 
 hipError_t launch_linear_mfma(const LinearArgs& a, const SegmentPlan& p)
 {
-    const dim3 block(kThreads);
     const auto* q = static_cast<const uint16_t*>(a.Q);
     const auto* k = static_cast<const uint16_t*>(a.K);
     const auto* v = static_cast<const uint16_t*>(a.V);
     auto* y = static_cast<uint16_t*>(a.Y);
     const int H = static_cast<int>(a.H), T = static_cast<int>(a.T);
     const int seg_len = static_cast<int>(p.seg_len);
+    const int64_t units = a.B * a.H;
     if (p.nseg > 1) {
-        const dim3 grid(static_cast<unsigned>(a.B * a.H * (p.nseg - 1) * 2));
-        hipLaunchKernelGGL(linear_mfma_kernel<true>, grid, block, kLdsBytes, a.stream, q, k, v,
-                           a.W0, a.w0_per_batch, a.eta, H, T, seg_len, p.nseg, p.maps, p.wstart, y,
-                           a.W_out);
+        const dim3 grid(static_cast<unsigned>(placed_grid(units, p.nseg - 1)));
+        hipLaunchKernelGGL(linear_mfma_kernel<true>, grid, dim3(2 * kThreads), kLdsBytes, a.stream, q, k,
+                           v, a.W0, a.w0_per_batch, a.eta, H, T, units, seg_len, p.nseg, p.maps,
+                           p.wstart, y, a.W_out);
         hipError_t e = hipGetLastError();
         if (e == hipSuccess)
             e = launch_linear_combine(a, p);
         if (e != hipSuccess)
             return e;
     }
-    const dim3 grid(static_cast<unsigned>(a.B * a.H * p.nseg));
-    hipLaunchKernelGGL(linear_mfma_kernel<false>, grid, block, kLdsBytes, a.stream, q, k, v,
-                       a.W0, a.w0_per_batch, a.eta, H, T, seg_len, p.nseg, p.maps, p.wstart, y,
+    const dim3 grid(static_cast<unsigned>(p.nseg > 1 ? placed_grid(units, p.nseg) : units));
+    hipLaunchKernelGGL(linear_mfma_kernel<false>, grid, dim3(kThreads), kLdsBytes, a.stream, q, k, v,
+                       a.W0, a.w0_per_batch, a.eta, H, T, units, seg_len, p.nseg, p.maps, p.wstart, y,
                        a.W_out);
     return hipGetLastError();
 }

@@ -86,18 +86,44 @@ struct StageRegs {
 // Row of W held in register r of accumulator tile mt by lane group g.
 __device__ __forceinline__ int wrow(int mt, int m) { return 16 * (m >> 2) + 4 * mt + (m & 3); }
 
+// Block id -> (chain u, block s of the chain) for nb blocks per chain.  With
+// at least 8 chains every block of chain u gets id = u (mod 8): workgroups
+// are dispatched to the 8 XCDs round robin, so they all share XCD u % 8 and
+// its L2 (grid 8 nb ceil(units / 8); ids with u >= units do nothing).  With
+// fewer chains that would leave XCDs idle, so blocks are numbered plainly.
+__device__ __forceinline__ void xcd_block(int id, int nb, int64_t units, int64_t& u, int& s)
+{
+    if (units < 8) {
+        u = id / nb;
+        s = id % nb;
+        return;
+    }
+    const int t = id >> 3;
+    u = 8 * static_cast<int64_t>(t / nb) + (id & 7);
+    s = t % nb;
+}
+__host__ __device__ inline int64_t placed_grid(int64_t units, int nb)
+{
+    return units < 8 ? units * nb : 8 * nb * ((units + 7) / 8);
+}
+
 // kMaps = false: the scan of segment s of a chain (Y rows of the segment; the
 //   last segment also writes W_out), started from W0 (one segment) or from
 //   the segment's start state in wstart.
 // kMaps = true: the affine map W_end = M W_start + N of segment s < nseg - 1;
 //   block half 0 runs the scan from W = I with V = 0 (giving M), half 1 from
-//   W = 0 with the segment's V (giving N).  No Y.
+//   W = 0 with the segment's V (giving N).  No Q, no Y.  (The two halves run
+//   as separate workgroups: this kernel is bound by the CU's fp32 MFMA rate,
+//   so sharing one CU would halve each half's speed.)
+// With nseg > 1 the blocks of chain u all run on XCD u % 8 (see xcd_block),
+// so the maps, start states and scans of a chain meet in one L2.
 template <bool kMaps>
 __global__ void __launch_bounds__(kThreads, 1)
 linear_mfma_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                        const float* __restrict__ V, const float* W0, int w0_per_batch,
-                       const float* __restrict__ eta, int H, int T, int seg_len, int nseg,
-                       float* maps, const float* wstart, float* __restrict__ Y, float* W_out)
+                       const float* __restrict__ eta, int H, int T, int64_t units, int seg_len,
+                       int nseg, float* maps, const float* wstart, float* __restrict__ Y,
+                       float* W_out)
 {
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
 
@@ -107,16 +133,16 @@ linear_mfma_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
     const int g = lane >> 4;
     const int col = 16 * w + c;
 
-    int64_t u;
-    int s, half = 0;
-    if (kMaps) {
-        const int per = 2 * (nseg - 1);
-        u = blockIdx.x / per;
-        s = (blockIdx.x % per) >> 1;
-        half = blockIdx.x & 1;
-    } else {
-        u = blockIdx.x / nseg;
-        s = blockIdx.x % nseg;
+    int64_t u = blockIdx.x;
+    int s = 0, half = 0;
+    if (nseg > 1) {
+        xcd_block(blockIdx.x, kMaps ? 2 * (nseg - 1) : nseg, units, u, s);
+        if (u >= units)                  // padding of the XCD placement
+            return;
+        if (kMaps) {
+            half = s & 1;
+            s >>= 1;
+        }
     }
     const int h = static_cast<int>(u % H);
     const float et = eta[h];
@@ -151,6 +177,8 @@ linear_mfma_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
     const __amdgpu_buffer_rsrc_t ry = chain_rsrc(Y + base, kMaps ? 0 : seg_bytes);
 
     const int nchunks = (t_len + kB - 1) / kB;
+    constexpr int kSetK = kSet;
+    static_assert((2 * kSetK) % kSlots == 0, "slot index must be static inside the loop");
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 
     // staging: lane l of wave w holds row 4w + l / 16, 16-byte segment l % 16
@@ -259,36 +287,36 @@ linear_mfma_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
     };
 
     if (nchunks > 0) {
-        StageRegs setA[kSet], setB[kSet];
+        StageRegs setA[kSetK], setB[kSetK];
         {
             StageRegs first;
             load_stage(first, 0);
             write_stage(first, 0);
         }
 #pragma unroll
-        for (int p = 0; p < kSet; ++p)
+        for (int p = 0; p < kSetK; ++p)
             load_stage(setA[p], 1 + p);
-        for (int c0 = 0; c0 < nchunks; c0 += 2 * kSet) {
+        for (int c0 = 0; c0 < nchunks; c0 += 2 * kSetK) {
 #pragma unroll
-            for (int p = 0; p < kSet; ++p)
-                load_stage(setB[p], c0 + kSet + 1 + p);
+            for (int p = 0; p < kSetK; ++p)
+                load_stage(setB[p], c0 + kSetK + 1 + p);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int p = 0; p < kSet; ++p) {
+            for (int p = 0; p < kSetK; ++p) {
                 if (c0 + p >= nchunks)       // uniform: the scan is done
                     goto done;
                 process(setA[p], c0 + p, p % kSlots);
             }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int p = 0; p < kSet; ++p)
-                load_stage(setA[p], c0 + 2 * kSet + 1 + p);
+            for (int p = 0; p < kSetK; ++p)
+                load_stage(setA[p], c0 + 2 * kSetK + 1 + p);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int p = 0; p < kSet; ++p) {
-                if (c0 + kSet + p >= nchunks)
+            for (int p = 0; p < kSetK; ++p) {
+                if (c0 + kSetK + p >= nchunks)
                     goto done;
-                process(setB[p], c0 + kSet + p, (kSet + p) % kSlots);
+                process(setB[p], c0 + kSetK + p, (kSetK + p) % kSlots);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -319,27 +347,27 @@ bool linear_mfma_f32_supports(const LinearArgs& a)
 
 hipError_t launch_linear_mfma_f32(const LinearArgs& a, const SegmentPlan& p)
 {
-    const dim3 block(kThreads);
     const auto* q = static_cast<const float*>(a.Q);
     const auto* k = static_cast<const float*>(a.K);
     const auto* v = static_cast<const float*>(a.V);
     auto* y = static_cast<float*>(a.Y);
     const int H = static_cast<int>(a.H), T = static_cast<int>(a.T);
     const int seg_len = static_cast<int>(p.seg_len);
+    const int64_t units = a.B * a.H;
     if (p.nseg > 1) {
-        const dim3 grid(static_cast<unsigned>(a.B * a.H * (p.nseg - 1) * 2));
-        hipLaunchKernelGGL(linear_mfma_f32_kernel<true>, grid, block, kLdsBytes, a.stream, q, k, v,
-                           a.W0, a.w0_per_batch, a.eta, H, T, seg_len, p.nseg, p.maps, p.wstart, y,
-                           a.W_out);
+        const dim3 grid(static_cast<unsigned>(placed_grid(units, 2 * (p.nseg - 1))));
+        hipLaunchKernelGGL(linear_mfma_f32_kernel<true>, grid, dim3(kThreads), kLdsBytes, a.stream, q,
+                           k, v, a.W0, a.w0_per_batch, a.eta, H, T, units, seg_len, p.nseg, p.maps,
+                           p.wstart, y, a.W_out);
         hipError_t e = hipGetLastError();
         if (e == hipSuccess)
             e = launch_linear_combine(a, p);
         if (e != hipSuccess)
             return e;
     }
-    const dim3 grid(static_cast<unsigned>(a.B * a.H * p.nseg));
-    hipLaunchKernelGGL(linear_mfma_f32_kernel<false>, grid, block, kLdsBytes, a.stream, q, k, v,
-                       a.W0, a.w0_per_batch, a.eta, H, T, seg_len, p.nseg, p.maps, p.wstart, y,
+    const dim3 grid(static_cast<unsigned>(p.nseg > 1 ? placed_grid(units, p.nseg) : units));
+    hipLaunchKernelGGL(linear_mfma_f32_kernel<false>, grid, dim3(kThreads), kLdsBytes, a.stream, q, k, v,
+                       a.W0, a.w0_per_batch, a.eta, H, T, units, seg_len, p.nseg, p.maps, p.wstart, y,
                        a.W_out);
     return hipGetLastError();
 }
