@@ -203,30 +203,39 @@ class Runner:
             self.decode_eager()
 
     def measure(self, steps, warmup):
+        """Time exactly `steps` steps between two synchronisations.  HIP events
+        on the launch stream mark the start, the end and (with decode steps)
+        the end of each step's forward call, so the forward duration comes from
+        the same timed region without an event between consecutive launches."""
         torch = self.torch
         self.capture_decode()
         for _ in range(warmup):
             self.forward()
             self.decode()
         torch.cuda.synchronize()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(steps)]
-        dv = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(steps)] if self.w.decode_steps else []
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        mids = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for _ in range(steps)] if self.w.decode_steps else []
         torch.cuda.synchronize()
         t0 = time.perf_counter()
+        start.record()
         for i in range(steps):
-            ev[i][0].record()
+            if mids:
+                mids[i][0].record()
             self.forward()
-            ev[i][1].record()
-            if dv:
-                dv[i][0].record()
-                self.decode()
-                dv[i][1].record()
+            if mids:
+                mids[i][1].record()
+            self.decode()
+        end.record()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        fwd = sum(a.elapsed_time(b) for a, b in ev) / steps / 1e3
-        dec = (sum(a.elapsed_time(b) for a, b in dv) / steps / 1e3) if dv else 0.0
+        total = start.elapsed_time(end) / 1e3
+        if mids:
+            fwd = sum(a.elapsed_time(b) for a, b in mids) / steps / 1e3
+            dec = (total - fwd * steps) / steps
+        else:
+            fwd, dec = total / steps, 0.0
         return wall / steps, fwd, dec
 
     def measure_cold(self, reps):
