@@ -17,6 +17,11 @@ Parity status of each function (how it is pinned, see tests/test_oracle.py):
                      autograd mini-batch GD, finite differences, dual form.
                      No exact worked example exists (SiLU is transcendental).
   linear_decode   -- pinned: n steps equal linear_forward with b=1.
+  linear_backward -- pinned: central finite differences of linear_forward in
+                     every coordinate (tiny sizes), the closed form of every
+                     gradient at eta=0 (independent of b), the gradients of
+                     causal linear attention (W0=0, one mini-batch), and the
+                     chain rule across two calls (resume from W_out).
 """
 from __future__ import annotations
 
@@ -61,6 +66,9 @@ def _load():
     lib.ttt_oracle_mlp_forward.restype = I
     lib.ttt_oracle_linear_decode.argtypes = [P, P, P, P, P, L, L, L, P]
     lib.ttt_oracle_linear_decode.restype = I
+    lib.ttt_oracle_linear_backward.argtypes = [P, P, P, P, I, P, L, L, L, L, L, P, P,
+                                               P, P, P, P, P, I]
+    lib.ttt_oracle_linear_backward.restype = I
     lib.ttt_oracle_max_threads.argtypes = []
     lib.ttt_oracle_max_threads.restype = I
     _lib = lib
@@ -103,6 +111,33 @@ def linear_forward(Q, K, V, W0, eta, b: int, nthreads: int = 0):
     if rc != 0:
         raise RuntimeError(f"oracle linear_forward failed ({rc})")
     return Y, W_out
+
+
+def linear_backward(Q, K, V, W0, eta, b: int, dY, dW_out, nthreads: int = 0):
+    """Vector-Jacobian product of linear_forward: the gradients of
+    <dY, Y> + <dW_out, W_out> with respect to Q, K, V, W0 and eta.
+    dY [B,H,T,d]; dW_out [B,H,d,d].  Returns (dQ, dK, dV, dW0, deta) in fp64,
+    dW0 shaped like W0 (summed over the batch when W0 is [H,d,d]) and deta [H]
+    (summed over the batch)."""
+    Q, K, V, W0, eta, dY, dW_out = map(_f64, (Q, K, V, W0, eta, dY, dW_out))
+    B, H, T, d = Q.shape
+    assert K.shape == Q.shape and V.shape == Q.shape and dY.shape == Q.shape
+    per_batch = 1 if W0.ndim == 4 else 0
+    assert W0.shape == ((B, H, d, d) if per_batch else (H, d, d))
+    assert eta.shape == (H,) and dW_out.shape == (B, H, d, d)
+    dQ = np.zeros((B, H, T, d))
+    dK = np.zeros((B, H, T, d))
+    dV = np.zeros((B, H, T, d))
+    dW0c = np.zeros((B, H, d, d))
+    detac = np.zeros((B, H))
+    rc = _load().ttt_oracle_linear_backward(_ptr(Q), _ptr(K), _ptr(V), _ptr(W0), per_batch,
+                                            _ptr(eta), B, H, T, d, int(b), _ptr(dY),
+                                            _ptr(dW_out), _ptr(dQ), _ptr(dK), _ptr(dV),
+                                            _ptr(dW0c), _ptr(detac), int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"oracle linear_backward failed ({rc})")
+    dW0 = dW0c if per_batch else dW0c.sum(axis=0)
+    return dQ, dK, dV, dW0, detac.sum(axis=0)
 
 
 def mlp_forward(Q, K, V, W1, W2, eta, b: int, nthreads: int = 0):

@@ -172,6 +172,199 @@ int ttt_oracle_linear_forward(const double* Q, const double* K, const double* V,
 }
 
 /* ------------------------------------------------------------------------ */
+/* Backward of the TTT-Linear scan: the vector-Jacobian product of the map    */
+/* (Q, K, V, W0, eta) -> (Y, W_out) computed above, for cotangents dY and     */
+/* dW_out.  Outer-loop training differentiates the layer output through the   */
+/* inner updates ([KV] section "Hardware Parallelization": the dual form      */
+/* exists for training; the uTTT write-up on thelatestinai.com, Figure 2(b):  */
+/* the read-output Jacobian runs backward through the earlier inner updates). */
+/*                                                                            */
+/* Written as reverse-mode differentiation of the primal loops of             */
+/* linear_chain, token by token, with every intermediate quantity recomputed  */
+/* from the chunk-start weights of the forward sweep:                         */
+/*   r_t = k_t Wc - v_t,  G_t = G_{t-1} + k_t^T r_t,  W_t = Wc - eta G_t,     */
+/*   y_t = q_t W_t,  and the weights after a chunk are W_{last token}.        */
+/* Adjoints are written xb (x-bar).                                           */
+/* ------------------------------------------------------------------------ */
+
+struct lin_bwd_ws {
+    double *Wcs;   /* [nchunks][d][d] chunk-start weights of the forward sweep */
+    double *Gs;    /* [b][d][d]  G_t of the tokens of the current chunk       */
+    double *R;     /* [b][d]     r_t of the tokens of the current chunk       */
+    double *Wt;    /* [d][d]     W_t                                          */
+    double *Wb;    /* [d][d]     adjoint of the weights after the chunk       */
+    double *Wcb;   /* [d][d]     adjoint of the chunk-start weights           */
+    double *Gb;    /* [d][d]     adjoint of G_t                               */
+    double *Wtb;   /* [d][d]     adjoint of W_t                               */
+    double *rb;    /* [d]        adjoint of r_t                               */
+};
+
+static void linear_chain_backward(const double* q, const double* k, const double* v,
+                                  const double* w_init, double eta, long T, long d, long b,
+                                  const double* dy, const double* dw_out,
+                                  double* dq, double* dk, double* dv, double* dw0,
+                                  double* deta, struct lin_bwd_ws* w)
+{
+    const long dd = d * d;
+    const long nc = (T + b - 1) / b;
+
+    /* forward sweep: chunk-start weights of every chunk */
+    memcpy(w->Wcs, w_init, (size_t)dd * sizeof(double));
+    for (long c = 0; c + 1 < nc; ++c) {
+        const long s = c * b, e = s + b;
+        const double* Wc = w->Wcs + c * dd;
+        double* Wn = w->Wcs + (c + 1) * dd;
+        memcpy(Wn, Wc, (size_t)dd * sizeof(double));
+        for (long t = s; t < e; ++t) {
+            for (long j = 0; j < d; ++j) {
+                double acc = 0.0;
+                for (long i = 0; i < d; ++i)
+                    acc += k[t * d + i] * Wc[i * d + j];
+                w->rb[j] = acc - v[t * d + j];
+            }
+            for (long i = 0; i < d; ++i)
+                for (long j = 0; j < d; ++j)
+                    Wn[i * d + j] -= eta * k[t * d + i] * w->rb[j];
+        }
+    }
+
+    /* backward sweep */
+    memcpy(w->Wb, dw_out, (size_t)dd * sizeof(double));
+    double eb = 0.0;
+    for (long c = nc - 1; c >= 0; --c) {
+        const long s = c * b, e = s + b < T ? s + b : T;
+        const double* Wc = w->Wcs + c * dd;
+        /* recompute r_t and G_t of the chunk */
+        for (long t = s; t < e; ++t) {
+            double* r = w->R + (t - s) * d;
+            double* G = w->Gs + (t - s) * dd;
+            for (long j = 0; j < d; ++j) {
+                double acc = 0.0;
+                for (long i = 0; i < d; ++i)
+                    acc += k[t * d + i] * Wc[i * d + j];
+                r[j] = acc - v[t * d + j];
+            }
+            for (long i = 0; i < d; ++i)
+                for (long j = 0; j < d; ++j)
+                    G[i * d + j] = (t > s ? G[i * d + j - dd] : 0.0) + k[t * d + i] * r[j];
+        }
+        memset(w->Wcb, 0, (size_t)dd * sizeof(double));
+        memset(w->Gb, 0, (size_t)dd * sizeof(double));
+        for (long t = e - 1; t >= s; --t) {
+            const double* r = w->R + (t - s) * d;
+            const double* G = w->Gs + (t - s) * dd;
+            /* W_t = Wc - eta G_t */
+            for (long x = 0; x < dd; ++x)
+                w->Wt[x] = Wc[x] - eta * G[x];
+            /* y_t = q_t W_t:  qb_t = yb_t W_t^T,  Wtb = q_t^T yb_t; the last token's
+             * W_t is also the weights after the chunk */
+            for (long i = 0; i < d; ++i) {
+                double acc = 0.0;
+                for (long j = 0; j < d; ++j)
+                    acc += dy[t * d + j] * w->Wt[i * d + j];
+                dq[t * d + i] = acc;
+            }
+            for (long i = 0; i < d; ++i)
+                for (long j = 0; j < d; ++j)
+                    w->Wtb[i * d + j] = q[t * d + i] * dy[t * d + j]
+                                        + (t == e - 1 ? w->Wb[i * d + j] : 0.0);
+            /* W_t = Wc - eta G_t:  Wcb += Wtb,  Gb += -eta Wtb,  etab += -<Wtb, G_t> */
+            for (long x = 0; x < dd; ++x) {
+                w->Wcb[x] += w->Wtb[x];
+                w->Gb[x] -= eta * w->Wtb[x];
+                eb -= w->Wtb[x] * G[x];
+            }
+            /* G_t = G_{t-1} + k_t^T r_t:  kb_t = Gb r_t,  rb_t = k_t Gb
+             * (Gb now holds the adjoint of G_t: every W_u with u >= t uses it) */
+            for (long i = 0; i < d; ++i) {
+                double acc = 0.0;
+                for (long j = 0; j < d; ++j)
+                    acc += w->Gb[i * d + j] * r[j];
+                dk[t * d + i] = acc;
+            }
+            for (long j = 0; j < d; ++j) {
+                double acc = 0.0;
+                for (long i = 0; i < d; ++i)
+                    acc += k[t * d + i] * w->Gb[i * d + j];
+                w->rb[j] = acc;
+            }
+            /* r_t = k_t Wc - v_t:  kb_t += rb_t Wc^T,  Wcb += k_t^T rb_t,  vb_t = -rb_t */
+            for (long i = 0; i < d; ++i) {
+                double acc = 0.0;
+                for (long j = 0; j < d; ++j)
+                    acc += w->rb[j] * Wc[i * d + j];
+                dk[t * d + i] += acc;
+            }
+            for (long i = 0; i < d; ++i)
+                for (long j = 0; j < d; ++j)
+                    w->Wcb[i * d + j] += k[t * d + i] * w->rb[j];
+            for (long j = 0; j < d; ++j)
+                dv[t * d + j] = -w->rb[j];
+        }
+        /* the chunk-start weights are the weights after the previous chunk */
+        memcpy(w->Wb, w->Wcb, (size_t)dd * sizeof(double));
+    }
+    memcpy(dw0, w->Wb, (size_t)dd * sizeof(double));
+    *deta = eb;
+}
+
+/* dQ, dK, dV: [B][H][T][d]; dW0 per chain: [B][H][d][d]; deta per chain:
+ * [B][H] (summing over the batch where W0 or eta is shared is left to the
+ * caller).  T = 0 gives dW0 = dW_out and deta = 0. */
+int ttt_oracle_linear_backward(const double* Q, const double* K, const double* V,
+                               const double* W0, int w0_per_batch, const double* eta,
+                               long B, long H, long T, long d, long b,
+                               const double* dY, const double* dW_out,
+                               double* dQ, double* dK, double* dV,
+                               double* dW0_chain, double* deta_chain, int nthreads)
+{
+    if (B < 0 || H < 0 || T < 0 || d < 1 || b < 1)
+        return ORACLE_EINVAL;
+    if (!W0 || !eta || !dW_out || !dW0_chain || !deta_chain ||
+        (T > 0 && (!Q || !K || !V || !dY || !dQ || !dK || !dV)))
+        return ORACLE_EINVAL;
+    const long dd = d * d;
+    const long units = B * H;
+    const long nc = (T + b - 1) / b;
+    const long bb = b < T ? b : (T > 0 ? T : 1);
+    int status = ORACLE_OK;
+    set_threads(nthreads);
+#pragma omp parallel
+    {
+        const size_t n = (size_t)((nc > 0 ? nc : 1) * dd + bb * dd + bb * d + 5 * dd + d);
+        double* buf = (double*)malloc(n * sizeof(double));
+        struct lin_bwd_ws w = {0};
+        if (!buf) {
+#pragma omp atomic write
+            status = ORACLE_ENOMEM;
+        } else {
+            w.Wcs = buf;
+            w.Gs = w.Wcs + (nc > 0 ? nc : 1) * dd;
+            w.R = w.Gs + bb * dd;
+            w.Wt = w.R + bb * d;
+            w.Wb = w.Wt + dd;
+            w.Wcb = w.Wb + dd;
+            w.Gb = w.Wcb + dd;
+            w.Wtb = w.Gb + dd;
+            w.rb = w.Wtb + dd;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (long u = 0; u < units; ++u) {
+            if (!buf)
+                continue;
+            long h = u % H;
+            const double* w_init = W0 + (w0_per_batch ? u : h) * dd;
+            const long off = u * T * d;
+            linear_chain_backward(Q + off, K + off, V + off, w_init, eta[h], T, d, b,
+                                  dY + off, dW_out + u * dd, dQ + off, dK + off, dV + off,
+                                  dW0_chain + u * dd, deta_chain + u, &w);
+        }
+        free(buf);
+    }
+    return status;
+}
+
+/* ------------------------------------------------------------------------ */
 /* TTT-MLP: f(z; W1, W2) = SiLU(z W1) W2, d -> m -> d, no biases             */
 /* ([SEQ] "TTT-MLP": two-layer MLP with a SiLU non-linearity).                */
 /* ------------------------------------------------------------------------ */

@@ -16,6 +16,7 @@ import pytest
 
 import oracle
 import test_oracle as pins
+import test_oracle_backward as bpins
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "ttt_oracle.c")
 
@@ -25,7 +26,8 @@ MUTANTS = {
     "gradient_transposed": ("G[i * d + j] += kt[i] * r[j];", "G[i * d + j] += kt[j] * r[i];"),
     "prediction_transposed": ("acc += kt[i] * Wc[i * d + j];", "acc += kt[i] * Wc[j * d + i];"),
     "readout_before_update": ("acc += qt[i] * Wt[i * d + j];", "acc += qt[i] * Wc[i * d + j];"),
-    "missing_half": ("Wt[x] = Wc[x] - eta * G[x];", "Wt[x] = Wc[x] - 2.0 * eta * G[x];"),
+    "missing_half": ("                Wt[x] = Wc[x] - eta * G[x];\n            /* y_t",
+                     "                Wt[x] = Wc[x] - 2.0 * eta * G[x];\n            /* y_t"),
     "gradient_not_accumulated": ("G[i * d + j] += kt[i] * r[j];", "G[i * d + j] = kt[i] * r[j];"),
     "silu_grad_sign": ("return s * (1.0 + x * (1.0 - s));", "return s * (1.0 - x * (1.0 - s));"),
     "silu_is_sigmoid": ("static double silu(double x) { return x * sigmoid(x); }",
@@ -38,6 +40,18 @@ MUTANTS = {
                            "acc += w->aq[p] * w->A2c[p * d + j];"),
     "decode_sign": ("Wu[i * d + j] -= eta[h] * g;", "Wu[i * d + j] += eta[h] * g;"),
     "decode_residual_uses_query": ("acc += kt[i] * Wu[i * d + j];", "acc += qt[i] * Wu[i * d + j];"),
+    # backward of the linear scan
+    "bwd_state_adjoint_sign": ("w->Gb[x] -= eta * w->Wtb[x];", "w->Gb[x] += eta * w->Wtb[x];"),
+    "bwd_dv_sign": ("dv[t * d + j] = -w->rb[j];", "dv[t * d + j] = w->rb[j];"),
+    "bwd_drops_final_state_adjoint": ("+ (t == e - 1 ? w->Wb[i * d + j] : 0.0);", "+ 0.0;"),
+    "bwd_dk_transposed": ("acc += w->rb[j] * Wc[i * d + j];", "acc += w->rb[j] * Wc[j * d + i];"),
+    "bwd_eta_sign": ("eb -= w->Wtb[x] * G[x];", "eb += w->Wtb[x] * G[x];"),
+    "bwd_prefix_not_accumulated": ("(t > s ? G[i * d + j - dd] : 0.0) + k[t * d + i] * r[j];",
+                                   "k[t * d + i] * r[j];"),
+    "bwd_dq_uses_chunk_start": ("acc += dy[t * d + j] * w->Wt[i * d + j];",
+                                "acc += dy[t * d + j] * Wc[i * d + j];"),
+    "bwd_state_adjoint_not_passed": ("memcpy(w->Wb, w->Wcb, (size_t)dd * sizeof(double));",
+                                     "memcpy(w->Wb, w->Wtb, (size_t)dd * sizeof(double));"),
 }
 
 
@@ -56,6 +70,11 @@ def _battery():
         ("mlp_fd", lambda: pins.test_mlp_gradient_matches_finite_differences(oracle)),
         ("decode_vs_scan", lambda: pins.test_decode_steps_equal_b1_scan(oracle)),
         ("decode_example", lambda: pins.test_decode_worked_example(oracle)),
+        ("bwd_fd", lambda: bpins.test_backward_matches_finite_differences(oracle, 2, 2, 7, 3, 3, False)),
+        ("bwd_autograd_b4", lambda: bpins.test_backward_matches_double_autograd(oracle, 4)),
+        ("bwd_eta_zero", lambda: bpins.test_backward_eta_zero_closed_form(oracle, 4)),
+        ("bwd_linear_attention", lambda: bpins.test_backward_linear_attention(oracle, 11, 16)),
+        ("bwd_chain_rule", lambda: bpins.test_backward_chain_rule_across_calls(oracle)),
     ]
     for name, fn in checks:
         try:
