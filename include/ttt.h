@@ -147,6 +147,48 @@ int ttt_linear_decode_step(const void* q, const void* k, const void* v, int qkv_
                            float* W, const float* eta, int64_t B, int64_t H, int d,
                            void* y, void* stream);
 
+/*
+ * Backward of the TTT-Linear scan, for outer-loop training: the gradients of
+ *     L = <dY, Y> + <dW_out, W_out>
+ * with respect to Q, K, V, W0 and eta, where (Y, W_out) is what
+ * ttt_linear_forward computes from the same arguments.  Training the outer
+ * model differentiates the layer output through the inner gradient steps
+ * (the dual form of the "Hardware Parallelization" section of the
+ * news.premlal.in page exists for training; the uTTT write-up on
+ * thelatestinai.com, Figure 2(b): the read-output Jacobian runs backward
+ * through the earlier inner updates).  Per mini-batch, in reverse order,
+ * with W the chunk-start weights, E = K W - V, A = tril(Q K^T) and G the
+ * gradient with respect to the weights after the chunk (G = dW_out after the
+ * last one):
+ *     P  = A^T dY + K G,   dV = eta_h P,   deta_h += -<P, E>
+ *     dA = -eta_h tril(dY E^T)
+ *     dQ = dY W^T + dA K
+ *     dK = -eta_h (P W^T + E G^T) + dA^T Q
+ *     G <- G + Q^T dY - eta_h K^T P
+ * and dW0 = G after the first mini-batch.  The chunk-start weights are
+ * recomputed from Q, K, V, W0 (nothing from the forward call is needed).
+ *
+ *   Q, K, V, W0, eta, B, H, T, b, w0_per_batch: as for ttt_linear_forward.
+ *   dY           [B][H][T][d], qkv_dtype, read only.
+ *   dW_out       fp32 [B][H][d][d], read only (pass zeros if W_out is unused).
+ *   dQ, dK, dV   [B][H][T][d], qkv_dtype, written.
+ *   dW0          fp32, W0's shape: [H][d][d] summed over the batch
+ *                (w0_per_batch = 0) or [B][H][d][d] (w0_per_batch = 1).
+ *   deta         fp32 [H], summed over the batch.
+ *   d = 64 and b = 16 only (other shapes: TTT_ERR_UNSUPPORTED).
+ *   B*H = 0 writes dW0 = 0 and deta = 0 (sums over an empty batch); T = 0
+ *   gives dW0 = dW_out (summed over the batch when W0 is shared), deta = 0.
+ * No output may overlap any other argument.  Workspace (the stream's, as for
+ * the segmented scan): B*H*ceil(T/16)*d*d*4 bytes of chunk-start states,
+ * plus B*H*d*d*4 bytes when W0 is shared.
+ * Errors as for ttt_linear_forward.
+ */
+int ttt_linear_backward(const void* Q, const void* K, const void* V, int qkv_dtype,
+                        const float* W0, int w0_per_batch, const float* eta,
+                        int64_t B, int64_t H, int64_t T, int d, int b,
+                        const void* dY, const float* dW_out,
+                        void* dQ, void* dK, void* dV, float* dW0, float* deta,
+                        void* stream);
 /* Static, human-readable text for a status code (never NULL). */
 /*
  * Number of sequence segments ttt_linear_forward would cut each chain into

@@ -10,6 +10,8 @@ Functions (same names as the C ABI):
     ttt_linear_forward(Q, K, V, W0, eta, b)           -> (Y, W_out)
     ttt_mlp_forward(Q, K, V, W1, W2, eta, b)          -> (Y, W1_out, W2_out)
     ttt_linear_decode_step(q, k, v, W, eta)           -> y   (W updated in place)
+    ttt_linear_backward(Q, K, V, W0, eta, b, dY, dW_out)
+                                                      -> (dQ, dK, dV, dW0, deta)
 """
 from __future__ import annotations
 
@@ -53,6 +55,9 @@ def load_library():
     lib.ttt_mlp_forward.restype = I
     lib.ttt_linear_decode_step.argtypes = [P, P, P, I, P, P, L, L, I, P, P]
     lib.ttt_linear_decode_step.restype = I
+    lib.ttt_linear_backward.argtypes = [P, P, P, I, P, I, P, L, L, L, I, I, P, P,
+                                        P, P, P, P, P, P]
+    lib.ttt_linear_backward.restype = I
     lib.ttt_linear_segments.argtypes = [L, L, L, I, I, I]
     lib.ttt_linear_segments.restype = I
     lib.ttt_status_string.argtypes = [I]
@@ -192,6 +197,49 @@ def ttt_linear_decode_step(q, k, v, W, eta, y=None, stream=None):
     return y
 
 
+def ttt_linear_backward(Q, K, V, W0, eta, b: int, dY, dW_out=None, dQ=None, dK=None, dV=None,
+                        dW0=None, deta=None, stream=None):
+    """Gradients of <dY, Y> + <dW_out, W_out> for (Y, W_out) =
+    ttt_linear_forward(Q, K, V, W0, eta, b), with respect to Q, K, V, W0 and
+    eta.  dY has Q's shape and dtype; dW_out fp32 [B,H,d,d] (None: zeros).
+    Returns (dQ, dK, dV in Q's dtype, dW0 fp32 shaped like W0 (summed over the
+    batch when W0 is [H,d,d]), deta fp32 [H] (summed over the batch))."""
+    lib = load_library()
+    if Q.dim() != 4:
+        raise ValueError("Q must be [B,H,T,d]")
+    dev = Q.device
+    B, H, T, d = Q.shape
+    for t, n in ((Q, "Q"), (K, "K"), (V, "V"), (dY, "dY")):
+        _need(t, n, dev, Q.dtype)
+        if t.shape != Q.shape:
+            raise ValueError(f"{n} shape {tuple(t.shape)} != Q shape {tuple(Q.shape)}")
+    _need(W0, "W0", dev, torch.float32)
+    _need(eta, "eta", dev, torch.float32)
+    per_batch = W0.dim() == 4
+    if W0.shape != ((B, H, d, d) if per_batch else (H, d, d)) or eta.shape != (H,):
+        raise ValueError("W0 must be [H,d,d] or [B,H,d,d] and eta [H]")
+    if dW_out is None:
+        dW_out = torch.zeros((B, H, d, d), device=dev, dtype=torch.float32)
+    _need(dW_out, "dW_out", dev, torch.float32)
+    if dW_out.shape != (B, H, d, d):
+        raise ValueError("dW_out must be [B,H,d,d]")
+    dQ = torch.empty_like(Q) if dQ is None else dQ
+    dK = torch.empty_like(Q) if dK is None else dK
+    dV = torch.empty_like(Q) if dV is None else dV
+    dW0 = torch.empty_like(W0) if dW0 is None else dW0
+    deta = torch.empty_like(eta) if deta is None else deta
+    for t, n in ((dQ, "dQ"), (dK, "dK"), (dV, "dV")):
+        _need(t, n, dev, Q.dtype)
+    _need(dW0, "dW0", dev, torch.float32)
+    _need(deta, "deta", dev, torch.float32)
+    _check(lib.ttt_linear_backward(Q.data_ptr(), K.data_ptr(), V.data_ptr(), _dtype_code(Q),
+                                   W0.data_ptr(), int(per_batch), eta.data_ptr(), B, H, T, d,
+                                   int(b), dY.data_ptr(), dW_out.data_ptr(), dQ.data_ptr(),
+                                   dK.data_ptr(), dV.data_ptr(), dW0.data_ptr(), deta.data_ptr(),
+                                   _stream_handle(dev, stream)))
+    return dQ, dK, dV, dW0, deta
+
+
 def ttt_linear_segments(B: int, H: int, T: int, d: int, b: int, dtype=torch.bfloat16) -> int:
     """Sequence segments ttt_linear_forward cuts each chain into for these
     sizes on the current device (1 = unsegmented)."""
@@ -202,7 +250,8 @@ def ttt_linear_segments(B: int, H: int, T: int, d: int, b: int, dtype=torch.bflo
 
 
 __all__ = [
-    "ttt_linear_forward", "ttt_mlp_forward", "ttt_linear_decode_step", "ttt_linear_segments",
+    "ttt_linear_forward", "ttt_mlp_forward", "ttt_linear_decode_step", "ttt_linear_backward",
+    "ttt_linear_segments",
     "load_library",
     "status_string", "TTTError", "LIB_PATH", "TTT_F32", "TTT_BF16",
 ]

@@ -247,6 +247,51 @@ int ttt_linear_segments(int64_t B, int64_t H, int64_t T, int d, int b, int qkv_d
     return 1;
 }
 
+int ttt_linear_backward(const void* Q, const void* K, const void* V, int qkv_dtype,
+                        const float* W0, int w0_per_batch, const float* eta,
+                        int64_t B, int64_t H, int64_t T, int d, int b,
+                        const void* dY, const float* dW_out,
+                        void* dQ, void* dK, void* dV, float* dW0, float* deta, void* stream)
+{
+    if (B < 0 || H < 0 || T < 0 || b < 1 || (w0_per_batch != 0 && w0_per_batch != 1))
+        return TTT_ERR_INVALID_ARG;
+    if (!valid_dtype(qkv_dtype) || d != 64 || b != 16)
+        return TTT_ERR_UNSUPPORTED;
+    int64_t units = B;
+    if (!mul_ok(units, H) || units > kMaxUnits) return TTT_ERR_UNSUPPORTED;
+    int64_t n_qkv = units;
+    if (!mul_ok(n_qkv, T) || !mul_ok(n_qkv, d) || !mul_ok(n_qkv, 4)) return TTT_ERR_UNSUPPORTED;
+    n_qkv = n_qkv / 4 * static_cast<int64_t>(elem_bytes(qkv_dtype));
+    const int64_t n_state = static_cast<int64_t>(d) * d * 4;
+    if (H > 0 && (!dW0 || !deta)) return TTT_ERR_INVALID_ARG;
+    if (units > 0 && (!W0 || !eta || !dW_out)) return TTT_ERR_INVALID_ARG;
+    if (units > 0 && T > 0 && (!Q || !K || !V || !dY || !dQ || !dK || !dV)) return TTT_ERR_INVALID_ARG;
+    if (H == 0) return TTT_OK;
+
+    const int64_t nq = units > 0 && T > 0 ? n_qkv : 0;
+    const Range rQ{Q, nq}, rK{K, nq}, rV{V, nq}, rdY{dY, nq};
+    const Range rW0{W0, units > 0 ? (w0_per_batch ? units : H) * n_state : 0};
+    const Range rEta{eta, units > 0 ? H * 4 : 0}, rdWo{dW_out, units * n_state};
+    const Range rdQ{dQ, nq}, rdK{dK, nq}, rdV{dV, nq};
+    const Range rdW0{dW0, (w0_per_batch ? units : H) * n_state}, rdEta{deta, H * 4};
+    const Range outs[] = {rdQ, rdK, rdV, rdW0, rdEta};
+    const Range all[] = {rQ, rK, rV, rdY, rW0, rEta, rdWo, rdQ, rdK, rdV, rdW0, rdEta};
+    for (const Range& o : outs) {
+        int hits = 0;   // an output overlaps itself once
+        for (const Range& x : all)
+            hits += overlap(o, x) ? 1 : 0;
+        if (hits > 1) return TTT_ERR_INVALID_ARG;
+    }
+
+    ttt::LinearBwdArgs a{Q, K, V, qkv_dtype, W0, w0_per_batch, eta, B, H, T, d, b,
+                         dY, dW_out, dQ, dK, dV, dW0, deta, static_cast<hipStream_t>(stream)};
+    if (!ttt::linear_backward_supports(a)) return TTT_ERR_UNSUPPORTED;
+    void* ws = nullptr;
+    if (workspace_get(&ws, ttt::linear_backward_workspace_bytes(a), a.stream) != hipSuccess)
+        return TTT_ERR_HIP;
+    return hip_status(ttt::launch_linear_backward(a, ws));
+}
+
 int ttt_mlp_forward(const void* Q, const void* K, const void* V, int qkv_dtype,
                     const float* W1_0, const float* W2_0, int w0_per_batch,
                     const float* eta, int64_t B, int64_t H, int64_t T, int d, int m, int b,

@@ -98,6 +98,19 @@ constexpr SegmentCosts kLinearF32Costs{1.90, 1.20, 0.90, 11.0, 2};
 bool mlp_mfma_supports(const MlpArgs& a);
 hipError_t launch_mlp_mfma(const MlpArgs& a);
 
+// Backward of the TTT-Linear scan (d = 64, b = 16).  The workspace holds the
+// recomputed chunk-start states (and per-chain dW0 when W0 is shared).
+struct LinearBwdArgs {
+    const void* Q; const void* K; const void* V; int dtype;
+    const float* W0; int w0_per_batch; const float* eta;
+    int64_t B, H, T; int d, b;
+    const void* dY; const float* dW_out;
+    void* dQ; void* dK; void* dV; float* dW0; float* deta; hipStream_t stream;
+};
+bool linear_backward_supports(const LinearBwdArgs& a);
+size_t linear_backward_workspace_bytes(const LinearBwdArgs& a);
+hipError_t launch_linear_backward(const LinearBwdArgs& a, void* workspace);
+
 // Decode step.
 hipError_t launch_decode(const DecodeArgs& a);
 

@@ -1,0 +1,519 @@
+// ttt_linear_backward.hip -- backward of the TTT-Linear dual-form scan for
+// head dim d = 64 and mini-batch b = 16, fp32 or bf16 Q/K/V, fp32 state.
+//
+// Outer-loop training differentiates the layer output through the inner
+// updates ("Test-Time Training Layers: How Inner-Loop Gradient Descent
+// Replaces the Transformer KV Cache ...", section "Hardware Parallelization:
+// The Dual Form and Mini-Batch GPU Acceleration": the dual form exists so the
+// layer trains efficiently; the uTTT write-up on thelatestinai.com, Figure
+// 2(b): the read-output Jacobian runs backward through the earlier inner
+// updates).  Given the cotangents dY of Y and dW_out of the final state, one
+// chunk of the forward
+//     E = K W - V,   A = tril(Q K^T),   Y = Q W - eta A E,   W' = W - eta K^T E
+// has, with G' the cotangent of W' (G' = dW_out after the last chunk),
+//     P   = A^T dY + K G'           dE = -eta P     deta += -<P, E>
+//     dA  = -eta tril(dY E^T)
+//     dQ  = dY W^T + dA K
+//     dK  = -eta (P W^T + E G'^T) + dA^T Q
+//     dV  = eta P
+//     G   = G' + Q^T dY + K^T dE    (the cotangent of the chunk-start W)
+// and dW0 is G after the first chunk.
+//
+// One workgroup of 4 waves per (batch, head) chain:
+//   sweep 1 (forward): recompute the chunk-start state W_c of every chunk and
+//     store it in the workspace (16 KB per chunk), wave w updating the 16
+//     output columns [16w, 16w + 16) of W (the loss separates over output
+//     columns);
+//   sweep 2 (reverse over the chunks): phase A is column-local, wave w owns
+//     columns [16w, 16w + 16) of E, P, dE and of the cotangent G (kept in
+//     registers); phase B needs sums over all 64 columns, so wave w there owns
+//     input dims [16w, 16w + 16) of dQ, dK (and dV), reading E, P and G' that
+//     phase A left in LDS.  Two barriers per chunk.
+// Every product is a v_mfma_f32_16x16x4_f32 (one MFMA shape throughout).
+// Layouts (lane l, c = l % 16, g = l / 16): A operand A[c][k-slot g], B
+// operand B[k-slot g][c], accumulator rows 4g..4g+3 of column c.  An
+// accumulator tile is therefore the B operand of a product over its row
+// index (k-step r takes register r: k = 4g + r) and, read as an A operand,
+// the transpose of itself -- which is how S = Q K^T turns into A^T and dA
+// into dA^T without data movement.
+//
+// Inputs of a chunk (Q, K, V, dY as fp32, and W_c) are staged through a
+// two-slot LDS ring, the next chunk's global loads issued before this chunk's
+// products.  LDS rows are padded to 68 floats so the 16 rows a 16-lane group
+// reads fall in different banks.  Tokens past T read as zero: they add
+// nothing to any product, and their rows are not stored.
+#include "ttt_internal.h"
+
+namespace ttt {
+namespace {
+
+constexpr int kD = 64;
+constexpr int kB = 16;
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kP = 68;                          // padded LDS row, floats
+constexpr int kTile = kB * kP;                  // a 16 x 64 tile
+constexpr int kWTile = kD * kP;                 // a 64 x 64 matrix
+constexpr int kSlotQ = 0;
+constexpr int kSlotK = kTile;
+constexpr int kSlotV = 2 * kTile;
+constexpr int kSlotDY = 3 * kTile;
+constexpr int kSlotW = 4 * kTile;
+constexpr int kSlotFloats = 4 * kTile + kWTile;
+constexpr int kOffE = 2 * kSlotFloats;          // E  [16][kP]
+constexpr int kOffP = kOffE + kTile;            // P  [16][kP]
+constexpr int kOffG = kOffP + kTile;            // G' [64][kP]
+constexpr int kDAP = 20;                        // padded row of a wave's dA copy
+constexpr int kOffDA = kOffG + kWTile;          // [4 waves][16][kDAP]
+constexpr int kOffRed = kOffDA + kWaves * kB * kDAP;
+constexpr int kLdsFloats = kOffRed + kWaves;
+constexpr int kLdsBytes = kLdsFloats * 4;       // 100880
+static_assert(kLdsBytes <= kMaxLdsBytes, "LDS budget");
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f32x4 mfma(float a, float b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// Four consecutive elements of a row as fp32 (raw register form while the
+// load is in flight, converted when written to LDS).
+template <typename In> struct Raw;
+template <> struct Raw<float> {
+    typedef f32x4 type;
+    __device__ static type load(const float* p, bool ok)
+    {
+        return ok ? *reinterpret_cast<const f32x4*>(p) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    __device__ static f32x4 to_f32(type x) { return x; }
+};
+template <> struct Raw<uint16_t> {
+    typedef u32x2 type;
+    __device__ static type load(const uint16_t* p, bool ok)
+    {
+        return ok ? *reinterpret_cast<const u32x2*>(p) : u32x2{0u, 0u};
+    }
+    __device__ static f32x4 to_f32(type x)
+    {
+        return f32x4{__uint_as_float(x[0] << 16), __uint_as_float(x[0] & 0xffff0000u),
+                     __uint_as_float(x[1] << 16), __uint_as_float(x[1] & 0xffff0000u)};
+    }
+};
+
+template <typename In>
+struct Stage {
+    typename Raw<In>::type q, k, v, dy;
+    f32x4 w[4];
+};
+
+__device__ __forceinline__ f32x4 lds4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+__device__ __forceinline__ void lds4(float* p, f32x4 x) { *reinterpret_cast<f32x4*>(p) = x; }
+
+template <typename In>
+__global__ void __launch_bounds__(kThreads, 1)
+linear_backward_kernel(const In* __restrict__ Q, const In* __restrict__ K, const In* __restrict__ V,
+                       const float* __restrict__ W0, int w0_per_batch,
+                       const float* __restrict__ eta, int H, int T,
+                       const In* __restrict__ dY, const float* __restrict__ dW_out,
+                       In* __restrict__ dQ, In* __restrict__ dK, In* __restrict__ dV,
+                       float* __restrict__ dW0_chain, float* __restrict__ deta_chain,
+                       float* __restrict__ states)
+{
+    extern __shared__ __attribute__((aligned(16))) float lds[];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = tid >> 6;
+    const int c = lane & 15;
+    const int g = lane >> 4;
+    const int64_t u = blockIdx.x;
+    const int h = static_cast<int>(u % H);
+    const float et = eta[h];
+    const int nchunks = (T + kB - 1) / kB;
+    const int64_t off = u * static_cast<int64_t>(T) * kD;
+    float* st = states + u * static_cast<int64_t>(nchunks) * kD * kD;
+
+    // staging: thread tid moves row tid / 16, columns 4 (tid % 16) .. +3 of
+    // each 16 x 64 tile, and rows tid / 16 + 16 q of W
+    const int srow = tid >> 4;
+    const int scol = 4 * (tid & 15);
+    auto load_stage = [&](Stage<In>& s, int chunk, bool qdy, bool wst) {
+        const int t = chunk * kB + srow;
+        const bool ok = t < T;
+        const int64_t e = off + static_cast<int64_t>(t) * kD + scol;
+        s.k = Raw<In>::load(K + e, ok);
+        s.v = Raw<In>::load(V + e, ok);
+        if (qdy) {
+            s.q = Raw<In>::load(Q + e, ok);
+            s.dy = Raw<In>::load(dY + e, ok);
+        }
+        if (wst) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                s.w[q] = *reinterpret_cast<const f32x4*>(st + static_cast<int64_t>(chunk) * kD * kD + (srow + 16 * q) * kD + scol);
+        }
+    };
+    auto store_stage = [&](const Stage<In>& s, int slot, bool qdy, bool wst) {
+        float* sl = lds + slot * kSlotFloats;
+        lds4(sl + kSlotK + srow * kP + scol, Raw<In>::to_f32(s.k));
+        lds4(sl + kSlotV + srow * kP + scol, Raw<In>::to_f32(s.v));
+        if (qdy) {
+            lds4(sl + kSlotQ + srow * kP + scol, Raw<In>::to_f32(s.q));
+            lds4(sl + kSlotDY + srow * kP + scol, Raw<In>::to_f32(s.dy));
+        }
+        if (wst) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                lds4(sl + kSlotW + (srow + 16 * q) * kP + scol, s.w[q]);
+        }
+    };
+
+    // E_J = K W[:, J] - V[:, J] for this wave's columns J = w, from the
+    // staged K, V of a slot and the W tiles Wt[i] (rows 16 i + 4g + r)
+    auto residual = [&](const float* sl, const float (&Wt)[4][4], f32x4 (&krow)[4]) {
+        f32x4 acc[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            acc[0][r] = -sl[kSlotV + (4 * g + r) * kP + 16 * w + c];
+        acc[1] = acc[2] = acc[3] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            krow[i] = lds4(sl + kSlotK + c * kP + 16 * i + 4 * g);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                acc[i] = mfma(krow[i][r], Wt[i][r], acc[i]);
+        return (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    };
+
+    if (nchunks == 0) {
+        // T = 0: dW0 = dW_out, deta = 0
+#pragma unroll
+        for (int q = 0; q < 16; ++q)
+            dW0_chain[u * kD * kD + q * kThreads + tid] = dW_out[u * kD * kD + q * kThreads + tid];
+        if (tid == 0)
+            deta_chain[u] = 0.f;
+        return;
+    }
+
+    // ---------------- sweep 1: chunk-start states ----------------
+    float Wt[4][4];
+    {
+        const float* w0 = W0 + (w0_per_batch ? u : h) * kD * kD;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                Wt[i][r] = w0[(16 * i + 4 * g + r) * kD + 16 * w + c];
+    }
+    {
+        Stage<In> nx;
+        load_stage(nx, 0, false, false);
+        store_stage(nx, 0, false, false);
+        __syncthreads();
+        for (int ch = 0; ch < nchunks; ++ch) {
+            float* sc = st + static_cast<int64_t>(ch) * kD * kD;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    sc[(16 * i + 4 * g + r) * kD + 16 * w + c] = Wt[i][r];
+            if (ch + 1 == nchunks)
+                break;
+            load_stage(nx, ch + 1, false, false);
+            const float* sl = lds + (ch & 1) * kSlotFloats;
+            f32x4 krow[4];
+            const f32x4 E = residual(sl, Wt, krow);
+            const f32x4 En = -et * E;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                f32x4 acc = {Wt[i][0], Wt[i][1], Wt[i][2], Wt[i][3]};
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    acc = mfma(sl[kSlotK + (4 * g + r) * kP + 16 * i + c], En[r], acc);
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    Wt[i][r] = acc[r];
+            }
+            store_stage(nx, (ch + 1) & 1, false, false);
+            __syncthreads();
+        }
+    }
+    // the states just stored are read back below by other threads
+    __threadfence();
+    __syncthreads();
+
+    // ---------------- sweep 2: reverse over the chunks ----------------
+    float Gt[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            Gt[i][r] = dW_out[u * kD * kD + (16 * i + 4 * g + r) * kD + 16 * w + c];
+    float deta_acc = 0.f;
+    float* Es = lds + kOffE;
+    float* Ps = lds + kOffP;
+    float* Gs = lds + kOffG;
+    float* dAs = lds + kOffDA + w * kB * kDAP;
+
+    Stage<In> nx;
+    load_stage(nx, nchunks - 1, true, true);
+    store_stage(nx, 0, true, true);
+    __syncthreads();
+    for (int ch = nchunks - 1; ch >= 0; --ch) {
+        const int slot = (nchunks - 1 - ch) & 1;
+        const float* sl = lds + slot * kSlotFloats;
+        if (ch > 0)
+            load_stage(nx, ch - 1, true, true);
+
+        // ---- phase A: columns J = w ----
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                Wt[i][r] = sl[kSlotW + (16 * i + 4 * g + r) * kP + 16 * w + c];
+        f32x4 krow[4];
+        const f32x4 E = residual(sl, Wt, krow);
+        // S = Q K^T: lane holds S[t = 4g + r][s = c]; A = tril(S) keeps s <= t
+        f32x4 qrow[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            qrow[i] = lds4(sl + kSlotQ + c * kP + 16 * i + 4 * g);
+        f32x4 sacc[4] = {};
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                sacc[i] = mfma(qrow[i][r], krow[i][r], sacc[i]);
+        f32x4 S = (sacc[0] + sacc[1]) + (sacc[2] + sacc[3]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            S[r] = c <= 4 * g + r ? S[r] : 0.f;
+        // P = A^T dY_J + K G'_J (S as an A operand is A^T)
+        float dyc[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            dyc[r] = sl[kSlotDY + (4 * g + r) * kP + 16 * w + c];
+        f32x4 pacc[4] = {};
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            pacc[0] = mfma(S[r], dyc[r], pacc[0]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                pacc[i] = mfma(krow[i][r], Gt[i][r], pacc[i]);
+        const f32x4 P = (pacc[0] + pacc[1]) + (pacc[2] + pacc[3]);
+        const f32x4 dE = -et * P;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            deta_acc -= P[r] * E[r];
+            Es[(4 * g + r) * kP + 16 * w + c] = E[r];
+            Ps[(4 * g + r) * kP + 16 * w + c] = P[r];
+        }
+        // G' to LDS for phase B, then G = G' + Q^T dY + K^T dE (over tokens)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f32x4 acc = {Gt[i][0], Gt[i][1], Gt[i][2], Gt[i][3]};
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                Gs[(16 * i + 4 * g + r) * kP + 16 * w + c] = Gt[i][r];
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                acc = mfma(sl[kSlotQ + (4 * g + r) * kP + 16 * i + c], dyc[r], acc);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                acc = mfma(sl[kSlotK + (4 * g + r) * kP + 16 * i + c], dE[r], acc);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                Gt[i][r] = acc[r];
+        }
+        __syncthreads();
+
+        // ---- phase B: input dims I = w ----
+        // dA = -eta tril(dY E^T): lane holds dA[t = 4g + r][s = c]
+        f32x4 dyrow[4], erow[4];
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb) {
+            dyrow[jb] = lds4(sl + kSlotDY + c * kP + 16 * jb + 4 * g);
+            erow[jb] = lds4(Es + c * kP + 16 * jb + 4 * g);
+        }
+        f32x4 aacc[4] = {};
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int jb = 0; jb < 4; ++jb)
+                aacc[jb] = mfma(dyrow[jb][r], erow[jb][r], aacc[jb]);
+        f32x4 dA = (aacc[0] + aacc[1]) + (aacc[2] + aacc[3]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            dA[r] = c <= 4 * g + r ? -et * dA[r] : 0.f;
+            dAs[(4 * g + r) * kDAP + c] = dA[r];
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // dQ_I = dY W[I, :]^T + dA K_I
+        f32x4 wrow[4];
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb)
+            wrow[jb] = lds4(sl + kSlotW + (16 * w + c) * kP + 16 * jb + 4 * g);
+        f32x4 qacc[4] = {};
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int jb = 0; jb < 4; ++jb)
+                qacc[jb] = mfma(dyrow[jb][r], wrow[jb][r], qacc[jb]);
+        {
+            const f32x4 darow = lds4(dAs + c * kDAP + 4 * g);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                qacc[0] = mfma(darow[r], sl[kSlotK + (4 * g + r) * kP + 16 * w + c], qacc[0]);
+        }
+        const f32x4 dq = (qacc[0] + qacc[1]) + (qacc[2] + qacc[3]);
+        // dK_I = -eta (P W[I, :]^T + E G'[I, :]^T) + dA^T Q_I
+        f32x4 kacc[4] = {};
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb) {
+            const f32x4 prow = lds4(Ps + c * kP + 16 * jb + 4 * g);
+            const f32x4 grow = lds4(Gs + (16 * w + c) * kP + 16 * jb + 4 * g);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                kacc[jb] = mfma(prow[r], wrow[jb][r], kacc[jb]);
+                kacc[jb] = mfma(erow[jb][r], grow[r], kacc[jb]);
+            }
+        }
+        f32x4 dk = -et * ((kacc[0] + kacc[1]) + (kacc[2] + kacc[3]));
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            dk = mfma(dA[r], sl[kSlotQ + (4 * g + r) * kP + 16 * w + c], dk);
+
+        // stores: rows t = 16 ch + 4g + r, column 16 w + c (P of phase A is
+        // this wave's column block, so dV = eta P needs no exchange)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = ch * kB + 4 * g + r;
+            if (t < T) {
+                const int64_t e = off + static_cast<int64_t>(t) * kD + 16 * w + c;
+                store_elem(dQ, e, dq[r]);
+                store_elem(dK, e, dk[r]);
+                store_elem(dV, e, et * P[r]);
+            }
+        }
+        if (ch > 0)
+            store_stage(nx, slot ^ 1, true, true);
+        __syncthreads();
+    }
+
+    // dW0 of this chain is the cotangent of the first chunk-start state
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            dW0_chain[u * kD * kD + (16 * i + 4 * g + r) * kD + 16 * w + c] = Gt[i][r];
+    // deta: sum over the lanes, then over the waves
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1)
+        deta_acc += __shfl_xor(deta_acc, m);
+    if (lane == 0)
+        lds[kOffRed + w] = deta_acc;
+    __syncthreads();
+    if (tid == 0)
+        deta_chain[u] = (lds[kOffRed] + lds[kOffRed + 1]) + (lds[kOffRed + 2] + lds[kOffRed + 3]);
+}
+
+// Sums over the batch, in batch order: dW0 (when W0 is shared by the batch)
+// and deta (always: eta is one value per head).
+__global__ void __launch_bounds__(256)
+linear_backward_reduce_kernel(const float* __restrict__ dW0_chain, const float* __restrict__ deta_chain,
+                              int64_t B, int H, int reduce_w, float* __restrict__ dW0,
+                              float* __restrict__ deta)
+{
+    const int64_t x = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    const int64_t n = static_cast<int64_t>(H) * kD * kD;
+    if (reduce_w && x < n) {
+        float s = 0.f;
+        for (int64_t bb = 0; bb < B; ++bb)
+            s += dW0_chain[bb * n + x];
+        dW0[x] = s;
+    }
+    if (x < H) {
+        float s = 0.f;
+        for (int64_t bb = 0; bb < B; ++bb)
+            s += deta_chain[bb * H + x];
+        deta[x] = s;
+    }
+}
+
+}  // namespace
+
+bool linear_backward_supports(const LinearBwdArgs& a)
+{
+    return a.d == kD && a.b == kB;
+}
+
+size_t linear_backward_workspace_bytes(const LinearBwdArgs& a)
+{
+    const int64_t units = a.B * a.H;
+    const int64_t nchunks = (a.T + kB - 1) / kB;
+    const size_t states = static_cast<size_t>(units) * nchunks * kD * kD * 4;
+    const size_t dw = a.w0_per_batch ? 0 : static_cast<size_t>(units) * kD * kD * 4;
+    return states + dw + static_cast<size_t>(units) * 4 + 256;
+}
+
+hipError_t launch_linear_backward(const LinearBwdArgs& a, void* workspace)
+{
+    const int64_t units = a.B * a.H;
+    const int64_t nchunks = (a.T + kB - 1) / kB;
+    char* ws = static_cast<char*>(workspace);
+    float* states = reinterpret_cast<float*>(ws);
+    ws += static_cast<size_t>(units) * nchunks * kD * kD * 4;
+    float* dw_chain = a.w0_per_batch ? a.dW0 : reinterpret_cast<float*>(ws);
+    if (!a.w0_per_batch)
+        ws += static_cast<size_t>(units) * kD * kD * 4;
+    float* deta_chain = reinterpret_cast<float*>(ws);
+
+    const dim3 grid(static_cast<unsigned>(units)), block(kThreads);
+    hipError_t e = hipSuccess;
+    if (units == 0) {
+        // nothing to differentiate: the batch sums below are zero
+    } else if (a.dtype == 0) {
+        e = hipFuncSetAttribute(reinterpret_cast<const void*>(linear_backward_kernel<float>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+        if (e != hipSuccess)
+            return e;
+        hipLaunchKernelGGL(linear_backward_kernel<float>, grid, block, kLdsBytes, a.stream,
+                           static_cast<const float*>(a.Q), static_cast<const float*>(a.K),
+                           static_cast<const float*>(a.V), a.W0, a.w0_per_batch, a.eta,
+                           static_cast<int>(a.H), static_cast<int>(a.T),
+                           static_cast<const float*>(a.dY), a.dW_out, static_cast<float*>(a.dQ),
+                           static_cast<float*>(a.dK), static_cast<float*>(a.dV), dw_chain,
+                           deta_chain, states);
+    } else {
+        e = hipFuncSetAttribute(reinterpret_cast<const void*>(linear_backward_kernel<uint16_t>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+        if (e != hipSuccess)
+            return e;
+        hipLaunchKernelGGL(linear_backward_kernel<uint16_t>, grid, block, kLdsBytes, a.stream,
+                           static_cast<const uint16_t*>(a.Q), static_cast<const uint16_t*>(a.K),
+                           static_cast<const uint16_t*>(a.V), a.W0, a.w0_per_batch, a.eta,
+                           static_cast<int>(a.H), static_cast<int>(a.T),
+                           static_cast<const uint16_t*>(a.dY), a.dW_out,
+                           static_cast<uint16_t*>(a.dQ), static_cast<uint16_t*>(a.dK),
+                           static_cast<uint16_t*>(a.dV), dw_chain, deta_chain, states);
+    }
+    if (units > 0) {
+        e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+    }
+    const int64_t n = a.w0_per_batch ? a.H : a.H * kD * kD;
+    hipLaunchKernelGGL(linear_backward_reduce_kernel, dim3(static_cast<unsigned>((n + 255) / 256)),
+                       dim3(256), 0, a.stream, dw_chain, deta_chain, a.B, static_cast<int>(a.H),
+                       a.w0_per_batch ? 0 : 1, a.dW0, a.deta);
+    return hipGetLastError();
+}
+
+}  // namespace ttt

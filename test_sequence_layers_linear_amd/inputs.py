@@ -21,6 +21,10 @@ N(0, 0.02) is read as a standard deviation of 0.02.  Real workloads are
 LayerNorm'd projections of language-model activations; iid Gaussians with
 unit-norm keys stand in for them.
 
+Backward cotangents (make_cotangents): dY ~ N(0, 1/d) in the input dtype and
+dW_out ~ N(0, 1/d) fp32, from their own seed -- a stand-in for the gradient an
+outer loss sends back into the layer.
+
 Generator: numpy.random.default_rng(seed), float32 standard normals scaled in
 float32, then cast to the input dtype (bf16 by round-to-nearest-even through
 torch).  Draw order: Q, K, V, initial state (W0, or W1 then W2), eta, then the
@@ -127,6 +131,20 @@ def make_inputs(w: Workload, seed: int, device="cpu", w0_per_batch: bool = False
         for name in ("dq", "dk", "dv"):
             out[name] = torch.from_numpy(_normal(rng, dshp, std)).to(w.torch_dtype)
     return {k: v.to(device) for k, v in out.items()}
+
+
+def make_cotangents(w: Workload, seed: int, device="cpu", zero_state: bool = False) -> dict:
+    """Seeded cotangents for the backward of a TTT-Linear workload: dY
+    [B,H,T,d] in the input dtype and dW_out [B,H,d,d] fp32 (zeros with
+    ``zero_state``, the case of a layer whose final state is not used)."""
+    rng = np.random.default_rng(seed)
+    std = 1.0 / math.sqrt(w.d)
+    dY = torch.from_numpy(_normal(rng, (w.B, w.H, w.T, w.d), std)).to(w.torch_dtype)
+    if zero_state:
+        dWo = torch.zeros((w.B, w.H, w.d, w.d), dtype=torch.float32)
+    else:
+        dWo = torch.from_numpy(_normal(rng, (w.B, w.H, w.d, w.d), std))
+    return {"dY": dY.to(device), "dW_out": dWo.to(device)}
 
 
 def default_seed(config: int) -> int:

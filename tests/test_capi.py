@@ -37,7 +37,8 @@ def lib():
 def test_exports_every_declared_function(lib):
     names = declared_functions()
     assert set(names) >= {"ttt_linear_forward", "ttt_mlp_forward", "ttt_linear_decode_step",
-                          "ttt_linear_segments", "ttt_status_string", "ttt_abi_version"}
+                          "ttt_linear_backward", "ttt_linear_segments", "ttt_status_string",
+                          "ttt_abi_version"}
     for n in names:
         assert hasattr(lib, n), f"{n} declared in ttt.h but not exported"
 
@@ -106,6 +107,30 @@ def dec(lib, q=QA, W=W0A, y=YA, dt=1, B=2, H=24, d=64):
 ])
 def test_decode_validation(lib, kw, expect):
     assert dec(lib, **kw) == expect
+
+
+DYA, DWOA, DQA, DKA, DVA, DW0A, DETA = (0xA0_0000_0000 + 0x10_0000_0000 * i for i in range(7))
+
+
+def bwd(lib, Q=QA, dt=1, W0=W0A, pb=0, eta=ETA, B=2, H=3, T=64, d=64, b=16, dY=DYA, dWo=DWOA,
+        dQ=DQA, dK=DKA, dV=DVA, dW0=DW0A, deta=DETA):
+    return lib.ttt_linear_backward(Q, KA, VA, dt, W0, pb, eta, B, H, T, d, b, dY, dWo, dQ, dK, dV,
+                                   dW0, deta, None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(B=-1), INVALID), (dict(T=-1), INVALID), (dict(b=0), INVALID), (dict(pb=3), INVALID),
+    (dict(Q=None), INVALID), (dict(dY=None), INVALID), (dict(dWo=None), INVALID),
+    (dict(dQ=None), INVALID), (dict(dW0=None), INVALID), (dict(deta=None), INVALID),
+    (dict(W0=None), INVALID), (dict(eta=None), INVALID),
+    (dict(d=32), UNSUPPORTED), (dict(b=8), UNSUPPORTED), (dict(dt=5), UNSUPPORTED),
+    (dict(dQ=QA), INVALID), (dict(dK=DQA + 8), INVALID), (dict(dV=DYA), INVALID),
+    (dict(dW0=DWOA), INVALID), (dict(deta=ETA), INVALID), (dict(dW0=W0A), INVALID),
+    (dict(deta=DW0A + 16), INVALID),
+    (dict(H=0), OK),
+])
+def test_backward_validation(lib, kw, expect):
+    assert bwd(lib, **kw) == expect
 
 
 def test_binding_rejects_cpu_tensors():
