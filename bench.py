@@ -21,6 +21,12 @@ segment scans, three launches back to back on the stream (roofline.kernel
 names them).  The decode steps of a workload run as one captured HIP graph.
 cpu_baseline = the fp64 oracle (plain loops, OpenMP over chains) timed on
 this host's cores on a bounded sample of the same workload.
+
+Each TTT-Linear workload also reports "backward": ttt_linear_backward (the
+gradients of Q, K, V, W0 and eta for seeded cotangents dY, dW_out) timed the
+same way, with its own roofline (fp32 MFMA: the kernel computes in fp32 for
+both input dtypes).  It is reported beside the forward, not folded into the
+headline value.
 """
 from __future__ import annotations
 
@@ -45,6 +51,7 @@ KERNEL_SOURCES = {
     "linear_mfma_f32_kernel[scan]": "ttt_linear_mfma_f32.hip",
     "linear_mfma_f32_kernel[maps]": "ttt_linear_mfma_f32.hip",
     "linear_combine_kernel": "ttt_linear_combine.hip",
+    "linear_backward_kernel": "ttt_linear_backward.hip",
     "linear_generic_kernel": "ttt_generic.hip",
     "mlp_generic_kernel": "ttt_generic.hip",
     "mlp_mfma_kernel": "ttt_mlp_mfma.hip",
@@ -66,6 +73,20 @@ def linear_work(w):
     d, units = w.d, w.B * w.H
     flops = units * sum(6 * n * d * d + 4 * n * n * d for n in _chunks(w.T, w.b))
     nbytes = units * w.T * 4 * d * s + w.H * d * d * 4 + units * d * d * 4
+    return flops, nbytes
+
+
+def linear_backward_work(w):
+    """flops and HBM bytes of one ttt_linear_backward call.  Flops per chunk
+    of n tokens: E, P (K G), dQ (dY W^T), two in dK, two in G -- 14 n d^2 --
+    and S, A^T dY, dA, dA K, dA^T Q -- 10 n^2 d.  Bytes: Q, K, V, dY read,
+    dQ, dK, dV written, W0, dW_out, dW0 once (the recomputed chunk-start
+    states that the kernel stores and reloads are extra traffic, not
+    algorithmic)."""
+    s = 4 if w.dtype == "fp32" else 2
+    d, units = w.d, w.B * w.H
+    flops = units * sum(14 * n * d * d + 10 * n * n * d for n in _chunks(w.T, w.b))
+    nbytes = units * w.T * 7 * d * s + (w.H + 2 * units) * d * d * 4
     return flops, nbytes
 
 
@@ -238,6 +259,31 @@ class Runner:
             fwd, dec = total / steps, 0.0
         return wall / steps, fwd, dec
 
+    def measure_backward(self, steps, warmup):
+        """Mean duration of ttt_linear_backward over `steps` calls between two
+        synchronisations (HIP events on the launch stream at both ends)."""
+        torch, g, w = self.torch, self.g, self.w
+        from test_sequence_layers_linear_amd.inputs import make_cotangents
+        cot = {k: v.cuda() for k, v in make_cotangents(w, 7).items()}
+        outs = dict(dQ=torch.empty_like(g["Q"]), dK=torch.empty_like(g["Q"]),
+                    dV=torch.empty_like(g["Q"]), dW0=torch.empty_like(g["W0"]),
+                    deta=torch.empty_like(g["eta"]))
+
+        def call():
+            self.ttt.ttt_linear_backward(g["Q"], g["K"], g["V"], g["W0"], g["eta"], w.b,
+                                         cot["dY"], cot["dW_out"], **outs)
+        for _ in range(warmup):
+            call()
+        torch.cuda.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record()
+        for _ in range(steps):
+            call()
+        end.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / 1e3 / steps
+
     def measure_cold(self, reps):
         """Forward duration with the 256 MB last-level cache flushed before each launch."""
         torch = self.torch
@@ -319,6 +365,13 @@ def measure_workload(cfg, steps, warmup, cold_reps):
         cold = r.measure_cold(cold_reps)
         out["forward_us_cold_llc"] = cold * 1e6
         out["roofline_cold_llc_frac"] = roofline(w, flops, nbytes, cold, kern)["frac"]
+    if w.kind == "linear" and w.d == 64 and w.b == 16:
+        bt = r.measure_backward(max(3, steps // 2), 2)
+        bf, bb = linear_backward_work(w)
+        wf = w.with_(dtype="fp32")       # the kernel's arithmetic: fp32 MFMA
+        rf = roofline(wf, bf, bb, bt, ["linear_backward_kernel"])
+        rf["traffic"] = stored_traffic(["linear_backward_kernel"], w.name)
+        out["backward"] = {"us": bt * 1e6, "tokens_per_s": w.B * w.T / bt, "roofline": rf}
     if w.decode_steps:
         df, db = decode_work(w)
         per = dec / w.decode_steps

@@ -178,9 +178,19 @@ int ttt_linear_decode_step(const void* q, const void* k, const void* v, int qkv_
  *   d = 64 and b = 16 only (other shapes: TTT_ERR_UNSUPPORTED).
  *   B*H = 0 writes dW0 = 0 and deta = 0 (sums over an empty batch); T = 0
  *   gives dW0 = dW_out (summed over the batch when W0 is shared), deta = 0.
- * No output may overlap any other argument.  Workspace (the stream's, as for
- * the segmented scan): B*H*ceil(T/16)*d*d*4 bytes of chunk-start states,
- * plus B*H*d*d*4 bytes when W0 is shared.
+ * No output may overlap any other argument.
+ *
+ * Segments.  When the chains are too few for the GPU, the backward is cut
+ * into sequence segments like the forward scan.  The cotangent G is affine
+ * too: per mini-batch G_start = (I - eta_h K^T K) G_end + (Q - eta_h A K)^T dY,
+ * which needs no W.  So the forward's maps and composition give every
+ * segment's start W, cotangent maps composed from dW_out backwards give every
+ * segment's end G, and then all segments run at once (deta and dW0 are
+ * summed in a fixed order).  ttt_linear_backward_segments reports the count;
+ * TTT_LINEAR_BWD_SEGMENTS=S (1..30) forces it.  Workspace (the stream's),
+ * in d*d*4-byte matrices per chain: S*ceil(ceil(T/16)/S) recomputed
+ * chunk-start states, with S > 1 another 6 S - 4 (maps, start and end
+ * states), and one more when W0 is shared (per-chain dW0).
  * Errors as for ttt_linear_forward.
  */
 int ttt_linear_backward(const void* Q, const void* K, const void* V, int qkv_dtype,
@@ -189,6 +199,12 @@ int ttt_linear_backward(const void* Q, const void* K, const void* V, int qkv_dty
                         const void* dY, const float* dW_out,
                         void* dQ, void* dK, void* dV, float* dW0, float* deta,
                         void* stream);
+/*
+ * Number of sequence segments ttt_linear_backward would cut each chain into
+ * for these sizes on the current device (1 = unsegmented).  Negative
+ * ttt_status for arguments ttt_linear_backward would reject.
+ */
+int ttt_linear_backward_segments(int64_t B, int64_t H, int64_t T, int d, int b, int qkv_dtype);
 /* Static, human-readable text for a status code (never NULL). */
 /*
  * Number of sequence segments ttt_linear_forward would cut each chain into

@@ -58,6 +58,8 @@ def load_library():
     lib.ttt_linear_backward.argtypes = [P, P, P, I, P, I, P, L, L, L, I, I, P, P,
                                         P, P, P, P, P, P]
     lib.ttt_linear_backward.restype = I
+    lib.ttt_linear_backward_segments.argtypes = [L, L, L, I, I, I]
+    lib.ttt_linear_backward_segments.restype = I
     lib.ttt_linear_segments.argtypes = [L, L, L, I, I, I]
     lib.ttt_linear_segments.restype = I
     lib.ttt_status_string.argtypes = [I]
@@ -249,9 +251,19 @@ def ttt_linear_segments(B: int, H: int, T: int, d: int, b: int, dtype=torch.bflo
     return n
 
 
+def ttt_linear_backward_segments(B: int, H: int, T: int, d: int, b: int,
+                                 dtype=torch.bfloat16) -> int:
+    """Sequence segments ttt_linear_backward cuts each chain into for these
+    sizes on the current device (1 = unsegmented)."""
+    code = TTT_F32 if dtype == torch.float32 else TTT_BF16
+    n = load_library().ttt_linear_backward_segments(int(B), int(H), int(T), int(d), int(b), code)
+    _check(min(n, 0))
+    return n
+
+
 __all__ = [
     "ttt_linear_forward", "ttt_mlp_forward", "ttt_linear_decode_step", "ttt_linear_backward",
-    "ttt_linear_segments",
+    "ttt_linear_segments", "ttt_linear_backward_segments",
     "load_library",
     "status_string", "TTTError", "LIB_PATH", "TTT_F32", "TTT_BF16",
 ]

@@ -107,6 +107,42 @@ ttt::SegmentPlan plan_segments(int64_t units, int64_t T, int chunk, const ttt::S
     return p;
 }
 
+// Segment count for the backward of a TTT-Linear scan: each segment pays
+// its chunks' forward map, cotangent map and backward, and the two
+// compositions (S - 1) steps each, plus four extra launches; every launch
+// fits one workgroup per CU.  TTT_LINEAR_BWD_SEGMENTS=S forces S segments.
+ttt::SegmentPlan plan_backward(int64_t units, int64_t T, int chunk, const ttt::BwdCosts& cost)
+{
+    ttt::SegmentPlan p;
+    p.seg_len = T;
+    const int64_t chunks = (T + chunk - 1) / chunk;
+    if (const char* env = getenv("TTT_LINEAR_BWD_SEGMENTS")) {
+        const long S = std::min<long>(strtol(env, nullptr, 10), ttt::kMaxSegments);
+        if (S >= 1 && chunks > 0) {
+            p.seg_len = ((chunks + S - 1) / S) * chunk;
+            p.nseg = static_cast<int>((T + p.seg_len - 1) / p.seg_len);
+            return p;
+        }
+    }
+    const int64_t cus = device_cus();
+    if (cus <= 0 || 2 * units > cus || chunks < 4) return p;
+    const int map_blocks = std::max(2, cost.fmap_blocks_per_segment);
+    double best = static_cast<double>(chunks) * cost.bwd;
+    int best_s = 1;
+    for (int S = 2; S <= ttt::kMaxSegments; ++S) {
+        if (units * S > cus || units * (S - 1) * map_blocks > cus) break;
+        const int64_t per = (chunks + S - 1) / S;
+        if (per < 2) break;
+        const double t = per * (cost.bwd + cost.fmap + cost.gmap) + 2.0 * (S - 1) * cost.apply + cost.launch;
+        if (t < best) { best = t; best_s = S; }
+    }
+    if (best_s > 1) {
+        p.seg_len = ((chunks + best_s - 1) / best_s) * chunk;
+        p.nseg = static_cast<int>((T + p.seg_len - 1) / p.seg_len);
+    }
+    return p;
+}
+
 // Workspace for the segment maps: one device buffer per (device, stream),
 // grown on demand and kept until the process ends.  Calls on one stream are
 // ordered by the stream, so they can share its buffer; calls on different
@@ -286,10 +322,25 @@ int ttt_linear_backward(const void* Q, const void* K, const void* V, int qkv_dty
     ttt::LinearBwdArgs a{Q, K, V, qkv_dtype, W0, w0_per_batch, eta, B, H, T, d, b,
                          dY, dW_out, dQ, dK, dV, dW0, deta, static_cast<hipStream_t>(stream)};
     if (!ttt::linear_backward_supports(a)) return TTT_ERR_UNSUPPORTED;
+    ttt::SegmentPlan p;
+    if (units > 0)
+        p = plan_backward(units, T, b, qkv_dtype == TTT_BF16 ? ttt::kLinearBwdBf16Costs
+                                                              : ttt::kLinearBwdF32Costs);
     void* ws = nullptr;
-    if (workspace_get(&ws, ttt::linear_backward_workspace_bytes(a), a.stream) != hipSuccess)
+    if (workspace_get(&ws, ttt::linear_backward_workspace_bytes(a, p), a.stream) != hipSuccess)
         return TTT_ERR_HIP;
-    return hip_status(ttt::launch_linear_backward(a, ws));
+    return hip_status(ttt::launch_linear_backward(a, p, ws));
+}
+
+int ttt_linear_backward_segments(int64_t B, int64_t H, int64_t T, int d, int b, int qkv_dtype)
+{
+    if (B < 0 || H < 0 || T < 0 || b < 1) return TTT_ERR_INVALID_ARG;
+    if (!valid_dtype(qkv_dtype) || d != 64 || b != 16) return TTT_ERR_UNSUPPORTED;
+    int64_t units = B;
+    if (!mul_ok(units, H) || units > kMaxUnits) return TTT_ERR_UNSUPPORTED;
+    if (units == 0 || T == 0) return 1;
+    return plan_backward(units, T, b, qkv_dtype == TTT_BF16 ? ttt::kLinearBwdBf16Costs
+                                                            : ttt::kLinearBwdF32Costs).nseg;
 }
 
 int ttt_mlp_forward(const void* Q, const void* K, const void* V, int qkv_dtype,

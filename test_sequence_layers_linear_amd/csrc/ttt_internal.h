@@ -75,7 +75,29 @@ struct SegmentPlan {
     int64_t seg_len = 0;
     float* maps = nullptr;
     float* wstart = nullptr;
+    bool starts_only = false;   // maps and start states only, no segment scans
 };
+
+// Block id -> (chain u, block s of the chain) for nb blocks per chain.  With
+// at least 8 chains every block of chain u gets id = u (mod 8): workgroups
+// are dispatched to the 8 XCDs round robin, so they all share XCD u % 8 and
+// its L2 (grid 8 nb ceil(units / 8); ids with u >= units do nothing).  With
+// fewer chains that would leave XCDs idle, so blocks are numbered plainly.
+__device__ __forceinline__ void xcd_block(int id, int nb, int64_t units, int64_t& u, int& s)
+{
+    if (units < 8) {
+        u = id / nb;
+        s = id % nb;
+        return;
+    }
+    const int t = id >> 3;
+    u = 8 * static_cast<int64_t>(t / nb) + (id & 7);
+    s = t % nb;
+}
+__host__ __device__ inline int64_t placed_grid(int64_t units, int nb)
+{
+    return units < 8 ? units * nb : 8 * nb * ((units + 7) / 8);
+}
 hipError_t launch_linear_combine(const LinearArgs& a, const SegmentPlan& p);
 size_t linear_combine_lds_bytes(int nseg);
 // most segments per chain (the combine step keeps every start state in LDS)
@@ -98,8 +120,12 @@ constexpr SegmentCosts kLinearF32Costs{1.90, 1.20, 0.90, 11.0, 2};
 bool mlp_mfma_supports(const MlpArgs& a);
 hipError_t launch_mlp_mfma(const MlpArgs& a);
 
-// Backward of the TTT-Linear scan (d = 64, b = 16).  The workspace holds the
-// recomputed chunk-start states (and per-chain dW0 when W0 is shared).
+// Backward of the TTT-Linear scan (d = 64, b = 16), optionally cut into
+// sequence segments like the forward: the forward maps give every segment's
+// start state, cotangent maps composed from dW_out backwards give every
+// segment's end cotangent, and then all segments run at once.  The workspace
+// holds those maps and states, the recomputed chunk-start states, and
+// per-chain dW0 (shared W0) and per-segment deta.
 struct LinearBwdArgs {
     const void* Q; const void* K; const void* V; int dtype;
     const float* W0; int w0_per_batch; const float* eta;
@@ -108,8 +134,18 @@ struct LinearBwdArgs {
     void* dQ; void* dK; void* dV; float* dW0; float* deta; hipStream_t stream;
 };
 bool linear_backward_supports(const LinearBwdArgs& a);
-size_t linear_backward_workspace_bytes(const LinearBwdArgs& a);
-hipError_t launch_linear_backward(const LinearBwdArgs& a, void* workspace);
+// Latencies (us) that size the backward's segment split: backward chunk,
+// forward map chunk, cotangent map chunk, one composition step, the fixed
+// cost of the four extra launches; workgroups per segment of the forward
+// maps launch (the cotangent maps always take two).
+struct BwdCosts {
+    double bwd, fmap, gmap, apply, launch;
+    int fmap_blocks_per_segment;
+};
+constexpr BwdCosts kLinearBwdF32Costs{5.2, 1.2, 1.5, 0.9, 20.0, 2};
+constexpr BwdCosts kLinearBwdBf16Costs{5.2, 0.43, 1.5, 0.9, 20.0, 1};
+size_t linear_backward_workspace_bytes(const LinearBwdArgs& a, const SegmentPlan& p);
+hipError_t launch_linear_backward(const LinearBwdArgs& a, const SegmentPlan& p, void* workspace);
 
 // Decode step.
 hipError_t launch_decode(const DecodeArgs& a);

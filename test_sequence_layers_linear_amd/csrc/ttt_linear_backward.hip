@@ -111,15 +111,26 @@ struct Stage {
 __device__ __forceinline__ f32x4 lds4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
 __device__ __forceinline__ void lds4(float* p, f32x4 x) { *reinterpret_cast<f32x4*>(p) = x; }
 
-template <typename In>
+// kGMap = false: the backward of segment s of a chain (all of it when
+//   nseg = 1): sweep 1 recomputes the segment's chunk-start states from its
+//   start state (W0, or wstart[u][s]) into the workspace, sweep 2 runs from the
+//   cotangent of the segment's end state (dW_out, or gend[u][nseg - 1 - s])
+//   back to its start, writing dQ, dK, dV of the segment's rows, the
+//   segment's share of deta and, for segment 0, dW0 of the chain.
+// kGMap = true: the affine map of the cotangent over segment s >= 1,
+//   G_start = M^G G_end + N^G (M^G from G_end = I with dY = 0, block half 0;
+//   N^G from G_end = 0 with the segment's dY, half 1), stored in the order
+//   the composition runs: gmaps[u][nseg - 1 - s][half].  No W is needed.
+template <typename In, bool kGMap>
 __global__ void __launch_bounds__(kThreads, 1)
 linear_backward_kernel(const In* __restrict__ Q, const In* __restrict__ K, const In* __restrict__ V,
                        const float* __restrict__ W0, int w0_per_batch,
-                       const float* __restrict__ eta, int H, int T,
+                       const float* __restrict__ eta, int H, int T, int64_t units, int seg_len,
+                       int nseg, const float* __restrict__ wstart, const float* __restrict__ gend,
                        const In* __restrict__ dY, const float* __restrict__ dW_out,
                        In* __restrict__ dQ, In* __restrict__ dK, In* __restrict__ dV,
                        float* __restrict__ dW0_chain, float* __restrict__ deta_chain,
-                       float* __restrict__ states)
+                       float* __restrict__ states, float* __restrict__ gmaps)
 {
     extern __shared__ __attribute__((aligned(16))) float lds[];
 
@@ -128,45 +139,63 @@ linear_backward_kernel(const In* __restrict__ Q, const In* __restrict__ K, const
     const int w = tid >> 6;
     const int c = lane & 15;
     const int g = lane >> 4;
-    const int64_t u = blockIdx.x;
+
+    int64_t u = blockIdx.x;
+    int s = 0, half = 0;
+    if (nseg > 1) {
+        xcd_block(blockIdx.x, kGMap ? 2 * (nseg - 1) : nseg, units, u, s);
+        if (u >= units)                  // padding of the XCD placement
+            return;
+        if (kGMap) {
+            half = s & 1;
+            s = (s >> 1) + 1;
+        }
+    }
     const int h = static_cast<int>(u % H);
     const float et = eta[h];
-    const int nchunks = (T + kB - 1) / kB;
+    const int seg_chunks = seg_len / kB;
+    const int c0 = s * seg_chunks;
+    const int c1 = min((T + kB - 1) / kB, c0 + seg_chunks);
     const int64_t off = u * static_cast<int64_t>(T) * kD;
-    float* st = states + u * static_cast<int64_t>(nchunks) * kD * kD;
+    float* st = states + (u * nseg + s) * static_cast<int64_t>(seg_chunks) * kD * kD;
+    // the M half of a cotangent map sees dY = 0 (a per-workgroup, uniform branch)
+    const bool use_dy = !kGMap || half == 1;
 
     // staging: thread tid moves row tid / 16, columns 4 (tid % 16) .. +3 of
     // each 16 x 64 tile, and rows tid / 16 + 16 q of W
     const int srow = tid >> 4;
     const int scol = 4 * (tid & 15);
-    auto load_stage = [&](Stage<In>& s, int chunk, bool qdy, bool wst) {
+    auto load_stage = [&](Stage<In>& x, int chunk, bool qdy, bool wst) {
         const int t = chunk * kB + srow;
         const bool ok = t < T;
         const int64_t e = off + static_cast<int64_t>(t) * kD + scol;
-        s.k = Raw<In>::load(K + e, ok);
-        s.v = Raw<In>::load(V + e, ok);
+        x.k = Raw<In>::load(K + e, ok);
+        if (!kGMap)
+            x.v = Raw<In>::load(V + e, ok);
         if (qdy) {
-            s.q = Raw<In>::load(Q + e, ok);
-            s.dy = Raw<In>::load(dY + e, ok);
+            x.q = Raw<In>::load(Q + e, ok);
+            x.dy = Raw<In>::load(dY + e, ok);
         }
         if (wst) {
+            const float* src = st + static_cast<int64_t>(chunk - c0) * kD * kD;
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-                s.w[q] = *reinterpret_cast<const f32x4*>(st + static_cast<int64_t>(chunk) * kD * kD + (srow + 16 * q) * kD + scol);
+                x.w[q] = *reinterpret_cast<const f32x4*>(src + (srow + 16 * q) * kD + scol);
         }
     };
-    auto store_stage = [&](const Stage<In>& s, int slot, bool qdy, bool wst) {
+    auto store_stage = [&](const Stage<In>& x, int slot, bool qdy, bool wst) {
         float* sl = lds + slot * kSlotFloats;
-        lds4(sl + kSlotK + srow * kP + scol, Raw<In>::to_f32(s.k));
-        lds4(sl + kSlotV + srow * kP + scol, Raw<In>::to_f32(s.v));
+        lds4(sl + kSlotK + srow * kP + scol, Raw<In>::to_f32(x.k));
+        if (!kGMap)
+            lds4(sl + kSlotV + srow * kP + scol, Raw<In>::to_f32(x.v));
         if (qdy) {
-            lds4(sl + kSlotQ + srow * kP + scol, Raw<In>::to_f32(s.q));
-            lds4(sl + kSlotDY + srow * kP + scol, Raw<In>::to_f32(s.dy));
+            lds4(sl + kSlotQ + srow * kP + scol, Raw<In>::to_f32(x.q));
+            lds4(sl + kSlotDY + srow * kP + scol, Raw<In>::to_f32(x.dy));
         }
         if (wst) {
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-                lds4(sl + kSlotW + (srow + 16 * q) * kP + scol, s.w[q]);
+                lds4(sl + kSlotW + (srow + 16 * q) * kP + scol, x.w[q]);
         }
     };
 
@@ -189,42 +218,31 @@ linear_backward_kernel(const In* __restrict__ Q, const In* __restrict__ K, const
         return (acc[0] + acc[1]) + (acc[2] + acc[3]);
     };
 
-    if (nchunks == 0) {
-        // T = 0: dW0 = dW_out, deta = 0
-#pragma unroll
-        for (int q = 0; q < 16; ++q)
-            dW0_chain[u * kD * kD + q * kThreads + tid] = dW_out[u * kD * kD + q * kThreads + tid];
-        if (tid == 0)
-            deta_chain[u] = 0.f;
-        return;
-    }
-
-    // ---------------- sweep 1: chunk-start states ----------------
+    // ---------------- sweep 1: chunk-start states of the segment ----------------
     float Wt[4][4];
-    {
-        const float* w0 = W0 + (w0_per_batch ? u : h) * kD * kD;
+    if (!kGMap && c1 > c0) {
+        const float* w0 = nseg > 1 ? wstart + (u * nseg + s) * kD * kD
+                                   : W0 + (w0_per_batch ? u : h) * kD * kD;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 Wt[i][r] = w0[(16 * i + 4 * g + r) * kD + 16 * w + c];
-    }
-    {
         Stage<In> nx;
-        load_stage(nx, 0, false, false);
+        load_stage(nx, c0, false, false);
         store_stage(nx, 0, false, false);
         __syncthreads();
-        for (int ch = 0; ch < nchunks; ++ch) {
-            float* sc = st + static_cast<int64_t>(ch) * kD * kD;
+        for (int ch = c0; ch < c1; ++ch) {
+            float* sc = st + static_cast<int64_t>(ch - c0) * kD * kD;
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     sc[(16 * i + 4 * g + r) * kD + 16 * w + c] = Wt[i][r];
-            if (ch + 1 == nchunks)
+            if (ch + 1 == c1)
                 break;
             load_stage(nx, ch + 1, false, false);
-            const float* sl = lds + (ch & 1) * kSlotFloats;
+            const float* sl = lds + ((ch - c0) & 1) * kSlotFloats;
             f32x4 krow[4];
             const f32x4 E = residual(sl, Wt, krow);
             const f32x4 En = -et * E;
@@ -238,69 +256,91 @@ linear_backward_kernel(const In* __restrict__ Q, const In* __restrict__ K, const
                 for (int r = 0; r < 4; ++r)
                     Wt[i][r] = acc[r];
             }
-            store_stage(nx, (ch + 1) & 1, false, false);
+            store_stage(nx, (ch - c0 + 1) & 1, false, false);
             __syncthreads();
         }
+        // the states just stored are read back below by other threads
+        __threadfence();
+        __syncthreads();
     }
-    // the states just stored are read back below by other threads
-    __threadfence();
-    __syncthreads();
 
-    // ---------------- sweep 2: reverse over the chunks ----------------
+    // ---------------- sweep 2: reverse over the chunks of the segment ----------------
     float Gt[4][4];
+    if (kGMap) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            Gt[i][r] = dW_out[u * kD * kD + (16 * i + 4 * g + r) * kD + 16 * w + c];
+            for (int r = 0; r < 4; ++r)
+                Gt[i][r] = half == 0 && 16 * i + 4 * g + r == 16 * w + c ? 1.f : 0.f;
+    } else {
+        const float* g1 = nseg > 1 ? gend + (u * nseg + (nseg - 1 - s)) * kD * kD
+                                   : dW_out + u * kD * kD;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                Gt[i][r] = g1[(16 * i + 4 * g + r) * kD + 16 * w + c];
+    }
     float deta_acc = 0.f;
     float* Es = lds + kOffE;
     float* Ps = lds + kOffP;
     float* Gs = lds + kOffG;
     float* dAs = lds + kOffDA + w * kB * kDAP;
 
-    Stage<In> nx;
-    load_stage(nx, nchunks - 1, true, true);
-    store_stage(nx, 0, true, true);
-    __syncthreads();
-    for (int ch = nchunks - 1; ch >= 0; --ch) {
-        const int slot = (nchunks - 1 - ch) & 1;
+    if (c1 > c0) {
+        Stage<In> nx;
+        load_stage(nx, c1 - 1, use_dy, !kGMap);
+        store_stage(nx, 0, use_dy, !kGMap);
+        __syncthreads();
+    }
+    for (int ch = c1 - 1; ch >= c0; --ch) {
+        const int slot = (c1 - 1 - ch) & 1;
         const float* sl = lds + slot * kSlotFloats;
-        if (ch > 0)
-            load_stage(nx, ch - 1, true, true);
+        Stage<In> nx;
+        if (ch > c0)
+            load_stage(nx, ch - 1, use_dy, !kGMap);
 
         // ---- phase A: columns J = w ----
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                Wt[i][r] = sl[kSlotW + (16 * i + 4 * g + r) * kP + 16 * w + c];
         f32x4 krow[4];
-        const f32x4 E = residual(sl, Wt, krow);
-        // S = Q K^T: lane holds S[t = 4g + r][s = c]; A = tril(S) keeps s <= t
-        f32x4 qrow[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            qrow[i] = lds4(sl + kSlotQ + c * kP + 16 * i + 4 * g);
-        f32x4 sacc[4] = {};
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
+        f32x4 E = {0.f, 0.f, 0.f, 0.f};
+        if (!kGMap) {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                sacc[i] = mfma(qrow[i][r], krow[i][r], sacc[i]);
-        f32x4 S = (sacc[0] + sacc[1]) + (sacc[2] + sacc[3]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            S[r] = c <= 4 * g + r ? S[r] : 0.f;
-        // P = A^T dY_J + K G'_J (S as an A operand is A^T)
-        float dyc[4];
+                for (int r = 0; r < 4; ++r)
+                    Wt[i][r] = sl[kSlotW + (16 * i + 4 * g + r) * kP + 16 * w + c];
+            E = residual(sl, Wt, krow);
+        } else {
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            dyc[r] = sl[kSlotDY + (4 * g + r) * kP + 16 * w + c];
+            for (int i = 0; i < 4; ++i)
+                krow[i] = lds4(sl + kSlotK + c * kP + 16 * i + 4 * g);
+        }
+        // P = A^T dY_J + K G'_J, A = tril(Q K^T) (S below holds S[t = 4g + r][s = c];
+        // as an A operand it is A^T)
         f32x4 pacc[4] = {};
+        float dyc[4] = {0.f, 0.f, 0.f, 0.f};
+        if (use_dy) {
+            f32x4 qrow[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            pacc[0] = mfma(S[r], dyc[r], pacc[0]);
+            for (int i = 0; i < 4; ++i)
+                qrow[i] = lds4(sl + kSlotQ + c * kP + 16 * i + 4 * g);
+            f32x4 sacc[4] = {};
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    sacc[i] = mfma(qrow[i][r], krow[i][r], sacc[i]);
+            f32x4 S = (sacc[0] + sacc[1]) + (sacc[2] + sacc[3]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                S[r] = c <= 4 * g + r ? S[r] : 0.f;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                dyc[r] = sl[kSlotDY + (4 * g + r) * kP + 16 * w + c];
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                pacc[0] = mfma(S[r], dyc[r], pacc[0]);
+        }
 #pragma unroll
         for (int r = 0; r < 4; ++r)
 #pragma unroll
@@ -308,22 +348,28 @@ linear_backward_kernel(const In* __restrict__ Q, const In* __restrict__ K, const
                 pacc[i] = mfma(krow[i][r], Gt[i][r], pacc[i]);
         const f32x4 P = (pacc[0] + pacc[1]) + (pacc[2] + pacc[3]);
         const f32x4 dE = -et * P;
+        if (!kGMap) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            deta_acc -= P[r] * E[r];
-            Es[(4 * g + r) * kP + 16 * w + c] = E[r];
-            Ps[(4 * g + r) * kP + 16 * w + c] = P[r];
+            for (int r = 0; r < 4; ++r) {
+                deta_acc -= P[r] * E[r];
+                Es[(4 * g + r) * kP + 16 * w + c] = E[r];
+                Ps[(4 * g + r) * kP + 16 * w + c] = P[r];
+            }
         }
         // G' to LDS for phase B, then G = G' + Q^T dY + K^T dE (over tokens)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             f32x4 acc = {Gt[i][0], Gt[i][1], Gt[i][2], Gt[i][3]};
+            if (!kGMap) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                Gs[(16 * i + 4 * g + r) * kP + 16 * w + c] = Gt[i][r];
+                for (int r = 0; r < 4; ++r)
+                    Gs[(16 * i + 4 * g + r) * kP + 16 * w + c] = Gt[i][r];
+            }
+            if (use_dy) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                acc = mfma(sl[kSlotQ + (4 * g + r) * kP + 16 * i + c], dyc[r], acc);
+                for (int r = 0; r < 4; ++r)
+                    acc = mfma(sl[kSlotQ + (4 * g + r) * kP + 16 * i + c], dyc[r], acc);
+            }
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 acc = mfma(sl[kSlotK + (4 * g + r) * kP + 16 * i + c], dE[r], acc);
@@ -331,89 +377,102 @@ linear_backward_kernel(const In* __restrict__ Q, const In* __restrict__ K, const
             for (int r = 0; r < 4; ++r)
                 Gt[i][r] = acc[r];
         }
-        __syncthreads();
 
-        // ---- phase B: input dims I = w ----
-        // dA = -eta tril(dY E^T): lane holds dA[t = 4g + r][s = c]
-        f32x4 dyrow[4], erow[4];
+        if (!kGMap) {
+            __syncthreads();
+            // ---- phase B: input dims I = w ----
+            // dA = -eta tril(dY E^T): lane holds dA[t = 4g + r][s = c]
+            f32x4 dyrow[4], erow[4];
 #pragma unroll
-        for (int jb = 0; jb < 4; ++jb) {
-            dyrow[jb] = lds4(sl + kSlotDY + c * kP + 16 * jb + 4 * g);
-            erow[jb] = lds4(Es + c * kP + 16 * jb + 4 * g);
-        }
-        f32x4 aacc[4] = {};
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-#pragma unroll
-            for (int jb = 0; jb < 4; ++jb)
-                aacc[jb] = mfma(dyrow[jb][r], erow[jb][r], aacc[jb]);
-        f32x4 dA = (aacc[0] + aacc[1]) + (aacc[2] + aacc[3]);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            dA[r] = c <= 4 * g + r ? -et * dA[r] : 0.f;
-            dAs[(4 * g + r) * kDAP + c] = dA[r];
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        // dQ_I = dY W[I, :]^T + dA K_I
-        f32x4 wrow[4];
-#pragma unroll
-        for (int jb = 0; jb < 4; ++jb)
-            wrow[jb] = lds4(sl + kSlotW + (16 * w + c) * kP + 16 * jb + 4 * g);
-        f32x4 qacc[4] = {};
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-#pragma unroll
-            for (int jb = 0; jb < 4; ++jb)
-                qacc[jb] = mfma(dyrow[jb][r], wrow[jb][r], qacc[jb]);
-        {
-            const f32x4 darow = lds4(dAs + c * kDAP + 4 * g);
+            for (int jb = 0; jb < 4; ++jb) {
+                dyrow[jb] = lds4(sl + kSlotDY + c * kP + 16 * jb + 4 * g);
+                erow[jb] = lds4(Es + c * kP + 16 * jb + 4 * g);
+            }
+            f32x4 aacc[4] = {};
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                qacc[0] = mfma(darow[r], sl[kSlotK + (4 * g + r) * kP + 16 * w + c], qacc[0]);
-        }
-        const f32x4 dq = (qacc[0] + qacc[1]) + (qacc[2] + qacc[3]);
-        // dK_I = -eta (P W[I, :]^T + E G'[I, :]^T) + dA^T Q_I
-        f32x4 kacc[4] = {};
 #pragma unroll
-        for (int jb = 0; jb < 4; ++jb) {
-            const f32x4 prow = lds4(Ps + c * kP + 16 * jb + 4 * g);
-            const f32x4 grow = lds4(Gs + (16 * w + c) * kP + 16 * jb + 4 * g);
+                for (int jb = 0; jb < 4; ++jb)
+                    aacc[jb] = mfma(dyrow[jb][r], erow[jb][r], aacc[jb]);
+            f32x4 dA = (aacc[0] + aacc[1]) + (aacc[2] + aacc[3]);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                kacc[jb] = mfma(prow[r], wrow[jb][r], kacc[jb]);
-                kacc[jb] = mfma(erow[jb][r], grow[r], kacc[jb]);
+                dA[r] = c <= 4 * g + r ? -et * dA[r] : 0.f;
+                dAs[(4 * g + r) * kDAP + c] = dA[r];
             }
-        }
-        f32x4 dk = -et * ((kacc[0] + kacc[1]) + (kacc[2] + kacc[3]));
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            // dQ_I = dY W[I, :]^T + dA K_I
+            f32x4 wrow[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            dk = mfma(dA[r], sl[kSlotQ + (4 * g + r) * kP + 16 * w + c], dk);
+            for (int jb = 0; jb < 4; ++jb)
+                wrow[jb] = lds4(sl + kSlotW + (16 * w + c) * kP + 16 * jb + 4 * g);
+            f32x4 qacc[4] = {};
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int jb = 0; jb < 4; ++jb)
+                    qacc[jb] = mfma(dyrow[jb][r], wrow[jb][r], qacc[jb]);
+            {
+                const f32x4 darow = lds4(dAs + c * kDAP + 4 * g);
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    qacc[0] = mfma(darow[r], sl[kSlotK + (4 * g + r) * kP + 16 * w + c], qacc[0]);
+            }
+            const f32x4 dq = (qacc[0] + qacc[1]) + (qacc[2] + qacc[3]);
+            // dK_I = -eta (P W[I, :]^T + E G'[I, :]^T) + dA^T Q_I
+            f32x4 kacc[4] = {};
+#pragma unroll
+            for (int jb = 0; jb < 4; ++jb) {
+                const f32x4 prow = lds4(Ps + c * kP + 16 * jb + 4 * g);
+                const f32x4 grow = lds4(Gs + (16 * w + c) * kP + 16 * jb + 4 * g);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    kacc[jb] = mfma(prow[r], wrow[jb][r], kacc[jb]);
+                    kacc[jb] = mfma(erow[jb][r], grow[r], kacc[jb]);
+                }
+            }
+            f32x4 dk = -et * ((kacc[0] + kacc[1]) + (kacc[2] + kacc[3]));
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                dk = mfma(dA[r], sl[kSlotQ + (4 * g + r) * kP + 16 * w + c], dk);
 
-        // stores: rows t = 16 ch + 4g + r, column 16 w + c (P of phase A is
-        // this wave's column block, so dV = eta P needs no exchange)
+            // stores: rows t = 16 ch + 4g + r, column 16 w + c (P of phase A is
+            // this wave's column block, so dV = eta P needs no exchange)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int t = ch * kB + 4 * g + r;
-            if (t < T) {
-                const int64_t e = off + static_cast<int64_t>(t) * kD + 16 * w + c;
-                store_elem(dQ, e, dq[r]);
-                store_elem(dK, e, dk[r]);
-                store_elem(dV, e, et * P[r]);
+            for (int r = 0; r < 4; ++r) {
+                const int t = ch * kB + 4 * g + r;
+                if (t < T) {
+                    const int64_t e = off + static_cast<int64_t>(t) * kD + 16 * w + c;
+                    store_elem(dQ, e, dq[r]);
+                    store_elem(dK, e, dk[r]);
+                    store_elem(dV, e, et * P[r]);
+                }
             }
         }
-        if (ch > 0)
-            store_stage(nx, slot ^ 1, true, true);
+        if (ch > c0)
+            store_stage(nx, slot ^ 1, use_dy, !kGMap);
         __syncthreads();
     }
 
-    // dW0 of this chain is the cotangent of the first chunk-start state
+    if (kGMap) {
+        float* out = gmaps + ((u * (nseg - 1) + (nseg - 1 - s)) * 2 + half) * kD * kD;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            dW0_chain[u * kD * kD + (16 * i + 4 * g + r) * kD + 16 * w + c] = Gt[i][r];
-    // deta: sum over the lanes, then over the waves
+            for (int r = 0; r < 4; ++r)
+                out[(16 * i + 4 * g + r) * kD + 16 * w + c] = Gt[i][r];
+        return;
+    }
+    // dW0 of the chain is the cotangent of the first chunk-start state
+    if (s == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                dW0_chain[u * kD * kD + (16 * i + 4 * g + r) * kD + 16 * w + c] = Gt[i][r];
+    }
+    // this segment's share of deta: sum over the lanes, then over the waves
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1)
         deta_acc += __shfl_xor(deta_acc, m);
@@ -421,30 +480,101 @@ linear_backward_kernel(const In* __restrict__ Q, const In* __restrict__ K, const
         lds[kOffRed + w] = deta_acc;
     __syncthreads();
     if (tid == 0)
-        deta_chain[u] = (lds[kOffRed] + lds[kOffRed + 1]) + (lds[kOffRed + 2] + lds[kOffRed + 3]);
+        deta_chain[u * nseg + s] = (lds[kOffRed] + lds[kOffRed + 1]) + (lds[kOffRed + 2] + lds[kOffRed + 3]);
 }
 
-// Sums over the batch, in batch order: dW0 (when W0 is shared by the batch)
-// and deta (always: eta is one value per head).
+// Sums in a fixed order: dW0 over the batch (when W0 is shared by the batch)
+// and deta over the batch and the segments (always: eta is one value per head).
 __global__ void __launch_bounds__(256)
 linear_backward_reduce_kernel(const float* __restrict__ dW0_chain, const float* __restrict__ deta_chain,
-                              int64_t B, int H, int reduce_w, float* __restrict__ dW0,
+                              int64_t B, int H, int nseg, int reduce_w, float* __restrict__ dW0,
                               float* __restrict__ deta)
 {
     const int64_t x = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
     const int64_t n = static_cast<int64_t>(H) * kD * kD;
     if (reduce_w && x < n) {
-        float s = 0.f;
+        float acc = 0.f;
         for (int64_t bb = 0; bb < B; ++bb)
-            s += dW0_chain[bb * n + x];
-        dW0[x] = s;
+            acc += dW0_chain[bb * n + x];
+        dW0[x] = acc;
     }
     if (x < H) {
-        float s = 0.f;
+        float acc = 0.f;
         for (int64_t bb = 0; bb < B; ++bb)
-            s += deta_chain[bb * H + x];
-        deta[x] = s;
+            for (int sg = 0; sg < nseg; ++sg)
+                acc += deta_chain[(bb * H + x) * nseg + sg];
+        deta[x] = acc;
     }
+}
+
+// workspace carve-up (floats): forward maps, start states, cotangent maps,
+// end cotangents (only with segments), chunk-start states, per-chain dW0
+// (shared W0 only), per-segment deta
+struct BwdWorkspace {
+    float *maps, *wstart, *gmaps, *gend, *states, *dw_chain, *deta_chain;
+    size_t bytes;
+};
+
+// One segment covers every chunk: seg_len = T rounded up to whole chunks.
+SegmentPlan normalized(const LinearBwdArgs& a, SegmentPlan p)
+{
+    if (p.nseg <= 1) {
+        p.nseg = 1;
+        p.seg_len = (a.T + kB - 1) / kB * kB;
+    }
+    return p;
+}
+
+BwdWorkspace carve(const LinearBwdArgs& a, const SegmentPlan& p, void* base)
+{
+    const size_t units = static_cast<size_t>(a.B * a.H);
+    const size_t st = kD * kD;
+    const size_t seg_chunks = static_cast<size_t>(p.seg_len / kB);
+    const size_t S = static_cast<size_t>(p.nseg);
+    size_t o = 0;
+    BwdWorkspace w{};
+    float* f = static_cast<float*>(base);
+    auto take = [&](size_t n) {
+        float* r = f ? f + o : nullptr;
+        o += (n + 63) / 64 * 64;       // 256-byte aligned pieces
+        return r;
+    };
+    if (S > 1) {
+        w.maps = take(units * (S - 1) * 2 * st);
+        w.wstart = take(units * S * st);
+        w.gmaps = take(units * (S - 1) * 2 * st);
+        w.gend = take(units * S * st);
+    }
+    w.states = take(units * S * seg_chunks * st);
+    w.dw_chain = a.w0_per_batch ? a.dW0 : take(units * st);
+    w.deta_chain = take(units * S);
+    w.bytes = o * sizeof(float);
+    return w;
+}
+
+template <typename In, bool kGMap>
+void launch_kernel(const LinearBwdArgs& a, const SegmentPlan& p, const BwdWorkspace& w, dim3 grid)
+{
+    hipLaunchKernelGGL((linear_backward_kernel<In, kGMap>), grid, dim3(kThreads), kLdsBytes, a.stream,
+                       static_cast<const In*>(a.Q), static_cast<const In*>(a.K),
+                       static_cast<const In*>(a.V), a.W0, a.w0_per_batch, a.eta,
+                       static_cast<int>(a.H), static_cast<int>(a.T), a.B * a.H,
+                       static_cast<int>(p.seg_len), p.nseg, w.wstart, w.gend,
+                       static_cast<const In*>(a.dY), a.dW_out, static_cast<In*>(a.dQ),
+                       static_cast<In*>(a.dK), static_cast<In*>(a.dV), w.dw_chain, w.deta_chain,
+                       w.states, w.gmaps);
+}
+
+template <typename In>
+hipError_t set_lds()
+{
+    for (const void* f : {reinterpret_cast<const void*>(linear_backward_kernel<In, false>),
+                          reinterpret_cast<const void*>(linear_backward_kernel<In, true>)}) {
+        const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+        if (e != hipSuccess)
+            return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace
@@ -454,65 +584,64 @@ bool linear_backward_supports(const LinearBwdArgs& a)
     return a.d == kD && a.b == kB;
 }
 
-size_t linear_backward_workspace_bytes(const LinearBwdArgs& a)
+size_t linear_backward_workspace_bytes(const LinearBwdArgs& a, const SegmentPlan& p)
 {
-    const int64_t units = a.B * a.H;
-    const int64_t nchunks = (a.T + kB - 1) / kB;
-    const size_t states = static_cast<size_t>(units) * nchunks * kD * kD * 4;
-    const size_t dw = a.w0_per_batch ? 0 : static_cast<size_t>(units) * kD * kD * 4;
-    return states + dw + static_cast<size_t>(units) * 4 + 256;
+    return carve(a, normalized(a, p), nullptr).bytes;
 }
 
-hipError_t launch_linear_backward(const LinearBwdArgs& a, void* workspace)
+hipError_t launch_linear_backward(const LinearBwdArgs& a, const SegmentPlan& plan, void* workspace)
 {
     const int64_t units = a.B * a.H;
-    const int64_t nchunks = (a.T + kB - 1) / kB;
-    char* ws = static_cast<char*>(workspace);
-    float* states = reinterpret_cast<float*>(ws);
-    ws += static_cast<size_t>(units) * nchunks * kD * kD * 4;
-    float* dw_chain = a.w0_per_batch ? a.dW0 : reinterpret_cast<float*>(ws);
-    if (!a.w0_per_batch)
-        ws += static_cast<size_t>(units) * kD * kD * 4;
-    float* deta_chain = reinterpret_cast<float*>(ws);
-
-    const dim3 grid(static_cast<unsigned>(units)), block(kThreads);
-    hipError_t e = hipSuccess;
-    if (units == 0) {
-        // nothing to differentiate: the batch sums below are zero
-    } else if (a.dtype == 0) {
-        e = hipFuncSetAttribute(reinterpret_cast<const void*>(linear_backward_kernel<float>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+    const SegmentPlan p = normalized(a, plan);
+    const BwdWorkspace w = carve(a, p, workspace);
+    const bool bf16 = a.dtype != 0;
+    hipError_t e = bf16 ? set_lds<uint16_t>() : set_lds<float>();
+    if (e != hipSuccess)
+        return e;
+    if (units > 0 && p.nseg > 1) {
+        // start state of every segment: the forward's maps and composition
+        const LinearArgs fa{a.Q, a.K, a.V, a.dtype, a.W0, a.w0_per_batch, a.eta, a.B, a.H, a.T,
+                            a.d, a.b, nullptr, nullptr, a.stream};
+        SegmentPlan fp = p;
+        fp.maps = w.maps;
+        fp.wstart = w.wstart;
+        fp.starts_only = true;
+        e = bf16 ? launch_linear_mfma(fa, fp) : launch_linear_mfma_f32(fa, fp);
         if (e != hipSuccess)
             return e;
-        hipLaunchKernelGGL(linear_backward_kernel<float>, grid, block, kLdsBytes, a.stream,
-                           static_cast<const float*>(a.Q), static_cast<const float*>(a.K),
-                           static_cast<const float*>(a.V), a.W0, a.w0_per_batch, a.eta,
-                           static_cast<int>(a.H), static_cast<int>(a.T),
-                           static_cast<const float*>(a.dY), a.dW_out, static_cast<float*>(a.dQ),
-                           static_cast<float*>(a.dK), static_cast<float*>(a.dV), dw_chain,
-                           deta_chain, states);
-    } else {
-        e = hipFuncSetAttribute(reinterpret_cast<const void*>(linear_backward_kernel<uint16_t>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+        // end cotangent of every segment: cotangent maps, then the same
+        // composition run from dW_out through the segments in reverse
+        const dim3 mgrid(static_cast<unsigned>(placed_grid(units, 2 * (p.nseg - 1))));
+        if (bf16)
+            launch_kernel<uint16_t, true>(a, p, w, mgrid);
+        else
+            launch_kernel<float, true>(a, p, w, mgrid);
+        e = hipGetLastError();
         if (e != hipSuccess)
             return e;
-        hipLaunchKernelGGL(linear_backward_kernel<uint16_t>, grid, block, kLdsBytes, a.stream,
-                           static_cast<const uint16_t*>(a.Q), static_cast<const uint16_t*>(a.K),
-                           static_cast<const uint16_t*>(a.V), a.W0, a.w0_per_batch, a.eta,
-                           static_cast<int>(a.H), static_cast<int>(a.T),
-                           static_cast<const uint16_t*>(a.dY), a.dW_out,
-                           static_cast<uint16_t*>(a.dQ), static_cast<uint16_t*>(a.dK),
-                           static_cast<uint16_t*>(a.dV), dw_chain, deta_chain, states);
+        const LinearArgs ga{a.Q, a.K, a.V, a.dtype, a.dW_out, 1, a.eta, a.B, a.H, a.T,
+                            a.d, a.b, nullptr, nullptr, a.stream};
+        SegmentPlan gp = p;
+        gp.maps = w.gmaps;
+        gp.wstart = w.gend;
+        e = launch_linear_combine(ga, gp);
+        if (e != hipSuccess)
+            return e;
     }
     if (units > 0) {
+        const dim3 grid(static_cast<unsigned>(p.nseg > 1 ? placed_grid(units, p.nseg) : units));
+        if (bf16)
+            launch_kernel<uint16_t, false>(a, p, w, grid);
+        else
+            launch_kernel<float, false>(a, p, w, grid);
         e = hipGetLastError();
         if (e != hipSuccess)
             return e;
     }
     const int64_t n = a.w0_per_batch ? a.H : a.H * kD * kD;
     hipLaunchKernelGGL(linear_backward_reduce_kernel, dim3(static_cast<unsigned>((n + 255) / 256)),
-                       dim3(256), 0, a.stream, dw_chain, deta_chain, a.B, static_cast<int>(a.H),
-                       a.w0_per_batch ? 0 : 1, a.dW0, a.deta);
+                       dim3(256), 0, a.stream, w.dw_chain, w.deta_chain, a.B, static_cast<int>(a.H),
+                       p.nseg, a.w0_per_batch ? 0 : 1, a.dW0, a.deta);
     return hipGetLastError();
 }
 

@@ -163,26 +163,6 @@ struct StageRegs {
     u32x4 k, q, v;
 };
 
-// Block id -> (chain u, block s of the chain) for nb blocks per chain.  With
-// at least 8 chains every block of chain u gets id = u (mod 8): workgroups
-// are dispatched to the 8 XCDs round robin, so they all share XCD u % 8 and
-// its L2 (grid 8 nb ceil(units / 8); ids with u >= units do nothing).  With
-// fewer chains that would leave XCDs idle, so blocks are numbered plainly.
-__device__ __forceinline__ void xcd_block(int id, int nb, int64_t units, int64_t& u, int& s)
-{
-    if (units < 8) {
-        u = id / nb;
-        s = id % nb;
-        return;
-    }
-    const int t = id >> 3;
-    u = 8 * static_cast<int64_t>(t / nb) + (id & 7);
-    s = t % nb;
-}
-__host__ __device__ inline int64_t placed_grid(int64_t units, int nb)
-{
-    return units < 8 ? units * nb : 8 * nb * ((units + 7) / 8);
-}
 
 // kMaps = false: the scan of segment s of a chain (Y rows of the segment; the
 //   last segment also writes W_out), started from W0 (one segment) or from
@@ -448,7 +428,7 @@ hipError_t launch_linear_mfma(const LinearArgs& a, const SegmentPlan& p)
         hipError_t e = hipGetLastError();
         if (e == hipSuccess)
             e = launch_linear_combine(a, p);
-        if (e != hipSuccess)
+        if (e != hipSuccess || p.starts_only)
             return e;
     }
     const dim3 grid(static_cast<unsigned>(p.nseg > 1 ? placed_grid(units, p.nseg) : units));

@@ -27,6 +27,8 @@ KERNEL_FILES = {
     "linear_mfma_f32_kernel[scan]": "ttt_linear_mfma_f32.hip",
     "linear_mfma_f32_kernel[maps]": "ttt_linear_mfma_f32.hip",
     "linear_combine_kernel": "ttt_linear_combine.hip",
+    "linear_backward_kernel": "ttt_linear_backward.hip",
+    "linear_backward_reduce_kernel": "ttt_linear_backward.hip",
     "linear_generic_kernel": "ttt_generic.hip",
     "mlp_generic_kernel": "ttt_generic.hip",
     "mlp_mfma_kernel": "ttt_mlp_mfma.hip",

@@ -22,11 +22,14 @@ def main():
     ap.add_argument("--reps", type=int, default=5)
     ap.add_argument("--copy-mib", type=int, default=256)
     ap.add_argument("--decode", action="store_true", help="also run the workload's decode steps")
+    ap.add_argument("--backward", action="store_true",
+                    help="run ttt_linear_backward (seeded cotangents) instead of the forward")
     args = ap.parse_args()
 
     import torch
     import test_sequence_layers_linear_amd as ttt
-    from test_sequence_layers_linear_amd.inputs import CONFIGS, default_seed, make_inputs
+    from test_sequence_layers_linear_amd.inputs import (CONFIGS, default_seed, make_cotangents,
+                                                        make_inputs)
 
     w = CONFIGS[args.config]
     g = {k: v.cuda() for k, v in make_inputs(w, default_seed(args.config)).items()}
@@ -36,9 +39,14 @@ def main():
     else:
         W1 = torch.empty((w.B, w.H, w.d, w.m), device="cuda")
         W2 = torch.empty((w.B, w.H, w.m, w.d), device="cuda")
+    if args.backward:
+        cot = {k: v.cuda() for k, v in make_cotangents(w, 7).items()}
     torch.cuda.synchronize()
     for _ in range(args.reps):
-        if w.kind == "linear":
+        if args.backward:
+            ttt.ttt_linear_backward(g["Q"], g["K"], g["V"], g["W0"], g["eta"], w.b, cot["dY"],
+                                    cot["dW_out"])
+        elif w.kind == "linear":
             ttt.ttt_linear_forward(g["Q"], g["K"], g["V"], g["W0"], g["eta"], w.b, Y=Y, W_out=W)
             if args.decode:
                 y = torch.empty_like(g["dq"][0])

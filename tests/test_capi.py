@@ -161,3 +161,19 @@ def test_segment_query_validation_and_override(lib, monkeypatch):
     assert lib.ttt_linear_segments(1, 4, 30 * 16, 64, 16, 0) == 30
     monkeypatch.setenv("TTT_LINEAR_SEGMENTS", "3")
     assert lib.ttt_linear_segments(1, 4, 2048, 32, 16, 0) == 1     # generic kernel: no split
+
+
+def test_backward_segment_query_validation_and_override(lib, monkeypatch):
+    """Same contract for the backward's segment count (TTT_LINEAR_BWD_SEGMENTS)."""
+    assert lib.ttt_linear_backward_segments(-1, 3, 64, 64, 16, 1) == INVALID
+    assert lib.ttt_linear_backward_segments(1, 3, 64, 64, 0, 1) == INVALID
+    assert lib.ttt_linear_backward_segments(1, 3, 64, 32, 16, 1) == UNSUPPORTED
+    assert lib.ttt_linear_backward_segments(1, 3, 64, 64, 8, 1) == UNSUPPORTED
+    assert lib.ttt_linear_backward_segments(1, 3, 64, 64, 16, 4) == UNSUPPORTED
+    assert lib.ttt_linear_backward_segments(0, 3, 64, 64, 16, 1) == 1
+    assert lib.ttt_linear_backward_segments(2, 3, 0, 64, 16, 1) == 1
+    monkeypatch.setenv("TTT_LINEAR_BWD_SEGMENTS", "7")
+    assert lib.ttt_linear_backward_segments(1, 4, 1000, 64, 16, 0) == 7   # 63 chunks, 9 each
+    assert lib.ttt_linear_backward_segments(1, 4, 40, 64, 16, 1) == 3
+    monkeypatch.setenv("TTT_LINEAR_BWD_SEGMENTS", "99")
+    assert lib.ttt_linear_backward_segments(1, 4, 2048, 64, 16, 1) == 26

@@ -62,6 +62,43 @@ def test_backward_small(dtype, B, H, T, per_batch, zero_state):
     _compare(_gpu(inp, cot, 16), _oracle(inp, cot, 16), TOL[dtype])
 
 
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("B,H,T,S,per_batch", [
+    (1, 2, 100, 2, False),        # 7 chunks: segments of 4 and 3, ragged last chunk
+    (2, 3, 333, 3, True),
+    (1, 4, 1000, 7, False),
+    (2, 1, 480, 30, False),       # 30 one-chunk segments
+    (2, 2, 48, 3, True),          # 3 chunks, one per segment
+])
+def test_backward_segmented(dtype, B, H, T, S, per_batch, monkeypatch):
+    monkeypatch.setenv("TTT_LINEAR_BWD_SEGMENTS", str(S))
+    got_s = ttt.ttt_linear_backward_segments(B, H, T, 64, 16,
+                                             torch.float32 if dtype == "fp32" else torch.bfloat16)
+    assert got_s == S
+    w = CONFIGS[3].with_(B=B, H=H, T=T, dtype=dtype, eta=("uniform", 0.1, 0.6))
+    seed = 7300 + B * 100 + H * 10 + S
+    announce("backward segmented", dtype, B, H, T, "segments", S, seed)
+    inp = make_inputs(w, seed, w0_per_batch=per_batch)
+    cot = make_cotangents(w, seed + 1)
+    _compare(_gpu(inp, cot, 16), _oracle(inp, cot, 16), TOL[dtype])
+
+
+def test_backward_segmented_close_to_single_segment(monkeypatch):
+    """fp32: a segmented backward is the same arithmetic in another rounding
+    order of the state and the cotangent."""
+    w = CONFIGS[2]
+    announce("backward segments vs one segment", w.name)
+    inp = make_inputs(w, default_seed(2))
+    cot = make_cotangents(w, default_seed(2) + 500)
+    seg = _gpu(inp, cot, w.b)
+    monkeypatch.setenv("TTT_LINEAR_BWD_SEGMENTS", "1")
+    one = _gpu(inp, cot, w.b)
+    for n, x, y in zip(NAMES, seg, one):
+        e = rel_l2(x, y.detach().to("cpu", torch.float64).numpy())
+        print(f"  {n} rel-L2 {e:.2e}", flush=True)
+        assert e <= 2e-6, n
+
+
 def test_backward_empty_sequence():
     w = CONFIGS[3].with_(B=2, H=3, T=0)
     announce("backward T=0")
@@ -90,7 +127,8 @@ def test_backward_deterministic():
 @pytest.mark.parametrize("cfg", [2, 3])
 def test_backward_config_full(cfg):
     w = CONFIGS[cfg]
-    announce("backward config", cfg, w.name)
+    announce("backward config", cfg, w.name, "segments",
+             ttt.ttt_linear_backward_segments(w.B, w.H, w.T, w.d, w.b, w.torch_dtype))
     inp = make_inputs(w, default_seed(cfg))
     cot = make_cotangents(w, default_seed(cfg) + 500)
     _compare(_gpu(inp, cot, w.b), _oracle(inp, cot, w.b), TOL[w.dtype])
