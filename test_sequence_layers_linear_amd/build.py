@@ -26,7 +26,7 @@ FLAGS = [
     f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}",
 ]
 
-# Per-file flags.  The TTT-Linear MFMA kernels keep every MFMA accumulator in
+# Per-file flags.  The TTT-Linear MFMA kernels (forward and backward) keep every MFMA accumulator in
 # ordinary VGPRs (they fit): otherwise the compiler places the results in
 # AGPRs and copies each one back to a VGPR before its VALU use, about a
 # quarter of the instructions of a chunk.  The TTT-MLP kernel needs the AGPRs
@@ -34,6 +34,7 @@ FLAGS = [
 EXTRA = {
     "ttt_linear_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "ttt_linear_mfma_f32.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "ttt_linear_backward.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 
