@@ -51,7 +51,9 @@ KERNEL_SOURCES = {
     "linear_mfma_f32_kernel[scan]": "ttt_linear_mfma_f32.hip",
     "linear_mfma_f32_kernel[maps]": "ttt_linear_mfma_f32.hip",
     "linear_combine_kernel": "ttt_linear_combine.hip",
-    "linear_backward_kernel": "ttt_linear_backward.hip",
+    "linear_backward_reduce_kernel": "ttt_linear_backward.hip",
+    "linear_backward_kernel[gmaps]": "ttt_linear_backward.hip",
+    "linear_backward_kernel[segments]": "ttt_linear_backward.hip",
     "linear_generic_kernel": "ttt_generic.hip",
     "mlp_generic_kernel": "ttt_generic.hip",
     "mlp_mfma_kernel": "ttt_mlp_mfma.hip",
@@ -114,6 +116,19 @@ def kernel_names(w, nseg):
         k = "linear_mfma_kernel" if w.dtype == "bf16" else "linear_mfma_f32_kernel"
         return [k + "[maps]", "linear_combine_kernel", k + "[scan]"] if nseg > 1 else [k + "[scan]"]
     return ["linear_generic_kernel"]
+
+
+def backward_kernel_names(w):
+    """Kernels one ttt_linear_backward call dispatches."""
+    import torch
+    import test_sequence_layers_linear_amd as ttt
+    n = ttt.ttt_linear_backward_segments(w.B, w.H, w.T, w.d, w.b,
+                                         torch.float32 if w.dtype == "fp32" else torch.bfloat16)
+    k = ["linear_backward_kernel[segments]", "linear_backward_reduce_kernel"]
+    if n > 1:
+        f = "linear_mfma_kernel[maps]" if w.dtype == "bf16" else "linear_mfma_f32_kernel[maps]"
+        k = [f, "linear_combine_kernel", "linear_backward_kernel[gmaps]", "linear_combine_kernel"] + k
+    return k
 
 
 def segments(w):
@@ -369,8 +384,9 @@ def measure_workload(cfg, steps, warmup, cold_reps):
         bt = r.measure_backward(max(3, steps // 2), 2)
         bf, bb = linear_backward_work(w)
         wf = w.with_(dtype="fp32")       # the kernel's arithmetic: fp32 MFMA
-        rf = roofline(wf, bf, bb, bt, ["linear_backward_kernel"])
-        rf["traffic"] = stored_traffic(["linear_backward_kernel"], w.name)
+        kern = backward_kernel_names(w)
+        rf = roofline(wf, bf, bb, bt, kern)
+        rf["traffic"] = stored_traffic(kern, w.name)
         out["backward"] = {"us": bt * 1e6, "tokens_per_s": w.B * w.T / bt, "roofline": rf}
     if w.decode_steps:
         df, db = decode_work(w)

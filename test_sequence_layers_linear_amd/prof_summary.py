@@ -27,7 +27,8 @@ KERNEL_FILES = {
     "linear_mfma_f32_kernel[scan]": "ttt_linear_mfma_f32.hip",
     "linear_mfma_f32_kernel[maps]": "ttt_linear_mfma_f32.hip",
     "linear_combine_kernel": "ttt_linear_combine.hip",
-    "linear_backward_kernel": "ttt_linear_backward.hip",
+    "linear_backward_kernel[gmaps]": "ttt_linear_backward.hip",
+    "linear_backward_kernel[segments]": "ttt_linear_backward.hip",
     "linear_backward_reduce_kernel": "ttt_linear_backward.hip",
     "linear_generic_kernel": "ttt_generic.hip",
     "mlp_generic_kernel": "ttt_generic.hip",
@@ -39,7 +40,10 @@ COPY_NAME = "__amd_rocclr_copyBuffer"
 
 def short_name(full: str) -> str:
     """Kernel key: the function name, with [maps] / [scan] for the two
-    instantiations of the TTT-Linear MFMA kernels."""
+    instantiations of the TTT-Linear MFMA kernels and [gmaps] / [segments]
+    for the backward's cotangent maps and segment backward."""
+    if "linear_backward_kernel<" in full:
+        return "linear_backward_kernel[gmaps]" if ", true>" in full else "linear_backward_kernel[segments]"
     for k in KERNEL_FILES:
         base = k.split("[")[0]
         if base + "<true>" in full:
