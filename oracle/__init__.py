@@ -17,6 +17,10 @@ Parity status of each function (how it is pinned, see tests/test_oracle.py):
                      autograd mini-batch GD, finite differences, dual form.
                      No exact worked example exists (SiLU is transcendental).
   linear_decode   -- pinned: n steps equal linear_forward with b=1.
+  linear_forward_ex -- pinned: per-token eta equal to the head's eta gives
+                     linear_forward; autograd mini-batch GD with per-token
+                     step sizes; a zero step size drops a token from the
+                     update; LayerNorm equals torch's layer_norm.
   linear_backward -- pinned: central finite differences of linear_forward in
                      every coordinate (tiny sizes), the closed form of every
                      gradient at eta=0 (independent of b), the gradients of
@@ -69,6 +73,10 @@ def _load():
     lib.ttt_oracle_linear_backward.argtypes = [P, P, P, P, I, P, L, L, L, L, L, P, P,
                                                P, P, P, P, P, I]
     lib.ttt_oracle_linear_backward.restype = I
+    lib.ttt_oracle_linear_forward_tok.argtypes = [P, P, P, P, I, P, L, L, L, L, L, P, P, I]
+    lib.ttt_oracle_linear_forward_tok.restype = I
+    lib.ttt_oracle_layernorm_rows.argtypes = [P, L, L, L, L, P, P, ctypes.c_double]
+    lib.ttt_oracle_layernorm_rows.restype = I
     lib.ttt_oracle_max_threads.argtypes = []
     lib.ttt_oracle_max_threads.restype = I
     _lib = lib
@@ -110,6 +118,51 @@ def linear_forward(Q, K, V, W0, eta, b: int, nthreads: int = 0):
                                            _ptr(W_out), int(nthreads))
     if rc != 0:
         raise RuntimeError(f"oracle linear_forward failed ({rc})")
+    return Y, W_out
+
+
+def layernorm(X, ln, eps: float):
+    """LayerNorm of every d-vector of X [B,H,T,d] with the head's gamma, beta
+    (ln [H,2,d]: gamma then beta), biased variance; fp64."""
+    X = _f64(X).copy()
+    ln = _f64(ln)
+    B, H, T, d = X.shape
+    assert ln.shape == (H, 2, d)
+    gamma = np.ascontiguousarray(ln[:, 0])
+    beta = np.ascontiguousarray(ln[:, 1])
+    if X.size:
+        rc = _load().ttt_oracle_layernorm_rows(_ptr(X), B * H * T, T, H, d, _ptr(gamma),
+                                               _ptr(beta), float(eps))
+        if rc != 0:
+            raise RuntimeError(f"oracle layernorm failed ({rc})")
+    return X
+
+
+def linear_forward_ex(Q, K, V, W0, eta, b: int, eta_tok=None, ln_q=None, ln_k=None,
+                      ln_eps: float = 1e-5, nthreads: int = 0):
+    """TTT-Linear with the input prologue: Q and K each LayerNorm'd over the
+    head dim when ln_q / ln_k ([H,2,d], gamma then beta) are given, and a step
+    size per token eta_tok [B,H,T] (else the head's eta).  Returns (Y, W_out)
+    in fp64."""
+    Q, K, V, W0, eta = map(_f64, (Q, K, V, W0, eta))
+    B, H, T, d = Q.shape
+    if ln_q is not None:
+        Q = layernorm(Q, ln_q, ln_eps)
+    if ln_k is not None:
+        K = layernorm(K, ln_k, ln_eps)
+    if eta_tok is None:
+        return linear_forward(Q, K, V, W0, eta, b, nthreads)
+    et = _f64(eta_tok)
+    assert et.shape == (B, H, T)
+    per_batch = 1 if W0.ndim == 4 else 0
+    assert W0.shape == ((B, H, d, d) if per_batch else (H, d, d))
+    Y = np.zeros((B, H, T, d))
+    W_out = np.zeros((B, H, d, d))
+    rc = _load().ttt_oracle_linear_forward_tok(_ptr(Q), _ptr(K), _ptr(V), _ptr(W0), per_batch,
+                                               _ptr(et), B, H, T, d, int(b), _ptr(Y),
+                                               _ptr(W_out), int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"oracle linear_forward_tok failed ({rc})")
     return Y, W_out
 
 

@@ -172,6 +172,116 @@ int ttt_oracle_linear_forward(const double* Q, const double* K, const double* V,
 }
 
 /* ------------------------------------------------------------------------ */
+/* TTT-Linear with a step size per token: token t's gradient term is scaled   */
+/* by eta_t instead of the head's eta (the uTTT write-up on thelatestinai.com, */
+/* Table D3: learning rates per token, head and matrix).  Same primal loops:  */
+/*   r_t = k_t Wc - v_t,  G_t = G_{t-1} + eta_t k_t^T r_t,  W_t = Wc - G_t,   */
+/*   y_t = q_t W_t.                                                           */
+/* eta_tok: [B][H][T].                                                        */
+/* ------------------------------------------------------------------------ */
+static void linear_chain_tok(const double* q, const double* k, const double* v,
+                             const double* w_init, const double* eta_t, long T, long d, long b,
+                             double* y, double* w_final,
+                             double* W, double* Wc, double* G, double* Wt, double* r)
+{
+    const long dd = d * d;
+    memcpy(W, w_init, (size_t)dd * sizeof(double));
+    for (long s = 0; s < T; s += b) {
+        long e = s + b < T ? s + b : T;
+        memcpy(Wc, W, (size_t)dd * sizeof(double));
+        memset(G, 0, (size_t)dd * sizeof(double));
+        for (long t = s; t < e; ++t) {
+            const double* kt = k + t * d;
+            const double* vt = v + t * d;
+            const double* qt = q + t * d;
+            for (long j = 0; j < d; ++j) {
+                double acc = 0.0;
+                for (long i = 0; i < d; ++i)
+                    acc += kt[i] * Wc[i * d + j];
+                r[j] = acc - vt[j];
+            }
+            /* G += eta_t k^T r: this token's step, at the chunk-start weights */
+            for (long i = 0; i < d; ++i)
+                for (long j = 0; j < d; ++j)
+                    G[i * d + j] += eta_t[t] * kt[i] * r[j];
+            for (long x = 0; x < dd; ++x)
+                Wt[x] = Wc[x] - G[x];
+            for (long j = 0; j < d; ++j) {
+                double acc = 0.0;
+                for (long i = 0; i < d; ++i)
+                    acc += qt[i] * Wt[i * d + j];
+                y[t * d + j] = acc;
+            }
+        }
+        memcpy(W, Wt, (size_t)dd * sizeof(double));
+    }
+    memcpy(w_final, W, (size_t)dd * sizeof(double));
+}
+
+int ttt_oracle_linear_forward_tok(const double* Q, const double* K, const double* V,
+                                  const double* W0, int w0_per_batch, const double* eta_tok,
+                                  long B, long H, long T, long d, long b,
+                                  double* Y, double* W_out, int nthreads)
+{
+    if (B < 0 || H < 0 || T < 0 || d < 1 || b < 1)
+        return ORACLE_EINVAL;
+    if (!W0 || !W_out || (T > 0 && (!Q || !K || !V || !Y || !eta_tok)))
+        return ORACLE_EINVAL;
+    const long dd = d * d;
+    const long units = B * H;
+    int status = ORACLE_OK;
+    set_threads(nthreads);
+#pragma omp parallel
+    {
+        double* ws = (double*)malloc((size_t)(4 * dd + d) * sizeof(double));
+        if (!ws) {
+#pragma omp atomic write
+            status = ORACLE_ENOMEM;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (long u = 0; u < units; ++u) {
+            if (!ws)
+                continue;
+            long h = u % H;
+            const double* w_init = W0 + (w0_per_batch ? u : h) * dd;
+            const long off = u * T * d;
+            linear_chain_tok(Q + off, K + off, V + off, w_init, eta_tok + u * T, T, d, b,
+                             Y + off, W_out + u * dd,
+                             ws, ws + dd, ws + 2 * dd, ws + 3 * dd, ws + 4 * dd);
+        }
+        free(ws);
+    }
+    return status;
+}
+
+/* LayerNorm over the last dimension of n rows of length d, in place:
+ * x <- (x - mean) / sqrt(var + eps) * gamma + beta, with the biased variance
+ * ([KV] listing: LayerNorm of the projected keys and queries).  gamma, beta
+ * point at [H][d] each; row i belongs to head (i / T) % H. */
+int ttt_oracle_layernorm_rows(double* X, long n, long T, long H, long d, const double* gamma,
+                              const double* beta, double eps)
+{
+    if (n < 0 || T < 1 || H < 1 || d < 1 || !gamma || !beta || eps < 0.0 || (n > 0 && !X))
+        return ORACLE_EINVAL;
+    for (long i = 0; i < n; ++i) {
+        double* x = X + i * d;
+        const long h = (i / T) % H;
+        double mean = 0.0;
+        for (long j = 0; j < d; ++j)
+            mean += x[j];
+        mean /= (double)d;
+        double var = 0.0;
+        for (long j = 0; j < d; ++j)
+            var += (x[j] - mean) * (x[j] - mean);
+        var /= (double)d;
+        const double inv = 1.0 / sqrt(var + eps);
+        for (long j = 0; j < d; ++j)
+            x[j] = (x[j] - mean) * inv * gamma[h * d + j] + beta[h * d + j];
+    }
+    return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Backward of the TTT-Linear scan: the vector-Jacobian product of the map    */
 /* (Q, K, V, W0, eta) -> (Y, W_out) computed above, for cotangents dY and     */
 /* dW_out.  Outer-loop training differentiates the layer output through the   */

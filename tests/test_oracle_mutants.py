@@ -17,15 +17,18 @@ import pytest
 import oracle
 import test_oracle as pins
 import test_oracle_backward as bpins
+import test_oracle_prologue as ppins
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "ttt_oracle.c")
 
 MUTANTS = {
-    "residual_sign": ("r[j] = acc - vt[j];\n            }\n            /* G +=",
-                      "r[j] = vt[j] - acc;\n            }\n            /* G +="),
+    "residual_sign": ("r[j] = acc - vt[j];\n            }\n            /* G += k^T r",
+                      "r[j] = vt[j] - acc;\n            }\n            /* G += k^T r"),
     "gradient_transposed": ("G[i * d + j] += kt[i] * r[j];", "G[i * d + j] += kt[j] * r[i];"),
-    "prediction_transposed": ("acc += kt[i] * Wc[i * d + j];", "acc += kt[i] * Wc[j * d + i];"),
-    "readout_before_update": ("acc += qt[i] * Wt[i * d + j];", "acc += qt[i] * Wc[i * d + j];"),
+    "prediction_transposed": ("acc += kt[i] * Wc[i * d + j];\n                r[j] = acc - vt[j];\n            }\n            /* G += k^T r",
+                              "acc += kt[i] * Wc[j * d + i];\n                r[j] = acc - vt[j];\n            }\n            /* G += k^T r"),
+    "readout_before_update": ("readout after the update) */\n            for (long j = 0; j < d; ++j) {\n                double acc = 0.0;\n                for (long i = 0; i < d; ++i)\n                    acc += qt[i] * Wt[i * d + j];",
+                              "readout after the update) */\n            for (long j = 0; j < d; ++j) {\n                double acc = 0.0;\n                for (long i = 0; i < d; ++i)\n                    acc += qt[i] * Wc[i * d + j];"),
     "missing_half": ("                Wt[x] = Wc[x] - eta * G[x];\n            /* y_t",
                      "                Wt[x] = Wc[x] - 2.0 * eta * G[x];\n            /* y_t"),
     "gradient_not_accumulated": ("G[i * d + j] += kt[i] * r[j];", "G[i * d + j] = kt[i] * r[j];"),
@@ -50,6 +53,14 @@ MUTANTS = {
                                    "k[t * d + i] * r[j];"),
     "bwd_dq_uses_chunk_start": ("acc += dy[t * d + j] * w->Wt[i * d + j];",
                                 "acc += dy[t * d + j] * Wc[i * d + j];"),
+    # prologue: per-token step size and LayerNorm
+    "tok_eta_dropped": ("G[i * d + j] += eta_t[t] * kt[i] * r[j];", "G[i * d + j] += kt[i] * r[j];"),
+    "tok_eta_of_chunk_start": ("G[i * d + j] += eta_t[t] * kt[i] * r[j];",
+                               "G[i * d + j] += eta_t[s] * kt[i] * r[j];"),
+    "ln_no_mean_in_variance": ("var += (x[j] - mean) * (x[j] - mean);", "var += x[j] * x[j];"),
+    "ln_gamma_beta_swapped": ("x[j] = (x[j] - mean) * inv * gamma[h * d + j] + beta[h * d + j];",
+                              "x[j] = (x[j] - mean) * inv * beta[h * d + j] + gamma[h * d + j];"),
+    "ln_eps_dropped": ("const double inv = 1.0 / sqrt(var + eps);", "const double inv = 1.0 / sqrt(var);"),
     "bwd_state_adjoint_not_passed": ("memcpy(w->Wb, w->Wcb, (size_t)dd * sizeof(double));",
                                      "memcpy(w->Wb, w->Wtb, (size_t)dd * sizeof(double));"),
 }
@@ -75,6 +86,10 @@ def _battery():
         ("bwd_eta_zero", lambda: bpins.test_backward_eta_zero_closed_form(oracle, 4)),
         ("bwd_linear_attention", lambda: bpins.test_backward_linear_attention(oracle, 11, 16)),
         ("bwd_chain_rule", lambda: bpins.test_backward_chain_rule_across_calls(oracle)),
+        ("ln_torch", lambda: ppins.test_layernorm_matches_torch(oracle, 1e-2)),
+        ("tok_eta_head", lambda: ppins.test_constant_token_eta_is_head_eta(oracle, 4)),
+        ("tok_eta_autograd", lambda: ppins.test_token_eta_matches_autograd(oracle, 3)),
+        ("tok_eta_zero", lambda: ppins.test_zero_token_eta_freezes_the_state(oracle)),
     ]
     for name, fn in checks:
         try:
