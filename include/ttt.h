@@ -105,6 +105,33 @@ int ttt_linear_forward(const void* Q, const void* K, const void* V, int qkv_dtyp
                        void* Y, float* W_out, void* stream);
 
 /*
+ * ttt_linear_forward with the layer's input prologue fused into the scan:
+ *   - LayerNorm of every q and k row over the head dim before the inner loop
+ *     (the TTT-Linear listing in the "Hardware Parallelization" section of the
+ *     news.premlal.in page normalises the projected keys and queries):
+ *         x <- (x - mean) / sqrt(var + ln_eps) * gamma_h + beta_h,
+ *     biased variance, one (gamma, beta) pair per head; V is not normalised;
+ *   - a step size per token instead of the head's (the uTTT write-up on
+ *     thelatestinai.com, Table D3: learning rates per token, head and
+ *     matrix): token t's gradient term is scaled by eta_tok[b][h][t], i.e.
+ *         Y = Q W - tril(Q K^T) diag(eta) E,   W_next = W - K^T diag(eta) E.
+ *
+ *   eta_tok      fp32 [B][H][T], or NULL for the head's eta (then eta [H]).
+ *   ln_q, ln_k   fp32 [H][2][d] (gamma row, then beta row), or NULL for none.
+ *   ln_eps       > 0 when either LayerNorm is given.
+ * Everything else as for ttt_linear_forward (eta [H] must be valid even when
+ * eta_tok is given).  With all three NULL this is ttt_linear_forward.  The
+ * prologue runs in the d = 64, b = 16 MFMA kernels (and their segment maps)
+ * only: other shapes return TTT_ERR_UNSUPPORTED.  With bf16 inputs the
+ * normalised rows are rounded to bf16 before the products, as the inputs
+ * would be.  eta_tok, ln_q and ln_k must not overlap Y or W_out.
+ */
+int ttt_linear_forward_ex(const void* Q, const void* K, const void* V, int qkv_dtype,
+                          const float* W0, int w0_per_batch, const float* eta,
+                          const float* eta_tok, const float* ln_q, const float* ln_k, float ln_eps,
+                          int64_t B, int64_t H, int64_t T, int d, int b,
+                          void* Y, float* W_out, void* stream);
+/*
  * TTT-MLP, chunked dual form.  Inner model f(z) = SiLU(z W1) W2, W1 [d][m],
  * W2 [m][d], no biases ("Test-Time Training (TTT) Layers for Sequence
  * Modeling", section "Variants": a two-layer MLP with a SiLU non-linearity).

@@ -8,6 +8,8 @@ libttt.so is missing or a call fails, an exception is raised.
 
 Functions (same names as the C ABI):
     ttt_linear_forward(Q, K, V, W0, eta, b)           -> (Y, W_out)
+    ttt_linear_forward_ex(Q, K, V, W0, eta, b, eta_tok, ln_q, ln_k, ln_eps)
+                                                      -> (Y, W_out)
     ttt_mlp_forward(Q, K, V, W1, W2, eta, b)          -> (Y, W1_out, W2_out)
     ttt_linear_decode_step(q, k, v, W, eta)           -> y   (W updated in place)
     ttt_linear_backward(Q, K, V, W0, eta, b, dY, dW_out)
@@ -51,6 +53,9 @@ def load_library():
     P, I, L = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
     lib.ttt_linear_forward.argtypes = [P, P, P, I, P, I, P, L, L, L, I, I, P, P, P]
     lib.ttt_linear_forward.restype = I
+    lib.ttt_linear_forward_ex.argtypes = [P, P, P, I, P, I, P, P, P, P, ctypes.c_float,
+                                          L, L, L, I, I, P, P, P]
+    lib.ttt_linear_forward_ex.restype = I
     lib.ttt_mlp_forward.argtypes = [P, P, P, I, P, P, I, P, L, L, L, I, I, I, P, P, P, P]
     lib.ttt_mlp_forward.restype = I
     lib.ttt_linear_decode_step.argtypes = [P, P, P, I, P, P, L, L, I, P, P]
@@ -134,6 +139,48 @@ def ttt_linear_forward(Q, K, V, W0, eta, b: int, Y=None, W_out=None, stream=None
                                   W0.data_ptr(), int(per_batch), eta.data_ptr(),
                                   B, H, T, d, int(b), Y.data_ptr(), W_out.data_ptr(),
                                   _stream_handle(dev, stream)))
+    return Y, W_out
+
+
+def ttt_linear_forward_ex(Q, K, V, W0, eta, b: int, eta_tok=None, ln_q=None, ln_k=None,
+                          ln_eps: float = 1e-5, Y=None, W_out=None, stream=None):
+    """ttt_linear_forward with the input prologue: q and k LayerNorm'd over
+    the head dim (ln_q / ln_k fp32 [H,2,d]: gamma, beta) and a step size per
+    token (eta_tok fp32 [B,H,T]); None leaves that part out."""
+    lib = load_library()
+    if Q.dim() != 4:
+        raise ValueError("Q must be [B,H,T,d]")
+    dev = Q.device
+    B, H, T, d = Q.shape
+    for t, n in ((Q, "Q"), (K, "K"), (V, "V")):
+        _need(t, n, dev, Q.dtype)
+        if t.shape != Q.shape:
+            raise ValueError(f"{n} shape {tuple(t.shape)} != Q shape {tuple(Q.shape)}")
+    _need(W0, "W0", dev, torch.float32)
+    _need(eta, "eta", dev, torch.float32)
+    per_batch = W0.dim() == 4
+    if W0.shape != ((B, H, d, d) if per_batch else (H, d, d)) or eta.shape != (H,):
+        raise ValueError("W0 must be [H,d,d] or [B,H,d,d] and eta [H]")
+    ptrs = []
+    for t, n, shape in ((eta_tok, "eta_tok", (B, H, T)), (ln_q, "ln_q", (H, 2, d)),
+                        (ln_k, "ln_k", (H, 2, d))):
+        if t is None:
+            ptrs.append(None)
+            continue
+        _need(t, n, dev, torch.float32)
+        if t.shape != shape:
+            raise ValueError(f"{n} must be {list(shape)}, got {tuple(t.shape)}")
+        ptrs.append(t.data_ptr())
+    if Y is None:
+        Y = torch.empty_like(Q)
+    if W_out is None:
+        W_out = torch.empty((B, H, d, d), device=dev, dtype=torch.float32)
+    _need(Y, "Y", dev, Q.dtype)
+    _need(W_out, "W_out", dev, torch.float32)
+    _check(lib.ttt_linear_forward_ex(Q.data_ptr(), K.data_ptr(), V.data_ptr(), _dtype_code(Q),
+                                     W0.data_ptr(), int(per_batch), eta.data_ptr(), ptrs[0],
+                                     ptrs[1], ptrs[2], float(ln_eps), B, H, T, d, int(b),
+                                     Y.data_ptr(), W_out.data_ptr(), _stream_handle(dev, stream)))
     return Y, W_out
 
 
@@ -262,7 +309,7 @@ def ttt_linear_backward_segments(B: int, H: int, T: int, d: int, b: int,
 
 
 __all__ = [
-    "ttt_linear_forward", "ttt_mlp_forward", "ttt_linear_decode_step", "ttt_linear_backward",
+    "ttt_linear_forward", "ttt_linear_forward_ex", "ttt_mlp_forward", "ttt_linear_decode_step", "ttt_linear_backward",
     "ttt_linear_segments", "ttt_linear_backward_segments",
     "load_library",
     "status_string", "TTTError", "LIB_PATH", "TTT_F32", "TTT_BF16",

@@ -226,10 +226,16 @@ const char* ttt_status_string(int status)
     }
 }
 
-int ttt_linear_forward(const void* Q, const void* K, const void* V, int qkv_dtype,
-                       const float* W0, int w0_per_batch, const float* eta,
-                       int64_t B, int64_t H, int64_t T, int d, int b,
-                       void* Y, float* W_out, void* stream)
+}  // extern "C"
+
+namespace {
+
+// ttt_linear_forward with an optional input prologue (pro.active(): d = 64,
+// b = 16 only).
+int linear_forward_impl(const void* Q, const void* K, const void* V, int qkv_dtype,
+                        const float* W0, int w0_per_batch, const float* eta,
+                        int64_t B, int64_t H, int64_t T, int d, int b,
+                        void* Y, float* W_out, void* stream, const ttt::Prologue& pro)
 {
     if (B < 0 || H < 0 || T < 0 || b < 1 || (w0_per_batch != 0 && w0_per_batch != 1))
         return TTT_ERR_INVALID_ARG;
@@ -255,9 +261,18 @@ int ttt_linear_forward(const void* Q, const void* K, const void* V, int qkv_dtyp
         if (overlap(rWo, in)) return TTT_ERR_INVALID_ARG;
     if (overlap(rWo, rW0) && !(w0_per_batch && static_cast<const void*>(W_out) == W0))
         return TTT_ERR_INVALID_ARG;
+    if (pro.active()) {
+        const Range rTok{pro.eta_tok, pro.eta_tok ? units * T * 4 : 0};
+        const Range rLq{pro.ln_q, pro.ln_q ? H * 2 * d * 4 : 0}, rLk{pro.ln_k, pro.ln_k ? H * 2 * d * 4 : 0};
+        for (const Range& in : {rTok, rLq, rLk})
+            if (overlap(rY, in) || overlap(rWo, in)) return TTT_ERR_INVALID_ARG;
+    }
 
     LinearArgs a{Q, K, V, qkv_dtype, W0, w0_per_batch, eta, B, H, T, d, b,
                  Y, W_out, static_cast<hipStream_t>(stream)};
+    a.pro = pro;
+    if (pro.active() && !ttt::linear_mfma_supports(a) && !ttt::linear_mfma_f32_supports(a))
+        return TTT_ERR_UNSUPPORTED;
     if (ttt::linear_mfma_supports(a))
         return run_linear_segmented(a, plan_segments(units, T, b, ttt::kLinearBf16Costs),
                                     ttt::launch_linear_mfma);
@@ -267,6 +282,39 @@ int ttt_linear_forward(const void* Q, const void* K, const void* V, int qkv_dtyp
     if (ttt::linear_generic_lds_bytes(d, b) > static_cast<size_t>(ttt::kMaxLdsBytes))
         return TTT_ERR_UNSUPPORTED;
     return hip_status(ttt::launch_linear_generic(a));
+}
+
+
+}  // namespace
+
+extern "C" {
+
+int ttt_linear_forward(const void* Q, const void* K, const void* V, int qkv_dtype,
+                       const float* W0, int w0_per_batch, const float* eta,
+                       int64_t B, int64_t H, int64_t T, int d, int b,
+                       void* Y, float* W_out, void* stream)
+{
+    return linear_forward_impl(Q, K, V, qkv_dtype, W0, w0_per_batch, eta, B, H, T, d, b, Y, W_out,
+                               stream, ttt::Prologue{});
+}
+
+int ttt_linear_forward_ex(const void* Q, const void* K, const void* V, int qkv_dtype,
+                          const float* W0, int w0_per_batch, const float* eta,
+                          const float* eta_tok, const float* ln_q, const float* ln_k, float ln_eps,
+                          int64_t B, int64_t H, int64_t T, int d, int b,
+                          void* Y, float* W_out, void* stream)
+{
+    if ((ln_q || ln_k) && !(ln_eps > 0.0f && ln_eps < 1e30f))
+        return TTT_ERR_INVALID_ARG;
+    ttt::Prologue pro;
+    pro.eta_tok = eta_tok;
+    pro.ln_q = ln_q;
+    pro.ln_k = ln_k;
+    pro.ln_eps = ln_eps;
+    if (pro.active() && B * H > 0 && T > 0 && (d != 64 || b != 16))
+        return TTT_ERR_UNSUPPORTED;
+    return linear_forward_impl(Q, K, V, qkv_dtype, W0, w0_per_batch, eta, B, H, T, d, b, Y, W_out,
+                               stream, pro);
 }
 
 int ttt_linear_segments(int64_t B, int64_t H, int64_t T, int d, int b, int qkv_dtype)

@@ -35,12 +35,54 @@ __device__ __forceinline__ float silu_f(float x) { return x / (1.0f + __expf(-x)
 // ---------------------------------------------------------------------------
 // launchers (each returns hipSuccess or the launch error)
 // ---------------------------------------------------------------------------
+// Optional input prologue of the TTT-Linear MFMA kernels: LayerNorm of the q
+// and k rows over the head dim (per-head gamma, beta; biased variance) and a
+// step size per token instead of the head's.  All null: the plain scan.
+struct Prologue {
+    const float* eta_tok = nullptr;   // [B][H][T]
+    const float* ln_q = nullptr;      // [H][2][d]: gamma row, then beta row
+    const float* ln_k = nullptr;
+    float ln_eps = 1e-5f;
+    bool active() const { return eta_tok || ln_q || ln_k; }
+};
+
 struct LinearArgs {
     const void* Q; const void* K; const void* V; int dtype;
     const float* W0; int w0_per_batch; const float* eta;
     int64_t B, H, T; int d, b;
     void* Y; float* W_out; hipStream_t stream;
+    Prologue pro{};
 };
+
+// LayerNorm of one 64-element row spread over kLanes consecutive lanes (kN
+// elements each, all lanes of the wave active): mean and biased variance by
+// butterfly sums inside the lane group, then (x - mean) / sqrt(var + eps) *
+// gamma + beta; a row that is not `valid` (past the sequence end) becomes 0.
+template <int kLanes, int kN>
+__device__ __forceinline__ void layernorm_row(float (&x)[kN], const float (&gm)[kN],
+                                              const float (&bt)[kN], float eps, bool valid)
+{
+    static_assert(kLanes * kN == 64, "one 64-element row");
+    float sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < kN; ++i)
+        sum += x[i];
+#pragma unroll
+    for (int m = 1; m < kLanes; m <<= 1)
+        sum += __shfl_xor(sum, m);
+    const float mean = sum * (1.0f / 64.0f);
+    float sq = 0.f;
+#pragma unroll
+    for (int i = 0; i < kN; ++i)
+        sq += (x[i] - mean) * (x[i] - mean);
+#pragma unroll
+    for (int m = 1; m < kLanes; m <<= 1)
+        sq += __shfl_xor(sq, m);
+    const float rstd = rsqrtf(sq * (1.0f / 64.0f) + eps);
+#pragma unroll
+    for (int i = 0; i < kN; ++i)
+        x[i] = valid ? (x[i] - mean) * rstd * gm[i] + bt[i] : 0.f;
+}
 
 struct MlpArgs {
     const void* Q; const void* K; const void* V; int dtype;

@@ -75,7 +75,6 @@ constexpr int kOffQ = kOffK + kB * kRowBytes;        // 2048
 constexpr int kOffV = kOffQ + kB * kRowBytes;        // 4096
 constexpr int kChunkBytes = kOffV + kB * kRowBytes;  // 6144
 constexpr int kSlotBytes = kChunkBytes * kStageChunks;
-constexpr int kLdsBytes = kSlotBytes * kSlots;       // 36864
 
 static_assert((2 * kSet) % kSlots == 0, "slot index must be static inside the loop");
 
@@ -161,6 +160,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t chain_rsrc(const void* base, i
 // lane l holds row 8w + l / 8, 16-byte segment l % 8.
 struct StageRegs {
     u32x4 k, q, v;
+    uint32_t eta;      // step size of this lane's token (prologue only)
 };
 
 
@@ -173,13 +173,18 @@ struct StageRegs {
 //   halves share the staged K.  No Q, no Y.
 // With nseg > 1 the blocks of chain u all run on XCD u % 8 (see xcd_block),
 // so the maps, start states and scans of a chain meet in one L2.
-template <bool kMaps>
+// kPro: the input prologue (Prologue in ttt_internal.h) is applied while the
+//   inputs are staged: K and Q rows LayerNorm'd over the head dim in fp32 and
+//   rounded to bf16, and each token's step size written after the stage in
+//   LDS, where it scales its row of the residual: E'[t] = -eta_t R[t] (the
+//   head's eta when no per-token step sizes are given).
+template <bool kMaps, bool kPro>
 __global__ void __launch_bounds__(kMaps ? 2 * kThreads : kThreads, 1)
 linear_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                    const uint16_t* __restrict__ V, const float* W0, int w0_per_batch,
                    const float* __restrict__ eta, int H, int T, int64_t units, int seg_len,
                    int nseg, float* maps, const float* wstart, uint16_t* __restrict__ Y,
-                   float* W_out)
+                   float* W_out, Prologue pro)
 {
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
 
@@ -239,6 +244,8 @@ linear_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     const __amdgpu_buffer_rsrc_t ry = chain_rsrc(Y + base, kMaps ? 0 : seg_bytes);
 
     const int nstages = (t_len + kStageTokens - 1) / kStageTokens;
+    // a slot also holds the stage's 32 step sizes when the prologue is on
+    constexpr int kSlotB = kPro ? kSlotBytes + kStageTokens * 4 : kSlotBytes;
     // stages per register set: the maps block runs 8 waves (half the
     // registers per wave), so it prefetches 3-6 stages ahead instead of 6-12
     constexpr int kSetK = kMaps ? kSet / 2 : kSet;
@@ -248,6 +255,23 @@ linear_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     // staging: this lane's row inside the stage and its 16-byte segment
     const int st_row = 8 * w + (lane >> 3);             // 0..31
     const int st_seg = lane & 7;
+    // prologue: LayerNorm gamma, beta of this lane's 8 columns 8 st_seg .. +7
+    const bool use_tok = kPro && pro.eta_tok != nullptr;
+    const bool ln_k = kPro && pro.ln_k != nullptr;
+    const bool ln_q = kPro && !kMaps && pro.ln_q != nullptr;
+    float gk[8], bk[8], gq[8], bq[8];
+    if constexpr (kPro) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            gk[e] = ln_k ? pro.ln_k[(2 * h) * kD + 8 * st_seg + e] : 1.f;
+            bk[e] = ln_k ? pro.ln_k[(2 * h + 1) * kD + 8 * st_seg + e] : 0.f;
+            gq[e] = ln_q ? pro.ln_q[(2 * h) * kD + 8 * st_seg + e] : 1.f;
+            bq[e] = ln_q ? pro.ln_q[(2 * h + 1) * kD + 8 * st_seg + e] : 0.f;
+        }
+    }
+    const __amdgpu_buffer_rsrc_t reta =
+        chain_rsrc(use_tok ? pro.eta_tok + u * static_cast<int64_t>(T) + t_begin : eta,
+                   use_tok ? static_cast<int64_t>(t_len) * 4 : 0);
     auto load_stage = [&](StageRegs& o, int stage) {
         if (!stager)
             return;
@@ -256,11 +280,36 @@ linear_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
         if (!kMaps)
             o.q = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0);
         o.v = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0);
+        if (use_tok)
+            o.eta = __builtin_amdgcn_raw_buffer_load_b32(reta, (stage * kStageTokens + st_row) * 4, 0, 0);
     };
-    auto write_stage = [&](const StageRegs& o, int slot) {
+    // LayerNorm of a staged row segment (8 bf16 per lane, 8 lanes per row),
+    // rounded back to bf16
+    auto norm = [&](u32x4 x, const float (&gm)[8], const float (&bt)[8], bool valid) {
+        float f[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            f[2 * e] = __uint_as_float(x[e] << 16);
+            f[2 * e + 1] = __uint_as_float(x[e] & 0xffff0000u);
+        }
+        layernorm_row<8, 8>(f, gm, bt, pro.ln_eps, valid);
+        const bf16x8 r = pack8(f32x4{f[0], f[1], f[2], f[3]}, f32x4{f[4], f[5], f[6], f[7]});
+        return __builtin_bit_cast(u32x4, r);
+    };
+    auto write_stage = [&](StageRegs o, int slot, int stage) {
         if (!stager)
             return;
-        unsigned char* chunk = lds + slot * kSlotBytes + (st_row >> 4) * kChunkBytes;
+        if constexpr (kPro) {
+            const bool valid = stage * kStageTokens + st_row < t_len;
+            if (ln_k)
+                o.k = norm(o.k, gk, bk, valid);
+            if (ln_q)
+                o.q = norm(o.q, gq, bq, valid);
+            if (st_seg == 0)
+                *reinterpret_cast<float*>(lds + slot * kSlotB + kSlotBytes + 4 * st_row) =
+                    use_tok ? __uint_as_float(o.eta) : et;
+        }
+        unsigned char* chunk = lds + slot * kSlotB + (st_row >> 4) * kChunkBytes;
         const int r = st_row & 15;
         *reinterpret_cast<u32x4*>(chunk + kOffK + swz(r, st_seg)) = o.k;
         if (!kMaps)
@@ -273,6 +322,7 @@ linear_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
         bf16x8 ka0, ka1, qa0, qa1;
         bf16x4 vrow;
         bf16x4 kt[4];
+        f32x4 eta4;        // step sizes of tokens 4g .. 4g+3 (prologue)
     };
     auto read_ops = [&](ChunkOps& o, const unsigned char* tile) {
         o.ka0 = *reinterpret_cast<const bf16x8*>(tile + kOffK + swz(c, g));
@@ -308,8 +358,9 @@ linear_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
         R = mfma32(o.ka0, b0, R);
         R = mfma32(o.ka1, b1, R);
 
-        // E' = eta (V - K W) = -eta R
-        const bf16x4 eb = pack4(-et * R);
+        // E' = eta (V - K W) = -eta R (row t scaled by its own step size
+        // with the prologue)
+        const bf16x4 eb = pack4(kPro ? -(o.eta4 * R) : -et * R);
 
         // W += K^T E'
 #pragma unroll
@@ -340,12 +391,16 @@ linear_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
 
     // Stage s: publish stage s + 1 (held in `next`), then compute stage s.
     auto process = [&](const StageRegs& next, int s, int slot) {
-        write_stage(next, (slot + 1) % kSlots);
+        write_stage(next, (slot + 1) % kSlots, s + 1);
         __syncthreads();
-        const unsigned char* sl = lds + slot * kSlotBytes;
+        const unsigned char* sl = lds + slot * kSlotB;
         ChunkOps o0, o1;
         read_ops(o0, sl);
         read_ops(o1, sl + kChunkBytes);
+        if constexpr (kPro) {
+            o0.eta4 = *reinterpret_cast<const f32x4*>(sl + kSlotBytes + 16 * g);
+            o1.eta4 = *reinterpret_cast<const f32x4*>(sl + kSlotBytes + 64 + 16 * g);
+        }
         step(o0, s * kStageTokens);
         step(o1, s * kStageTokens + kB);
     };
@@ -355,7 +410,7 @@ linear_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
         {
             StageRegs first;
             load_stage(first, 0);
-            write_stage(first, 0);
+            write_stage(first, 0, 0);
         }
 #pragma unroll
         for (int p = 0; p < kSetK; ++p)
@@ -411,7 +466,10 @@ bool linear_mfma_supports(const LinearArgs& a)
     return a.dtype == 1 && a.d == kD && a.b == kB && a.T <= max_tokens;
 }
 
-hipError_t launch_linear_mfma(const LinearArgs& a, const SegmentPlan& p)
+namespace {
+
+template <bool kPro>
+hipError_t launch_bf16(const LinearArgs& a, const SegmentPlan& p)
 {
     const auto* q = static_cast<const uint16_t*>(a.Q);
     const auto* k = static_cast<const uint16_t*>(a.K);
@@ -420,11 +478,12 @@ hipError_t launch_linear_mfma(const LinearArgs& a, const SegmentPlan& p)
     const int H = static_cast<int>(a.H), T = static_cast<int>(a.T);
     const int seg_len = static_cast<int>(p.seg_len);
     const int64_t units = a.B * a.H;
+    const int lds = kSlots * (kPro ? kSlotBytes + kStageTokens * 4 : kSlotBytes);
     if (p.nseg > 1) {
         const dim3 grid(static_cast<unsigned>(placed_grid(units, p.nseg - 1)));
-        hipLaunchKernelGGL(linear_mfma_kernel<true>, grid, dim3(2 * kThreads), kLdsBytes, a.stream, q, k,
-                           v, a.W0, a.w0_per_batch, a.eta, H, T, units, seg_len, p.nseg, p.maps,
-                           p.wstart, y, a.W_out);
+        hipLaunchKernelGGL((linear_mfma_kernel<true, kPro>), grid, dim3(2 * kThreads), lds, a.stream, q,
+                           k, v, a.W0, a.w0_per_batch, a.eta, H, T, units, seg_len, p.nseg, p.maps,
+                           p.wstart, y, a.W_out, a.pro);
         hipError_t e = hipGetLastError();
         if (e == hipSuccess)
             e = launch_linear_combine(a, p);
@@ -432,10 +491,17 @@ hipError_t launch_linear_mfma(const LinearArgs& a, const SegmentPlan& p)
             return e;
     }
     const dim3 grid(static_cast<unsigned>(p.nseg > 1 ? placed_grid(units, p.nseg) : units));
-    hipLaunchKernelGGL(linear_mfma_kernel<false>, grid, dim3(kThreads), kLdsBytes, a.stream, q, k, v,
+    hipLaunchKernelGGL((linear_mfma_kernel<false, kPro>), grid, dim3(kThreads), lds, a.stream, q, k, v,
                        a.W0, a.w0_per_batch, a.eta, H, T, units, seg_len, p.nseg, p.maps, p.wstart, y,
-                       a.W_out);
+                       a.W_out, a.pro);
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_linear_mfma(const LinearArgs& a, const SegmentPlan& p)
+{
+    return a.pro.active() ? launch_bf16<true>(a, p) : launch_bf16<false>(a, p);
 }
 
 }  // namespace ttt

@@ -53,7 +53,6 @@ constexpr int kOffQ = kOffK + kB * kRowBytes;        // 4096
 constexpr int kOffKt = kOffQ + kB * kRowBytes;       // 8192  [64 i][16 t] fp32
 constexpr int kOffVt = kOffKt + kD * kB * 4;         // 12288 [64 j][16 t] fp32
 constexpr int kSlotBytes = kOffVt + kD * kB * 4;     // 16384
-constexpr int kLdsBytes = kSlotBytes * kSlots;       // 49152
 
 static_assert((2 * kSet) % kSlots == 0, "slot index must be static inside the loop");
 
@@ -81,6 +80,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t chain_rsrc(const void* base, i
 
 struct StageRegs {
     u32x4 k, q, v;
+    uint32_t eta;      // step size of this lane's token (prologue only)
 };
 
 // Row of W held in register r of accumulator tile mt by lane group g.
@@ -97,13 +97,18 @@ __device__ __forceinline__ int wrow(int mt, int m) { return 16 * (m >> 2) + 4 * 
 //   so sharing one CU would halve each half's speed.)
 // With nseg > 1 the blocks of chain u all run on XCD u % 8 (see xcd_block),
 // so the maps, start states and scans of a chain meet in one L2.
-template <bool kMaps>
+// kPro: the input prologue (Prologue in ttt_internal.h) is applied while the
+//   inputs are staged: K and Q rows LayerNorm'd over the head dim, and each
+//   token's step size written next to the chunk in LDS, where it scales its
+//   row of the residual: E'[t] = -eta_t R[t] (the head's eta when no
+//   per-token step sizes are given).
+template <bool kMaps, bool kPro>
 __global__ void __launch_bounds__(kThreads, 1)
 linear_mfma_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                        const float* __restrict__ V, const float* W0, int w0_per_batch,
                        const float* __restrict__ eta, int H, int T, int64_t units, int seg_len,
                        int nseg, float* maps, const float* wstart, float* __restrict__ Y,
-                       float* W_out)
+                       float* W_out, Prologue pro)
 {
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
 
@@ -157,6 +162,8 @@ linear_mfma_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
     const __amdgpu_buffer_rsrc_t ry = chain_rsrc(Y + base, kMaps ? 0 : seg_bytes);
 
     const int nchunks = (t_len + kB - 1) / kB;
+    // a slot also holds the chunk's 16 step sizes when the prologue is on
+    constexpr int kSlotB = kPro ? kSlotBytes + kB * 4 : kSlotBytes;
     constexpr int kSetK = kSet;
     static_assert((2 * kSetK) % kSlots == 0, "slot index must be static inside the loop");
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
@@ -164,15 +171,54 @@ linear_mfma_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
     // staging: lane l of wave w holds row 4w + l / 16, 16-byte segment l % 16
     const int st_row = 4 * w + (lane >> 4);
     const int st_seg = lane & 15;
+    // prologue: LayerNorm gamma, beta of this lane's 4 columns 4 st_seg .. +3
+    const bool use_tok = kPro && pro.eta_tok != nullptr;
+    const bool ln_k = kPro && pro.ln_k != nullptr;
+    const bool ln_q = kPro && !kMaps && pro.ln_q != nullptr;
+    float gk[4], bk[4], gq[4], bq[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        gk[e] = ln_k ? pro.ln_k[(2 * h) * kD + 4 * st_seg + e] : 1.f;
+        bk[e] = ln_k ? pro.ln_k[(2 * h + 1) * kD + 4 * st_seg + e] : 0.f;
+        gq[e] = ln_q ? pro.ln_q[(2 * h) * kD + 4 * st_seg + e] : 1.f;
+        bq[e] = ln_q ? pro.ln_q[(2 * h + 1) * kD + 4 * st_seg + e] : 0.f;
+    }
+    const __amdgpu_buffer_rsrc_t reta =
+        chain_rsrc(use_tok ? pro.eta_tok + u * static_cast<int64_t>(T) + t_begin : eta,
+                   use_tok ? static_cast<int64_t>(t_len) * 4 : 0);
     auto load_stage = [&](StageRegs& o, int chunk) {
         const int off = (chunk * kB + st_row) * kRowBytes + st_seg * 16;
         o.k = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
         if (!kMaps)
             o.q = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0);
         o.v = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0);
+        if (use_tok)
+            o.eta = __builtin_amdgcn_raw_buffer_load_b32(reta, (chunk * kB + st_row) * 4, 0, 0);
     };
-    auto write_stage = [&](const StageRegs& o, int slot) {
-        unsigned char* sl = lds + slot * kSlotBytes;
+    // LayerNorm of a staged row segment (16 lanes per row)
+    auto norm = [&](u32x4 x, const float (&gm)[4], const float (&bt)[4], bool valid) {
+        float f[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            f[e] = __uint_as_float(x[e]);
+        layernorm_row<16, 4>(f, gm, bt, pro.ln_eps, valid);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            x[e] = __float_as_uint(f[e]);
+        return x;
+    };
+    auto write_stage = [&](StageRegs o, int slot, int chunk) {
+        unsigned char* sl = lds + slot * kSlotB;
+        if constexpr (kPro) {
+            const bool valid = chunk * kB + st_row < t_len;
+            if (ln_k)
+                o.k = norm(o.k, gk, bk, valid);
+            if (ln_q)
+                o.q = norm(o.q, gq, bq, valid);
+            if (st_seg == 0)
+                *reinterpret_cast<float*>(sl + kSlotBytes + 4 * st_row) =
+                    use_tok ? __uint_as_float(o.eta) : et;
+        }
         *reinterpret_cast<u32x4*>(sl + kOffK + swz_row(st_row, st_seg)) = o.k;
         if (!kMaps)
             *reinterpret_cast<u32x4*>(sl + kOffQ + swz_row(st_row, st_seg)) = o.q;
@@ -191,6 +237,7 @@ linear_mfma_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
         f32x4 q[4];        // Q[t = c][16g + 4x .. +3]
         f32x4 kt[4];       // K^T[16g... see below]: kt[mt] = K[4g .. 4g+3][i = 16(c/4) + 4mt + c%4]
         f32x4 vt;          // V[4g .. 4g+3][col]
+        f32x4 eta4;        // step sizes of tokens 4g .. 4g+3 (prologue)
     };
     auto read_ops = [&](ChunkOps& o, const unsigned char* sl) {
 #pragma unroll
@@ -204,6 +251,8 @@ linear_mfma_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
             o.kt[mt] = *reinterpret_cast<const f32x4*>(
                 sl + kOffKt + swz_kt(16 * (c >> 2) + 4 * mt + (c & 3), g));
         o.vt = *reinterpret_cast<const f32x4*>(sl + kOffVt + swz_vt(col, g));
+        if constexpr (kPro)
+            o.eta4 = *reinterpret_cast<const f32x4*>(sl + kSlotBytes + 16 * g);
     };
 
     auto step = [&](const ChunkOps& o, int t0) {
@@ -230,7 +279,7 @@ linear_mfma_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
         const f32x4 Rs = (R[0] + R[1]) + (R[2] + R[3]);
 
         // E' = -eta R: lane (c = j, g) holds E'[t = 4g + q][j]
-        const f32x4 Ep = -et * Rs;
+        const f32x4 Ep = kPro ? -(o.eta4 * Rs) : -et * Rs;
 
         // W += K^T E' (k-steps q over tokens t = 4g + q)
 #pragma unroll
@@ -259,10 +308,10 @@ linear_mfma_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
     };
 
     auto process = [&](const StageRegs& next, int chunk, int slot) {
-        write_stage(next, (slot + 1) % kSlots);
+        write_stage(next, (slot + 1) % kSlots, chunk + 1);
         __syncthreads();
         ChunkOps o;
-        read_ops(o, lds + slot * kSlotBytes);
+        read_ops(o, lds + slot * kSlotB);
         step(o, chunk * kB);
     };
 
@@ -271,7 +320,7 @@ linear_mfma_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
         {
             StageRegs first;
             load_stage(first, 0);
-            write_stage(first, 0);
+            write_stage(first, 0, 0);
         }
 #pragma unroll
         for (int p = 0; p < kSetK; ++p)
@@ -325,7 +374,10 @@ bool linear_mfma_f32_supports(const LinearArgs& a)
     return a.dtype == 0 && a.d == kD && a.b == kB && a.T <= max_tokens;
 }
 
-hipError_t launch_linear_mfma_f32(const LinearArgs& a, const SegmentPlan& p)
+namespace {
+
+template <bool kPro>
+hipError_t launch_f32(const LinearArgs& a, const SegmentPlan& p)
 {
     const auto* q = static_cast<const float*>(a.Q);
     const auto* k = static_cast<const float*>(a.K);
@@ -334,11 +386,12 @@ hipError_t launch_linear_mfma_f32(const LinearArgs& a, const SegmentPlan& p)
     const int H = static_cast<int>(a.H), T = static_cast<int>(a.T);
     const int seg_len = static_cast<int>(p.seg_len);
     const int64_t units = a.B * a.H;
+    const int lds = kSlots * (kPro ? kSlotBytes + kB * 4 : kSlotBytes);
     if (p.nseg > 1) {
         const dim3 grid(static_cast<unsigned>(placed_grid(units, 2 * (p.nseg - 1))));
-        hipLaunchKernelGGL(linear_mfma_f32_kernel<true>, grid, dim3(kThreads), kLdsBytes, a.stream, q,
+        hipLaunchKernelGGL((linear_mfma_f32_kernel<true, kPro>), grid, dim3(kThreads), lds, a.stream, q,
                            k, v, a.W0, a.w0_per_batch, a.eta, H, T, units, seg_len, p.nseg, p.maps,
-                           p.wstart, y, a.W_out);
+                           p.wstart, y, a.W_out, a.pro);
         hipError_t e = hipGetLastError();
         if (e == hipSuccess)
             e = launch_linear_combine(a, p);
@@ -346,10 +399,17 @@ hipError_t launch_linear_mfma_f32(const LinearArgs& a, const SegmentPlan& p)
             return e;
     }
     const dim3 grid(static_cast<unsigned>(p.nseg > 1 ? placed_grid(units, p.nseg) : units));
-    hipLaunchKernelGGL(linear_mfma_f32_kernel<false>, grid, dim3(kThreads), kLdsBytes, a.stream, q, k, v,
-                       a.W0, a.w0_per_batch, a.eta, H, T, units, seg_len, p.nseg, p.maps, p.wstart, y,
-                       a.W_out);
+    hipLaunchKernelGGL((linear_mfma_f32_kernel<false, kPro>), grid, dim3(kThreads), lds, a.stream, q, k,
+                       v, a.W0, a.w0_per_batch, a.eta, H, T, units, seg_len, p.nseg, p.maps, p.wstart,
+                       y, a.W_out, a.pro);
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_linear_mfma_f32(const LinearArgs& a, const SegmentPlan& p)
+{
+    return a.pro.active() ? launch_f32<true>(a, p) : launch_f32<false>(a, p);
 }
 
 }  // namespace ttt

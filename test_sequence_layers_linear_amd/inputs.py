@@ -25,6 +25,11 @@ Backward cotangents (make_cotangents): dY ~ N(0, 1/d) in the input dtype and
 dW_out ~ N(0, 1/d) fp32, from their own seed -- a stand-in for the gradient an
 outer loss sends back into the layer.
 
+Input prologue (make_prologue): LayerNorm gamma ~ U[0.8, 1.2] and beta ~
+N(0, 0.1^2) per head for q and for k, and per-token step sizes
+eta_t ~ U[0.1/d, 0.6/d] (LayerNorm'd keys have |k|^2 about d, so eta_t |k|^2
+stays below 1 and each step contracts).
+
 Generator: numpy.random.default_rng(seed), float32 standard normals scaled in
 float32, then cast to the input dtype (bf16 by round-to-nearest-even through
 torch).  Draw order: Q, K, V, initial state (W0, or W1 then W2), eta, then the
@@ -145,6 +150,22 @@ def make_cotangents(w: Workload, seed: int, device="cpu", zero_state: bool = Fal
     else:
         dWo = torch.from_numpy(_normal(rng, (w.B, w.H, w.d, w.d), std))
     return {"dY": dY.to(device), "dW_out": dWo.to(device)}
+
+
+def make_prologue(w: Workload, seed: int, device="cpu") -> dict:
+    """Seeded prologue parameters for a TTT-Linear workload: ln_q, ln_k
+    [H,2,d] fp32 (gamma row, beta row), eta_tok [B,H,T] fp32 and a head eta
+    [H] on the same scale."""
+    rng = np.random.default_rng(seed)
+    out = {}
+    for name in ("ln_q", "ln_k"):
+        gamma = rng.uniform(0.8, 1.2, size=(w.H, w.d)).astype(np.float32)
+        beta = _normal(rng, (w.H, w.d), 0.1)
+        out[name] = torch.from_numpy(np.stack([gamma, beta], axis=1))
+    lo, hi = 0.1 / w.d, 0.6 / w.d
+    out["eta_tok"] = torch.from_numpy(rng.uniform(lo, hi, size=(w.B, w.H, w.T)).astype(np.float32))
+    out["eta"] = torch.from_numpy(rng.uniform(lo, hi, size=(w.H,)).astype(np.float32))
+    return {k: v.to(device) for k, v in out.items()}
 
 
 def default_seed(config: int) -> int:

@@ -37,7 +37,8 @@ def lib():
 def test_exports_every_declared_function(lib):
     names = declared_functions()
     assert set(names) >= {"ttt_linear_forward", "ttt_mlp_forward", "ttt_linear_decode_step",
-                          "ttt_linear_backward", "ttt_linear_segments", "ttt_status_string",
+                          "ttt_linear_backward", "ttt_linear_forward_ex", "ttt_linear_segments",
+                          "ttt_linear_backward_segments", "ttt_status_string",
                           "ttt_abi_version"}
     for n in names:
         assert hasattr(lib, n), f"{n} declared in ttt.h but not exported"
@@ -69,6 +70,28 @@ def lin(lib, Q=QA, K=KA, V=VA, dt=1, W0=W0A, pb=0, eta=ETA, B=2, H=3, T=64, d=64
 ])
 def test_linear_validation(lib, kw, expect):
     assert lin(lib, **kw) == expect
+
+
+TOKA, LNQA, LNKA = (0xC0_0000_0000 + 0x10_0000_0000 * i for i in range(3))
+
+
+def linx(lib, tok=TOKA, lnq=LNQA, lnk=LNKA, eps=1e-5, d=64, b=16, Y=YA, Wo=WOA, T=64, dt=1, B=2):
+    return lib.ttt_linear_forward_ex(QA, KA, VA, dt, W0A, 0, ETA, tok, lnq, lnk, eps, B, 3, T, d, b,
+                                     Y, Wo, None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(eps=0.0), INVALID), (dict(eps=-1.0), INVALID), (dict(eps=float("nan")), INVALID),
+    (dict(d=32), UNSUPPORTED), (dict(b=8), UNSUPPORTED), (dict(d=32, tok=None), UNSUPPORTED),
+    (dict(Y=TOKA), INVALID), (dict(Wo=LNKA + 64), INVALID), (dict(Y=LNQA), INVALID),
+    (dict(B=0), OK),
+    # eps is not checked when no LayerNorm is asked for; every prologue pointer
+    # NULL falls back to the plain forward's rules
+    (dict(lnq=None, lnk=None, eps=0.0, B=0), OK),
+    (dict(tok=None, lnq=None, lnk=None, d=48), UNSUPPORTED),
+])
+def test_linear_forward_ex_validation(lib, kw, expect):
+    assert linx(lib, **kw) == expect
 
 
 def test_linear_no_inputs_needed_when_empty(lib):

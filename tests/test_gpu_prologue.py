@@ -1,0 +1,95 @@
+"""GPU parity of ttt_linear_forward_ex (LayerNorm of q and k, step size per
+token) against the fp64 oracle's linear_forward_ex.
+
+Relative L2 of Y and W_out within 1e-4 for fp32 inputs and 2e-2 for bf16
+inputs (whose normalised rows are rounded to bf16 before the products, while
+the oracle keeps them exact).  Cases: each part of the prologue alone and
+together, ragged tails, segmented scans (forced segment counts) and two
+benchmark workloads at full size.
+"""
+import pytest
+import torch
+
+import oracle
+import test_sequence_layers_linear_amd as ttt
+from parity_util import CONFIGS, TOL, announce, default_seed, make_inputs, rel_l2, to_gpu
+from test_sequence_layers_linear_amd.inputs import make_prologue
+
+pytestmark = pytest.mark.gpu
+
+PARTS = {"ln": ("ln_q", "ln_k"), "ln_k": ("ln_k",), "tok": ("eta_tok",),
+         "all": ("ln_q", "ln_k", "eta_tok")}
+
+
+def _run(w, seed, parts, per_batch=False, eps=1e-5):
+    inp = make_inputs(w, seed, w0_per_batch=per_batch)
+    pro = make_prologue(w, seed + 3)
+    inp["eta"] = pro["eta"]
+    kw = {k: pro[k] for k in parts}
+    g = to_gpu(inp)
+    gk = to_gpu(kw)
+    Y, W = ttt.ttt_linear_forward_ex(g["Q"], g["K"], g["V"], g["W0"], g["eta"], w.b, ln_eps=eps, **gk)
+    torch.cuda.synchronize()
+    Yr, Wr = oracle.linear_forward_ex(inp["Q"], inp["K"], inp["V"], inp["W0"], inp["eta"], w.b,
+                                      ln_eps=eps, **kw)
+    ey, ew = rel_l2(Y, Yr), rel_l2(W, Wr)
+    print(f"  rel-L2 Y {ey:.3e}  W {ew:.3e}", flush=True)
+    return ey, ew
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("part", sorted(PARTS))
+@pytest.mark.parametrize("B,H,T,per_batch", [(1, 2, 16, False), (2, 3, 77, True), (1, 2, 300, False)])
+def test_prologue_small(dtype, part, B, H, T, per_batch, monkeypatch):
+    monkeypatch.setenv("TTT_LINEAR_SEGMENTS", "1")
+    w = CONFIGS[3].with_(B=B, H=H, T=T, dtype=dtype)
+    seed = 9000 + B * 100 + H * 10 + T
+    announce("prologue", dtype, part, B, H, T, seed)
+    ey, ew = _run(w, seed, PARTS[part], per_batch)
+    assert ey <= TOL[dtype] and ew <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("T,S", [(100, 2), (333, 3), (480, 30)])
+def test_prologue_segmented(dtype, T, S, monkeypatch):
+    monkeypatch.setenv("TTT_LINEAR_SEGMENTS", str(S))
+    w = CONFIGS[3].with_(B=1, H=3, T=T, dtype=dtype)
+    seed = 9100 + T + S
+    announce("prologue segmented", dtype, T, S, seed)
+    ey, ew = _run(w, seed, PARTS["all"])
+    assert ey <= TOL[dtype] and ew <= TOL[dtype]
+
+
+def test_prologue_eps_matters_for_flat_rows():
+    """A constant key row normalises to beta alone; eps only scales the zero."""
+    w = CONFIGS[3].with_(B=1, H=2, T=40, dtype="fp32")
+    announce("prologue flat rows")
+    inp = make_inputs(w, 9200)
+    inp["K"][0, 1, 5] = 0.25
+    pro = make_prologue(w, 9203)
+    inp["eta"] = pro["eta"]
+    g = to_gpu(inp)
+    Y, W = ttt.ttt_linear_forward_ex(g["Q"], g["K"], g["V"], g["W0"], g["eta"], 16,
+                                     ln_k=pro["ln_k"].cuda(), ln_eps=1e-3)
+    torch.cuda.synchronize()
+    Yr, Wr = oracle.linear_forward_ex(inp["Q"], inp["K"], inp["V"], inp["W0"], inp["eta"], 16,
+                                      ln_k=pro["ln_k"], ln_eps=1e-3)
+    assert rel_l2(Y, Yr) <= 1e-4 and rel_l2(W, Wr) <= 1e-4
+
+
+def test_prologue_off_is_plain_forward():
+    w = CONFIGS[3].with_(B=2, H=2, T=200)
+    announce("prologue off")
+    g = to_gpu(make_inputs(w, 9300))
+    Y0, W0 = ttt.ttt_linear_forward(g["Q"], g["K"], g["V"], g["W0"], g["eta"], 16)
+    Y1, W1 = ttt.ttt_linear_forward_ex(g["Q"], g["K"], g["V"], g["W0"], g["eta"], 16)
+    torch.cuda.synchronize()
+    assert torch.equal(Y0, Y1) and torch.equal(W0, W1)
+
+
+@pytest.mark.parametrize("cfg", [2, 3])
+def test_prologue_config_full(cfg):
+    w = CONFIGS[cfg]
+    announce("prologue config", cfg, w.name)
+    ey, ew = _run(w, default_seed(cfg) + 900, PARTS["all"])
+    assert ey <= TOL[w.dtype] and ew <= TOL[w.dtype]
