@@ -26,7 +26,8 @@ Each TTT-Linear workload also reports "backward": ttt_linear_backward (the
 gradients of Q, K, V, W0 and eta for seeded cotangents dY, dW_out) timed the
 same way, with its own roofline (fp32 MFMA: the kernel computes in fp32 for
 both input dtypes).  It is reported beside the forward, not folded into the
-headline value.
+headline value.  "prologue" times ttt_linear_forward_ex on the same inputs
+with LayerNorm of q and k and a step size per token fused into the scan.
 """
 from __future__ import annotations
 
@@ -299,6 +300,29 @@ class Runner:
         torch.cuda.synchronize()
         return start.elapsed_time(end) / 1e3 / steps
 
+    def measure_prologue(self, steps, warmup):
+        """Mean duration of ttt_linear_forward_ex with the whole prologue
+        (LayerNorm of q and k, per-token step sizes)."""
+        torch, g, w = self.torch, self.g, self.w
+        from test_sequence_layers_linear_amd.inputs import make_prologue
+        pro = {k: v.cuda() for k, v in make_prologue(w, 11).items()}
+
+        def call():
+            self.ttt.ttt_linear_forward_ex(g["Q"], g["K"], g["V"], g["W0"], pro["eta"], w.b,
+                                           eta_tok=pro["eta_tok"], ln_q=pro["ln_q"],
+                                           ln_k=pro["ln_k"], Y=self.Y, W_out=self.W)
+        for _ in range(warmup):
+            call()
+        torch.cuda.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record()
+        for _ in range(steps):
+            call()
+        end.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / 1e3 / steps
+
     def measure_cold(self, reps):
         """Forward duration with the 256 MB last-level cache flushed before each launch."""
         torch = self.torch
@@ -386,8 +410,11 @@ def measure_workload(cfg, steps, warmup, cold_reps):
         wf = w.with_(dtype="fp32")       # the kernel's arithmetic: fp32 MFMA
         kern = backward_kernel_names(w)
         rf = roofline(wf, bf, bb, bt, kern)
-        rf["traffic"] = stored_traffic(kern, w.name)
+        rf["traffic"] = stored_traffic(kern, w.name + "/backward")
         out["backward"] = {"us": bt * 1e6, "tokens_per_s": w.B * w.T / bt, "roofline": rf}
+        pt = r.measure_prologue(max(3, steps // 2), 2)
+        out["prologue"] = {"us": pt * 1e6, "tokens_per_s": w.B * w.T / pt,
+                           "vs_plain_forward": pt / fwd}
     if w.decode_steps:
         df, db = decode_work(w)
         per = dec / w.decode_steps

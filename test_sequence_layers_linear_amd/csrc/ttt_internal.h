@@ -54,10 +54,32 @@ struct LinearArgs {
     Prologue pro{};
 };
 
+// Sum over each aligned group of kLanes (8 or 16) lanes, every lane of the
+// group receiving it, with DPP lane permutes (no LDS round trip): quad
+// xor 1, quad xor 2, then the half-row mirror (lane i <-> 7 - i: the other
+// quad) and, for 16 lanes, the row mirror (i <-> 15 - i: the other half).
+template <int kCtrl>
+__device__ __forceinline__ float dpp_mov(float v)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), kCtrl,
+                                                              0xf, 0xf, true));
+}
+template <int kLanes>
+__device__ __forceinline__ float group_sum(float x)
+{
+    static_assert(kLanes == 8 || kLanes == 16, "8 or 16 lanes");
+    x += dpp_mov<0xb1>(x);      // quad_perm [1, 0, 3, 2]
+    x += dpp_mov<0x4e>(x);      // quad_perm [2, 3, 0, 1]
+    x += dpp_mov<0x141>(x);     // row_half_mirror
+    if (kLanes == 16)
+        x += dpp_mov<0x140>(x); // row_mirror
+    return x;
+}
+
 // LayerNorm of one 64-element row spread over kLanes consecutive lanes (kN
-// elements each, all lanes of the wave active): mean and biased variance by
-// butterfly sums inside the lane group, then (x - mean) / sqrt(var + eps) *
-// gamma + beta; a row that is not `valid` (past the sequence end) becomes 0.
+// elements each, all lanes of the wave active): mean and biased variance
+// (two passes), then (x - mean) / sqrt(var + eps) * gamma + beta; a row that
+// is not `valid` (past the sequence end) becomes 0.
 template <int kLanes, int kN>
 __device__ __forceinline__ void layernorm_row(float (&x)[kN], const float (&gm)[kN],
                                               const float (&bt)[kN], float eps, bool valid)
@@ -67,18 +89,12 @@ __device__ __forceinline__ void layernorm_row(float (&x)[kN], const float (&gm)[
 #pragma unroll
     for (int i = 0; i < kN; ++i)
         sum += x[i];
-#pragma unroll
-    for (int m = 1; m < kLanes; m <<= 1)
-        sum += __shfl_xor(sum, m);
-    const float mean = sum * (1.0f / 64.0f);
+    const float mean = group_sum<kLanes>(sum) * (1.0f / 64.0f);
     float sq = 0.f;
 #pragma unroll
     for (int i = 0; i < kN; ++i)
         sq += (x[i] - mean) * (x[i] - mean);
-#pragma unroll
-    for (int m = 1; m < kLanes; m <<= 1)
-        sq += __shfl_xor(sq, m);
-    const float rstd = rsqrtf(sq * (1.0f / 64.0f) + eps);
+    const float rstd = rsqrtf(group_sum<kLanes>(sq) * (1.0f / 64.0f) + eps);
 #pragma unroll
     for (int i = 0; i < kN; ++i)
         x[i] = valid ? (x[i] - mean) * rstd * gm[i] + bt[i] : 0.f;

@@ -296,15 +296,24 @@ linear_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
         const bf16x8 r = pack8(f32x4{f[0], f[1], f[2], f[3]}, f32x4{f[4], f[5], f[6], f[7]});
         return __builtin_bit_cast(u32x4, r);
     };
-    auto write_stage = [&](StageRegs o, int slot, int stage) {
-        if (!stager)
-            return;
+    // LayerNorm a stage's rows in their registers, at the end of the stage
+    // before the one that writes them to LDS: after that stage's products, so
+    // that the scheduler can overlap the two
+    auto prep = [&](StageRegs& o, int stage) {
         if constexpr (kPro) {
+            if (!stager)
+                return;
             const bool valid = stage * kStageTokens + st_row < t_len;
             if (ln_k)
                 o.k = norm(o.k, gk, bk, valid);
             if (ln_q)
                 o.q = norm(o.q, gq, bq, valid);
+        }
+    };
+    auto write_stage = [&](const StageRegs& o, int slot) {
+        if (!stager)
+            return;
+        if constexpr (kPro) {
             if (st_seg == 0)
                 *reinterpret_cast<float*>(lds + slot * kSlotB + kSlotBytes + 4 * st_row) =
                     use_tok ? __uint_as_float(o.eta) : et;
@@ -390,8 +399,8 @@ linear_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     };
 
     // Stage s: publish stage s + 1 (held in `next`), then compute stage s.
-    auto process = [&](const StageRegs& next, int s, int slot) {
-        write_stage(next, (slot + 1) % kSlots, s + 1);
+    auto process = [&](const StageRegs& next, int s, int slot, StageRegs& ahead) {
+        write_stage(next, (slot + 1) % kSlots);
         __syncthreads();
         const unsigned char* sl = lds + slot * kSlotB;
         ChunkOps o0, o1;
@@ -403,6 +412,7 @@ linear_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
         }
         step(o0, s * kStageTokens);
         step(o1, s * kStageTokens + kB);
+        prep(ahead, s + 2);
     };
 
     if (nstages > 0) {
@@ -410,11 +420,13 @@ linear_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
         {
             StageRegs first;
             load_stage(first, 0);
-            write_stage(first, 0, 0);
+            prep(first, 0);
+            write_stage(first, 0);
         }
 #pragma unroll
         for (int p = 0; p < kSetK; ++p)
             load_stage(setA[p], 1 + p);
+        prep(setA[0], 1);
         // stages s0 .. s0 + 2 kSetK - 1 per iteration; setA holds s0 + 1 .. s0 + kSetK
         for (int s0 = 0; s0 < nstages; s0 += 2 * kSetK) {
 #pragma unroll
@@ -425,7 +437,7 @@ linear_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
             for (int p = 0; p < kSetK; ++p) {
                 if (s0 + p >= nstages)       // uniform: the scan is done
                     goto done;
-                process(setA[p], s0 + p, p % kSlots);
+                process(setA[p], s0 + p, p % kSlots, p + 1 < kSetK ? setA[p + 1] : setB[0]);
             }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -436,7 +448,8 @@ linear_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
             for (int p = 0; p < kSetK; ++p) {
                 if (s0 + kSetK + p >= nstages)
                     goto done;
-                process(setB[p], s0 + kSetK + p, (kSetK + p) % kSlots);
+                process(setB[p], s0 + kSetK + p, (kSetK + p) % kSlots,
+                        p + 1 < kSetK ? setB[p + 1] : setA[0]);
             }
             __builtin_amdgcn_sched_barrier(0);
         }

@@ -207,14 +207,21 @@ linear_mfma_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
             x[e] = __float_as_uint(f[e]);
         return x;
     };
-    auto write_stage = [&](StageRegs o, int slot, int chunk) {
-        unsigned char* sl = lds + slot * kSlotB;
+    // LayerNorm a chunk's rows in their registers, at the end of the chunk
+    // before the one that writes them to LDS: after that chunk's products, so
+    // that the scheduler can overlap the two
+    auto prep = [&](StageRegs& o, int chunk) {
         if constexpr (kPro) {
             const bool valid = chunk * kB + st_row < t_len;
             if (ln_k)
                 o.k = norm(o.k, gk, bk, valid);
             if (ln_q)
                 o.q = norm(o.q, gq, bq, valid);
+        }
+    };
+    auto write_stage = [&](const StageRegs& o, int slot) {
+        unsigned char* sl = lds + slot * kSlotB;
+        if constexpr (kPro) {
             if (st_seg == 0)
                 *reinterpret_cast<float*>(sl + kSlotBytes + 4 * st_row) =
                     use_tok ? __uint_as_float(o.eta) : et;
@@ -307,12 +314,13 @@ linear_mfma_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
         }
     };
 
-    auto process = [&](const StageRegs& next, int chunk, int slot) {
-        write_stage(next, (slot + 1) % kSlots, chunk + 1);
+    auto process = [&](const StageRegs& next, int chunk, int slot, StageRegs& ahead) {
+        write_stage(next, (slot + 1) % kSlots);
         __syncthreads();
         ChunkOps o;
         read_ops(o, lds + slot * kSlotB);
         step(o, chunk * kB);
+        prep(ahead, chunk + 2);
     };
 
     if (nchunks > 0) {
@@ -320,11 +328,13 @@ linear_mfma_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
         {
             StageRegs first;
             load_stage(first, 0);
-            write_stage(first, 0, 0);
+            prep(first, 0);
+            write_stage(first, 0);
         }
 #pragma unroll
         for (int p = 0; p < kSetK; ++p)
             load_stage(setA[p], 1 + p);
+        prep(setA[0], 1);
         for (int c0 = 0; c0 < nchunks; c0 += 2 * kSetK) {
 #pragma unroll
             for (int p = 0; p < kSetK; ++p)
@@ -334,7 +344,7 @@ linear_mfma_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
             for (int p = 0; p < kSetK; ++p) {
                 if (c0 + p >= nchunks)       // uniform: the scan is done
                     goto done;
-                process(setA[p], c0 + p, p % kSlots);
+                process(setA[p], c0 + p, p % kSlots, p + 1 < kSetK ? setA[p + 1] : setB[0]);
             }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -345,7 +355,8 @@ linear_mfma_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
             for (int p = 0; p < kSetK; ++p) {
                 if (c0 + kSetK + p >= nchunks)
                     goto done;
-                process(setB[p], c0 + kSetK + p, (kSetK + p) % kSlots);
+                process(setB[p], c0 + kSetK + p, (kSetK + p) % kSlots,
+                        p + 1 < kSetK ? setB[p + 1] : setA[0]);
             }
             __builtin_amdgcn_sched_barrier(0);
         }

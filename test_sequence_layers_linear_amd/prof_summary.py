@@ -46,9 +46,9 @@ def short_name(full: str) -> str:
         return "linear_backward_kernel[gmaps]" if ", true>" in full else "linear_backward_kernel[segments]"
     for k in KERNEL_FILES:
         base = k.split("[")[0]
-        if base + "<true>" in full:
+        if base + "<true" in full:
             return base + "[maps]"
-        if base + "<false>" in full:
+        if base + "<false" in full:
             return base + "[scan]"
         if base + "(" in full or base + "<" in full:
             return k
@@ -83,6 +83,9 @@ def main():
     ap.add_argument("--title", help="heading (default: the workload name)")
     ap.add_argument("--command", required=True, help="the rocprofv3 command lines that made the data")
     ap.add_argument("--copy-mib", type=int, default=256)
+    ap.add_argument("--call", default="forward", choices=["forward", "backward"],
+                    help="which call the trace covers (the traffic table keys the backward's "
+                         "kernels under '<workload>/backward')")
     ap.add_argument("--out", required=True)
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"))
     args = ap.parse_args()
@@ -122,7 +125,8 @@ def main():
                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
                      f"{rd / 1e6:.3f} | {wb / 1e6:.3f} |")
         if fr and wr:
-            table.setdefault(name, {})[w.name] = {
+            key = w.name if args.call == "forward" else w.name + "/backward"
+            table.setdefault(name, {})[key] = {
                 "source_sha": source_sha(name), "bytes_per_launch": int(rd + wb),
                 "read_bytes": int(rd), "write_bytes": int(wb),
                 "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
