@@ -119,8 +119,14 @@ int ttt_linear_forward(const void* Q, const void* K, const void* V, int qkv_dtyp
  *   eta_tok      fp32 [B][H][T], or NULL for the head's eta (then eta [H]).
  *   ln_q, ln_k   fp32 [H][2][d] (gamma row, then beta row), or NULL for none.
  *   ln_eps       > 0 when either LayerNorm is given.
+ *   read_mode    0: token t reads out with the weights after its own update
+ *                (the pages' rule, as ttt_linear_forward); 1: every token of
+ *                a mini-batch reads out with the mini-batch's start weights,
+ *                Y = Q W (the uTTT write-up, Figure 2(a): forward reads use
+ *                the chunk-start state).  The state recurrence is the same.
  * Everything else as for ttt_linear_forward (eta [H] must be valid even when
- * eta_tok is given).  With all three NULL this is ttt_linear_forward.  The
+ * eta_tok is given).  With all three NULL and read_mode 0 this is
+ * ttt_linear_forward.  The
  * prologue runs in the d = 64, b = 16 MFMA kernels (and their segment maps)
  * only: other shapes return TTT_ERR_UNSUPPORTED.  With bf16 inputs the
  * normalised rows are rounded to bf16 before the products, as the inputs
@@ -129,7 +135,7 @@ int ttt_linear_forward(const void* Q, const void* K, const void* V, int qkv_dtyp
 int ttt_linear_forward_ex(const void* Q, const void* K, const void* V, int qkv_dtype,
                           const float* W0, int w0_per_batch, const float* eta,
                           const float* eta_tok, const float* ln_q, const float* ln_k, float ln_eps,
-                          int64_t B, int64_t H, int64_t T, int d, int b,
+                          int read_mode, int64_t B, int64_t H, int64_t T, int d, int b,
                           void* Y, float* W_out, void* stream);
 /*
  * TTT-MLP, chunked dual form.  Inner model f(z) = SiLU(z W1) W2, W1 [d][m],

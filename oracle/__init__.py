@@ -20,7 +20,10 @@ Parity status of each function (how it is pinned, see tests/test_oracle.py):
   linear_forward_ex -- pinned: per-token eta equal to the head's eta gives
                      linear_forward; autograd mini-batch GD with per-token
                      step sizes; a zero step size drops a token from the
-                     update; LayerNorm equals torch's layer_norm.
+                     update; LayerNorm equals torch's layer_norm; the
+                     chunk-start read is block-causal linear attention for
+                     W0 = 0, online GD read before the update for b = 1, and
+                     leaves W_out unchanged.
   linear_backward -- pinned: central finite differences of linear_forward in
                      every coordinate (tiny sizes), the closed form of every
                      gradient at eta=0 (independent of b), the gradients of
@@ -73,7 +76,7 @@ def _load():
     lib.ttt_oracle_linear_backward.argtypes = [P, P, P, P, I, P, L, L, L, L, L, P, P,
                                                P, P, P, P, P, I]
     lib.ttt_oracle_linear_backward.restype = I
-    lib.ttt_oracle_linear_forward_tok.argtypes = [P, P, P, P, I, P, L, L, L, L, L, P, P, I]
+    lib.ttt_oracle_linear_forward_tok.argtypes = [P, P, P, P, I, P, I, L, L, L, L, L, P, P, I]
     lib.ttt_oracle_linear_forward_tok.restype = I
     lib.ttt_oracle_layernorm_rows.argtypes = [P, L, L, L, L, P, P, ctypes.c_double]
     lib.ttt_oracle_layernorm_rows.restype = I
@@ -139,27 +142,29 @@ def layernorm(X, ln, eps: float):
 
 
 def linear_forward_ex(Q, K, V, W0, eta, b: int, eta_tok=None, ln_q=None, ln_k=None,
-                      ln_eps: float = 1e-5, nthreads: int = 0):
+                      ln_eps: float = 1e-5, read_chunk_start: bool = False, nthreads: int = 0):
     """TTT-Linear with the input prologue: Q and K each LayerNorm'd over the
     head dim when ln_q / ln_k ([H,2,d], gamma then beta) are given, and a step
-    size per token eta_tok [B,H,T] (else the head's eta).  Returns (Y, W_out)
-    in fp64."""
+    size per token eta_tok [B,H,T] (else the head's eta).  read_chunk_start:
+    every token reads out with its mini-batch's start weights.  Returns
+    (Y, W_out) in fp64."""
     Q, K, V, W0, eta = map(_f64, (Q, K, V, W0, eta))
     B, H, T, d = Q.shape
     if ln_q is not None:
         Q = layernorm(Q, ln_q, ln_eps)
     if ln_k is not None:
         K = layernorm(K, ln_k, ln_eps)
-    if eta_tok is None:
+    if eta_tok is None and not read_chunk_start:
         return linear_forward(Q, K, V, W0, eta, b, nthreads)
-    et = _f64(eta_tok)
+    et = _f64(eta_tok) if eta_tok is not None else np.broadcast_to(eta[None, :, None], (B, H, T)).copy()
     assert et.shape == (B, H, T)
     per_batch = 1 if W0.ndim == 4 else 0
     assert W0.shape == ((B, H, d, d) if per_batch else (H, d, d))
     Y = np.zeros((B, H, T, d))
     W_out = np.zeros((B, H, d, d))
     rc = _load().ttt_oracle_linear_forward_tok(_ptr(Q), _ptr(K), _ptr(V), _ptr(W0), per_batch,
-                                               _ptr(et), B, H, T, d, int(b), _ptr(Y),
+                                               _ptr(et), int(bool(read_chunk_start)), B, H, T, d,
+                                               int(b), _ptr(Y),
                                                _ptr(W_out), int(nthreads))
     if rc != 0:
         raise RuntimeError(f"oracle linear_forward_tok failed ({rc})")

@@ -177,11 +177,13 @@ int ttt_oracle_linear_forward(const double* Q, const double* K, const double* V,
 /* Table D3: learning rates per token, head and matrix).  Same primal loops:  */
 /*   r_t = k_t Wc - v_t,  G_t = G_{t-1} + eta_t k_t^T r_t,  W_t = Wc - G_t,   */
 /*   y_t = q_t W_t.                                                           */
-/* eta_tok: [B][H][T].                                                        */
+/* eta_tok: [B][H][T].  read_start != 0: every token of a mini-batch reads   */
+/* out with the chunk-start weights instead, y_t = q_t Wc (the uTTT write-up, */
+/* Figure 2(a): forward reads use the chunk-start state).                     */
 /* ------------------------------------------------------------------------ */
 static void linear_chain_tok(const double* q, const double* k, const double* v,
-                             const double* w_init, const double* eta_t, long T, long d, long b,
-                             double* y, double* w_final,
+                             const double* w_init, const double* eta_t, int read_start,
+                             long T, long d, long b, double* y, double* w_final,
                              double* W, double* Wc, double* G, double* Wt, double* r)
 {
     const long dd = d * d;
@@ -206,10 +208,11 @@ static void linear_chain_tok(const double* q, const double* k, const double* v,
                     G[i * d + j] += eta_t[t] * kt[i] * r[j];
             for (long x = 0; x < dd; ++x)
                 Wt[x] = Wc[x] - G[x];
+            const double* Wr = read_start ? Wc : Wt;
             for (long j = 0; j < d; ++j) {
                 double acc = 0.0;
                 for (long i = 0; i < d; ++i)
-                    acc += qt[i] * Wt[i * d + j];
+                    acc += qt[i] * Wr[i * d + j];
                 y[t * d + j] = acc;
             }
         }
@@ -220,7 +223,7 @@ static void linear_chain_tok(const double* q, const double* k, const double* v,
 
 int ttt_oracle_linear_forward_tok(const double* Q, const double* K, const double* V,
                                   const double* W0, int w0_per_batch, const double* eta_tok,
-                                  long B, long H, long T, long d, long b,
+                                  int read_start, long B, long H, long T, long d, long b,
                                   double* Y, double* W_out, int nthreads)
 {
     if (B < 0 || H < 0 || T < 0 || d < 1 || b < 1)
@@ -245,8 +248,8 @@ int ttt_oracle_linear_forward_tok(const double* Q, const double* K, const double
             long h = u % H;
             const double* w_init = W0 + (w0_per_batch ? u : h) * dd;
             const long off = u * T * d;
-            linear_chain_tok(Q + off, K + off, V + off, w_init, eta_tok + u * T, T, d, b,
-                             Y + off, W_out + u * dd,
+            linear_chain_tok(Q + off, K + off, V + off, w_init, eta_tok + u * T, read_start,
+                             T, d, b, Y + off, W_out + u * dd,
                              ws, ws + dd, ws + 2 * dd, ws + 3 * dd, ws + 4 * dd);
         }
         free(ws);

@@ -53,7 +53,7 @@ def load_library():
     P, I, L = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
     lib.ttt_linear_forward.argtypes = [P, P, P, I, P, I, P, L, L, L, I, I, P, P, P]
     lib.ttt_linear_forward.restype = I
-    lib.ttt_linear_forward_ex.argtypes = [P, P, P, I, P, I, P, P, P, P, ctypes.c_float,
+    lib.ttt_linear_forward_ex.argtypes = [P, P, P, I, P, I, P, P, P, P, ctypes.c_float, I,
                                           L, L, L, I, I, P, P, P]
     lib.ttt_linear_forward_ex.restype = I
     lib.ttt_mlp_forward.argtypes = [P, P, P, I, P, P, I, P, L, L, L, I, I, I, P, P, P, P]
@@ -143,10 +143,12 @@ def ttt_linear_forward(Q, K, V, W0, eta, b: int, Y=None, W_out=None, stream=None
 
 
 def ttt_linear_forward_ex(Q, K, V, W0, eta, b: int, eta_tok=None, ln_q=None, ln_k=None,
-                          ln_eps: float = 1e-5, Y=None, W_out=None, stream=None):
+                          ln_eps: float = 1e-5, read_chunk_start: bool = False, Y=None,
+                          W_out=None, stream=None):
     """ttt_linear_forward with the input prologue: q and k LayerNorm'd over
     the head dim (ln_q / ln_k fp32 [H,2,d]: gamma, beta) and a step size per
-    token (eta_tok fp32 [B,H,T]); None leaves that part out."""
+    token (eta_tok fp32 [B,H,T]); None leaves that part out.
+    read_chunk_start: tokens read out with their mini-batch's start weights."""
     lib = load_library()
     if Q.dim() != 4:
         raise ValueError("Q must be [B,H,T,d]")
@@ -179,7 +181,8 @@ def ttt_linear_forward_ex(Q, K, V, W0, eta, b: int, eta_tok=None, ln_q=None, ln_
     _need(W_out, "W_out", dev, torch.float32)
     _check(lib.ttt_linear_forward_ex(Q.data_ptr(), K.data_ptr(), V.data_ptr(), _dtype_code(Q),
                                      W0.data_ptr(), int(per_batch), eta.data_ptr(), ptrs[0],
-                                     ptrs[1], ptrs[2], float(ln_eps), B, H, T, d, int(b),
+                                     ptrs[1], ptrs[2], float(ln_eps), int(bool(read_chunk_start)),
+                                     B, H, T, d, int(b),
                                      Y.data_ptr(), W_out.data_ptr(), _stream_handle(dev, stream)))
     return Y, W_out
 

@@ -301,16 +301,19 @@ int ttt_linear_forward(const void* Q, const void* K, const void* V, int qkv_dtyp
 int ttt_linear_forward_ex(const void* Q, const void* K, const void* V, int qkv_dtype,
                           const float* W0, int w0_per_batch, const float* eta,
                           const float* eta_tok, const float* ln_q, const float* ln_k, float ln_eps,
-                          int64_t B, int64_t H, int64_t T, int d, int b,
+                          int read_mode, int64_t B, int64_t H, int64_t T, int d, int b,
                           void* Y, float* W_out, void* stream)
 {
     if ((ln_q || ln_k) && !(ln_eps > 0.0f && ln_eps < 1e30f))
+        return TTT_ERR_INVALID_ARG;
+    if (read_mode != 0 && read_mode != 1)
         return TTT_ERR_INVALID_ARG;
     ttt::Prologue pro;
     pro.eta_tok = eta_tok;
     pro.ln_q = ln_q;
     pro.ln_k = ln_k;
     pro.ln_eps = ln_eps;
+    pro.read_start = read_mode;
     if (pro.active() && B * H > 0 && T > 0 && (d != 64 || b != 16))
         return TTT_ERR_UNSUPPORTED;
     return linear_forward_impl(Q, K, V, qkv_dtype, W0, w0_per_batch, eta, B, H, T, d, b, Y, W_out,

@@ -43,7 +43,8 @@ struct Prologue {
     const float* ln_q = nullptr;      // [H][2][d]: gamma row, then beta row
     const float* ln_k = nullptr;
     float ln_eps = 1e-5f;
-    bool active() const { return eta_tok || ln_q || ln_k; }
+    int read_start = 0;               // 1: tokens read out with the chunk-start W
+    bool active() const { return eta_tok || ln_q || ln_k || read_start; }
 };
 
 struct LinearArgs {

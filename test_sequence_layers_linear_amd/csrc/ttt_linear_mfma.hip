@@ -177,7 +177,8 @@ struct StageRegs {
 //   inputs are staged: K and Q rows LayerNorm'd over the head dim in fp32 and
 //   rounded to bf16, and each token's step size written after the stage in
 //   LDS, where it scales its row of the residual: E'[t] = -eta_t R[t] (the
-//   head's eta when no per-token step sizes are given).
+//   head's eta when no per-token step sizes are given); with read_start every
+//   token reads out with the chunk-start W (the tril term is dropped).
 template <bool kMaps, bool kPro>
 __global__ void __launch_bounds__(kMaps ? 2 * kThreads : kThreads, 1)
 linear_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
@@ -388,7 +389,8 @@ linear_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 Sm[r] = (4 * g + r <= c) ? St[r] : 0.f;
-            const bf16x4 sb = pack4(Sm);
+            // (the chunk-start read drops the intra-chunk term: zero operand)
+            const bf16x4 sb = (kPro && pro.read_start) ? bf16x4{} : pack4(Sm);
             Yt = mfma16_as32(eb, sb, Yt);
 
             // Y[t0 + c][16w + 4g .. +3]; rows past the segment fall outside the buffer.

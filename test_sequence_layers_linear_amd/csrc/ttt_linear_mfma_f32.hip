@@ -101,7 +101,8 @@ __device__ __forceinline__ int wrow(int mt, int m) { return 16 * (m >> 2) + 4 * 
 //   inputs are staged: K and Q rows LayerNorm'd over the head dim, and each
 //   token's step size written next to the chunk in LDS, where it scales its
 //   row of the residual: E'[t] = -eta_t R[t] (the head's eta when no
-//   per-token step sizes are given).
+//   per-token step sizes are given); with read_start every token reads out
+//   with the chunk-start W (the tril term is dropped).
 template <bool kMaps, bool kPro>
 __global__ void __launch_bounds__(kThreads, 1)
 linear_mfma_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
@@ -299,9 +300,11 @@ linear_mfma_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
             f32x4 S = (St[0] + St[1]) + (St[2] + St[3]);
             const f32x4 Ys = (Yt[0] + Yt[1]) + (Yt[2] + Yt[3]);
             // S^T masked: lane (c = t, g) holds S[t][t' = 4g + q]; keep t' <= t
+            // (the chunk-start read drops the intra-chunk term)
+            const bool keep = !(kPro && pro.read_start);
 #pragma unroll
             for (int qq = 0; qq < 4; ++qq)
-                S[qq] = (4 * g + qq <= c) ? S[qq] : 0.f;
+                S[qq] = (keep && 4 * g + qq <= c) ? S[qq] : 0.f;
             f32x4 Y2 = zero;
 #pragma unroll
             for (int qq = 0; qq < 4; ++qq)

@@ -75,15 +75,18 @@ def test_linear_validation(lib, kw, expect):
 TOKA, LNQA, LNKA = (0xC0_0000_0000 + 0x10_0000_0000 * i for i in range(3))
 
 
-def linx(lib, tok=TOKA, lnq=LNQA, lnk=LNKA, eps=1e-5, d=64, b=16, Y=YA, Wo=WOA, T=64, dt=1, B=2):
-    return lib.ttt_linear_forward_ex(QA, KA, VA, dt, W0A, 0, ETA, tok, lnq, lnk, eps, B, 3, T, d, b,
-                                     Y, Wo, None)
+def linx(lib, tok=TOKA, lnq=LNQA, lnk=LNKA, eps=1e-5, rm=0, d=64, b=16, Y=YA, Wo=WOA, T=64, dt=1,
+         B=2):
+    return lib.ttt_linear_forward_ex(QA, KA, VA, dt, W0A, 0, ETA, tok, lnq, lnk, eps, rm, B, 3, T,
+                                     d, b, Y, Wo, None)
 
 
 @pytest.mark.parametrize("kw,expect", [
     (dict(eps=0.0), INVALID), (dict(eps=-1.0), INVALID), (dict(eps=float("nan")), INVALID),
     (dict(d=32), UNSUPPORTED), (dict(b=8), UNSUPPORTED), (dict(d=32, tok=None), UNSUPPORTED),
     (dict(Y=TOKA), INVALID), (dict(Wo=LNKA + 64), INVALID), (dict(Y=LNQA), INVALID),
+    (dict(rm=2), INVALID), (dict(rm=-1), INVALID),
+    (dict(tok=None, lnq=None, lnk=None, rm=1, d=32), UNSUPPORTED),
     (dict(B=0), OK),
     # eps is not checked when no LayerNorm is asked for; every prologue pointer
     # NULL falls back to the plain forward's rules

@@ -93,3 +93,26 @@ def test_prologue_config_full(cfg):
     announce("prologue config", cfg, w.name)
     ey, ew = _run(w, default_seed(cfg) + 900, PARTS["all"])
     assert ey <= TOL[w.dtype] and ew <= TOL[w.dtype]
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("T,S,parts", [(77, 1, ()), (300, 1, ("eta_tok",)), (333, 3, ("ln_q", "ln_k", "eta_tok"))])
+def test_chunk_start_read(dtype, T, S, parts, monkeypatch):
+    """Tokens read out with their mini-batch's start weights (read_mode 1)."""
+    monkeypatch.setenv("TTT_LINEAR_SEGMENTS", str(S))
+    w = CONFIGS[3].with_(B=2, H=3, T=T, dtype=dtype)
+    seed = 9400 + T + S
+    announce("chunk-start read", dtype, T, S, parts, seed)
+    inp = make_inputs(w, seed)
+    pro = make_prologue(w, seed + 3)
+    inp["eta"] = pro["eta"]
+    kw = {k: pro[k] for k in parts}
+    g = to_gpu(inp)
+    Y, W = ttt.ttt_linear_forward_ex(g["Q"], g["K"], g["V"], g["W0"], g["eta"], 16,
+                                     read_chunk_start=True, **to_gpu(kw))
+    torch.cuda.synchronize()
+    Yr, Wr = oracle.linear_forward_ex(inp["Q"], inp["K"], inp["V"], inp["W0"], inp["eta"], 16,
+                                      read_chunk_start=True, **kw)
+    ey, ew = rel_l2(Y, Yr), rel_l2(W, Wr)
+    print(f"  rel-L2 Y {ey:.3e}  W {ew:.3e}", flush=True)
+    assert ey <= TOL[dtype] and ew <= TOL[dtype]

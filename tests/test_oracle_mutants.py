@@ -57,6 +57,8 @@ MUTANTS = {
     "tok_eta_dropped": ("G[i * d + j] += eta_t[t] * kt[i] * r[j];", "G[i * d + j] += kt[i] * r[j];"),
     "tok_eta_of_chunk_start": ("G[i * d + j] += eta_t[t] * kt[i] * r[j];",
                                "G[i * d + j] += eta_t[s] * kt[i] * r[j];"),
+    "chunk_start_read_uses_updated": ("const double* Wr = read_start ? Wc : Wt;",
+                                      "const double* Wr = read_start ? Wt : Wt;"),
     "ln_no_mean_in_variance": ("var += (x[j] - mean) * (x[j] - mean);", "var += x[j] * x[j];"),
     "ln_gamma_beta_swapped": ("x[j] = (x[j] - mean) * inv * gamma[h * d + j] + beta[h * d + j];",
                               "x[j] = (x[j] - mean) * inv * beta[h * d + j] + gamma[h * d + j];"),
@@ -90,6 +92,8 @@ def _battery():
         ("tok_eta_head", lambda: ppins.test_constant_token_eta_is_head_eta(oracle, 4)),
         ("tok_eta_autograd", lambda: ppins.test_token_eta_matches_autograd(oracle, 3)),
         ("tok_eta_zero", lambda: ppins.test_zero_token_eta_freezes_the_state(oracle)),
+        ("start_read_la", lambda: ppins.test_chunk_start_read_is_block_causal_linear_attention(oracle, 13, 8)),
+        ("start_read_b1", lambda: ppins.test_chunk_start_read_b1_is_online_gd_read_before_update(oracle)),
     ]
     for name, fn in checks:
         try:

@@ -110,3 +110,45 @@ def test_zero_token_eta_freezes_the_state(oracle):
                                       eta_tok=et[:, :, :16])
     assert _rel(W, W1) < 1e-15
     assert _rel(Y[:, :, 16:], Q[:, :, 16:] @ W1) < 1e-13
+
+
+# --------------------------------------------------------------------------
+# chunk-start read (the uTTT write-up, Figure 2(a))
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("T,b", [(32, 16), (13, 8), (16, 16)])
+def test_chunk_start_read_is_block_causal_linear_attention(oracle, T, b):
+    # from W0 = 0 the weights of mini-batch 1 are eta K_0^T V_0 exactly, so
+    # the first two mini-batches read block-causal linear attention
+    rng = np.random.default_rng(810 + T + b)
+    Q, K, V, _, eta, _ = _case(rng, B=1, H=2, T=T, d=6)
+    W0 = np.zeros((2, 6, 6))
+    Y, _ = oracle.linear_forward_ex(Q, K, V, W0, eta, b, read_chunk_start=True)
+    for h in range(2):
+        ref = np.zeros((T, 6))
+        for t in range(T):
+            for s in range(t - t % b):          # tokens of earlier mini-batches only
+                ref[t] += eta[h] * np.dot(Q[0, h, t], K[0, h, s]) * V[0, h, s]
+        assert _rel(Y[0, h], ref) < 1e-13
+
+
+def test_chunk_start_read_b1_is_online_gd_read_before_update(oracle):
+    rng = np.random.default_rng(820)
+    Q, K, V, W0, eta, _ = _case(rng, B=1, H=1, T=25, d=5)
+    Wcol = W0[0].T.copy()
+    ys = []
+    for t in range(25):
+        ys.append(Wcol @ Q[0, 0, t])            # read with the weights before this token
+        err = Wcol @ K[0, 0, t] - V[0, 0, t]
+        Wcol = Wcol - eta[0] * np.outer(err, K[0, 0, t])
+    Y, W = oracle.linear_forward_ex(Q, K, V, W0, eta, 1, read_chunk_start=True)
+    assert _rel(Y[0, 0], np.array(ys)) < 1e-13
+    assert _rel(W[0, 0], Wcol.T) < 1e-13
+
+
+def test_chunk_start_read_keeps_the_state_recurrence(oracle):
+    rng = np.random.default_rng(830)
+    Q, K, V, W0, eta, _ = _case(rng, B=2, H=2, T=45, d=7)
+    et = rng.uniform(0.05, 0.3, size=(2, 2, 45))
+    _, W1 = oracle.linear_forward_ex(Q, K, V, W0, eta, 16, eta_tok=et, read_chunk_start=True)
+    _, W2 = oracle.linear_forward_ex(Q, K, V, W0, eta, 16, eta_tok=et)
+    np.testing.assert_array_equal(W1, W2)
