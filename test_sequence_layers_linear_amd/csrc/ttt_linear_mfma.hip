@@ -102,33 +102,30 @@ __device__ __forceinline__ f32x4 mfma16(bf16x4 a, bf16x4 b, f32x4 c)
 // the upper four k-slots zero, so that every accumulation chain has one shape.
 __device__ __forceinline__ f32x4 mfma16_as32(bf16x4 a, bf16x4 b, f32x4 c)
 {
-    bf16x8 a8, b8;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        a8[e] = a[e];
-        b8[e] = b[e];
-        a8[4 + e] = static_cast<__bf16>(0.0f);
-        b8[4 + e] = static_cast<__bf16>(0.0f);
-    }
-    return mfma32(a8, b8, c);
+    const u32x2 aw = __builtin_bit_cast(u32x2, a), bw = __builtin_bit_cast(u32x2, b);
+    return mfma32(__builtin_bit_cast(bf16x8, u32x4{aw[0], aw[1], 0u, 0u}),
+                  __builtin_bit_cast(bf16x8, u32x4{bw[0], bw[1], 0u, 0u}), c);
+}
+
+// fp32 -> bf16 (round to nearest even), two values per conversion
+// instruction.  Built from 32-bit words: element-wise conversions feeding an
+// MFMA operand otherwise compile to one conversion per value plus permutes.
+__device__ __forceinline__ uint32_t cvt2(float a, float b)
+{
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
 
 __device__ __forceinline__ bf16x8 pack8(f32x4 lo, f32x4 hi)
 {
-    bf16x8 r;
-    r[0] = static_cast<__bf16>(lo[0]); r[1] = static_cast<__bf16>(lo[1]);
-    r[2] = static_cast<__bf16>(lo[2]); r[3] = static_cast<__bf16>(lo[3]);
-    r[4] = static_cast<__bf16>(hi[0]); r[5] = static_cast<__bf16>(hi[1]);
-    r[6] = static_cast<__bf16>(hi[2]); r[7] = static_cast<__bf16>(hi[3]);
-    return r;
+    return __builtin_bit_cast(bf16x8, u32x4{cvt2(lo[0], lo[1]), cvt2(lo[2], lo[3]),
+                                            cvt2(hi[0], hi[1]), cvt2(hi[2], hi[3])});
 }
 
 __device__ __forceinline__ bf16x4 pack4(f32x4 x)
 {
-    bf16x4 r;
-    r[0] = static_cast<__bf16>(x[0]); r[1] = static_cast<__bf16>(x[1]);
-    r[2] = static_cast<__bf16>(x[2]); r[3] = static_cast<__bf16>(x[3]);
-    return r;
+    return __builtin_bit_cast(bf16x4, u32x2{cvt2(x[0], x[1]), cvt2(x[2], x[3])});
 }
 
 __device__ __forceinline__ int rho(int mt, int m)

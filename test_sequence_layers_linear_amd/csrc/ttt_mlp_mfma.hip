@@ -94,23 +94,24 @@ __device__ __forceinline__ f32x4 mfma16(bf16x4 a, bf16x4 b, f32x4 c)
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a),
                                                      __builtin_bit_cast(i16x4, b), c, 0, 0, 0);
 }
+// fp32 -> bf16 (round to nearest even), two values per conversion
+// instruction.  Built from 32-bit words: element-wise conversions feeding an
+// MFMA operand otherwise compile to one conversion per value plus permutes.
+__device__ __forceinline__ uint32_t cvt2(float a, float b)
+{
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+
 __device__ __forceinline__ bf16x8 pack8(f32x4 lo, f32x4 hi)
 {
-    bf16x8 r;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        r[e] = static_cast<__bf16>(lo[e]);
-        r[4 + e] = static_cast<__bf16>(hi[e]);
-    }
-    return r;
+    return __builtin_bit_cast(bf16x8, u32x4{cvt2(lo[0], lo[1]), cvt2(lo[2], lo[3]),
+                                            cvt2(hi[0], hi[1]), cvt2(hi[2], hi[3])});
 }
 __device__ __forceinline__ bf16x4 pack4(f32x4 x)
 {
-    bf16x4 r;
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-        r[e] = static_cast<__bf16>(x[e]);
-    return r;
+    return __builtin_bit_cast(bf16x4, u32x2{cvt2(x[0], x[1]), cvt2(x[2], x[3])});
 }
 // A 16x16x16 product accumulated onto a 16x16x32 result (or the reverse)
 // needs more wait states on gfx950 than the compiler inserts between the two;
@@ -118,16 +119,9 @@ __device__ __forceinline__ bf16x4 pack4(f32x4 x)
 // every accumulation chain uses one shape.
 __device__ __forceinline__ f32x4 mfma16_as32(bf16x4 a, bf16x4 b, f32x4 c)
 {
-    const bf16x4 z = {};
-    bf16x8 a8, b8;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        a8[e] = a[e];
-        b8[e] = b[e];
-        a8[4 + e] = z[e];
-        b8[4 + e] = z[e];
-    }
-    return mfma32(a8, b8, c);
+    const u32x2 aw = __builtin_bit_cast(u32x2, a), bw = __builtin_bit_cast(u32x2, b);
+    return mfma32(__builtin_bit_cast(bf16x8, u32x4{aw[0], aw[1], 0u, 0u}),
+                  __builtin_bit_cast(bf16x8, u32x4{bw[0], bw[1], 0u, 0u}), c);
 }
 __device__ __forceinline__ bf16x8 cat8(bf16x4 lo, bf16x4 hi)
 {
