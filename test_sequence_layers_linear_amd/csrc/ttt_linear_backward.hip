@@ -37,11 +37,18 @@
 // the transpose of itself -- which is how S = Q K^T turns into A^T and dA
 // into dA^T without data movement.
 //
-// Inputs of a chunk (Q, K, V, dY as fp32, and W_c) are staged through a
-// two-slot LDS ring, the next chunk's global loads issued before this chunk's
-// products.  LDS rows are padded to 68 floats so the 16 rows a 16-lane group
-// reads fall in different banks.  Tokens past T read as zero: they add
-// nothing to any product, and their rows are not stored.
+// Inputs of a chunk (Q, K, dY as fp32) are staged through a two-slot LDS
+// ring, the next chunk's global loads issued before this chunk's products;
+// each wave loads the 16 V columns it needs straight into registers, and W_c
+// has one LDS buffer: every wave reads the W rows it needs in phase B before
+// the mid-chunk barrier, so the next W_c is written right after that barrier.
+// That keeps a workgroup at 73 KB of LDS and under 256 VGPRs (two fit on a
+// CU; measured, two per CU run at half the speed each: the chunk is bound by
+// the SIMD's VALU and fp32 MFMA issue, so the segment planner keeps one per
+// CU).  LDS rows are
+// padded to 68 floats so the 16 rows a 16-lane group reads fall in different
+// banks.  Tokens past T read as zero: they add nothing to any product, and
+// their rows are not stored.
 #include "ttt_internal.h"
 
 namespace ttt {
@@ -56,19 +63,19 @@ constexpr int kTile = kB * kP;                  // a 16 x 64 tile
 constexpr int kWTile = kD * kP;                 // a 64 x 64 matrix
 constexpr int kSlotQ = 0;
 constexpr int kSlotK = kTile;
-constexpr int kSlotV = 2 * kTile;
-constexpr int kSlotDY = 3 * kTile;
-constexpr int kSlotW = 4 * kTile;
-constexpr int kSlotFloats = 4 * kTile + kWTile;
-constexpr int kOffE = 2 * kSlotFloats;          // E  [16][kP]
+constexpr int kSlotDY = 2 * kTile;
+constexpr int kSlotFloats = 3 * kTile;          // one chunk's Q, K, dY
+constexpr int kOffW = 2 * kSlotFloats;          // W_c [64][kP], one buffer
+constexpr int kOffE = kOffW + kWTile;           // E  [16][kP]
 constexpr int kOffP = kOffE + kTile;            // P  [16][kP]
 constexpr int kOffG = kOffP + kTile;            // G' [64][kP]
 constexpr int kDAP = 20;                        // padded row of a wave's dA copy
 constexpr int kOffDA = kOffG + kWTile;          // [4 waves][16][kDAP]
 constexpr int kOffRed = kOffDA + kWaves * kB * kDAP;
 constexpr int kLdsFloats = kOffRed + kWaves;
-constexpr int kLdsBytes = kLdsFloats * 4;       // 100880
-static_assert(kLdsBytes <= kMaxLdsBytes, "LDS budget");
+constexpr int kLdsBytes = kLdsFloats * 4;       // 74768
+constexpr int kGMapLdsBytes = 2 * kSlotFloats * 4;   // the cotangent maps use the slots only
+static_assert(2 * kLdsBytes <= kMaxLdsBytes, "two workgroups per CU");
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -102,9 +109,13 @@ template <> struct Raw<uint16_t> {
     }
 };
 
+__device__ __forceinline__ float to_f(float x) { return x; }
+__device__ __forceinline__ float to_f(uint16_t x) { return __uint_as_float(static_cast<uint32_t>(x) << 16); }
+
 template <typename In>
 struct Stage {
-    typename Raw<In>::type q, k, v, dy;
+    typename Raw<In>::type q, k, dy;
+    In v[4];           // V[4g + r][16w + c]: this lane's entries of its wave's columns
     f32x4 w[4];
 };
 
@@ -122,7 +133,7 @@ __device__ __forceinline__ void lds4(float* p, f32x4 x) { *reinterpret_cast<f32x
 //   N^G from G_end = 0 with the segment's dY, half 1), stored in the order
 //   the composition runs: gmaps[u][nseg - 1 - s][half].  No W is needed.
 template <typename In, bool kGMap>
-__global__ void __launch_bounds__(kThreads, 1)
+__global__ void __launch_bounds__(kThreads, 2)
 linear_backward_kernel(const In* __restrict__ Q, const In* __restrict__ K, const In* __restrict__ V,
                        const float* __restrict__ W0, int w0_per_batch,
                        const float* __restrict__ eta, int H, int T, int64_t units, int seg_len,
@@ -170,8 +181,13 @@ linear_backward_kernel(const In* __restrict__ Q, const In* __restrict__ K, const
         const bool ok = t < T;
         const int64_t e = off + static_cast<int64_t>(t) * kD + scol;
         x.k = Raw<In>::load(K + e, ok);
-        if (!kGMap)
-            x.v = Raw<In>::load(V + e, ok);
+        if (!kGMap) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int tv = chunk * kB + 4 * g + r;
+                x.v[r] = tv < T ? V[off + static_cast<int64_t>(tv) * kD + 16 * w + c] : In(0);
+            }
+        }
         if (qdy) {
             x.q = Raw<In>::load(Q + e, ok);
             x.dy = Raw<In>::load(dY + e, ok);
@@ -183,29 +199,28 @@ linear_backward_kernel(const In* __restrict__ Q, const In* __restrict__ K, const
                 x.w[q] = *reinterpret_cast<const f32x4*>(src + (srow + 16 * q) * kD + scol);
         }
     };
-    auto store_stage = [&](const Stage<In>& x, int slot, bool qdy, bool wst) {
+    auto store_stage = [&](const Stage<In>& x, int slot, bool qdy) {
         float* sl = lds + slot * kSlotFloats;
         lds4(sl + kSlotK + srow * kP + scol, Raw<In>::to_f32(x.k));
-        if (!kGMap)
-            lds4(sl + kSlotV + srow * kP + scol, Raw<In>::to_f32(x.v));
         if (qdy) {
             lds4(sl + kSlotQ + srow * kP + scol, Raw<In>::to_f32(x.q));
             lds4(sl + kSlotDY + srow * kP + scol, Raw<In>::to_f32(x.dy));
         }
-        if (wst) {
+    };
+    auto store_w = [&](const Stage<In>& x) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                lds4(sl + kSlotW + (srow + 16 * q) * kP + scol, x.w[q]);
-        }
+        for (int q = 0; q < 4; ++q)
+            lds4(lds + kOffW + (srow + 16 * q) * kP + scol, x.w[q]);
     };
 
     // E_J = K W[:, J] - V[:, J] for this wave's columns J = w, from the
-    // staged K, V of a slot and the W tiles Wt[i] (rows 16 i + 4g + r)
-    auto residual = [&](const float* sl, const float (&Wt)[4][4], f32x4 (&krow)[4]) {
+    // staged K of a slot, this lane's V entries and the W tiles Wt[i] (rows
+    // 16 i + 4g + r)
+    auto residual = [&](const float* sl, const float (&Wt)[4][4], const In (&vr)[4], f32x4 (&krow)[4]) {
         f32x4 acc[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-            acc[0][r] = -sl[kSlotV + (4 * g + r) * kP + 16 * w + c];
+            acc[0][r] = -to_f(vr[r]);
         acc[1] = acc[2] = acc[3] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -230,7 +245,11 @@ linear_backward_kernel(const In* __restrict__ Q, const In* __restrict__ K, const
                 Wt[i][r] = w0[(16 * i + 4 * g + r) * kD + 16 * w + c];
         Stage<In> nx;
         load_stage(nx, c0, false, false);
-        store_stage(nx, 0, false, false);
+        store_stage(nx, 0, false);
+        In vcur[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            vcur[r] = nx.v[r];
         __syncthreads();
         for (int ch = c0; ch < c1; ++ch) {
             float* sc = st + static_cast<int64_t>(ch - c0) * kD * kD;
@@ -244,7 +263,7 @@ linear_backward_kernel(const In* __restrict__ Q, const In* __restrict__ K, const
             load_stage(nx, ch + 1, false, false);
             const float* sl = lds + ((ch - c0) & 1) * kSlotFloats;
             f32x4 krow[4];
-            const f32x4 E = residual(sl, Wt, krow);
+            const f32x4 E = residual(sl, Wt, vcur, krow);
             const f32x4 En = -et * E;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -256,7 +275,10 @@ linear_backward_kernel(const In* __restrict__ Q, const In* __restrict__ K, const
                 for (int r = 0; r < 4; ++r)
                     Wt[i][r] = acc[r];
             }
-            store_stage(nx, (ch - c0 + 1) & 1, false, false);
+            store_stage(nx, (ch - c0 + 1) & 1, false);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                vcur[r] = nx.v[r];
             __syncthreads();
         }
         // the states just stored are read back below by other threads
@@ -287,10 +309,17 @@ linear_backward_kernel(const In* __restrict__ Q, const In* __restrict__ K, const
     float* Gs = lds + kOffG;
     float* dAs = lds + kOffDA + w * kB * kDAP;
 
+    In vcur[4] = {};
     if (c1 > c0) {
         Stage<In> nx;
         load_stage(nx, c1 - 1, use_dy, !kGMap);
-        store_stage(nx, 0, use_dy, !kGMap);
+        store_stage(nx, 0, use_dy);
+        if (!kGMap) {
+            store_w(nx);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                vcur[r] = nx.v[r];
+        }
         __syncthreads();
     }
     for (int ch = c1 - 1; ch >= c0; --ch) {
@@ -303,13 +332,17 @@ linear_backward_kernel(const In* __restrict__ Q, const In* __restrict__ K, const
         // ---- phase A: columns J = w ----
         f32x4 krow[4];
         f32x4 E = {0.f, 0.f, 0.f, 0.f};
+        f32x4 wrow[4];       // W[16 w + c][16 jb + 4g .. +3] for phase B
         if (!kGMap) {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    Wt[i][r] = sl[kSlotW + (16 * i + 4 * g + r) * kP + 16 * w + c];
-            E = residual(sl, Wt, krow);
+                    Wt[i][r] = lds[kOffW + (16 * i + 4 * g + r) * kP + 16 * w + c];
+#pragma unroll
+            for (int jb = 0; jb < 4; ++jb)
+                wrow[jb] = lds4(lds + kOffW + (16 * w + c) * kP + 16 * jb + 4 * g);
+            E = residual(sl, Wt, vcur, krow);
         } else {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
@@ -380,6 +413,9 @@ linear_backward_kernel(const In* __restrict__ Q, const In* __restrict__ K, const
 
         if (!kGMap) {
             __syncthreads();
+            // every wave has read W_c: the next chunk's W_c may replace it
+            if (ch > c0)
+                store_w(nx);
             // ---- phase B: input dims I = w ----
             // dA = -eta tril(dY E^T): lane holds dA[t = 4g + r][s = c]
             f32x4 dyrow[4], erow[4];
@@ -403,10 +439,6 @@ linear_backward_kernel(const In* __restrict__ Q, const In* __restrict__ K, const
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             // dQ_I = dY W[I, :]^T + dA K_I
-            f32x4 wrow[4];
-#pragma unroll
-            for (int jb = 0; jb < 4; ++jb)
-                wrow[jb] = lds4(sl + kSlotW + (16 * w + c) * kP + 16 * jb + 4 * g);
             f32x4 qacc[4] = {};
 #pragma unroll
             for (int r = 0; r < 4; ++r)
@@ -450,8 +482,14 @@ linear_backward_kernel(const In* __restrict__ Q, const In* __restrict__ K, const
                 }
             }
         }
-        if (ch > c0)
-            store_stage(nx, slot ^ 1, use_dy, !kGMap);
+        if (ch > c0) {
+            store_stage(nx, slot ^ 1, use_dy);
+            if (!kGMap) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    vcur[r] = nx.v[r];
+            }
+        }
         __syncthreads();
     }
 
@@ -555,7 +593,8 @@ BwdWorkspace carve(const LinearBwdArgs& a, const SegmentPlan& p, void* base)
 template <typename In, bool kGMap>
 void launch_kernel(const LinearBwdArgs& a, const SegmentPlan& p, const BwdWorkspace& w, dim3 grid)
 {
-    hipLaunchKernelGGL((linear_backward_kernel<In, kGMap>), grid, dim3(kThreads), kLdsBytes, a.stream,
+    hipLaunchKernelGGL((linear_backward_kernel<In, kGMap>), grid, dim3(kThreads),
+                       kGMap ? kGMapLdsBytes : kLdsBytes, a.stream,
                        static_cast<const In*>(a.Q), static_cast<const In*>(a.K),
                        static_cast<const In*>(a.V), a.W0, a.w0_per_batch, a.eta,
                        static_cast<int>(a.H), static_cast<int>(a.T), a.B * a.H,
