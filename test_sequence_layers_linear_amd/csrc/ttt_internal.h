@@ -174,8 +174,8 @@ bool linear_mfma_supports(const LinearArgs& a);
 hipError_t launch_linear_mfma(const LinearArgs& a, const SegmentPlan& p);
 bool linear_mfma_f32_supports(const LinearArgs& a);
 hipError_t launch_linear_mfma_f32(const LinearArgs& a, const SegmentPlan& p);
-constexpr SegmentCosts kLinearBf16Costs{0.35, 0.43, 0.90, 11.0, 1};
-constexpr SegmentCosts kLinearF32Costs{1.90, 1.20, 0.90, 11.0, 2};
+constexpr SegmentCosts kLinearBf16Costs{0.35, 0.43, 0.60, 8.5, 1};
+constexpr SegmentCosts kLinearF32Costs{1.38, 0.90, 0.60, 8.5, 2};
 bool mlp_mfma_supports(const MlpArgs& a);
 hipError_t launch_mlp_mfma(const MlpArgs& a);
 
@@ -201,8 +201,8 @@ struct BwdCosts {
     double bwd, fmap, gmap, apply, launch;
     int fmap_blocks_per_segment;
 };
-constexpr BwdCosts kLinearBwdF32Costs{5.2, 1.2, 1.5, 0.9, 20.0, 2};
-constexpr BwdCosts kLinearBwdBf16Costs{5.2, 0.43, 1.5, 0.9, 20.0, 1};
+constexpr BwdCosts kLinearBwdF32Costs{5.2, 0.9, 1.5, 0.6, 20.0, 2};
+constexpr BwdCosts kLinearBwdBf16Costs{5.2, 0.43, 1.5, 0.6, 20.0, 1};
 size_t linear_backward_workspace_bytes(const LinearBwdArgs& a, const SegmentPlan& p);
 hipError_t launch_linear_backward(const LinearBwdArgs& a, const SegmentPlan& p, void* workspace);
 

@@ -37,8 +37,8 @@ constexpr int kDepth = 6;                // steps of operands in flight
 
 }  // namespace
 
-// LDS of one combine workgroup for a chain of nseg segments (the loop runs
-// whole rounds of kDepth steps; the extra steps write spare slots)
+// LDS of one combine workgroup for a chain of nseg segments (kDepth spare
+// slots beyond the nseg start states)
 size_t linear_combine_lds_bytes(int nseg)
 {
     return static_cast<size_t>(nseg + kDepth) * kSliceFloats * 4;
@@ -112,28 +112,40 @@ linear_combine_kernel(const float* W0, int w0_per_batch, int H, int64_t units,
         load_ops(a[q], n[q], q);             // nseg >= 2 whenever this kernel runs
     __syncthreads();
 
-    for (int j0 = 0; j0 + 1 < nseg; j0 += kDepth) {
+    // step j with the operands of ring entry q: W_{j+1} slice into LDS, then
+    // the ring entry reloaded for step j + kDepth
+    auto step = [&](int q, int j) {
+        const float* Wc = Wl + j * kSliceFloats;
+        float b[16];
 #pragma unroll
-        for (int q = 0; q < kDepth; ++q) {
-            const int j = j0 + q;
-            const float* Wc = Wl + j * kSliceFloats;
-            float b[16];
+        for (int s = 0; s < 16; ++s)
+            b[s] = Wc[(16 * g + s) * kPad + c];
+        f32x4 acc[4] = {n[q], {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-            for (int s = 0; s < 16; ++s)
-                b[s] = Wc[(16 * g + s) * kPad + c];
-            f32x4 acc[4] = {n[q], {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        for (int s = 0; s < 16; ++s)
+            acc[s & 3] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[q][s >> 2][s & 3], b[s], acc[s & 3],
+                                                              0, 0, 0);
+        const f32x4 res = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+        float* Wn = Wl + (j + 1) * kSliceFloats;
 #pragma unroll
-            for (int s = 0; s < 16; ++s)
-                acc[s & 3] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[q][s >> 2][s & 3], b[s], acc[s & 3],
-                                                                  0, 0, 0);
-            const f32x4 res = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-            float* Wn = Wl + (j + 1) * kSliceFloats;
+        for (int r = 0; r < 4; ++r)
+            Wn[(16 * I + 4 * g + r) * kPad + c] = res[r];
+        load_ops(a[q], n[q], j + kDepth);
+        __syncthreads();
+    };
+    // full rounds of kDepth steps, then the last partial round with an exit
+    // (kept out of the full rounds, whose schedule it would disturb)
+    int j0 = 0;
+    for (; j0 + kDepth + 1 <= nseg; j0 += kDepth) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                Wn[(16 * I + 4 * g + r) * kPad + c] = res[r];
-            load_ops(a[q], n[q], j + kDepth);
-            __syncthreads();
-        }
+        for (int q = 0; q < kDepth; ++q)
+            step(q, j0 + q);
+    }
+#pragma unroll
+    for (int q = 0; q < kDepth; ++q) {
+        if (j0 + q + 1 >= nseg)          // uniform: every start state is done
+            break;
+        step(q, j0 + q);
     }
 
     for (int j = 0; j < nseg; ++j) {
