@@ -238,6 +238,21 @@ int ttt_linear_backward(const void* Q, const void* K, const void* V, int qkv_dty
  * ttt_status for arguments ttt_linear_backward would reject.
  */
 int ttt_linear_backward_segments(int64_t B, int64_t H, int64_t T, int d, int b, int qkv_dtype);
+/*
+ * ttt_linear_decode_step with the input prologue of ttt_linear_forward_ex,
+ * for one token: q and k LayerNorm'd over the head dim (ln_q, ln_k [H][2][d],
+ * NULL for none; ln_eps > 0 when used), the token's own step size eta_tok
+ * [B][H] (NULL: the head's eta), and read_mode 1 reading out before the
+ * update (y = q W, the one-token case of the chunk-start read).  So a
+ * sequence prefilled with ttt_linear_forward_ex continues token by token with
+ * the same rules.  Any d of ttt_linear_decode_step; computed in fp32 (the
+ * normalised rows are not rounded to bf16).  Errors as for
+ * ttt_linear_decode_step; eta_tok, ln_q, ln_k must not overlap y or W.
+ */
+int ttt_linear_decode_step_ex(const void* q, const void* k, const void* v, int qkv_dtype,
+                              float* W, const float* eta, const float* eta_tok,
+                              const float* ln_q, const float* ln_k, float ln_eps, int read_mode,
+                              int64_t B, int64_t H, int d, void* y, void* stream);
 /* Static, human-readable text for a status code (never NULL). */
 /*
  * Number of sequence segments ttt_linear_forward would cut each chain into

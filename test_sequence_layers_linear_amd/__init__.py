@@ -60,6 +60,9 @@ def load_library():
     lib.ttt_mlp_forward.restype = I
     lib.ttt_linear_decode_step.argtypes = [P, P, P, I, P, P, L, L, I, P, P]
     lib.ttt_linear_decode_step.restype = I
+    lib.ttt_linear_decode_step_ex.argtypes = [P, P, P, I, P, P, P, P, P, ctypes.c_float, I,
+                                              L, L, I, P, P]
+    lib.ttt_linear_decode_step_ex.restype = I
     lib.ttt_linear_backward.argtypes = [P, P, P, I, P, I, P, L, L, L, I, I, P, P,
                                         P, P, P, P, P, P]
     lib.ttt_linear_backward.restype = I
@@ -292,6 +295,44 @@ def ttt_linear_backward(Q, K, V, W0, eta, b: int, dY, dW_out=None, dQ=None, dK=N
     return dQ, dK, dV, dW0, deta
 
 
+def ttt_linear_decode_step_ex(q, k, v, W, eta, eta_tok=None, ln_q=None, ln_k=None,
+                              ln_eps: float = 1e-5, read_chunk_start: bool = False, y=None,
+                              stream=None):
+    """ttt_linear_decode_step with the input prologue of ttt_linear_forward_ex
+    (eta_tok fp32 [B,H]; ln_q / ln_k fp32 [H,2,d]); W updated in place."""
+    lib = load_library()
+    if q.dim() != 3:
+        raise ValueError("q must be [B,H,d]")
+    dev = q.device
+    B, H, d = q.shape
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, dev, q.dtype)
+        if t.shape != q.shape:
+            raise ValueError(f"{n} shape {tuple(t.shape)} != q shape {tuple(q.shape)}")
+    _need(W, "W", dev, torch.float32)
+    _need(eta, "eta", dev, torch.float32)
+    if W.shape != (B, H, d, d) or eta.shape != (H,):
+        raise ValueError("W must be [B,H,d,d] and eta [H]")
+    ptrs = []
+    for t, n, shape in ((eta_tok, "eta_tok", (B, H)), (ln_q, "ln_q", (H, 2, d)),
+                        (ln_k, "ln_k", (H, 2, d))):
+        if t is None:
+            ptrs.append(None)
+            continue
+        _need(t, n, dev, torch.float32)
+        if t.shape != shape:
+            raise ValueError(f"{n} must be {list(shape)}, got {tuple(t.shape)}")
+        ptrs.append(t.data_ptr())
+    if y is None:
+        y = torch.empty_like(q)
+    _need(y, "y", dev, q.dtype)
+    _check(lib.ttt_linear_decode_step_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), _dtype_code(q),
+                                         W.data_ptr(), eta.data_ptr(), ptrs[0], ptrs[1], ptrs[2],
+                                         float(ln_eps), int(bool(read_chunk_start)), B, H, d,
+                                         y.data_ptr(), _stream_handle(dev, stream)))
+    return y
+
+
 def ttt_linear_segments(B: int, H: int, T: int, d: int, b: int, dtype=torch.bfloat16) -> int:
     """Sequence segments ttt_linear_forward cuts each chain into for these
     sizes on the current device (1 = unsegmented)."""
@@ -312,7 +353,8 @@ def ttt_linear_backward_segments(B: int, H: int, T: int, d: int, b: int,
 
 
 __all__ = [
-    "ttt_linear_forward", "ttt_linear_forward_ex", "ttt_mlp_forward", "ttt_linear_decode_step", "ttt_linear_backward",
+    "ttt_linear_forward", "ttt_linear_forward_ex", "ttt_mlp_forward", "ttt_linear_decode_step",
+    "ttt_linear_decode_step_ex", "ttt_linear_backward",
     "ttt_linear_segments", "ttt_linear_backward_segments",
     "load_library",
     "status_string", "TTTError", "LIB_PATH", "TTT_F32", "TTT_BF16",

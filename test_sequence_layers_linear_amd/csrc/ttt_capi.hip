@@ -440,9 +440,13 @@ int ttt_mlp_forward(const void* Q, const void* K, const void* V, int qkv_dtype,
     return hip_status(ttt::launch_mlp_generic(a));
 }
 
-int ttt_linear_decode_step(const void* q, const void* k, const void* v, int qkv_dtype,
-                           float* W, const float* eta, int64_t B, int64_t H, int d,
-                           void* y, void* stream)
+}  // extern "C"
+
+namespace {
+
+int decode_impl(const void* q, const void* k, const void* v, int qkv_dtype, float* W,
+                const float* eta, int64_t B, int64_t H, int d, void* y, void* stream,
+                const ttt::Prologue& pro)
 {
     if (B < 0 || H < 0) return TTT_ERR_INVALID_ARG;
     if (!valid_dtype(qkv_dtype) || !d_supported(d)) return TTT_ERR_UNSUPPORTED;
@@ -457,8 +461,44 @@ int ttt_linear_decode_step(const void* q, const void* k, const void* v, int qkv_
         if (overlap(ry, in)) return TTT_ERR_INVALID_ARG;
     for (const Range& in : {rq, rk, rv, rEta})
         if (overlap(rW, in)) return TTT_ERR_INVALID_ARG;
+    if (pro.active()) {
+        const Range rTok{pro.eta_tok, pro.eta_tok ? units * 4 : 0};
+        const Range rLq{pro.ln_q, pro.ln_q ? H * 2 * d * 4 : 0}, rLk{pro.ln_k, pro.ln_k ? H * 2 * d * 4 : 0};
+        for (const Range& in : {rTok, rLq, rLk})
+            if (overlap(ry, in) || overlap(rW, in)) return TTT_ERR_INVALID_ARG;
+    }
     DecodeArgs a{q, k, v, qkv_dtype, W, eta, B, H, d, y, static_cast<hipStream_t>(stream)};
+    a.pro = pro;
     return hip_status(ttt::launch_decode(a));
+}
+
+}  // namespace
+
+extern "C" {
+
+int ttt_linear_decode_step(const void* q, const void* k, const void* v, int qkv_dtype,
+                           float* W, const float* eta, int64_t B, int64_t H, int d,
+                           void* y, void* stream)
+{
+    return decode_impl(q, k, v, qkv_dtype, W, eta, B, H, d, y, stream, ttt::Prologue{});
+}
+
+int ttt_linear_decode_step_ex(const void* q, const void* k, const void* v, int qkv_dtype,
+                              float* W, const float* eta, const float* eta_tok,
+                              const float* ln_q, const float* ln_k, float ln_eps, int read_mode,
+                              int64_t B, int64_t H, int d, void* y, void* stream)
+{
+    if ((ln_q || ln_k) && !(ln_eps > 0.0f && ln_eps < 1e30f))
+        return TTT_ERR_INVALID_ARG;
+    if (read_mode != 0 && read_mode != 1)
+        return TTT_ERR_INVALID_ARG;
+    ttt::Prologue pro;
+    pro.eta_tok = eta_tok;
+    pro.ln_q = ln_q;
+    pro.ln_k = ln_k;
+    pro.ln_eps = ln_eps;
+    pro.read_start = read_mode;
+    return decode_impl(q, k, v, qkv_dtype, W, eta, B, H, d, y, stream, pro);
 }
 
 }  // extern "C"

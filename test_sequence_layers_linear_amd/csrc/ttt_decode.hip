@@ -14,6 +14,11 @@
 //
 // y_j uses q W'_j = q W_j - eta (q . k) r_j, algebraically the readout with
 // the updated column, so W is read once and written once.
+//
+// kPro: the input prologue of ttt_linear_forward_ex for one token: q and k
+// LayerNorm'd over the head dim (waves 0 and 1, one row each, butterfly sums
+// over the wave), the token's own step size, and with read_start the readout
+// before the update (y = q W), the b = 1 case of the chunk-start read.
 #include "ttt_internal.h"
 
 namespace ttt {
@@ -22,11 +27,36 @@ namespace {
 constexpr int kCols = 16;
 constexpr int kRowGroups = 16;
 
-template <typename TIn>
+// LayerNorm of the d <= 128 values in buf (LDS) by one whole wave: lane l
+// holds elements l and l + 64
+__device__ void layernorm_wave(float* buf, int d, const float* __restrict__ prm, int h, float eps)
+{
+    const int l = threadIdx.x & 63;
+    const float x0 = l < d ? buf[l] : 0.f;
+    const float x1 = l + 64 < d ? buf[l + 64] : 0.f;
+    float sum = x0 + x1;
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1)
+        sum += __shfl_xor(sum, m);
+    const float mean = sum / static_cast<float>(d);
+    const float d0 = l < d ? x0 - mean : 0.f;
+    const float d1 = l + 64 < d ? x1 - mean : 0.f;
+    float sq = d0 * d0 + d1 * d1;
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1)
+        sq += __shfl_xor(sq, m);
+    const float rstd = rsqrtf(sq / static_cast<float>(d) + eps);
+    if (l < d)
+        buf[l] = d0 * rstd * prm[(2 * h) * d + l] + prm[(2 * h + 1) * d + l];
+    if (l + 64 < d)
+        buf[l + 64] = d1 * rstd * prm[(2 * h) * d + l + 64] + prm[(2 * h + 1) * d + l + 64];
+}
+
+template <typename TIn, bool kPro>
 __global__ void __launch_bounds__(kCols * kRowGroups)
 decode_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
               const TIn* __restrict__ v, float* __restrict__ W,
-              const float* __restrict__ eta, int H, int d, TIn* __restrict__ y)
+              const float* __restrict__ eta, int H, int d, TIn* __restrict__ y, Prologue pro)
 {
     __shared__ float ks[128], qs[128];
     __shared__ float red_k[kRowGroups][kCols + 1], red_q[kRowGroups][kCols + 1];
@@ -43,6 +73,16 @@ decode_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
         qs[x] = load_elem(q, u * d + x);
     }
     __syncthreads();
+    if constexpr (kPro) {
+        if (pro.ln_k || pro.ln_q) {
+            const int wv = threadIdx.x >> 6;          // wave-uniform roles
+            if (wv == 0 && pro.ln_k)
+                layernorm_wave(ks, d, pro.ln_k, h, pro.ln_eps);
+            if (wv == 1 && pro.ln_q)
+                layernorm_wave(qs, d, pro.ln_q, h, pro.ln_eps);
+            __syncthreads();
+        }
+    }
 
     float* Wu = W + u * d * d;
     const int rows = d / kRowGroups;  // 1, 2, 4 or 8
@@ -66,7 +106,7 @@ decode_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
         qk_s = acc;
     }
     __syncthreads();
-    const float et = eta[h];
+    const float et = (kPro && pro.eta_tok) ? pro.eta_tok[u] : eta[h];
     if (ig == 0) {
         float kw = 0.f, qw = 0.f;
         for (int g = 0; g < kRowGroups; ++g) {
@@ -75,7 +115,7 @@ decode_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
         }
         const float r = kw - load_elem(v, u * d + j);
         rcol[jl] = r;
-        store_elem(y, u * d + j, qw - et * qk_s * r);
+        store_elem(y, u * d + j, (kPro && pro.read_start) ? qw : qw - et * qk_s * r);
     }
     __syncthreads();
     const float r = rcol[jl];
@@ -88,23 +128,29 @@ decode_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
     }
 }
 
-}  // namespace
-
-hipError_t launch_decode(const DecodeArgs& a)
+template <bool kPro>
+hipError_t launch(const DecodeArgs& a)
 {
     const dim3 grid(static_cast<unsigned>(a.B * a.H), static_cast<unsigned>(a.d / kCols));
     const dim3 block(kCols * kRowGroups);
     if (a.dtype == 0)
-        hipLaunchKernelGGL(decode_kernel<float>, grid, block, 0, a.stream,
+        hipLaunchKernelGGL((decode_kernel<float, kPro>), grid, block, 0, a.stream,
                            static_cast<const float*>(a.q), static_cast<const float*>(a.k),
                            static_cast<const float*>(a.v), a.W, a.eta, static_cast<int>(a.H),
-                           a.d, static_cast<float*>(a.y));
+                           a.d, static_cast<float*>(a.y), a.pro);
     else
-        hipLaunchKernelGGL(decode_kernel<uint16_t>, grid, block, 0, a.stream,
+        hipLaunchKernelGGL((decode_kernel<uint16_t, kPro>), grid, block, 0, a.stream,
                            static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                            static_cast<const uint16_t*>(a.v), a.W, a.eta, static_cast<int>(a.H),
-                           a.d, static_cast<uint16_t*>(a.y));
+                           a.d, static_cast<uint16_t*>(a.y), a.pro);
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeArgs& a)
+{
+    return a.pro.active() ? launch<true>(a) : launch<false>(a);
 }
 
 }  // namespace ttt

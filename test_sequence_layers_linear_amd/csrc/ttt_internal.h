@@ -112,6 +112,7 @@ struct DecodeArgs {
     const void* q; const void* k; const void* v; int dtype;
     float* W; const float* eta; int64_t B, H; int d;
     void* y; hipStream_t stream;
+    Prologue pro{};                   // eta_tok is [B][H] here (one token)
 };
 
 // Generic kernels: any supported d and b, fp32 arithmetic, state in LDS

@@ -38,7 +38,8 @@ def test_exports_every_declared_function(lib):
     names = declared_functions()
     assert set(names) >= {"ttt_linear_forward", "ttt_mlp_forward", "ttt_linear_decode_step",
                           "ttt_linear_backward", "ttt_linear_forward_ex", "ttt_linear_segments",
-                          "ttt_linear_backward_segments", "ttt_status_string",
+                          "ttt_linear_backward_segments", "ttt_linear_decode_step_ex",
+                          "ttt_status_string",
                           "ttt_abi_version"}
     for n in names:
         assert hasattr(lib, n), f"{n} declared in ttt.h but not exported"
@@ -157,6 +158,20 @@ def bwd(lib, Q=QA, dt=1, W0=W0A, pb=0, eta=ETA, B=2, H=3, T=64, d=64, b=16, dY=D
 ])
 def test_backward_validation(lib, kw, expect):
     assert bwd(lib, **kw) == expect
+
+
+def decx(lib, tok=TOKA, lnq=LNQA, lnk=LNKA, eps=1e-5, rm=0, d=64, y=YA, W=W0A, B=2):
+    return lib.ttt_linear_decode_step_ex(QA, KA, VA, 1, W, ETA, tok, lnq, lnk, eps, rm, B, 24, d,
+                                         y, None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(eps=0.0), INVALID), (dict(rm=3), INVALID), (dict(d=96), UNSUPPORTED),
+    (dict(y=TOKA), INVALID), (dict(W=LNQA), INVALID), (dict(y=LNKA + 100), INVALID),
+    (dict(B=0), OK), (dict(lnq=None, lnk=None, eps=-1.0, B=0), OK),
+])
+def test_decode_ex_validation(lib, kw, expect):
+    assert decx(lib, **kw) == expect
 
 
 def test_binding_rejects_cpu_tensors():

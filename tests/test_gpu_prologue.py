@@ -116,3 +116,39 @@ def test_chunk_start_read(dtype, T, S, parts, monkeypatch):
     ey, ew = rel_l2(Y, Yr), rel_l2(W, Wr)
     print(f"  rel-L2 Y {ey:.3e}  W {ew:.3e}", flush=True)
     assert ey <= TOL[dtype] and ew <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("d", [16, 64, 128])
+@pytest.mark.parametrize("parts,read_start", [(("ln_q", "ln_k", "eta_tok"), False),
+                                              (("ln_k",), True), ((), True)])
+def test_decode_step_ex(dtype, d, parts, read_start):
+    """Three prologue decode steps from a random state against the oracle's
+    one-token forward (b = 1) with per-batch W0 = the state."""
+    w = CONFIGS[3].with_(B=2, H=3, T=3, d=d, dtype=dtype)
+    seed = 9500 + d + len(parts) + int(read_start)
+    announce("decode_ex", dtype, d, parts, read_start, seed)
+    inp = make_inputs(w, seed, w0_per_batch=True)
+    pro = make_prologue(w, seed + 3)
+    inp["eta"] = pro["eta"]
+    W = inp["W0"].clone().cuda()
+    Wref = inp["W0"]
+    for t in range(3):
+        kw = {k: pro[k] for k in parts if k != "eta_tok"}
+        if "eta_tok" in parts:
+            kw["eta_tok"] = pro["eta_tok"][:, :, t].contiguous()
+        y = ttt.ttt_linear_decode_step_ex(inp["Q"][:, :, t].contiguous().cuda(),
+                                          inp["K"][:, :, t].contiguous().cuda(),
+                                          inp["V"][:, :, t].contiguous().cuda(), W,
+                                          inp["eta"].cuda(), read_chunk_start=read_start,
+                                          **to_gpu(kw))
+        torch.cuda.synchronize()
+        okw = {k: pro[k] for k in parts if k != "eta_tok"}
+        if "eta_tok" in parts:
+            okw["eta_tok"] = pro["eta_tok"][:, :, t:t + 1]
+        yr, Wref = oracle.linear_forward_ex(inp["Q"][:, :, t:t + 1], inp["K"][:, :, t:t + 1],
+                                            inp["V"][:, :, t:t + 1], Wref, inp["eta"], 1,
+                                            read_chunk_start=read_start, **okw)
+        ey, ew = rel_l2(y, yr[:, :, 0]), rel_l2(W, Wref)
+        print(f"  step {t} rel-L2 y {ey:.3e}  W {ew:.3e}", flush=True)
+        assert ey <= TOL[dtype] and ew <= TOL[dtype]
