@@ -109,8 +109,10 @@ ttt::SegmentPlan plan_segments(int64_t units, int64_t T, int chunk, const ttt::S
 
 // Segment count for the backward of a TTT-Linear scan: each segment pays
 // its chunks' forward map, cotangent map and backward, and the two
-// compositions (S - 1) steps each, plus four extra launches; every launch
-// fits one workgroup per CU.  TTT_LINEAR_BWD_SEGMENTS=S forces S segments.
+// compositions (S - 1) steps each, plus four extra launches.  The segment
+// backward runs one workgroup per CU (two per CU run at half the speed each);
+// the maps launches may put two on a CU (the cotangent maps use 26 KB of LDS
+// and half the registers).  TTT_LINEAR_BWD_SEGMENTS=S forces S segments.
 ttt::SegmentPlan plan_backward(int64_t units, int64_t T, int chunk, const ttt::BwdCosts& cost)
 {
     ttt::SegmentPlan p;
@@ -130,7 +132,7 @@ ttt::SegmentPlan plan_backward(int64_t units, int64_t T, int chunk, const ttt::B
     double best = static_cast<double>(chunks) * cost.bwd;
     int best_s = 1;
     for (int S = 2; S <= ttt::kMaxSegments; ++S) {
-        if (units * S > cus || units * (S - 1) * map_blocks > cus) break;
+        if (units * S > cus || units * (S - 1) * map_blocks > 2 * cus) break;
         const int64_t per = (chunks + S - 1) / S;
         if (per < 2) break;
         const double t = per * (cost.bwd + cost.fmap + cost.gmap) + 2.0 * (S - 1) * cost.apply + cost.launch;
