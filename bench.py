@@ -24,8 +24,8 @@ this host's cores on a bounded sample of the same workload.
 
 Each TTT-Linear workload also reports "backward": ttt_linear_backward (the
 gradients of Q, K, V, W0 and eta for seeded cotangents dY, dW_out) timed the
-same way, with its own roofline (fp32 MFMA: the kernel computes in fp32 for
-both input dtypes).  It is reported beside the forward, not folded into the
+same way, with its own roofline (the MFMA peak of the input dtype: bf16
+inputs run on bf16 MFMA, fp32 inputs on fp32 MFMA).  It is reported beside the forward, not folded into the
 headline value.  "prologue" times ttt_linear_forward_ex on the same inputs
 with LayerNorm of q and k and a step size per token fused into the scan.
 """
@@ -55,6 +55,8 @@ KERNEL_SOURCES = {
     "linear_backward_reduce_kernel": "ttt_linear_backward.hip",
     "linear_backward_kernel[gmaps]": "ttt_linear_backward.hip",
     "linear_backward_kernel[segments]": "ttt_linear_backward.hip",
+    "linear_backward_bf16_kernel[gmaps]": "ttt_linear_backward_bf16.hip",
+    "linear_backward_bf16_kernel[segments]": "ttt_linear_backward_bf16.hip",
     "linear_generic_kernel": "ttt_generic.hip",
     "mlp_generic_kernel": "ttt_generic.hip",
     "mlp_mfma_kernel": "ttt_mlp_mfma.hip",
@@ -125,10 +127,11 @@ def backward_kernel_names(w):
     import test_sequence_layers_linear_amd as ttt
     n = ttt.ttt_linear_backward_segments(w.B, w.H, w.T, w.d, w.b,
                                          torch.float32 if w.dtype == "fp32" else torch.bfloat16)
-    k = ["linear_backward_kernel[segments]", "linear_backward_reduce_kernel"]
+    b = "linear_backward_bf16_kernel" if w.dtype == "bf16" else "linear_backward_kernel"
+    k = [b + "[segments]", "linear_backward_reduce_kernel"]
     if n > 1:
         f = "linear_mfma_kernel[maps]" if w.dtype == "bf16" else "linear_mfma_f32_kernel[maps]"
-        k = [f, "linear_combine_kernel", "linear_backward_kernel[gmaps]", "linear_combine_kernel"] + k
+        k = [f, "linear_combine_kernel", b + "[gmaps]", "linear_combine_kernel"] + k
     return k
 
 
@@ -407,9 +410,8 @@ def measure_workload(cfg, steps, warmup, cold_reps):
     if w.kind == "linear" and w.d == 64 and w.b == 16:
         bt = r.measure_backward(max(3, steps // 2), 2)
         bf, bb = linear_backward_work(w)
-        wf = w.with_(dtype="fp32")       # the kernel's arithmetic: fp32 MFMA
         kern = backward_kernel_names(w)
-        rf = roofline(wf, bf, bb, bt, kern)
+        rf = roofline(w, bf, bb, bt, kern)   # bf16 inputs run on bf16 MFMA, fp32 on fp32
         rf["traffic"] = stored_traffic(kern, w.name + "/backward")
         out["backward"] = {"us": bt * 1e6, "tokens_per_s": w.B * w.T / bt, "roofline": rf}
         pt = r.measure_prologue(max(3, steps // 2), 2)

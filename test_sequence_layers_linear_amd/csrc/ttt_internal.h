@@ -193,6 +193,16 @@ struct LinearBwdArgs {
     const void* dY; const float* dW_out;
     void* dQ; void* dK; void* dV; float* dW0; float* deta; hipStream_t stream;
 };
+// Device buffers of one backward call (carved from the stream's workspace;
+// the segment maps and states only with several segments).
+struct BwdBuffers {
+    float *maps, *wstart, *gmaps, *gend, *states, *dw_chain, *deta_chain;
+    size_t bytes;
+};
+// bf16 inputs on bf16 MFMA (ttt_linear_backward_bf16.hip): the cotangent maps
+// (gmap) or the segment backward, on the given grid.
+hipError_t launch_linear_backward_bf16(const LinearBwdArgs& a, const SegmentPlan& p, bool gmap,
+                                       const BwdBuffers& b, dim3 grid);
 bool linear_backward_supports(const LinearBwdArgs& a);
 // Latencies (us) that size the backward's segment split: backward chunk,
 // forward map chunk, cotangent map chunk, one composition step, the fixed

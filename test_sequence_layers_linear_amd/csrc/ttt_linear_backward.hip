@@ -548,10 +548,7 @@ linear_backward_reduce_kernel(const float* __restrict__ dW0_chain, const float* 
 // workspace carve-up (floats): forward maps, start states, cotangent maps,
 // end cotangents (only with segments), chunk-start states, per-chain dW0
 // (shared W0 only), per-segment deta
-struct BwdWorkspace {
-    float *maps, *wstart, *gmaps, *gend, *states, *dw_chain, *deta_chain;
-    size_t bytes;
-};
+using BwdWorkspace = BwdBuffers;
 
 // One segment covers every chunk: seg_len = T rounded up to whole chunks.
 SegmentPlan normalized(const LinearBwdArgs& a, SegmentPlan p)
@@ -634,7 +631,7 @@ hipError_t launch_linear_backward(const LinearBwdArgs& a, const SegmentPlan& pla
     const SegmentPlan p = normalized(a, plan);
     const BwdWorkspace w = carve(a, p, workspace);
     const bool bf16 = a.dtype != 0;
-    hipError_t e = bf16 ? set_lds<uint16_t>() : set_lds<float>();
+    hipError_t e = bf16 ? hipSuccess : set_lds<float>();
     if (e != hipSuccess)
         return e;
     if (units > 0 && p.nseg > 1) {
@@ -651,11 +648,12 @@ hipError_t launch_linear_backward(const LinearBwdArgs& a, const SegmentPlan& pla
         // end cotangent of every segment: cotangent maps, then the same
         // composition run from dW_out through the segments in reverse
         const dim3 mgrid(static_cast<unsigned>(placed_grid(units, 2 * (p.nseg - 1))));
-        if (bf16)
-            launch_kernel<uint16_t, true>(a, p, w, mgrid);
-        else
+        if (bf16) {
+            e = launch_linear_backward_bf16(a, p, true, w, mgrid);
+        } else {
             launch_kernel<float, true>(a, p, w, mgrid);
-        e = hipGetLastError();
+            e = hipGetLastError();
+        }
         if (e != hipSuccess)
             return e;
         const LinearArgs ga{a.Q, a.K, a.V, a.dtype, a.dW_out, 1, a.eta, a.B, a.H, a.T,
@@ -669,11 +667,12 @@ hipError_t launch_linear_backward(const LinearBwdArgs& a, const SegmentPlan& pla
     }
     if (units > 0) {
         const dim3 grid(static_cast<unsigned>(p.nseg > 1 ? placed_grid(units, p.nseg) : units));
-        if (bf16)
-            launch_kernel<uint16_t, false>(a, p, w, grid);
-        else
+        if (bf16) {
+            e = launch_linear_backward_bf16(a, p, false, w, grid);
+        } else {
             launch_kernel<float, false>(a, p, w, grid);
-        e = hipGetLastError();
+            e = hipGetLastError();
+        }
         if (e != hipSuccess)
             return e;
     }

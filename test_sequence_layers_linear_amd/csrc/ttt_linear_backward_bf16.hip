@@ -1,0 +1,480 @@
+// ttt_linear_backward_bf16.hip -- backward of the TTT-Linear dual-form scan
+// for bf16 Q/K/V on bf16 MFMA (d = 64, b = 16; fp32 state, cotangent and
+// accumulation).  Same recurrence, segments and work split as the fp32
+// kernel in ttt_linear_backward.hip (see there for the derivation):
+//     P  = A^T dY + K G'      dE = -eta P      deta += -<P, E>
+//     dA = -eta tril(dY E^T)  dQ = dY W^T + dA K
+//     dK = -eta (P W^T + E G'^T) + dA^T Q      dV = eta P
+//     G  = G' + Q^T dY + K^T dE
+// with every product on v_mfma_f32_16x16x32_bf16 (contractions over the
+// 64-wide head dim) or v_mfma_f32_16x16x16_bf16 (over the 16 tokens of a
+// chunk); operands are rounded to bf16 as in the forward kernel, results
+// accumulate in fp32.
+//
+// Layouts (lane l, c = l % 16, g = l / 16): 16x16x32 A operand lane holds
+// A[c][8g .. 8g+7], B operand B[8g .. 8g+7][c]; 16x16x16 A operand A[c][4g ..
+// 4g+3], B operand B[4g .. 4g+3][c]; accumulators rows 4g .. 4g+3 of column
+// c.  The state W (sweep 1) and the cotangent G keep their 64 x 16 column
+// block as four fp32 accumulator tiles mt whose row m is input index
+// rho(mt, m) = 32 (mt / 2) + 8 (m / 4) + 4 (mt % 2) + m % 4, so tiles 2s and
+// 2s + 1 packed to bf16 are the B operand of a product over the input index
+// i in [32 s, 32 s + 32) (k-slot (g, e) <-> i = 32 s + 8 g + e), and the
+// 16x16x16 products that update them take A = K^T or Q^T read in the same
+// rho order.  An accumulator read as a 16x16x16 A operand is the transpose of
+// itself, which gives A^T from S = Q K^T and dA^T from dA.  Products of the
+// two shapes never share an accumulator (they are summed in fp32 instead).
+//
+// LDS (bf16, 16-byte segments of each 128-byte row XOR-swizzled by row):
+// a two-slot ring of the chunk's Q, K, dY tiles, W_c^T (one buffer), E and P
+// tiles and G'^T for phase B.  Column reads use ds_read_b64_tr_b16: within a
+// 16-lane group, lane i receives element i % 4 of the 8-byte block addressed
+// by lane 4k + i / 4 as its element k, so lanes addressing rows r0 + j / 4 at
+// columns x0 + 4 (j % 4) hand lane i the 4 values X[r0 .. r0 + 3][x0 + i].
+// The chunk-start states go to the workspace as bf16 W^T (8 KB per chunk).
+#include "ttt_internal.h"
+
+namespace ttt {
+namespace {
+
+constexpr int kD = 64;
+constexpr int kB = 16;
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRow = kD * 2;                    // bytes per bf16 row
+constexpr int kTileB = kB * kRow;               // 2048: a 16 x 64 tile
+constexpr int kMatB = kD * kRow;                // 8192: a 64 x 64 matrix
+constexpr int kSlotQ = 0;
+constexpr int kSlotK = kTileB;
+constexpr int kSlotDY = 2 * kTileB;
+constexpr int kSlotBytes = 3 * kTileB;
+constexpr int kOffW = 2 * kSlotBytes;           // W_c^T [64 j][64 i]
+constexpr int kOffE = kOffW + kMatB;            // E  [16][64]
+constexpr int kOffP = kOffE + kTileB;           // P  [16][64]
+constexpr int kOffG = kOffP + kTileB;           // G'^T [64 j][64 i]
+constexpr int kOffRed = kOffG + kMatB;
+constexpr int kLdsBytes = kOffRed + 16;         // 32784
+constexpr int kGMapLdsBytes = 2 * kSlotBytes;   // the cotangent maps use the slots only
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16(bf16x4 a, bf16x4 b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a),
+                                                     __builtin_bit_cast(i16x4, b), c, 0, 0, 0);
+}
+
+// fp32 pairs -> one word of two bf16 (round to nearest even)
+__device__ __forceinline__ uint32_t cvt2(float a, float b)
+{
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+__device__ __forceinline__ bf16x8 pack8(f32x4 lo, f32x4 hi)
+{
+    return __builtin_bit_cast(bf16x8, u32x4{cvt2(lo[0], lo[1]), cvt2(lo[2], lo[3]),
+                                            cvt2(hi[0], hi[1]), cvt2(hi[2], hi[3])});
+}
+__device__ __forceinline__ bf16x4 pack4(f32x4 x)
+{
+    return __builtin_bit_cast(bf16x4, u32x2{cvt2(x[0], x[1]), cvt2(x[2], x[3])});
+}
+__device__ __forceinline__ bf16x8 join(bf16x4 lo, bf16x4 hi)
+{
+    const u32x2 a = __builtin_bit_cast(u32x2, lo), b = __builtin_bit_cast(u32x2, hi);
+    return __builtin_bit_cast(bf16x8, u32x4{a[0], a[1], b[0], b[1]});
+}
+
+__device__ __forceinline__ int rho(int mt, int m)
+{
+    return 32 * (mt >> 1) + 8 * (m >> 2) + 4 * (mt & 1) + (m & 3);
+}
+
+// byte offset of 16-byte segment `seg` of row `r` in a swizzled tile
+__device__ __forceinline__ int swz(int r, int seg) { return r * kRow + ((seg ^ (r & 7)) << 4); }
+// byte offset of element x of row r
+__device__ __forceinline__ int swz_elem(int r, int x) { return swz(r, x >> 3) + 2 * (x & 7); }
+
+__device__ __forceinline__ bf16x4 read_tr16(const unsigned char* p)
+{
+    typedef __bf16 lds_bf16x4 __attribute__((ext_vector_type(4)));
+    const auto q = (__attribute__((address_space(3))) lds_bf16x4*)(
+        (__attribute__((address_space(3))) unsigned char*)(p));
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(q);
+}
+// X[r0 .. r0 + 3][x0 + c] for lane (c, .) of a row-major swizzled tile
+// (x0 a multiple of 16)
+__device__ __forceinline__ bf16x4 col4(const unsigned char* tile, int r0, int x0, int c)
+{
+    return read_tr16(tile + swz_elem(r0 + (c >> 2), x0 + 4 * (c & 3)));
+}
+// X[r0 .. r0 + 3][rho(mt, c)]: the rho-ordered column block of input tile mt
+__device__ __forceinline__ bf16x4 col4_rho(const unsigned char* tile, int r0, int mt, int c)
+{
+    return read_tr16(tile + swz(r0 + (c >> 2), 4 * (mt >> 1) + (c & 3)) + 8 * (mt & 1));
+}
+__device__ __forceinline__ bf16x8 row8(const unsigned char* tile, int r, int seg)
+{
+    return *reinterpret_cast<const bf16x8*>(tile + swz(r, seg));
+}
+
+struct Stage {
+    u32x2 q, k, dy;    // 4 bf16 of row tid / 16, columns 4 (tid % 16) .. +3
+    uint16_t v[4];     // V[4g + r][16w + c]: this lane's entries of its wave's columns
+    u32x4 w[2];        // W_c^T row tid / 4, segments 2 (tid % 4), +1
+};
+
+template <bool kGMap>
+__global__ void __launch_bounds__(kThreads, 2)
+linear_backward_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                            const uint16_t* __restrict__ V, const float* __restrict__ W0,
+                            int w0_per_batch, const float* __restrict__ eta, int H, int T,
+                            int64_t units, int seg_len, int nseg, const float* __restrict__ wstart,
+                            const float* __restrict__ gend, const uint16_t* __restrict__ dY,
+                            const float* __restrict__ dW_out, uint16_t* __restrict__ dQ,
+                            uint16_t* __restrict__ dK, uint16_t* __restrict__ dV,
+                            float* __restrict__ dW0_chain, float* __restrict__ deta_chain,
+                            uint16_t* __restrict__ states, float* __restrict__ gmaps)
+{
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = tid >> 6;
+    const int c = lane & 15;
+    const int g = lane >> 4;
+    const int col = 16 * w + c;
+
+    int64_t u = blockIdx.x;
+    int s = 0, half = 0;
+    if (nseg > 1) {
+        xcd_block(blockIdx.x, kGMap ? 2 * (nseg - 1) : nseg, units, u, s);
+        if (u >= units)                  // padding of the XCD placement
+            return;
+        if (kGMap) {
+            half = s & 1;
+            s = (s >> 1) + 1;
+        }
+    }
+    const int h = static_cast<int>(u % H);
+    const float et = eta[h];
+    const int seg_chunks = seg_len / kB;
+    const int c0 = s * seg_chunks;
+    const int c1 = min((T + kB - 1) / kB, c0 + seg_chunks);
+    const int64_t off = u * static_cast<int64_t>(T) * kD;
+    uint16_t* st = states + (u * nseg + s) * static_cast<int64_t>(seg_chunks) * kD * kD;
+    const bool use_dy = !kGMap || half == 1;     // uniform per workgroup
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+
+    // staging of the 16 x 64 tiles: thread tid moves 8 bytes of row tid / 16
+    const int srow = tid >> 4;
+    const int scol = 4 * (tid & 15);
+    const int sbyte = swz(srow, scol >> 3) + 8 * (tid & 1);
+    auto load_stage = [&](Stage& x, int chunk, bool qdy, bool wst) {
+        const int t = chunk * kB + srow;
+        const bool ok = t < T;
+        const int64_t e = off + static_cast<int64_t>(t) * kD + scol;
+        x.k = ok ? *reinterpret_cast<const u32x2*>(K + e) : u32x2{0u, 0u};
+        if (qdy) {
+            x.q = ok ? *reinterpret_cast<const u32x2*>(Q + e) : u32x2{0u, 0u};
+            x.dy = ok ? *reinterpret_cast<const u32x2*>(dY + e) : u32x2{0u, 0u};
+        }
+        if (!kGMap) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int tv = chunk * kB + 4 * g + r;
+                x.v[r] = tv < T ? V[off + static_cast<int64_t>(tv) * kD + col] : uint16_t(0);
+            }
+        }
+        if (wst) {
+            const uint16_t* src = st + static_cast<int64_t>(chunk - c0) * kD * kD + (tid >> 2) * kD;
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+                x.w[q] = *reinterpret_cast<const u32x4*>(src + 8 * (2 * (tid & 3) + q));
+        }
+    };
+    auto store_stage = [&](const Stage& x, int slot, bool qdy) {
+        unsigned char* sl = lds + slot * kSlotBytes;
+        *reinterpret_cast<u32x2*>(sl + kSlotK + sbyte) = x.k;
+        if (qdy) {
+            *reinterpret_cast<u32x2*>(sl + kSlotQ + sbyte) = x.q;
+            *reinterpret_cast<u32x2*>(sl + kSlotDY + sbyte) = x.dy;
+        }
+    };
+    auto store_w = [&](const Stage& x) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+            *reinterpret_cast<u32x4*>(lds + kOffW + swz(tid >> 2, 2 * (tid & 3) + q)) = x.w[q];
+    };
+    auto vneg = [&](const uint16_t (&v)[4]) {
+        f32x4 r;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            r[q] = -__uint_as_float(static_cast<uint32_t>(v[q]) << 16);
+        return r;
+    };
+
+    // ---------------- sweep 1: chunk-start states of the segment ----------------
+    if (!kGMap && c1 > c0) {
+        f32x4 Wacc[4];           // W[rho(mt, 4g + r)][col]
+        {
+            const float* w0 = nseg > 1 ? wstart + (u * nseg + s) * kD * kD
+                                       : W0 + (w0_per_batch ? u : h) * kD * kD;
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    Wacc[mt][r] = w0[rho(mt, 4 * g + r) * kD + col];
+        }
+        Stage nx;
+        load_stage(nx, c0, false, false);
+        store_stage(nx, 0, false);
+        uint16_t vcur[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            vcur[r] = nx.v[r];
+        __syncthreads();
+        for (int ch = c0; ch < c1; ++ch) {
+            // W_c^T row col: 16 bytes at i = 8g .. and 32 + 8g ..
+            const bf16x8 b0 = pack8(Wacc[0], Wacc[1]);
+            const bf16x8 b1 = pack8(Wacc[2], Wacc[3]);
+            uint16_t* sc = st + static_cast<int64_t>(ch - c0) * kD * kD + col * kD;
+            *reinterpret_cast<bf16x8*>(sc + 8 * g) = b0;
+            *reinterpret_cast<bf16x8*>(sc + 32 + 8 * g) = b1;
+            if (ch + 1 == c1)
+                break;
+            load_stage(nx, ch + 1, false, false);
+            const unsigned char* sl = lds + ((ch - c0) & 1) * kSlotBytes;
+            // E = K W_J - V, W += K^T (-eta E)
+            f32x4 R = mfma32(row8(sl + kSlotK, c, g), b0, vneg(vcur));
+            R = mfma32(row8(sl + kSlotK, c, 4 + g), b1, R);
+            const bf16x4 eb = pack4(-et * R);
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+                Wacc[mt] = mfma16(col4_rho(sl + kSlotK, 4 * g, mt, c), eb, Wacc[mt]);
+            store_stage(nx, (ch - c0 + 1) & 1, false);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                vcur[r] = nx.v[r];
+            __syncthreads();
+        }
+        // the states just stored are read back below by other threads
+        __threadfence();
+        __syncthreads();
+    }
+
+    // ---------------- sweep 2: reverse over the chunks of the segment ----------------
+    f32x4 Gacc[4];               // G[rho(mt, 4g + r)][col]
+    if (kGMap) {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                Gacc[mt][r] = half == 0 && rho(mt, 4 * g + r) == col ? 1.f : 0.f;
+    } else {
+        const float* g1 = nseg > 1 ? gend + (u * nseg + (nseg - 1 - s)) * kD * kD
+                                   : dW_out + u * kD * kD;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                Gacc[mt][r] = g1[rho(mt, 4 * g + r) * kD + col];
+    }
+    float deta_acc = 0.f;
+
+    uint16_t vcur[4] = {0, 0, 0, 0};
+    if (c1 > c0) {
+        Stage nx;
+        load_stage(nx, c1 - 1, use_dy, !kGMap);
+        store_stage(nx, 0, use_dy);
+        if (!kGMap) {
+            store_w(nx);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                vcur[r] = nx.v[r];
+        }
+        __syncthreads();
+    }
+    for (int ch = c1 - 1; ch >= c0; --ch) {
+        const int slot = (c1 - 1 - ch) & 1;
+        const unsigned char* sl = lds + slot * kSlotBytes;
+        Stage nx;
+        if (ch > c0)
+            load_stage(nx, ch - 1, use_dy, !kGMap);
+
+        // ---- phase A: columns J = w ----
+        const bf16x8 ka0 = row8(sl + kSlotK, c, g);
+        const bf16x8 ka1 = row8(sl + kSlotK, c, 4 + g);
+        const bf16x8 gb0 = pack8(Gacc[0], Gacc[1]);       // G'_J as a B operand
+        const bf16x8 gb1 = pack8(Gacc[2], Gacc[3]);
+        f32x4 E = zero;
+        bf16x8 wb[2];                                     // W[16 w + c][32 s + 8g ..] for phase B
+        if (!kGMap) {
+            E = mfma32(ka0, row8(lds + kOffW, col, g), vneg(vcur));
+            E = mfma32(ka1, row8(lds + kOffW, col, 4 + g), E);
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+                wb[q] = join(col4(lds + kOffW, 32 * q + 8 * g, 16 * w, c),
+                             col4(lds + kOffW, 32 * q + 8 * g + 4, 16 * w, c));
+        }
+        // P = A^T dY_J + K G'_J  (A = tril(Q K^T); S holds S[t = 4g + r][s = c])
+        f32x4 P1 = zero;
+        bf16x4 dyt = {};
+        if (use_dy) {
+            f32x4 S = mfma32(row8(sl + kSlotQ, c, g), ka0, zero);
+            S = mfma32(row8(sl + kSlotQ, c, 4 + g), ka1, S);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                S[r] = c <= 4 * g + r ? S[r] : 0.f;
+            dyt = col4(sl + kSlotDY, 4 * g, 16 * w, c);  // dY[4g + r][col]
+            P1 = mfma16(pack4(S), dyt, zero);
+        }
+        f32x4 P2 = mfma32(ka0, gb0, zero);
+        P2 = mfma32(ka1, gb1, P2);
+        const f32x4 P = P1 + P2;
+        const f32x4 dE = -et * P;
+        if (!kGMap) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                deta_acc -= P[r] * E[r];
+                *reinterpret_cast<__bf16*>(lds + kOffE + swz_elem(4 * g + r, col)) = static_cast<__bf16>(E[r]);
+                *reinterpret_cast<__bf16*>(lds + kOffP + swz_elem(4 * g + r, col)) = static_cast<__bf16>(P[r]);
+            }
+            // G'^T row col: i = 8g .. and 32 + 8g ..
+            *reinterpret_cast<bf16x8*>(lds + kOffG + swz(col, g)) = gb0;
+            *reinterpret_cast<bf16x8*>(lds + kOffG + swz(col, 4 + g)) = gb1;
+        }
+        // G = G' + Q^T dY_J + K^T dE  (over the 16 tokens; A in rho order)
+        const bf16x4 deb = pack4(dE);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            f32x4 acc = Gacc[mt];
+            if (use_dy)
+                acc = mfma16(col4_rho(sl + kSlotQ, 4 * g, mt, c), dyt, acc);
+            Gacc[mt] = mfma16(col4_rho(sl + kSlotK, 4 * g, mt, c), deb, acc);
+        }
+
+        if (!kGMap) {
+            __syncthreads();
+            // every wave has read W_c: the next chunk's W_c may replace it
+            if (ch > c0)
+                store_w(nx);
+            // ---- phase B: input dims I = w ----
+            const bf16x8 ya0 = row8(sl + kSlotDY, c, g), ya1 = row8(sl + kSlotDY, c, 4 + g);
+            const bf16x8 ea0 = row8(lds + kOffE, c, g), ea1 = row8(lds + kOffE, c, 4 + g);
+            // dA[t = 4g + r][s = c] and dA^T[s = 4g + r][t = c], masked and scaled
+            f32x4 dA = mfma32(ya0, ea0, zero);
+            dA = mfma32(ya1, ea1, dA);
+            f32x4 dAT = mfma32(ea0, ya0, zero);
+            dAT = mfma32(ea1, ya1, dAT);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                dA[r] = c <= 4 * g + r ? -et * dA[r] : 0.f;
+                dAT[r] = 4 * g + r <= c ? -et * dAT[r] : 0.f;
+            }
+            // dQ_I = dY W[I, :]^T + dA K_I
+            f32x4 q1 = mfma32(ya0, wb[0], zero);
+            q1 = mfma32(ya1, wb[1], q1);
+            const f32x4 q2 = mfma16(pack4(dAT), col4(sl + kSlotK, 4 * g, 16 * w, c), zero);
+            const f32x4 dq = q1 + q2;
+            // dK_I = -eta (P W[I, :]^T + E G'[I, :]^T) + dA^T Q_I
+            bf16x8 gt[2];
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+                gt[q] = join(col4(lds + kOffG, 32 * q + 8 * g, 16 * w, c),
+                             col4(lds + kOffG, 32 * q + 8 * g + 4, 16 * w, c));
+            f32x4 k1 = mfma32(row8(lds + kOffP, c, g), wb[0], zero);
+            k1 = mfma32(row8(lds + kOffP, c, 4 + g), wb[1], k1);
+            k1 = mfma32(ea0, gt[0], k1);
+            k1 = mfma32(ea1, gt[1], k1);
+            const f32x4 k2 = mfma16(pack4(dA), col4(sl + kSlotQ, 4 * g, 16 * w, c), zero);
+            const f32x4 dk = -et * k1 + k2;
+
+            // rows t = 16 ch + 4g + r, column 16 w + c; dV = eta P (this wave's
+            // columns from phase A)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = ch * kB + 4 * g + r;
+                if (t < T) {
+                    const int64_t e = off + static_cast<int64_t>(t) * kD + col;
+                    store_elem(dQ, e, dq[r]);
+                    store_elem(dK, e, dk[r]);
+                    store_elem(dV, e, et * P[r]);
+                }
+            }
+        }
+        if (ch > c0) {
+            store_stage(nx, slot ^ 1, use_dy);
+            if (!kGMap) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    vcur[r] = nx.v[r];
+            }
+        }
+        __syncthreads();
+    }
+
+    if (kGMap) {
+        float* out = gmaps + ((u * (nseg - 1) + (nseg - 1 - s)) * 2 + half) * kD * kD;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                out[rho(mt, 4 * g + r) * kD + col] = Gacc[mt][r];
+        return;
+    }
+    if (s == 0) {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                dW0_chain[u * kD * kD + rho(mt, 4 * g + r) * kD + col] = Gacc[mt][r];
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1)
+        deta_acc += __shfl_xor(deta_acc, m);
+    float* red = reinterpret_cast<float*>(lds + kOffRed);
+    if (lane == 0)
+        red[w] = deta_acc;
+    __syncthreads();
+    if (tid == 0)
+        deta_chain[u * nseg + s] = (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+}  // namespace
+
+hipError_t launch_linear_backward_bf16(const LinearBwdArgs& a, const SegmentPlan& p, bool gmap,
+                                       const BwdBuffers& b, dim3 grid)
+{
+    const auto* q = static_cast<const uint16_t*>(a.Q);
+    const auto* k = static_cast<const uint16_t*>(a.K);
+    const auto* v = static_cast<const uint16_t*>(a.V);
+    const auto* dy = static_cast<const uint16_t*>(a.dY);
+    auto* dq = static_cast<uint16_t*>(a.dQ);
+    auto* dk = static_cast<uint16_t*>(a.dK);
+    auto* dv = static_cast<uint16_t*>(a.dV);
+    auto* st = reinterpret_cast<uint16_t*>(b.states);
+    const int H = static_cast<int>(a.H), T = static_cast<int>(a.T), seg = static_cast<int>(p.seg_len);
+    if (gmap)
+        hipLaunchKernelGGL(linear_backward_bf16_kernel<true>, grid, dim3(kThreads), kGMapLdsBytes,
+                           a.stream, q, k, v, a.W0, a.w0_per_batch, a.eta, H, T, a.B * a.H, seg,
+                           p.nseg, b.wstart, b.gend, dy, a.dW_out, dq, dk, dv, b.dw_chain,
+                           b.deta_chain, st, b.gmaps);
+    else
+        hipLaunchKernelGGL(linear_backward_bf16_kernel<false>, grid, dim3(kThreads), kLdsBytes,
+                           a.stream, q, k, v, a.W0, a.w0_per_batch, a.eta, H, T, a.B * a.H, seg,
+                           p.nseg, b.wstart, b.gend, dy, a.dW_out, dq, dk, dv, b.dw_chain,
+                           b.deta_chain, st, b.gmaps);
+    return hipGetLastError();
+}
+
+}  // namespace ttt

@@ -29,6 +29,8 @@ KERNEL_FILES = {
     "linear_combine_kernel": "ttt_linear_combine.hip",
     "linear_backward_kernel[gmaps]": "ttt_linear_backward.hip",
     "linear_backward_kernel[segments]": "ttt_linear_backward.hip",
+    "linear_backward_bf16_kernel[gmaps]": "ttt_linear_backward_bf16.hip",
+    "linear_backward_bf16_kernel[segments]": "ttt_linear_backward_bf16.hip",
     "linear_backward_reduce_kernel": "ttt_linear_backward.hip",
     "linear_generic_kernel": "ttt_generic.hip",
     "mlp_generic_kernel": "ttt_generic.hip",
@@ -44,6 +46,9 @@ def short_name(full: str) -> str:
     for the backward's cotangent maps and segment backward."""
     if "linear_backward_kernel<" in full:
         return "linear_backward_kernel[gmaps]" if ", true>" in full else "linear_backward_kernel[segments]"
+    if "linear_backward_bf16_kernel<" in full:
+        return ("linear_backward_bf16_kernel[gmaps]" if "<true>" in full
+                else "linear_backward_bf16_kernel[segments]")
     for k in KERNEL_FILES:
         base = k.split("[")[0]
         if base + "<true" in full:
