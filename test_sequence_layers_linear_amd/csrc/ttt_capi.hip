@@ -109,10 +109,10 @@ ttt::SegmentPlan plan_segments(int64_t units, int64_t T, int chunk, const ttt::S
 
 // Segment count for the backward of a TTT-Linear scan: each segment pays
 // its chunks' forward map, cotangent map and backward, and the two
-// compositions (S - 1) steps each, plus four extra launches.  The segment
-// backward runs one workgroup per CU (two per CU run at half the speed each);
-// the maps launches may put two on a CU (the cotangent maps use 26 KB of LDS
-// and half the registers).  TTT_LINEAR_BWD_SEGMENTS=S forces S segments.
+// compositions (S - 1) steps each, plus four extra launches.  Up to
+// max_per_cu segment-backward workgroups share a CU, each slowed by `share`
+// per extra workgroup per CU; the maps launches may hold maps_per_cu per CU.
+// TTT_LINEAR_BWD_SEGMENTS=S forces S segments.
 ttt::SegmentPlan plan_backward(int64_t units, int64_t T, int chunk, const ttt::BwdCosts& cost)
 {
     ttt::SegmentPlan p;
@@ -127,15 +127,18 @@ ttt::SegmentPlan plan_backward(int64_t units, int64_t T, int chunk, const ttt::B
         }
     }
     const int64_t cus = device_cus();
-    if (cus <= 0 || 2 * units > cus || chunks < 4) return p;
+    if (cus <= 0 || 2 * units > cost.max_per_cu * cus || chunks < 4) return p;
     const int map_blocks = std::max(2, cost.fmap_blocks_per_segment);
     double best = static_cast<double>(chunks) * cost.bwd;
     int best_s = 1;
     for (int S = 2; S <= ttt::kMaxSegments; ++S) {
-        if (units * S > cus || units * (S - 1) * map_blocks > 2 * cus) break;
+        if (units * S > cost.max_per_cu * cus || units * (S - 1) * map_blocks > cost.maps_per_cu * cus)
+            break;
         const int64_t per = (chunks + S - 1) / S;
         if (per < 2) break;
-        const double t = per * (cost.bwd + cost.fmap + cost.gmap) + 2.0 * (S - 1) * cost.apply + cost.launch;
+        const double load = std::max(1.0, static_cast<double>(units * S) / static_cast<double>(cus));
+        const double t = per * (cost.bwd * (1.0 + cost.share * (load - 1.0)) + cost.fmap + cost.gmap) +
+                         2.0 * (S - 1) * cost.apply + cost.launch;
         if (t < best) { best = t; best_s = S; }
     }
     if (best_s > 1) {

@@ -204,16 +204,23 @@ struct BwdBuffers {
 hipError_t launch_linear_backward_bf16(const LinearBwdArgs& a, const SegmentPlan& p, bool gmap,
                                        const BwdBuffers& b, dim3 grid);
 bool linear_backward_supports(const LinearBwdArgs& a);
-// Latencies (us) that size the backward's segment split: backward chunk,
-// forward map chunk, cotangent map chunk, one composition step, the fixed
-// cost of the four extra launches; workgroups per segment of the forward
-// maps launch (the cotangent maps always take two).
+// Latencies (us) that size the backward's segment split: backward chunk
+// (one workgroup on a CU), forward map chunk, cotangent map chunk, one
+// composition step, the fixed cost of the four extra launches; workgroups per
+// segment of the forward maps launch (the cotangent maps always take two);
+// segment-backward workgroups a CU may hold, and the slowdown of each per
+// extra workgroup per CU (measured on MI355X: the bf16 kernel's 32 KB of LDS
+// let two share a CU, each 1.7x slower at 1.9 per CU; the fp32 kernel gains
+// nothing from sharing); maps workgroups a CU may hold.
 struct BwdCosts {
     double bwd, fmap, gmap, apply, launch;
     int fmap_blocks_per_segment;
+    int max_per_cu;
+    double share;
+    int maps_per_cu;
 };
-constexpr BwdCosts kLinearBwdF32Costs{5.2, 0.9, 1.5, 0.6, 20.0, 2};
-constexpr BwdCosts kLinearBwdBf16Costs{5.2, 0.43, 1.5, 0.6, 20.0, 1};
+constexpr BwdCosts kLinearBwdF32Costs{5.2, 0.9, 1.5, 0.6, 20.0, 2, 1, 0.0, 2};
+constexpr BwdCosts kLinearBwdBf16Costs{2.63, 0.43, 1.0, 0.6, 20.0, 1, 2, 0.7, 4};
 size_t linear_backward_workspace_bytes(const LinearBwdArgs& a, const SegmentPlan& p);
 hipError_t launch_linear_backward(const LinearBwdArgs& a, const SegmentPlan& p, void* workspace);
 
