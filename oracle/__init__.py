@@ -24,6 +24,11 @@ Parity status of each function (how it is pinned, see tests/test_oracle.py):
                      chunk-start read is block-causal linear attention for
                      W0 = 0, online GD read before the update for b = 1, and
                      leaves W_out unchanged.
+  linear_backward_ex -- pinned: equals linear_backward with the prologue off;
+                     finite differences of linear_forward_ex in every
+                     coordinate (q, k, v, W0, per-token eta, gamma, beta),
+                     with and without the chunk-start read; torch autograd
+                     of layer_norm for the LayerNorm part.
   linear_backward -- pinned: central finite differences of linear_forward in
                      every coordinate (tiny sizes), the closed form of every
                      gradient at eta=0 (independent of b), the gradients of
@@ -80,6 +85,11 @@ def _load():
     lib.ttt_oracle_linear_forward_tok.restype = I
     lib.ttt_oracle_layernorm_rows.argtypes = [P, L, L, L, L, P, P, ctypes.c_double]
     lib.ttt_oracle_layernorm_rows.restype = I
+    lib.ttt_oracle_linear_backward_tok.argtypes = [P, P, P, P, I, P, I, L, L, L, L, L, P, P,
+                                                   P, P, P, P, P, I]
+    lib.ttt_oracle_linear_backward_tok.restype = I
+    lib.ttt_oracle_layernorm_rows_backward.argtypes = [P, P, L, L, L, L, P, ctypes.c_double, P]
+    lib.ttt_oracle_layernorm_rows_backward.restype = I
     lib.ttt_oracle_max_threads.argtypes = []
     lib.ttt_oracle_max_threads.restype = I
     _lib = lib
@@ -196,6 +206,54 @@ def linear_backward(Q, K, V, W0, eta, b: int, dY, dW_out, nthreads: int = 0):
         raise RuntimeError(f"oracle linear_backward failed ({rc})")
     dW0 = dW0c if per_batch else dW0c.sum(axis=0)
     return dQ, dK, dV, dW0, detac.sum(axis=0)
+
+
+def linear_backward_ex(Q, K, V, W0, eta, b: int, dY, dW_out, eta_tok=None, ln_q=None,
+                       ln_k=None, ln_eps: float = 1e-5, read_chunk_start: bool = False,
+                       nthreads: int = 0):
+    """Vector-Jacobian product of linear_forward_ex.  Returns a dict with dQ,
+    dK, dV (of the raw inputs), dW0 (shaped like W0, summed over the batch
+    when shared), deta [H] (head step sizes; zero when eta_tok is given),
+    deta_tok [B,H,T] (when eta_tok is given), dln_q / dln_k [H,2,d] (when
+    given)."""
+    Q, K, V, W0, eta, dY, dW_out = map(_f64, (Q, K, V, W0, eta, dY, dW_out))
+    B, H, T, d = Q.shape
+    per_batch = 1 if W0.ndim == 4 else 0
+    Qn = layernorm(Q, ln_q, ln_eps) if ln_q is not None else Q
+    Kn = layernorm(K, ln_k, ln_eps) if ln_k is not None else K
+    et = (_f64(eta_tok) if eta_tok is not None
+          else np.ascontiguousarray(np.broadcast_to(eta[None, :, None], (B, H, T))))
+    dQ = np.zeros((B, H, T, d))
+    dK = np.zeros((B, H, T, d))
+    dV = np.zeros((B, H, T, d))
+    dW0c = np.zeros((B, H, d, d))
+    detat = np.zeros((B, H, T))
+    rc = _load().ttt_oracle_linear_backward_tok(_ptr(Qn), _ptr(Kn), _ptr(V), _ptr(W0), per_batch,
+                                                _ptr(et), int(bool(read_chunk_start)), B, H, T,
+                                                d, int(b), _ptr(dY), _ptr(dW_out), _ptr(dQ),
+                                                _ptr(dK), _ptr(dV), _ptr(dW0c), _ptr(detat),
+                                                int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"oracle linear_backward_tok failed ({rc})")
+    out = {"dV": dV, "dW0": dW0c if per_batch else dW0c.sum(axis=0)}
+    for name, X, dX, ln in (("Q", Q, dQ, ln_q), ("K", K, dK, ln_k)):
+        if ln is not None:
+            ln = _f64(ln)
+            dgb = np.zeros((H, 2, d))
+            if X.size:
+                rc = _load().ttt_oracle_layernorm_rows_backward(
+                    _ptr(X), _ptr(dX), B * H * T, T, H, d, _ptr(np.ascontiguousarray(ln[:, 0])),
+                    float(ln_eps), _ptr(dgb))
+                if rc != 0:
+                    raise RuntimeError(f"oracle layernorm backward failed ({rc})")
+            out["dln_" + name.lower()] = dgb
+        out["d" + name] = dX
+    if eta_tok is None:
+        out["deta"] = detat.sum(axis=(0, 2))
+    else:
+        out["deta"] = np.zeros(H)
+        out["deta_tok"] = detat
+    return out
 
 
 def mlp_forward(Q, K, V, W1, W2, eta, b: int, nthreads: int = 0):

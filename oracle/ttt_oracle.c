@@ -478,6 +478,224 @@ int ttt_oracle_linear_backward(const double* Q, const double* K, const double* V
 }
 
 /* ------------------------------------------------------------------------ */
+/* Backward of linear_chain_tok (per-token step sizes, optional chunk-start   */
+/* read): reverse mode of its primal loops, token by token, as above:         */
+/*   r_t = k_t Wc - v_t,  G_t = G_{t-1} + eta_t k_t^T r_t,  W_t = Wc - G_t,   */
+/*   y_t = q_t (read_start ? Wc : W_t);  weights after a chunk = W_last.      */
+/* deta_tok receives the gradient of every token's step size.                 */
+/* ------------------------------------------------------------------------ */
+static void linear_chain_tok_backward(const double* q, const double* k, const double* v,
+                                      const double* w_init, const double* eta_t, int read_start,
+                                      long T, long d, long b, const double* dy,
+                                      const double* dw_out, double* dq, double* dk, double* dv,
+                                      double* dw0, double* deta_tok, struct lin_bwd_ws* w)
+{
+    const long dd = d * d;
+    const long nc = (T + b - 1) / b;
+
+    /* forward sweep: chunk-start weights */
+    memcpy(w->Wcs, w_init, (size_t)dd * sizeof(double));
+    for (long c = 0; c + 1 < nc; ++c) {
+        const long s = c * b, e = s + b;
+        const double* Wc = w->Wcs + c * dd;
+        double* Wn = w->Wcs + (c + 1) * dd;
+        memcpy(Wn, Wc, (size_t)dd * sizeof(double));
+        for (long t = s; t < e; ++t) {
+            for (long j = 0; j < d; ++j) {
+                double acc = 0.0;
+                for (long i = 0; i < d; ++i)
+                    acc += k[t * d + i] * Wc[i * d + j];
+                w->rb[j] = acc - v[t * d + j];
+            }
+            for (long i = 0; i < d; ++i)
+                for (long j = 0; j < d; ++j)
+                    Wn[i * d + j] -= eta_t[t] * k[t * d + i] * w->rb[j];
+        }
+    }
+
+    memcpy(w->Wb, dw_out, (size_t)dd * sizeof(double));
+    for (long c = nc - 1; c >= 0; --c) {
+        const long s = c * b, e = s + b < T ? s + b : T;
+        const double* Wc = w->Wcs + c * dd;
+        for (long t = s; t < e; ++t) {
+            double* r = w->R + (t - s) * d;
+            double* G = w->Gs + (t - s) * dd;
+            for (long j = 0; j < d; ++j) {
+                double acc = 0.0;
+                for (long i = 0; i < d; ++i)
+                    acc += k[t * d + i] * Wc[i * d + j];
+                r[j] = acc - v[t * d + j];
+            }
+            for (long i = 0; i < d; ++i)
+                for (long j = 0; j < d; ++j)
+                    G[i * d + j] = (t > s ? G[i * d + j - dd] : 0.0) + eta_t[t] * k[t * d + i] * r[j];
+        }
+        memset(w->Wcb, 0, (size_t)dd * sizeof(double));
+        memset(w->Gb, 0, (size_t)dd * sizeof(double));
+        for (long t = e - 1; t >= s; --t) {
+            const double* r = w->R + (t - s) * d;
+            const double* G = w->Gs + (t - s) * dd;
+            for (long x = 0; x < dd; ++x)
+                w->Wt[x] = Wc[x] - G[x];
+            /* readout: y_t = q_t Wr with Wr = Wc or W_t */
+            const double* Wr = read_start ? Wc : w->Wt;
+            for (long i = 0; i < d; ++i) {
+                double acc = 0.0;
+                for (long j = 0; j < d; ++j)
+                    acc += dy[t * d + j] * Wr[i * d + j];
+                dq[t * d + i] = acc;
+            }
+            /* adjoint of W_t: the readout's share (when it reads W_t) and, for
+             * the last token, the weights after the chunk */
+            for (long i = 0; i < d; ++i)
+                for (long j = 0; j < d; ++j) {
+                    const double qy = q[t * d + i] * dy[t * d + j];
+                    w->Wtb[i * d + j] = (read_start ? 0.0 : qy) + (t == e - 1 ? w->Wb[i * d + j] : 0.0);
+                    if (read_start)
+                        w->Wcb[i * d + j] += qy;
+                }
+            /* W_t = Wc - G_t */
+            for (long x = 0; x < dd; ++x) {
+                w->Wcb[x] += w->Wtb[x];
+                w->Gb[x] -= w->Wtb[x];
+            }
+            /* G_t = G_{t-1} + eta_t k_t^T r_t:  etab_t = k_t Gb r_t^T,
+             * kb_t = eta_t Gb r_t,  rb_t = eta_t k_t Gb */
+            double et_b = 0.0;
+            for (long i = 0; i < d; ++i) {
+                double acc = 0.0;
+                for (long j = 0; j < d; ++j)
+                    acc += w->Gb[i * d + j] * r[j];
+                dk[t * d + i] = eta_t[t] * acc;
+                et_b += k[t * d + i] * acc;
+            }
+            deta_tok[t] = et_b;
+            for (long j = 0; j < d; ++j) {
+                double acc = 0.0;
+                for (long i = 0; i < d; ++i)
+                    acc += k[t * d + i] * w->Gb[i * d + j];
+                w->rb[j] = eta_t[t] * acc;
+            }
+            /* r_t = k_t Wc - v_t */
+            for (long i = 0; i < d; ++i) {
+                double acc = 0.0;
+                for (long j = 0; j < d; ++j)
+                    acc += w->rb[j] * Wc[i * d + j];
+                dk[t * d + i] += acc;
+            }
+            for (long i = 0; i < d; ++i)
+                for (long j = 0; j < d; ++j)
+                    w->Wcb[i * d + j] += k[t * d + i] * w->rb[j];
+            for (long j = 0; j < d; ++j)
+                dv[t * d + j] = -w->rb[j];
+        }
+        memcpy(w->Wb, w->Wcb, (size_t)dd * sizeof(double));
+    }
+    memcpy(dw0, w->Wb, (size_t)dd * sizeof(double));
+}
+
+/* dQ, dK, dV: [B][H][T][d]; dW0 per chain [B][H][d][d]; deta_tok [B][H][T]. */
+int ttt_oracle_linear_backward_tok(const double* Q, const double* K, const double* V,
+                                   const double* W0, int w0_per_batch, const double* eta_tok,
+                                   int read_start, long B, long H, long T, long d, long b,
+                                   const double* dY, const double* dW_out,
+                                   double* dQ, double* dK, double* dV,
+                                   double* dW0_chain, double* deta_tok, int nthreads)
+{
+    if (B < 0 || H < 0 || T < 0 || d < 1 || b < 1)
+        return ORACLE_EINVAL;
+    if (!W0 || !dW_out || !dW0_chain ||
+        (T > 0 && (!Q || !K || !V || !dY || !dQ || !dK || !dV || !eta_tok || !deta_tok)))
+        return ORACLE_EINVAL;
+    const long dd = d * d;
+    const long units = B * H;
+    const long nc = (T + b - 1) / b;
+    const long bb = b < T ? b : (T > 0 ? T : 1);
+    int status = ORACLE_OK;
+    set_threads(nthreads);
+#pragma omp parallel
+    {
+        const size_t n = (size_t)((nc > 0 ? nc : 1) * dd + bb * dd + bb * d + 5 * dd + d);
+        double* buf = (double*)malloc(n * sizeof(double));
+        struct lin_bwd_ws w = {0};
+        if (!buf) {
+#pragma omp atomic write
+            status = ORACLE_ENOMEM;
+        } else {
+            w.Wcs = buf;
+            w.Gs = w.Wcs + (nc > 0 ? nc : 1) * dd;
+            w.R = w.Gs + bb * dd;
+            w.Wt = w.R + bb * d;
+            w.Wb = w.Wt + dd;
+            w.Wcb = w.Wb + dd;
+            w.Gb = w.Wcb + dd;
+            w.Wtb = w.Gb + dd;
+            w.rb = w.Wtb + dd;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (long u = 0; u < units; ++u) {
+            if (!buf)
+                continue;
+            long h = u % H;
+            const double* w_init = W0 + (w0_per_batch ? u : h) * dd;
+            const long off = u * T * d;
+            linear_chain_tok_backward(Q + off, K + off, V + off, w_init, eta_tok + u * T,
+                                      read_start, T, d, b, dY + off, dW_out + u * dd, dQ + off,
+                                      dK + off, dV + off, dW0_chain + u * dd, deta_tok + u * T, &w);
+        }
+        free(buf);
+    }
+    return status;
+}
+
+/* Backward of ttt_oracle_layernorm_rows: given X (the rows before the
+ * normalisation) and dX holding the gradient of the normalised rows,
+ * overwrite dX with the gradient of the raw rows and add the gradients of
+ * gamma and beta into dgb ([H][2][d]: gamma row, then beta row).  With
+ * xh = (x - mean) / sqrt(var + eps) and y = xh gamma + beta:
+ *   dgamma += dy xh,  dbeta += dy,  dxh = dy gamma,
+ *   dx = (dxh - mean(dxh) - xh mean(dxh xh)) / sqrt(var + eps). */
+int ttt_oracle_layernorm_rows_backward(const double* X, double* dX, long n, long T, long H, long d,
+                                       const double* gamma, double eps, double* dgb)
+{
+    if (n < 0 || T < 1 || H < 1 || d < 1 || !gamma || !dgb || eps < 0.0 || (n > 0 && (!X || !dX)))
+        return ORACLE_EINVAL;
+    double* xh = (double*)malloc((size_t)(2 * d) * sizeof(double));
+    if (!xh)
+        return ORACLE_ENOMEM;
+    double* dxh = xh + d;
+    for (long i = 0; i < n; ++i) {
+        const double* x = X + i * d;
+        double* g = dX + i * d;
+        const long h = (i / T) % H;
+        double mean = 0.0;
+        for (long j = 0; j < d; ++j)
+            mean += x[j];
+        mean /= (double)d;
+        double var = 0.0;
+        for (long j = 0; j < d; ++j)
+            var += (x[j] - mean) * (x[j] - mean);
+        var /= (double)d;
+        const double inv = 1.0 / sqrt(var + eps);
+        double m1 = 0.0, m2 = 0.0;
+        for (long j = 0; j < d; ++j) {
+            xh[j] = (x[j] - mean) * inv;
+            dgb[(2 * h) * d + j] += g[j] * xh[j];
+            dgb[(2 * h + 1) * d + j] += g[j];
+            dxh[j] = g[j] * gamma[h * d + j];
+            m1 += dxh[j];
+            m2 += dxh[j] * xh[j];
+        }
+        m1 /= (double)d;
+        m2 /= (double)d;
+        for (long j = 0; j < d; ++j)
+            g[j] = (dxh[j] - m1 - xh[j] * m2) * inv;
+    }
+    free(xh);
+    return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------------ */
 /* TTT-MLP: f(z; W1, W2) = SiLU(z W1) W2, d -> m -> d, no biases             */
 /* ([SEQ] "TTT-MLP": two-layer MLP with a SiLU non-linearity).                */
 /* ------------------------------------------------------------------------ */

@@ -18,6 +18,7 @@ import oracle
 import test_oracle as pins
 import test_oracle_backward as bpins
 import test_oracle_prologue as ppins
+import test_oracle_prologue_backward as pbpins
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "ttt_oracle.c")
 
@@ -45,9 +46,12 @@ MUTANTS = {
     "decode_residual_uses_query": ("acc += kt[i] * Wu[i * d + j];", "acc += qt[i] * Wu[i * d + j];"),
     # backward of the linear scan
     "bwd_state_adjoint_sign": ("w->Gb[x] -= eta * w->Wtb[x];", "w->Gb[x] += eta * w->Wtb[x];"),
-    "bwd_dv_sign": ("dv[t * d + j] = -w->rb[j];", "dv[t * d + j] = w->rb[j];"),
-    "bwd_drops_final_state_adjoint": ("+ (t == e - 1 ? w->Wb[i * d + j] : 0.0);", "+ 0.0;"),
-    "bwd_dk_transposed": ("acc += w->rb[j] * Wc[i * d + j];", "acc += w->rb[j] * Wc[j * d + i];"),
+    "bwd_dv_sign": ("dv[t * d + j] = -w->rb[j];\n        }\n        /* the chunk-start weights",
+                    "dv[t * d + j] = w->rb[j];\n        }\n        /* the chunk-start weights"),
+    "bwd_drops_final_state_adjoint": ("dy[t * d + j]\n                                        + (t == e - 1 ? w->Wb[i * d + j] : 0.0);",
+                                      "dy[t * d + j]\n                                        + 0.0;"),
+    "bwd_dk_transposed": ("vb_t = -rb_t */\n            for (long i = 0; i < d; ++i) {\n                double acc = 0.0;\n                for (long j = 0; j < d; ++j)\n                    acc += w->rb[j] * Wc[i * d + j];",
+                          "vb_t = -rb_t */\n            for (long i = 0; i < d; ++i) {\n                double acc = 0.0;\n                for (long j = 0; j < d; ++j)\n                    acc += w->rb[j] * Wc[j * d + i];"),
     "bwd_eta_sign": ("eb -= w->Wtb[x] * G[x];", "eb += w->Wtb[x] * G[x];"),
     "bwd_prefix_not_accumulated": ("(t > s ? G[i * d + j - dd] : 0.0) + k[t * d + i] * r[j];",
                                    "k[t * d + i] * r[j];"),
@@ -59,12 +63,28 @@ MUTANTS = {
                                "G[i * d + j] += eta_t[s] * kt[i] * r[j];"),
     "chunk_start_read_uses_updated": ("const double* Wr = read_start ? Wc : Wt;",
                                       "const double* Wr = read_start ? Wt : Wt;"),
-    "ln_no_mean_in_variance": ("var += (x[j] - mean) * (x[j] - mean);", "var += x[j] * x[j];"),
+    "ln_no_mean_in_variance": ("var += (x[j] - mean) * (x[j] - mean);\n        var /= (double)d;\n        const double inv = 1.0 / sqrt(var + eps);\n        for (long j = 0; j < d; ++j)\n            x[j] =",
+                               "var += x[j] * x[j];\n        var /= (double)d;\n        const double inv = 1.0 / sqrt(var + eps);\n        for (long j = 0; j < d; ++j)\n            x[j] ="),
     "ln_gamma_beta_swapped": ("x[j] = (x[j] - mean) * inv * gamma[h * d + j] + beta[h * d + j];",
                               "x[j] = (x[j] - mean) * inv * beta[h * d + j] + gamma[h * d + j];"),
-    "ln_eps_dropped": ("const double inv = 1.0 / sqrt(var + eps);", "const double inv = 1.0 / sqrt(var);"),
-    "bwd_state_adjoint_not_passed": ("memcpy(w->Wb, w->Wcb, (size_t)dd * sizeof(double));",
-                                     "memcpy(w->Wb, w->Wtb, (size_t)dd * sizeof(double));"),
+    "ln_eps_dropped": ("const double inv = 1.0 / sqrt(var + eps);\n        for (long j = 0; j < d; ++j)\n            x[j] =",
+                       "const double inv = 1.0 / sqrt(var);\n        for (long j = 0; j < d; ++j)\n            x[j] ="),
+    "bwd_state_adjoint_not_passed": ("previous chunk */\n        memcpy(w->Wb, w->Wcb, (size_t)dd * sizeof(double));",
+                                     "previous chunk */\n        memcpy(w->Wb, w->Wtb, (size_t)dd * sizeof(double));"),
+    # backward through the prologue
+    "tokbwd_deta_drops_key": ("et_b += k[t * d + i] * acc;", "et_b += acc;"),
+    "tokbwd_dk_missing_eta": ("dk[t * d + i] = eta_t[t] * acc;", "dk[t * d + i] = acc;"),
+    "tokbwd_rb_missing_eta": ("w->rb[j] = eta_t[t] * acc;", "w->rb[j] = acc;"),
+    "tokbwd_start_read_adjoint_dropped": ("w->Wcb[i * d + j] += qy;", "w->Wcb[i * d + j] += 0.0;"),
+    "tokbwd_dq_reads_updated": ("const double* Wr = read_start ? Wc : w->Wt;",
+                                "const double* Wr = w->Wt;"),
+    "tokbwd_state_adjoint_not_passed": ("memcpy(w->Wb, w->Wcb, (size_t)dd * sizeof(double));\n    }\n    memcpy(dw0, w->Wb, (size_t)dd * sizeof(double));\n}\n\n/* dQ, dK, dV: [B][H][T][d]; dW0 per chain [B][H][d][d]; deta_tok",
+                                        "memcpy(w->Wb, w->Wtb, (size_t)dd * sizeof(double));\n    }\n    memcpy(dw0, w->Wb, (size_t)dd * sizeof(double));\n}\n\n/* dQ, dK, dV: [B][H][T][d]; dW0 per chain [B][H][d][d]; deta_tok"),
+    "lnbwd_drops_mean_term": ("g[j] = (dxh[j] - m1 - xh[j] * m2) * inv;", "g[j] = (dxh[j] - xh[j] * m2) * inv;"),
+    "lnbwd_drops_projection": ("g[j] = (dxh[j] - m1 - xh[j] * m2) * inv;", "g[j] = (dxh[j] - m1) * inv;"),
+    "lnbwd_dgamma_of_raw_rows": ("dgb[(2 * h) * d + j] += g[j] * xh[j];", "dgb[(2 * h) * d + j] += g[j] * x[j];"),
+    "lnbwd_dbeta_scaled": ("dgb[(2 * h + 1) * d + j] += g[j];",
+                           "dgb[(2 * h + 1) * d + j] += g[j] * gamma[h * d + j];"),
 }
 
 
@@ -94,6 +114,11 @@ def _battery():
         ("tok_eta_zero", lambda: ppins.test_zero_token_eta_freezes_the_state(oracle)),
         ("start_read_la", lambda: ppins.test_chunk_start_read_is_block_causal_linear_attention(oracle, 13, 8)),
         ("start_read_b1", lambda: ppins.test_chunk_start_read_b1_is_online_gd_read_before_update(oracle)),
+        ("pbwd_off", lambda: pbpins.test_prologue_off_is_linear_backward(oracle, 2, 3, 37, 16, False)),
+        ("pbwd_fd", lambda: pbpins.test_matches_finite_differences(oracle, 7, 3, 3, True, True)),
+        ("pbwd_autograd", lambda: pbpins.test_matches_torch_autograd(oracle, 4, False)),
+        ("pbwd_autograd_start", lambda: pbpins.test_matches_torch_autograd(oracle, 4, True)),
+        ("pbwd_token_sum", lambda: pbpins.test_token_eta_gradients_sum_to_head_gradient(oracle, False)),
     ]
     for name, fn in checks:
         try:
