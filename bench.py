@@ -27,7 +27,8 @@ gradients of Q, K, V, W0 and eta for seeded cotangents dY, dW_out) timed the
 same way, with its own roofline (the MFMA peak of the input dtype: bf16
 inputs run on bf16 MFMA, fp32 inputs on fp32 MFMA).  It is reported beside the forward, not folded into the
 headline value.  "prologue" times ttt_linear_forward_ex on the same inputs
-with LayerNorm of q and k and a step size per token fused into the scan.
+with LayerNorm of q and k and a step size per token fused into the scan, and
+"backward_prologue" ttt_linear_backward_ex, the backward through them.
 """
 from __future__ import annotations
 
@@ -57,6 +58,10 @@ KERNEL_SOURCES = {
     "linear_backward_kernel[segments]": "ttt_linear_backward.hip",
     "linear_backward_bf16_kernel[gmaps]": "ttt_linear_backward_bf16.hip",
     "linear_backward_bf16_kernel[segments]": "ttt_linear_backward_bf16.hip",
+    "linear_backward_kernel[gmaps+prologue]": "ttt_linear_backward.hip",
+    "linear_backward_kernel[segments+prologue]": "ttt_linear_backward.hip",
+    "linear_backward_bf16_kernel[gmaps+prologue]": "ttt_linear_backward_bf16.hip",
+    "linear_backward_bf16_kernel[segments+prologue]": "ttt_linear_backward_bf16.hip",
     "linear_generic_kernel": "ttt_generic.hip",
     "mlp_generic_kernel": "ttt_generic.hip",
     "mlp_mfma_kernel": "ttt_mlp_mfma.hip",
@@ -278,19 +283,27 @@ class Runner:
             fwd, dec = total / steps, 0.0
         return wall / steps, fwd, dec
 
-    def measure_backward(self, steps, warmup):
+    def measure_backward(self, steps, warmup, prologue=False):
         """Mean duration of ttt_linear_backward over `steps` calls between two
-        synchronisations (HIP events on the launch stream at both ends)."""
+        synchronisations (HIP events on the launch stream at both ends); with
+        `prologue`, of ttt_linear_backward_ex through LayerNorm of q and k and
+        per-token step sizes."""
         torch, g, w = self.torch, self.g, self.w
-        from test_sequence_layers_linear_amd.inputs import make_cotangents
+        from test_sequence_layers_linear_amd.inputs import make_cotangents, make_prologue
         cot = {k: v.cuda() for k, v in make_cotangents(w, 7).items()}
         outs = dict(dQ=torch.empty_like(g["Q"]), dK=torch.empty_like(g["Q"]),
                     dV=torch.empty_like(g["Q"]), dW0=torch.empty_like(g["W0"]),
                     deta=torch.empty_like(g["eta"]))
+        pro = {k: v.cuda() for k, v in make_prologue(w, 11).items()}
 
         def call():
-            self.ttt.ttt_linear_backward(g["Q"], g["K"], g["V"], g["W0"], g["eta"], w.b,
-                                         cot["dY"], cot["dW_out"], **outs)
+            if prologue:
+                self.ttt.ttt_linear_backward_ex(g["Q"], g["K"], g["V"], g["W0"], pro["eta"], w.b,
+                                                cot["dY"], cot["dW_out"], eta_tok=pro["eta_tok"],
+                                                ln_q=pro["ln_q"], ln_k=pro["ln_k"])
+            else:
+                self.ttt.ttt_linear_backward(g["Q"], g["K"], g["V"], g["W0"], g["eta"], w.b,
+                                             cot["dY"], cot["dW_out"], **outs)
         for _ in range(warmup):
             call()
         torch.cuda.synchronize()
@@ -417,6 +430,9 @@ def measure_workload(cfg, steps, warmup, cold_reps):
         pt = r.measure_prologue(max(3, steps // 2), 2)
         out["prologue"] = {"us": pt * 1e6, "tokens_per_s": w.B * w.T / pt,
                            "vs_plain_forward": pt / fwd}
+        bpt = r.measure_backward(max(3, steps // 2), 2, prologue=True)
+        out["backward_prologue"] = {"us": bpt * 1e6, "tokens_per_s": w.B * w.T / bpt,
+                                    "vs_plain_backward": bpt / bt}
     if w.decode_steps:
         df, db = decode_work(w)
         per = dec / w.decode_steps

@@ -233,6 +233,48 @@ int ttt_linear_backward(const void* Q, const void* K, const void* V, int qkv_dty
                         void* dQ, void* dK, void* dV, float* dW0, float* deta,
                         void* stream);
 /*
+ * ttt_linear_backward with the input prologue of ttt_linear_forward_ex: the
+ * gradients of L = <dY, Y> + <dW_out, W_out> for (Y, W_out) =
+ * ttt_linear_forward_ex of the same arguments, so a model whose layer
+ * LayerNorms q and k (the TTT-Linear listing of the "Hardware
+ * Parallelization" section of the news.premlal.in page), learns a step size
+ * per token (the uTTT write-up on thelatestinai.com, Table D3) or reads out
+ * with the chunk-start weights (its Figure 2(a)) trains through this call.
+ * With Qn, Kn the LayerNorm'd rows, eta_t the step sizes and Et = diag(eta_t) E,
+ * per mini-batch in reverse order:
+ *     P  = A^T dY + Kn G,  dV = diag(eta_t) P,  deta_t = -<P_t, E_t>
+ *     dA = -tril(dY Et^T)          (A = 0 and dA = 0 with read_mode 1)
+ *     dQn = dY W^T + dA Kn,  dKn = -diag(eta_t) (P W^T + E G^T) + dA^T Qn
+ *     G <- G + Qn^T dY - Kn^T diag(eta_t) P
+ * and the LayerNorm backward takes dQn, dKn to the raw rows:
+ *     dx = rstd (g gamma - mean(g gamma) - xh mean(g gamma xh)),
+ *     dgamma += g xh, dbeta += g  (xh the normalised row, g its gradient).
+ *
+ *   Q, K            the raw rows (before the LayerNorm), as for
+ *                   ttt_linear_forward_ex; eta, eta_tok, ln_q, ln_k, ln_eps,
+ *                   read_mode: its prologue arguments (eta is read always).
+ *   deta_tok        fp32 [B][H][T], written: d L / d eta_tok.  Must be given
+ *                   exactly when eta_tok is; deta is then all zero.
+ *   dln_q, dln_k    fp32 [H][2][d] (gamma row, beta row), written: summed over
+ *                   the batch.  Must be given exactly when ln_q / ln_k are.
+ *   the rest        as for ttt_linear_backward (dQ, dK are the gradients of
+ *                   the raw rows; deta is the head step's gradient).
+ * d = 64 and b = 16 only.  Computed like ttt_linear_backward (bf16 Q/K/V:
+ * normalised rows rounded to bf16 for the MFMA operands; the LayerNorm and its
+ * backward in fp32).  The per-token eta gradients need no reduction; gamma,
+ * beta sums run over (batch, segment) in a fixed order: deterministic.
+ * TTT_ERR_INVALID_ARG also for a prologue input without its gradient output
+ * (or the reverse), ln_eps <= 0 with a LayerNorm, read_mode not 0 or 1, or
+ * any overlap of an output with another argument.
+ */
+int ttt_linear_backward_ex(const void* Q, const void* K, const void* V, int qkv_dtype,
+                           const float* W0, int w0_per_batch, const float* eta,
+                           const float* eta_tok, const float* ln_q, const float* ln_k,
+                           float ln_eps, int read_mode, int64_t B, int64_t H, int64_t T, int d,
+                           int b, const void* dY, const float* dW_out, void* dQ, void* dK,
+                           void* dV, float* dW0, float* deta, float* deta_tok, float* dln_q,
+                           float* dln_k, void* stream);
+/*
  * Number of sequence segments ttt_linear_backward would cut each chain into
  * for these sizes on the current device (1 = unsegmented).  Negative
  * ttt_status for arguments ttt_linear_backward would reject.

@@ -66,6 +66,9 @@ def load_library():
     lib.ttt_linear_backward.argtypes = [P, P, P, I, P, I, P, L, L, L, I, I, P, P,
                                         P, P, P, P, P, P]
     lib.ttt_linear_backward.restype = I
+    lib.ttt_linear_backward_ex.argtypes = [P, P, P, I, P, I, P, P, P, P, ctypes.c_float, I,
+                                           L, L, L, I, I, P, P, P, P, P, P, P, P, P, P, P]
+    lib.ttt_linear_backward_ex.restype = I
     lib.ttt_linear_backward_segments.argtypes = [L, L, L, I, I, I]
     lib.ttt_linear_backward_segments.restype = I
     lib.ttt_linear_segments.argtypes = [L, L, L, I, I, I]
@@ -293,6 +296,61 @@ def ttt_linear_backward(Q, K, V, W0, eta, b: int, dY, dW_out=None, dQ=None, dK=N
                                    dK.data_ptr(), dV.data_ptr(), dW0.data_ptr(), deta.data_ptr(),
                                    _stream_handle(dev, stream)))
     return dQ, dK, dV, dW0, deta
+
+
+def ttt_linear_backward_ex(Q, K, V, W0, eta, b: int, dY, dW_out=None, eta_tok=None, ln_q=None,
+                           ln_k=None, ln_eps: float = 1e-5, read_chunk_start: bool = False,
+                           stream=None):
+    """Gradients of <dY, Y> + <dW_out, W_out> for (Y, W_out) =
+    ttt_linear_forward_ex(Q, K, V, W0, eta, b, eta_tok, ln_q, ln_k, ln_eps,
+    read_chunk_start).  Returns a dict: dQ, dK, dV (of the raw rows, Q's
+    dtype), dW0 (shaped like W0, summed over the batch when shared), deta [H]
+    (zero when eta_tok is given), and deta_tok [B,H,T], dln_q, dln_k [H,2,d]
+    for the prologue inputs that are given."""
+    lib = load_library()
+    if Q.dim() != 4:
+        raise ValueError("Q must be [B,H,T,d]")
+    dev = Q.device
+    B, H, T, d = Q.shape
+    for t, n in ((Q, "Q"), (K, "K"), (V, "V"), (dY, "dY")):
+        _need(t, n, dev, Q.dtype)
+        if t.shape != Q.shape:
+            raise ValueError(f"{n} shape {tuple(t.shape)} != Q shape {tuple(Q.shape)}")
+    _need(W0, "W0", dev, torch.float32)
+    _need(eta, "eta", dev, torch.float32)
+    per_batch = W0.dim() == 4
+    if W0.shape != ((B, H, d, d) if per_batch else (H, d, d)) or eta.shape != (H,):
+        raise ValueError("W0 must be [H,d,d] or [B,H,d,d] and eta [H]")
+    if dW_out is None:
+        dW_out = torch.zeros((B, H, d, d), device=dev, dtype=torch.float32)
+    _need(dW_out, "dW_out", dev, torch.float32)
+    if dW_out.shape != (B, H, d, d):
+        raise ValueError("dW_out must be [B,H,d,d]")
+    out = {"dQ": torch.empty_like(Q), "dK": torch.empty_like(Q), "dV": torch.empty_like(Q),
+           "dW0": torch.empty_like(W0), "deta": torch.empty_like(eta)}
+    ins, grads = [], []
+    for t, n, shape in ((eta_tok, "eta_tok", (B, H, T)), (ln_q, "ln_q", (H, 2, d)),
+                        (ln_k, "ln_k", (H, 2, d))):
+        if t is None:
+            ins.append(None)
+            grads.append(None)
+            continue
+        _need(t, n, dev, torch.float32)
+        if t.shape != shape:
+            raise ValueError(f"{n} must be {list(shape)}, got {tuple(t.shape)}")
+        g = torch.empty(shape, device=dev, dtype=torch.float32)
+        out["d" + n] = g
+        ins.append(t.data_ptr())
+        grads.append(g.data_ptr())
+    _check(lib.ttt_linear_backward_ex(Q.data_ptr(), K.data_ptr(), V.data_ptr(), _dtype_code(Q),
+                                      W0.data_ptr(), int(per_batch), eta.data_ptr(), ins[0],
+                                      ins[1], ins[2], float(ln_eps), int(bool(read_chunk_start)),
+                                      B, H, T, d, int(b), dY.data_ptr(), dW_out.data_ptr(),
+                                      out["dQ"].data_ptr(), out["dK"].data_ptr(),
+                                      out["dV"].data_ptr(), out["dW0"].data_ptr(),
+                                      out["deta"].data_ptr(), grads[0], grads[1], grads[2],
+                                      _stream_handle(dev, stream)))
+    return out
 
 
 def ttt_linear_decode_step_ex(q, k, v, W, eta, eta_tok=None, ln_q=None, ln_k=None,

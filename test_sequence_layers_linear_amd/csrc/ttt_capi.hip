@@ -19,7 +19,7 @@ using ttt::LinearArgs;
 using ttt::MlpArgs;
 using ttt::DecodeArgs;
 
-constexpr int kAbiVersion = (1 << 16) | 1;
+constexpr int kAbiVersion = (1 << 16) | 2;
 
 bool valid_dtype(int dt) { return dt == TTT_F32 || dt == TTT_BF16; }
 size_t elem_bytes(int dt) { return dt == TTT_F32 ? 4 : 2; }
@@ -339,11 +339,17 @@ int ttt_linear_segments(int64_t B, int64_t H, int64_t T, int d, int b, int qkv_d
     return 1;
 }
 
-int ttt_linear_backward(const void* Q, const void* K, const void* V, int qkv_dtype,
-                        const float* W0, int w0_per_batch, const float* eta,
-                        int64_t B, int64_t H, int64_t T, int d, int b,
-                        const void* dY, const float* dW_out,
-                        void* dQ, void* dK, void* dV, float* dW0, float* deta, void* stream)
+}  // extern "C"
+
+namespace {
+
+int linear_backward_impl(const void* Q, const void* K, const void* V, int qkv_dtype,
+                         const float* W0, int w0_per_batch, const float* eta,
+                         int64_t B, int64_t H, int64_t T, int d, int b,
+                         const void* dY, const float* dW_out,
+                         void* dQ, void* dK, void* dV, float* dW0, float* deta,
+                         const ttt::Prologue& pro, float* deta_tok, float* dln_q, float* dln_k,
+                         void* stream)
 {
     if (B < 0 || H < 0 || T < 0 || b < 1 || (w0_per_batch != 0 && w0_per_batch != 1))
         return TTT_ERR_INVALID_ARG;
@@ -358,16 +364,25 @@ int ttt_linear_backward(const void* Q, const void* K, const void* V, int qkv_dty
     if (H > 0 && (!dW0 || !deta)) return TTT_ERR_INVALID_ARG;
     if (units > 0 && (!W0 || !eta || !dW_out)) return TTT_ERR_INVALID_ARG;
     if (units > 0 && T > 0 && (!Q || !K || !V || !dY || !dQ || !dK || !dV)) return TTT_ERR_INVALID_ARG;
+    // each prologue input comes with its gradient output
+    if ((pro.eta_tok != nullptr) != (deta_tok != nullptr) || (pro.ln_q != nullptr) != (dln_q != nullptr) ||
+        (pro.ln_k != nullptr) != (dln_k != nullptr))
+        return TTT_ERR_INVALID_ARG;
     if (H == 0) return TTT_OK;
 
     const int64_t nq = units > 0 && T > 0 ? n_qkv : 0;
+    const int64_t ntok = units > 0 && T > 0 ? units * T * 4 : 0;
+    const int64_t nln = H * 2 * d * 4;
     const Range rQ{Q, nq}, rK{K, nq}, rV{V, nq}, rdY{dY, nq};
     const Range rW0{W0, units > 0 ? (w0_per_batch ? units : H) * n_state : 0};
     const Range rEta{eta, units > 0 ? H * 4 : 0}, rdWo{dW_out, units * n_state};
+    const Range rEt{pro.eta_tok, ntok}, rLq{pro.ln_q, pro.ln_q ? nln : 0}, rLk{pro.ln_k, pro.ln_k ? nln : 0};
     const Range rdQ{dQ, nq}, rdK{dK, nq}, rdV{dV, nq};
     const Range rdW0{dW0, (w0_per_batch ? units : H) * n_state}, rdEta{deta, H * 4};
-    const Range outs[] = {rdQ, rdK, rdV, rdW0, rdEta};
-    const Range all[] = {rQ, rK, rV, rdY, rW0, rEta, rdWo, rdQ, rdK, rdV, rdW0, rdEta};
+    const Range rdEt{deta_tok, deta_tok ? ntok : 0}, rdLq{dln_q, dln_q ? nln : 0}, rdLk{dln_k, dln_k ? nln : 0};
+    const Range outs[] = {rdQ, rdK, rdV, rdW0, rdEta, rdEt, rdLq, rdLk};
+    const Range all[] = {rQ, rK, rV, rdY, rW0, rEta, rdWo, rEt, rLq, rLk,
+                         rdQ, rdK, rdV, rdW0, rdEta, rdEt, rdLq, rdLk};
     for (const Range& o : outs) {
         int hits = 0;   // an output overlaps itself once
         for (const Range& x : all)
@@ -377,6 +392,10 @@ int ttt_linear_backward(const void* Q, const void* K, const void* V, int qkv_dty
 
     ttt::LinearBwdArgs a{Q, K, V, qkv_dtype, W0, w0_per_batch, eta, B, H, T, d, b,
                          dY, dW_out, dQ, dK, dV, dW0, deta, static_cast<hipStream_t>(stream)};
+    a.pro = pro;
+    a.deta_tok = deta_tok;
+    a.dln_q = dln_q;
+    a.dln_k = dln_k;
     if (!ttt::linear_backward_supports(a)) return TTT_ERR_UNSUPPORTED;
     ttt::SegmentPlan p;
     if (units > 0)
@@ -386,6 +405,43 @@ int ttt_linear_backward(const void* Q, const void* K, const void* V, int qkv_dty
     if (workspace_get(&ws, ttt::linear_backward_workspace_bytes(a, p), a.stream) != hipSuccess)
         return TTT_ERR_HIP;
     return hip_status(ttt::launch_linear_backward(a, p, ws));
+}
+
+}  // namespace
+
+extern "C" {
+
+int ttt_linear_backward(const void* Q, const void* K, const void* V, int qkv_dtype,
+                        const float* W0, int w0_per_batch, const float* eta,
+                        int64_t B, int64_t H, int64_t T, int d, int b,
+                        const void* dY, const float* dW_out,
+                        void* dQ, void* dK, void* dV, float* dW0, float* deta, void* stream)
+{
+    return linear_backward_impl(Q, K, V, qkv_dtype, W0, w0_per_batch, eta, B, H, T, d, b, dY,
+                                dW_out, dQ, dK, dV, dW0, deta, ttt::Prologue{}, nullptr, nullptr,
+                                nullptr, stream);
+}
+
+int ttt_linear_backward_ex(const void* Q, const void* K, const void* V, int qkv_dtype,
+                           const float* W0, int w0_per_batch, const float* eta,
+                           const float* eta_tok, const float* ln_q, const float* ln_k,
+                           float ln_eps, int read_mode, int64_t B, int64_t H, int64_t T, int d,
+                           int b, const void* dY, const float* dW_out, void* dQ, void* dK,
+                           void* dV, float* dW0, float* deta, float* deta_tok, float* dln_q,
+                           float* dln_k, void* stream)
+{
+    if ((ln_q || ln_k) && !(ln_eps > 0.0f && ln_eps < 1e30f))
+        return TTT_ERR_INVALID_ARG;
+    if (read_mode != 0 && read_mode != 1)
+        return TTT_ERR_INVALID_ARG;
+    ttt::Prologue pro;
+    pro.eta_tok = eta_tok;
+    pro.ln_q = ln_q;
+    pro.ln_k = ln_k;
+    pro.ln_eps = ln_eps;
+    pro.read_start = read_mode;
+    return linear_backward_impl(Q, K, V, qkv_dtype, W0, w0_per_batch, eta, B, H, T, d, b, dY,
+                                dW_out, dQ, dK, dV, dW0, deta, pro, deta_tok, dln_q, dln_k, stream);
 }
 
 int ttt_linear_backward_segments(int64_t B, int64_t H, int64_t T, int d, int b, int qkv_dtype)

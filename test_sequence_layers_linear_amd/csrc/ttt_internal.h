@@ -101,6 +101,54 @@ __device__ __forceinline__ void layernorm_row(float (&x)[kN], const float (&gm)[
         x[i] = valid ? (x[i] - mean) * rstd * gm[i] + bt[i] : 0.f;
 }
 
+// The same LayerNorm keeping what its backward needs: xh = (x - mean) * rstd
+// (0 for a row that is not `valid`) and rstd.
+template <int kLanes, int kN>
+__device__ __forceinline__ void layernorm_row_keep(const float (&x)[kN], float eps, bool valid,
+                                                   float (&xh)[kN], float& rstd)
+{
+    static_assert(kLanes * kN == 64, "one 64-element row");
+    float sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < kN; ++i)
+        sum += x[i];
+    const float mean = group_sum<kLanes>(sum) * (1.0f / 64.0f);
+    float sq = 0.f;
+#pragma unroll
+    for (int i = 0; i < kN; ++i)
+        sq += (x[i] - mean) * (x[i] - mean);
+    rstd = rsqrtf(group_sum<kLanes>(sq) * (1.0f / 64.0f) + eps);
+#pragma unroll
+    for (int i = 0; i < kN; ++i)
+        xh[i] = valid ? (x[i] - mean) * rstd : 0.f;
+}
+
+// Backward of layernorm_row for one row spread like it: given the gradient
+// gy of the normalised row y = xh * gamma + beta, returns the gradient of the
+// raw row in gy and adds gy * xh, gy to the gamma, beta sums:
+//     dxh = gy gamma,  dx = rstd (dxh - mean(dxh) - xh mean(dxh xh)).
+template <int kLanes, int kN>
+__device__ __forceinline__ void layernorm_row_backward(float (&gy)[kN], const float (&xh)[kN],
+                                                       float rstd, const float (&gm)[kN],
+                                                       float (&dgamma)[kN], float (&dbeta)[kN])
+{
+    float dxh[kN];
+    float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+    for (int i = 0; i < kN; ++i) {
+        dgamma[i] += gy[i] * xh[i];
+        dbeta[i] += gy[i];
+        dxh[i] = gy[i] * gm[i];
+        s1 += dxh[i];
+        s2 += dxh[i] * xh[i];
+    }
+    s1 = group_sum<kLanes>(s1) * (1.0f / 64.0f);
+    s2 = group_sum<kLanes>(s2) * (1.0f / 64.0f);
+#pragma unroll
+    for (int i = 0; i < kN; ++i)
+        gy[i] = rstd * (dxh[i] - s1 - xh[i] * s2);
+}
+
 struct MlpArgs {
     const void* Q; const void* K; const void* V; int dtype;
     const float* W1_0; const float* W2_0; int w0_per_batch; const float* eta;
@@ -186,19 +234,31 @@ hipError_t launch_mlp_mfma(const MlpArgs& a);
 // segment's end cotangent, and then all segments run at once.  The workspace
 // holds those maps and states, the recomputed chunk-start states, and
 // per-chain dW0 (shared W0) and per-segment deta.
+// With the prologue on, Q and K are the raw rows (LayerNorm'd inside), the
+// step sizes are per token when pro.eta_tok is set (their gradients go to
+// deta_tok [B][H][T]; deta is then 0), and dln_q, dln_k [H][2][d] receive the
+// gradients of the LayerNorm gamma, beta rows (when ln_q, ln_k are set).
 struct LinearBwdArgs {
     const void* Q; const void* K; const void* V; int dtype;
     const float* W0; int w0_per_batch; const float* eta;
     int64_t B, H, T; int d, b;
     const void* dY; const float* dW_out;
     void* dQ; void* dK; void* dV; float* dW0; float* deta; hipStream_t stream;
+    Prologue pro{};
+    float* deta_tok = nullptr;
+    float* dln_q = nullptr;
+    float* dln_k = nullptr;
 };
 // Device buffers of one backward call (carved from the stream's workspace;
-// the segment maps and states only with several segments).
+// the segment maps and states only with several segments; the per-segment
+// LayerNorm gradient sums only with the prologue).
 struct BwdBuffers {
-    float *maps, *wstart, *gmaps, *gend, *states, *dw_chain, *deta_chain;
+    float *maps, *wstart, *gmaps, *gend, *states, *dw_chain, *deta_chain, *dln_chain;
     size_t bytes;
 };
+// Per-segment LayerNorm gradient sums: [B H][nseg][4][64] floats in the order
+// gamma_q, beta_q, gamma_k, beta_k.
+constexpr int kDlnRows = 4;
 // bf16 inputs on bf16 MFMA (ttt_linear_backward_bf16.hip): the cotangent maps
 // (gmap) or the segment backward, on the given grid.
 hipError_t launch_linear_backward_bf16(const LinearBwdArgs& a, const SegmentPlan& p, bool gmap,

@@ -49,6 +49,13 @@
 // padded to 68 floats so the 16 rows a 16-lane group reads fall in different
 // banks.  Tokens past T read as zero: they add nothing to any product, and
 // their rows are not stored.
+//
+// kPro: the input prologue, as in the bf16 kernel (ttt_linear_backward_bf16.hip):
+// Q, K LayerNorm'd while staged (the staging threads keep xh and 1/std),
+// per-token step sizes (E, P, dK, dV scale by row, dA by column), the
+// chunk-start read dropping A, and an epilogue in which the staging threads
+// apply the LayerNorm backward to dQ, dK of the normalised rows (through LDS),
+// store them and sum the gamma, beta gradients.  83 KB of LDS: one per CU.
 #include "ttt_internal.h"
 
 namespace ttt {
@@ -76,6 +83,17 @@ constexpr int kLdsFloats = kOffRed + kWaves;
 constexpr int kLdsBytes = kLdsFloats * 4;       // 74768
 constexpr int kGMapLdsBytes = 2 * kSlotFloats * 4;   // the cotangent maps use the slots only
 static_assert(2 * kLdsBytes <= kMaxLdsBytes, "two workgroups per CU");
+// prologue additions (floats), after the plain layout; the cotangent maps
+// put the slots' step sizes right after the slots
+constexpr int kOffEtaMain = kLdsFloats;          // [2 slots][16] eta_t
+constexpr int kOffEtaGMap = 2 * kSlotFloats;
+constexpr int kOffDQ = kOffEtaMain + 2 * kB;     // [16][kP] dQ of the normalised rows
+constexpr int kOffDK = kOffDQ + kTile;
+constexpr int kOffDeta = kOffDK + kTile;         // [4 waves][16]
+constexpr int kProLdsBytes = (kOffDeta + kWaves * kB) * 4;
+constexpr int kProGMapLdsBytes = (kOffEtaGMap + 2 * kB) * 4;
+static_assert(kProLdsBytes <= kMaxLdsBytes, "one workgroup per CU");
+static_assert(kWaves * 4 * kD <= 2 * kTile, "the gamma/beta reduction fits the dQ, dK tiles");
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -117,7 +135,22 @@ struct Stage {
     typename Raw<In>::type q, k, dy;
     In v[4];           // V[4g + r][16w + c]: this lane's entries of its wave's columns
     f32x4 w[4];
+    float eta;         // kPro: the step size of row tid / 16 (0 past T)
+    bool ok;           // row tid / 16 is a token (< T)
 };
+
+// four consecutive outputs of a row: 16 bytes (fp32) or 8 bytes (bf16)
+__device__ __forceinline__ void store_row4(float* p, const float (&x)[4])
+{
+    *reinterpret_cast<f32x4*>(p) = f32x4{x[0], x[1], x[2], x[3]};
+}
+__device__ __forceinline__ void store_row4(uint16_t* p, const float (&x)[4])
+{
+    *reinterpret_cast<u32x2*>(p) = u32x2{static_cast<uint32_t>(f32_to_bf16_bits(x[0])) |
+                                             (static_cast<uint32_t>(f32_to_bf16_bits(x[1])) << 16),
+                                         static_cast<uint32_t>(f32_to_bf16_bits(x[2])) |
+                                             (static_cast<uint32_t>(f32_to_bf16_bits(x[3])) << 16)};
+}
 
 __device__ __forceinline__ f32x4 lds4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
 __device__ __forceinline__ void lds4(float* p, f32x4 x) { *reinterpret_cast<f32x4*>(p) = x; }
@@ -132,8 +165,8 @@ __device__ __forceinline__ void lds4(float* p, f32x4 x) { *reinterpret_cast<f32x
 //   G_start = M^G G_end + N^G (M^G from G_end = I with dY = 0, block half 0;
 //   N^G from G_end = 0 with the segment's dY, half 1), stored in the order
 //   the composition runs: gmaps[u][nseg - 1 - s][half].  No W is needed.
-template <typename In, bool kGMap>
-__global__ void __launch_bounds__(kThreads, 2)
+template <typename In, bool kGMap, bool kPro>
+__global__ void __launch_bounds__(kThreads, kPro && !kGMap ? 1 : 2)
 linear_backward_kernel(const In* __restrict__ Q, const In* __restrict__ K, const In* __restrict__ V,
                        const float* __restrict__ W0, int w0_per_batch,
                        const float* __restrict__ eta, int H, int T, int64_t units, int seg_len,
@@ -141,7 +174,8 @@ linear_backward_kernel(const In* __restrict__ Q, const In* __restrict__ K, const
                        const In* __restrict__ dY, const float* __restrict__ dW_out,
                        In* __restrict__ dQ, In* __restrict__ dK, In* __restrict__ dV,
                        float* __restrict__ dW0_chain, float* __restrict__ deta_chain,
-                       float* __restrict__ states, float* __restrict__ gmaps)
+                       float* __restrict__ states, float* __restrict__ gmaps,
+                       Prologue pro, float* __restrict__ deta_tok, float* __restrict__ dln_chain)
 {
     extern __shared__ __attribute__((aligned(16))) float lds[];
 
@@ -176,10 +210,42 @@ linear_backward_kernel(const In* __restrict__ Q, const In* __restrict__ K, const
     // each 16 x 64 tile, and rows tid / 16 + 16 q of W
     const int srow = tid >> 4;
     const int scol = 4 * (tid & 15);
+
+    // prologue state of this staging thread (as in the bf16 kernel)
+    const bool use_tok = kPro && pro.eta_tok != nullptr;
+    const bool ln_q = kPro && pro.ln_q != nullptr;
+    const bool ln_k = kPro && pro.ln_k != nullptr;
+    const bool a_on = !kPro || !pro.read_start;      // uniform: the tril(Q K^T) term
+    float* const etas = lds + (kGMap ? kOffEtaGMap : kOffEtaMain);
+    float gmq[4], btq[4], gmk[4], btk[4];
+    float xq[4] = {}, xk[4] = {}, rq = 1.f, rk = 1.f;
+    float dgq[4] = {}, dbq[4] = {}, dgk[4] = {}, dbk[4] = {};
+    if constexpr (kPro) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            gmq[e] = ln_q ? pro.ln_q[(2 * h) * kD + scol + e] : 1.f;
+            btq[e] = ln_q ? pro.ln_q[(2 * h + 1) * kD + scol + e] : 0.f;
+            gmk[e] = ln_k ? pro.ln_k[(2 * h) * kD + scol + e] : 1.f;
+            btk[e] = ln_k ? pro.ln_k[(2 * h + 1) * kD + scol + e] : 0.f;
+        }
+    }
+    auto norm = [&](f32x4 x, const float (&gm)[4], const float (&bt)[4], bool valid,
+                    float (&xh)[4], float& rstd) {
+        const float f[4] = {x[0], x[1], x[2], x[3]};
+        layernorm_row_keep<16, 4>(f, pro.ln_eps, valid, xh, rstd);
+        f32x4 y;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            y[e] = valid ? xh[e] * gm[e] + bt[e] : 0.f;
+        return y;
+    };
     auto load_stage = [&](Stage<In>& x, int chunk, bool qdy, bool wst) {
         const int t = chunk * kB + srow;
         const bool ok = t < T;
         const int64_t e = off + static_cast<int64_t>(t) * kD + scol;
+        x.ok = ok;
+        if constexpr (kPro)
+            x.eta = !ok ? 0.f : use_tok ? pro.eta_tok[u * T + t] : et;
         x.k = Raw<In>::load(K + e, ok);
         if (!kGMap) {
 #pragma unroll
@@ -201,11 +267,30 @@ linear_backward_kernel(const In* __restrict__ Q, const In* __restrict__ K, const
     };
     auto store_stage = [&](const Stage<In>& x, int slot, bool qdy) {
         float* sl = lds + slot * kSlotFloats;
-        lds4(sl + kSlotK + srow * kP + scol, Raw<In>::to_f32(x.k));
+        f32x4 kx = Raw<In>::to_f32(x.k);
+        if constexpr (kPro) {
+            if (ln_k)
+                kx = norm(kx, gmk, btk, x.ok, xk, rk);
+            if ((tid & 15) == 0)
+                etas[slot * kB + srow] = x.eta;
+        }
+        lds4(sl + kSlotK + srow * kP + scol, kx);
         if (qdy) {
-            lds4(sl + kSlotQ + srow * kP + scol, Raw<In>::to_f32(x.q));
+            f32x4 qx = Raw<In>::to_f32(x.q);
+            if constexpr (kPro) {
+                if (ln_q)
+                    qx = norm(qx, gmq, btq, x.ok, xq, rq);
+            }
+            lds4(sl + kSlotQ + srow * kP + scol, qx);
             lds4(sl + kSlotDY + srow * kP + scol, Raw<In>::to_f32(x.dy));
         }
+    };
+    // step sizes of rows 4g .. 4g + 3 of a slot (the head's without the prologue)
+    auto rows_eta = [&](int slot) {
+        if constexpr (kPro)
+            return lds4(etas + slot * kB + 4 * g);
+        else
+            return f32x4{et, et, et, et};
     };
     auto store_w = [&](const Stage<In>& x) {
 #pragma unroll
@@ -264,7 +349,7 @@ linear_backward_kernel(const In* __restrict__ Q, const In* __restrict__ K, const
             const float* sl = lds + ((ch - c0) & 1) * kSlotFloats;
             f32x4 krow[4];
             const f32x4 E = residual(sl, Wt, vcur, krow);
-            const f32x4 En = -et * E;
+            const f32x4 En = -(rows_eta((ch - c0) & 1) * E);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 f32x4 acc = {Wt[i][0], Wt[i][1], Wt[i][2], Wt[i][3]};
@@ -353,6 +438,11 @@ linear_backward_kernel(const In* __restrict__ Q, const In* __restrict__ K, const
         f32x4 pacc[4] = {};
         float dyc[4] = {0.f, 0.f, 0.f, 0.f};
         if (use_dy) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                dyc[r] = sl[kSlotDY + (4 * g + r) * kP + 16 * w + c];
+        }
+        if (use_dy && a_on) {
             f32x4 qrow[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i)
@@ -369,9 +459,6 @@ linear_backward_kernel(const In* __restrict__ Q, const In* __restrict__ K, const
                 S[r] = c <= 4 * g + r ? S[r] : 0.f;
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                dyc[r] = sl[kSlotDY + (4 * g + r) * kP + 16 * w + c];
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
                 pacc[0] = mfma(S[r], dyc[r], pacc[0]);
         }
 #pragma unroll
@@ -380,11 +467,19 @@ linear_backward_kernel(const In* __restrict__ Q, const In* __restrict__ K, const
             for (int i = 0; i < 4; ++i)
                 pacc[i] = mfma(krow[i][r], Gt[i][r], pacc[i]);
         const f32x4 P = (pacc[0] + pacc[1]) + (pacc[2] + pacc[3]);
-        const f32x4 dE = -et * P;
+        const f32x4 er = rows_eta(slot);                  // eta of rows 4g + r
+        const f32x4 dE = -(er * P);
         if (!kGMap) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                deta_acc -= P[r] * E[r];
+                if (use_tok) {
+                    // -<P_t, E_t> over this wave's 16 columns
+                    const float pe = group_sum<16>(P[r] * E[r]);
+                    if (c == 0)
+                        lds[kOffDeta + w * kB + 4 * g + r] = pe;
+                } else {
+                    deta_acc -= P[r] * E[r];
+                }
                 Es[(4 * g + r) * kP + 16 * w + c] = E[r];
                 Ps[(4 * g + r) * kP + 16 * w + c] = P[r];
             }
@@ -424,20 +519,25 @@ linear_backward_kernel(const In* __restrict__ Q, const In* __restrict__ K, const
                 dyrow[jb] = lds4(sl + kSlotDY + c * kP + 16 * jb + 4 * g);
                 erow[jb] = lds4(Es + c * kP + 16 * jb + 4 * g);
             }
-            f32x4 aacc[4] = {};
+            f32x4 dA = {0.f, 0.f, 0.f, 0.f};
+            if (a_on) {
+                f32x4 aacc[4] = {};
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
+                for (int r = 0; r < 4; ++r)
 #pragma unroll
-                for (int jb = 0; jb < 4; ++jb)
-                    aacc[jb] = mfma(dyrow[jb][r], erow[jb][r], aacc[jb]);
-            f32x4 dA = (aacc[0] + aacc[1]) + (aacc[2] + aacc[3]);
+                    for (int jb = 0; jb < 4; ++jb)
+                        aacc[jb] = mfma(dyrow[jb][r], erow[jb][r], aacc[jb]);
+                dA = (aacc[0] + aacc[1]) + (aacc[2] + aacc[3]);
+                // dA[t][s] scales by eta_s (s = c)
+                const float ec = kPro ? etas[slot * kB + c] : et;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                dA[r] = c <= 4 * g + r ? -et * dA[r] : 0.f;
-                dAs[(4 * g + r) * kDAP + c] = dA[r];
+                for (int r = 0; r < 4; ++r) {
+                    dA[r] = c <= 4 * g + r ? -ec * dA[r] : 0.f;
+                    dAs[(4 * g + r) * kDAP + c] = dA[r];
+                }
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             }
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             // dQ_I = dY W[I, :]^T + dA K_I
             f32x4 qacc[4] = {};
 #pragma unroll
@@ -445,7 +545,7 @@ linear_backward_kernel(const In* __restrict__ Q, const In* __restrict__ K, const
 #pragma unroll
                 for (int jb = 0; jb < 4; ++jb)
                     qacc[jb] = mfma(dyrow[jb][r], wrow[jb][r], qacc[jb]);
-            {
+            if (a_on) {
                 const f32x4 darow = lds4(dAs + c * kDAP + 4 * g);
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
@@ -464,10 +564,13 @@ linear_backward_kernel(const In* __restrict__ Q, const In* __restrict__ K, const
                     kacc[jb] = mfma(erow[jb][r], grow[r], kacc[jb]);
                 }
             }
-            f32x4 dk = -et * ((kacc[0] + kacc[1]) + (kacc[2] + kacc[3]));
+            // rows t = 4g + r: the step sizes of phase A's rows
+            f32x4 dk = -(er * ((kacc[0] + kacc[1]) + (kacc[2] + kacc[3])));
+            if (a_on) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                dk = mfma(dA[r], sl[kSlotQ + (4 * g + r) * kP + 16 * w + c], dk);
+                for (int r = 0; r < 4; ++r)
+                    dk = mfma(dA[r], sl[kSlotQ + (4 * g + r) * kP + 16 * w + c], dk);
+            }
 
             // stores: rows t = 16 ch + 4g + r, column 16 w + c (P of phase A is
             // this wave's column block, so dV = eta P needs no exchange)
@@ -476,9 +579,45 @@ linear_backward_kernel(const In* __restrict__ Q, const In* __restrict__ K, const
                 const int t = ch * kB + 4 * g + r;
                 if (t < T) {
                     const int64_t e = off + static_cast<int64_t>(t) * kD + 16 * w + c;
-                    store_elem(dQ, e, dq[r]);
-                    store_elem(dK, e, dk[r]);
-                    store_elem(dV, e, et * P[r]);
+                    if constexpr (!kPro) {
+                        store_elem(dQ, e, dq[r]);
+                        store_elem(dK, e, dk[r]);
+                    }
+                    store_elem(dV, e, er[r] * P[r]);
+                }
+            }
+            if constexpr (kPro) {
+                // the gradients of the normalised rows go to the staging
+                // threads for the LayerNorm backward
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    lds[kOffDQ + (4 * g + r) * kP + 16 * w + c] = dq[r];
+                    lds[kOffDK + (4 * g + r) * kP + 16 * w + c] = dk[r];
+                }
+                __syncthreads();
+                float gq[4], gk[4];
+                {
+                    const f32x4 a = lds4(lds + kOffDQ + srow * kP + scol);
+                    const f32x4 b = lds4(lds + kOffDK + srow * kP + scol);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        gq[e] = a[e];
+                        gk[e] = b[e];
+                    }
+                }
+                if (ln_q)
+                    layernorm_row_backward<16, 4>(gq, xq, rq, gmq, dgq, dbq);
+                if (ln_k)
+                    layernorm_row_backward<16, 4>(gk, xk, rk, gmk, dgk, dbk);
+                const int t = ch * kB + srow;
+                if (t < T) {
+                    const int64_t e = off + static_cast<int64_t>(t) * kD + scol;
+                    store_row4(dQ + e, gq);
+                    store_row4(dK + e, gk);
+                    if (use_tok && (tid & 15) == 0) {
+                        const float* pd = lds + kOffDeta;
+                        deta_tok[u * T + t] = -((pd[srow] + pd[kB + srow]) + (pd[2 * kB + srow] + pd[3 * kB + srow]));
+                    }
                 }
             }
         }
@@ -516,20 +655,57 @@ linear_backward_kernel(const In* __restrict__ Q, const In* __restrict__ K, const
         deta_acc += __shfl_xor(deta_acc, m);
     if (lane == 0)
         lds[kOffRed + w] = deta_acc;
-    __syncthreads();
+    if constexpr (kPro) {
+        // gamma, beta gradients: over the 4 rows of the wave (lanes 16 apart),
+        // then over the waves; out[a][col], a = gamma_q, beta_q, gamma_k, beta_k
+        float* lr = lds + kOffDQ;                        // [4 waves][4][64]
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float v4[4] = {dgq[e], dbq[e], dgk[e], dbk[e]};
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                float x = v4[a];
+                x += __shfl_xor(x, 16);
+                x += __shfl_xor(x, 32);
+                if (lane < 16)
+                    lr[(w * 4 + a) * kD + scol + e] = x;
+            }
+        }
+        __syncthreads();
+        dln_chain[(u * nseg + s) * (kDlnRows * kD) + tid] =
+            (lr[tid] + lr[256 + tid]) + (lr[512 + tid] + lr[768 + tid]);
+    } else {
+        __syncthreads();
+    }
     if (tid == 0)
         deta_chain[u * nseg + s] = (lds[kOffRed] + lds[kOffRed + 1]) + (lds[kOffRed + 2] + lds[kOffRed + 3]);
 }
 
 // Sums in a fixed order: dW0 over the batch (when W0 is shared by the batch)
 // and deta over the batch and the segments (always: eta is one value per head).
+// With the prologue also the LayerNorm gamma, beta gradients over the batch
+// and the segments: dln_q, dln_k [H][2][64] from dln_chain [B H][nseg][4][64].
 __global__ void __launch_bounds__(256)
 linear_backward_reduce_kernel(const float* __restrict__ dW0_chain, const float* __restrict__ deta_chain,
                               int64_t B, int H, int nseg, int reduce_w, float* __restrict__ dW0,
-                              float* __restrict__ deta)
+                              float* __restrict__ deta, const float* __restrict__ dln_chain,
+                              float* __restrict__ dln_q, float* __restrict__ dln_k)
 {
     const int64_t x = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
     const int64_t n = static_cast<int64_t>(H) * kD * kD;
+    if (dln_chain && x < static_cast<int64_t>(H) * kDlnRows * kD) {
+        const int hh = static_cast<int>(x / (kDlnRows * kD));
+        const int a = static_cast<int>(x / kD) % kDlnRows;      // gamma_q, beta_q, gamma_k, beta_k
+        const int col = static_cast<int>(x % kD);
+        float* out = a < 2 ? dln_q : dln_k;
+        if (out) {
+            float acc = 0.f;
+            for (int64_t bb = 0; bb < B; ++bb)
+                for (int sg = 0; sg < nseg; ++sg)
+                    acc += dln_chain[((bb * H + hh) * nseg + sg) * (kDlnRows * kD) + a * kD + col];
+            out[(2 * hh + (a & 1)) * kD + col] = acc;
+        }
+    }
     if (reduce_w && x < n) {
         float acc = 0.f;
         for (int64_t bb = 0; bb < B; ++bb)
@@ -583,30 +759,46 @@ BwdWorkspace carve(const LinearBwdArgs& a, const SegmentPlan& p, void* base)
     w.states = take(units * S * seg_chunks * st);
     w.dw_chain = a.w0_per_batch ? a.dW0 : take(units * st);
     w.deta_chain = take(units * S);
+    w.dln_chain = a.pro.active() ? take(units * S * kDlnRows * kD) : nullptr;
     w.bytes = o * sizeof(float);
     return w;
 }
 
-template <typename In, bool kGMap>
+template <typename In, bool kGMap, bool kPro>
 void launch_kernel(const LinearBwdArgs& a, const SegmentPlan& p, const BwdWorkspace& w, dim3 grid)
 {
-    hipLaunchKernelGGL((linear_backward_kernel<In, kGMap>), grid, dim3(kThreads),
-                       kGMap ? kGMapLdsBytes : kLdsBytes, a.stream,
-                       static_cast<const In*>(a.Q), static_cast<const In*>(a.K),
+    const int lds = kPro ? (kGMap ? kProGMapLdsBytes : kProLdsBytes)
+                         : (kGMap ? kGMapLdsBytes : kLdsBytes);
+    hipLaunchKernelGGL((linear_backward_kernel<In, kGMap, kPro>), grid, dim3(kThreads), lds,
+                       a.stream, static_cast<const In*>(a.Q), static_cast<const In*>(a.K),
                        static_cast<const In*>(a.V), a.W0, a.w0_per_batch, a.eta,
                        static_cast<int>(a.H), static_cast<int>(a.T), a.B * a.H,
                        static_cast<int>(p.seg_len), p.nseg, w.wstart, w.gend,
                        static_cast<const In*>(a.dY), a.dW_out, static_cast<In*>(a.dQ),
                        static_cast<In*>(a.dK), static_cast<In*>(a.dV), w.dw_chain, w.deta_chain,
-                       w.states, w.gmaps);
+                       w.states, w.gmaps, a.pro, a.deta_tok, w.dln_chain);
+}
+
+template <typename In, bool kGMap>
+void launch_kernel(const LinearBwdArgs& a, const SegmentPlan& p, const BwdWorkspace& w, dim3 grid)
+{
+    if (a.pro.active())
+        launch_kernel<In, kGMap, true>(a, p, w, grid);
+    else
+        launch_kernel<In, kGMap, false>(a, p, w, grid);
 }
 
 template <typename In>
 hipError_t set_lds()
 {
-    for (const void* f : {reinterpret_cast<const void*>(linear_backward_kernel<In, false>),
-                          reinterpret_cast<const void*>(linear_backward_kernel<In, true>)}) {
-        const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+    const struct { const void* f; int bytes; } k[] = {
+        {reinterpret_cast<const void*>(linear_backward_kernel<In, false, false>), kLdsBytes},
+        {reinterpret_cast<const void*>(linear_backward_kernel<In, true, false>), kGMapLdsBytes},
+        {reinterpret_cast<const void*>(linear_backward_kernel<In, false, true>), kProLdsBytes},
+        {reinterpret_cast<const void*>(linear_backward_kernel<In, true, true>), kProGMapLdsBytes},
+    };
+    for (const auto& x : k) {
+        const hipError_t e = hipFuncSetAttribute(x.f, hipFuncAttributeMaxDynamicSharedMemorySize, x.bytes);
         if (e != hipSuccess)
             return e;
     }
@@ -636,8 +828,9 @@ hipError_t launch_linear_backward(const LinearBwdArgs& a, const SegmentPlan& pla
         return e;
     if (units > 0 && p.nseg > 1) {
         // start state of every segment: the forward's maps and composition
-        const LinearArgs fa{a.Q, a.K, a.V, a.dtype, a.W0, a.w0_per_batch, a.eta, a.B, a.H, a.T,
-                            a.d, a.b, nullptr, nullptr, a.stream};
+        LinearArgs fa{a.Q, a.K, a.V, a.dtype, a.W0, a.w0_per_batch, a.eta, a.B, a.H, a.T,
+                      a.d, a.b, nullptr, nullptr, a.stream};
+        fa.pro = a.pro;
         SegmentPlan fp = p;
         fp.maps = w.maps;
         fp.wstart = w.wstart;
@@ -676,10 +869,13 @@ hipError_t launch_linear_backward(const LinearBwdArgs& a, const SegmentPlan& pla
         if (e != hipSuccess)
             return e;
     }
-    const int64_t n = a.w0_per_batch ? a.H : a.H * kD * kD;
+    int64_t n = a.w0_per_batch ? a.H : a.H * kD * kD;
+    if (a.pro.active())
+        n = n > a.H * kDlnRows * kD ? n : a.H * kDlnRows * kD;
     hipLaunchKernelGGL(linear_backward_reduce_kernel, dim3(static_cast<unsigned>((n + 255) / 256)),
                        dim3(256), 0, a.stream, w.dw_chain, w.deta_chain, a.B, static_cast<int>(a.H),
-                       p.nseg, a.w0_per_batch ? 0 : 1, a.dW0, a.deta);
+                       p.nseg, a.w0_per_batch ? 0 : 1, a.dW0, a.deta, w.dln_chain, a.dln_q,
+                       a.dln_k);
     return hipGetLastError();
 }
 

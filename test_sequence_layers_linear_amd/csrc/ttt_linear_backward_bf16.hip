@@ -31,6 +31,16 @@
 // by lane 4k + i / 4 as its element k, so lanes addressing rows r0 + j / 4 at
 // columns x0 + 4 (j % 4) hand lane i the 4 values X[r0 .. r0 + 3][x0 + i].
 // The chunk-start states go to the workspace as bf16 W^T (8 KB per chunk).
+//
+// kPro: the input prologue.  Raw Q, K rows are LayerNorm'd (per-head gamma,
+// beta over the 64-wide head dim) as they are staged into LDS, keeping the
+// normalised rows xh and 1/std per row in the staging threads' registers; a
+// step size per token eta_t replaces the head's (E and P scale by row, dA by
+// column: dA[t][s] = -eta_s dY_t . E_s); the chunk-start read drops A.  dQ and
+// dK of the normalised rows go through LDS to the staging threads, which apply
+// the LayerNorm backward to their row segment, store the raw-row gradients
+// and sum the gamma, beta gradients; per-token deta_t = -<P_t, E_t> is summed
+// over the columns of each wave and then over the waves.
 #include "ttt_internal.h"
 
 namespace ttt {
@@ -47,13 +57,27 @@ constexpr int kSlotQ = 0;
 constexpr int kSlotK = kTileB;
 constexpr int kSlotDY = 2 * kTileB;
 constexpr int kSlotBytes = 3 * kTileB;
-constexpr int kOffW = 2 * kSlotBytes;           // W_c^T [64 j][64 i]
-constexpr int kOffE = kOffW + kMatB;            // E  [16][64]
-constexpr int kOffP = kOffE + kTileB;           // P  [16][64]
-constexpr int kOffG = kOffP + kTileB;           // G'^T [64 j][64 i]
-constexpr int kOffRed = kOffG + kMatB;
-constexpr int kLdsBytes = kOffRed + 16;         // 32784
-constexpr int kGMapLdsBytes = 2 * kSlotBytes;   // the cotangent maps use the slots only
+constexpr int kFP = 68;                         // padded fp32 row of the dQ, dK tiles
+
+// LDS layout (bytes); kPro adds the slots' step sizes, the fp32 dQ, dK tiles
+// of the normalised rows and the per-wave deta_t partial sums.
+template <bool kPro>
+struct Lay {
+    static constexpr int kEta = 2 * kSlotBytes;            // [2 slots][16] eta_t (kPro)
+    static constexpr int kW = kEta + (kPro ? 2 * kB * 4 : 0);   // W_c^T [64 j][64 i]
+    static constexpr int kE = kW + kMatB;                  // E  [16][64]
+    static constexpr int kP = kE + kTileB;                 // P  [16][64]
+    static constexpr int kG = kP + kTileB;                 // G'^T [64 j][64 i]
+    static constexpr int kRed = kG + kMatB;                // [4] deta partials
+    static constexpr int kDQ = kRed + 16;                  // [16][kFP] fp32 (kPro)
+    static constexpr int kDK = kDQ + kB * kFP * 4;
+    static constexpr int kDeta = kDK + kB * kFP * 4;       // [4 waves][16] (kPro)
+    static constexpr int kBytes = kPro ? kDeta + kWaves * kB * 4 : kRed + 16;
+    static constexpr int kGMapBytes = kW;                  // the cotangent maps use the slots only
+};
+static_assert(Lay<false>::kBytes == 32784, "plain layout");
+static_assert(2 * Lay<true>::kBytes <= kMaxLdsBytes, "two workgroups per CU");
+static_assert(kWaves * 4 * kD * 4 <= 2 * kB * kFP * 4, "the gamma/beta reduction fits the dQ, dK tiles");
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -131,9 +155,19 @@ struct Stage {
     u32x2 q, k, dy;    // 4 bf16 of row tid / 16, columns 4 (tid % 16) .. +3
     uint16_t v[4];     // V[4g + r][16w + c]: this lane's entries of its wave's columns
     u32x4 w[2];        // W_c^T row tid / 4, segments 2 (tid % 4), +1
+    float eta;         // kPro: the step size of row tid / 16 (0 past T)
+    bool ok;           // row tid / 16 is a token (< T)
 };
 
-template <bool kGMap>
+__device__ __forceinline__ void unpack4(u32x2 x, float (&f)[4])
+{
+    f[0] = __uint_as_float(x[0] << 16);
+    f[1] = __uint_as_float(x[0] & 0xffff0000u);
+    f[2] = __uint_as_float(x[1] << 16);
+    f[3] = __uint_as_float(x[1] & 0xffff0000u);
+}
+
+template <bool kGMap, bool kPro>
 __global__ void __launch_bounds__(kThreads, 2)
 linear_backward_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                             const uint16_t* __restrict__ V, const float* __restrict__ W0,
@@ -143,9 +177,12 @@ linear_backward_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __re
                             const float* __restrict__ dW_out, uint16_t* __restrict__ dQ,
                             uint16_t* __restrict__ dK, uint16_t* __restrict__ dV,
                             float* __restrict__ dW0_chain, float* __restrict__ deta_chain,
-                            uint16_t* __restrict__ states, float* __restrict__ gmaps)
+                            uint16_t* __restrict__ states, float* __restrict__ gmaps,
+                            Prologue pro, float* __restrict__ deta_tok, float* __restrict__ dln_chain)
 {
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+    using L = Lay<kPro>;
+    constexpr int kOffW = L::kW, kOffE = L::kE, kOffP = L::kP, kOffG = L::kG, kOffRed = L::kRed;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -179,10 +216,44 @@ linear_backward_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __re
     const int srow = tid >> 4;
     const int scol = 4 * (tid & 15);
     const int sbyte = swz(srow, scol >> 3) + 8 * (tid & 1);
+
+    // prologue state of this staging thread: gamma, beta of its 4 columns,
+    // the normalised rows and 1/std of the chunk last staged (its epilogue
+    // runs before the next chunk is staged), and the gamma, beta gradients
+    const bool use_tok = kPro && pro.eta_tok != nullptr;
+    const bool ln_q = kPro && pro.ln_q != nullptr;
+    const bool ln_k = kPro && pro.ln_k != nullptr;
+    const bool a_on = !kPro || !pro.read_start;      // uniform: the tril(Q K^T) term
+    float gmq[4], btq[4], gmk[4], btk[4];
+    float xq[4] = {}, xk[4] = {}, rq = 1.f, rk = 1.f;
+    float dgq[4] = {}, dbq[4] = {}, dgk[4] = {}, dbk[4] = {};
+    if constexpr (kPro) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            gmq[e] = ln_q ? pro.ln_q[(2 * h) * kD + scol + e] : 1.f;
+            btq[e] = ln_q ? pro.ln_q[(2 * h + 1) * kD + scol + e] : 0.f;
+            gmk[e] = ln_k ? pro.ln_k[(2 * h) * kD + scol + e] : 1.f;
+            btk[e] = ln_k ? pro.ln_k[(2 * h + 1) * kD + scol + e] : 0.f;
+        }
+    }
+    // LayerNorm of a staged row segment, back to bf16; keeps xh and 1/std
+    auto norm = [&](u32x2 x, const float (&gm)[4], const float (&bt)[4], bool valid,
+                    float (&xh)[4], float& rstd) {
+        float f[4];
+        unpack4(x, f);
+        layernorm_row_keep<16, 4>(f, pro.ln_eps, valid, xh, rstd);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            f[e] = valid ? xh[e] * gm[e] + bt[e] : 0.f;
+        return u32x2{cvt2(f[0], f[1]), cvt2(f[2], f[3])};
+    };
     auto load_stage = [&](Stage& x, int chunk, bool qdy, bool wst) {
         const int t = chunk * kB + srow;
         const bool ok = t < T;
         const int64_t e = off + static_cast<int64_t>(t) * kD + scol;
+        x.ok = ok;
+        if constexpr (kPro)
+            x.eta = !ok ? 0.f : use_tok ? pro.eta_tok[u * T + t] : et;
         x.k = ok ? *reinterpret_cast<const u32x2*>(K + e) : u32x2{0u, 0u};
         if (qdy) {
             x.q = ok ? *reinterpret_cast<const u32x2*>(Q + e) : u32x2{0u, 0u};
@@ -202,13 +273,30 @@ linear_backward_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __re
                 x.w[q] = *reinterpret_cast<const u32x4*>(src + 8 * (2 * (tid & 3) + q));
         }
     };
+    // (with the prologue: LayerNorm first, and the rows' step sizes)
     auto store_stage = [&](const Stage& x, int slot, bool qdy) {
         unsigned char* sl = lds + slot * kSlotBytes;
-        *reinterpret_cast<u32x2*>(sl + kSlotK + sbyte) = x.k;
+        u32x2 kx = x.k, qx = x.q;
+        if constexpr (kPro) {
+            if (ln_k)
+                kx = norm(x.k, gmk, btk, x.ok, xk, rk);
+            if (qdy && ln_q)
+                qx = norm(x.q, gmq, btq, x.ok, xq, rq);
+            if ((tid & 15) == 0)
+                reinterpret_cast<float*>(lds + L::kEta)[slot * kB + srow] = x.eta;
+        }
+        *reinterpret_cast<u32x2*>(sl + kSlotK + sbyte) = kx;
         if (qdy) {
-            *reinterpret_cast<u32x2*>(sl + kSlotQ + sbyte) = x.q;
+            *reinterpret_cast<u32x2*>(sl + kSlotQ + sbyte) = qx;
             *reinterpret_cast<u32x2*>(sl + kSlotDY + sbyte) = x.dy;
         }
+    };
+    // step sizes of rows 4g .. 4g + 3 of a slot (the head's without the prologue)
+    auto rows_eta = [&](int slot) {
+        if constexpr (kPro)
+            return *reinterpret_cast<const f32x4*>(lds + L::kEta + 4 * (slot * kB + 4 * g));
+        else
+            return f32x4{et, et, et, et};
     };
     auto store_w = [&](const Stage& x) {
 #pragma unroll
@@ -257,7 +345,7 @@ linear_backward_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __re
             // E = K W_J - V, W += K^T (-eta E)
             f32x4 R = mfma32(row8(sl + kSlotK, c, g), b0, vneg(vcur));
             R = mfma32(row8(sl + kSlotK, c, 4 + g), b1, R);
-            const bf16x4 eb = pack4(-et * R);
+            const bf16x4 eb = pack4(-(rows_eta((ch - c0) & 1) * R));
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt)
                 Wacc[mt] = mfma16(col4_rho(sl + kSlotK, 4 * g, mt, c), eb, Wacc[mt]);
@@ -330,22 +418,36 @@ linear_backward_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __re
         f32x4 P1 = zero;
         bf16x4 dyt = {};
         if (use_dy) {
-            f32x4 S = mfma32(row8(sl + kSlotQ, c, g), ka0, zero);
-            S = mfma32(row8(sl + kSlotQ, c, 4 + g), ka1, S);
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                S[r] = c <= 4 * g + r ? S[r] : 0.f;
             dyt = col4(sl + kSlotDY, 4 * g, 16 * w, c);  // dY[4g + r][col]
-            P1 = mfma16(pack4(S), dyt, zero);
+            if (a_on) {
+                f32x4 S = mfma32(row8(sl + kSlotQ, c, g), ka0, zero);
+                S = mfma32(row8(sl + kSlotQ, c, 4 + g), ka1, S);
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    S[r] = c <= 4 * g + r ? S[r] : 0.f;
+                P1 = mfma16(pack4(S), dyt, zero);
+            }
         }
         f32x4 P2 = mfma32(ka0, gb0, zero);
         P2 = mfma32(ka1, gb1, P2);
         const f32x4 P = P1 + P2;
-        const f32x4 dE = -et * P;
+        const f32x4 er = rows_eta(slot);                  // eta of rows 4g + r
+        const f32x4 dE = -(er * P);
         if (!kGMap) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                deta_acc -= P[r] * E[r];
+                if constexpr (kPro) {
+                    if (use_tok) {
+                        // -<P_t, E_t> over this wave's 16 columns
+                        const float pe = group_sum<16>(P[r] * E[r]);
+                        if (c == 0)
+                            reinterpret_cast<float*>(lds + L::kDeta)[w * kB + 4 * g + r] = pe;
+                    } else {
+                        deta_acc -= P[r] * E[r];
+                    }
+                } else {
+                    deta_acc -= P[r] * E[r];
+                }
                 *reinterpret_cast<__bf16*>(lds + kOffE + swz_elem(4 * g + r, col)) = static_cast<__bf16>(E[r]);
                 *reinterpret_cast<__bf16*>(lds + kOffP + swz_elem(4 * g + r, col)) = static_cast<__bf16>(P[r]);
             }
@@ -372,20 +474,26 @@ linear_backward_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __re
             const bf16x8 ya0 = row8(sl + kSlotDY, c, g), ya1 = row8(sl + kSlotDY, c, 4 + g);
             const bf16x8 ea0 = row8(lds + kOffE, c, g), ea1 = row8(lds + kOffE, c, 4 + g);
             // dA[t = 4g + r][s = c] and dA^T[s = 4g + r][t = c], masked and scaled
-            f32x4 dA = mfma32(ya0, ea0, zero);
-            dA = mfma32(ya1, ea1, dA);
-            f32x4 dAT = mfma32(ea0, ya0, zero);
-            dAT = mfma32(ea1, ya1, dAT);
+            f32x4 dA = zero, dAT = zero;
+            if (a_on) {
+                dA = mfma32(ya0, ea0, zero);
+                dA = mfma32(ya1, ea1, dA);
+                dAT = mfma32(ea0, ya0, zero);
+                dAT = mfma32(ea1, ya1, dAT);
+                // dA[t][s] scales by eta_s (s = c), dA^T[s][t] by eta_s (s = 4g + r)
+                const float ec = kPro ? reinterpret_cast<const float*>(lds + L::kEta)[slot * kB + c] : et;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                dA[r] = c <= 4 * g + r ? -et * dA[r] : 0.f;
-                dAT[r] = 4 * g + r <= c ? -et * dAT[r] : 0.f;
+                for (int r = 0; r < 4; ++r) {
+                    dA[r] = c <= 4 * g + r ? -ec * dA[r] : 0.f;
+                    dAT[r] = 4 * g + r <= c ? -er[r] * dAT[r] : 0.f;
+                }
             }
             // dQ_I = dY W[I, :]^T + dA K_I
             f32x4 q1 = mfma32(ya0, wb[0], zero);
             q1 = mfma32(ya1, wb[1], q1);
-            const f32x4 q2 = mfma16(pack4(dAT), col4(sl + kSlotK, 4 * g, 16 * w, c), zero);
-            const f32x4 dq = q1 + q2;
+            f32x4 dq = q1;
+            if (a_on)
+                dq += mfma16(pack4(dAT), col4(sl + kSlotK, 4 * g, 16 * w, c), zero);
             // dK_I = -eta (P W[I, :]^T + E G'[I, :]^T) + dA^T Q_I
             bf16x8 gt[2];
 #pragma unroll
@@ -396,8 +504,9 @@ linear_backward_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __re
             k1 = mfma32(row8(lds + kOffP, c, 4 + g), wb[1], k1);
             k1 = mfma32(ea0, gt[0], k1);
             k1 = mfma32(ea1, gt[1], k1);
-            const f32x4 k2 = mfma16(pack4(dA), col4(sl + kSlotQ, 4 * g, 16 * w, c), zero);
-            const f32x4 dk = -et * k1 + k2;
+            f32x4 dk = -(er * k1);
+            if (a_on)
+                dk += mfma16(pack4(dA), col4(sl + kSlotQ, 4 * g, 16 * w, c), zero);
 
             // rows t = 16 ch + 4g + r, column 16 w + c; dV = eta P (this wave's
             // columns from phase A)
@@ -406,9 +515,47 @@ linear_backward_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __re
                 const int t = ch * kB + 4 * g + r;
                 if (t < T) {
                     const int64_t e = off + static_cast<int64_t>(t) * kD + col;
-                    store_elem(dQ, e, dq[r]);
-                    store_elem(dK, e, dk[r]);
-                    store_elem(dV, e, et * P[r]);
+                    if constexpr (!kPro) {
+                        store_elem(dQ, e, dq[r]);
+                        store_elem(dK, e, dk[r]);
+                    }
+                    store_elem(dV, e, er[r] * P[r]);
+                }
+            }
+            if constexpr (kPro) {
+                // the gradients of the normalised rows go to the staging
+                // threads for the LayerNorm backward
+                float* tq = reinterpret_cast<float*>(lds + L::kDQ);
+                float* tk = reinterpret_cast<float*>(lds + L::kDK);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    tq[(4 * g + r) * kFP + col] = dq[r];
+                    tk[(4 * g + r) * kFP + col] = dk[r];
+                }
+                __syncthreads();
+                float gq[4], gk[4];
+                {
+                    const f32x4 a = *reinterpret_cast<const f32x4*>(tq + srow * kFP + scol);
+                    const f32x4 b = *reinterpret_cast<const f32x4*>(tk + srow * kFP + scol);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        gq[e] = a[e];
+                        gk[e] = b[e];
+                    }
+                }
+                if (ln_q)
+                    layernorm_row_backward<16, 4>(gq, xq, rq, gmq, dgq, dbq);
+                if (ln_k)
+                    layernorm_row_backward<16, 4>(gk, xk, rk, gmk, dgk, dbk);
+                const int t = ch * kB + srow;
+                if (t < T) {
+                    const int64_t e = off + static_cast<int64_t>(t) * kD + scol;
+                    *reinterpret_cast<u32x2*>(dQ + e) = u32x2{cvt2(gq[0], gq[1]), cvt2(gq[2], gq[3])};
+                    *reinterpret_cast<u32x2*>(dK + e) = u32x2{cvt2(gk[0], gk[1]), cvt2(gk[2], gk[3])};
+                    if (use_tok && (tid & 15) == 0) {
+                        const float* pd = reinterpret_cast<const float*>(lds + L::kDeta);
+                        deta_tok[u * T + t] = -((pd[srow] + pd[kB + srow]) + (pd[2 * kB + srow] + pd[3 * kB + srow]));
+                    }
                 }
             }
         }
@@ -445,9 +592,45 @@ linear_backward_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __re
     float* red = reinterpret_cast<float*>(lds + kOffRed);
     if (lane == 0)
         red[w] = deta_acc;
-    __syncthreads();
+    if constexpr (kPro) {
+        // gamma, beta gradients: over the 4 rows of the wave (lanes 16 apart),
+        // then over the waves; out[a][col], a = gamma_q, beta_q, gamma_k, beta_k
+        float* lr = reinterpret_cast<float*>(lds + L::kDQ);    // [4 waves][4][64]
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float v4[4] = {dgq[e], dbq[e], dgk[e], dbk[e]};
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                float x = v4[a];
+                x += __shfl_xor(x, 16);
+                x += __shfl_xor(x, 32);
+                if (lane < 16)
+                    lr[(w * 4 + a) * kD + scol + e] = x;
+            }
+        }
+        __syncthreads();
+        const float x = (lr[tid] + lr[256 + tid]) + (lr[512 + tid] + lr[768 + tid]);
+        dln_chain[(u * nseg + s) * (kDlnRows * kD) + tid] = x;
+    } else {
+        __syncthreads();
+    }
     if (tid == 0)
         deta_chain[u * nseg + s] = (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+template <bool kGMap, bool kPro>
+void launch_bf16(const LinearBwdArgs& a, const SegmentPlan& p, const BwdBuffers& b, dim3 grid)
+{
+    hipLaunchKernelGGL((linear_backward_bf16_kernel<kGMap, kPro>), grid, dim3(kThreads),
+                       kGMap ? Lay<kPro>::kGMapBytes : Lay<kPro>::kBytes, a.stream,
+                       static_cast<const uint16_t*>(a.Q), static_cast<const uint16_t*>(a.K),
+                       static_cast<const uint16_t*>(a.V), a.W0, a.w0_per_batch, a.eta,
+                       static_cast<int>(a.H), static_cast<int>(a.T), a.B * a.H,
+                       static_cast<int>(p.seg_len), p.nseg, b.wstart, b.gend,
+                       static_cast<const uint16_t*>(a.dY), a.dW_out, static_cast<uint16_t*>(a.dQ),
+                       static_cast<uint16_t*>(a.dK), static_cast<uint16_t*>(a.dV), b.dw_chain,
+                       b.deta_chain, reinterpret_cast<uint16_t*>(b.states), b.gmaps, a.pro,
+                       a.deta_tok, b.dln_chain);
 }
 
 }  // namespace
@@ -455,25 +638,11 @@ linear_backward_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __re
 hipError_t launch_linear_backward_bf16(const LinearBwdArgs& a, const SegmentPlan& p, bool gmap,
                                        const BwdBuffers& b, dim3 grid)
 {
-    const auto* q = static_cast<const uint16_t*>(a.Q);
-    const auto* k = static_cast<const uint16_t*>(a.K);
-    const auto* v = static_cast<const uint16_t*>(a.V);
-    const auto* dy = static_cast<const uint16_t*>(a.dY);
-    auto* dq = static_cast<uint16_t*>(a.dQ);
-    auto* dk = static_cast<uint16_t*>(a.dK);
-    auto* dv = static_cast<uint16_t*>(a.dV);
-    auto* st = reinterpret_cast<uint16_t*>(b.states);
-    const int H = static_cast<int>(a.H), T = static_cast<int>(a.T), seg = static_cast<int>(p.seg_len);
+    const bool pro = a.pro.active();
     if (gmap)
-        hipLaunchKernelGGL(linear_backward_bf16_kernel<true>, grid, dim3(kThreads), kGMapLdsBytes,
-                           a.stream, q, k, v, a.W0, a.w0_per_batch, a.eta, H, T, a.B * a.H, seg,
-                           p.nseg, b.wstart, b.gend, dy, a.dW_out, dq, dk, dv, b.dw_chain,
-                           b.deta_chain, st, b.gmaps);
+        pro ? launch_bf16<true, true>(a, p, b, grid) : launch_bf16<true, false>(a, p, b, grid);
     else
-        hipLaunchKernelGGL(linear_backward_bf16_kernel<false>, grid, dim3(kThreads), kLdsBytes,
-                           a.stream, q, k, v, a.W0, a.w0_per_batch, a.eta, H, T, a.B * a.H, seg,
-                           p.nseg, b.wstart, b.gend, dy, a.dW_out, dq, dk, dv, b.dw_chain,
-                           b.deta_chain, st, b.gmaps);
+        pro ? launch_bf16<false, true>(a, p, b, grid) : launch_bf16<false, false>(a, p, b, grid);
     return hipGetLastError();
 }
 

@@ -31,6 +31,10 @@ KERNEL_FILES = {
     "linear_backward_kernel[segments]": "ttt_linear_backward.hip",
     "linear_backward_bf16_kernel[gmaps]": "ttt_linear_backward_bf16.hip",
     "linear_backward_bf16_kernel[segments]": "ttt_linear_backward_bf16.hip",
+    "linear_backward_kernel[gmaps+prologue]": "ttt_linear_backward.hip",
+    "linear_backward_kernel[segments+prologue]": "ttt_linear_backward.hip",
+    "linear_backward_bf16_kernel[gmaps+prologue]": "ttt_linear_backward_bf16.hip",
+    "linear_backward_bf16_kernel[segments+prologue]": "ttt_linear_backward_bf16.hip",
     "linear_backward_reduce_kernel": "ttt_linear_backward.hip",
     "linear_generic_kernel": "ttt_generic.hip",
     "mlp_generic_kernel": "ttt_generic.hip",
@@ -43,12 +47,14 @@ COPY_NAME = "__amd_rocclr_copyBuffer"
 def short_name(full: str) -> str:
     """Kernel key: the function name, with [maps] / [scan] for the two
     instantiations of the TTT-Linear MFMA kernels and [gmaps] / [segments]
-    for the backward's cotangent maps and segment backward."""
-    if "linear_backward_kernel<" in full:
-        return "linear_backward_kernel[gmaps]" if ", true>" in full else "linear_backward_kernel[segments]"
-    if "linear_backward_bf16_kernel<" in full:
-        return ("linear_backward_bf16_kernel[gmaps]" if "<true>" in full
-                else "linear_backward_bf16_kernel[segments]")
+    for the backward's cotangent maps and segment backward (+prologue for
+    the instantiations with the input prologue)."""
+    for base in ("linear_backward_kernel", "linear_backward_bf16_kernel"):
+        if base + "<" in full:
+            args = [a.strip() for a in full.split(base + "<", 1)[1].split(">", 1)[0].split(",")]
+            flags = [a for a in args if a in ("true", "false")]     # kGMap, kPro
+            role = "gmaps" if flags[0] == "true" else "segments"
+            return f"{base}[{role}{'+prologue' if flags[1] == 'true' else ''}]"
     for k in KERNEL_FILES:
         base = k.split("[")[0]
         if base + "<true" in full:

@@ -160,6 +160,41 @@ def test_backward_validation(lib, kw, expect):
     assert bwd(lib, **kw) == expect
 
 
+# prologue inputs and their gradients, apart from every address above
+PTOKA, PLNQA, PLNKA, DTOKA, DLNQA, DLNKA = (0x200_0000_0000 + 0x10_0000_0000 * i for i in range(6))
+
+
+def bwdx(lib, tok=PTOKA, lnq=PLNQA, lnk=PLNKA, eps=1e-5, rm=0, dtok=DTOKA, dlnq=DLNQA, dlnk=DLNKA,
+         d=64, b=16, H=3, dQ=DQA, deta=DETA):
+    return lib.ttt_linear_backward_ex(QA, KA, VA, 1, W0A, 0, ETA, tok, lnq, lnk, eps, rm, 2, H, 64,
+                                      d, b, DYA, DWOA, dQ, DKA, DVA, DW0A, deta, dtok, dlnq, dlnk,
+                                      None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(eps=0.0), INVALID), (dict(eps=float("inf")), INVALID), (dict(rm=2), INVALID),
+    # every prologue input comes with its gradient output and the reverse
+    (dict(dtok=None), INVALID), (dict(tok=None), INVALID), (dict(dlnq=None), INVALID),
+    (dict(lnk=None), INVALID), (dict(tok=None, dtok=None, lnq=None, dlnq=None, d=32), UNSUPPORTED),
+    (dict(d=32), UNSUPPORTED), (dict(b=8), UNSUPPORTED),
+    (dict(dtok=PTOKA), INVALID), (dict(dlnq=PLNQA + 4), INVALID), (dict(dlnk=DLNQA + 8), INVALID),
+    (dict(dtok=DQA + 64), INVALID), (dict(dQ=DLNKA), INVALID), (dict(deta=DTOKA + 4), INVALID),
+    (dict(H=0), OK), (dict(lnq=None, dlnq=None, lnk=None, dlnk=None, eps=0.0, H=0), OK),
+])
+def test_backward_ex_validation(lib, kw, expect):
+    assert bwdx(lib, **kw) == expect
+
+
+def test_backward_ex_fixture_addresses_are_disjoint():
+    # the valid default call of bwdx must not overlap itself, so that each
+    # INVALID case above fails for its own reason
+    spans = [(a, 0x10_0000_0000) for a in (QA, KA, VA, W0A, ETA, DYA, DWOA, DQA, DKA, DVA, DW0A,
+                                           DETA, PTOKA, PLNQA, PLNKA, DTOKA, DLNQA, DLNKA)]
+    spans.sort()
+    for (a, n), (b, _) in zip(spans, spans[1:]):
+        assert a + n <= b
+
+
 def decx(lib, tok=TOKA, lnq=LNQA, lnk=LNKA, eps=1e-5, rm=0, d=64, y=YA, W=W0A, B=2):
     return lib.ttt_linear_decode_step_ex(QA, KA, VA, 1, W, ETA, tok, lnq, lnk, eps, rm, B, 24, d,
                                          y, None)
