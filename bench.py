@@ -52,6 +52,8 @@ KERNEL_SOURCES = {
     "linear_mfma_kernel[maps]": "ttt_linear_mfma.hip",
     "linear_mfma_f32_kernel[scan]": "ttt_linear_mfma_f32.hip",
     "linear_mfma_f32_kernel[maps]": "ttt_linear_mfma_f32.hip",
+    "linear_cols_f32_kernel[scan]": "ttt_linear_cols_f32.hip",
+    "linear_cols_f32_kernel[maps]": "ttt_linear_cols_f32.hip",
     "linear_combine_kernel": "ttt_linear_combine.hip",
     "linear_backward_reduce_kernel": "ttt_linear_backward.hip",
     "linear_backward_kernel[gmaps]": "ttt_linear_backward.hip",
@@ -121,9 +123,22 @@ def kernel_names(w, nseg):
         return ["mlp_mfma_kernel" if (w.dtype == "bf16" and w.d == 64 and w.m == 256 and w.b == 16)
                 else "mlp_generic_kernel"]
     if w.d == 64 and w.b == 16:
-        k = "linear_mfma_kernel" if w.dtype == "bf16" else "linear_mfma_f32_kernel"
+        if w.dtype == "bf16":
+            k = "linear_mfma_kernel"
+        else:
+            k = "linear_cols_f32_kernel" if f32_cols(w) else "linear_mfma_f32_kernel"
         return [k + "[maps]", "linear_combine_kernel", k + "[scan]"] if nseg > 1 else [k + "[scan]"]
     return ["linear_generic_kernel"]
+
+
+def f32_cols(w):
+    """Whether the library runs this fp32 TTT-Linear scan with each chain's W
+    split by columns over 4 workgroups (while B*H*4 fits the CUs, unless
+    TTT_LINEAR_F32_COLS=0)."""
+    import torch
+    if os.environ.get("TTT_LINEAR_F32_COLS", "1").strip() == "0":
+        return False
+    return w.B * w.H * 4 <= torch.cuda.get_device_properties(0).multi_processor_count
 
 
 def backward_kernel_names(w):

@@ -35,6 +35,7 @@ EXTRA = {
     "ttt_linear_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "ttt_linear_mfma_f32.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "ttt_linear_backward.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "ttt_linear_cols_f32.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

@@ -90,11 +90,14 @@ ttt::SegmentPlan plan_segments(int64_t units, int64_t T, int chunk, const ttt::S
         }
     }
     const int64_t cus = device_cus();
-    if (cus <= 0 || 2 * units > cus || chunks < 4) return p;
+    const int64_t scan_blocks = units * cost.scan_blocks_per_segment;
+    if (cus <= 0 || 2 * scan_blocks > cus || chunks < 4) return p;
     double best = static_cast<double>(chunks) * cost.fwd;
     int best_s = 1;
     for (int S = 2; S <= ttt::kMaxSegments; ++S) {
-        if (units * S > cus || units * (S - 1) * cost.map_blocks_per_segment > cus) break;
+        if (scan_blocks * S > cus ||
+            units * (S - 1) * cost.map_blocks_per_segment > cost.map_blocks_per_cu * cus)
+            break;
         const int64_t per = (chunks + S - 1) / S;
         if (per < 2) break;
         const double t = per * (cost.map + cost.fwd) + (S - 1) * cost.apply + cost.launch;
@@ -195,6 +198,19 @@ hipError_t workspace_get(void** ptr, size_t bytes, hipStream_t stream)
     return hipSuccess;
 }
 
+// fp32 scans split each chain's columns over 4 workgroups while those fit the
+// CUs (fewer chains than a quarter of the CUs); with more chains the GPU is
+// already full and the one-workgroup kernel does the same MFMA work with less
+// traffic.  TTT_LINEAR_F32_COLS=0 turns the split off.
+bool use_cols_f32(const LinearArgs& a)
+{
+    if (!ttt::linear_cols_f32_supports(a)) return false;
+    if (const char* env = getenv("TTT_LINEAR_F32_COLS"))
+        if (strtol(env, nullptr, 10) == 0) return false;
+    const int64_t cus = device_cus();
+    return cus > 0 && a.B * a.H * ttt::kColsSlices <= cus;
+}
+
 // Runs a segmented MFMA linear scan: workspace for the maps and the segment
 // start states, then the launches.  The start states (including the copy of
 // W0 for the first segment) are complete before any segment writes W_out, so
@@ -281,6 +297,9 @@ int linear_forward_impl(const void* Q, const void* K, const void* V, int qkv_dty
     if (ttt::linear_mfma_supports(a))
         return run_linear_segmented(a, plan_segments(units, T, b, ttt::kLinearBf16Costs),
                                     ttt::launch_linear_mfma);
+    if (use_cols_f32(a))
+        return run_linear_segmented(a, plan_segments(units, T, b, ttt::kLinearF32ColsCosts),
+                                    ttt::launch_linear_cols_f32);
     if (ttt::linear_mfma_f32_supports(a))
         return run_linear_segmented(a, plan_segments(units, T, b, ttt::kLinearF32Costs),
                                     ttt::launch_linear_mfma_f32);
@@ -335,6 +354,7 @@ int ttt_linear_segments(int64_t B, int64_t H, int64_t T, int d, int b, int qkv_d
                  nullptr, nullptr, nullptr};
     if (units == 0 || T == 0) return 1;
     if (ttt::linear_mfma_supports(a)) return plan_segments(units, T, b, ttt::kLinearBf16Costs).nseg;
+    if (use_cols_f32(a)) return plan_segments(units, T, b, ttt::kLinearF32ColsCosts).nseg;
     if (ttt::linear_mfma_f32_supports(a)) return plan_segments(units, T, b, ttt::kLinearF32Costs).nseg;
     return 1;
 }

@@ -217,7 +217,9 @@ constexpr int kMaxSegments = 30;   // with the ring's spare slots: 36 x 4352 B o
 // and the fixed cost of the two extra launches.
 struct SegmentCosts {
     double fwd, map, apply, launch;
-    int map_blocks_per_segment;   // workgroups of the maps launch per segment
+    int map_blocks_per_segment;       // workgroups of the maps launch per segment
+    int scan_blocks_per_segment = 1;  // workgroups of the scan launch per segment
+    int map_blocks_per_cu = 1;        // maps workgroups one CU may hold
 };
 bool linear_mfma_supports(const LinearArgs& a);
 hipError_t launch_linear_mfma(const LinearArgs& a, const SegmentPlan& p);
@@ -225,6 +227,13 @@ bool linear_mfma_f32_supports(const LinearArgs& a);
 hipError_t launch_linear_mfma_f32(const LinearArgs& a, const SegmentPlan& p);
 constexpr SegmentCosts kLinearBf16Costs{0.35, 0.43, 0.60, 8.5, 1};
 constexpr SegmentCosts kLinearF32Costs{1.38, 0.90, 0.60, 8.5, 2};
+// fp32 Q/K/V with each chain's W split by columns over 4 workgroups
+// (ttt_linear_cols_f32.hip; the plain scan only): used while the chains'
+// 4 workgroups each fit the GPU's CUs, where it cuts a chunk's latency.
+bool linear_cols_f32_supports(const LinearArgs& a);
+hipError_t launch_linear_cols_f32(const LinearArgs& a, const SegmentPlan& p);
+constexpr int kColsSlices = 4;
+constexpr SegmentCosts kLinearF32ColsCosts{0.79, 0.55, 0.60, 8.5, 2 * kColsSlices, kColsSlices, 2};
 bool mlp_mfma_supports(const MlpArgs& a);
 hipError_t launch_mlp_mfma(const MlpArgs& a);
 

@@ -26,6 +26,8 @@ KERNEL_FILES = {
     "linear_mfma_kernel[maps]": "ttt_linear_mfma.hip",
     "linear_mfma_f32_kernel[scan]": "ttt_linear_mfma_f32.hip",
     "linear_mfma_f32_kernel[maps]": "ttt_linear_mfma_f32.hip",
+    "linear_cols_f32_kernel[scan]": "ttt_linear_cols_f32.hip",
+    "linear_cols_f32_kernel[maps]": "ttt_linear_cols_f32.hip",
     "linear_combine_kernel": "ttt_linear_combine.hip",
     "linear_backward_kernel[gmaps]": "ttt_linear_backward.hip",
     "linear_backward_kernel[segments]": "ttt_linear_backward.hip",
@@ -94,9 +96,10 @@ def main():
     ap.add_argument("--title", help="heading (default: the workload name)")
     ap.add_argument("--command", required=True, help="the rocprofv3 command lines that made the data")
     ap.add_argument("--copy-mib", type=int, default=256)
-    ap.add_argument("--call", default="forward", choices=["forward", "backward"],
-                    help="which call the trace covers (the traffic table keys the backward's "
-                         "kernels under '<workload>/backward')")
+    ap.add_argument("--call", default="forward",
+                    choices=["forward", "backward", "forward_prologue", "backward_prologue"],
+                    help="which call the trace covers (the traffic table keys the kernels of "
+                         "any call but the forward under '<workload>/<call>')")
     ap.add_argument("--out", required=True)
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"))
     args = ap.parse_args()
@@ -136,7 +139,7 @@ def main():
                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
                      f"{rd / 1e6:.3f} | {wb / 1e6:.3f} |")
         if fr and wr:
-            key = w.name if args.call == "forward" else w.name + "/backward"
+            key = w.name if args.call == "forward" else w.name + "/" + args.call
             table.setdefault(name, {})[key] = {
                 "source_sha": source_sha(name), "bytes_per_launch": int(rd + wb),
                 "read_bytes": int(rd), "write_bytes": int(wb),

@@ -24,12 +24,15 @@ def main():
     ap.add_argument("--decode", action="store_true", help="also run the workload's decode steps")
     ap.add_argument("--backward", action="store_true",
                     help="run ttt_linear_backward (seeded cotangents) instead of the forward")
+    ap.add_argument("--prologue", action="store_true",
+                    help="with the input prologue (LayerNorm of q and k, per-token step sizes): "
+                         "ttt_linear_forward_ex / ttt_linear_backward_ex")
     args = ap.parse_args()
 
     import torch
     import test_sequence_layers_linear_amd as ttt
     from test_sequence_layers_linear_amd.inputs import (CONFIGS, default_seed, make_cotangents,
-                                                        make_inputs)
+                                                        make_inputs, make_prologue)
 
     w = CONFIGS[args.config]
     g = {k: v.cuda() for k, v in make_inputs(w, default_seed(args.config)).items()}
@@ -41,11 +44,20 @@ def main():
         W2 = torch.empty((w.B, w.H, w.m, w.d), device="cuda")
     if args.backward:
         cot = {k: v.cuda() for k, v in make_cotangents(w, 7).items()}
+    if args.prologue:
+        pro = {k: v.cuda() for k, v in make_prologue(w, 11).items()}
+        pkw = {k: pro[k] for k in ("eta_tok", "ln_q", "ln_k")}
     torch.cuda.synchronize()
     for _ in range(args.reps):
-        if args.backward:
+        if args.backward and args.prologue:
+            ttt.ttt_linear_backward_ex(g["Q"], g["K"], g["V"], g["W0"], pro["eta"], w.b, cot["dY"],
+                                       cot["dW_out"], **pkw)
+        elif args.backward:
             ttt.ttt_linear_backward(g["Q"], g["K"], g["V"], g["W0"], g["eta"], w.b, cot["dY"],
                                     cot["dW_out"])
+        elif args.prologue:
+            ttt.ttt_linear_forward_ex(g["Q"], g["K"], g["V"], g["W0"], pro["eta"], w.b, Y=Y,
+                                      W_out=W, **pkw)
         elif w.kind == "linear":
             ttt.ttt_linear_forward(g["Q"], g["K"], g["V"], g["W0"], g["eta"], w.b, Y=Y, W_out=W)
             if args.decode:

@@ -263,3 +263,35 @@ def test_segmented_close_to_single_segment(monkeypatch):
     Y16, W16 = linear_gpu(g, 16)
     assert rel_l2(Y16, Y1.double().cpu().numpy()) <= 2e-6
     assert rel_l2(W16, W1.double().cpu().numpy()) <= 2e-6
+
+
+# ---------------------------------------------------------------------------
+# fp32 scans with few chains split each chain's columns over 4 workgroups;
+# the one-workgroup kernel still runs with many chains, with the prologue and
+# for the backward's start states (TTT_LINEAR_F32_COLS=0 selects it here)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("T,S,per_batch", [(16, 1, False), (515, 1, True), (1000, 7, False),
+                                           (2048, 16, False), (333, 3, True)])
+def test_f32_one_workgroup_kernel(T, S, per_batch, monkeypatch):
+    monkeypatch.setenv("TTT_LINEAR_F32_COLS", "0")
+    monkeypatch.setenv("TTT_LINEAR_SEGMENTS", str(S))
+    w = CONFIGS[2].with_(B=2, H=3, T=T, w0=("normal", 0.3), eta=("uniform", 0.01, 0.1))
+    announce("linear fp32 one workgroup per chain", T, S, per_batch)
+    _check(make_inputs(w, 500 + T + S, w0_per_batch=per_batch), 16, "fp32")
+
+
+@pytest.mark.parametrize("S", ["1", "5", "16"])
+def test_f32_column_split_close_to_one_workgroup(S, monkeypatch):
+    """The column split changes only the order of the sums over the 64 input
+    rows (four partial products added in LDS)."""
+    monkeypatch.setenv("TTT_LINEAR_SEGMENTS", S)
+    w = CONFIGS[2].with_(B=1, H=4, T=1100, w0=("normal", 0.3))
+    announce("fp32 column split vs one workgroup", S)
+    g = to_gpu(make_inputs(w, 91))
+    Y1, W1 = linear_gpu(g, 16)
+    monkeypatch.setenv("TTT_LINEAR_F32_COLS", "0")
+    Y0, W0 = linear_gpu(g, 16)
+    ey = rel_l2(Y1, Y0.double().cpu().numpy())
+    ew = rel_l2(W1, W0.double().cpu().numpy())
+    print(f"  rel-L2 Y {ey:.2e}  W {ew:.2e}", flush=True)
+    assert ey <= 2e-6 and ew <= 2e-6
