@@ -17,8 +17,9 @@ roofline.achieved = algorithmic bytes (HBM bound) or flops (MFMA bound) of
 one forward call / its mean duration from HIP events recorded on the launch
 stream around every call in the timed region.  A call is one kernel launch,
 except a segmented TTT-Linear scan: maps, start-state composition and
-segment scans, three launches back to back on the stream (roofline.kernel
-names them).  The decode steps of a workload run as one captured HIP graph.
+segment scans, three launches back to back on the stream, or two for the
+fp32 column-split scan, whose segments compose their own start states
+(roofline.kernel names them).  The decode steps of a workload run as one captured HIP graph.
 cpu_baseline = the fp64 oracle (plain loops, OpenMP over chains) timed on
 this host's cores on a bounded sample of the same workload.
 
@@ -123,10 +124,11 @@ def kernel_names(w, nseg):
         return ["mlp_mfma_kernel" if (w.dtype == "bf16" and w.d == 64 and w.m == 256 and w.b == 16)
                 else "mlp_generic_kernel"]
     if w.d == 64 and w.b == 16:
-        if w.dtype == "bf16":
-            k = "linear_mfma_kernel"
-        else:
-            k = "linear_cols_f32_kernel" if f32_cols(w) else "linear_mfma_f32_kernel"
+        if w.dtype == "fp32" and f32_cols(w):
+            # the segment scans compose their own start states: no combine launch
+            k = "linear_cols_f32_kernel"
+            return [k + "[maps]", k + "[scan]"] if nseg > 1 else [k + "[scan]"]
+        k = "linear_mfma_kernel" if w.dtype == "bf16" else "linear_mfma_f32_kernel"
         return [k + "[maps]", "linear_combine_kernel", k + "[scan]"] if nseg > 1 else [k + "[scan]"]
     return ["linear_generic_kernel"]
 

@@ -233,7 +233,7 @@ constexpr SegmentCosts kLinearF32Costs{1.38, 0.90, 0.60, 8.5, 2};
 bool linear_cols_f32_supports(const LinearArgs& a);
 hipError_t launch_linear_cols_f32(const LinearArgs& a, const SegmentPlan& p);
 constexpr int kColsSlices = 4;
-constexpr SegmentCosts kLinearF32ColsCosts{0.79, 0.55, 0.60, 8.5, 2 * kColsSlices, kColsSlices, 2};
+constexpr SegmentCosts kLinearF32ColsCosts{0.79, 0.55, 0.90, 4.5, 2 * kColsSlices, kColsSlices, 2};
 bool mlp_mfma_supports(const MlpArgs& a);
 hipError_t launch_mlp_mfma(const MlpArgs& a);
 

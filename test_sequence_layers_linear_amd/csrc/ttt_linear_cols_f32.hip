@@ -38,7 +38,14 @@
 //
 // kMaps = true computes the affine map W_end = M W_start + N of a segment
 // (half 0: from W = I with V = 0, giving M; half 1: from W = 0, giving N),
-// column slice J of each, as the segment scan needs (see ttt_internal.h).
+// column slice J of each, as the segment scan needs (see ttt_internal.h); the
+// workgroups of segment 0 also copy W0 into the workspace.  The scan of
+// segment s then composes its own start state from that copy,
+//     W_{j+1} = M_j W_j + N_j,   j = 0 .. s - 1,
+// in the same layout (each step: the waves' row tiles to LDS, transposed,
+// one barrier, 16 k-steps over the 64 rows), so the start states need no
+// launch of their own and never go through memory; segment s is ready after
+// s steps, the last one after nseg - 1, as with a separate composition.
 #include "ttt_internal.h"
 
 namespace ttt {
@@ -93,8 +100,8 @@ __global__ void __launch_bounds__(kThreads, 1)
 linear_cols_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                        const float* __restrict__ V, const float* W0, int w0_per_batch,
                        const float* __restrict__ eta, int H, int T, int64_t units, int seg_len,
-                       int nseg, float* maps, const float* wstart, float* __restrict__ Y,
-                       float* W_out)
+                       int nseg, float* maps, float* wstart, float* __restrict__ Y,
+                       float* W_out, int compose)
 {
     using L = Lay<kMaps>;
     constexpr int kOffK = L::kOffK, kOffQ = L::kOffQ, kOffV = L::kOffV, kSlotFloats = L::kSlotFloats;
@@ -128,11 +135,73 @@ linear_cols_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
         for (int r = 0; r < 4; ++r)
             Wr[r] = (half == 0 && 16 * w + 4 * g + r == 16 * J + c) ? 1.f : 0.f;
     } else {
-        const float* w0 = nseg > 1 ? wstart + (u * nseg + s) * kD * kD
+        const float* w0 = nseg > 1 ? wstart + (u * nseg + (compose ? 0 : s)) * kD * kD
                                    : W0 + (w0_per_batch ? u : h) * kD * kD;
 #pragma unroll
         for (int r = 0; r < 4; ++r)
             Wr[r] = w0[(16 * w + 4 * g + r) * kD + 16 * J + c];
+    }
+    if (kMaps && s == 0 && half == 0) {
+        // the copy of W0 the scans start from (W_out may overwrite W0)
+        const float* w0 = W0 + (w0_per_batch ? u : h) * kD * kD;
+        float* dst = wstart + u * nseg * kD * kD;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int i = (tid >> 4) + 16 * q;
+            dst[i * kD + 16 * J + (tid & 15)] = w0[i * kD + 16 * J + (tid & 15)];
+        }
+    }
+    if (!kMaps && compose && s > 0) {
+        // W_s from W_0 through the maps of segments 0 .. s - 1; wave w's A
+        // operand of k-step ks is M_j[16w + c][16g + ks] (a 64-byte run per
+        // lane), its B operand W_j[16g + ks][c] from the transposed slice
+        // [column][row] in LDS (two buffers by step parity); operands of step
+        // j + kDepth load while step j runs
+        constexpr int kDepth = 3;
+        constexpr int kColP = kD + 4;            // [16 columns][kColP] per buffer
+        f32x4 ma[kDepth][4], mn[kDepth];
+        auto load_map = [&](f32x4 (&a)[4], f32x4& n, int j) {
+            const float* M = maps + (u * (nseg - 1) + min(j, s - 1)) * 2 * kD * kD;
+            const float* N = M + kD * kD;
+#pragma unroll
+            for (int x = 0; x < 4; ++x)
+                a[x] = *reinterpret_cast<const f32x4*>(M + (16 * w + c) * kD + 16 * g + 4 * x);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                n[r] = N[(16 * w + 4 * g + r) * kD + 16 * J + c];
+        };
+#pragma unroll
+        for (int q = 0; q < kDepth; ++q)
+            load_map(ma[q], mn[q], q);
+        auto cstep = [&](int q, int j) {
+            float* Wt = lds + (j & 1) * 16 * kColP;
+            *reinterpret_cast<f32x4*>(Wt + c * kColP + 16 * w + 4 * g) = Wr;
+            __syncthreads();
+            f32x4 b[4];
+#pragma unroll
+            for (int x = 0; x < 4; ++x)
+                b[x] = *reinterpret_cast<const f32x4*>(Wt + c * kColP + 16 * g + 4 * x);
+            const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+            f32x4 acc[4] = {mn[q], zero, zero, zero};
+#pragma unroll
+            for (int ks = 0; ks < 16; ++ks)
+                acc[ks & 3] = mfma(ma[q][ks >> 2][ks & 3], b[ks >> 2][ks & 3], acc[ks & 3]);
+            Wr = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+            load_map(ma[q], mn[q], j + kDepth);
+        };
+        int j0 = 0;
+        for (; j0 + kDepth <= s; j0 += kDepth) {
+#pragma unroll
+            for (int q = 0; q < kDepth; ++q)
+                cstep(q, j0 + q);
+        }
+#pragma unroll
+        for (int q = 0; q < kDepth; ++q) {
+            if (j0 + q >= s)             // uniform
+                break;
+            cstep(q, j0 + q);
+        }
+        __syncthreads();                 // the slice buffers are the tile slots below
     }
 
     const int64_t base = (u * static_cast<int64_t>(T) + t_begin) * kD;
@@ -301,17 +370,18 @@ hipError_t launch_linear_cols_f32(const LinearArgs& a, const SegmentPlan& p)
         const dim3 grid(static_cast<unsigned>(placed_grid(units, 2 * kSlices * (p.nseg - 1))));
         hipLaunchKernelGGL((linear_cols_f32_kernel<true>), grid, dim3(kThreads), 0, a.stream, q, k, v,
                            a.W0, a.w0_per_batch, a.eta, H, T, units, seg_len, p.nseg, p.maps,
-                           p.wstart, y, a.W_out);
+                           p.wstart, y, a.W_out, 0);
         hipError_t e = hipGetLastError();
-        if (e == hipSuccess)
-            e = launch_linear_combine(a, p);
-        if (e != hipSuccess || p.starts_only)
+        if (e != hipSuccess)
             return e;
+        if (p.starts_only)               // every start state, for a caller that needs them
+            return launch_linear_combine(a, p);
     }
+    // segments compose their start states from the maps and the copy of W0
     const dim3 grid(static_cast<unsigned>(placed_grid(units, kSlices * p.nseg)));
     hipLaunchKernelGGL((linear_cols_f32_kernel<false>), grid, dim3(kThreads), 0, a.stream, q, k, v,
                        a.W0, a.w0_per_batch, a.eta, H, T, units, seg_len, p.nseg, p.maps, p.wstart,
-                       y, a.W_out);
+                       y, a.W_out, 1);
     return hipGetLastError();
 }
 
