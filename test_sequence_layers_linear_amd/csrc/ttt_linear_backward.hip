@@ -681,44 +681,67 @@ linear_backward_kernel(const In* __restrict__ Q, const In* __restrict__ K, const
         deta_chain[u * nseg + s] = (lds[kOffRed] + lds[kOffRed + 1]) + (lds[kOffRed + 2] + lds[kOffRed + 3]);
 }
 
-// Sums in a fixed order: dW0 over the batch (when W0 is shared by the batch)
-// and deta over the batch and the segments (always: eta is one value per head).
-// With the prologue also the LayerNorm gamma, beta gradients over the batch
-// and the segments: dln_q, dln_k [H][2][64] from dln_chain [B H][nseg][4][64].
+// Sums in a fixed order: dW0 over the batch (when W0 is shared by the batch),
+// deta over the batch and the segments (always: eta is one value per head)
+// and, with the prologue, the LayerNorm gamma, beta gradients over the batch
+// and the segments (dln_q, dln_k [H][2][64] from dln_chain [B H][nseg][4][64]).
+// The first w_blocks blocks give each dW0 element a thread (B independent
+// loads); the rest give each deta and LayerNorm element a wave, whose lanes
+// sum every 64th of its B * nseg terms and then combine by a butterfly: the
+// terms load in parallel, and the order is the same on every run.
 __global__ void __launch_bounds__(256)
 linear_backward_reduce_kernel(const float* __restrict__ dW0_chain, const float* __restrict__ deta_chain,
-                              int64_t B, int H, int nseg, int reduce_w, float* __restrict__ dW0,
+                              int64_t B, int H, int nseg, int64_t w_blocks, float* __restrict__ dW0,
                               float* __restrict__ deta, const float* __restrict__ dln_chain,
                               float* __restrict__ dln_q, float* __restrict__ dln_k)
 {
-    const int64_t x = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
     const int64_t n = static_cast<int64_t>(H) * kD * kD;
-    if (dln_chain && x < static_cast<int64_t>(H) * kDlnRows * kD) {
-        const int hh = static_cast<int>(x / (kDlnRows * kD));
-        const int a = static_cast<int>(x / kD) % kDlnRows;      // gamma_q, beta_q, gamma_k, beta_k
-        const int col = static_cast<int>(x % kD);
-        float* out = a < 2 ? dln_q : dln_k;
-        if (out) {
+    if (blockIdx.x < w_blocks) {
+        const int64_t x = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+        if (x < n) {
             float acc = 0.f;
+#pragma unroll 8
             for (int64_t bb = 0; bb < B; ++bb)
-                for (int sg = 0; sg < nseg; ++sg)
-                    acc += dln_chain[((bb * H + hh) * nseg + sg) * (kDlnRows * kD) + a * kD + col];
-            out[(2 * hh + (a & 1)) * kD + col] = acc;
+                acc += dW0_chain[bb * n + x];
+            dW0[x] = acc;
         }
+        return;
     }
-    if (reduce_w && x < n) {
-        float acc = 0.f;
-        for (int64_t bb = 0; bb < B; ++bb)
-            acc += dW0_chain[bb * n + x];
-        dW0[x] = acc;
+    const int lane = threadIdx.x & 63;
+    const int64_t task = (static_cast<int64_t>(blockIdx.x) - w_blocks) * 4 + (threadIdx.x >> 6);
+    const int64_t terms = B * nseg;
+    const float* src;
+    int64_t stride;                      // between the terms of one (batch, segment) step
+    float* out;
+    if (task < H) {
+        src = deta_chain + task * nseg;
+        stride = 1;
+        out = deta + task;
+    } else {
+        const int64_t e = task - H;      // [H][4][64]
+        if (!dln_chain || e >= static_cast<int64_t>(H) * kDlnRows * kD)
+            return;
+        const int hh = static_cast<int>(e / (kDlnRows * kD));
+        const int a = static_cast<int>(e / kD) % kDlnRows;   // gamma_q, beta_q, gamma_k, beta_k
+        const int col = static_cast<int>(e % kD);
+        out = a < 2 ? dln_q : dln_k;
+        if (!out)
+            return;
+        out += (2 * hh + (a & 1)) * kD + col;
+        src = dln_chain + static_cast<int64_t>(hh) * nseg * (kDlnRows * kD) + a * kD + col;
+        stride = kDlnRows * kD;
     }
-    if (x < H) {
-        float acc = 0.f;
-        for (int64_t bb = 0; bb < B; ++bb)
-            for (int sg = 0; sg < nseg; ++sg)
-                acc += deta_chain[(bb * H + x) * nseg + sg];
-        deta[x] = acc;
+    // term q = bb nseg + sg sits at src + (bb H nseg + sg) stride
+    float acc = 0.f;
+    for (int64_t q = lane; q < terms; q += 64) {
+        const int64_t bb = q / nseg, sg = q % nseg;
+        acc += src[(bb * H * nseg + sg) * stride];
     }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1)
+        acc += __shfl_xor(acc, m);
+    if (lane == 0)
+        *out = acc;
 }
 
 // workspace carve-up (floats): forward maps, start states, cotangent maps,
@@ -869,13 +892,12 @@ hipError_t launch_linear_backward(const LinearBwdArgs& a, const SegmentPlan& pla
         if (e != hipSuccess)
             return e;
     }
-    int64_t n = a.w0_per_batch ? a.H : a.H * kD * kD;
-    if (a.pro.active())
-        n = n > a.H * kDlnRows * kD ? n : a.H * kDlnRows * kD;
-    hipLaunchKernelGGL(linear_backward_reduce_kernel, dim3(static_cast<unsigned>((n + 255) / 256)),
-                       dim3(256), 0, a.stream, w.dw_chain, w.deta_chain, a.B, static_cast<int>(a.H),
-                       p.nseg, a.w0_per_batch ? 0 : 1, a.dW0, a.deta, w.dln_chain, a.dln_q,
-                       a.dln_k);
+    const int64_t w_blocks = a.w0_per_batch ? 0 : (a.H * kD * kD + 255) / 256;
+    const int64_t wave_tasks = a.H + (a.pro.active() ? a.H * kDlnRows * kD : 0);
+    hipLaunchKernelGGL(linear_backward_reduce_kernel,
+                       dim3(static_cast<unsigned>(w_blocks + (wave_tasks + 3) / 4)), dim3(256), 0,
+                       a.stream, w.dw_chain, w.deta_chain, a.B, static_cast<int>(a.H), p.nseg,
+                       w_blocks, a.dW0, a.deta, w.dln_chain, a.dln_q, a.dln_k);
     return hipGetLastError();
 }
 
