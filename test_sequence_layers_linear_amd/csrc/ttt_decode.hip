@@ -13,7 +13,9 @@
 // rows of one column, loads them once, and writes them back once.
 //
 // y_j uses q W'_j = q W_j - eta (q . k) r_j, algebraically the readout with
-// the updated column, so W is read once and written once.
+// the updated column, so W is read once and written once.  Every global load
+// is issued before the first barrier (one trip to memory per step), and
+// q . k is summed like k W_j and q W_j, from per-thread partials.
 //
 // kPro: the input prologue of ttt_linear_forward_ex for one token: q and k
 // LayerNorm'd over the head dim (waves 0 and 1, one row each, butterfly sums
@@ -60,20 +62,34 @@ decode_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
 {
     __shared__ float ks[128], qs[128];
     __shared__ float red_k[kRowGroups][kCols + 1], red_q[kRowGroups][kCols + 1];
+    __shared__ float red_qk[kRowGroups];
     __shared__ float rcol[kCols];
-    __shared__ float qk_s;
 
     const int64_t u = blockIdx.x;
     const int h = static_cast<int>(u % H);
     const int jl = threadIdx.x % kCols;
     const int ig = threadIdx.x / kCols;
     const int j = blockIdx.y * kCols + jl;
-    for (int x = threadIdx.x; x < d; x += kCols * kRowGroups) {
-        ks[x] = load_elem(k, u * d + x);
-        qs[x] = load_elem(q, u * d + x);
-    }
-    __syncthreads();
+    const int rows = d / kRowGroups;  // 1, 2, 4 or 8
+
+    // every global load first, so the step costs one trip to memory: this
+    // thread's d / 16 rows of column j of W, v_j, and (plain step) the k and
+    // q entries of those rows
+    float* Wu = W + u * d * d;
+    float w[8], kr[8], qr[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+        if (r < rows)
+            w[r] = Wu[(ig + kRowGroups * r) * d + j];
+    const float vj = load_elem(v, u * d + j);
+    const float et = (kPro && pro.eta_tok) ? pro.eta_tok[u] : eta[h];
     if constexpr (kPro) {
+        // the LayerNorm needs whole rows: stage k and q in LDS
+        for (int x = threadIdx.x; x < d; x += kCols * kRowGroups) {
+            ks[x] = load_elem(k, u * d + x);
+            qs[x] = load_elem(q, u * d + x);
+        }
+        __syncthreads();
         if (pro.ln_k || pro.ln_q) {
             const int wv = threadIdx.x >> 6;          // wave-uniform roles
             if (wv == 0 && pro.ln_k)
@@ -82,50 +98,53 @@ decode_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
                 layernorm_wave(qs, d, pro.ln_q, h, pro.ln_eps);
             __syncthreads();
         }
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+            if (r < rows) {
+                kr[r] = ks[ig + kRowGroups * r];
+                qr[r] = qs[ig + kRowGroups * r];
+            }
+    } else {
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+            if (r < rows) {
+                kr[r] = load_elem(k, u * d + ig + kRowGroups * r);
+                qr[r] = load_elem(q, u * d + ig + kRowGroups * r);
+            }
     }
 
-    float* Wu = W + u * d * d;
-    const int rows = d / kRowGroups;  // 1, 2, 4 or 8
-    float w[8];
-    float pk = 0.f, pq = 0.f;
+    // partial k W_j, q W_j and q . k over this thread's rows, then the sums
+    // over the 16 row groups
+    float pk = 0.f, pq = 0.f, pqk = 0.f;
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
+    for (int r = 0; r < 8; ++r)
         if (r < rows) {
-            const int i = ig + kRowGroups * r;
-            w[r] = Wu[i * d + j];
-            pk += ks[i] * w[r];
-            pq += qs[i] * w[r];
+            pk += kr[r] * w[r];
+            pq += qr[r] * w[r];
+            pqk += qr[r] * kr[r];
         }
-    }
     red_k[ig][jl] = pk;
     red_q[ig][jl] = pq;
-    if (threadIdx.x == 0) {
-        float acc = 0.f;
-        for (int i = 0; i < d; ++i)
-            acc += qs[i] * ks[i];
-        qk_s = acc;
-    }
+    if (jl == 0)
+        red_qk[ig] = pqk;
     __syncthreads();
-    const float et = (kPro && pro.eta_tok) ? pro.eta_tok[u] : eta[h];
     if (ig == 0) {
-        float kw = 0.f, qw = 0.f;
+        float kw = 0.f, qw = 0.f, qk = 0.f;
         for (int g = 0; g < kRowGroups; ++g) {
             kw += red_k[g][jl];
             qw += red_q[g][jl];
+            qk += red_qk[g];
         }
-        const float r = kw - load_elem(v, u * d + j);
+        const float r = kw - vj;
         rcol[jl] = r;
-        store_elem(y, u * d + j, (kPro && pro.read_start) ? qw : qw - et * qk_s * r);
+        store_elem(y, u * d + j, (kPro && pro.read_start) ? qw : qw - et * qk * r);
     }
     __syncthreads();
     const float r = rcol[jl];
 #pragma unroll
-    for (int rr = 0; rr < 8; ++rr) {
-        if (rr < rows) {
-            const int i = ig + kRowGroups * rr;
-            Wu[i * d + j] = w[rr] - et * (ks[i] * r);
-        }
-    }
+    for (int rr = 0; rr < 8; ++rr)
+        if (rr < rows)
+            Wu[(ig + kRowGroups * rr) * d + j] = w[rr] - et * (kr[rr] * r);
 }
 
 template <bool kPro>
