@@ -63,15 +63,17 @@ constexpr int kVP = 20;                          // padded V slice row (floats)
 constexpr int kTileFloats = 256;                 // one 16 x 16 accumulator tile, lane order
 constexpr int kBufferDword3 = 0x00020000;        // raw buffer resource word 3 (gfx9 family)
 
-// LDS layout (floats): a slot holds the chunk's K, Q (scan only) and V slice;
-// the partial tiles [2 parity][kinds][4 waves][256] follow the slots (the maps
-// have only P, and no Q: 25 KB, so several share a CU)
-template <bool kMaps>
+// LDS layout (floats): a slot holds the chunk's K, Q (scan only) and V slice
+// (and with the prologue its 16 step sizes); the partial tiles [2 parity]
+// [kinds][4 waves][256] follow the slots (the maps have only P, and no Q:
+// 25 KB, so several share a CU)
+template <bool kMaps, bool kPro>
 struct Lay {
     static constexpr int kOffK = 0;
     static constexpr int kOffQ = kOffK + kB * kP;
     static constexpr int kOffV = kOffQ + (kMaps ? 0 : kB * kP);
-    static constexpr int kSlotFloats = kOffV + kB * kVP;
+    static constexpr int kOffEta = kOffV + kB * kVP;
+    static constexpr int kSlotFloats = kOffEta + (kPro ? kB : 0);
     static constexpr int kKinds = kMaps ? 1 : 3;
     static constexpr int kOffPart = kSlots * kSlotFloats;
     static constexpr int kFloats = kOffPart + 2 * kKinds * kWaves * kTileFloats;
@@ -93,17 +95,23 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t chain_rsrc(const void* base, i
 
 struct StageRegs {
     u32x4 k, q, v;     // 16 bytes of K and Q row tid / 16; of the V slice (tid < 64)
+    uint32_t eta;      // step size of row tid / 16 (prologue, per-token step sizes)
 };
 
-template <bool kMaps>
+// kPro: the input prologue (Prologue in ttt_internal.h) applied as a chunk is
+// written to LDS: its K and Q rows LayerNorm'd over the head dim (16 lanes
+// per row, DPP sums) and its step sizes beside the tiles, which scale the
+// residual rows, E'[t] = -eta_t E[t]; with read_start the tril term is
+// dropped (every token reads the chunk-start W).
+template <bool kMaps, bool kPro>
 __global__ void __launch_bounds__(kThreads, 1)
 linear_cols_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                        const float* __restrict__ V, const float* W0, int w0_per_batch,
                        const float* __restrict__ eta, int H, int T, int64_t units, int seg_len,
                        int nseg, float* maps, float* wstart, float* __restrict__ Y,
-                       float* W_out, int compose)
+                       float* W_out, int compose, Prologue pro)
 {
-    using L = Lay<kMaps>;
+    using L = Lay<kMaps, kPro>;
     constexpr int kOffK = L::kOffK, kOffQ = L::kOffQ, kOffV = L::kOffV, kSlotFloats = L::kSlotFloats;
     __shared__ __attribute__((aligned(16))) float lds[L::kFloats];
 
@@ -219,6 +227,23 @@ linear_cols_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
     const int st_col = 4 * (tid & 15);
     const int sv_row = (tid & 63) >> 2;
     const int sv_col = 4 * (tid & 3);
+    // prologue: gamma, beta of this thread's 4 columns
+    const bool use_tok = kPro && pro.eta_tok != nullptr;
+    const bool ln_k = kPro && pro.ln_k != nullptr;
+    const bool ln_q = kPro && !kMaps && pro.ln_q != nullptr;
+    float gk[4], bk[4], gq[4], bq[4];
+    if constexpr (kPro) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            gk[e] = ln_k ? pro.ln_k[(2 * h) * kD + st_col + e] : 1.f;
+            bk[e] = ln_k ? pro.ln_k[(2 * h + 1) * kD + st_col + e] : 0.f;
+            gq[e] = ln_q ? pro.ln_q[(2 * h) * kD + st_col + e] : 1.f;
+            bq[e] = ln_q ? pro.ln_q[(2 * h + 1) * kD + st_col + e] : 0.f;
+        }
+    }
+    const __amdgpu_buffer_rsrc_t reta =
+        chain_rsrc(use_tok ? pro.eta_tok + u * static_cast<int64_t>(T) + t_begin : eta,
+                   use_tok ? static_cast<int64_t>(t_len) * 4 : 0);
     auto load_stage = [&](StageRegs& o, int chunk) {
         const int off = ((chunk * kB + st_row) * kD + st_col) * 4;
         o.k = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
@@ -226,12 +251,35 @@ linear_cols_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
             o.q = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0);
         o.v = __builtin_amdgcn_raw_buffer_load_b128(
             rv, ((chunk * kB + sv_row) * kD + 16 * J + sv_col) * 4, 0, 0);
+        if (use_tok)
+            o.eta = __builtin_amdgcn_raw_buffer_load_b32(reta, (chunk * kB + st_row) * 4, 0, 0);
     };
-    auto write_stage = [&](const StageRegs& o, int slot) {
-        float* sl = lds + slot * kSlotFloats;
-        *reinterpret_cast<u32x4*>(sl + kOffK + st_row * kP + st_col) = o.k;
+    auto norm = [&](u32x4 x, const float (&gm)[4], const float (&bt)[4], bool valid) {
+        float f[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            f[e] = __uint_as_float(x[e]);
+        layernorm_row<16, 4>(f, gm, bt, pro.ln_eps, valid);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            x[e] = __float_as_uint(f[e]);
+        return x;
+    };
+    auto write_stage = [&](const StageRegs& o, int chunk) {
+        float* sl = lds + (chunk % kSlots) * kSlotFloats;
+        u32x4 kx = o.k, qx = o.q;
+        if constexpr (kPro) {
+            const bool valid = chunk * kB + st_row < t_len;
+            if (ln_k)
+                kx = norm(kx, gk, bk, valid);
+            if (ln_q)
+                qx = norm(qx, gq, bq, valid);
+            if ((tid & 15) == 0)
+                sl[L::kOffEta + st_row] = use_tok ? __uint_as_float(o.eta) : et;
+        }
+        *reinterpret_cast<u32x4*>(sl + kOffK + st_row * kP + st_col) = kx;
         if (!kMaps)
-            *reinterpret_cast<u32x4*>(sl + kOffQ + st_row * kP + st_col) = o.q;
+            *reinterpret_cast<u32x4*>(sl + kOffQ + st_row * kP + st_col) = qx;
         if (w == 0)
             *reinterpret_cast<u32x4*>(sl + kOffV + sv_row * kVP + sv_col) = o.v;
     };
@@ -277,7 +325,11 @@ linear_cols_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
         for (int x = 1; x < kWaves; ++x)
             E += *reinterpret_cast<const f32x4*>(part(par, 0, x));
         E -= vv;
-        const f32x4 Ep = -et * E;
+        f32x4 Ep;
+        if constexpr (kPro)     // rows 4g + r scale by their own step sizes
+            Ep = -(*reinterpret_cast<const f32x4*>(sl + L::kOffEta + 4 * g) * E);
+        else
+            Ep = -et * E;
 #pragma unroll
         for (int r = 0; r < 4; ++r)
             Wr = mfma(kt[r], Ep[r], Wr);
@@ -290,10 +342,12 @@ linear_cols_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                 Rs += *reinterpret_cast<const f32x4*>(part(par, 1, x));
                 Ss += *reinterpret_cast<const f32x4*>(part(par, 2, x));
             }
-            // lane (c = t, g) holds S[t][s = 4g + r]: keep s <= t
+            // lane (c = t, g) holds S[t][s = 4g + r]: keep s <= t (none with
+            // the chunk-start read)
+            const bool keep = !(kPro && pro.read_start);
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                Ss[r] = 4 * g + r <= c ? Ss[r] : 0.f;
+                Ss[r] = keep && 4 * g + r <= c ? Ss[r] : 0.f;
             f32x4 Yv = Rs;
 #pragma unroll
             for (int r = 0; r < 4; ++r)
@@ -319,7 +373,7 @@ linear_cols_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
         // reloaded with chunk ch + 2 + kRing (p = ch mod kRing)
         auto advance = [&](int ch, StageRegs& set) {
             chunk_step(ch);
-            write_stage(set, (ch + 2) % kSlots);
+            write_stage(set, ch + 2);
             load_stage(set, ch + 2 + kRing);
         };
         // full rounds without exits, then the last partial round
@@ -354,10 +408,13 @@ linear_cols_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
 bool linear_cols_f32_supports(const LinearArgs& a)
 {
     const int64_t max_tokens = (int64_t{1} << 31) / (kD * 4) - kB * (kRing + 4);
-    return a.dtype == 0 && a.d == kD && a.b == kB && a.T <= max_tokens && !a.pro.active();
+    return a.dtype == 0 && a.d == kD && a.b == kB && a.T <= max_tokens;
 }
 
-hipError_t launch_linear_cols_f32(const LinearArgs& a, const SegmentPlan& p)
+namespace {
+
+template <bool kPro>
+hipError_t launch_cols(const LinearArgs& a, const SegmentPlan& p)
 {
     const auto* q = static_cast<const float*>(a.Q);
     const auto* k = static_cast<const float*>(a.K);
@@ -368,9 +425,9 @@ hipError_t launch_linear_cols_f32(const LinearArgs& a, const SegmentPlan& p)
     const int64_t units = a.B * a.H;
     if (p.nseg > 1) {
         const dim3 grid(static_cast<unsigned>(placed_grid(units, 2 * kSlices * (p.nseg - 1))));
-        hipLaunchKernelGGL((linear_cols_f32_kernel<true>), grid, dim3(kThreads), 0, a.stream, q, k, v,
-                           a.W0, a.w0_per_batch, a.eta, H, T, units, seg_len, p.nseg, p.maps,
-                           p.wstart, y, a.W_out, 0);
+        hipLaunchKernelGGL((linear_cols_f32_kernel<true, kPro>), grid, dim3(kThreads), 0, a.stream, q,
+                           k, v, a.W0, a.w0_per_batch, a.eta, H, T, units, seg_len, p.nseg, p.maps,
+                           p.wstart, y, a.W_out, 0, a.pro);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;
@@ -379,10 +436,17 @@ hipError_t launch_linear_cols_f32(const LinearArgs& a, const SegmentPlan& p)
     }
     // segments compose their start states from the maps and the copy of W0
     const dim3 grid(static_cast<unsigned>(placed_grid(units, kSlices * p.nseg)));
-    hipLaunchKernelGGL((linear_cols_f32_kernel<false>), grid, dim3(kThreads), 0, a.stream, q, k, v,
-                       a.W0, a.w0_per_batch, a.eta, H, T, units, seg_len, p.nseg, p.maps, p.wstart,
-                       y, a.W_out, 1);
+    hipLaunchKernelGGL((linear_cols_f32_kernel<false, kPro>), grid, dim3(kThreads), 0, a.stream, q, k,
+                       v, a.W0, a.w0_per_batch, a.eta, H, T, units, seg_len, p.nseg, p.maps,
+                       p.wstart, y, a.W_out, 1, a.pro);
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_linear_cols_f32(const LinearArgs& a, const SegmentPlan& p)
+{
+    return a.pro.active() ? launch_cols<true>(a, p) : launch_cols<false>(a, p);
 }
 
 }  // namespace ttt
