@@ -95,6 +95,12 @@ typedef enum {
  * not.  ttt_linear_segments reports the segment count a call would use; the
  * environment variable TTT_LINEAR_SEGMENTS=S (1..30) forces S segments.
  *
+ * fp32 Q/K/V at d = 64, b = 16 with B*H*4 <= the GPU's compute units: each
+ * chain's W is split by columns over 4 workgroups (the dual form keeps W's
+ * output columns apart), and the segments compose their own start states
+ * (no composition launch).  Same arithmetic, another order of the sums over
+ * the 64 input rows.  TTT_LINEAR_F32_COLS=0 keeps one workgroup per chain.
+ *
  * Errors: TTT_ERR_INVALID_ARG, TTT_ERR_UNSUPPORTED (d, b, dtype, or on-chip
  * memory the shape needs), TTT_ERR_HIP (including a failed workspace
  * allocation).

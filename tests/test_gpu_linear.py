@@ -295,3 +295,14 @@ def test_f32_column_split_close_to_one_workgroup(S, monkeypatch):
     ew = rel_l2(W1, W0.double().cpu().numpy())
     print(f"  rel-L2 Y {ey:.2e}  W {ew:.2e}", flush=True)
     assert ey <= 2e-6 and ew <= 2e-6
+
+
+@pytest.mark.parametrize("B,H,T", [(1, 2, 1000), (2, 2, 3001), (1, 4, 2048)])
+def test_f32_planned_segments(B, H, T):
+    """The library's own segment plan for few fp32 chains (column split, the
+    segments composing their own start states)."""
+    w = CONFIGS[2].with_(B=B, H=H, T=T, w0=("normal", 0.3), eta=("uniform", 0.01, 0.1))
+    n = ttt.ttt_linear_segments(B, H, T, 64, 16, torch.float32)
+    announce("fp32 planned segments", B, H, T, "segments", n)
+    assert n > 1
+    _check(make_inputs(w, 600 + T), 16, "fp32")

@@ -49,6 +49,20 @@ def test_prologue_small(dtype, part, B, H, T, per_batch, monkeypatch):
     assert ey <= TOL[dtype] and ew <= TOL[dtype]
 
 
+@pytest.mark.parametrize("part", ["all", "tok"])
+@pytest.mark.parametrize("T,S", [(77, 1), (333, 3)])
+def test_prologue_f32_one_workgroup_kernel(part, T, S, monkeypatch):
+    """fp32 with one workgroup per chain (the kernel for many chains; few
+    chains split W by columns unless TTT_LINEAR_F32_COLS=0)."""
+    monkeypatch.setenv("TTT_LINEAR_F32_COLS", "0")
+    monkeypatch.setenv("TTT_LINEAR_SEGMENTS", str(S))
+    w = CONFIGS[3].with_(B=2, H=3, T=T, dtype="fp32")
+    seed = 9200 + T + S
+    announce("prologue fp32 one workgroup per chain", part, T, S, seed)
+    ey, ew = _run(w, seed, PARTS[part])
+    assert ey <= TOL["fp32"] and ew <= TOL["fp32"]
+
+
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 @pytest.mark.parametrize("T,S", [(100, 2), (333, 3), (480, 30)])
 def test_prologue_segmented(dtype, T, S, monkeypatch):
@@ -95,11 +109,14 @@ def test_prologue_config_full(cfg):
     assert ey <= TOL[w.dtype] and ew <= TOL[w.dtype]
 
 
-@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("dtype", ["fp32", "bf16", "fp32-one-workgroup"])
 @pytest.mark.parametrize("T,S,parts", [(77, 1, ()), (300, 1, ("eta_tok",)), (333, 3, ("ln_q", "ln_k", "eta_tok"))])
 def test_chunk_start_read(dtype, T, S, parts, monkeypatch):
     """Tokens read out with their mini-batch's start weights (read_mode 1)."""
     monkeypatch.setenv("TTT_LINEAR_SEGMENTS", str(S))
+    if dtype == "fp32-one-workgroup":
+        monkeypatch.setenv("TTT_LINEAR_F32_COLS", "0")
+        dtype = "fp32"
     w = CONFIGS[3].with_(B=2, H=3, T=T, dtype=dtype)
     seed = 9400 + T + S
     announce("chunk-start read", dtype, T, S, parts, seed)
