@@ -203,6 +203,16 @@ mlp_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 W2b[a][b][r] = w2[(kHid * w + 16 * b + c) * kD + 16 * a + 4 * g + r];
             }
 
+    // the weights must have arrived before the scan: an empty asm use of
+    // each register makes the wait for their loads happen here, once, rather
+    // than inside the chunk loop (where the wait counters cannot tell these
+    // old loads from the staged chunks', and would drain every load in flight)
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < kHT; ++b)
+            asm volatile("" : "+v"(W1a[a][b]), "+v"(W2a[b][a]), "+v"(W2b[a][b]));
+
     bf16x4 eye;       // identity as a B operand: B[k = 4g + r][n = c] = (k == n)
 #pragma unroll
     for (int r = 0; r < 4; ++r)
