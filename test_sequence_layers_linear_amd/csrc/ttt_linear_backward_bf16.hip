@@ -118,6 +118,16 @@ __device__ __forceinline__ bf16x8 join(bf16x4 lo, bf16x4 hi)
     return __builtin_bit_cast(bf16x8, u32x4{a[0], a[1], b[0], b[1]});
 }
 
+// Raw buffer resource over a chain's rows: loads past `bytes` read zero and
+// stores past it are dropped, so the tokens past T need no branch (a memory
+// operation under a branch costs the compiler's wait counts their precision,
+// and the stage loads of the chunks ahead must stay in flight).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t chain_rsrc(const void* base, int64_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes),
+                                             0x00020000);
+}
+
 __device__ __forceinline__ int rho(int mt, int m)
 {
     return 32 * (mt >> 1) + 8 * (m >> 2) + 4 * (mt & 1) + (m & 3);
@@ -153,7 +163,9 @@ __device__ __forceinline__ bf16x8 row8(const unsigned char* tile, int r, int seg
 
 struct Stage {
     u32x2 q, k, dy;    // 4 bf16 of row tid / 16, columns 4 (tid % 16) .. +3
-    uint16_t v[4];     // V[4g + r][16w + c]: this lane's entries of its wave's columns
+    uint32_t v[4];     // V[4g + r][16w + c] of this lane's column: the 4-byte word holding
+                       // the bf16 value (a whole word: no extension after the load, so
+                       // the value can stay in flight; vneg picks the half)
     u32x4 w[2];        // W_c^T row tid / 4, segments 2 (tid % 4), +1
     float eta;         // kPro: the step size of row tid / 16 (0 past T)
     bool ok;           // row tid / 16 is a token (< T)
@@ -208,6 +220,14 @@ linear_backward_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __re
     const int c0 = s * seg_chunks;
     const int c1 = min((T + kB - 1) / kB, c0 + seg_chunks);
     const int64_t off = u * static_cast<int64_t>(T) * kD;
+    const int64_t chain_bytes = static_cast<int64_t>(T) * kD * 2;
+    const __amdgpu_buffer_rsrc_t r_q = chain_rsrc(Q + off, chain_bytes);
+    const __amdgpu_buffer_rsrc_t r_k = chain_rsrc(K + off, chain_bytes);
+    const __amdgpu_buffer_rsrc_t r_v = chain_rsrc(V + off, kGMap ? 0 : chain_bytes);
+    const __amdgpu_buffer_rsrc_t r_dy = chain_rsrc(dY + off, chain_bytes);
+    const __amdgpu_buffer_rsrc_t r_dq = chain_rsrc(dQ + off, kGMap ? 0 : chain_bytes);
+    const __amdgpu_buffer_rsrc_t r_dk = chain_rsrc(dK + off, kGMap ? 0 : chain_bytes);
+    const __amdgpu_buffer_rsrc_t r_dv = chain_rsrc(dV + off, kGMap ? 0 : chain_bytes);
     uint16_t* st = states + (u * nseg + s) * static_cast<int64_t>(seg_chunks) * kD * kD;
     const bool use_dy = !kGMap || half == 1;     // uniform per workgroup
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
@@ -236,6 +256,12 @@ linear_backward_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __re
             btk[e] = ln_k ? pro.ln_k[(2 * h + 1) * kD + scol + e] : 0.f;
         }
     }
+    const __amdgpu_buffer_rsrc_t r_eta =
+        chain_rsrc(use_tok ? pro.eta_tok + u * static_cast<int64_t>(T) : eta,
+                   use_tok ? static_cast<int64_t>(T) * 4 : 0);
+    const __amdgpu_buffer_rsrc_t r_deta =
+        chain_rsrc(use_tok && !kGMap ? deta_tok + u * static_cast<int64_t>(T) : eta,
+                   use_tok && !kGMap ? static_cast<int64_t>(T) * 4 : 0);
     // LayerNorm of a staged row segment, back to bf16; keeps xh and 1/std
     auto norm = [&](u32x2 x, const float (&gm)[4], const float (&bt)[4], bool valid,
                     float (&xh)[4], float& rstd) {
@@ -247,24 +273,24 @@ linear_backward_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __re
             f[e] = valid ? xh[e] * gm[e] + bt[e] : 0.f;
         return u32x2{cvt2(f[0], f[1]), cvt2(f[2], f[3])};
     };
-    auto load_stage = [&](Stage& x, int chunk, bool qdy, bool wst) {
+    auto load_stage = [&](Stage& x, int chunk, bool qdy, bool wst, bool with_v = true) {
         const int t = chunk * kB + srow;
-        const bool ok = t < T;
-        const int64_t e = off + static_cast<int64_t>(t) * kD + scol;
-        x.ok = ok;
-        if constexpr (kPro)
-            x.eta = !ok ? 0.f : use_tok ? pro.eta_tok[u * T + t] : et;
-        x.k = ok ? *reinterpret_cast<const u32x2*>(K + e) : u32x2{0u, 0u};
-        if (qdy) {
-            x.q = ok ? *reinterpret_cast<const u32x2*>(Q + e) : u32x2{0u, 0u};
-            x.dy = ok ? *reinterpret_cast<const u32x2*>(dY + e) : u32x2{0u, 0u};
+        const int eb = (t * kD + scol) * 2;
+        x.ok = t < T;
+        if constexpr (kPro) {
+            const float tok = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r_eta, t * 4, 0, 0));
+            x.eta = use_tok ? tok : (x.ok ? et : 0.f);
         }
-        if (!kGMap) {
+        x.k = __builtin_amdgcn_raw_buffer_load_b64(r_k, eb, 0, 0);
+        if (qdy) {
+            x.q = __builtin_amdgcn_raw_buffer_load_b64(r_q, eb, 0, 0);
+            x.dy = __builtin_amdgcn_raw_buffer_load_b64(r_dy, eb, 0, 0);
+        }
+        if (!kGMap && with_v) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int tv = chunk * kB + 4 * g + r;
-                x.v[r] = tv < T ? V[off + static_cast<int64_t>(tv) * kD + col] : uint16_t(0);
-            }
+            for (int r = 0; r < 4; ++r)
+                x.v[r] = __builtin_amdgcn_raw_buffer_load_b32(
+                    r_v, ((chunk * kB + 4 * g + r) * kD + (col & ~1)) * 2, 0, 0);
         }
         if (wst) {
             const uint16_t* src = st + static_cast<int64_t>(chunk - c0) * kD * kD + (tid >> 2) * kD;
@@ -303,11 +329,11 @@ linear_backward_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __re
         for (int q = 0; q < 2; ++q)
             *reinterpret_cast<u32x4*>(lds + kOffW + swz(tid >> 2, 2 * (tid & 3) + q)) = x.w[q];
     };
-    auto vneg = [&](const uint16_t (&v)[4]) {
+    auto vneg = [&](const uint32_t (&v)[4]) {
         f32x4 r;
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-            r[q] = -__uint_as_float(static_cast<uint32_t>(v[q]) << 16);
+            r[q] = -__uint_as_float((col & 1) ? (v[q] & 0xffff0000u) : (v[q] << 16));
         return r;
     };
 
@@ -323,37 +349,68 @@ linear_backward_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __re
                 for (int r = 0; r < 4; ++r)
                     Wacc[mt][r] = w0[rho(mt, 4 * g + r) * kD + col];
         }
-        Stage nx;
-        load_stage(nx, c0, false, false);
-        store_stage(nx, 0, false);
-        uint16_t vcur[4];
+        // The chunks ahead in two rings of kAhead register sets: K of chunk
+        // ch + 1 in kring[(ch - c0) % kAhead] (written to LDS at chunk ch),
+        // V of chunk ch in vring[(ch - c0) % kAhead] (used at chunk ch, each
+        // entry in place, so no register copy waits for a load in flight);
+        // the loop runs in rounds of kAhead chunks to keep the ring indices
+        // static, and a scheduling barrier closes each step
+        constexpr int kAhead = 4;
+        Stage kring[kAhead];
+        uint32_t vring[kAhead][4];
+        auto load_v = [&](uint32_t (&v)[4], int chunk) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            vcur[r] = nx.v[r];
+            for (int r = 0; r < 4; ++r)
+                v[r] = __builtin_amdgcn_raw_buffer_load_b32(
+                    r_v, ((chunk * kB + 4 * g + r) * kD + (col & ~1)) * 2, 0, 0);
+        };
+        {
+            Stage first;
+            load_stage(first, c0, false, false, false);
+            store_stage(first, 0, false);
+        }
+#pragma unroll
+        for (int q = 0; q < kAhead; ++q) {
+            load_v(vring[q], c0 + q);
+            load_stage(kring[q], c0 + 1 + q, false, false, false);
+        }
         __syncthreads();
-        for (int ch = c0; ch < c1; ++ch) {
+        // (`last`: the segment's last chunk, whose state is stored and nothing
+        // more; a constant false in the full rounds)
+        auto sweep1_step = [&](int ch, Stage& knext, uint32_t (&vc)[4], bool last) {
             // W_c^T row col: 16 bytes at i = 8g .. and 32 + 8g ..
             const bf16x8 b0 = pack8(Wacc[0], Wacc[1]);
             const bf16x8 b1 = pack8(Wacc[2], Wacc[3]);
             uint16_t* sc = st + static_cast<int64_t>(ch - c0) * kD * kD + col * kD;
             *reinterpret_cast<bf16x8*>(sc + 8 * g) = b0;
             *reinterpret_cast<bf16x8*>(sc + 32 + 8 * g) = b1;
-            if (ch + 1 == c1)
-                break;
-            load_stage(nx, ch + 1, false, false);
+            if (last)
+                return;
             const unsigned char* sl = lds + ((ch - c0) & 1) * kSlotBytes;
             // E = K W_J - V, W += K^T (-eta E)
-            f32x4 R = mfma32(row8(sl + kSlotK, c, g), b0, vneg(vcur));
+            f32x4 R = mfma32(row8(sl + kSlotK, c, g), b0, vneg(vc));
             R = mfma32(row8(sl + kSlotK, c, 4 + g), b1, R);
             const bf16x4 eb = pack4(-(rows_eta((ch - c0) & 1) * R));
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt)
                 Wacc[mt] = mfma16(col4_rho(sl + kSlotK, 4 * g, mt, c), eb, Wacc[mt]);
-            store_stage(nx, (ch - c0 + 1) & 1, false);
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                vcur[r] = nx.v[r];
+            load_v(vc, ch + kAhead);
+            store_stage(knext, (ch - c0 + 1) & 1, false);
+            load_stage(knext, ch + 1 + kAhead, false, false, false);
             __syncthreads();
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        int ch = c0;
+        for (; ch + kAhead < c1; ch += kAhead) {
+#pragma unroll
+            for (int q = 0; q < kAhead; ++q)
+                sweep1_step(ch + q, kring[q], vring[q], false);
+        }
+#pragma unroll
+        for (int q = 0; q < kAhead; ++q) {
+            if (ch + q >= c1)            // uniform
+                break;
+            sweep1_step(ch + q, kring[q], vring[q], ch + q + 1 == c1);
         }
         // the states just stored are read back below by other threads
         __threadfence();
@@ -379,7 +436,7 @@ linear_backward_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __re
     }
     float deta_acc = 0.f;
 
-    uint16_t vcur[4] = {0, 0, 0, 0};
+    uint32_t vcur[4] = {0, 0, 0, 0};
     if (c1 > c0) {
         Stage nx;
         load_stage(nx, c1 - 1, use_dy, !kGMap);
@@ -512,15 +569,12 @@ linear_backward_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __re
             // columns from phase A)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int t = ch * kB + 4 * g + r;
-                if (t < T) {
-                    const int64_t e = off + static_cast<int64_t>(t) * kD + col;
-                    if constexpr (!kPro) {
-                        store_elem(dQ, e, dq[r]);
-                        store_elem(dK, e, dk[r]);
-                    }
-                    store_elem(dV, e, er[r] * P[r]);
+                const int eb = ((ch * kB + 4 * g + r) * kD + col) * 2;    // past T: dropped
+                if constexpr (!kPro) {
+                    __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_bits(dq[r]), r_dq, eb, 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_bits(dk[r]), r_dk, eb, 0, 0);
                 }
+                __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_bits(er[r] * P[r]), r_dv, eb, 0, 0);
             }
             if constexpr (kPro) {
                 // the gradients of the normalised rows go to the staging
@@ -548,14 +602,16 @@ linear_backward_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __re
                 if (ln_k)
                     layernorm_row_backward<16, 4>(gk, xk, rk, gmk, dgk, dbk);
                 const int t = ch * kB + srow;
-                if (t < T) {
-                    const int64_t e = off + static_cast<int64_t>(t) * kD + scol;
-                    *reinterpret_cast<u32x2*>(dQ + e) = u32x2{cvt2(gq[0], gq[1]), cvt2(gq[2], gq[3])};
-                    *reinterpret_cast<u32x2*>(dK + e) = u32x2{cvt2(gk[0], gk[1]), cvt2(gk[2], gk[3])};
-                    if (use_tok && (tid & 15) == 0) {
-                        const float* pd = reinterpret_cast<const float*>(lds + L::kDeta);
-                        deta_tok[u * T + t] = -((pd[srow] + pd[kB + srow]) + (pd[2 * kB + srow] + pd[3 * kB + srow]));
-                    }
+                const int eb = (t * kD + scol) * 2;                     // past T: dropped
+                __builtin_amdgcn_raw_buffer_store_b64(u32x2{cvt2(gq[0], gq[1]), cvt2(gq[2], gq[3])},
+                                                      r_dq, eb, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b64(u32x2{cvt2(gk[0], gk[1]), cvt2(gk[2], gk[3])},
+                                                      r_dk, eb, 0, 0);
+                if (use_tok) {
+                    // the row's 16 lanes store the same sum (no branch)
+                    const float* pd = reinterpret_cast<const float*>(lds + L::kDeta);
+                    const float de = -((pd[srow] + pd[kB + srow]) + (pd[2 * kB + srow] + pd[3 * kB + srow]));
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(de), r_deta, t * 4, 0, 0);
                 }
             }
         }
