@@ -97,6 +97,7 @@ static_assert(kWaves * 4 * kD <= 2 * kTile, "the gamma/beta reduction fits the d
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ f32x4 mfma(float a, float b, f32x4 c)
 {
@@ -126,6 +127,16 @@ template <> struct Raw<uint16_t> {
                      __uint_as_float(x[1] << 16), __uint_as_float(x[1] & 0xffff0000u)};
     }
 };
+
+// Raw buffer resource over a chain's rows: loads past `bytes` read zero and
+// stores past it are dropped, so the tokens past T need no branch (a memory
+// operation under a branch costs the compiler's wait counts their precision,
+// and the stage loads of the chunks ahead must stay in flight).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t chain_rsrc(const void* base, int64_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes),
+                                             0x00020000);
+}
 
 __device__ __forceinline__ float to_f(float x) { return x; }
 __device__ __forceinline__ float to_f(uint16_t x) { return __uint_as_float(static_cast<uint32_t>(x) << 16); }
@@ -203,6 +214,18 @@ linear_backward_kernel(const In* __restrict__ Q, const In* __restrict__ K, const
     const int c1 = min((T + kB - 1) / kB, c0 + seg_chunks);
     const int64_t off = u * static_cast<int64_t>(T) * kD;
     float* st = states + (u * nseg + s) * static_cast<int64_t>(seg_chunks) * kD * kD;
+    static_assert(sizeof(In) == 4, "fp32 rows (bf16 inputs run in ttt_linear_backward_bf16.hip)");
+    const int64_t chain_bytes = static_cast<int64_t>(T) * kD * 4;
+    const __amdgpu_buffer_rsrc_t r_q = chain_rsrc(Q + off, chain_bytes);
+    const __amdgpu_buffer_rsrc_t r_k = chain_rsrc(K + off, chain_bytes);
+    const __amdgpu_buffer_rsrc_t r_v = chain_rsrc(V + off, kGMap ? 0 : chain_bytes);
+    const __amdgpu_buffer_rsrc_t r_dy = chain_rsrc(dY + off, chain_bytes);
+    const __amdgpu_buffer_rsrc_t r_dq = chain_rsrc(dQ + off, kGMap ? 0 : chain_bytes);
+    const __amdgpu_buffer_rsrc_t r_dk = chain_rsrc(dK + off, kGMap ? 0 : chain_bytes);
+    const __amdgpu_buffer_rsrc_t r_dv = chain_rsrc(dV + off, kGMap ? 0 : chain_bytes);
+    // this segment's chunk-start states in the workspace
+    const __amdgpu_buffer_rsrc_t r_st =
+        chain_rsrc(st, kGMap ? 0 : static_cast<int64_t>(seg_chunks) * kD * kD * 4);
     // the M half of a cotangent map sees dY = 0 (a per-workgroup, uniform branch)
     const bool use_dy = !kGMap || half == 1;
 
@@ -229,6 +252,12 @@ linear_backward_kernel(const In* __restrict__ Q, const In* __restrict__ K, const
             btk[e] = ln_k ? pro.ln_k[(2 * h + 1) * kD + scol + e] : 0.f;
         }
     }
+    const __amdgpu_buffer_rsrc_t r_eta =
+        chain_rsrc(use_tok ? pro.eta_tok + u * static_cast<int64_t>(T) : eta,
+                   use_tok ? static_cast<int64_t>(T) * 4 : 0);
+    const __amdgpu_buffer_rsrc_t r_deta =
+        chain_rsrc(use_tok && !kGMap ? deta_tok + u * static_cast<int64_t>(T) : eta,
+                   use_tok && !kGMap ? static_cast<int64_t>(T) * 4 : 0);
     auto norm = [&](f32x4 x, const float (&gm)[4], const float (&bt)[4], bool valid,
                     float (&xh)[4], float& rstd) {
         const float f[4] = {x[0], x[1], x[2], x[3]};
@@ -239,30 +268,31 @@ linear_backward_kernel(const In* __restrict__ Q, const In* __restrict__ K, const
             y[e] = valid ? xh[e] * gm[e] + bt[e] : 0.f;
         return y;
     };
-    auto load_stage = [&](Stage<In>& x, int chunk, bool qdy, bool wst) {
+    auto load_stage = [&](Stage<In>& x, int chunk, bool qdy, bool wst, bool with_v = true) {
         const int t = chunk * kB + srow;
-        const bool ok = t < T;
-        const int64_t e = off + static_cast<int64_t>(t) * kD + scol;
-        x.ok = ok;
-        if constexpr (kPro)
-            x.eta = !ok ? 0.f : use_tok ? pro.eta_tok[u * T + t] : et;
-        x.k = Raw<In>::load(K + e, ok);
-        if (!kGMap) {
+        const int eb = (t * kD + scol) * 4;
+        x.ok = t < T;
+        if constexpr (kPro) {
+            const float tok = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r_eta, t * 4, 0, 0));
+            x.eta = use_tok ? tok : (x.ok ? et : 0.f);
+        }
+        x.k = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r_k, eb, 0, 0));
+        if (!kGMap && with_v) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int tv = chunk * kB + 4 * g + r;
-                x.v[r] = tv < T ? V[off + static_cast<int64_t>(tv) * kD + 16 * w + c] : In(0);
-            }
+            for (int r = 0; r < 4; ++r)
+                x.v[r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                    r_v, ((chunk * kB + 4 * g + r) * kD + 16 * w + c) * 4, 0, 0));
         }
         if (qdy) {
-            x.q = Raw<In>::load(Q + e, ok);
-            x.dy = Raw<In>::load(dY + e, ok);
+            x.q = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r_q, eb, 0, 0));
+            x.dy = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r_dy, eb, 0, 0));
         }
         if (wst) {
-            const float* src = st + static_cast<int64_t>(chunk - c0) * kD * kD;
+            // chunk c0 - 1 (loaded ahead of the first chunk) falls outside: zeros
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-                x.w[q] = *reinterpret_cast<const f32x4*>(src + (srow + 16 * q) * kD + scol);
+                x.w[q] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                    r_st, (((chunk - c0) * kD + srow + 16 * q) * kD + scol) * 4, 0, 0));
         }
     };
     auto store_stage = [&](const Stage<In>& x, int slot, bool qdy) {
@@ -328,27 +358,44 @@ linear_backward_kernel(const In* __restrict__ Q, const In* __restrict__ K, const
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 Wt[i][r] = w0[(16 * i + 4 * g + r) * kD + 16 * w + c];
-        Stage<In> nx;
-        load_stage(nx, c0, false, false);
-        store_stage(nx, 0, false);
-        In vcur[4];
+        // The chunks ahead in two rings of kAhead register sets (as in the
+        // bf16 kernel): K of chunk ch + 1 in kring[(ch - c0) % kAhead], V of
+        // chunk ch in vring[(ch - c0) % kAhead], each entry used in place;
+        // rounds of kAhead chunks keep the indices static
+        constexpr int kAhead = 4;
+        Stage<In> kring[kAhead];
+        In vring[kAhead][4];
+        auto load_v = [&](In (&v)[4], int chunk) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            vcur[r] = nx.v[r];
+            for (int r = 0; r < 4; ++r)
+                v[r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                    r_v, ((chunk * kB + 4 * g + r) * kD + 16 * w + c) * 4, 0, 0));
+        };
+        {
+            Stage<In> first;
+            load_stage(first, c0, false, false, false);
+            store_stage(first, 0, false);
+        }
+#pragma unroll
+        for (int q = 0; q < kAhead; ++q) {
+            load_v(vring[q], c0 + q);
+            load_stage(kring[q], c0 + 1 + q, false, false, false);
+        }
         __syncthreads();
-        for (int ch = c0; ch < c1; ++ch) {
+        // (`last`: the segment's last chunk, whose state is stored and nothing
+        // more; a constant false in the full rounds)
+        auto sweep1_step = [&](int ch, Stage<In>& knext, In (&vc)[4], bool last) {
             float* sc = st + static_cast<int64_t>(ch - c0) * kD * kD;
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     sc[(16 * i + 4 * g + r) * kD + 16 * w + c] = Wt[i][r];
-            if (ch + 1 == c1)
-                break;
-            load_stage(nx, ch + 1, false, false);
+            if (last)
+                return;
             const float* sl = lds + ((ch - c0) & 1) * kSlotFloats;
             f32x4 krow[4];
-            const f32x4 E = residual(sl, Wt, vcur, krow);
+            const f32x4 E = residual(sl, Wt, vc, krow);
             const f32x4 En = -(rows_eta((ch - c0) & 1) * E);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -360,11 +407,23 @@ linear_backward_kernel(const In* __restrict__ Q, const In* __restrict__ K, const
                 for (int r = 0; r < 4; ++r)
                     Wt[i][r] = acc[r];
             }
-            store_stage(nx, (ch - c0 + 1) & 1, false);
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                vcur[r] = nx.v[r];
+            load_v(vc, ch + kAhead);
+            store_stage(knext, (ch - c0 + 1) & 1, false);
+            load_stage(knext, ch + 1 + kAhead, false, false, false);
             __syncthreads();
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        int ch = c0;
+        for (; ch + kAhead < c1; ch += kAhead) {
+#pragma unroll
+            for (int q = 0; q < kAhead; ++q)
+                sweep1_step(ch + q, kring[q], vring[q], false);
+        }
+#pragma unroll
+        for (int q = 0; q < kAhead; ++q) {
+            if (ch + q >= c1)            // uniform
+                break;
+            sweep1_step(ch + q, kring[q], vring[q], ch + q + 1 == c1);
         }
         // the states just stored are read back below by other threads
         __threadfence();
@@ -411,8 +470,9 @@ linear_backward_kernel(const In* __restrict__ Q, const In* __restrict__ K, const
         const int slot = (c1 - 1 - ch) & 1;
         const float* sl = lds + slot * kSlotFloats;
         Stage<In> nx;
-        if (ch > c0)
-            load_stage(nx, ch - 1, use_dy, !kGMap);
+        // (unconditional, so the loads keep exact wait counts: at the first
+        // chunk it reads chunk c0 - 1, unused, zeros where it is outside)
+        load_stage(nx, ch - 1, use_dy, !kGMap);
 
         // ---- phase A: columns J = w ----
         f32x4 krow[4];
@@ -576,15 +636,12 @@ linear_backward_kernel(const In* __restrict__ Q, const In* __restrict__ K, const
             // this wave's column block, so dV = eta P needs no exchange)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int t = ch * kB + 4 * g + r;
-                if (t < T) {
-                    const int64_t e = off + static_cast<int64_t>(t) * kD + 16 * w + c;
-                    if constexpr (!kPro) {
-                        store_elem(dQ, e, dq[r]);
-                        store_elem(dK, e, dk[r]);
-                    }
-                    store_elem(dV, e, er[r] * P[r]);
+                const int eb = ((ch * kB + 4 * g + r) * kD + 16 * w + c) * 4;   // past T: dropped
+                if constexpr (!kPro) {
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dq[r]), r_dq, eb, 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dk[r]), r_dk, eb, 0, 0);
                 }
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(er[r] * P[r]), r_dv, eb, 0, 0);
             }
             if constexpr (kPro) {
                 // the gradients of the normalised rows go to the staging
@@ -610,14 +667,16 @@ linear_backward_kernel(const In* __restrict__ Q, const In* __restrict__ K, const
                 if (ln_k)
                     layernorm_row_backward<16, 4>(gk, xk, rk, gmk, dgk, dbk);
                 const int t = ch * kB + srow;
-                if (t < T) {
-                    const int64_t e = off + static_cast<int64_t>(t) * kD + scol;
-                    store_row4(dQ + e, gq);
-                    store_row4(dK + e, gk);
-                    if (use_tok && (tid & 15) == 0) {
-                        const float* pd = lds + kOffDeta;
-                        deta_tok[u * T + t] = -((pd[srow] + pd[kB + srow]) + (pd[2 * kB + srow] + pd[3 * kB + srow]));
-                    }
+                const int eb = (t * kD + scol) * 4;                     // past T: dropped
+                __builtin_amdgcn_raw_buffer_store_b128(
+                    __builtin_bit_cast(u32x4, f32x4{gq[0], gq[1], gq[2], gq[3]}), r_dq, eb, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b128(
+                    __builtin_bit_cast(u32x4, f32x4{gk[0], gk[1], gk[2], gk[3]}), r_dk, eb, 0, 0);
+                if (use_tok) {
+                    // the row's 16 lanes store the same sum (no branch)
+                    const float* pd = lds + kOffDeta;
+                    const float de = -((pd[srow] + pd[kB + srow]) + (pd[2 * kB + srow] + pd[3 * kB + srow]));
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(de), r_deta, t * 4, 0, 0);
                 }
             }
         }

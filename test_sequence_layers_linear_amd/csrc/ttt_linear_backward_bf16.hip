@@ -229,6 +229,9 @@ linear_backward_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __re
     const __amdgpu_buffer_rsrc_t r_dk = chain_rsrc(dK + off, kGMap ? 0 : chain_bytes);
     const __amdgpu_buffer_rsrc_t r_dv = chain_rsrc(dV + off, kGMap ? 0 : chain_bytes);
     uint16_t* st = states + (u * nseg + s) * static_cast<int64_t>(seg_chunks) * kD * kD;
+    // this segment's chunk-start states (bf16 W^T) in the workspace
+    const __amdgpu_buffer_rsrc_t r_st =
+        chain_rsrc(st, kGMap ? 0 : static_cast<int64_t>(seg_chunks) * kD * kD * 2);
     const bool use_dy = !kGMap || half == 1;     // uniform per workgroup
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 
@@ -293,10 +296,11 @@ linear_backward_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __re
                     r_v, ((chunk * kB + 4 * g + r) * kD + (col & ~1)) * 2, 0, 0);
         }
         if (wst) {
-            const uint16_t* src = st + static_cast<int64_t>(chunk - c0) * kD * kD + (tid >> 2) * kD;
+            // chunk c0 - 1 (loaded ahead of the first chunk) falls outside: zeros
 #pragma unroll
             for (int q = 0; q < 2; ++q)
-                x.w[q] = *reinterpret_cast<const u32x4*>(src + 8 * (2 * (tid & 3) + q));
+                x.w[q] = __builtin_amdgcn_raw_buffer_load_b128(
+                    r_st, (((chunk - c0) * kD + (tid >> 2)) * kD + 8 * (2 * (tid & 3) + q)) * 2, 0, 0);
         }
     };
     // (with the prologue: LayerNorm first, and the rows' step sizes)
@@ -453,8 +457,9 @@ linear_backward_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __re
         const int slot = (c1 - 1 - ch) & 1;
         const unsigned char* sl = lds + slot * kSlotBytes;
         Stage nx;
-        if (ch > c0)
-            load_stage(nx, ch - 1, use_dy, !kGMap);
+        // (unconditional, so the loads keep exact wait counts: at the first
+        // chunk it reads chunk c0 - 1, unused, zeros where it is outside)
+        load_stage(nx, ch - 1, use_dy, !kGMap);
 
         // ---- phase A: columns J = w ----
         const bf16x8 ka0 = row8(sl + kSlotK, c, g);
