@@ -176,8 +176,15 @@ struct StageRegs {
 //   LDS, where it scales its row of the residual: E'[t] = -eta_t R[t] (the
 //   head's eta when no per-token step sizes are given); with read_start every
 //   token reads out with the chunk-start W (the tril term is dropped).
+// kMaps = false with kPro: 12 waves in two roles.  Waves 0-3 compute (as in
+//   the plain scan); waves 4-11 only stage, one stage ahead of the compute
+//   waves: waves 4-7 load K, V and the step sizes and LayerNorm K, waves
+//   8-11 load and LayerNorm Q, and both write their rows to LDS.  So the
+//   normalisation's VALU work runs beside the chunk chain on the same SIMDs
+//   (one wave of each kind per SIMD) instead of inside it.  The roles run
+//   loops of their own with one barrier per stage each.
 template <bool kMaps, bool kPro>
-__global__ void __launch_bounds__(kMaps ? 2 * kThreads : kThreads, 1)
+__global__ void __launch_bounds__(kMaps ? 2 * kThreads : (kPro ? 3 * kThreads : kThreads), 1)
 linear_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                    const uint16_t* __restrict__ V, const float* W0, int w0_per_batch,
                    const float* __restrict__ eta, int H, int T, int64_t units, int seg_len,
@@ -190,8 +197,10 @@ linear_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     const int w = (threadIdx.x >> 6) & (kWaves - 1);
     // wave-uniform role flags, made scalar so that the compiler branches on
     // them instead of masking lanes
+    constexpr bool kSplit = kPro && !kMaps;
     const int half = kMaps ? __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 8)) : 0;
-    const bool stager = !kMaps || __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6)) < kWaves;
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+    const bool stager = kSplit ? wave >= kWaves : (!kMaps || wave < kWaves);
     const int c = lane & 15;
     const int g = lane >> 4;
     const int col = 16 * w + c;          // this lane's column of W
@@ -218,7 +227,7 @@ linear_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 Wacc[mt][r] = (half == 0 && rho(mt, 4 * g + r) == col) ? 1.0f : 0.0f;
-    } else {
+    } else if (!kSplit || !stager) {
         const float* w0 = nseg > 1 ? wstart + (u * nseg + s) * kD * kD
                                    : W0 + (w0_per_batch ? u : h) * kD * kD;
 #pragma unroll
@@ -278,7 +287,7 @@ linear_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
         if (!kMaps)
             o.q = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0);
         o.v = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0);
-        if (use_tok)
+        if (kPro)             // a zero-sized resource without per-token step sizes
             o.eta = __builtin_amdgcn_raw_buffer_load_b32(reta, (stage * kStageTokens + st_row) * 4, 0, 0);
     };
     // LayerNorm of a staged row segment (8 bf16 per lane, 8 lanes per row),
@@ -312,9 +321,9 @@ linear_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
         if (!stager)
             return;
         if constexpr (kPro) {
-            if (st_seg == 0)
-                *reinterpret_cast<float*>(lds + slot * kSlotB + kSlotBytes + 4 * st_row) =
-                    use_tok ? __uint_as_float(o.eta) : et;
+            // (the 8 lanes of a row store the same value: no lane branch)
+            *reinterpret_cast<float*>(lds + slot * kSlotB + kSlotBytes + 4 * st_row) =
+                use_tok ? __uint_as_float(o.eta) : et;
         }
         unsigned char* chunk = lds + slot * kSlotB + (st_row >> 4) * kChunkBytes;
         const int r = st_row & 15;
@@ -414,7 +423,110 @@ linear_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
         prep(ahead, s + 2);
     };
 
-    if (nstages > 0) {
+    if (kSplit && nstages > 0) {
+        if (stager) {
+            // waves 4-7 (kgrp) and 8-11 run the same instruction stream on
+            // different buffers: x is K or Q, y is V or nothing, e the step
+            // sizes or nothing (a zero-sized resource reads as zero)
+            const bool kgrp = wave < 2 * kWaves;
+            const __amdgpu_buffer_rsrc_t rx = chain_rsrc((kgrp ? K : Q) + base, seg_bytes);
+            const __amdgpu_buffer_rsrc_t ry = chain_rsrc(V + base, kgrp ? seg_bytes : 0);
+            const __amdgpu_buffer_rsrc_t re =
+                chain_rsrc(use_tok ? pro.eta_tok + u * static_cast<int64_t>(T) + t_begin : eta,
+                           use_tok && kgrp ? static_cast<int64_t>(t_len) * 4 : 0);
+            const bool ln_x = kgrp ? ln_k : ln_q;
+            const int off_x = kgrp ? kOffK : kOffQ;
+            float gx[8], bx[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                gx[e] = kgrp ? gk[e] : gq[e];
+                bx[e] = kgrp ? bk[e] : bq[e];
+            }
+            struct Rows {
+                u32x4 x, y;
+                uint32_t e;
+            };
+            auto load = [&](Rows& o, int stage) {
+                const int off = (stage * kStageTokens + st_row) * kRowBytes + st_seg * 16;
+                o.x = __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0);
+                o.y = __builtin_amdgcn_raw_buffer_load_b128(ry, off, 0, 0);
+                o.e = __builtin_amdgcn_raw_buffer_load_b32(re, (stage * kStageTokens + st_row) * 4, 0, 0);
+            };
+            // LayerNorm'd rows of stage `stage` into LDS slot `slot`
+            auto put = [&](Rows& o, int stage, int slot) {
+                if (ln_x)
+                    o.x = norm(o.x, gx, bx, stage * kStageTokens + st_row < t_len);
+                unsigned char* chunk = lds + slot * kSlotB + (st_row >> 4) * kChunkBytes;
+                const int r = st_row & 15;
+                *reinterpret_cast<u32x4*>(chunk + off_x + swz(r, st_seg)) = o.x;
+                if (kgrp) {
+                    *reinterpret_cast<u32x4*>(chunk + kOffV + swz(r, st_seg)) = o.y;
+                    // (the 8 lanes of a row store the same value)
+                    *reinterpret_cast<float*>(lds + slot * kSlotB + kSlotBytes + 4 * st_row) =
+                        use_tok ? __uint_as_float(o.e) : et;
+                }
+            };
+            // stage s + 1 goes to LDS before barrier s; loads run 6 to 12
+            // stages ahead in two register sets, as in the plain scan
+            Rows setA[kSet], setB[kSet];
+            {
+                Rows first;
+                load(first, 0);
+                put(first, 0, 0);
+            }
+#pragma unroll
+            for (int p = 0; p < kSet; ++p)
+                load(setA[p], 1 + p);
+            for (int s0 = 0; s0 < nstages; s0 += 2 * kSet) {
+#pragma unroll
+                for (int p = 0; p < kSet; ++p)
+                    load(setB[p], s0 + kSet + 1 + p);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int p = 0; p < kSet; ++p) {
+                    if (s0 + p >= nstages)       // uniform: the scan is done
+                        goto done;
+                    put(setA[p], s0 + p + 1, (p + 1) % kSlots);
+                    __syncthreads();
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int p = 0; p < kSet; ++p)
+                    load(setA[p], s0 + 2 * kSet + 1 + p);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int p = 0; p < kSet; ++p) {
+                    if (s0 + kSet + p >= nstages)
+                        goto done;
+                    put(setB[p], s0 + kSet + p + 1, (kSet + p + 1) % kSlots);
+                    __syncthreads();
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        } else {
+            // the start state is in registers before the loop (otherwise the
+            // wait for it lands inside the loop and waits for the Y stores)
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+                asm volatile("" : "+v"(Wacc[mt]));
+            for (int s0 = 0; s0 < nstages; s0 += kSlots) {
+#pragma unroll
+                for (int p = 0; p < kSlots; ++p) {
+                    if (s0 + p >= nstages)
+                        goto done;
+                    __syncthreads();
+                    const unsigned char* sl = lds + p * kSlotB;
+                    ChunkOps o0, o1;
+                    read_ops(o0, sl);
+                    read_ops(o1, sl + kChunkBytes);
+                    o0.eta4 = *reinterpret_cast<const f32x4*>(sl + kSlotBytes + 16 * g);
+                    o1.eta4 = *reinterpret_cast<const f32x4*>(sl + kSlotBytes + 64 + 16 * g);
+                    step(o0, (s0 + p) * kStageTokens);
+                    step(o1, (s0 + p) * kStageTokens + kB);
+                }
+            }
+        }
+    } else if (nstages > 0) {
         StageRegs setA[kSetK], setB[kSetK];
         {
             StageRegs first;
@@ -454,6 +566,8 @@ linear_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
         }
     }
 done:
+    if (kSplit && stager)
+        return;
 
     float* wo;
     if (kMaps)
@@ -503,7 +617,8 @@ hipError_t launch_bf16(const LinearArgs& a, const SegmentPlan& p)
             return e;
     }
     const dim3 grid(static_cast<unsigned>(p.nseg > 1 ? placed_grid(units, p.nseg) : units));
-    hipLaunchKernelGGL((linear_mfma_kernel<false, kPro>), grid, dim3(kThreads), lds, a.stream, q, k, v,
+    hipLaunchKernelGGL((linear_mfma_kernel<false, kPro>), grid, dim3(kPro ? 3 * kThreads : kThreads), lds,
+                       a.stream, q, k, v,
                        a.W0, a.w0_per_batch, a.eta, H, T, units, seg_len, p.nseg, p.maps, p.wstart, y,
                        a.W_out, a.pro);
     return hipGetLastError();
