@@ -28,6 +28,12 @@ KERNEL_FILES = {
     "linear_mfma_f32_kernel[maps]": "ttt_linear_mfma_f32.hip",
     "linear_cols_f32_kernel[scan]": "ttt_linear_cols_f32.hip",
     "linear_cols_f32_kernel[maps]": "ttt_linear_cols_f32.hip",
+    "linear_mfma_kernel[scan+prologue]": "ttt_linear_mfma.hip",
+    "linear_mfma_kernel[maps+prologue]": "ttt_linear_mfma.hip",
+    "linear_mfma_f32_kernel[scan+prologue]": "ttt_linear_mfma_f32.hip",
+    "linear_mfma_f32_kernel[maps+prologue]": "ttt_linear_mfma_f32.hip",
+    "linear_cols_f32_kernel[scan+prologue]": "ttt_linear_cols_f32.hip",
+    "linear_cols_f32_kernel[maps+prologue]": "ttt_linear_cols_f32.hip",
     "linear_combine_kernel": "ttt_linear_combine.hip",
     "linear_backward_kernel[gmaps]": "ttt_linear_backward.hip",
     "linear_backward_kernel[segments]": "ttt_linear_backward.hip",
@@ -48,7 +54,7 @@ COPY_NAME = "__amd_rocclr_copyBuffer"
 
 def short_name(full: str) -> str:
     """Kernel key: the function name, with [maps] / [scan] for the two
-    instantiations of the TTT-Linear MFMA kernels and [gmaps] / [segments]
+    instantiations of the TTT-Linear forward kernels and [gmaps] / [segments]
     for the backward's cotangent maps and segment backward (+prologue for
     the instantiations with the input prologue)."""
     for base in ("linear_backward_kernel", "linear_backward_bf16_kernel"):
@@ -59,10 +65,13 @@ def short_name(full: str) -> str:
             return f"{base}[{role}{'+prologue' if flags[1] == 'true' else ''}]"
     for k in KERNEL_FILES:
         base = k.split("[")[0]
-        if base + "<true" in full:
-            return base + "[maps]"
-        if base + "<false" in full:
-            return base + "[scan]"
+        if base.startswith("linear_backward"):
+            continue
+        if base + "<true" in full or base + "<false" in full:
+            args = [a.strip() for a in full.split(base + "<", 1)[1].split(">", 1)[0].split(",")]
+            flags = [a for a in args if a in ("true", "false")]     # kMaps, kPro
+            pro = "+prologue" if len(flags) > 1 and flags[1] == "true" else ""
+            return f"{base}[{'maps' if flags[0] == 'true' else 'scan'}{pro}]"
         if base + "(" in full or base + "<" in full:
             return k
     return full.split("(")[0][-60:]
