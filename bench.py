@@ -421,8 +421,8 @@ def run_cpu_baseline(w, host, target_s):
 
 # ---------------------------------------------------------------------------
 def measure_workload(cfg, steps, warmup, cold_reps):
-    from test_sequence_layers_linear_amd.inputs import CONFIGS, default_seed
-    w = CONFIGS[cfg]
+    from test_sequence_layers_linear_amd.inputs import WORKLOADS, default_seed
+    w = WORKLOADS[cfg]
     r = Runner(w, default_seed(cfg))
     per_step, fwd, dec = r.measure(steps, warmup)
     flops, nbytes = (linear_work if w.kind == "linear" else mlp_work)(w)
@@ -471,7 +471,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on exactly one GPU: this build has no multi-GPU path "
+        print(f"bench.py runs on exactly one GPU: the library has no multi-GPU path "
               f"(--gpus {args.gpus} requested). (batch, head) chains are independent, so "
               "several GPUs would each run this same kernel on their share.", file=sys.stderr)
         sys.exit(2)

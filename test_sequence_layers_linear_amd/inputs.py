@@ -68,7 +68,7 @@ class Workload:
         return torch.float32 if self.dtype == "fp32" else torch.bfloat16
 
 
-CONFIGS = {
+WORKLOADS = {
     1: Workload("linear", B=1, H=1, T=64, d=16, b=16, dtype="fp32", w0=("zero",),
                 eta=("const", 0.1), name="ttt_linear_B1_H1_d16_T64_b16_fp32"),
     2: Workload("linear", B=1, H=4, T=2048, d=64, b=16, dtype="fp32", w0=("normal", 0.02),

@@ -115,15 +115,15 @@ def main():
 
     import sys
     sys.path.insert(0, ROOT)
-    from test_sequence_layers_linear_amd.inputs import CONFIGS
-    w = CONFIGS[args.config]
+    from test_sequence_layers_linear_amd.inputs import WORKLOADS
+    w = WORKLOADS[args.config]
 
     stats = list(csv.DictReader(open(one_csv(args.trace, "kernel_stats.csv"))))
     have_bytes = bool(args.fetch and args.write)
     fetch = counter_per_kernel(args.fetch) if have_bytes else {}
     write = counter_per_kernel(args.write) if have_bytes else {}
     lines = [f"# rocprofv3 summary: {args.title or w.name}", "",
-             "Commands (run from /tmp on the GPU box, repo at $R):", "", "```", args.command, "```", ""]
+             "Commands (run from /tmp on the MI355X host, repo at $R):", "", "```", args.command, "```", ""]
     f_scale = w_scale = 1.0
     if have_bytes:
         copy_bytes = args.copy_mib * 1024 * 1024

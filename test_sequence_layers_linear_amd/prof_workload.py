@@ -31,10 +31,10 @@ def main():
 
     import torch
     import test_sequence_layers_linear_amd as ttt
-    from test_sequence_layers_linear_amd.inputs import (CONFIGS, default_seed, make_cotangents,
+    from test_sequence_layers_linear_amd.inputs import (WORKLOADS, default_seed, make_cotangents,
                                                         make_inputs, make_prologue)
 
-    w = CONFIGS[args.config]
+    w = WORKLOADS[args.config]
     g = {k: v.cuda() for k, v in make_inputs(w, default_seed(args.config)).items()}
     Y = torch.empty_like(g["Q"])
     if w.kind == "linear":

@@ -4,7 +4,7 @@ import torch
 
 import oracle
 import test_sequence_layers_linear_amd as ttt
-from test_sequence_layers_linear_amd.inputs import CONFIGS, Workload, default_seed, make_inputs
+from test_sequence_layers_linear_amd.inputs import WORKLOADS, Workload, default_seed, make_inputs
 
 # relative-L2 bounds: fp32 inputs 1e-4, bf16 inputs with fp32 state 2e-2
 TOL = {"fp32": 1e-4, "bf16": 2e-2}
@@ -69,5 +69,5 @@ def announce(*parts):
 
 
 __all__ = ["TOL", "rel_l2", "to_gpu", "select_chains", "linear_oracle", "mlp_oracle",
-           "linear_gpu", "mlp_gpu", "sample_chains", "announce", "CONFIGS", "Workload",
+           "linear_gpu", "mlp_gpu", "sample_chains", "announce", "WORKLOADS", "Workload",
            "default_seed", "make_inputs"]

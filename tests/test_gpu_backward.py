@@ -13,7 +13,7 @@ import torch
 
 import oracle
 import test_sequence_layers_linear_amd as ttt
-from parity_util import CONFIGS, TOL, announce, default_seed, make_inputs, rel_l2, to_gpu
+from parity_util import WORKLOADS, TOL, announce, default_seed, make_inputs, rel_l2, to_gpu
 from test_sequence_layers_linear_amd.inputs import make_cotangents
 
 pytestmark = pytest.mark.gpu
@@ -54,7 +54,7 @@ def _compare(got, ref, tol, skip=()):
     (3, 2, 96, False, True),      # final state unused (dW_out = 0)
 ])
 def test_backward_small(dtype, B, H, T, per_batch, zero_state):
-    w = CONFIGS[3].with_(B=B, H=H, T=T, dtype=dtype, eta=("uniform", 0.1, 0.6))
+    w = WORKLOADS[3].with_(B=B, H=H, T=T, dtype=dtype, eta=("uniform", 0.1, 0.6))
     seed = 7000 + B * 100 + H * 10 + T
     announce("backward", dtype, B, H, T, "per_batch" if per_batch else "shared", seed)
     inp = make_inputs(w, seed, w0_per_batch=per_batch)
@@ -75,7 +75,7 @@ def test_backward_segmented(dtype, B, H, T, S, per_batch, monkeypatch):
     got_s = ttt.ttt_linear_backward_segments(B, H, T, 64, 16,
                                              torch.float32 if dtype == "fp32" else torch.bfloat16)
     assert got_s == S
-    w = CONFIGS[3].with_(B=B, H=H, T=T, dtype=dtype, eta=("uniform", 0.1, 0.6))
+    w = WORKLOADS[3].with_(B=B, H=H, T=T, dtype=dtype, eta=("uniform", 0.1, 0.6))
     seed = 7300 + B * 100 + H * 10 + S
     announce("backward segmented", dtype, B, H, T, "segments", S, seed)
     inp = make_inputs(w, seed, w0_per_batch=per_batch)
@@ -86,7 +86,7 @@ def test_backward_segmented(dtype, B, H, T, S, per_batch, monkeypatch):
 def test_backward_segmented_close_to_single_segment(monkeypatch):
     """fp32: a segmented backward is the same arithmetic in another rounding
     order of the state and the cotangent."""
-    w = CONFIGS[2]
+    w = WORKLOADS[2]
     announce("backward segments vs one segment", w.name)
     inp = make_inputs(w, default_seed(2))
     cot = make_cotangents(w, default_seed(2) + 500)
@@ -100,7 +100,7 @@ def test_backward_segmented_close_to_single_segment(monkeypatch):
 
 
 def test_backward_empty_sequence():
-    w = CONFIGS[3].with_(B=2, H=3, T=0)
+    w = WORKLOADS[3].with_(B=2, H=3, T=0)
     announce("backward T=0")
     inp = make_inputs(w, 7100)
     cot = make_cotangents(w, 7101)
@@ -111,7 +111,7 @@ def test_backward_empty_sequence():
 
 
 def test_backward_deterministic():
-    w = CONFIGS[3].with_(B=2, H=4, T=300)
+    w = WORKLOADS[3].with_(B=2, H=4, T=300)
     announce("backward determinism")
     inp = to_gpu(make_inputs(w, 7200))
     cot = to_gpu(make_cotangents(w, 7201))
@@ -126,7 +126,7 @@ def test_backward_deterministic():
 
 @pytest.mark.parametrize("cfg", [2, 3])
 def test_backward_config_full(cfg):
-    w = CONFIGS[cfg]
+    w = WORKLOADS[cfg]
     announce("backward config", cfg, w.name, "segments",
              ttt.ttt_linear_backward_segments(w.B, w.H, w.T, w.d, w.b, w.torch_dtype))
     inp = make_inputs(w, default_seed(cfg))
@@ -135,7 +135,7 @@ def test_backward_config_full(cfg):
 
 
 def test_backward_config4_sampled_chains():
-    w = CONFIGS[4]
+    w = WORKLOADS[4]
     announce("backward config 4 sampled chains", w.name)
     inp = make_inputs(w, default_seed(4), w0_per_batch=True)
     cot = make_cotangents(w, default_seed(4) + 500)

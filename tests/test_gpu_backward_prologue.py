@@ -16,7 +16,7 @@ import torch
 
 import oracle
 import test_sequence_layers_linear_amd as ttt
-from parity_util import CONFIGS, TOL, announce, default_seed, make_inputs, rel_l2, to_gpu
+from parity_util import WORKLOADS, TOL, announce, default_seed, make_inputs, rel_l2, to_gpu
 from test_sequence_layers_linear_amd.inputs import make_cotangents, make_prologue
 
 pytestmark = pytest.mark.gpu
@@ -61,7 +61,7 @@ def _compare(got, ref, tol, names=None):
 @pytest.mark.parametrize("B,H,T,per_batch", [(1, 2, 16, False), (2, 3, 77, True), (1, 2, 300, False)])
 def test_backward_prologue_small(dtype, part, read_start, B, H, T, per_batch, monkeypatch):
     monkeypatch.setenv("TTT_LINEAR_BWD_SEGMENTS", "1")
-    w = CONFIGS[3].with_(B=B, H=H, T=T, dtype=dtype)
+    w = WORKLOADS[3].with_(B=B, H=H, T=T, dtype=dtype)
     seed = 9500 + B * 100 + H * 10 + T
     announce("backward prologue", dtype, part, "start-read" if read_start else "", B, H, T, seed)
     inp, kw, cot = _case(w, seed, PARTS[part], per_batch)
@@ -75,7 +75,7 @@ def test_backward_prologue_small(dtype, part, read_start, B, H, T, per_batch, mo
 
 def test_backward_read_start_alone():
     # only the chunk-start read: no LayerNorm, the head's step size
-    w = CONFIGS[3].with_(B=2, H=2, T=90, dtype="fp32")
+    w = WORKLOADS[3].with_(B=2, H=2, T=90, dtype="fp32")
     announce("backward chunk-start read only")
     inp, _, cot = _case(w, 9601, ())
     _compare(_gpu(inp, {}, cot, 16, True), _oracle(inp, {}, cot, 16, True), TOL["fp32"])
@@ -85,7 +85,7 @@ def test_backward_read_start_alone():
 @pytest.mark.parametrize("T,S,per_batch", [(100, 2, False), (333, 3, True), (480, 30, False)])
 def test_backward_prologue_segmented(dtype, T, S, per_batch, monkeypatch):
     monkeypatch.setenv("TTT_LINEAR_BWD_SEGMENTS", str(S))
-    w = CONFIGS[3].with_(B=2, H=2, T=T, dtype=dtype)
+    w = WORKLOADS[3].with_(B=2, H=2, T=T, dtype=dtype)
     assert ttt.ttt_linear_backward_segments(w.B, w.H, w.T, w.d, w.b, w.torch_dtype) == S
     seed = 9700 + T + S
     announce("backward prologue segmented", dtype, T, S, seed)
@@ -94,7 +94,7 @@ def test_backward_prologue_segmented(dtype, T, S, per_batch, monkeypatch):
 
 
 def test_backward_prologue_empty_sequence():
-    w = CONFIGS[3].with_(B=2, H=3, T=0)
+    w = WORKLOADS[3].with_(B=2, H=3, T=0)
     announce("backward prologue T=0")
     inp, kw, cot = _case(w, 9800, PARTS["all"])
     got = _gpu(inp, kw, cot, 16, False)
@@ -105,7 +105,7 @@ def test_backward_prologue_empty_sequence():
 
 
 def test_backward_prologue_deterministic():
-    w = CONFIGS[3].with_(B=2, H=4, T=300)
+    w = WORKLOADS[3].with_(B=2, H=4, T=300)
     announce("backward prologue determinism")
     inp, kw, cot = _case(w, 9810, PARTS["all"])
     a = _gpu(inp, kw, cot, 16, False)
@@ -116,7 +116,7 @@ def test_backward_prologue_deterministic():
 
 @pytest.mark.parametrize("cfg", [2, 3])
 def test_backward_prologue_config_full(cfg):
-    w = CONFIGS[cfg]
+    w = WORKLOADS[cfg]
     announce("backward prologue config", cfg, w.name, "segments",
              ttt.ttt_linear_backward_segments(w.B, w.H, w.T, w.d, w.b, w.torch_dtype))
     inp, kw, cot = _case(w, default_seed(cfg) + 700, PARTS["all"])
@@ -124,7 +124,7 @@ def test_backward_prologue_config_full(cfg):
 
 
 def test_backward_prologue_config4_sampled_chains():
-    w = CONFIGS[4]
+    w = WORKLOADS[4]
     announce("backward prologue config 4 sampled chains", w.name)
     inp, kw, cot = _case(w, default_seed(4) + 700, PARTS["all"], per_batch=True)
     got = _gpu(inp, kw, cot, w.b, False)

@@ -5,7 +5,7 @@ import torch
 
 import oracle
 import test_sequence_layers_linear_amd as ttt
-from parity_util import (CONFIGS, TOL, announce, default_seed, linear_gpu, make_inputs, rel_l2,
+from parity_util import (WORKLOADS, TOL, announce, default_seed, linear_gpu, make_inputs, rel_l2,
                          sample_chains, select_chains, to_gpu)
 
 pytestmark = pytest.mark.gpu
@@ -16,7 +16,7 @@ pytestmark = pytest.mark.gpu
 def test_decode_steps_match_online_gd(d, dtype):
     """n decode steps from a per-(batch, head) state == the oracle's b = 1 scan."""
     announce("decode", d, dtype)
-    w = CONFIGS[2].with_(B=2, H=3, T=9, d=d, dtype=dtype, eta=("uniform", 0.01, 0.1))
+    w = WORKLOADS[2].with_(B=2, H=3, T=9, d=d, dtype=dtype, eta=("uniform", 0.01, 0.1))
     inp = make_inputs(w, 70 + d, w0_per_batch=True)
     Yr, Wr = oracle.linear_forward(inp["Q"], inp["K"], inp["V"], inp["W0"], inp["eta"], 1)
     g = to_gpu(inp)
@@ -36,7 +36,7 @@ def test_decode_steps_match_online_gd(d, dtype):
 def test_config4_prefill_then_256_decode_steps():
     """The long-context workload's tail: forward over T = 32768 tokens, then
     256 single-token steps from the final W, on sampled chains."""
-    w = CONFIGS[4]
+    w = WORKLOADS[4]
     announce("decode after config 4 prefill", w.name)
     inp = make_inputs(w, default_seed(4))
     g = to_gpu(inp)
@@ -82,7 +82,7 @@ def test_decode_steps_in_a_hip_graph_match_eager():
     """Decode steps captured once in a HIP graph and replayed several times
     (with eager work and synchronisation between the replays) give exactly
     the eager results each time."""
-    w = CONFIGS[4].with_(B=2, H=3, T=16, decode_steps=8)
+    w = WORKLOADS[4].with_(B=2, H=3, T=16, decode_steps=8)
     g = to_gpu(make_inputs(w, 91, w0_per_batch=True))
     W = g["W0"].clone()
     y = torch.empty_like(g["dq"][0])

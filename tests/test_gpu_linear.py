@@ -15,7 +15,7 @@ import pytest
 import torch
 
 import test_sequence_layers_linear_amd as ttt
-from parity_util import (CONFIGS, TOL, announce, default_seed, linear_gpu, linear_oracle,
+from parity_util import (WORKLOADS, TOL, announce, default_seed, linear_gpu, linear_oracle,
                          make_inputs, rel_l2, sample_chains, select_chains, to_gpu)
 
 pytestmark = pytest.mark.gpu
@@ -33,14 +33,14 @@ def _check(inp, b, dtype, tol=None):
 
 @pytest.mark.parametrize("cfg", [1, 2, 3])
 def test_config_full(cfg):
-    w = CONFIGS[cfg]
+    w = WORKLOADS[cfg]
     announce("linear config", cfg, w.name)
     inp = make_inputs(w, default_seed(cfg))
     _check(inp, w.b, w.dtype)
 
 
 def test_config4_sampled_chains_full_length():
-    w = CONFIGS[4]
+    w = WORKLOADS[4]
     announce("linear config 4 sampled chains", w.name)
     inp = make_inputs(w, default_seed(4))
     Y, W = linear_gpu(to_gpu(inp), w.b)
@@ -64,14 +64,14 @@ def test_config4_sampled_chains_full_length():
 @pytest.mark.parametrize("B,H,T", [(1, 1, 1), (1, 1, 5), (1, 1, 16), (1, 1, 17), (1, 3, 31),
                                    (2, 3, 48), (3, 1, 100), (1, 7, 257), (2, 2, 1000)])
 def test_mfma_shapes(B, H, T):
-    w = CONFIGS[3].with_(B=B, H=H, T=T)
+    w = WORKLOADS[3].with_(B=B, H=H, T=T)
     announce("linear mfma", B, H, T)
     _check(make_inputs(w, 7 + T), 16, "bf16")
 
 
 @pytest.mark.parametrize("B,H,T", [(1, 1, 1), (1, 1, 17), (2, 3, 48), (1, 7, 257), (2, 2, 1000)])
 def test_mfma_fp32_shapes(B, H, T):
-    w = CONFIGS[2].with_(B=B, H=H, T=T, eta=("uniform", 0.01, 0.1))
+    w = WORKLOADS[2].with_(B=B, H=H, T=T, eta=("uniform", 0.01, 0.1))
     announce("linear mfma fp32", B, H, T)
     _check(make_inputs(w, 9 + T), 16, "fp32")
 
@@ -82,13 +82,13 @@ def test_mfma_fp32_shapes(B, H, T):
                                        (32, 16, "bf16"), (128, 16, "bf16"), (64, 8, "bf16"),
                                        (64, 32, "bf16"), (64, 1, "bf16")])
 def test_generic_shapes(d, b, dtype):
-    w = CONFIGS[2].with_(B=2, H=3, T=3 * b + 5, d=d, b=b, dtype=dtype, eta=("uniform", 0.01, 0.1))
+    w = WORKLOADS[2].with_(B=2, H=3, T=3 * b + 5, d=d, b=b, dtype=dtype, eta=("uniform", 0.01, 0.1))
     announce("linear generic", d, b, dtype)
     _check(make_inputs(w, 100 + d + b), b, dtype)
 
 
 def test_empty_sequence_copies_state():
-    w = CONFIGS[3].with_(B=2, H=3, T=0)
+    w = WORKLOADS[3].with_(B=2, H=3, T=0)
     inp = to_gpu(make_inputs(w, 5))
     Y, W = linear_gpu(inp, 16)
     assert Y.shape == (2, 3, 0, 64)
@@ -97,7 +97,7 @@ def test_empty_sequence_copies_state():
 
 @pytest.mark.parametrize("cfg", [2, 3])
 def test_eta_zero(cfg):
-    w = CONFIGS[cfg].with_(B=2, H=2, T=100, eta=("const", 0.0))
+    w = WORKLOADS[cfg].with_(B=2, H=2, T=100, eta=("const", 0.0))
     inp = make_inputs(w, 11)
     g = to_gpu(inp)
     Y, W = linear_gpu(g, 16)
@@ -156,7 +156,7 @@ def test_worked_examples_bit_exact(path):
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("cfg", [2, 3])
 def test_deterministic(cfg):
-    w = CONFIGS[cfg].with_(B=2, H=3, T=512)
+    w = WORKLOADS[cfg].with_(B=2, H=3, T=512)
     g = to_gpu(make_inputs(w, 21))
     Y1, W1 = linear_gpu(g, 16)
     Y2, W2 = linear_gpu(g, 16)
@@ -169,7 +169,7 @@ def test_chaining_through_state_is_exact(cfg, monkeypatch):
     the fp32 state is stored and reloaded exactly (one segment per chain: a
     segmented scan composes the same updates in another order)."""
     monkeypatch.setenv("TTT_LINEAR_SEGMENTS", "1")
-    w = CONFIGS[cfg].with_(B=2, H=3, T=160)
+    w = WORKLOADS[cfg].with_(B=2, H=3, T=160)
     g = to_gpu(make_inputs(w, 31))
     Y, W = linear_gpu(g, 16)
     first = {k: (v[:, :, :64].contiguous() if k in "QKV" else v) for k, v in g.items()}
@@ -183,7 +183,7 @@ def test_chaining_through_state_is_exact(cfg, monkeypatch):
 
 @pytest.mark.parametrize("cfg", [2, 3])
 def test_in_place_state_update(cfg):
-    w = CONFIGS[cfg].with_(B=2, H=3, T=80)
+    w = WORKLOADS[cfg].with_(B=2, H=3, T=80)
     inp = make_inputs(w, 41, w0_per_batch=True)
     g = to_gpu(inp)
     Y_ref, W_ref = linear_gpu(g, 16)
@@ -196,7 +196,7 @@ def test_in_place_state_update(cfg):
 
 @pytest.mark.parametrize("cfg", [2, 3])
 def test_guard_bands_untouched(cfg):
-    w = CONFIGS[cfg].with_(B=2, H=3, T=37)
+    w = WORKLOADS[cfg].with_(B=2, H=3, T=37)
     g = to_gpu(make_inputs(w, 51))
     G = 4096
     dt = g["Q"].dtype
@@ -214,7 +214,7 @@ def test_guard_bands_untouched(cfg):
 
 
 def test_nan_propagates():
-    w = CONFIGS[3].with_(B=1, H=2, T=64)
+    w = WORKLOADS[3].with_(B=1, H=2, T=64)
     inp = make_inputs(w, 61)
     inp["V"][0, 1, 20, 3] = float("nan")
     Y, W = linear_gpu(to_gpu(inp), 16)
@@ -232,7 +232,7 @@ def test_nan_propagates():
                                            (100, 50, True), (512, 4, False), (48, 3, False)])
 def test_segmented_scan(cfg, T, S, per_batch, monkeypatch):
     monkeypatch.setenv("TTT_LINEAR_SEGMENTS", str(S))
-    w = CONFIGS[cfg].with_(B=2, H=3, T=T, w0=("normal", 0.3), eta=("uniform", 0.01, 0.1))
+    w = WORKLOADS[cfg].with_(B=2, H=3, T=T, w0=("normal", 0.3), eta=("uniform", 0.01, 0.1))
     announce("linear segmented", cfg, T, S, per_batch)
     _check(make_inputs(w, 400 + T + S, w0_per_batch=per_batch), 16, w.dtype)
 
@@ -242,7 +242,7 @@ def test_segmented_in_place_and_deterministic(cfg, monkeypatch):
     """W_out == W0 with several segments: the later segments still start from
     the original W0; repeated calls agree bit for bit."""
     monkeypatch.setenv("TTT_LINEAR_SEGMENTS", "4")
-    w = CONFIGS[cfg].with_(B=2, H=3, T=300)
+    w = WORKLOADS[cfg].with_(B=2, H=3, T=300)
     g = to_gpu(make_inputs(w, 71, w0_per_batch=True))
     Y_ref, W_ref = linear_gpu(g, 16)
     Y_again, W_again = linear_gpu(g, 16)
@@ -255,7 +255,7 @@ def test_segmented_in_place_and_deterministic(cfg, monkeypatch):
 
 def test_segmented_close_to_single_segment(monkeypatch):
     """fp32: the composed maps change only the rounding order."""
-    w = CONFIGS[2].with_(B=1, H=4, T=1024, w0=("normal", 0.3))
+    w = WORKLOADS[2].with_(B=1, H=4, T=1024, w0=("normal", 0.3))
     g = to_gpu(make_inputs(w, 81))
     monkeypatch.setenv("TTT_LINEAR_SEGMENTS", "1")
     Y1, W1 = linear_gpu(g, 16)
@@ -275,7 +275,7 @@ def test_segmented_close_to_single_segment(monkeypatch):
 def test_f32_one_workgroup_kernel(T, S, per_batch, monkeypatch):
     monkeypatch.setenv("TTT_LINEAR_F32_COLS", "0")
     monkeypatch.setenv("TTT_LINEAR_SEGMENTS", str(S))
-    w = CONFIGS[2].with_(B=2, H=3, T=T, w0=("normal", 0.3), eta=("uniform", 0.01, 0.1))
+    w = WORKLOADS[2].with_(B=2, H=3, T=T, w0=("normal", 0.3), eta=("uniform", 0.01, 0.1))
     announce("linear fp32 one workgroup per chain", T, S, per_batch)
     _check(make_inputs(w, 500 + T + S, w0_per_batch=per_batch), 16, "fp32")
 
@@ -285,7 +285,7 @@ def test_f32_column_split_close_to_one_workgroup(S, monkeypatch):
     """The column split changes only the order of the sums over the 64 input
     rows (four partial products added in LDS)."""
     monkeypatch.setenv("TTT_LINEAR_SEGMENTS", S)
-    w = CONFIGS[2].with_(B=1, H=4, T=1100, w0=("normal", 0.3))
+    w = WORKLOADS[2].with_(B=1, H=4, T=1100, w0=("normal", 0.3))
     announce("fp32 column split vs one workgroup", S)
     g = to_gpu(make_inputs(w, 91))
     Y1, W1 = linear_gpu(g, 16)
@@ -301,7 +301,7 @@ def test_f32_column_split_close_to_one_workgroup(S, monkeypatch):
 def test_f32_planned_segments(B, H, T):
     """The library's own segment plan for few fp32 chains (column split, the
     segments composing their own start states)."""
-    w = CONFIGS[2].with_(B=B, H=H, T=T, w0=("normal", 0.3), eta=("uniform", 0.01, 0.1))
+    w = WORKLOADS[2].with_(B=B, H=H, T=T, w0=("normal", 0.3), eta=("uniform", 0.01, 0.1))
     n = ttt.ttt_linear_segments(B, H, T, 64, 16, torch.float32)
     announce("fp32 planned segments", B, H, T, "segments", n)
     assert n > 1

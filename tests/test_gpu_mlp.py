@@ -3,7 +3,7 @@ import pytest
 import torch
 
 import test_sequence_layers_linear_amd as ttt
-from parity_util import (CONFIGS, TOL, announce, default_seed, make_inputs, mlp_gpu, mlp_oracle,
+from parity_util import (WORKLOADS, TOL, announce, default_seed, make_inputs, mlp_gpu, mlp_oracle,
                          rel_l2, sample_chains, select_chains, to_gpu)
 
 pytestmark = pytest.mark.gpu
@@ -25,7 +25,7 @@ def _check(inp, b, dtype):
                                            (16, 16, 1, 9, "fp32")])
 def test_mlp_shapes(d, m, b, T, dtype):
     announce("mlp", d, m, b, T, dtype)
-    w = CONFIGS[5].with_(B=2, H=3, T=T, d=d, m=m, b=b, dtype=dtype)
+    w = WORKLOADS[5].with_(B=2, H=3, T=T, d=d, m=m, b=b, dtype=dtype)
     _check(make_inputs(w, 200 + d + m + T), b, dtype)
 
 
@@ -37,12 +37,12 @@ def test_mlp_strong_state(T, std, eta, per_batch):
     updates change Y by 70-100 % in rel-L2 here; larger eta at T = 100 makes
     the inner descent itself diverge)."""
     announce("mlp strong state", T, std, eta, per_batch)
-    w = CONFIGS[5].with_(B=2, H=3, T=T, w0=("normal", std), eta=("const", eta))
+    w = WORKLOADS[5].with_(B=2, H=3, T=T, w0=("normal", std), eta=("const", eta))
     _check(make_inputs(w, 300 + T, w0_per_batch=per_batch), 16, "bf16")
 
 
 def test_config5_sampled_chains_full_length():
-    w = CONFIGS[5]
+    w = WORKLOADS[5]
     announce("mlp config 5 sampled chains", w.name)
     inp = make_inputs(w, default_seed(5))
     Y, W1, W2 = mlp_gpu(to_gpu(inp), w.b)
@@ -57,7 +57,7 @@ def test_config5_sampled_chains_full_length():
 
 
 def test_mlp_eta_zero_keeps_state():
-    w = CONFIGS[5].with_(B=1, H=2, T=64, eta=("const", 0.0))
+    w = WORKLOADS[5].with_(B=1, H=2, T=64, eta=("const", 0.0))
     g = to_gpu(make_inputs(w, 9))
     Y, W1, W2 = mlp_gpu(g, 16)
     assert torch.equal(W1, g["W1"][None].expand_as(W1))
@@ -65,7 +65,7 @@ def test_mlp_eta_zero_keeps_state():
 
 
 def test_mlp_deterministic_and_empty():
-    w = CONFIGS[5].with_(B=2, H=2, T=80)
+    w = WORKLOADS[5].with_(B=2, H=2, T=80)
     g = to_gpu(make_inputs(w, 19))
     a = mlp_gpu(g, 16)
     b = mlp_gpu(g, 16)

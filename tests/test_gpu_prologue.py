@@ -12,7 +12,7 @@ import torch
 
 import oracle
 import test_sequence_layers_linear_amd as ttt
-from parity_util import CONFIGS, TOL, announce, default_seed, make_inputs, rel_l2, to_gpu
+from parity_util import WORKLOADS, TOL, announce, default_seed, make_inputs, rel_l2, to_gpu
 from test_sequence_layers_linear_amd.inputs import make_prologue
 
 pytestmark = pytest.mark.gpu
@@ -42,7 +42,7 @@ def _run(w, seed, parts, per_batch=False, eps=1e-5):
 @pytest.mark.parametrize("B,H,T,per_batch", [(1, 2, 16, False), (2, 3, 77, True), (1, 2, 300, False)])
 def test_prologue_small(dtype, part, B, H, T, per_batch, monkeypatch):
     monkeypatch.setenv("TTT_LINEAR_SEGMENTS", "1")
-    w = CONFIGS[3].with_(B=B, H=H, T=T, dtype=dtype)
+    w = WORKLOADS[3].with_(B=B, H=H, T=T, dtype=dtype)
     seed = 9000 + B * 100 + H * 10 + T
     announce("prologue", dtype, part, B, H, T, seed)
     ey, ew = _run(w, seed, PARTS[part], per_batch)
@@ -56,7 +56,7 @@ def test_prologue_f32_one_workgroup_kernel(part, T, S, monkeypatch):
     chains split W by columns unless TTT_LINEAR_F32_COLS=0)."""
     monkeypatch.setenv("TTT_LINEAR_F32_COLS", "0")
     monkeypatch.setenv("TTT_LINEAR_SEGMENTS", str(S))
-    w = CONFIGS[3].with_(B=2, H=3, T=T, dtype="fp32")
+    w = WORKLOADS[3].with_(B=2, H=3, T=T, dtype="fp32")
     seed = 9200 + T + S
     announce("prologue fp32 one workgroup per chain", part, T, S, seed)
     ey, ew = _run(w, seed, PARTS[part])
@@ -67,7 +67,7 @@ def test_prologue_f32_one_workgroup_kernel(part, T, S, monkeypatch):
 @pytest.mark.parametrize("T,S", [(100, 2), (333, 3), (480, 30)])
 def test_prologue_segmented(dtype, T, S, monkeypatch):
     monkeypatch.setenv("TTT_LINEAR_SEGMENTS", str(S))
-    w = CONFIGS[3].with_(B=1, H=3, T=T, dtype=dtype)
+    w = WORKLOADS[3].with_(B=1, H=3, T=T, dtype=dtype)
     seed = 9100 + T + S
     announce("prologue segmented", dtype, T, S, seed)
     ey, ew = _run(w, seed, PARTS["all"])
@@ -76,7 +76,7 @@ def test_prologue_segmented(dtype, T, S, monkeypatch):
 
 def test_prologue_eps_matters_for_flat_rows():
     """A constant key row normalises to beta alone; eps only scales the zero."""
-    w = CONFIGS[3].with_(B=1, H=2, T=40, dtype="fp32")
+    w = WORKLOADS[3].with_(B=1, H=2, T=40, dtype="fp32")
     announce("prologue flat rows")
     inp = make_inputs(w, 9200)
     inp["K"][0, 1, 5] = 0.25
@@ -92,7 +92,7 @@ def test_prologue_eps_matters_for_flat_rows():
 
 
 def test_prologue_off_is_plain_forward():
-    w = CONFIGS[3].with_(B=2, H=2, T=200)
+    w = WORKLOADS[3].with_(B=2, H=2, T=200)
     announce("prologue off")
     g = to_gpu(make_inputs(w, 9300))
     Y0, W0 = ttt.ttt_linear_forward(g["Q"], g["K"], g["V"], g["W0"], g["eta"], 16)
@@ -103,7 +103,7 @@ def test_prologue_off_is_plain_forward():
 
 @pytest.mark.parametrize("cfg", [2, 3])
 def test_prologue_config_full(cfg):
-    w = CONFIGS[cfg]
+    w = WORKLOADS[cfg]
     announce("prologue config", cfg, w.name)
     ey, ew = _run(w, default_seed(cfg) + 900, PARTS["all"])
     assert ey <= TOL[w.dtype] and ew <= TOL[w.dtype]
@@ -117,7 +117,7 @@ def test_chunk_start_read(dtype, T, S, parts, monkeypatch):
     if dtype == "fp32-one-workgroup":
         monkeypatch.setenv("TTT_LINEAR_F32_COLS", "0")
         dtype = "fp32"
-    w = CONFIGS[3].with_(B=2, H=3, T=T, dtype=dtype)
+    w = WORKLOADS[3].with_(B=2, H=3, T=T, dtype=dtype)
     seed = 9400 + T + S
     announce("chunk-start read", dtype, T, S, parts, seed)
     inp = make_inputs(w, seed)
@@ -142,7 +142,7 @@ def test_chunk_start_read(dtype, T, S, parts, monkeypatch):
 def test_decode_step_ex(dtype, d, parts, read_start):
     """Three prologue decode steps from a random state against the oracle's
     one-token forward (b = 1) with per-batch W0 = the state."""
-    w = CONFIGS[3].with_(B=2, H=3, T=3, d=d, dtype=dtype)
+    w = WORKLOADS[3].with_(B=2, H=3, T=3, d=d, dtype=dtype)
     seed = 9500 + d + len(parts) + int(read_start)
     announce("decode_ex", dtype, d, parts, read_start, seed)
     inp = make_inputs(w, seed, w0_per_batch=True)
