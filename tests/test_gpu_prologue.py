@@ -12,7 +12,8 @@ import torch
 
 import oracle
 import test_sequence_layers_linear_amd as ttt
-from parity_util import WORKLOADS, TOL, announce, default_seed, make_inputs, rel_l2, to_gpu
+from parity_util import (WORKLOADS, TOL, announce, default_seed, make_inputs, rel_l2,
+                         sample_chains, select_chains, to_gpu)
 from test_sequence_layers_linear_amd.inputs import make_prologue
 
 pytestmark = pytest.mark.gpu
@@ -107,6 +108,33 @@ def test_prologue_config_full(cfg):
     announce("prologue config", cfg, w.name)
     ey, ew = _run(w, default_seed(cfg) + 900, PARTS["all"])
     assert ey <= TOL[w.dtype] and ew <= TOL[w.dtype]
+
+
+def test_prologue_config4_sampled_chains_full_length():
+    """The 32768-token workload with the whole prologue, in the launch
+    configuration the benchmark times (planned segments: maps, combine and the
+    staging-wave scans), on three chains the oracle computes one by one."""
+    w = WORKLOADS[4]
+    announce("prologue config 4 sampled chains", w.name)
+    inp = make_inputs(w, default_seed(4) + 900)
+    pro = make_prologue(w, default_seed(4) + 903)
+    inp["eta"] = pro["eta"]
+    g = to_gpu(inp)
+    Y, W = ttt.ttt_linear_forward_ex(g["Q"], g["K"], g["V"], g["W0"], g["eta"], w.b,
+                                     **to_gpu({k: pro[k] for k in PARTS["all"]}))
+    torch.cuda.synchronize()
+    chains = sample_chains(w.B, w.H, 3, seed=45)
+    sub = select_chains(inp, chains)
+    heads = [h for _, h in chains]
+    sub_pro = {"ln_q": pro["ln_q"][heads], "ln_k": pro["ln_k"][heads],
+               "eta_tok": torch.stack([pro["eta_tok"][b, h] for b, h in chains])[None]}
+    Yr, Wr = oracle.linear_forward_ex(sub["Q"], sub["K"], sub["V"], sub["W0"], sub["eta"], w.b, **sub_pro)
+    Ys = torch.stack([Y[b, h] for b, h in chains])[None]
+    Ws = torch.stack([W[b, h] for b, h in chains])[None]
+    ey, ew = rel_l2(Ys, Yr), rel_l2(Ws, Wr)
+    print(f"  chains {chains} rel-L2 Y {ey:.3e}  W {ew:.3e}", flush=True)
+    assert ey <= TOL["bf16"] and ew <= TOL["bf16"]
+    assert torch.isfinite(Y.float()).all() and torch.isfinite(W).all()
 
 
 @pytest.mark.parametrize("dtype", ["fp32", "bf16", "fp32-one-workgroup"])
