@@ -176,6 +176,9 @@ struct StageRegs {
 //   LDS, where it scales its row of the residual: E'[t] = -eta_t R[t] (the
 //   head's eta when no per-token step sizes are given); with read_start every
 //   token reads out with the chunk-start W (the tril term is dropped).
+// kMaps = true with kPro: 12 waves, waves 0-7 the two halves as above and
+//   waves 8-11 staging K, V and the step sizes (K LayerNorm'd), as the K
+//   group of the scan below.
 // kMaps = false with kPro: 12 waves in two roles.  Waves 0-3 compute (as in
 //   the plain scan); waves 4-11 only stage, one stage ahead of the compute
 //   waves: waves 4-7 load K, V and the step sizes and LayerNorm K, waves
@@ -184,7 +187,7 @@ struct StageRegs {
 //   (one wave of each kind per SIMD) instead of inside it.  The roles run
 //   loops of their own with one barrier per stage each.
 template <bool kMaps, bool kPro>
-__global__ void __launch_bounds__(kMaps ? 2 * kThreads : (kPro ? 3 * kThreads : kThreads), 1)
+__global__ void __launch_bounds__(kPro ? 3 * kThreads : (kMaps ? 2 * kThreads : kThreads), 1)
 linear_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                    const uint16_t* __restrict__ V, const float* W0, int w0_per_batch,
                    const float* __restrict__ eta, int H, int T, int64_t units, int seg_len,
@@ -197,10 +200,11 @@ linear_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     const int w = (threadIdx.x >> 6) & (kWaves - 1);
     // wave-uniform role flags, made scalar so that the compiler branches on
     // them instead of masking lanes
-    constexpr bool kSplit = kPro && !kMaps;
+    constexpr bool kSplit = kPro;
+    // (half is 2 on the staging waves 8-11 of a maps block with the prologue)
     const int half = kMaps ? __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 8)) : 0;
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
-    const bool stager = kSplit ? wave >= kWaves : (!kMaps || wave < kWaves);
+    const bool stager = kSplit ? wave >= (kMaps ? 2 : 1) * kWaves : (!kMaps || wave < kWaves);
     const int c = lane & 15;
     const int g = lane >> 4;
     const int col = 16 * w + c;          // this lane's column of W
@@ -428,7 +432,7 @@ linear_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
             // waves 4-7 (kgrp) and 8-11 run the same instruction stream on
             // different buffers: x is K or Q, y is V or nothing, e the step
             // sizes or nothing (a zero-sized resource reads as zero)
-            const bool kgrp = wave < 2 * kWaves;
+            const bool kgrp = kMaps || wave < 2 * kWaves;
             const __amdgpu_buffer_rsrc_t rx = chain_rsrc((kgrp ? K : Q) + base, seg_bytes);
             const __amdgpu_buffer_rsrc_t ry = chain_rsrc(V + base, kgrp ? seg_bytes : 0);
             const __amdgpu_buffer_rsrc_t re =
@@ -467,23 +471,24 @@ linear_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
                 }
             };
             // stage s + 1 goes to LDS before barrier s; loads run 6 to 12
-            // stages ahead in two register sets, as in the plain scan
-            Rows setA[kSet], setB[kSet];
+            // stages ahead in two register sets, as in the plain scan (3 to
+            // 6 in a maps block, whose 12 waves have fewer registers each)
+            Rows setA[kSetK], setB[kSetK];
             {
                 Rows first;
                 load(first, 0);
                 put(first, 0, 0);
             }
 #pragma unroll
-            for (int p = 0; p < kSet; ++p)
+            for (int p = 0; p < kSetK; ++p)
                 load(setA[p], 1 + p);
-            for (int s0 = 0; s0 < nstages; s0 += 2 * kSet) {
+            for (int s0 = 0; s0 < nstages; s0 += 2 * kSetK) {
 #pragma unroll
-                for (int p = 0; p < kSet; ++p)
-                    load(setB[p], s0 + kSet + 1 + p);
+                for (int p = 0; p < kSetK; ++p)
+                    load(setB[p], s0 + kSetK + 1 + p);
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int p = 0; p < kSet; ++p) {
+                for (int p = 0; p < kSetK; ++p) {
                     if (s0 + p >= nstages)       // uniform: the scan is done
                         goto done;
                     put(setA[p], s0 + p + 1, (p + 1) % kSlots);
@@ -491,14 +496,14 @@ linear_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
                 }
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int p = 0; p < kSet; ++p)
-                    load(setA[p], s0 + 2 * kSet + 1 + p);
+                for (int p = 0; p < kSetK; ++p)
+                    load(setA[p], s0 + 2 * kSetK + 1 + p);
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int p = 0; p < kSet; ++p) {
-                    if (s0 + kSet + p >= nstages)
+                for (int p = 0; p < kSetK; ++p) {
+                    if (s0 + kSetK + p >= nstages)
                         goto done;
-                    put(setB[p], s0 + kSet + p + 1, (kSet + p + 1) % kSlots);
+                    put(setB[p], s0 + kSetK + p + 1, (kSetK + p + 1) % kSlots);
                     __syncthreads();
                 }
                 __builtin_amdgcn_sched_barrier(0);
@@ -607,7 +612,8 @@ hipError_t launch_bf16(const LinearArgs& a, const SegmentPlan& p)
     const int lds = kSlots * (kPro ? kSlotBytes + kStageTokens * 4 : kSlotBytes);
     if (p.nseg > 1) {
         const dim3 grid(static_cast<unsigned>(placed_grid(units, p.nseg - 1)));
-        hipLaunchKernelGGL((linear_mfma_kernel<true, kPro>), grid, dim3(2 * kThreads), lds, a.stream, q,
+        hipLaunchKernelGGL((linear_mfma_kernel<true, kPro>), grid, dim3(kPro ? 3 * kThreads : 2 * kThreads), lds,
+                           a.stream, q,
                            k, v, a.W0, a.w0_per_batch, a.eta, H, T, units, seg_len, p.nseg, p.maps,
                            p.wstart, y, a.W_out, a.pro);
         hipError_t e = hipGetLastError();
