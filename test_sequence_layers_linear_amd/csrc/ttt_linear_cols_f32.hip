@@ -102,9 +102,13 @@ struct StageRegs {
 // written to LDS: its K and Q rows LayerNorm'd over the head dim (16 lanes
 // per row, DPP sums) and its step sizes beside the tiles, which scale the
 // residual rows, E'[t] = -eta_t E[t]; with read_start the tril term is
-// dropped (every token reads the chunk-start W).
+// dropped (every token reads the chunk-start W).  The scan with the prologue
+// runs 8 waves: waves 0-3 compute as above, waves 4-7 only stage (load,
+// LayerNorm and write each chunk to LDS two chunks ahead, one barrier per
+// chunk like the compute waves), so the normalisation's VALU work runs beside
+// the chunk chain on the same SIMDs instead of inside it.
 template <bool kMaps, bool kPro>
-__global__ void __launch_bounds__(kThreads, 1)
+__global__ void __launch_bounds__(kPro && !kMaps ? 2 * kThreads : kThreads, 1)
 linear_cols_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                        const float* __restrict__ V, const float* W0, int w0_per_batch,
                        const float* __restrict__ eta, int H, int T, int64_t units, int seg_len,
@@ -120,6 +124,9 @@ linear_cols_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const int c = lane & 15;
     const int g = lane >> 4;
+    constexpr bool kSplit = kPro && !kMaps;
+    const bool stager = kSplit && w >= kWaves;   // waves 4-7 of the split scan
+    const int sid = tid & (kThreads - 1);        // staging thread index
 
     // chain u, segment s (and map half), column slice J
     int64_t u;
@@ -142,7 +149,7 @@ linear_cols_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
 #pragma unroll
         for (int r = 0; r < 4; ++r)
             Wr[r] = (half == 0 && 16 * w + 4 * g + r == 16 * J + c) ? 1.f : 0.f;
-    } else {
+    } else if (!stager) {
         const float* w0 = nseg > 1 ? wstart + (u * nseg + (compose ? 0 : s)) * kD * kD
                                    : W0 + (w0_per_batch ? u : h) * kD * kD;
 #pragma unroll
@@ -159,7 +166,10 @@ linear_cols_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
             dst[i * kD + 16 * J + (tid & 15)] = w0[i * kD + 16 * J + (tid & 15)];
         }
     }
-    if (!kMaps && compose && s > 0) {
+    if (!kMaps && compose && s > 0 && stager) {
+        for (int j = 0; j <= s; ++j)     // the composition's s barriers and the one after it
+            __syncthreads();
+    } else if (!kMaps && compose && s > 0) {
         // W_s from W_0 through the maps of segments 0 .. s - 1; wave w's A
         // operand of k-step ks is M_j[16w + c][16g + ks] (a 64-byte run per
         // lane), its B operand W_j[16g + ks][c] from the transposed slice
@@ -223,10 +233,10 @@ linear_cols_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
     // 4 (tid % 16) ..), and lane l of every wave loads 16 bytes of the V slice
     // (row l / 4, columns 16J + 4 (l % 4) ..), which wave 0 writes to LDS;
     // out-of-range reads give zeros
-    const int st_row = tid >> 4;
-    const int st_col = 4 * (tid & 15);
-    const int sv_row = (tid & 63) >> 2;
-    const int sv_col = 4 * (tid & 3);
+    const int st_row = sid >> 4;
+    const int st_col = 4 * (sid & 15);
+    const int sv_row = (sid & 63) >> 2;
+    const int sv_col = 4 * (sid & 3);
     // prologue: gamma, beta of this thread's 4 columns
     const bool use_tok = kPro && pro.eta_tok != nullptr;
     const bool ln_k = kPro && pro.ln_k != nullptr;
@@ -274,13 +284,13 @@ linear_cols_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                 kx = norm(kx, gk, bk, valid);
             if (ln_q)
                 qx = norm(qx, gq, bq, valid);
-            if ((tid & 15) == 0)
-                sl[L::kOffEta + st_row] = use_tok ? __uint_as_float(o.eta) : et;
+            // (the 16 lanes of a row store the same value: no lane branch)
+            sl[L::kOffEta + st_row] = use_tok ? __uint_as_float(o.eta) : et;
         }
         *reinterpret_cast<u32x4*>(sl + kOffK + st_row * kP + st_col) = kx;
         if (!kMaps)
             *reinterpret_cast<u32x4*>(sl + kOffQ + st_row * kP + st_col) = qx;
-        if (w == 0)
+        if ((sid >> 6) == 0)
             *reinterpret_cast<u32x4*>(sl + kOffV + sv_row * kVP + sv_col) = o.v;
     };
     // partial tile `kind` (0 P, 1 R, 2 S^T) of wave wv, chunk parity par
@@ -359,7 +369,44 @@ linear_cols_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
         }
     };
 
-    if (nchunks > 0) {
+    if (kSplit && nchunks > 0) {
+        if (stager) {
+            StageRegs ring[kRing];
+#pragma unroll
+            for (int q = 0; q < kRing; ++q)
+                load_stage(ring[q], q);
+            write_stage(ring[0], 0);
+            write_stage(ring[1], 1);
+            load_stage(ring[0], kRing);
+            load_stage(ring[1], kRing + 1);
+            __syncthreads();
+            // barrier ch (the compute waves' barrier of chunk ch), then chunk
+            // ch + 2 into its slot (last read by chunk ch - 1) and its register
+            // set reloaded with chunk ch + 2 + kRing
+            auto advance = [&](int ch, StageRegs& set) {
+                __syncthreads();
+                write_stage(set, ch + 2);
+                load_stage(set, ch + 2 + kRing);
+            };
+            int c0 = 0;
+            for (; c0 + kRing <= nchunks; c0 += kRing) {
+#pragma unroll
+                for (int p = 0; p < kRing; ++p)
+                    advance(c0 + p, ring[(p + 2) % kRing]);
+            }
+#pragma unroll
+            for (int p = 0; p < kRing; ++p) {
+                if (c0 + p >= nchunks)   // uniform: the scan is done
+                    break;
+                advance(c0 + p, ring[(p + 2) % kRing]);
+            }
+            return;
+        }
+        __syncthreads();                 // chunks 0 and 1 are in LDS
+        asm volatile("" : "+v"(Wr));     // the start state is in registers before the loop
+        for (int ch = 0; ch < nchunks; ++ch)
+            chunk_step(ch);
+    } else if (nchunks > 0) {
         StageRegs ring[kRing];
 #pragma unroll
         for (int q = 0; q < kRing; ++q)
@@ -436,7 +483,8 @@ hipError_t launch_cols(const LinearArgs& a, const SegmentPlan& p)
     }
     // segments compose their start states from the maps and the copy of W0
     const dim3 grid(static_cast<unsigned>(placed_grid(units, kSlices * p.nseg)));
-    hipLaunchKernelGGL((linear_cols_f32_kernel<false, kPro>), grid, dim3(kThreads), 0, a.stream, q, k,
+    hipLaunchKernelGGL((linear_cols_f32_kernel<false, kPro>), grid, dim3(kPro ? 2 * kThreads : kThreads), 0,
+                       a.stream, q, k,
                        v, a.W0, a.w0_per_batch, a.eta, H, T, units, seg_len, p.nseg, p.maps,
                        p.wstart, y, a.W_out, 1, a.pro);
     return hipGetLastError();
