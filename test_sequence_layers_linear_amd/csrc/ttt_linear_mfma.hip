@@ -165,9 +165,11 @@ struct StageRegs {
 //   last segment also writes W_out), started from W0 (one segment) or from
 //   the segment's start state in wstart.
 // kMaps = true: the affine map W_end = M W_start + N of segment s < nseg - 1,
-//   8 waves: waves 0-3 (half 0) run the scan from W = I with V = 0 (giving
+//   12 waves: waves 0-3 (half 0) run the scan from W = I with V = 0 (giving
 //   M), waves 4-7 (half 1) from W = 0 with the segment's V (giving N); both
-//   halves share the staged K.  No Q, no Y.
+//   halves share the staged K, which waves 8-11 load and write to LDS (as
+//   the K group of the prologue scan below; with the prologue they also
+//   LayerNorm it and stage the step sizes).  No Q, no Y.
 // With nseg > 1 the blocks of chain u all run on XCD u % 8 (see xcd_block),
 // so the maps, start states and scans of a chain meet in one L2.
 // kPro: the input prologue (Prologue in ttt_internal.h) is applied while the
@@ -176,9 +178,6 @@ struct StageRegs {
 //   LDS, where it scales its row of the residual: E'[t] = -eta_t R[t] (the
 //   head's eta when no per-token step sizes are given); with read_start every
 //   token reads out with the chunk-start W (the tril term is dropped).
-// kMaps = true with kPro: 12 waves, waves 0-7 the two halves as above and
-//   waves 8-11 staging K, V and the step sizes (K LayerNorm'd), as the K
-//   group of the scan below.
 // kMaps = false with kPro: 12 waves in two roles.  Waves 0-3 compute (as in
 //   the plain scan); waves 4-11 only stage, one stage ahead of the compute
 //   waves: waves 4-7 load K, V and the step sizes and LayerNorm K, waves
@@ -187,7 +186,7 @@ struct StageRegs {
 //   (one wave of each kind per SIMD) instead of inside it.  The roles run
 //   loops of their own with one barrier per stage each.
 template <bool kMaps, bool kPro>
-__global__ void __launch_bounds__(kPro ? 3 * kThreads : (kMaps ? 2 * kThreads : kThreads), 1)
+__global__ void __launch_bounds__(kPro || kMaps ? 3 * kThreads : kThreads, 1)
 linear_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                    const uint16_t* __restrict__ V, const float* W0, int w0_per_batch,
                    const float* __restrict__ eta, int H, int T, int64_t units, int seg_len,
@@ -200,8 +199,8 @@ linear_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     const int w = (threadIdx.x >> 6) & (kWaves - 1);
     // wave-uniform role flags, made scalar so that the compiler branches on
     // them instead of masking lanes
-    constexpr bool kSplit = kPro;
-    // (half is 2 on the staging waves 8-11 of a maps block with the prologue)
+    constexpr bool kSplit = kPro || kMaps;
+    // (half is 2 on the staging waves 8-11 of a maps block)
     const int half = kMaps ? __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 8)) : 0;
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
     const bool stager = kSplit ? wave >= (kMaps ? 2 : 1) * kWaves : (!kMaps || wave < kWaves);
@@ -454,7 +453,8 @@ linear_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
                 const int off = (stage * kStageTokens + st_row) * kRowBytes + st_seg * 16;
                 o.x = __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0);
                 o.y = __builtin_amdgcn_raw_buffer_load_b128(ry, off, 0, 0);
-                o.e = __builtin_amdgcn_raw_buffer_load_b32(re, (stage * kStageTokens + st_row) * 4, 0, 0);
+                if constexpr (kPro)
+                    o.e = __builtin_amdgcn_raw_buffer_load_b32(re, (stage * kStageTokens + st_row) * 4, 0, 0);
             };
             // LayerNorm'd rows of stage `stage` into LDS slot `slot`
             auto put = [&](Rows& o, int stage, int slot) {
@@ -466,8 +466,9 @@ linear_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
                 if (kgrp) {
                     *reinterpret_cast<u32x4*>(chunk + kOffV + swz(r, st_seg)) = o.y;
                     // (the 8 lanes of a row store the same value)
-                    *reinterpret_cast<float*>(lds + slot * kSlotB + kSlotBytes + 4 * st_row) =
-                        use_tok ? __uint_as_float(o.e) : et;
+                    if constexpr (kPro)
+                        *reinterpret_cast<float*>(lds + slot * kSlotB + kSlotBytes + 4 * st_row) =
+                            use_tok ? __uint_as_float(o.e) : et;
                 }
             };
             // stage s + 1 goes to LDS before barrier s; loads run 6 to 12
@@ -524,8 +525,10 @@ linear_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
                     ChunkOps o0, o1;
                     read_ops(o0, sl);
                     read_ops(o1, sl + kChunkBytes);
-                    o0.eta4 = *reinterpret_cast<const f32x4*>(sl + kSlotBytes + 16 * g);
-                    o1.eta4 = *reinterpret_cast<const f32x4*>(sl + kSlotBytes + 64 + 16 * g);
+                    if constexpr (kPro) {
+                        o0.eta4 = *reinterpret_cast<const f32x4*>(sl + kSlotBytes + 16 * g);
+                        o1.eta4 = *reinterpret_cast<const f32x4*>(sl + kSlotBytes + 64 + 16 * g);
+                    }
                     step(o0, (s0 + p) * kStageTokens);
                     step(o1, (s0 + p) * kStageTokens + kB);
                 }
@@ -612,7 +615,7 @@ hipError_t launch_bf16(const LinearArgs& a, const SegmentPlan& p)
     const int lds = kSlots * (kPro ? kSlotBytes + kStageTokens * 4 : kSlotBytes);
     if (p.nseg > 1) {
         const dim3 grid(static_cast<unsigned>(placed_grid(units, p.nseg - 1)));
-        hipLaunchKernelGGL((linear_mfma_kernel<true, kPro>), grid, dim3(kPro ? 3 * kThreads : 2 * kThreads), lds,
+        hipLaunchKernelGGL((linear_mfma_kernel<true, kPro>), grid, dim3(3 * kThreads), lds,
                            a.stream, q,
                            k, v, a.W0, a.w0_per_batch, a.eta, H, T, units, seg_len, p.nseg, p.maps,
                            p.wstart, y, a.W_out, a.pro);
