@@ -225,7 +225,7 @@ bool linear_mfma_supports(const LinearArgs& a);
 hipError_t launch_linear_mfma(const LinearArgs& a, const SegmentPlan& p);
 bool linear_mfma_f32_supports(const LinearArgs& a);
 hipError_t launch_linear_mfma_f32(const LinearArgs& a, const SegmentPlan& p);
-constexpr SegmentCosts kLinearBf16Costs{0.35, 0.43, 0.60, 8.5, 1};
+constexpr SegmentCosts kLinearBf16Costs{0.35, 0.25, 0.60, 8.5, 1};
 constexpr SegmentCosts kLinearF32Costs{1.38, 0.90, 0.60, 8.5, 2};
 // fp32 Q/K/V with each chain's W split by columns over 4 workgroups
 // (ttt_linear_cols_f32.hip, with or without the prologue): used while the chains'
