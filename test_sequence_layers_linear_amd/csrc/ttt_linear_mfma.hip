@@ -13,7 +13,9 @@
 // Work split.  One workgroup (4 waves) per (batch, head) chain.  The loss
 // 1/2 sum_j (k . W[:, j] - v_j)^2 separates over output columns j, so wave w
 // owns the 16 columns [16w, 16w + 16) of W outright and no partial result
-// ever moves between waves; the waves share only the staged inputs.
+// ever moves between waves; the waves share only the staged inputs.  (The
+// segment maps and the scan with the input prologue add waves that only
+// stage: see the kernel's comment.)
 //
 // Register dataflow (16x16 MFMA layouts; lane l, c = l % 16, g = l / 16):
 //   C/D tile    : lane holds rows 4g..4g+3 of column c.
