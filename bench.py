@@ -9,19 +9,27 @@ are already resident in HBM:
   - TTT-Linear workloads: ttt_linear_forward, then the workload's single-token
     decode steps (ttt_linear_decode_step) from the final state, if any;
   - TTT-MLP workloads: ttt_mlp_forward.
---config picks the workload (1..5, default 2: B1 H4 d64 T2048 b16 fp32).
-Unless --quick is given, the other d = 64 workloads are measured too and
-reported under "workloads" in the same line.
+--config picks the workload (1..5, default 4: TTT-Linear B2 H24 d64 T32768
+b16 bf16 plus 256 decode steps, the largest d = 64, b = 16 TTT-Linear
+workload on one GPU).  value = B*T / seconds per step (the decode steps'
+time included).  Unless --quick is given, the other d = 64 workloads are
+measured too and reported under "workloads" in the same line.
 
 roofline.achieved = algorithmic bytes (HBM bound) or flops (MFMA bound) of
 one forward call / its mean duration from HIP events recorded on the launch
-stream around every call in the timed region.  A call is one kernel launch,
-except a segmented TTT-Linear scan: maps, start-state composition and
-segment scans, three launches back to back on the stream, or two for the
-fp32 column-split scan, whose segments compose their own start states
-(roofline.kernel names them).  The decode steps of a workload run as one captured HIP graph.
+stream around the call, with the 256 MB last-level cache flushed (a 512 MB
+buffer written) before every call; the same figure for back-to-back calls in
+the timed region is roofline.warm.  A call is one kernel launch, except a
+segmented TTT-Linear scan: maps, start-state composition and segment scans,
+three launches back to back on the stream, or two for the fp32 column-split
+scan, whose segments compose their own start states (roofline.kernel names
+them).  roofline.peak is the datasheet figure; roofline.peak_measured is what
+a plain streaming copy or a dense MFMA loop (include/ttt_roofs.h) reaches on
+this GPU, and frac_of_measured the fraction of that.  The decode steps of a
+workload run as one captured HIP graph.
 cpu_baseline = the fp64 oracle (plain loops, OpenMP over chains) timed on
-this host's cores on a bounded sample of the same workload.
+this host's cores on a bounded sample of the same workload: with all host
+threads (one chain each), and with one thread (single_thread).
 
 Each TTT-Linear workload also reports "backward": ttt_linear_backward (the
 gradients of Q, K, V, W0 and eta for seeded cotangents dY, dW_out) timed the
@@ -191,18 +199,79 @@ def stored_traffic(kernels, workload):
     return total
 
 
-def roofline(w, flops, nbytes, seconds, kernels):
+def roofline(w, flops, nbytes, seconds, kernels, roofs=None, warm_seconds=None):
+    """Roofline object of one forward call: `seconds` is its flushed-cache
+    mean duration, `warm_seconds` (optional) the back-to-back one; `roofs`
+    the measured copy bandwidth and MFMA throughputs."""
     dt = "bf16" if w.dtype == "bf16" else "fp32"
     ridge = PEAK_FLOPS[dt] / PEAK_HBM
+    roofs = roofs or {}
     if flops / nbytes > ridge:
         ach, peak, unit, bound = flops / seconds / 1e12, PEAK_FLOPS[dt] / 1e12, "TFLOP/s", "mfma"
+        meas = roofs.get("mfma_" + dt + "_tflops")
+        warm = flops / warm_seconds / 1e12 if warm_seconds else None
     else:
         ach, peak, unit, bound = nbytes / seconds / 1e9, PEAK_HBM / 1e9, "GB/s", "hbm"
-    return {"bound": bound, "achieved": round(ach, 3), "peak": peak, "unit": unit,
-            "frac": round(ach / peak, 5), "traffic": stored_traffic(kernels, w.name),
-            "kernel": " + ".join(kernels), "mean_launch_us": round(seconds * 1e6, 3),
-            "algorithmic_flops": flops, "algorithmic_bytes": nbytes,
-            "active_cu_ceiling": round(min(1.0, w.B * w.H / 256), 4)}
+        meas = roofs.get("copy_GBps")
+        warm = nbytes / warm_seconds / 1e9 if warm_seconds else None
+    out = {"bound": bound, "achieved": round(ach, 3), "peak": peak, "unit": unit,
+           "frac": round(ach / peak, 5), "traffic": stored_traffic(kernels, w.name),
+           "kernel": " + ".join(kernels), "mean_launch_us": round(seconds * 1e6, 3),
+           "timing": "HIP events around each call, last-level cache flushed before it",
+           "peak_measured": round(meas, 3) if meas else None,
+           "frac_of_measured": round(ach / meas, 5) if meas else None,
+           "algorithmic_flops": flops, "algorithmic_bytes": nbytes,
+           "active_cu_ceiling": round(min(1.0, w.B * w.H / 256), 4)}
+    if warm_seconds:
+        out["warm"] = {"achieved": round(warm, 3), "frac": round(warm / peak, 5),
+                       "mean_launch_us": round(warm_seconds * 1e6, 3),
+                       "timing": "mean over the back-to-back calls of the timed region"}
+    return out
+
+
+def measure_roofs():
+    """Achievable HBM bandwidth (a 1 GiB streaming copy) and dense MFMA
+    throughput (bf16 16x16x32 and fp32 16x16x4 loops on 8 waves per CU) on
+    this GPU, from the plain kernels of include/ttt_roofs.h; median of 5."""
+    import ctypes
+    import torch
+    import test_sequence_layers_linear_amd as ttt
+    lib = ttt.load_library()
+    lib.ttt_roof_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    lib.ttt_roof_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
+                                  ctypes.POINTER(ctypes.c_double), ctypes.c_void_p]
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def timed(fn, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b) / 1e3)
+        ts.sort()
+        return ts[len(ts) // 2]
+
+    nbytes = 1 << 30
+    src = torch.ones(nbytes // 4, device="cuda")
+    dst = torch.empty_like(src)
+    t = timed(lambda: ttt._check(lib.ttt_roof_copy(src.data_ptr(), dst.data_ptr(), nbytes, stream)))
+    out = {"copy_GBps": 2 * nbytes / t / 1e9, "copy_bytes": nbytes}
+    del src, dst
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    waves = cus * 8
+    sink = torch.empty(waves * 64, device="cuda")
+    for dt, name, iters in ((1, "bf16", 20000), (0, "fp32", 10000)):
+        fl = ctypes.c_double(0.0)
+        t = timed(lambda: ttt._check(lib.ttt_roof_mfma(sink.data_ptr(), dt, waves, iters,
+                                                       ctypes.byref(fl), stream)), reps=3)
+        out[f"mfma_{name}_tflops"] = fl.value / t / 1e12
+    torch.cuda.empty_cache()
+    return out
 
 
 # ---------------------------------------------------------------------------
@@ -226,13 +295,17 @@ class Runner:
             self.W2 = torch.empty((w.B, w.H, w.m, w.d), device="cuda")
         if w.decode_steps:
             self.y = torch.empty_like(g["dq"][0])
+        if w.kind == "linear":
+            self.ws = torch.empty(ttt.ttt_linear_workspace_bytes(w.B, w.H, w.T, w.d, w.b,
+                                                                 w.torch_dtype),
+                                  dtype=torch.uint8, device="cuda")
         torch.cuda.synchronize()
 
     def forward(self):
         g, ttt = self.g, self.ttt
         if self.w.kind == "linear":
             ttt.ttt_linear_forward(g["Q"], g["K"], g["V"], g["W0"], g["eta"], self.w.b,
-                                   Y=self.Y, W_out=self.W)
+                                   Y=self.Y, W_out=self.W, workspace=self.ws)
         else:
             ttt.ttt_mlp_forward(g["Q"], g["K"], g["V"], g["W1"], g["W2"], g["eta"], self.w.b,
                                 Y=self.Y, W1_out=self.W1, W2_out=self.W2)
@@ -312,15 +385,18 @@ class Runner:
                     dV=torch.empty_like(g["Q"]), dW0=torch.empty_like(g["W0"]),
                     deta=torch.empty_like(g["eta"]))
         pro = {k: v.cuda() for k, v in make_prologue(w, 11).items()}
+        ws = torch.empty(self.ttt.ttt_linear_backward_workspace_bytes(w.B, w.H, w.T, w.d, w.b,
+                                                                      w.torch_dtype),
+                         dtype=torch.uint8, device="cuda")
 
         def call():
             if prologue:
                 self.ttt.ttt_linear_backward_ex(g["Q"], g["K"], g["V"], g["W0"], pro["eta"], w.b,
                                                 cot["dY"], cot["dW_out"], eta_tok=pro["eta_tok"],
-                                                ln_q=pro["ln_q"], ln_k=pro["ln_k"])
+                                                ln_q=pro["ln_q"], ln_k=pro["ln_k"], workspace=ws)
             else:
                 self.ttt.ttt_linear_backward(g["Q"], g["K"], g["V"], g["W0"], g["eta"], w.b,
-                                             cot["dY"], cot["dW_out"], **outs)
+                                             cot["dY"], cot["dW_out"], workspace=ws, **outs)
         for _ in range(warmup):
             call()
         torch.cuda.synchronize()
@@ -343,7 +419,8 @@ class Runner:
         def call():
             self.ttt.ttt_linear_forward_ex(g["Q"], g["K"], g["V"], g["W0"], pro["eta"], w.b,
                                            eta_tok=pro["eta_tok"], ln_q=pro["ln_q"],
-                                           ln_k=pro["ln_k"], Y=self.Y, W_out=self.W)
+                                           ln_k=pro["ln_k"], Y=self.Y, W_out=self.W,
+                                           workspace=self.ws)
         for _ in range(warmup):
             call()
         torch.cuda.synchronize()
@@ -357,7 +434,8 @@ class Runner:
         return start.elapsed_time(end) / 1e3 / steps
 
     def measure_cold(self, reps):
-        """Forward duration with the 256 MB last-level cache flushed before each launch."""
+        """Forward duration with the 256 MB last-level cache flushed (a 512 MB
+        buffer written) before each call: (mean, median) over `reps` calls."""
         torch = self.torch
         junk = torch.empty(512 * 1024 * 1024 // 4, device="cuda")
         times = []
@@ -370,8 +448,9 @@ class Runner:
             torch.cuda.synchronize()
             times.append(a.elapsed_time(b) / 1e3)
         del junk
+        mean = sum(times) / len(times)
         times.sort()
-        return times[len(times) // 2]
+        return mean, times[len(times) // 2]
 
 
 # ---------------------------------------------------------------------------
@@ -388,39 +467,58 @@ def _select(host, chains, T):
 
 
 def run_cpu_baseline(w, host, target_s):
+    """The oracle on a bounded sample of the workload: k = min(chains, host
+    threads) (batch, head) chains at full length, one OpenMP thread each,
+    repeated to about target_s seconds; then one chain on one thread."""
     import oracle
     threads = max(1, oracle.max_threads())
     units = [(b, h) for b in range(w.B) for h in range(w.H)]
-    k = min(len(units), threads)
-    chains = units[:k]
-    sub = _select(host, chains, w.T)
 
-    def once():
-        if w.kind == "linear":
-            oracle.linear_forward(sub["Q"], sub["K"], sub["V"], sub["W0"], sub["eta"], w.b,
-                                  nthreads=k)
-        else:
-            oracle.mlp_forward(sub["Q"], sub["K"], sub["V"], sub["W1"], sub["W2"], sub["eta"],
-                               w.b, nthreads=k)
+    def timed(chains, nthreads, budget):
+        sub = _select(host, chains, w.T)
 
-    t0 = time.perf_counter()
-    once()
-    first = time.perf_counter() - t0
-    reps = max(1, int(math.ceil((target_s - first) / max(first, 1e-6))))
-    reps = min(reps, 1000)
-    t0 = time.perf_counter()
-    for _ in range(reps):
+        def once():
+            if w.kind == "linear":
+                oracle.linear_forward(sub["Q"], sub["K"], sub["V"], sub["W0"], sub["eta"], w.b,
+                                      nthreads=nthreads)
+            else:
+                oracle.mlp_forward(sub["Q"], sub["K"], sub["V"], sub["W1"], sub["W2"], sub["eta"],
+                                   w.b, nthreads=nthreads)
+        t0 = time.perf_counter()
         once()
-    el = time.perf_counter() - t0
-    tokens = k * w.T * reps / w.H      # B*T-equivalent tokens (all heads of a token)
-    return {"value": round(tokens / el, 3), "unit": "tokens/s", "cores": k, "kind": "oracle",
-            "sample": f"{k} of {len(units)} (batch, head) chains at full T={w.T}, "
+        first = time.perf_counter() - t0
+        reps = max(1, min(1000, int(math.ceil((budget - first) / max(first, 1e-6)))))
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            once()
+        el = time.perf_counter() - t0
+        # B*T-equivalent tokens: a token of the workload covers all H heads
+        return len(chains) * w.T * reps / w.H / el, reps, el
+
+    k = min(len(units), threads)
+    v_all, reps, el = timed(units[:k], k, target_s)
+    v_one, reps1, el1 = timed(units[:1], 1, target_s / 2)
+    return {"value": round(v_all, 3), "unit": "tokens/s", "cores": k, "kind": "oracle",
+            "sample": f"{k} of {len(units)} (batch, head) chains at full T={w.T} on {k} threads, "
                       f"{reps} repetitions, {el:.1f} s; tokens counted as chains*T/H",
-            "host_threads_available": threads}
+            "single_thread": {"value": round(v_one, 3), "cores": 1,
+                              "sample": f"chain (0, 0) at full T={w.T}, {reps1} repetitions, "
+                                        f"{el1:.1f} s"},
+            "host_threads_available": threads, "host_cpu": _cpu_model()}
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 # ---------------------------------------------------------------------------
-def measure_workload(cfg, steps, warmup, cold_reps):
+def measure_workload(cfg, steps, warmup, cold_reps, roofs=None):
     from test_sequence_layers_linear_amd.inputs import WORKLOADS, default_seed
     w = WORKLOADS[cfg]
     r = Runner(w, default_seed(cfg))
@@ -428,15 +526,13 @@ def measure_workload(cfg, steps, warmup, cold_reps):
     flops, nbytes = (linear_work if w.kind == "linear" else mlp_work)(w)
     nseg = segments(w)
     kern = kernel_names(w, nseg)
+    cold_mean, cold_median = r.measure_cold(cold_reps)
     out = {"workload": w.name, "config": cfg, "tokens_per_s": w.B * w.T / per_step,
            "segments_per_chain": nseg,
            "ms_per_step": per_step * 1e3, "forward_us": fwd * 1e6,
+           "forward_us_cold_llc": cold_mean * 1e6, "forward_us_cold_llc_median": cold_median * 1e6,
            "forward_tokens_per_s": w.B * w.T / fwd,
-           "roofline": roofline(w, flops, nbytes, fwd, kern)}
-    if cold_reps:
-        cold = r.measure_cold(cold_reps)
-        out["forward_us_cold_llc"] = cold * 1e6
-        out["roofline_cold_llc_frac"] = roofline(w, flops, nbytes, cold, kern)["frac"]
+           "roofline": roofline(w, flops, nbytes, cold_mean, kern, roofs, warm_seconds=fwd)}
     if w.kind == "linear" and w.d == 64 and w.b == 16:
         bt = r.measure_backward(max(3, steps // 2), 2)
         bf, bb = linear_backward_work(w)
@@ -465,7 +561,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--config", type=int, default=4, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--quick", action="store_true", help="only the selected workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -480,17 +576,22 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     print(f"[bench] workload config {args.config}: steps {args.steps} warmup {args.warmup}",
           file=sys.stderr, flush=True)
-    w, runner, main_res = measure_workload(args.config, args.steps, args.warmup, cold_reps=5)
+    print("[bench] measured roofs (stream copy, MFMA loops)", file=sys.stderr, flush=True)
+    roofs = measure_roofs()
+    print(f"[bench]   copy {roofs['copy_GBps']:.0f} GB/s, bf16 MFMA {roofs['mfma_bf16_tflops']:.0f} "
+          f"TFLOP/s, fp32 MFMA {roofs['mfma_fp32_tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)
+    w, runner, main_res = measure_workload(args.config, args.steps, args.warmup, cold_reps=30,
+                                           roofs=roofs)
     print(f"[bench] {w.name}: {main_res['tokens_per_s']:.4g} tokens/s", file=sys.stderr, flush=True)
 
     extras = {}
     if not args.quick:
-        for cfg in (3, 4, 5):
+        for cfg in (2, 3, 4, 5):
             if cfg == args.config:
                 continue
             st = 10 if cfg != 5 else 3
             print(f"[bench] extra workload config {cfg}", file=sys.stderr, flush=True)
-            _, rr, res = measure_workload(cfg, st, 2, cold_reps=3)
+            _, rr, res = measure_workload(cfg, st, 2, cold_reps=10, roofs=roofs)
             extras[str(cfg)] = res
             del rr
             torch.cuda.empty_cache()
@@ -517,6 +618,7 @@ def main():
                                    else "one GPU; one workgroup per (batch, head) chain")},
         "roofline": main_res["roofline"],
         "cpu_baseline": cpu,
+        "measured_roofs": roofs,
         "detail": {k: v for k, v in main_res.items() if k not in ("roofline",)},
         "workloads": extras,
         "device": torch.cuda.get_device_name(0),

@@ -21,15 +21,18 @@
  *     (T mod b != 0) follows the same rules.
  *   - eta is one fp32 learning rate per head.
  *   - All arrays are dense, row-major, and live in DEVICE memory owned by the
- *     caller.  The only memory the library allocates is the workspace of a
- *     segmented TTT-Linear scan (below): one device buffer per (device,
- *     stream) pair, grown on demand and kept until the process exits.  No
- *     other state is kept between calls.
+ *     caller.  The library allocates no memory and keeps no state between
+ *     calls.  The TTT-Linear scan and its backward take a caller-owned device
+ *     workspace (sized by ttt_linear_workspace_bytes /
+ *     ttt_linear_backward_workspace_bytes for the same sizes); its contents
+ *     need no initialisation and are scratch after the call.  Calls that use
+ *     one workspace must be ordered (e.g. on one stream).
  *   - qkv_dtype selects the element type of Q/K/V/Y (and q/k/v/y): TTT_F32
  *     (float) or TTT_BF16 (bfloat16 bits, round-to-nearest-even on output).
  *     Fast-weight state is always fp32.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default
- *     stream) and the call returns without synchronising.
+ *     stream) and the call returns without synchronising; no call makes a
+ *     synchronising HIP call, so every call can be captured into a HIP graph.
  *   - Arguments are validated before any HIP call; on an error nothing is
  *     launched and nothing is written.  No C++ exception crosses the ABI.
  *   - Results are deterministic run to run (no atomics, fixed reduction
@@ -90,10 +93,12 @@ typedef enum {
  * composes them into every segment's start state, and one runs all segments'
  * scans at once.  The result is the same mini-batch descent; only the fp32
  * rounding order of the state differs from a single-segment scan.  The
- * maps and start states (B*H*(3 nseg - 2)*d*d*4 bytes) live in the stream's
- * workspace: calls on one stream share it, calls on different streams do
- * not.  ttt_linear_segments reports the segment count a call would use; the
- * environment variable TTT_LINEAR_SEGMENTS=S (1..30) forces S segments.
+ * maps and start states (B*H*(3 nseg - 2)*d*d*4 bytes) live in the caller's
+ * workspace.  The call uses the segment count ttt_linear_segments reports
+ * when workspace_bytes >= ttt_linear_workspace_bytes(B, H, T, d, b,
+ * qkv_dtype); with less it uses the fastest count whose maps and states fit
+ * (NULL / 0 bytes: one segment, which needs none).  The environment variable
+ * TTT_LINEAR_SEGMENTS=S (1..30) forces S segments (fewer if they do not fit).
  *
  * fp32 Q/K/V at d = 64, b = 16 with B*H*4 <= the GPU's compute units: each
  * chain's W is split by columns over 4 workgroups (the dual form keeps W's
@@ -101,14 +106,29 @@ typedef enum {
  * (no composition launch).  Same arithmetic, another order of the sums over
  * the 64 input rows.  TTT_LINEAR_F32_COLS=0 keeps one workgroup per chain.
  *
- * Errors: TTT_ERR_INVALID_ARG, TTT_ERR_UNSUPPORTED (d, b, dtype, or on-chip
- * memory the shape needs), TTT_ERR_HIP (including a failed workspace
- * allocation).
+ *   workspace    device memory of workspace_bytes bytes (may be NULL when
+ *                workspace_bytes is 0), owned by the caller; must not overlap
+ *                any other argument.
+ *
+ * Errors: TTT_ERR_INVALID_ARG (also workspace_bytes < 0, or a NULL workspace
+ * with workspace_bytes > 0), TTT_ERR_UNSUPPORTED (d, b, dtype, T above
+ * 2^31 - 1 or the kernels' own length bound, or on-chip memory the shape
+ * needs), TTT_ERR_HIP (a kernel launch failed).
  */
 int ttt_linear_forward(const void* Q, const void* K, const void* V, int qkv_dtype,
                        const float* W0, int w0_per_batch, const float* eta,
                        int64_t B, int64_t H, int64_t T, int d, int b,
-                       void* Y, float* W_out, void* stream);
+                       void* Y, float* W_out, void* workspace, int64_t workspace_bytes,
+                       void* stream);
+
+/*
+ * Workspace bytes ttt_linear_forward (and ttt_linear_forward_ex) uses for
+ * these sizes on the current device: B*H*(3 S - 2)*d*d*4 for the S segments
+ * ttt_linear_segments reports, 0 when unsegmented.  Negative ttt_status for
+ * sizes the forward would reject.  Needs no device memory; queries the
+ * device's compute-unit count.
+ */
+int64_t ttt_linear_workspace_bytes(int64_t B, int64_t H, int64_t T, int d, int b, int qkv_dtype);
 
 /*
  * ttt_linear_forward with the layer's input prologue fused into the scan:
@@ -142,7 +162,8 @@ int ttt_linear_forward_ex(const void* Q, const void* K, const void* V, int qkv_d
                           const float* W0, int w0_per_batch, const float* eta,
                           const float* eta_tok, const float* ln_q, const float* ln_k, float ln_eps,
                           int read_mode, int64_t B, int64_t H, int64_t T, int d, int b,
-                          void* Y, float* W_out, void* stream);
+                          void* Y, float* W_out, void* workspace, int64_t workspace_bytes,
+                          void* stream);
 /*
  * TTT-MLP, chunked dual form.  Inner model f(z) = SiLU(z W1) W2, W1 [d][m],
  * W2 [m][d], no biases ("Test-Time Training (TTT) Layers for Sequence
@@ -226,10 +247,14 @@ int ttt_linear_decode_step(const void* q, const void* k, const void* v, int qkv_
  * segment's start W, cotangent maps composed from dW_out backwards give every
  * segment's end G, and then all segments run at once (deta and dW0 are
  * summed in a fixed order).  ttt_linear_backward_segments reports the count;
- * TTT_LINEAR_BWD_SEGMENTS=S (1..30) forces it.  Workspace (the stream's),
- * in d*d*4-byte matrices per chain: S*ceil(ceil(T/16)/S) recomputed
- * chunk-start states, with S > 1 another 6 S - 4 (maps, start and end
- * states), and one more when W0 is shared (per-chain dW0).
+ * TTT_LINEAR_BWD_SEGMENTS=S (1..30) forces it.  Workspace, caller-owned, in
+ * d*d*4-byte matrices per chain: S*ceil(ceil(T/16)/S) recomputed chunk-start
+ * states (half that for bf16 inputs, which store them in bf16), with S > 1
+ * another 6 S - 4 (maps, start and end states), and one more when W0 is
+ * shared (per-chain dW0).  With workspace_bytes >=
+ * ttt_linear_backward_workspace_bytes(...) the call uses the count
+ * ttt_linear_backward_segments reports; with less, the fastest count that
+ * fits; if not even one segment's states fit, TTT_ERR_INVALID_ARG.
  * Errors as for ttt_linear_forward.
  */
 int ttt_linear_backward(const void* Q, const void* K, const void* V, int qkv_dtype,
@@ -237,7 +262,16 @@ int ttt_linear_backward(const void* Q, const void* K, const void* V, int qkv_dty
                         int64_t B, int64_t H, int64_t T, int d, int b,
                         const void* dY, const float* dW_out,
                         void* dQ, void* dK, void* dV, float* dW0, float* deta,
-                        void* stream);
+                        void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * Workspace bytes that serve every ttt_linear_backward and
+ * ttt_linear_backward_ex call of these sizes on the current device (shared or
+ * per-batch W0, with or without the prologue).  Negative ttt_status for sizes
+ * the backward would reject.
+ */
+int64_t ttt_linear_backward_workspace_bytes(int64_t B, int64_t H, int64_t T, int d, int b,
+                                            int qkv_dtype);
 /*
  * ttt_linear_backward with the input prologue of ttt_linear_forward_ex: the
  * gradients of L = <dY, Y> + <dW_out, W_out> for (Y, W_out) =
@@ -279,7 +313,7 @@ int ttt_linear_backward_ex(const void* Q, const void* K, const void* V, int qkv_
                            float ln_eps, int read_mode, int64_t B, int64_t H, int64_t T, int d,
                            int b, const void* dY, const float* dW_out, void* dQ, void* dK,
                            void* dV, float* dW0, float* deta, float* deta_tok, float* dln_q,
-                           float* dln_k, void* stream);
+                           float* dln_k, void* workspace, int64_t workspace_bytes, void* stream);
 /*
  * Number of sequence segments ttt_linear_backward would cut each chain into
  * for these sizes on the current device (1 = unsegmented).  Negative
@@ -301,16 +335,17 @@ int ttt_linear_decode_step_ex(const void* q, const void* k, const void* v, int q
                               float* W, const float* eta, const float* eta_tok,
                               const float* ln_q, const float* ln_k, float ln_eps, int read_mode,
                               int64_t B, int64_t H, int d, void* y, void* stream);
-/* Static, human-readable text for a status code (never NULL). */
 /*
  * Number of sequence segments ttt_linear_forward would cut each chain into
- * for these sizes on the current device (1 = one workgroup scans the whole
+ * for these sizes on the current device, given at least
+ * ttt_linear_workspace_bytes of workspace (1 = one workgroup scans the whole
  * chain).  Returns a negative ttt_status for arguments ttt_linear_forward
  * would reject.  Needs no device memory; queries the device's compute-unit
  * count.
  */
 int ttt_linear_segments(int64_t B, int64_t H, int64_t T, int d, int b, int qkv_dtype);
 
+/* Static, human-readable text for a status code (never NULL). */
 const char* ttt_status_string(int status);
 
 /* ABI version of this header: (major << 16) | minor. */

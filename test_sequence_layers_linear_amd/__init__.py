@@ -2,8 +2,8 @@
 
 Argument marshalling only.  Every step of the scan runs in the HIP kernels
 behind the C ABI declared in include/ttt.h; this module checks tensor
-properties, allocates outputs with torch (device memory only) and passes raw
-device pointers plus the current HIP stream.  There is no CPU fallback: if
+properties, allocates outputs and workspaces with torch (device memory only)
+and passes raw device pointers plus the current HIP stream.  There is no CPU fallback: if
 libttt.so is missing or a call fails, an exception is raised.
 
 Functions (same names as the C ABI):
@@ -51,10 +51,10 @@ def load_library():
                            "or python test_sequence_layers_linear_amd/build.py")
     lib = ctypes.CDLL(LIB_PATH)
     P, I, L = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
-    lib.ttt_linear_forward.argtypes = [P, P, P, I, P, I, P, L, L, L, I, I, P, P, P]
+    lib.ttt_linear_forward.argtypes = [P, P, P, I, P, I, P, L, L, L, I, I, P, P, P, L, P]
     lib.ttt_linear_forward.restype = I
     lib.ttt_linear_forward_ex.argtypes = [P, P, P, I, P, I, P, P, P, P, ctypes.c_float, I,
-                                          L, L, L, I, I, P, P, P]
+                                          L, L, L, I, I, P, P, P, L, P]
     lib.ttt_linear_forward_ex.restype = I
     lib.ttt_mlp_forward.argtypes = [P, P, P, I, P, P, I, P, L, L, L, I, I, I, P, P, P, P]
     lib.ttt_mlp_forward.restype = I
@@ -64,15 +64,19 @@ def load_library():
                                               L, L, I, P, P]
     lib.ttt_linear_decode_step_ex.restype = I
     lib.ttt_linear_backward.argtypes = [P, P, P, I, P, I, P, L, L, L, I, I, P, P,
-                                        P, P, P, P, P, P]
+                                        P, P, P, P, P, P, L, P]
     lib.ttt_linear_backward.restype = I
     lib.ttt_linear_backward_ex.argtypes = [P, P, P, I, P, I, P, P, P, P, ctypes.c_float, I,
-                                           L, L, L, I, I, P, P, P, P, P, P, P, P, P, P, P]
+                                           L, L, L, I, I, P, P, P, P, P, P, P, P, P, P, P, L, P]
     lib.ttt_linear_backward_ex.restype = I
     lib.ttt_linear_backward_segments.argtypes = [L, L, L, I, I, I]
     lib.ttt_linear_backward_segments.restype = I
     lib.ttt_linear_segments.argtypes = [L, L, L, I, I, I]
     lib.ttt_linear_segments.restype = I
+    lib.ttt_linear_workspace_bytes.argtypes = [L, L, L, I, I, I]
+    lib.ttt_linear_workspace_bytes.restype = L
+    lib.ttt_linear_backward_workspace_bytes.argtypes = [L, L, L, I, I, I]
+    lib.ttt_linear_backward_workspace_bytes.restype = L
     lib.ttt_status_string.argtypes = [I]
     lib.ttt_status_string.restype = ctypes.c_char_p
     lib.ttt_abi_version.argtypes = []
@@ -111,15 +115,33 @@ def _need(t: torch.Tensor, name: str, device, dtype=None):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _workspace(nbytes: int, device, workspace):
+    """The workspace tensor of a call: the caller's (uint8, on the device,
+    at least nbytes) or a new torch allocation of nbytes."""
+    if nbytes < 0:
+        _check(nbytes)
+    if workspace is None:
+        return torch.empty(max(int(nbytes), 0), dtype=torch.uint8, device=device)
+    _need(workspace, "workspace", device, torch.uint8)
+    return workspace
+
+
+def _ws_args(ws):
+    return (ws.data_ptr() if ws.numel() else None), ws.numel()
+
+
 def _stream_handle(device, stream):
     if stream is None:
         stream = torch.cuda.current_stream(device)
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def ttt_linear_forward(Q, K, V, W0, eta, b: int, Y=None, W_out=None, stream=None):
+def ttt_linear_forward(Q, K, V, W0, eta, b: int, Y=None, W_out=None, workspace=None,
+                       stream=None):
     """TTT-Linear dual-form forward.  Q,K,V [B,H,T,d] fp32/bf16 on a GPU;
     W0 fp32 [H,d,d] (shared over the batch) or [B,H,d,d]; eta fp32 [H].
+    workspace: a uint8 device tensor for the segment maps (None: one of
+    ttt_linear_workspace_bytes bytes is allocated with torch).
     Returns (Y [B,H,T,d] in Q's dtype, W_out fp32 [B,H,d,d])."""
     lib = load_library()
     if Q.dim() != 4:
@@ -141,16 +163,18 @@ def ttt_linear_forward(Q, K, V, W0, eta, b: int, Y=None, W_out=None, stream=None
         W_out = torch.empty((B, H, d, d), device=dev, dtype=torch.float32)
     _need(Y, "Y", dev, Q.dtype)
     _need(W_out, "W_out", dev, torch.float32)
+    ws = _workspace(lib.ttt_linear_workspace_bytes(B, H, T, d, int(b), _dtype_code(Q))
+                    if workspace is None else 0, dev, workspace)
     _check(lib.ttt_linear_forward(Q.data_ptr(), K.data_ptr(), V.data_ptr(), _dtype_code(Q),
                                   W0.data_ptr(), int(per_batch), eta.data_ptr(),
                                   B, H, T, d, int(b), Y.data_ptr(), W_out.data_ptr(),
-                                  _stream_handle(dev, stream)))
+                                  *_ws_args(ws), _stream_handle(dev, stream)))
     return Y, W_out
 
 
 def ttt_linear_forward_ex(Q, K, V, W0, eta, b: int, eta_tok=None, ln_q=None, ln_k=None,
                           ln_eps: float = 1e-5, read_chunk_start: bool = False, Y=None,
-                          W_out=None, stream=None):
+                          W_out=None, workspace=None, stream=None):
     """ttt_linear_forward with the input prologue: q and k LayerNorm'd over
     the head dim (ln_q / ln_k fp32 [H,2,d]: gamma, beta) and a step size per
     token (eta_tok fp32 [B,H,T]); None leaves that part out.
@@ -185,11 +209,14 @@ def ttt_linear_forward_ex(Q, K, V, W0, eta, b: int, eta_tok=None, ln_q=None, ln_
         W_out = torch.empty((B, H, d, d), device=dev, dtype=torch.float32)
     _need(Y, "Y", dev, Q.dtype)
     _need(W_out, "W_out", dev, torch.float32)
+    ws = _workspace(lib.ttt_linear_workspace_bytes(B, H, T, d, int(b), _dtype_code(Q))
+                    if workspace is None else 0, dev, workspace)
     _check(lib.ttt_linear_forward_ex(Q.data_ptr(), K.data_ptr(), V.data_ptr(), _dtype_code(Q),
                                      W0.data_ptr(), int(per_batch), eta.data_ptr(), ptrs[0],
                                      ptrs[1], ptrs[2], float(ln_eps), int(bool(read_chunk_start)),
                                      B, H, T, d, int(b),
-                                     Y.data_ptr(), W_out.data_ptr(), _stream_handle(dev, stream)))
+                                     Y.data_ptr(), W_out.data_ptr(), *_ws_args(ws),
+                                     _stream_handle(dev, stream)))
     return Y, W_out
 
 
@@ -256,7 +283,7 @@ def ttt_linear_decode_step(q, k, v, W, eta, y=None, stream=None):
 
 
 def ttt_linear_backward(Q, K, V, W0, eta, b: int, dY, dW_out=None, dQ=None, dK=None, dV=None,
-                        dW0=None, deta=None, stream=None):
+                        dW0=None, deta=None, workspace=None, stream=None):
     """Gradients of <dY, Y> + <dW_out, W_out> for (Y, W_out) =
     ttt_linear_forward(Q, K, V, W0, eta, b), with respect to Q, K, V, W0 and
     eta.  dY has Q's shape and dtype; dW_out fp32 [B,H,d,d] (None: zeros).
@@ -290,17 +317,19 @@ def ttt_linear_backward(Q, K, V, W0, eta, b: int, dY, dW_out=None, dQ=None, dK=N
         _need(t, n, dev, Q.dtype)
     _need(dW0, "dW0", dev, torch.float32)
     _need(deta, "deta", dev, torch.float32)
+    ws = _workspace(lib.ttt_linear_backward_workspace_bytes(B, H, T, d, int(b), _dtype_code(Q))
+                    if workspace is None else 0, dev, workspace)
     _check(lib.ttt_linear_backward(Q.data_ptr(), K.data_ptr(), V.data_ptr(), _dtype_code(Q),
                                    W0.data_ptr(), int(per_batch), eta.data_ptr(), B, H, T, d,
                                    int(b), dY.data_ptr(), dW_out.data_ptr(), dQ.data_ptr(),
                                    dK.data_ptr(), dV.data_ptr(), dW0.data_ptr(), deta.data_ptr(),
-                                   _stream_handle(dev, stream)))
+                                   *_ws_args(ws), _stream_handle(dev, stream)))
     return dQ, dK, dV, dW0, deta
 
 
 def ttt_linear_backward_ex(Q, K, V, W0, eta, b: int, dY, dW_out=None, eta_tok=None, ln_q=None,
                            ln_k=None, ln_eps: float = 1e-5, read_chunk_start: bool = False,
-                           stream=None):
+                           workspace=None, stream=None):
     """Gradients of <dY, Y> + <dW_out, W_out> for (Y, W_out) =
     ttt_linear_forward_ex(Q, K, V, W0, eta, b, eta_tok, ln_q, ln_k, ln_eps,
     read_chunk_start).  Returns a dict: dQ, dK, dV (of the raw rows, Q's
@@ -342,6 +371,8 @@ def ttt_linear_backward_ex(Q, K, V, W0, eta, b: int, dY, dW_out=None, eta_tok=No
         out["d" + n] = g
         ins.append(t.data_ptr())
         grads.append(g.data_ptr())
+    ws = _workspace(lib.ttt_linear_backward_workspace_bytes(B, H, T, d, int(b), _dtype_code(Q))
+                    if workspace is None else 0, dev, workspace)
     _check(lib.ttt_linear_backward_ex(Q.data_ptr(), K.data_ptr(), V.data_ptr(), _dtype_code(Q),
                                       W0.data_ptr(), int(per_batch), eta.data_ptr(), ins[0],
                                       ins[1], ins[2], float(ln_eps), int(bool(read_chunk_start)),
@@ -349,7 +380,7 @@ def ttt_linear_backward_ex(Q, K, V, W0, eta, b: int, dY, dW_out=None, eta_tok=No
                                       out["dQ"].data_ptr(), out["dK"].data_ptr(),
                                       out["dV"].data_ptr(), out["dW0"].data_ptr(),
                                       out["deta"].data_ptr(), grads[0], grads[1], grads[2],
-                                      _stream_handle(dev, stream)))
+                                      *_ws_args(ws), _stream_handle(dev, stream)))
     return out
 
 
@@ -400,6 +431,26 @@ def ttt_linear_segments(B: int, H: int, T: int, d: int, b: int, dtype=torch.bflo
     return n
 
 
+def ttt_linear_workspace_bytes(B: int, H: int, T: int, d: int, b: int,
+                               dtype=torch.bfloat16) -> int:
+    """Workspace bytes ttt_linear_forward uses for these sizes on the current
+    device (0 when the scan is not segmented)."""
+    code = TTT_F32 if dtype == torch.float32 else TTT_BF16
+    n = load_library().ttt_linear_workspace_bytes(int(B), int(H), int(T), int(d), int(b), code)
+    _check(min(n, 0))
+    return n
+
+
+def ttt_linear_backward_workspace_bytes(B: int, H: int, T: int, d: int, b: int,
+                                        dtype=torch.bfloat16) -> int:
+    """Workspace bytes that serve every ttt_linear_backward(_ex) call of these sizes."""
+    code = TTT_F32 if dtype == torch.float32 else TTT_BF16
+    n = load_library().ttt_linear_backward_workspace_bytes(int(B), int(H), int(T), int(d),
+                                                           int(b), code)
+    _check(min(n, 0))
+    return n
+
+
 def ttt_linear_backward_segments(B: int, H: int, T: int, d: int, b: int,
                                  dtype=torch.bfloat16) -> int:
     """Sequence segments ttt_linear_backward cuts each chain into for these
@@ -413,7 +464,8 @@ def ttt_linear_backward_segments(B: int, H: int, T: int, d: int, b: int,
 __all__ = [
     "ttt_linear_forward", "ttt_linear_forward_ex", "ttt_mlp_forward", "ttt_linear_decode_step",
     "ttt_linear_decode_step_ex", "ttt_linear_backward",
-    "ttt_linear_segments", "ttt_linear_backward_segments",
+    "ttt_linear_segments", "ttt_linear_backward_segments", "ttt_linear_workspace_bytes",
+    "ttt_linear_backward_workspace_bytes",
     "load_library",
     "status_string", "TTTError", "LIB_PATH", "TTT_F32", "TTT_BF16",
 ]

@@ -36,6 +36,9 @@ EXTRA = {
     "ttt_linear_mfma_f32.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "ttt_linear_backward.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "ttt_linear_cols_f32.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    # the MFMA loop of the measured roof: AGPR accumulators make the compiler
+    # rotate them through VGPRs every iteration
+    "ttt_roofs.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

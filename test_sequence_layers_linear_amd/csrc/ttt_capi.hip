@@ -10,8 +10,7 @@
 
 #include <algorithm>
 #include <atomic>
-#include <mutex>
-#include <vector>
+#include <functional>
 
 namespace {
 
@@ -19,7 +18,7 @@ using ttt::LinearArgs;
 using ttt::MlpArgs;
 using ttt::DecodeArgs;
 
-constexpr int kAbiVersion = (1 << 16) | 2;
+constexpr int kAbiVersion = (2 << 16) | 0;
 
 bool valid_dtype(int dt) { return dt == TTT_F32 || dt == TTT_BF16; }
 size_t elem_bytes(int dt) { return dt == TTT_F32 ? 4 : 2; }
@@ -49,6 +48,9 @@ bool d_supported(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 
 // largest grid.x the launchers use
 constexpr int64_t kMaxUnits = 0x7fffffff;
+// longest sequence: every kernel indexes a chain's tokens with 32-bit ints
+// (the MFMA kernels' byte offsets are bounded tighter by their own checks)
+constexpr int64_t kMaxTokens = 0x7fffffff;
 
 int hip_status(hipError_t e) { return e == hipSuccess ? TTT_OK : TTT_ERR_HIP; }
 
@@ -68,30 +70,53 @@ int device_cus()
     return n;
 }
 
-// Segment count for a chain-parallel scan of `units` chains of T tokens.
-// Each launch of the split runs all its workgroups at once, one per CU (more
-// would queue or share CUs and stretch the slowest ones), so S is limited to
-// what fits; within that it minimises
-//   ceil(chunks / S) (map + fwd) + (S - 1) apply + launch
-// against the unsplit chunks * fwd (costs measured on MI355X).
-// TTT_LINEAR_SEGMENTS=S (1 <= S <= kMaxSegments) forces S segments (at least
-// one chunk each), for tests and tuning.
-ttt::SegmentPlan plan_segments(int64_t units, int64_t T, int chunk, const ttt::SegmentCosts& cost)
+// Workspace of a segmented forward with S segments per chain: the maps of
+// segments 0..S-2 ([units][S-1][2][d][d]) and the start states
+// ([units][S][d][d]), fp32.  One segment needs none.
+int64_t forward_workspace_bytes(int64_t units, int d, int S)
+{
+    if (S <= 1) return 0;
+    return units * (3 * static_cast<int64_t>(S) - 2) * d * d * static_cast<int64_t>(sizeof(float));
+}
+
+ttt::SegmentPlan with_segments(int64_t T, int chunk, int S)
 {
     ttt::SegmentPlan p;
     p.seg_len = T;
     const int64_t chunks = (T + chunk - 1) / chunk;
+    if (S > 1 && chunks > 0) {
+        p.seg_len = ((chunks + S - 1) / S) * chunk;
+        p.nseg = static_cast<int>((T + p.seg_len - 1) / p.seg_len);
+    }
+    return p;
+}
+
+// Segment count for a chain-parallel scan of `units` chains of T tokens whose
+// maps and start states must fit in `ws_bytes` of workspace.  Each launch of
+// the split runs all its workgroups at once, one per CU (more would queue or
+// share CUs and stretch the slowest ones), so S is limited to what fits;
+// within that it minimises
+//   ceil(chunks / S) (map + fwd) + (S - 1) apply + launch
+// against the unsplit chunks * fwd (costs measured on MI355X).
+// TTT_LINEAR_SEGMENTS=S (1 <= S <= kMaxSegments) forces S segments (at least
+// one chunk each; fewer if the workspace is too small), for tests and tuning.
+ttt::SegmentPlan plan_segments(int64_t units, int64_t T, int chunk, int d,
+                               const ttt::SegmentCosts& cost, int64_t ws_bytes)
+{
+    const int64_t chunks = (T + chunk - 1) / chunk;
+    auto fits = [&](int S) { return forward_workspace_bytes(units, d, S) <= ws_bytes; };
     if (const char* env = getenv("TTT_LINEAR_SEGMENTS")) {
-        const long S = std::min<long>(strtol(env, nullptr, 10), ttt::kMaxSegments);
+        long S = std::min<long>(strtol(env, nullptr, 10), ttt::kMaxSegments);
         if (S >= 1 && chunks > 0) {
-            p.seg_len = ((chunks + S - 1) / S) * chunk;
-            p.nseg = static_cast<int>((T + p.seg_len - 1) / p.seg_len);
-            return p;
+            S = std::min<long>(S, chunks);
+            while (S > 1 && !fits(static_cast<int>(with_segments(T, chunk, static_cast<int>(S)).nseg)))
+                --S;
+            return with_segments(T, chunk, static_cast<int>(S));
         }
     }
     const int64_t cus = device_cus();
     const int64_t scan_blocks = units * cost.scan_blocks_per_segment;
-    if (cus <= 0 || 2 * scan_blocks > cus || chunks < 4) return p;
+    if (cus <= 0 || 2 * scan_blocks > cus || chunks < 4) return with_segments(T, chunk, 1);
     double best = static_cast<double>(chunks) * cost.fwd;
     int best_s = 1;
     for (int S = 2; S <= ttt::kMaxSegments; ++S) {
@@ -100,14 +125,11 @@ ttt::SegmentPlan plan_segments(int64_t units, int64_t T, int chunk, const ttt::S
             break;
         const int64_t per = (chunks + S - 1) / S;
         if (per < 2) break;
+        if (!fits(with_segments(T, chunk, S).nseg)) continue;
         const double t = per * (cost.map + cost.fwd) + (S - 1) * cost.apply + cost.launch;
         if (t < best) { best = t; best_s = S; }
     }
-    if (best_s > 1) {
-        p.seg_len = ((chunks + best_s - 1) / best_s) * chunk;
-        p.nseg = static_cast<int>((T + p.seg_len - 1) / p.seg_len);
-    }
-    return p;
+    return with_segments(T, chunk, best_s);
 }
 
 // Segment count for the backward of a TTT-Linear scan: each segment pays
@@ -116,19 +138,20 @@ ttt::SegmentPlan plan_segments(int64_t units, int64_t T, int chunk, const ttt::S
 // max_per_cu segment-backward workgroups share a CU, each slowed by `share`
 // per extra workgroup per CU; the maps launches may hold maps_per_cu per CU.
 // TTT_LINEAR_BWD_SEGMENTS=S forces S segments.
-ttt::SegmentPlan plan_backward(int64_t units, int64_t T, int chunk, const ttt::BwdCosts& cost)
+ttt::SegmentPlan plan_backward(int64_t units, int64_t T, int chunk, const ttt::BwdCosts& cost,
+                               const std::function<bool(const ttt::SegmentPlan&)>& fits)
 {
-    ttt::SegmentPlan p;
-    p.seg_len = T;
     const int64_t chunks = (T + chunk - 1) / chunk;
     if (const char* env = getenv("TTT_LINEAR_BWD_SEGMENTS")) {
-        const long S = std::min<long>(strtol(env, nullptr, 10), ttt::kMaxSegments);
+        long S = std::min<long>(strtol(env, nullptr, 10), ttt::kMaxSegments);
         if (S >= 1 && chunks > 0) {
-            p.seg_len = ((chunks + S - 1) / S) * chunk;
-            p.nseg = static_cast<int>((T + p.seg_len - 1) / p.seg_len);
-            return p;
+            S = std::min<long>(S, chunks);
+            while (S > 1 && !fits(with_segments(T, chunk, static_cast<int>(S))))
+                --S;
+            return with_segments(T, chunk, static_cast<int>(S));
         }
     }
+    ttt::SegmentPlan p = with_segments(T, chunk, 1);
     const int64_t cus = device_cus();
     if (cus <= 0 || 2 * units > cost.max_per_cu * cus || chunks < 4) return p;
     const int map_blocks = std::max(2, cost.fmap_blocks_per_segment);
@@ -142,60 +165,9 @@ ttt::SegmentPlan plan_backward(int64_t units, int64_t T, int chunk, const ttt::B
         const double load = std::max(1.0, static_cast<double>(units * S) / static_cast<double>(cus));
         const double t = per * (cost.bwd * (1.0 + cost.share * (load - 1.0)) + cost.fmap + cost.gmap) +
                          2.0 * (S - 1) * cost.apply + cost.launch;
-        if (t < best) { best = t; best_s = S; }
+        if (t < best && fits(with_segments(T, chunk, S))) { best = t; best_s = S; }
     }
-    if (best_s > 1) {
-        p.seg_len = ((chunks + best_s - 1) / best_s) * chunk;
-        p.nseg = static_cast<int>((T + p.seg_len - 1) / p.seg_len);
-    }
-    return p;
-}
-
-// Workspace for the segment maps: one device buffer per (device, stream),
-// grown on demand and kept until the process ends.  Calls on one stream are
-// ordered by the stream, so they can share its buffer; calls on different
-// streams get different buffers.  Before a buffer is replaced by a larger one
-// its stream is synchronised, so no enqueued kernel still uses it.
-hipError_t workspace_get(void** ptr, size_t bytes, hipStream_t stream)
-{
-    struct Entry {
-        int dev;
-        hipStream_t stream;
-        void* p;
-        size_t bytes;
-    };
-    static std::mutex mu;
-    static std::vector<Entry> cache;
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    std::lock_guard<std::mutex> lock(mu);
-    Entry* hit = nullptr;
-    for (Entry& x : cache)
-        if (x.dev == dev && x.stream == stream) hit = &x;
-    if (hit && hit->bytes >= bytes) {
-        *ptr = hit->p;
-        return hipSuccess;
-    }
-    if (hit) {
-        e = hipStreamSynchronize(stream);
-        if (e != hipSuccess) return e;
-        e = hipFree(hit->p);
-        hit->p = nullptr;
-        hit->bytes = 0;
-        if (e != hipSuccess) return e;
-    }
-    void* p = nullptr;
-    e = hipMalloc(&p, bytes);
-    if (e != hipSuccess) return e;
-    if (hit) {
-        hit->p = p;
-        hit->bytes = bytes;
-    } else {
-        cache.push_back(Entry{dev, stream, p, bytes});
-    }
-    *ptr = p;
-    return hipSuccess;
+    return with_segments(T, chunk, best_s);
 }
 
 // fp32 scans split each chain's columns over 4 workgroups while those fit the
@@ -211,20 +183,17 @@ bool use_cols_f32(const LinearArgs& a)
     return cus > 0 && a.B * a.H * ttt::kColsSlices <= cus;
 }
 
-// Runs a segmented MFMA linear scan: workspace for the maps and the segment
-// start states, then the launches.  The start states (including the copy of
-// W0 for the first segment) are complete before any segment writes W_out, so
-// W_out may overwrite W0.
-int run_linear_segmented(LinearArgs a, ttt::SegmentPlan p,
+// Runs a (possibly segmented) MFMA linear scan with the maps and start
+// states in the caller's workspace (planned to fit it).  The start states
+// (including the copy of W0 for the first segment) are complete before any
+// segment writes W_out, so W_out may overwrite W0.
+int run_linear_segmented(LinearArgs a, ttt::SegmentPlan p, void* ws,
                          hipError_t (*launch)(const LinearArgs&, const ttt::SegmentPlan&))
 {
     if (p.nseg <= 1) return hip_status(launch(a, p));
     const int64_t units = a.B * a.H;
     const size_t state = static_cast<size_t>(a.d) * a.d * sizeof(float);
     const size_t map_bytes = static_cast<size_t>(units) * (p.nseg - 1) * 2 * state;
-    const size_t start_bytes = static_cast<size_t>(units) * p.nseg * state;
-    void* ws = nullptr;
-    if (workspace_get(&ws, map_bytes + start_bytes, a.stream) != hipSuccess) return TTT_ERR_HIP;
     p.maps = static_cast<float*>(ws);
     p.wstart = p.maps + map_bytes / sizeof(float);
     return hip_status(launch(a, p));
@@ -251,23 +220,55 @@ const char* ttt_status_string(int status)
 
 namespace {
 
+// The MFMA scan (with its segment costs) that runs a TTT-Linear forward, or
+// none (the generic kernel: never segmented).
+struct LinearScan {
+    const ttt::SegmentCosts* cost;
+    hipError_t (*launch)(const LinearArgs&, const ttt::SegmentPlan&);
+};
+
+LinearScan pick_scan(const LinearArgs& a)
+{
+    if (ttt::linear_mfma_supports(a)) return {&ttt::kLinearBf16Costs, ttt::launch_linear_mfma};
+    if (use_cols_f32(a)) return {&ttt::kLinearF32ColsCosts, ttt::launch_linear_cols_f32};
+    if (ttt::linear_mfma_f32_supports(a)) return {&ttt::kLinearF32Costs, ttt::launch_linear_mfma_f32};
+    return {nullptr, nullptr};
+}
+
+// The plan a forward of these sizes uses with `ws_bytes` of workspace.
+ttt::SegmentPlan plan_forward(const LinearArgs& a, int64_t ws_bytes)
+{
+    const LinearScan k = pick_scan(a);
+    if (!k.cost || a.B * a.H == 0 || a.T == 0) return with_segments(a.T, a.b, 1);
+    return plan_segments(a.B * a.H, a.T, a.b, a.d, *k.cost, ws_bytes);
+}
+
+// Size checks shared by the TTT-Linear entry points and their queries.
+int linear_sizes_status(int64_t B, int64_t H, int64_t T, int d, int b, int qkv_dtype)
+{
+    if (B < 0 || H < 0 || T < 0 || b < 1) return TTT_ERR_INVALID_ARG;
+    if (!valid_dtype(qkv_dtype) || !d_supported(d) || b > 64) return TTT_ERR_UNSUPPORTED;
+    int64_t units = B;
+    if (!mul_ok(units, H) || units > kMaxUnits || T > kMaxTokens) return TTT_ERR_UNSUPPORTED;
+    int64_t n = units;
+    if (!mul_ok(n, T) || !mul_ok(n, d) || !mul_ok(n, 4)) return TTT_ERR_UNSUPPORTED;
+    return TTT_OK;
+}
+
 // ttt_linear_forward with an optional input prologue (pro.active(): d = 64,
-// b = 16 only).
+// b = 16 only) and the caller's workspace.
 int linear_forward_impl(const void* Q, const void* K, const void* V, int qkv_dtype,
                         const float* W0, int w0_per_batch, const float* eta,
                         int64_t B, int64_t H, int64_t T, int d, int b,
-                        void* Y, float* W_out, void* stream, const ttt::Prologue& pro)
+                        void* Y, float* W_out, void* ws, int64_t ws_bytes, void* stream,
+                        const ttt::Prologue& pro)
 {
-    if (B < 0 || H < 0 || T < 0 || b < 1 || (w0_per_batch != 0 && w0_per_batch != 1))
-        return TTT_ERR_INVALID_ARG;
-    if (!valid_dtype(qkv_dtype) || !d_supported(d) || b > 64)
-        return TTT_ERR_UNSUPPORTED;
-    int64_t units = B;
-    if (!mul_ok(units, H) || units > kMaxUnits) return TTT_ERR_UNSUPPORTED;
+    if (w0_per_batch != 0 && w0_per_batch != 1) return TTT_ERR_INVALID_ARG;
+    if (ws_bytes < 0 || (ws_bytes > 0 && !ws)) return TTT_ERR_INVALID_ARG;
+    if (const int st = linear_sizes_status(B, H, T, d, b, qkv_dtype)) return st;
+    const int64_t units = B * H;
     if (units == 0) return TTT_OK;
-    int64_t n_qkv = units;
-    if (!mul_ok(n_qkv, T) || !mul_ok(n_qkv, d) || !mul_ok(n_qkv, 4)) return TTT_ERR_UNSUPPORTED;
-    n_qkv = n_qkv / 4 * static_cast<int64_t>(elem_bytes(qkv_dtype));
+    const int64_t n_qkv = units * T * d * static_cast<int64_t>(elem_bytes(qkv_dtype));
     const int64_t n_state = static_cast<int64_t>(d) * d * 4;
     if (!W0 || !eta || !W_out) return TTT_ERR_INVALID_ARG;
     if (T > 0 && (!Q || !K || !V || !Y)) return TTT_ERR_INVALID_ARG;
@@ -282,27 +283,22 @@ int linear_forward_impl(const void* Q, const void* K, const void* V, int qkv_dty
         if (overlap(rWo, in)) return TTT_ERR_INVALID_ARG;
     if (overlap(rWo, rW0) && !(w0_per_batch && static_cast<const void*>(W_out) == W0))
         return TTT_ERR_INVALID_ARG;
-    if (pro.active()) {
-        const Range rTok{pro.eta_tok, pro.eta_tok ? units * T * 4 : 0};
-        const Range rLq{pro.ln_q, pro.ln_q ? H * 2 * d * 4 : 0}, rLk{pro.ln_k, pro.ln_k ? H * 2 * d * 4 : 0};
-        for (const Range& in : {rTok, rLq, rLk})
-            if (overlap(rY, in) || overlap(rWo, in)) return TTT_ERR_INVALID_ARG;
-    }
+    const Range rTok{pro.eta_tok, pro.eta_tok ? units * T * 4 : 0};
+    const Range rLq{pro.ln_q, pro.ln_q ? H * 2 * d * 4 : 0}, rLk{pro.ln_k, pro.ln_k ? H * 2 * d * 4 : 0};
+    for (const Range& in : {rTok, rLq, rLk})
+        if (overlap(rY, in) || overlap(rWo, in)) return TTT_ERR_INVALID_ARG;
+    const Range rWs{ws, ws_bytes};
+    for (const Range& x : {rQ, rK, rV, rY, rW0, rWo, rEta, rTok, rLq, rLk})
+        if (overlap(rWs, x)) return TTT_ERR_INVALID_ARG;
 
     LinearArgs a{Q, K, V, qkv_dtype, W0, w0_per_batch, eta, B, H, T, d, b,
                  Y, W_out, static_cast<hipStream_t>(stream)};
     a.pro = pro;
     if (pro.active() && !ttt::linear_mfma_supports(a) && !ttt::linear_mfma_f32_supports(a))
         return TTT_ERR_UNSUPPORTED;
-    if (ttt::linear_mfma_supports(a))
-        return run_linear_segmented(a, plan_segments(units, T, b, ttt::kLinearBf16Costs),
-                                    ttt::launch_linear_mfma);
-    if (use_cols_f32(a))
-        return run_linear_segmented(a, plan_segments(units, T, b, ttt::kLinearF32ColsCosts),
-                                    ttt::launch_linear_cols_f32);
-    if (ttt::linear_mfma_f32_supports(a))
-        return run_linear_segmented(a, plan_segments(units, T, b, ttt::kLinearF32Costs),
-                                    ttt::launch_linear_mfma_f32);
+    const LinearScan k = pick_scan(a);
+    if (k.launch)
+        return run_linear_segmented(a, plan_forward(a, ws_bytes), ws, k.launch);
     if (ttt::linear_generic_lds_bytes(d, b) > static_cast<size_t>(ttt::kMaxLdsBytes))
         return TTT_ERR_UNSUPPORTED;
     return hip_status(ttt::launch_linear_generic(a));
@@ -316,17 +312,19 @@ extern "C" {
 int ttt_linear_forward(const void* Q, const void* K, const void* V, int qkv_dtype,
                        const float* W0, int w0_per_batch, const float* eta,
                        int64_t B, int64_t H, int64_t T, int d, int b,
-                       void* Y, float* W_out, void* stream)
+                       void* Y, float* W_out, void* workspace, int64_t workspace_bytes,
+                       void* stream)
 {
     return linear_forward_impl(Q, K, V, qkv_dtype, W0, w0_per_batch, eta, B, H, T, d, b, Y, W_out,
-                               stream, ttt::Prologue{});
+                               workspace, workspace_bytes, stream, ttt::Prologue{});
 }
 
 int ttt_linear_forward_ex(const void* Q, const void* K, const void* V, int qkv_dtype,
                           const float* W0, int w0_per_batch, const float* eta,
                           const float* eta_tok, const float* ln_q, const float* ln_k, float ln_eps,
                           int read_mode, int64_t B, int64_t H, int64_t T, int d, int b,
-                          void* Y, float* W_out, void* stream)
+                          void* Y, float* W_out, void* workspace, int64_t workspace_bytes,
+                          void* stream)
 {
     if ((ln_q || ln_k) && !(ln_eps > 0.0f && ln_eps < 1e30f))
         return TTT_ERR_INVALID_ARG;
@@ -341,22 +339,23 @@ int ttt_linear_forward_ex(const void* Q, const void* K, const void* V, int qkv_d
     if (pro.active() && B * H > 0 && T > 0 && (d != 64 || b != 16))
         return TTT_ERR_UNSUPPORTED;
     return linear_forward_impl(Q, K, V, qkv_dtype, W0, w0_per_batch, eta, B, H, T, d, b, Y, W_out,
-                               stream, pro);
+                               workspace, workspace_bytes, stream, pro);
+}
+
+int64_t ttt_linear_workspace_bytes(int64_t B, int64_t H, int64_t T, int d, int b, int qkv_dtype)
+{
+    if (const int st = linear_sizes_status(B, H, T, d, b, qkv_dtype)) return st;
+    LinearArgs a{nullptr, nullptr, nullptr, qkv_dtype, nullptr, 0, nullptr, B, H, T, d, b,
+                 nullptr, nullptr, nullptr};
+    return forward_workspace_bytes(B * H, d, plan_forward(a, INT64_MAX).nseg);
 }
 
 int ttt_linear_segments(int64_t B, int64_t H, int64_t T, int d, int b, int qkv_dtype)
 {
-    if (B < 0 || H < 0 || T < 0 || b < 1) return TTT_ERR_INVALID_ARG;
-    if (!valid_dtype(qkv_dtype) || !d_supported(d) || b > 64) return TTT_ERR_UNSUPPORTED;
-    int64_t units = B;
-    if (!mul_ok(units, H) || units > kMaxUnits) return TTT_ERR_UNSUPPORTED;
+    if (const int st = linear_sizes_status(B, H, T, d, b, qkv_dtype)) return st;
     LinearArgs a{nullptr, nullptr, nullptr, qkv_dtype, nullptr, 0, nullptr, B, H, T, d, b,
                  nullptr, nullptr, nullptr};
-    if (units == 0 || T == 0) return 1;
-    if (ttt::linear_mfma_supports(a)) return plan_segments(units, T, b, ttt::kLinearBf16Costs).nseg;
-    if (use_cols_f32(a)) return plan_segments(units, T, b, ttt::kLinearF32ColsCosts).nseg;
-    if (ttt::linear_mfma_f32_supports(a)) return plan_segments(units, T, b, ttt::kLinearF32Costs).nseg;
-    return 1;
+    return plan_forward(a, INT64_MAX).nseg;
 }
 
 }  // extern "C"
@@ -369,17 +368,14 @@ int linear_backward_impl(const void* Q, const void* K, const void* V, int qkv_dt
                          const void* dY, const float* dW_out,
                          void* dQ, void* dK, void* dV, float* dW0, float* deta,
                          const ttt::Prologue& pro, float* deta_tok, float* dln_q, float* dln_k,
-                         void* stream)
+                         void* ws, int64_t ws_bytes, void* stream)
 {
-    if (B < 0 || H < 0 || T < 0 || b < 1 || (w0_per_batch != 0 && w0_per_batch != 1))
-        return TTT_ERR_INVALID_ARG;
-    if (!valid_dtype(qkv_dtype) || d != 64 || b != 16)
-        return TTT_ERR_UNSUPPORTED;
-    int64_t units = B;
-    if (!mul_ok(units, H) || units > kMaxUnits) return TTT_ERR_UNSUPPORTED;
-    int64_t n_qkv = units;
-    if (!mul_ok(n_qkv, T) || !mul_ok(n_qkv, d) || !mul_ok(n_qkv, 4)) return TTT_ERR_UNSUPPORTED;
-    n_qkv = n_qkv / 4 * static_cast<int64_t>(elem_bytes(qkv_dtype));
+    if (w0_per_batch != 0 && w0_per_batch != 1) return TTT_ERR_INVALID_ARG;
+    if (ws_bytes < 0 || (ws_bytes > 0 && !ws)) return TTT_ERR_INVALID_ARG;
+    if (const int st = linear_sizes_status(B, H, T, d, b, qkv_dtype)) return st;
+    if (d != 64 || b != 16) return TTT_ERR_UNSUPPORTED;
+    const int64_t units = B * H;
+    const int64_t n_qkv = units * T * d * static_cast<int64_t>(elem_bytes(qkv_dtype));
     const int64_t n_state = static_cast<int64_t>(d) * d * 4;
     if (H > 0 && (!dW0 || !deta)) return TTT_ERR_INVALID_ARG;
     if (units > 0 && (!W0 || !eta || !dW_out)) return TTT_ERR_INVALID_ARG;
@@ -400,9 +396,10 @@ int linear_backward_impl(const void* Q, const void* K, const void* V, int qkv_dt
     const Range rdQ{dQ, nq}, rdK{dK, nq}, rdV{dV, nq};
     const Range rdW0{dW0, (w0_per_batch ? units : H) * n_state}, rdEta{deta, H * 4};
     const Range rdEt{deta_tok, deta_tok ? ntok : 0}, rdLq{dln_q, dln_q ? nln : 0}, rdLk{dln_k, dln_k ? nln : 0};
-    const Range outs[] = {rdQ, rdK, rdV, rdW0, rdEta, rdEt, rdLq, rdLk};
+    const Range rWs{ws, ws_bytes};
+    const Range outs[] = {rdQ, rdK, rdV, rdW0, rdEta, rdEt, rdLq, rdLk, rWs};
     const Range all[] = {rQ, rK, rV, rdY, rW0, rEta, rdWo, rEt, rLq, rLk,
-                         rdQ, rdK, rdV, rdW0, rdEta, rdEt, rdLq, rdLk};
+                         rdQ, rdK, rdV, rdW0, rdEta, rdEt, rdLq, rdLk, rWs};
     for (const Range& o : outs) {
         int hits = 0;   // an output overlaps itself once
         for (const Range& x : all)
@@ -417,14 +414,25 @@ int linear_backward_impl(const void* Q, const void* K, const void* V, int qkv_dt
     a.dln_q = dln_q;
     a.dln_k = dln_k;
     if (!ttt::linear_backward_supports(a)) return TTT_ERR_UNSUPPORTED;
+    auto fits = [&](const ttt::SegmentPlan& p) {
+        return static_cast<int64_t>(ttt::linear_backward_workspace_bytes(a, p)) <= ws_bytes;
+    };
     ttt::SegmentPlan p;
     if (units > 0)
         p = plan_backward(units, T, b, qkv_dtype == TTT_BF16 ? ttt::kLinearBwdBf16Costs
-                                                              : ttt::kLinearBwdF32Costs);
-    void* ws = nullptr;
-    if (workspace_get(&ws, ttt::linear_backward_workspace_bytes(a, p), a.stream) != hipSuccess)
-        return TTT_ERR_HIP;
+                                                              : ttt::kLinearBwdF32Costs, fits);
+    if (!fits(p)) return TTT_ERR_INVALID_ARG;   // not even one segment's states fit
     return hip_status(ttt::launch_linear_backward(a, p, ws));
+}
+
+// Backward arguments for a workspace query: shared W0 and the prologue's
+// buffers, the most any variant of the call needs.
+ttt::LinearBwdArgs bwd_query_args(int64_t B, int64_t H, int64_t T, int d, int b, int qkv_dtype)
+{
+    ttt::LinearBwdArgs a{nullptr, nullptr, nullptr, qkv_dtype, nullptr, 0, nullptr, B, H, T, d, b,
+                         nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
+    a.pro.read_start = 1;
+    return a;
 }
 
 }  // namespace
@@ -435,11 +443,12 @@ int ttt_linear_backward(const void* Q, const void* K, const void* V, int qkv_dty
                         const float* W0, int w0_per_batch, const float* eta,
                         int64_t B, int64_t H, int64_t T, int d, int b,
                         const void* dY, const float* dW_out,
-                        void* dQ, void* dK, void* dV, float* dW0, float* deta, void* stream)
+                        void* dQ, void* dK, void* dV, float* dW0, float* deta,
+                        void* workspace, int64_t workspace_bytes, void* stream)
 {
     return linear_backward_impl(Q, K, V, qkv_dtype, W0, w0_per_batch, eta, B, H, T, d, b, dY,
                                 dW_out, dQ, dK, dV, dW0, deta, ttt::Prologue{}, nullptr, nullptr,
-                                nullptr, stream);
+                                nullptr, workspace, workspace_bytes, stream);
 }
 
 int ttt_linear_backward_ex(const void* Q, const void* K, const void* V, int qkv_dtype,
@@ -448,7 +457,7 @@ int ttt_linear_backward_ex(const void* Q, const void* K, const void* V, int qkv_
                            float ln_eps, int read_mode, int64_t B, int64_t H, int64_t T, int d,
                            int b, const void* dY, const float* dW_out, void* dQ, void* dK,
                            void* dV, float* dW0, float* deta, float* deta_tok, float* dln_q,
-                           float* dln_k, void* stream)
+                           float* dln_k, void* workspace, int64_t workspace_bytes, void* stream)
 {
     if ((ln_q || ln_k) && !(ln_eps > 0.0f && ln_eps < 1e30f))
         return TTT_ERR_INVALID_ARG;
@@ -461,18 +470,32 @@ int ttt_linear_backward_ex(const void* Q, const void* K, const void* V, int qkv_
     pro.ln_eps = ln_eps;
     pro.read_start = read_mode;
     return linear_backward_impl(Q, K, V, qkv_dtype, W0, w0_per_batch, eta, B, H, T, d, b, dY,
-                                dW_out, dQ, dK, dV, dW0, deta, pro, deta_tok, dln_q, dln_k, stream);
+                                dW_out, dQ, dK, dV, dW0, deta, pro, deta_tok, dln_q, dln_k,
+                                workspace, workspace_bytes, stream);
 }
 
 int ttt_linear_backward_segments(int64_t B, int64_t H, int64_t T, int d, int b, int qkv_dtype)
 {
-    if (B < 0 || H < 0 || T < 0 || b < 1) return TTT_ERR_INVALID_ARG;
-    if (!valid_dtype(qkv_dtype) || d != 64 || b != 16) return TTT_ERR_UNSUPPORTED;
-    int64_t units = B;
-    if (!mul_ok(units, H) || units > kMaxUnits) return TTT_ERR_UNSUPPORTED;
-    if (units == 0 || T == 0) return 1;
-    return plan_backward(units, T, b, qkv_dtype == TTT_BF16 ? ttt::kLinearBwdBf16Costs
-                                                            : ttt::kLinearBwdF32Costs).nseg;
+    if (const int st = linear_sizes_status(B, H, T, d, b, qkv_dtype)) return st;
+    if (d != 64 || b != 16) return TTT_ERR_UNSUPPORTED;
+    if (B * H == 0 || T == 0) return 1;
+    return plan_backward(B * H, T, b, qkv_dtype == TTT_BF16 ? ttt::kLinearBwdBf16Costs
+                                                            : ttt::kLinearBwdF32Costs,
+                         [](const ttt::SegmentPlan&) { return true; }).nseg;
+}
+
+int64_t ttt_linear_backward_workspace_bytes(int64_t B, int64_t H, int64_t T, int d, int b,
+                                            int qkv_dtype)
+{
+    if (const int st = linear_sizes_status(B, H, T, d, b, qkv_dtype)) return st;
+    if (d != 64 || b != 16) return TTT_ERR_UNSUPPORTED;
+    const ttt::LinearBwdArgs a = bwd_query_args(B, H, T, d, b, qkv_dtype);
+    ttt::SegmentPlan p;
+    if (B * H > 0 && T > 0)
+        p = plan_backward(B * H, T, b, qkv_dtype == TTT_BF16 ? ttt::kLinearBwdBf16Costs
+                                                             : ttt::kLinearBwdF32Costs,
+                          [](const ttt::SegmentPlan&) { return true; });
+    return static_cast<int64_t>(ttt::linear_backward_workspace_bytes(a, p));
 }
 
 int ttt_mlp_forward(const void* Q, const void* K, const void* V, int qkv_dtype,
@@ -486,7 +509,7 @@ int ttt_mlp_forward(const void* Q, const void* K, const void* V, int qkv_dtype,
         m % 16 != 0 || m > 512)
         return TTT_ERR_UNSUPPORTED;
     int64_t units = B;
-    if (!mul_ok(units, H) || units > kMaxUnits) return TTT_ERR_UNSUPPORTED;
+    if (!mul_ok(units, H) || units > kMaxUnits || T > kMaxTokens) return TTT_ERR_UNSUPPORTED;
     if (units == 0) return TTT_OK;
     int64_t n_qkv = units;
     if (!mul_ok(n_qkv, T) || !mul_ok(n_qkv, d) || !mul_ok(n_qkv, 4)) return TTT_ERR_UNSUPPORTED;

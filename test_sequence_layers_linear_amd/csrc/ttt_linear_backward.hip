@@ -838,7 +838,8 @@ BwdWorkspace carve(const LinearBwdArgs& a, const SegmentPlan& p, void* base)
         w.gmaps = take(units * (S - 1) * 2 * st);
         w.gend = take(units * S * st);
     }
-    w.states = take(units * S * seg_chunks * st);
+    // chunk-start states: fp32 W for fp32 inputs, bf16 W^T (half the bytes) for bf16
+    w.states = take(units * S * seg_chunks * st / (a.dtype != 0 ? 2 : 1));
     w.dw_chain = a.w0_per_batch ? a.dW0 : take(units * st);
     w.deta_chain = take(units * S);
     w.dln_chain = a.pro.active() ? take(units * S * kDlnRows * kD) : nullptr;
@@ -891,7 +892,10 @@ hipError_t set_lds()
 
 bool linear_backward_supports(const LinearBwdArgs& a)
 {
-    return a.d == kD && a.b == kB;
+    // per-chain byte offsets are 32-bit (fp32 rows of 256 bytes; the forward
+    // maps and start-state kernels it launches have the same bound)
+    const int64_t max_tokens = (int64_t{1} << 31) / (kD * 4) - kB * 64;
+    return a.d == kD && a.b == kB && a.T <= max_tokens;
 }
 
 size_t linear_backward_workspace_bytes(const LinearBwdArgs& a, const SegmentPlan& p)

@@ -24,6 +24,9 @@ def main():
     ap.add_argument("--decode", action="store_true", help="also run the workload's decode steps")
     ap.add_argument("--backward", action="store_true",
                     help="run ttt_linear_backward (seeded cotangents) instead of the forward")
+    ap.add_argument("--flush", action="store_true",
+                    help="write a 512 MB buffer before every call (the 256 MB last-level cache "
+                         "flushed, as bench.py's roofline timing does)")
     ap.add_argument("--prologue", action="store_true",
                     help="with the input prologue (LayerNorm of q and k, per-token step sizes): "
                          "ttt_linear_forward_ex / ttt_linear_backward_ex")
@@ -47,19 +50,28 @@ def main():
     if args.prologue:
         pro = {k: v.cuda() for k, v in make_prologue(w, 11).items()}
         pkw = {k: pro[k] for k in ("eta_tok", "ln_q", "ln_k")}
+    ws = None
+    if w.kind == "linear":
+        nbytes = (ttt.ttt_linear_backward_workspace_bytes if args.backward
+                  else ttt.ttt_linear_workspace_bytes)(w.B, w.H, w.T, w.d, w.b, w.torch_dtype)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    junk = torch.empty(512 * 1024 * 1024 // 4, device="cuda") if args.flush else None
     torch.cuda.synchronize()
     for _ in range(args.reps):
+        if junk is not None:
+            junk.fill_(1.0)
         if args.backward and args.prologue:
             ttt.ttt_linear_backward_ex(g["Q"], g["K"], g["V"], g["W0"], pro["eta"], w.b, cot["dY"],
-                                       cot["dW_out"], **pkw)
+                                       cot["dW_out"], workspace=ws, **pkw)
         elif args.backward:
             ttt.ttt_linear_backward(g["Q"], g["K"], g["V"], g["W0"], g["eta"], w.b, cot["dY"],
-                                    cot["dW_out"])
+                                    cot["dW_out"], workspace=ws)
         elif args.prologue:
             ttt.ttt_linear_forward_ex(g["Q"], g["K"], g["V"], g["W0"], pro["eta"], w.b, Y=Y,
-                                      W_out=W, **pkw)
+                                      W_out=W, workspace=ws, **pkw)
         elif w.kind == "linear":
-            ttt.ttt_linear_forward(g["Q"], g["K"], g["V"], g["W0"], g["eta"], w.b, Y=Y, W_out=W)
+            ttt.ttt_linear_forward(g["Q"], g["K"], g["V"], g["W0"], g["eta"], w.b, Y=Y, W_out=W,
+                                   workspace=ws)
             if args.decode:
                 y = torch.empty_like(g["dq"][0])
                 for s in range(w.decode_steps):

@@ -1,4 +1,6 @@
 """Helpers shared by the GPU parity tests (comparison only, no method arithmetic)."""
+import functools
+
 import numpy as np
 import torch
 
@@ -58,6 +60,24 @@ def mlp_gpu(inp_gpu: dict, b: int):
     return out
 
 
+@functools.lru_cache(maxsize=2)
+def cached_inputs(cfg: int, seed: int, w0_per_batch: bool = False) -> dict:
+    """make_inputs of a full-size workload, kept for the tests that reuse it
+    (the 32768-token workload takes seconds to draw).  Callers must not
+    modify the returned tensors."""
+    return make_inputs(WORKLOADS[cfg], seed, w0_per_batch=w0_per_batch)
+
+
+def per_chain_rel_l2(x, ref):
+    """Relative L2 of each (batch, head) chain of [B,H,...] tensors (diagnostic)."""
+    x = x.detach().to("cpu", torch.float64).numpy() if isinstance(x, torch.Tensor) else x
+    x, ref = np.asarray(x, dtype=np.float64), np.asarray(ref, dtype=np.float64)
+    B, H = ref.shape[:2]
+    d = (x - ref).reshape(B * H, -1)
+    r = ref.reshape(B * H, -1)
+    return np.linalg.norm(d, axis=1) / np.maximum(np.linalg.norm(r, axis=1), 1e-300)
+
+
 def sample_chains(B: int, H: int, n: int, seed: int):
     rng = np.random.default_rng(seed)
     idx = rng.choice(B * H, size=min(n, B * H), replace=False)
@@ -70,4 +90,4 @@ def announce(*parts):
 
 __all__ = ["TOL", "rel_l2", "to_gpu", "select_chains", "linear_oracle", "mlp_oracle",
            "linear_gpu", "mlp_gpu", "sample_chains", "announce", "WORKLOADS", "Workload",
-           "default_seed", "make_inputs"]
+           "default_seed", "make_inputs", "cached_inputs", "per_chain_rel_l2"]

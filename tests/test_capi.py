@@ -6,6 +6,7 @@ is made (so these run on a machine with no GPU).  Fake, never-dereferenced
 addresses stand in for device buffers.
 """
 import ctypes
+import glob
 import os
 import re
 
@@ -14,7 +15,7 @@ import pytest
 import test_sequence_layers_linear_amd as ttt
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "ttt.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 OK, INVALID, UNSUPPORTED = ttt.TTT_OK, ttt.TTT_ERR_INVALID_ARG, ttt.TTT_ERR_UNSUPPORTED
 
@@ -24,7 +25,7 @@ W1A, W2A, W1O, W2O = (0x90_0000_0000 + 0x10_0000_0000 * i for i in range(4))
 
 
 def declared_functions():
-    text = open(HEADER).read()
+    text = "\n".join(open(h).read() for h in HEADERS)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(ttt_\w+)\s*\(", text, flags=re.M)))
 
@@ -39,7 +40,8 @@ def test_exports_every_declared_function(lib):
     assert set(names) >= {"ttt_linear_forward", "ttt_mlp_forward", "ttt_linear_decode_step",
                           "ttt_linear_backward", "ttt_linear_forward_ex", "ttt_linear_segments",
                           "ttt_linear_backward_segments", "ttt_linear_decode_step_ex",
-                          "ttt_status_string",
+                          "ttt_linear_workspace_bytes", "ttt_linear_backward_workspace_bytes",
+                          "ttt_status_string", "ttt_roof_copy", "ttt_roof_mfma",
                           "ttt_abi_version"}
     for n in names:
         assert hasattr(lib, n), f"{n} declared in ttt.h but not exported"
@@ -48,12 +50,16 @@ def test_exports_every_declared_function(lib):
 def test_status_strings_and_version(lib):
     for s in (OK, INVALID, UNSUPPORTED, ttt.TTT_ERR_HIP, 12345):
         assert isinstance(ttt.status_string(s), str) and ttt.status_string(s)
-    assert lib.ttt_abi_version() >> 16 == 1
+    assert lib.ttt_abi_version() >> 16 == 2
+
+
+# a fake workspace address apart from every other one
+WSA = 0x300_0000_0000
 
 
 def lin(lib, Q=QA, K=KA, V=VA, dt=1, W0=W0A, pb=0, eta=ETA, B=2, H=3, T=64, d=64, b=16,
-        Y=YA, Wo=WOA):
-    return lib.ttt_linear_forward(Q, K, V, dt, W0, pb, eta, B, H, T, d, b, Y, Wo, None)
+        Y=YA, Wo=WOA, ws=None, wsb=0):
+    return lib.ttt_linear_forward(Q, K, V, dt, W0, pb, eta, B, H, T, d, b, Y, Wo, ws, wsb, None)
 
 
 @pytest.mark.parametrize("kw,expect", [
@@ -68,6 +74,12 @@ def lin(lib, Q=QA, K=KA, V=VA, dt=1, W0=W0A, pb=0, eta=ETA, B=2, H=3, T=64, d=64
     (dict(Y=WOA), INVALID), (dict(Wo=QA), INVALID), (dict(Wo=W0A), INVALID),
     (dict(Wo=W0A + 4, pb=1), INVALID),
     (dict(B=0), OK), (dict(H=0), OK),
+    # the caller's workspace
+    (dict(wsb=-1), INVALID), (dict(ws=None, wsb=4096), INVALID),
+    (dict(ws=QA + 128, wsb=4096), INVALID), (dict(ws=WOA - 64, wsb=4096), INVALID),
+    (dict(ws=YA, wsb=1), INVALID),
+    # sequence length beyond the 32-bit token index
+    (dict(T=2**31), UNSUPPORTED),
 ])
 def test_linear_validation(lib, kw, expect):
     assert lin(lib, **kw) == expect
@@ -79,7 +91,7 @@ TOKA, LNQA, LNKA = (0xC0_0000_0000 + 0x10_0000_0000 * i for i in range(3))
 def linx(lib, tok=TOKA, lnq=LNQA, lnk=LNKA, eps=1e-5, rm=0, d=64, b=16, Y=YA, Wo=WOA, T=64, dt=1,
          B=2):
     return lib.ttt_linear_forward_ex(QA, KA, VA, dt, W0A, 0, ETA, tok, lnq, lnk, eps, rm, B, 3, T,
-                                     d, b, Y, Wo, None)
+                                     d, b, Y, Wo, None, 0, None)
 
 
 @pytest.mark.parametrize("kw,expect", [
@@ -101,7 +113,7 @@ def test_linear_forward_ex_validation(lib, kw, expect):
 def test_linear_no_inputs_needed_when_empty(lib):
     # B*H == 0: a no-op, even with null pointers
     assert lib.ttt_linear_forward(None, None, None, 1, None, 0, None, 0, 4, 8, 64, 16,
-                                  None, None, None) == OK
+                                  None, None, None, 0, None) == OK
 
 
 def mlp(lib, dt=1, W1=W1A, W2=W2A, pb=0, B=2, H=3, T=64, d=64, m=256, b=16, Y=YA,
@@ -116,7 +128,7 @@ def mlp(lib, dt=1, W1=W1A, W2=W2A, pb=0, B=2, H=3, T=64, d=64, m=256, b=16, Y=YA
     (dict(d=128), UNSUPPORTED), (dict(m=100), UNSUPPORTED), (dict(m=1024), UNSUPPORTED),
     (dict(dt=3), UNSUPPORTED), (dict(b=80), UNSUPPORTED),
     (dict(Y=W1A), INVALID), (dict(W1o=W2O), INVALID), (dict(W1o=W1A), INVALID),
-    (dict(B=0), OK),
+    (dict(B=0), OK), (dict(T=2**31), UNSUPPORTED),
 ])
 def test_mlp_validation(lib, kw, expect):
     assert mlp(lib, **kw) == expect
@@ -140,9 +152,9 @@ DYA, DWOA, DQA, DKA, DVA, DW0A, DETA = (0xA0_0000_0000 + 0x10_0000_0000 * i for 
 
 
 def bwd(lib, Q=QA, dt=1, W0=W0A, pb=0, eta=ETA, B=2, H=3, T=64, d=64, b=16, dY=DYA, dWo=DWOA,
-        dQ=DQA, dK=DKA, dV=DVA, dW0=DW0A, deta=DETA):
+        dQ=DQA, dK=DKA, dV=DVA, dW0=DW0A, deta=DETA, ws=WSA, wsb=1 << 30):
     return lib.ttt_linear_backward(Q, KA, VA, dt, W0, pb, eta, B, H, T, d, b, dY, dWo, dQ, dK, dV,
-                                   dW0, deta, None)
+                                   dW0, deta, ws, wsb, None)
 
 
 @pytest.mark.parametrize("kw,expect", [
@@ -155,6 +167,11 @@ def bwd(lib, Q=QA, dt=1, W0=W0A, pb=0, eta=ETA, B=2, H=3, T=64, d=64, b=16, dY=D
     (dict(dW0=DWOA), INVALID), (dict(deta=ETA), INVALID), (dict(dW0=W0A), INVALID),
     (dict(deta=DW0A + 16), INVALID),
     (dict(H=0), OK),
+    # the caller's workspace: required (the chunk-start states), never overlapping
+    (dict(wsb=-8), INVALID), (dict(ws=None), INVALID), (dict(ws=None, wsb=0), INVALID),
+    (dict(wsb=1000), INVALID), (dict(ws=DQA - 4096), INVALID), (dict(ws=QA), INVALID),
+    # the kernels' 32-bit byte offsets bound a chain's length
+    (dict(T=2**24), UNSUPPORTED), (dict(T=2**31), UNSUPPORTED),
 ])
 def test_backward_validation(lib, kw, expect):
     assert bwd(lib, **kw) == expect
@@ -168,7 +185,7 @@ def bwdx(lib, tok=PTOKA, lnq=PLNQA, lnk=PLNKA, eps=1e-5, rm=0, dtok=DTOKA, dlnq=
          d=64, b=16, H=3, dQ=DQA, deta=DETA):
     return lib.ttt_linear_backward_ex(QA, KA, VA, 1, W0A, 0, ETA, tok, lnq, lnk, eps, rm, 2, H, 64,
                                       d, b, DYA, DWOA, dQ, DKA, DVA, DW0A, deta, dtok, dlnq, dlnk,
-                                      None)
+                                      WSA, 1 << 30, None)
 
 
 @pytest.mark.parametrize("kw,expect", [
@@ -189,7 +206,7 @@ def test_backward_ex_fixture_addresses_are_disjoint():
     # the valid default call of bwdx must not overlap itself, so that each
     # INVALID case above fails for its own reason
     spans = [(a, 0x10_0000_0000) for a in (QA, KA, VA, W0A, ETA, DYA, DWOA, DQA, DKA, DVA, DW0A,
-                                           DETA, PTOKA, PLNQA, PLNKA, DTOKA, DLNQA, DLNKA)]
+                                           DETA, PTOKA, PLNQA, PLNKA, DTOKA, DLNQA, DLNKA, WSA)]
     spans.sort()
     for (a, n), (b, _) in zip(spans, spans[1:]):
         assert a + n <= b
@@ -253,3 +270,51 @@ def test_backward_segment_query_validation_and_override(lib, monkeypatch):
     assert lib.ttt_linear_backward_segments(1, 4, 40, 64, 16, 1) == 3
     monkeypatch.setenv("TTT_LINEAR_BWD_SEGMENTS", "99")
     assert lib.ttt_linear_backward_segments(1, 4, 2048, 64, 16, 1) == 26
+
+
+def test_workspace_queries(lib, monkeypatch):
+    """Workspace sizes: the forward needs B*H*(3S - 2) d x d fp32 matrices for S
+    segments (none unsegmented); the backward's figure covers the chunk-start
+    states (bf16 W^T for bf16 inputs, fp32 W otherwise), a per-chain dW0 and
+    the small per-segment sums, each piece padded to 256 bytes."""
+    monkeypatch.delenv("TTT_LINEAR_SEGMENTS", raising=False)
+    monkeypatch.delenv("TTT_LINEAR_BWD_SEGMENTS", raising=False)
+    assert lib.ttt_linear_workspace_bytes(-1, 3, 64, 64, 16, 1) == INVALID
+    assert lib.ttt_linear_workspace_bytes(1, 3, 64, 48, 16, 1) == UNSUPPORTED
+    assert lib.ttt_linear_workspace_bytes(1, 3, 2**31, 64, 16, 1) == UNSUPPORTED
+    assert lib.ttt_linear_workspace_bytes(0, 3, 64, 64, 16, 1) == 0
+    assert lib.ttt_linear_workspace_bytes(1, 3, 64, 32, 16, 1) == 0        # generic kernel
+    monkeypatch.setenv("TTT_LINEAR_SEGMENTS", "4")
+    assert lib.ttt_linear_workspace_bytes(1, 4, 2048, 64, 16, 0) == 4 * (3 * 4 - 2) * 64 * 64 * 4
+    assert lib.ttt_linear_workspace_bytes(2, 3, 2048, 64, 16, 1) == 6 * (3 * 4 - 2) * 64 * 64 * 4
+    assert lib.ttt_linear_workspace_bytes(1, 4, 16, 64, 16, 0) == 0        # one mini-batch
+
+    assert lib.ttt_linear_backward_workspace_bytes(1, 3, 64, 32, 16, 1) == UNSUPPORTED
+    monkeypatch.setenv("TTT_LINEAR_BWD_SEGMENTS", "1")
+    st = 64 * 64 * 4
+    units, chunks = 2, 4
+    pad = lambda n: (n + 255) // 256 * 256
+    small = pad(units * 4) + pad(units * 4 * 64 * 4)     # deta per segment, LayerNorm sums
+    for dt, state in ((1, st // 2), (0, st)):
+        want = pad(units * chunks * state) + pad(units * st) + small
+        assert lib.ttt_linear_backward_workspace_bytes(1, 2, 64, 64, 16, dt) == want
+    # the plain call with shared W0 needs the states, dW0 per chain and deta
+    # (no LayerNorm sums); one byte short of that is rejected before any launch
+    need = pad(units * chunks * st // 2) + pad(units * st) + pad(units * 4)
+    assert bwd(lib, B=1, H=2, ws=WSA, wsb=need - 1) == INVALID
+
+
+def test_roof_probe_validation(lib):
+    """The roof kernels reject bad arguments before any launch."""
+    lib.ttt_roof_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    lib.ttt_roof_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
+                                  ctypes.c_void_p, ctypes.c_void_p]
+    assert lib.ttt_roof_copy(None, YA, 1024, None) == INVALID
+    assert lib.ttt_roof_copy(QA, YA, 1000, None) == INVALID          # not a multiple of 16
+    assert lib.ttt_roof_copy(QA + 4, YA, 1024, None) == INVALID      # unaligned
+    assert lib.ttt_roof_copy(QA, QA + 512, 1024, None) == INVALID    # overlapping
+    assert lib.ttt_roof_copy(QA, YA, 0, None) == OK
+    assert lib.ttt_roof_mfma(None, 1, 1024, 10, None, None) == INVALID
+    assert lib.ttt_roof_mfma(YA, 2, 1024, 10, None, None) == INVALID
+    assert lib.ttt_roof_mfma(YA, 1, 1022, 10, None, None) == INVALID
+    assert lib.ttt_roof_mfma(YA, 0, 1024, 0, None, None) == INVALID

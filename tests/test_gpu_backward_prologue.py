@@ -6,11 +6,9 @@ Every gradient -- dQ, dK (of the raw rows), dV, dW0, deta, deta_tok, dln_q,
 dln_k -- is compared in relative L2 on the same seeded inputs and cotangents:
 within 1e-4 for fp32 Q/K/V and 2e-2 for bf16 Q/K/V (normalised rows and
 gradients rounded to bf16).  Cases: each part of the prologue alone and
-together, the chunk-start read, ragged tails, forced segment counts, and two
-benchmark workloads at full size (the long one on sampled chains, without
-the batch-summed LayerNorm gradients).
+together, the chunk-start read, ragged tails, forced segment counts, and three
+benchmark workloads at full size (every chain).
 """
-import numpy as np
 import pytest
 import torch
 
@@ -123,22 +121,12 @@ def test_backward_prologue_config_full(cfg):
     _compare(_gpu(inp, kw, cot, w.b, False), _oracle(inp, kw, cot, w.b, False), TOL[w.dtype])
 
 
-def test_backward_prologue_config4_sampled_chains():
+def test_backward_prologue_config4_full():
+    """The 32768-token workload's backward through the whole prologue, W0
+    given per batch, every chain and every gradient (the LayerNorm and head-eta
+    gradients summed over the batch on both sides), relative L2 over the whole
+    tensors."""
     w = WORKLOADS[4]
-    announce("backward prologue config 4 sampled chains", w.name)
+    announce("backward prologue config 4, all chains", w.name)
     inp, kw, cot = _case(w, default_seed(4) + 700, PARTS["all"], per_batch=True)
-    got = _gpu(inp, kw, cot, w.b, False)
-    rng = np.random.default_rng(46)
-    for i in sorted(rng.choice(w.B * w.H, size=2, replace=False)):
-        bb, h = int(i) // w.H, int(i) % w.H
-        sub = {k: inp[k][bb:bb + 1, h:h + 1] for k in ("Q", "K", "V", "W0")}
-        sub["eta"] = inp["eta"][h:h + 1]
-        skw = {"eta_tok": kw["eta_tok"][bb:bb + 1, h:h + 1], "ln_q": kw["ln_q"][h:h + 1],
-               "ln_k": kw["ln_k"][h:h + 1]}
-        scot = {k: cot[k][bb:bb + 1, h:h + 1] for k in ("dY", "dW_out")}
-        ref = _oracle(sub, skw, scot, w.b, False)
-        part = {n: got[n][bb:bb + 1, h:h + 1] for n in ("dQ", "dK", "dV", "dW0", "deta_tok")}
-        print(f"  chain ({bb}, {h})", flush=True)
-        _compare(part, ref, TOL["bf16"], names=sorted(part))
-    for x in got.values():
-        assert torch.isfinite(x.float()).all()
+    _compare(_gpu(inp, kw, cot, w.b, False), _oracle(inp, kw, cot, w.b, False), TOL["bf16"])

@@ -5,8 +5,8 @@ import torch
 
 import oracle
 import test_sequence_layers_linear_amd as ttt
-from parity_util import (WORKLOADS, TOL, announce, default_seed, linear_gpu, make_inputs, rel_l2,
-                         sample_chains, select_chains, to_gpu)
+from parity_util import (WORKLOADS, TOL, announce, cached_inputs, default_seed, linear_gpu,
+                         make_inputs, per_chain_rel_l2, rel_l2, to_gpu)
 
 pytestmark = pytest.mark.gpu
 
@@ -35,10 +35,11 @@ def test_decode_steps_match_online_gd(d, dtype):
 
 def test_config4_prefill_then_256_decode_steps():
     """The long-context workload's tail: forward over T = 32768 tokens, then
-    256 single-token steps from the final W, on sampled chains."""
+    256 single-token steps from the final W, every chain, relative L2 over the
+    whole tensor of the 256 outputs and of the final state."""
     w = WORKLOADS[4]
-    announce("decode after config 4 prefill", w.name)
-    inp = make_inputs(w, default_seed(4))
+    announce("decode after config 4 prefill, all chains", w.name)
+    inp = cached_inputs(4, default_seed(4))
     g = to_gpu(inp)
     _, W = linear_gpu(g, w.b)
     ys = []
@@ -46,21 +47,15 @@ def test_config4_prefill_then_256_decode_steps():
         ys.append(ttt.ttt_linear_decode_step(g["dq"][s], g["dk"][s], g["dv"][s], W, g["eta"]))
     torch.cuda.synchronize()
     y = torch.stack(ys)                           # [steps, B, H, d]
-    chains = sample_chains(w.B, w.H, 2, seed=45)
-    sub = select_chains(inp, chains)
-    _, Wr = oracle.linear_forward(sub["Q"], sub["K"], sub["V"], sub["W0"], sub["eta"], w.b)
-    dq = torch.stack([inp["dq"][:, b, h] for b, h in chains], dim=1)[:, None]
-    dk = torch.stack([inp["dk"][:, b, h] for b, h in chains], dim=1)[:, None]
-    dv = torch.stack([inp["dv"][:, b, h] for b, h in chains], dim=1)[:, None]
+    _, Wr = oracle.linear_forward(inp["Q"], inp["K"], inp["V"], inp["W0"], inp["eta"], w.b)
     yr = []
     for s in range(w.decode_steps):
-        ys_, Wr = oracle.linear_decode(dq[s], dk[s], dv[s], Wr, sub["eta"])
+        ys_, Wr = oracle.linear_decode(inp["dq"][s], inp["dk"][s], inp["dv"][s], Wr, inp["eta"])
         yr.append(ys_)
     yr = np.stack(yr)
-    yg = torch.stack([y[:, b, h] for b, h in chains], dim=1)[:, None]
-    Wg = torch.stack([W[b, h] for b, h in chains])[None]
-    ey, ew = rel_l2(yg, yr), rel_l2(Wg, Wr)
-    print(f"  chains {chains} rel-L2 y {ey:.3e}  W {ew:.3e}", flush=True)
+    ey, ew = rel_l2(y, yr), rel_l2(W, Wr)
+    print(f"  rel-L2 y {ey:.3e}  W {ew:.3e}  (worst chain W {per_chain_rel_l2(W, Wr).max():.3e})",
+          flush=True)
     assert ey <= TOL["bf16"] and ew <= TOL["bf16"]
 
 

@@ -3,8 +3,8 @@
 Element-by-element relative-L2 comparison on the same seeded inputs: within
 1e-4 for fp32 Q/K/V and 2e-2 for bf16 Q/K/V (fp32 state), for Y and for the
 final W.  Small cases span several chunks and a ragged tail; the benchmark
-workloads run at full size (the 32768-token one on sampled chains, which the
-oracle computes one by one).
+workloads run at full size, every chain, with the relative L2 taken over the
+whole tensor.
 """
 import json
 import os
@@ -15,8 +15,8 @@ import pytest
 import torch
 
 import test_sequence_layers_linear_amd as ttt
-from parity_util import (WORKLOADS, TOL, announce, default_seed, linear_gpu, linear_oracle,
-                         make_inputs, rel_l2, sample_chains, select_chains, to_gpu)
+from parity_util import (WORKLOADS, TOL, announce, cached_inputs, default_seed, linear_gpu,
+                         linear_oracle, make_inputs, per_chain_rel_l2, rel_l2, to_gpu)
 
 pytestmark = pytest.mark.gpu
 
@@ -39,23 +39,21 @@ def test_config_full(cfg):
     _check(inp, w.b, w.dtype)
 
 
-def test_config4_sampled_chains_full_length():
+def test_config4_full():
+    """The 32768-token workload in the launch configuration the benchmark
+    times (the planned segments: maps, composition, segment scans), all 48
+    chains against the oracle, relative L2 over the whole Y and W tensors."""
     w = WORKLOADS[4]
-    announce("linear config 4 sampled chains", w.name)
-    inp = make_inputs(w, default_seed(4))
+    announce("linear config 4, all chains", w.name, "segments",
+             ttt.ttt_linear_segments(w.B, w.H, w.T, w.d, w.b, torch.bfloat16))
+    inp = cached_inputs(4, default_seed(4))
     Y, W = linear_gpu(to_gpu(inp), w.b)
-    chains = sample_chains(w.B, w.H, 3, seed=44)
-    sub = select_chains(inp, chains)
-    Yr, Wr = linear_oracle(sub, w.b)
-    Ys = torch.stack([Y[b, h] for b, h in chains])[None]
-    Ws = torch.stack([W[b, h] for b, h in chains])[None]
-    ey, ew = rel_l2(Ys, Yr), rel_l2(Ws, Wr)
-    print(f"  chains {chains} rel-L2 Y {ey:.3e}  W {ew:.3e}", flush=True)
+    Yr, Wr = linear_oracle(inp, w.b)
+    ey, ew = rel_l2(Y, Yr), rel_l2(W, Wr)
+    cy, cw = per_chain_rel_l2(Y, Yr), per_chain_rel_l2(W, Wr)
+    print(f"  rel-L2 Y {ey:.3e}  W {ew:.3e}  (worst chain: Y {cy.max():.3e}, W {cw.max():.3e})",
+          flush=True)
     assert ey <= TOL["bf16"] and ew <= TOL["bf16"]
-    # properties that hold for every chain at any size: finite, and the
-    # state stays bounded (eta * |K^T K| < 2 keeps each step contractive)
-    assert torch.isfinite(Y.float()).all() and torch.isfinite(W).all()
-    assert W.abs().max().item() < 10.0
 
 
 # ---------------------------------------------------------------------------
@@ -306,3 +304,77 @@ def test_f32_planned_segments(B, H, T):
     announce("fp32 planned segments", B, H, T, "segments", n)
     assert n > 1
     _check(make_inputs(w, 600 + T), 16, "fp32")
+
+
+# ---------------------------------------------------------------------------
+# the caller's workspace: the segment maps live there; a smaller one gives
+# fewer segments (none without a workspace); the call can be captured
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("cfg", [2, 3])
+def test_workspace_limits_segments(cfg, monkeypatch):
+    monkeypatch.setenv("TTT_LINEAR_SEGMENTS", "8")
+    w = WORKLOADS[cfg].with_(B=2, H=3, T=1000, w0=("normal", 0.3), eta=("uniform", 0.01, 0.1))
+    announce("workspace limits the segment count", cfg)
+    inp = make_inputs(w, 800 + cfg)
+    g = to_gpu(inp)
+    full = ttt.ttt_linear_workspace_bytes(w.B, w.H, w.T, 64, 16, w.torch_dtype)
+    assert full == w.B * w.H * (3 * 8 - 2) * 64 * 64 * 4
+    Yr, Wr = linear_oracle(inp, 16)
+
+    def run(nbytes):
+        ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        Y, W = ttt.ttt_linear_forward(g["Q"], g["K"], g["V"], g["W0"], g["eta"], 16, workspace=ws)
+        torch.cuda.synchronize()
+        return Y, W
+
+    def forced(S):
+        monkeypatch.setenv("TTT_LINEAR_SEGMENTS", str(S))
+        out = run(ttt.ttt_linear_workspace_bytes(w.B, w.H, w.T, 64, 16, w.torch_dtype))
+        monkeypatch.setenv("TTT_LINEAR_SEGMENTS", "8")
+        return out
+
+    for nbytes, S in ((0, 1), (full - 1, 7), (w.B * w.H * (3 * 4 - 2) * 64 * 64 * 4, 4), (full, 8)):
+        Y, W = run(nbytes)
+        Ys, Ws = forced(S)
+        assert torch.equal(Y, Ys) and torch.equal(W, Ws), (nbytes, S)
+        ey, ew = rel_l2(Y, Yr), rel_l2(W, Wr)
+        print(f"  {nbytes} bytes -> {S} segments: rel-L2 Y {ey:.2e}  W {ew:.2e}", flush=True)
+        assert ey <= TOL[w.dtype] and ew <= TOL[w.dtype]
+
+
+def test_graph_capture_config4_shape():
+    """A segmented forward of the 32768-token workload's shape captured in a
+    HIP graph: every replay equals the eager call bit for bit, with other
+    eager work on the stream between the replays."""
+    w = WORKLOADS[4]
+    assert ttt.ttt_linear_segments(w.B, w.H, w.T, 64, 16, torch.bfloat16) > 1
+    announce("graph capture, config 4 shape")
+    g = to_gpu(cached_inputs(4, default_seed(4)))
+    Y_e, W_e = linear_gpu(g, 16)
+    Y = torch.empty_like(Y_e)
+    W = torch.empty_like(W_e)
+    ws = torch.empty(ttt.ttt_linear_workspace_bytes(w.B, w.H, w.T, 64, 16, torch.bfloat16),
+                     dtype=torch.uint8, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):          # warm the launch path off the capture
+        ttt.ttt_linear_forward(g["Q"], g["K"], g["V"], g["W0"], g["eta"], 16, Y=Y, W_out=W,
+                               workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        ttt.ttt_linear_forward(g["Q"], g["K"], g["V"], g["W0"], g["eta"], 16, Y=Y, W_out=W,
+                               workspace=ws)
+    other = make_inputs(w.with_(B=1, H=4, T=3000), 4242)
+    og = to_gpu(other)
+    for rep in range(3):
+        Y.zero_()
+        W.zero_()
+        ws.fill_(0xff)
+        # eager work between the replays, also through the workspace
+        ttt.ttt_linear_forward(og["Q"], og["K"], og["V"], og["W0"], og["eta"], 16, workspace=ws)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(Y, Y_e) and torch.equal(W, W_e), rep

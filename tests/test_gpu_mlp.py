@@ -4,7 +4,7 @@ import torch
 
 import test_sequence_layers_linear_amd as ttt
 from parity_util import (WORKLOADS, TOL, announce, default_seed, make_inputs, mlp_gpu, mlp_oracle,
-                         rel_l2, sample_chains, select_chains, to_gpu)
+                         per_chain_rel_l2, rel_l2, to_gpu)
 
 pytestmark = pytest.mark.gpu
 
@@ -41,19 +41,18 @@ def test_mlp_strong_state(T, std, eta, per_batch):
     _check(make_inputs(w, 300 + T, w0_per_batch=per_batch), 16, "bf16")
 
 
-def test_config5_sampled_chains_full_length():
+def test_config5_full():
+    """The TTT-MLP workload at full size, all 48 chains, relative L2 over the
+    whole Y, W1 and W2 tensors."""
     w = WORKLOADS[5]
-    announce("mlp config 5 sampled chains", w.name)
+    announce("mlp config 5, all chains", w.name)
     inp = make_inputs(w, default_seed(5))
     Y, W1, W2 = mlp_gpu(to_gpu(inp), w.b)
-    chains = sample_chains(w.B, w.H, 2, seed=55)
-    sub = select_chains(inp, chains)
-    Yr, W1r, W2r = mlp_oracle(sub, w.b)
-    pick = lambda X: torch.stack([X[b, h] for b, h in chains])[None]
-    e = (rel_l2(pick(Y), Yr), rel_l2(pick(W1), W1r), rel_l2(pick(W2), W2r))
-    print(f"  chains {chains} rel-L2 Y %.3e  W1 %.3e  W2 %.3e" % e, flush=True)
+    Yr, W1r, W2r = mlp_oracle(inp, w.b)
+    e = (rel_l2(Y, Yr), rel_l2(W1, W1r), rel_l2(W2, W2r))
+    print("  rel-L2 Y %.3e  W1 %.3e  W2 %.3e" % e
+          + f"  (worst chain Y {per_chain_rel_l2(Y, Yr).max():.3e})", flush=True)
     assert max(e) <= TOL["bf16"]
-    assert torch.isfinite(Y.float()).all()
 
 
 def test_mlp_eta_zero_keeps_state():

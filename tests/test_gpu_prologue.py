@@ -4,16 +4,16 @@ token) against the fp64 oracle's linear_forward_ex.
 Relative L2 of Y and W_out within 1e-4 for fp32 inputs and 2e-2 for bf16
 inputs (whose normalised rows are rounded to bf16 before the products, while
 the oracle keeps them exact).  Cases: each part of the prologue alone and
-together, ragged tails, segmented scans (forced segment counts) and two
-benchmark workloads at full size.
+together, ragged tails, segmented scans (forced segment counts) and three
+benchmark workloads at full size (every chain).
 """
 import pytest
 import torch
 
 import oracle
 import test_sequence_layers_linear_amd as ttt
-from parity_util import (WORKLOADS, TOL, announce, default_seed, make_inputs, rel_l2,
-                         sample_chains, select_chains, to_gpu)
+from parity_util import (WORKLOADS, TOL, announce, default_seed, make_inputs, per_chain_rel_l2,
+                         rel_l2, to_gpu)
 from test_sequence_layers_linear_amd.inputs import make_prologue
 
 pytestmark = pytest.mark.gpu
@@ -110,31 +110,25 @@ def test_prologue_config_full(cfg):
     assert ey <= TOL[w.dtype] and ew <= TOL[w.dtype]
 
 
-def test_prologue_config4_sampled_chains_full_length():
+def test_prologue_config4_full():
     """The 32768-token workload with the whole prologue, in the launch
     configuration the benchmark times (planned segments: maps, combine and the
-    staging-wave scans), on three chains the oracle computes one by one."""
+    staging-wave scans), all 48 chains, relative L2 over the whole tensors."""
     w = WORKLOADS[4]
-    announce("prologue config 4 sampled chains", w.name)
-    inp = make_inputs(w, default_seed(4) + 900)
+    announce("prologue config 4, all chains", w.name)
+    inp = dict(make_inputs(w, default_seed(4) + 900))
     pro = make_prologue(w, default_seed(4) + 903)
     inp["eta"] = pro["eta"]
     g = to_gpu(inp)
     Y, W = ttt.ttt_linear_forward_ex(g["Q"], g["K"], g["V"], g["W0"], g["eta"], w.b,
                                      **to_gpu({k: pro[k] for k in PARTS["all"]}))
     torch.cuda.synchronize()
-    chains = sample_chains(w.B, w.H, 3, seed=45)
-    sub = select_chains(inp, chains)
-    heads = [h for _, h in chains]
-    sub_pro = {"ln_q": pro["ln_q"][heads], "ln_k": pro["ln_k"][heads],
-               "eta_tok": torch.stack([pro["eta_tok"][b, h] for b, h in chains])[None]}
-    Yr, Wr = oracle.linear_forward_ex(sub["Q"], sub["K"], sub["V"], sub["W0"], sub["eta"], w.b, **sub_pro)
-    Ys = torch.stack([Y[b, h] for b, h in chains])[None]
-    Ws = torch.stack([W[b, h] for b, h in chains])[None]
-    ey, ew = rel_l2(Ys, Yr), rel_l2(Ws, Wr)
-    print(f"  chains {chains} rel-L2 Y {ey:.3e}  W {ew:.3e}", flush=True)
+    Yr, Wr = oracle.linear_forward_ex(inp["Q"], inp["K"], inp["V"], inp["W0"], inp["eta"], w.b,
+                                      **{k: pro[k] for k in PARTS["all"]})
+    ey, ew = rel_l2(Y, Yr), rel_l2(W, Wr)
+    print(f"  rel-L2 Y {ey:.3e}  W {ew:.3e}  (worst chain Y {per_chain_rel_l2(Y, Yr).max():.3e})",
+          flush=True)
     assert ey <= TOL["bf16"] and ew <= TOL["bf16"]
-    assert torch.isfinite(Y.float()).all() and torch.isfinite(W).all()
 
 
 @pytest.mark.parametrize("dtype", ["fp32", "bf16", "fp32-one-workgroup"])
