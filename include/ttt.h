@@ -122,6 +122,32 @@ int ttt_linear_forward(const void* Q, const void* K, const void* V, int qkv_dtyp
                        void* stream);
 
 /*
+ * ttt_linear_forward for callers that cannot allocate device memory or pass a
+ * workspace (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  Same arguments without the workspace, same plan
+ * and kernels as ttt_linear_forward given at least
+ * ttt_linear_workspace_bytes of workspace, so the results are identical bit
+ * for bit.  The segment maps and start states go to a static device array of
+ * ttt_linear_noalloc_max_workspace_bytes() (16 MiB) that every device the
+ * library runs on holds until the process ends; sizes whose plan needs more
+ * return TTT_ERR_UNSUPPORTED (every planned call on a 256-CU MI355X fits:
+ * at most B*H*(3 S - 2) matrices of 16 KB with B*H*S <= 256).  The call
+ * allocates nothing.  Its contents need no clearing (every byte read is
+ * written first in the same call).  All calls on one device share that
+ * array: calls that overlap in time on one device (different streams, or
+ * host threads without ordering) race on it and must be serialised by the
+ * caller.  Errors as for ttt_linear_forward; TTT_ERR_HIP also if the array's
+ * device address cannot be obtained.
+ */
+int ttt_linear_forward_noalloc(const void* Q, const void* K, const void* V, int qkv_dtype,
+                               const float* W0, int w0_per_batch, const float* eta,
+                               int64_t B, int64_t H, int64_t T, int d, int b,
+                               void* Y, float* W_out, void* stream);
+
+/* Bytes of the static array ttt_linear_forward_noalloc uses. */
+int64_t ttt_linear_noalloc_max_workspace_bytes(void);
+
+/*
  * Workspace bytes ttt_linear_forward (and ttt_linear_forward_ex) uses for
  * these sizes on the current device: B*H*(3 S - 2)*d*d*4 for the S segments
  * ttt_linear_segments reports, 0 when unsegmented.  Negative ttt_status for

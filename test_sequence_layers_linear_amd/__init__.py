@@ -73,6 +73,10 @@ def load_library():
     lib.ttt_linear_backward_segments.restype = I
     lib.ttt_linear_segments.argtypes = [L, L, L, I, I, I]
     lib.ttt_linear_segments.restype = I
+    lib.ttt_linear_forward_noalloc.argtypes = [P, P, P, I, P, I, P, L, L, L, I, I, P, P, P]
+    lib.ttt_linear_forward_noalloc.restype = I
+    lib.ttt_linear_noalloc_max_workspace_bytes.argtypes = []
+    lib.ttt_linear_noalloc_max_workspace_bytes.restype = L
     lib.ttt_linear_workspace_bytes.argtypes = [L, L, L, I, I, I]
     lib.ttt_linear_workspace_bytes.restype = L
     lib.ttt_linear_backward_workspace_bytes.argtypes = [L, L, L, I, I, I]
@@ -169,6 +173,36 @@ def ttt_linear_forward(Q, K, V, W0, eta, b: int, Y=None, W_out=None, workspace=N
                                   W0.data_ptr(), int(per_batch), eta.data_ptr(),
                                   B, H, T, d, int(b), Y.data_ptr(), W_out.data_ptr(),
                                   *_ws_args(ws), _stream_handle(dev, stream)))
+    return Y, W_out
+
+
+def ttt_linear_forward_noalloc(Q, K, V, W0, eta, b: int, Y, W_out, stream=None):
+    """ttt_linear_forward through the entry point that allocates nothing: the
+    segment maps live in the library's static device scratch.  Y and W_out
+    must be given (preallocated).  Calls that overlap on one device race on
+    that scratch."""
+    lib = load_library()
+    if Q.dim() != 4:
+        raise ValueError("Q must be [B,H,T,d]")
+    dev = Q.device
+    B, H, T, d = Q.shape
+    for t, n in ((Q, "Q"), (K, "K"), (V, "V")):
+        _need(t, n, dev, Q.dtype)
+        if t.shape != Q.shape:
+            raise ValueError(f"{n} shape {tuple(t.shape)} != Q shape {tuple(Q.shape)}")
+    _need(W0, "W0", dev, torch.float32)
+    _need(eta, "eta", dev, torch.float32)
+    per_batch = W0.dim() == 4
+    if W0.shape != ((B, H, d, d) if per_batch else (H, d, d)) or eta.shape != (H,):
+        raise ValueError("W0 must be [H,d,d] or [B,H,d,d] and eta [H]")
+    _need(Y, "Y", dev, Q.dtype)
+    _need(W_out, "W_out", dev, torch.float32)
+    if Y.shape != Q.shape or W_out.shape != (B, H, d, d):
+        raise ValueError("Y must be shaped like Q and W_out [B,H,d,d]")
+    _check(lib.ttt_linear_forward_noalloc(Q.data_ptr(), K.data_ptr(), V.data_ptr(),
+                                          _dtype_code(Q), W0.data_ptr(), int(per_batch),
+                                          eta.data_ptr(), B, H, T, d, int(b), Y.data_ptr(),
+                                          W_out.data_ptr(), _stream_handle(dev, stream)))
     return Y, W_out
 
 
@@ -462,7 +496,8 @@ def ttt_linear_backward_segments(B: int, H: int, T: int, d: int, b: int,
 
 
 __all__ = [
-    "ttt_linear_forward", "ttt_linear_forward_ex", "ttt_mlp_forward", "ttt_linear_decode_step",
+    "ttt_linear_forward", "ttt_linear_forward_ex", "ttt_linear_forward_noalloc",
+    "ttt_mlp_forward", "ttt_linear_decode_step",
     "ttt_linear_decode_step_ex", "ttt_linear_backward",
     "ttt_linear_segments", "ttt_linear_backward_segments", "ttt_linear_workspace_bytes",
     "ttt_linear_backward_workspace_bytes",

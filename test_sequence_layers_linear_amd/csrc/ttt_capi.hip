@@ -11,6 +11,7 @@
 #include <algorithm>
 #include <atomic>
 #include <functional>
+#include <mutex>
 
 namespace {
 
@@ -255,13 +256,39 @@ int linear_sizes_status(int64_t B, int64_t H, int64_t T, int d, int b, int qkv_d
     return TTT_OK;
 }
 
+// Scratch of ttt_linear_forward_noalloc: the segment maps and start states
+// of one call, in a file-scope device array instead of caller memory.  Every
+// device the library runs on holds its own copy until the process ends.
+constexpr int64_t kScratchBytes = int64_t{16} << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// Device address of the current device's copy of `scratch`, looked up once
+// per device (the array's name is not a device address in host code).
+int scratch_address(void** out)
+{
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void* addr[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return TTT_ERR_HIP;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return TTT_ERR_HIP;
+        addr[dev] = p;
+    }
+    *out = addr[dev];
+    return TTT_OK;
+}
+
 // ttt_linear_forward with an optional input prologue (pro.active(): d = 64,
-// b = 16 only) and the caller's workspace.
+// b = 16 only) and the caller's workspace, or (use_scratch) the static
+// scratch with the plan a sufficient workspace would get.
 int linear_forward_impl(const void* Q, const void* K, const void* V, int qkv_dtype,
                         const float* W0, int w0_per_batch, const float* eta,
                         int64_t B, int64_t H, int64_t T, int d, int b,
                         void* Y, float* W_out, void* ws, int64_t ws_bytes, void* stream,
-                        const ttt::Prologue& pro)
+                        const ttt::Prologue& pro, bool use_scratch = false)
 {
     if (w0_per_batch != 0 && w0_per_batch != 1) return TTT_ERR_INVALID_ARG;
     if (ws_bytes < 0 || (ws_bytes > 0 && !ws)) return TTT_ERR_INVALID_ARG;
@@ -297,8 +324,15 @@ int linear_forward_impl(const void* Q, const void* K, const void* V, int qkv_dty
     if (pro.active() && !ttt::linear_mfma_supports(a) && !ttt::linear_mfma_f32_supports(a))
         return TTT_ERR_UNSUPPORTED;
     const LinearScan k = pick_scan(a);
-    if (k.launch)
-        return run_linear_segmented(a, plan_forward(a, ws_bytes), ws, k.launch);
+    if (k.launch) {
+        if (!use_scratch) return run_linear_segmented(a, plan_forward(a, ws_bytes), ws, k.launch);
+        const ttt::SegmentPlan p = plan_forward(a, INT64_MAX);
+        if (forward_workspace_bytes(units, d, p.nseg) > kScratchBytes) return TTT_ERR_UNSUPPORTED;
+        void* sp = nullptr;
+        if (p.nseg > 1)
+            if (const int st = scratch_address(&sp)) return st;
+        return run_linear_segmented(a, p, sp, k.launch);
+    }
     if (ttt::linear_generic_lds_bytes(d, b) > static_cast<size_t>(ttt::kMaxLdsBytes))
         return TTT_ERR_UNSUPPORTED;
     return hip_status(ttt::launch_linear_generic(a));
@@ -341,6 +375,17 @@ int ttt_linear_forward_ex(const void* Q, const void* K, const void* V, int qkv_d
     return linear_forward_impl(Q, K, V, qkv_dtype, W0, w0_per_batch, eta, B, H, T, d, b, Y, W_out,
                                workspace, workspace_bytes, stream, pro);
 }
+
+int ttt_linear_forward_noalloc(const void* Q, const void* K, const void* V, int qkv_dtype,
+                               const float* W0, int w0_per_batch, const float* eta,
+                               int64_t B, int64_t H, int64_t T, int d, int b,
+                               void* Y, float* W_out, void* stream)
+{
+    return linear_forward_impl(Q, K, V, qkv_dtype, W0, w0_per_batch, eta, B, H, T, d, b, Y, W_out,
+                               nullptr, 0, stream, ttt::Prologue{}, true);
+}
+
+int64_t ttt_linear_noalloc_max_workspace_bytes(void) { return kScratchBytes; }
 
 int64_t ttt_linear_workspace_bytes(int64_t B, int64_t H, int64_t T, int d, int b, int qkv_dtype)
 {

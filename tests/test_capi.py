@@ -42,6 +42,7 @@ def test_exports_every_declared_function(lib):
                           "ttt_linear_backward_segments", "ttt_linear_decode_step_ex",
                           "ttt_linear_workspace_bytes", "ttt_linear_backward_workspace_bytes",
                           "ttt_status_string", "ttt_roof_copy", "ttt_roof_mfma",
+                          "ttt_linear_forward_noalloc", "ttt_linear_noalloc_max_workspace_bytes",
                           "ttt_abi_version"}
     for n in names:
         assert hasattr(lib, n), f"{n} declared in ttt.h but not exported"
@@ -318,3 +319,24 @@ def test_roof_probe_validation(lib):
     assert lib.ttt_roof_mfma(YA, 2, 1024, 10, None, None) == INVALID
     assert lib.ttt_roof_mfma(YA, 1, 1022, 10, None, None) == INVALID
     assert lib.ttt_roof_mfma(YA, 0, 1024, 0, None, None) == INVALID
+
+
+def test_noalloc_validation_and_limit(lib, monkeypatch):
+    """The entry point without allocation validates like ttt_linear_forward and
+    rejects sizes whose plan needs more than its static scratch (16 MiB)
+    before any HIP call."""
+    f = lib.ttt_linear_forward_noalloc
+    lib.ttt_linear_noalloc_max_workspace_bytes.restype = ctypes.c_int64
+    assert lib.ttt_linear_noalloc_max_workspace_bytes() == 16 << 20
+
+    def na(**kw):
+        a = dict(Q=QA, K=KA, V=VA, dt=1, W0=W0A, pb=0, eta=ETA, B=2, H=24, T=32768, d=64, b=16,
+                 Y=YA, Wo=WOA)
+        a.update(kw)
+        return f(a["Q"], a["K"], a["V"], a["dt"], a["W0"], a["pb"], a["eta"], a["B"], a["H"],
+                 a["T"], a["d"], a["b"], a["Y"], a["Wo"], None)
+    assert na(Q=None) == INVALID and na(Y=QA) == INVALID and na(d=48) == UNSUPPORTED
+    assert na(B=0) == OK
+    # 30 forced segments of 48 chains: 48 * 88 matrices of 16 KB = 69 MB > 16 MiB
+    monkeypatch.setenv("TTT_LINEAR_SEGMENTS", "30")
+    assert na() == UNSUPPORTED
