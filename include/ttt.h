@@ -80,6 +80,8 @@ typedef enum {
  *                state update); no other overlap between an output and any
  *                argument is allowed.
  *   B, H, T      >= 0.  B*H = 0 is a no-op.  T = 0 writes W_out = W0.
+ *                B*H above 2^20 returns TTT_ERR_UNSUPPORTED (for every entry
+ *                point).
  *   d            16, 32, 64 or 128.
  *   b            mini-batch size, 1 <= b <= 64.  (d = 64, b = 16 runs the
  *                MFMA kernels; other shapes run a plainer kernel.)
@@ -222,8 +224,8 @@ int ttt_mlp_forward(const void* Q, const void* K, const void* V, int qkv_dtype,
  * sequential form as the one for token-by-token decoding):
  *     r = k W - v;   W <- W - eta_h k^T r;   y = q W   (updated W)
  *
- *   q, k, v      [B][H][d], qkv_dtype, read only.
- *   W            fp32 [B][H][d][d], updated IN PLACE.
+ *   q, k, v      [B][H][d], qkv_dtype, read only; q and k 16-byte aligned.
+ *   W            fp32 [B][H][d][d], updated IN PLACE; 16-byte aligned.
  *   eta          fp32 [H].
  *   y            [B][H][d], qkv_dtype, written; must not overlap any input.
  *   d            16, 32, 64 or 128.

@@ -47,8 +47,9 @@ bool overlap(const Range& a, const Range& b)
 
 bool d_supported(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 
-// largest grid.x the launchers use
-constexpr int64_t kMaxUnits = 0x7fffffff;
+// most (batch, head) chains: a launch's grid, counted in work-items, must
+// stay below 2^32 (the widest launch has up to 768 threads per chain)
+constexpr int64_t kMaxUnits = int64_t{1} << 20;
 // longest sequence: every kernel indexes a chain's tokens with 32-bit ints
 // (the MFMA kernels' byte offsets are bounded tighter by their own checks)
 constexpr int64_t kMaxTokens = 0x7fffffff;
@@ -603,6 +604,9 @@ int decode_impl(const void* q, const void* k, const void* v, int qkv_dtype, floa
     if (!mul_ok(units, H) || units > kMaxUnits) return TTT_ERR_UNSUPPORTED;
     if (units == 0) return TTT_OK;
     if (!q || !k || !v || !W || !eta || !y) return TTT_ERR_INVALID_ARG;
+    // the step reads rows of q, k and W with 16-byte loads
+    for (const void* ptr : {q, k, static_cast<const void*>(W)})
+        if (reinterpret_cast<uintptr_t>(ptr) % 16 != 0) return TTT_ERR_INVALID_ARG;
     const int64_t n_vec = units * d * static_cast<int64_t>(elem_bytes(qkv_dtype));
     const Range rq{q, n_vec}, rk{k, n_vec}, rv{v, n_vec}, ry{y, n_vec};
     const Range rW{W, units * d * d * 4}, rEta{eta, H * 4};

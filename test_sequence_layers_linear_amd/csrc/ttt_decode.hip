@@ -5,163 +5,200 @@
 // section "Hardware Parallelization" names this sequential form as the one
 // for token-by-token decoding with O(1) step cost).
 //
-// The step is HBM-bound on the fp32 state (read + write d*d*4 bytes per
-// (batch, head)).  Output columns of W are independent (column j needs only
-// W[:, j], k, q and v_j), so each (batch, head) is split over d/16 workgroups
-// of 16 columns; this gives B*H*d/16 workgroups instead of B*H.  Inside a
-// workgroup 16 row groups x 16 columns of threads: each thread owns d/16
-// rows of one column, loads them once, and writes them back once.
-//
-// y_j uses q W'_j = q W_j - eta (q . k) r_j, algebraically the readout with
-// the updated column, so W is read once and written once.  Every global load
-// is issued before the first barrier (one trip to memory per step), and
-// q . k is summed like k W_j and q W_j, from per-thread partials.
+// The step is bound by the fp32 state (read + write d*d*4 bytes per
+// (batch, head)) and, at these sizes, by latency: one trip to memory and
+// back plus the launch.  Output columns of W are independent (column j needs
+// only W[:, j], k, q and v_j), so one wave serves up to 64 columns of one
+// (batch, head) with 16-byte accesses and no LDS or barrier.  y_j uses
+// q W'_j = q W_j - eta (q . k) r_j, algebraically the readout with the
+// updated column, so W is read once and written once, and every global load
+// is issued before any arithmetic.
 //
 // kPro: the input prologue of ttt_linear_forward_ex for one token: q and k
-// LayerNorm'd over the head dim (waves 0 and 1, one row each, butterfly sums
-// over the wave), the token's own step size, and with read_start the readout
-// before the update (y = q W), the b = 1 case of the chunk-start read.
+// LayerNorm'd over the head dim, the token's own step size, and with
+// read_start the readout before the update (y = q W), the b = 1 case of the
+// chunk-start read.
 #include "ttt_internal.h"
 
 namespace ttt {
 namespace {
 
-constexpr int kCols = 16;
-constexpr int kRowGroups = 16;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-// LayerNorm of the d <= 128 values in buf (LDS) by one whole wave: lane l
-// holds elements l and l + 64
-__device__ void layernorm_wave(float* buf, int d, const float* __restrict__ prm, int h, float eps)
+// R consecutive q/k elements of the lane's row block (fp32 or bf16) in fp32.
+template <int R>
+__device__ __forceinline__ void load_block(const float* p, float (&x)[R])
 {
-    const int l = threadIdx.x & 63;
-    const float x0 = l < d ? buf[l] : 0.f;
-    const float x1 = l + 64 < d ? buf[l + 64] : 0.f;
-    float sum = x0 + x1;
 #pragma unroll
-    for (int m = 32; m >= 1; m >>= 1)
-        sum += __shfl_xor(sum, m);
-    const float mean = sum / static_cast<float>(d);
-    const float d0 = l < d ? x0 - mean : 0.f;
-    const float d1 = l + 64 < d ? x1 - mean : 0.f;
-    float sq = d0 * d0 + d1 * d1;
+    for (int i = 0; i < R; i += 4) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(p + i);
+        x[i] = v[0]; x[i + 1] = v[1]; x[i + 2] = v[2]; x[i + 3] = v[3];
+    }
+}
+template <int R>
+__device__ __forceinline__ void load_block(const uint16_t* p, float (&x)[R])
+{
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    if constexpr (R == 4) {
+        const u32x2 v = *reinterpret_cast<const u32x2*>(p);
 #pragma unroll
-    for (int m = 32; m >= 1; m >>= 1)
-        sq += __shfl_xor(sq, m);
-    const float rstd = rsqrtf(sq / static_cast<float>(d) + eps);
-    if (l < d)
-        buf[l] = d0 * rstd * prm[(2 * h) * d + l] + prm[(2 * h + 1) * d + l];
-    if (l + 64 < d)
-        buf[l + 64] = d1 * rstd * prm[(2 * h) * d + l + 64] + prm[(2 * h + 1) * d + l + 64];
+        for (int e = 0; e < 2; ++e) {
+            x[2 * e] = __uint_as_float(v[e] << 16);
+            x[2 * e + 1] = __uint_as_float(v[e] & 0xffff0000u);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < R; i += 8) {
+            const u32x4 v = *reinterpret_cast<const u32x4*>(p + i);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                x[i + 2 * e] = __uint_as_float(v[e] << 16);
+                x[i + 2 * e + 1] = __uint_as_float(v[e] & 0xffff0000u);
+            }
+        }
+    }
+}
+
+// Sum over the wave's four row groups (lanes l, l ^ 16, l ^ 32, l ^ 48).
+__device__ __forceinline__ float rowgroup_sum(float x)
+{
+    x += __shfl_xor(x, 16);
+    x += __shfl_xor(x, 32);
+    return x;
+}
+
+// One wave per (batch, head) and 64-column slice of W.  Lane l holds the four
+// columns j = 64 slice + 4 (l % 16) .. + 3 over the R = d / 4 rows
+// (l / 16) R .. + R - 1: each of its R float4 loads and stores is one row
+// segment, so one instruction of the wave moves four 256-byte rows.  Sums over
+// the input index run over the lane's rows, then over the four row groups
+// with two lane shuffles.  k and q: each lane reads its R-row block.
+template <typename TIn, int kD, bool kPro>
+__global__ void __launch_bounds__(64)
+decode_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
+              const TIn* __restrict__ v, float* __restrict__ W,
+              const float* __restrict__ eta, int H, TIn* __restrict__ y, Prologue pro)
+{
+    constexpr int kSlices = (kD + 63) / 64;
+    constexpr int R = kD / 4;                     // rows per lane
+    constexpr int kGroups = kD / 4 < 16 ? kD / 4 : 16;   // column groups per wave
+    const int lane = threadIdx.x;
+    const int64_t u = blockIdx.x / kSlices;
+    const int cg = lane & 15, rg = lane >> 4;
+    // d < 64: lanes past the last column group only help with the sums
+    const bool active = cg < kGroups;
+    const int j0 = (blockIdx.x % kSlices) * 64 + 4 * (active ? cg : 0);
+    const int h = static_cast<int>(u % H);
+    const int i0 = rg * R;
+
+    // every global load first: one trip to memory per step
+    float* Wu = W + u * kD * kD;
+    f32x4 w[R];
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+        w[i] = *reinterpret_cast<const f32x4*>(Wu + (i0 + i) * kD + j0);
+    float kr[R], qr[R];
+    load_block<R>(k + u * kD + i0, kr);
+    load_block<R>(q + u * kD + i0, qr);
+    float vj[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        vj[e] = load_elem(v, u * kD + j0 + e);
+    const float et = (kPro && pro.eta_tok) ? pro.eta_tok[u] : eta[h];
+
+    if constexpr (kPro) {
+        // LayerNorm of the whole k and q rows: each row group holds R of the
+        // d elements; the sums run over the lane's block, then the groups
+        auto norm = [&](float (&x)[R], const float* prm) {
+            float s = 0.f;
+#pragma unroll
+            for (int i = 0; i < R; ++i)
+                s += x[i];
+            const float mean = rowgroup_sum(s) * (1.0f / kD);
+            float sq = 0.f;
+#pragma unroll
+            for (int i = 0; i < R; ++i)
+                sq += (x[i] - mean) * (x[i] - mean);
+            const float rstd = rsqrtf(rowgroup_sum(sq) * (1.0f / kD) + pro.ln_eps);
+#pragma unroll
+            for (int i = 0; i < R; ++i)
+                x[i] = (x[i] - mean) * rstd * prm[(2 * h) * kD + i0 + i] + prm[(2 * h + 1) * kD + i0 + i];
+        };
+        if (pro.ln_k)
+            norm(kr, pro.ln_k);
+        if (pro.ln_q)
+            norm(qr, pro.ln_q);
+    }
+
+    // k W_j, q W_j over the lane's rows, and q . k, then over the row groups
+    float kw[4] = {0.f, 0.f, 0.f, 0.f}, qw[4] = {0.f, 0.f, 0.f, 0.f}, qk = 0.f;
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            kw[e] += kr[i] * w[i][e];
+            qw[e] += qr[i] * w[i][e];
+        }
+        qk += qr[i] * kr[i];
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        kw[e] = rowgroup_sum(kw[e]);
+        qw[e] = rowgroup_sum(qw[e]);
+    }
+    qk = rowgroup_sum(qk);
+    if (!active)
+        return;
+    float r[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        r[e] = kw[e] - vj[e];
+    // q W'_j = q W_j - eta (q . k) r_j: the readout with the updated column
+    if (rg == 0) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            store_elem(y, u * kD + j0 + e, (kPro && pro.read_start) ? qw[e] : qw[e] - et * qk * r[e]);
+    }
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+        f32x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            o[e] = w[i][e] - et * (kr[i] * r[e]);
+        *reinterpret_cast<f32x4*>(Wu + (i0 + i) * kD + j0) = o;
+    }
+}
+
+template <typename TIn, int kD, bool kPro>
+void launch_d(const DecodeArgs& a)
+{
+    constexpr int kSlices = (kD + 63) / 64;
+    const dim3 grid(static_cast<unsigned>(a.B * a.H * kSlices));
+    hipLaunchKernelGGL((decode_kernel<TIn, kD, kPro>), grid, dim3(64), 0, a.stream,
+                       static_cast<const TIn*>(a.q), static_cast<const TIn*>(a.k),
+                       static_cast<const TIn*>(a.v), a.W, a.eta, static_cast<int>(a.H),
+                       static_cast<TIn*>(a.y), a.pro);
 }
 
 template <typename TIn, bool kPro>
-__global__ void __launch_bounds__(kCols * kRowGroups)
-decode_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
-              const TIn* __restrict__ v, float* __restrict__ W,
-              const float* __restrict__ eta, int H, int d, TIn* __restrict__ y, Prologue pro)
+void launch_t(const DecodeArgs& a)
 {
-    __shared__ float ks[128], qs[128];
-    __shared__ float red_k[kRowGroups][kCols + 1], red_q[kRowGroups][kCols + 1];
-    __shared__ float red_qk[kRowGroups];
-    __shared__ float rcol[kCols];
-
-    const int64_t u = blockIdx.x;
-    const int h = static_cast<int>(u % H);
-    const int jl = threadIdx.x % kCols;
-    const int ig = threadIdx.x / kCols;
-    const int j = blockIdx.y * kCols + jl;
-    const int rows = d / kRowGroups;  // 1, 2, 4 or 8
-
-    // every global load first, so the step costs one trip to memory: this
-    // thread's d / 16 rows of column j of W, v_j, and (plain step) the k and
-    // q entries of those rows
-    float* Wu = W + u * d * d;
-    float w[8], kr[8], qr[8];
-#pragma unroll
-    for (int r = 0; r < 8; ++r)
-        if (r < rows)
-            w[r] = Wu[(ig + kRowGroups * r) * d + j];
-    const float vj = load_elem(v, u * d + j);
-    const float et = (kPro && pro.eta_tok) ? pro.eta_tok[u] : eta[h];
-    if constexpr (kPro) {
-        // the LayerNorm needs whole rows: stage k and q in LDS
-        for (int x = threadIdx.x; x < d; x += kCols * kRowGroups) {
-            ks[x] = load_elem(k, u * d + x);
-            qs[x] = load_elem(q, u * d + x);
-        }
-        __syncthreads();
-        if (pro.ln_k || pro.ln_q) {
-            const int wv = threadIdx.x >> 6;          // wave-uniform roles
-            if (wv == 0 && pro.ln_k)
-                layernorm_wave(ks, d, pro.ln_k, h, pro.ln_eps);
-            if (wv == 1 && pro.ln_q)
-                layernorm_wave(qs, d, pro.ln_q, h, pro.ln_eps);
-            __syncthreads();
-        }
-#pragma unroll
-        for (int r = 0; r < 8; ++r)
-            if (r < rows) {
-                kr[r] = ks[ig + kRowGroups * r];
-                qr[r] = qs[ig + kRowGroups * r];
-            }
-    } else {
-#pragma unroll
-        for (int r = 0; r < 8; ++r)
-            if (r < rows) {
-                kr[r] = load_elem(k, u * d + ig + kRowGroups * r);
-                qr[r] = load_elem(q, u * d + ig + kRowGroups * r);
-            }
+    switch (a.d) {
+    case 16: launch_d<TIn, 16, kPro>(a); break;
+    case 32: launch_d<TIn, 32, kPro>(a); break;
+    case 64: launch_d<TIn, 64, kPro>(a); break;
+    default: launch_d<TIn, 128, kPro>(a); break;
     }
-
-    // partial k W_j, q W_j and q . k over this thread's rows, then the sums
-    // over the 16 row groups
-    float pk = 0.f, pq = 0.f, pqk = 0.f;
-#pragma unroll
-    for (int r = 0; r < 8; ++r)
-        if (r < rows) {
-            pk += kr[r] * w[r];
-            pq += qr[r] * w[r];
-            pqk += qr[r] * kr[r];
-        }
-    red_k[ig][jl] = pk;
-    red_q[ig][jl] = pq;
-    if (jl == 0)
-        red_qk[ig] = pqk;
-    __syncthreads();
-    if (ig == 0) {
-        float kw = 0.f, qw = 0.f, qk = 0.f;
-        for (int g = 0; g < kRowGroups; ++g) {
-            kw += red_k[g][jl];
-            qw += red_q[g][jl];
-            qk += red_qk[g];
-        }
-        const float r = kw - vj;
-        rcol[jl] = r;
-        store_elem(y, u * d + j, (kPro && pro.read_start) ? qw : qw - et * qk * r);
-    }
-    __syncthreads();
-    const float r = rcol[jl];
-#pragma unroll
-    for (int rr = 0; rr < 8; ++rr)
-        if (rr < rows)
-            Wu[(ig + kRowGroups * rr) * d + j] = w[rr] - et * (kr[rr] * r);
 }
 
 template <bool kPro>
 hipError_t launch(const DecodeArgs& a)
 {
-    const dim3 grid(static_cast<unsigned>(a.B * a.H), static_cast<unsigned>(a.d / kCols));
-    const dim3 block(kCols * kRowGroups);
     if (a.dtype == 0)
-        hipLaunchKernelGGL((decode_kernel<float, kPro>), grid, block, 0, a.stream,
-                           static_cast<const float*>(a.q), static_cast<const float*>(a.k),
-                           static_cast<const float*>(a.v), a.W, a.eta, static_cast<int>(a.H),
-                           a.d, static_cast<float*>(a.y), a.pro);
+        launch_t<float, kPro>(a);
     else
-        hipLaunchKernelGGL((decode_kernel<uint16_t, kPro>), grid, block, 0, a.stream,
-                           static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
-                           static_cast<const uint16_t*>(a.v), a.W, a.eta, static_cast<int>(a.H),
-                           a.d, static_cast<uint16_t*>(a.y), a.pro);
+        launch_t<uint16_t, kPro>(a);
     return hipGetLastError();
 }
 

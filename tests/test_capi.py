@@ -79,8 +79,8 @@ def lin(lib, Q=QA, K=KA, V=VA, dt=1, W0=W0A, pb=0, eta=ETA, B=2, H=3, T=64, d=64
     (dict(wsb=-1), INVALID), (dict(ws=None, wsb=4096), INVALID),
     (dict(ws=QA + 128, wsb=4096), INVALID), (dict(ws=WOA - 64, wsb=4096), INVALID),
     (dict(ws=YA, wsb=1), INVALID),
-    # sequence length beyond the 32-bit token index
-    (dict(T=2**31), UNSUPPORTED),
+    # sequence length beyond the 32-bit token index; more chains than a grid holds
+    (dict(T=2**31), UNSUPPORTED), (dict(B=2**20 + 1, H=1, T=1), UNSUPPORTED),
 ])
 def test_linear_validation(lib, kw, expect):
     assert lin(lib, **kw) == expect
@@ -143,7 +143,9 @@ def dec(lib, q=QA, W=W0A, y=YA, dt=1, B=2, H=24, d=64):
     (dict(B=-1), INVALID), (dict(q=None), INVALID), (dict(W=None), INVALID),
     (dict(y=None), INVALID), (dict(d=96), UNSUPPORTED), (dict(dt=9), UNSUPPORTED),
     (dict(y=QA), INVALID), (dict(y=W0A), INVALID), (dict(W=KA), INVALID),
-    (dict(B=0), OK),
+    (dict(B=0), OK), (dict(B=2**20, H=2), UNSUPPORTED),
+    # rows of q, k and W are read with 16-byte loads
+    (dict(q=QA + 8), INVALID), (dict(W=W0A + 4), INVALID),
 ])
 def test_decode_validation(lib, kw, expect):
     assert dec(lib, **kw) == expect
