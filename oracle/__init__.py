@@ -29,6 +29,13 @@ Parity status of each function (how it is pinned, see tests/test_oracle.py):
                      coordinate (q, k, v, W0, per-token eta, gamma, beta),
                      with and without the chunk-start read; torch autograd
                      of layer_norm for the LayerNorm part.
+  linear_momentum -- pinned: a hand-worked d=2 example (tests/golden), the
+                     heavy-ball closed form of the scalar recursion, beta=0
+                     equal to linear_forward (b=1 for exact token steps, b for
+                     chunk-start gradients), torch autograd gradients with
+                     momentum steps, the chunk closed form of the momentum
+                     sums (chunk-start gradients), and the triangular-solve
+                     chunk form in dual.py (exact token steps).
   linear_backward -- pinned: central finite differences of linear_forward in
                      every coordinate (tiny sizes), the closed form of every
                      gradient at eta=0 (independent of b), the gradients of
@@ -90,6 +97,9 @@ def _load():
     lib.ttt_oracle_linear_backward_tok.restype = I
     lib.ttt_oracle_layernorm_rows_backward.argtypes = [P, P, L, L, L, L, P, ctypes.c_double, P]
     lib.ttt_oracle_layernorm_rows_backward.restype = I
+    lib.ttt_oracle_linear_momentum.argtypes = [P, P, P, P, I, P, P, P, I, L, L, L, L, L,
+                                               P, P, P, I]
+    lib.ttt_oracle_linear_momentum.restype = I
     lib.ttt_oracle_max_threads.argtypes = []
     lib.ttt_oracle_max_threads.restype = I
     _lib = lib
@@ -254,6 +264,34 @@ def linear_backward_ex(Q, K, V, W0, eta, b: int, dY, dW_out, eta_tok=None, ln_q=
         out["deta"] = np.zeros(H)
         out["deta_tok"] = detat
     return out
+
+
+def linear_momentum(Q, K, V, W0, eta, beta, b: int = 1, M0=None, grad_mode: int = 0,
+                    nthreads: int = 0):
+    """Momentum GD on TTT-Linear, token by token (E2-TTT write-up, "E2-TTT's
+    Breakthrough").  grad_mode 0: exact token-level gradients at W_{t-1};
+    1: gradients at the start of each chunk of b tokens.  W0 [H,d,d] or
+    [B,H,d,d]; M0 None (zero) or [B,H,d,d]; eta, beta [H].
+    Returns (Y [B,H,T,d], W_out, M_out [B,H,d,d]) in fp64."""
+    Q, K, V, W0, eta, beta = map(_f64, (Q, K, V, W0, eta, beta))
+    B, H, T, d = Q.shape
+    assert K.shape == Q.shape and V.shape == Q.shape
+    per_batch = 1 if W0.ndim == 4 else 0
+    assert W0.shape == ((B, H, d, d) if per_batch else (H, d, d))
+    assert eta.shape == (H,) and beta.shape == (H,)
+    if M0 is not None:
+        M0 = _f64(M0)
+        assert M0.shape == (B, H, d, d)
+    Y = np.zeros((B, H, T, d))
+    W_out = np.zeros((B, H, d, d))
+    M_out = np.zeros((B, H, d, d))
+    rc = _load().ttt_oracle_linear_momentum(_ptr(Q), _ptr(K), _ptr(V), _ptr(W0), per_batch,
+                                            None if M0 is None else _ptr(M0), _ptr(eta),
+                                            _ptr(beta), int(grad_mode), B, H, T, d, int(b),
+                                            _ptr(Y), _ptr(W_out), _ptr(M_out), int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"oracle linear_momentum failed ({rc})")
+    return Y, W_out, M_out
 
 
 def mlp_forward(Q, K, V, W1, W2, eta, b: int, nthreads: int = 0):

@@ -16,6 +16,22 @@ TTT-Linear, one chunk (rows = tokens, row-vector form z W):
                                           out after its own update
     W_next = W - eta * K^T E
 
+TTT-Linear with momentum (the E2-TTT write-up on zhichai.net, sections
+"E2-TTT's Breakthrough" and "Core Math": the chunk-end W and M computed in
+closed form from the chunk-start W_k, M_k).  Token t of a chunk (0-based)
+sees the weights after the chunk's first t tokens,
+    W_(t) = W - eta c_t M - eta sum_{u<t} dsum_{t-1-u} k_u^T r_u,
+    c_t = beta + ... + beta^t,   dsum_m = 1 + beta + ... + beta^m,
+so with E = K W - V the exact token-level residuals solve the unit lower
+triangular system
+    (I + eta A) R = E - eta diag(c_t) K M,   A[t, u] = dsum_{t-1-u} (k_t . k_u), u < t
+(with gradients at the chunk start instead, R = E), and then
+    Y      = Q W - eta diag(c_{t+1}) Q M - eta (tril(Q K^T) o Dsum) R,
+             Dsum[t, u] = dsum_{t-u}
+    W_next = W - eta c_n M - eta K^T diag(dsum_{n-1-u}) R
+    M_next = beta^n M + K^T diag(beta^{n-1-u}) R.
+This is a derivation of this module, not a formula printed on the page.
+
 TTT-MLP f(z) = SiLU(z W1) W2, one chunk, all gradients at the chunk start:
     Hk = K W1, Ak = SiLU(Hk), E = Ak W2 - V
     D  = (E W2^T) * SiLU'(Hk)
@@ -53,6 +69,43 @@ def linear_dual(Q, K, V, W0, eta, b):
                 W = W - eta[h] * Kc.T @ E
             W_out[bi, h] = W
     return Y, W_out
+
+
+def linear_momentum_dual(Q, K, V, W0, eta, beta, b, M0=None, grad_mode=0):
+    Q, K, V, W0, eta, beta = (np.asarray(a, dtype=np.float64)
+                              for a in (Q, K, V, W0, eta, beta))
+    B, H, T, d = Q.shape
+    Y = np.zeros_like(Q)
+    W_out = np.zeros((B, H, d, d))
+    M_out = np.zeros((B, H, d, d))
+    for bi in range(B):
+        for h in range(H):
+            W = (W0[bi, h] if W0.ndim == 4 else W0[h]).copy()
+            M = np.zeros((d, d)) if M0 is None else np.asarray(M0, np.float64)[bi, h].copy()
+            bt, et = beta[h], eta[h]
+            for s in range(0, T, b):
+                e = min(s + b, T)
+                n = e - s
+                Qc, Kc, Vc = Q[bi, h, s:e], K[bi, h, s:e], V[bi, h, s:e]
+                pw = bt ** np.arange(n + 1)                 # beta^0 .. beta^n
+                c = np.concatenate([[0.0], np.cumsum(pw[1:])])   # c_0 .. c_n
+                dsum = np.cumsum(pw)                        # dsum_0 .. dsum_n
+                idx = np.arange(n)
+                lag = idx[:, None] - idx[None, :]           # t - u
+                E = Kc @ W - Vc
+                if grad_mode == 0:
+                    A = np.where(lag > 0, dsum[np.maximum(lag - 1, 0)], 0.0) * (Kc @ Kc.T)
+                    rhs = E - et * c[:n, None] * (Kc @ M)
+                    R = np.linalg.solve(np.eye(n) + et * A, rhs)
+                else:
+                    R = E
+                S = np.where(lag >= 0, dsum[np.maximum(lag, 0)], 0.0) * (Qc @ Kc.T)
+                Y[bi, h, s:e] = Qc @ W - et * c[1:, None] * (Qc @ M) - et * S @ R
+                W = W - et * c[n] * M - et * Kc.T @ (dsum[n - 1 - idx][:, None] * R)
+                M = pw[n] * M + Kc.T @ (pw[n - 1 - idx][:, None] * R)
+            W_out[bi, h] = W
+            M_out[bi, h] = M
+    return Y, W_out, M_out
 
 
 def mlp_dual(Q, K, V, W1, W2, eta, b):

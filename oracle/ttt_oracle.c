@@ -26,7 +26,13 @@
  *         paragraph on fast weights being reset at the end of a sequence.
  *   [E2]  the E2-TTT write-up on zhichai.net, section "The Curse of
  *         Efficiency" (gradients computed at each chunk's start and applied to
- *         the whole chunk).
+ *         the whole chunk), section "E2-TTT's Breakthrough: A Closed-Form
+ *         Solution" (gradient descent or momentum gradient descent on the
+ *         squared loss, fast weights W and momentum M evolving token by token,
+ *         the chunk-end W and M computed exactly) and section "Technical
+ *         Details and Practical Implications", "Core Math (Simplified)"
+ *         (learning rate alpha, momentum coefficient beta, W_k and M_k at each
+ *         chunk's start).
  *
  * What is computed: mini-batch gradient descent in PRIMAL form, token by token,
  * every intermediate fast weight W_t materialised.  This is the plain
@@ -883,4 +889,101 @@ int ttt_oracle_linear_decode(const double* q, const double* k, const double* v,
     }
     free(r);
     return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* TTT-Linear with momentum gradient descent ([E2] "E2-TTT's Breakthrough"   */
+/* and "Core Math"): fast weights W and a momentum M of the same shape, one   */
+/* step per token on the squared loss 1/2 ||k W - v||^2:                      */
+/*     r_t = k_t W_g - v_t                (residual; grad = k_t^T r_t)        */
+/*     M_t = beta M_{t-1} + k_t^T r_t                                         */
+/*     W_t = W_{t-1} - eta M_t                                                */
+/*     y_t = q_t W_t                      (readout after the update, [KV])    */
+/* The point W_g where the gradient is taken:                                 */
+/*   grad_mode 0: W_g = W_{t-1}, the exact token-level step (online GD, and   */
+/*                momentum GD, with no chunk approximation);                  */
+/*   grad_mode 1: W_g = the weights at the start of the token's chunk of b    */
+/*                tokens (the chunk-start gradients of "The Curse of          */
+/*                Efficiency"); with beta = 0 this is the mini-batch scan of  */
+/*                ttt_oracle_linear_forward.                                  */
+/* b only matters in grad_mode 1.  beta is one value per head, like eta.      */
+/* M0: null (every chain starts with M = 0) or [B][H][d][d].                  */
+/* Outputs Y [B][H][T][d], W_out and M_out [B][H][d][d].                      */
+/* ------------------------------------------------------------------------ */
+static void momentum_chain(const double* q, const double* k, const double* v,
+                           const double* w_init, const double* m_init, double eta, double beta,
+                           int grad_mode, long T, long d, long b, double* y, double* w_final,
+                           double* m_final, double* W, double* M, double* Wc, double* r)
+{
+    const long dd = d * d;
+    memcpy(W, w_init, (size_t)dd * sizeof(double));
+    if (m_init)
+        memcpy(M, m_init, (size_t)dd * sizeof(double));
+    else
+        memset(M, 0, (size_t)dd * sizeof(double));
+    for (long t = 0; t < T; ++t) {
+        if (t % b == 0)
+            memcpy(Wc, W, (size_t)dd * sizeof(double));   /* chunk start */
+        const double* Wg = grad_mode ? Wc : W;
+        const double* kt = k + t * d;
+        const double* vt = v + t * d;
+        const double* qt = q + t * d;
+        for (long j = 0; j < d; ++j) {
+            double acc = 0.0;
+            for (long i = 0; i < d; ++i)
+                acc += kt[i] * Wg[i * d + j];
+            r[j] = acc - vt[j];
+        }
+        /* M <- beta M + k^T r, then W <- W - eta M */
+        for (long i = 0; i < d; ++i)
+            for (long j = 0; j < d; ++j) {
+                M[i * d + j] = beta * M[i * d + j] + kt[i] * r[j];
+                W[i * d + j] -= eta * M[i * d + j];
+            }
+        for (long j = 0; j < d; ++j) {
+            double acc = 0.0;
+            for (long i = 0; i < d; ++i)
+                acc += qt[i] * W[i * d + j];
+            y[t * d + j] = acc;
+        }
+    }
+    memcpy(w_final, W, (size_t)dd * sizeof(double));
+    memcpy(m_final, M, (size_t)dd * sizeof(double));
+}
+
+int ttt_oracle_linear_momentum(const double* Q, const double* K, const double* V,
+                               const double* W0, int w0_per_batch, const double* M0,
+                               const double* eta, const double* beta, int grad_mode,
+                               long B, long H, long T, long d, long b,
+                               double* Y, double* W_out, double* M_out, int nthreads)
+{
+    if (B < 0 || H < 0 || T < 0 || d < 1 || b < 1 || (grad_mode != 0 && grad_mode != 1))
+        return ORACLE_EINVAL;
+    if (!W0 || !eta || !beta || !W_out || !M_out || (T > 0 && (!Q || !K || !V || !Y)))
+        return ORACLE_EINVAL;
+    const long dd = d * d;
+    const long units = B * H;
+    int status = ORACLE_OK;
+    set_threads(nthreads);
+#pragma omp parallel
+    {
+        double* ws = (double*)malloc((size_t)(3 * dd + d) * sizeof(double));
+        if (!ws) {
+#pragma omp atomic write
+            status = ORACLE_ENOMEM;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (long u = 0; u < units; ++u) {
+            if (!ws)
+                continue;
+            long h = u % H;
+            const long off = u * T * d;
+            momentum_chain(Q + off, K + off, V + off, W0 + (w0_per_batch ? u : h) * dd,
+                           M0 ? M0 + u * dd : NULL, eta[h], beta[h], grad_mode, T, d, b,
+                           Y + off, W_out + u * dd, M_out + u * dd,
+                           ws, ws + dd, ws + 2 * dd, ws + 3 * dd);
+        }
+        free(ws);
+    }
+    return status;
 }

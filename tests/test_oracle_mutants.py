@@ -17,6 +17,7 @@ import pytest
 import oracle
 import test_oracle as pins
 import test_oracle_backward as bpins
+import test_oracle_momentum as mpins
 import test_oracle_prologue as ppins
 import test_oracle_prologue_backward as pbpins
 
@@ -85,6 +86,19 @@ MUTANTS = {
     "lnbwd_dgamma_of_raw_rows": ("dgb[(2 * h) * d + j] += g[j] * xh[j];", "dgb[(2 * h) * d + j] += g[j] * x[j];"),
     "lnbwd_dbeta_scaled": ("dgb[(2 * h + 1) * d + j] += g[j];",
                            "dgb[(2 * h + 1) * d + j] += g[j] * gamma[h * d + j];"),
+    # momentum GD (exact token steps and chunk-start gradients)
+    "mom_beta_scales_gradient": ("M[i * d + j] = beta * M[i * d + j] + kt[i] * r[j];",
+                                 "M[i * d + j] = beta * (M[i * d + j] + kt[i] * r[j]);"),
+    "mom_step_uses_gradient": ("W[i * d + j] -= eta * M[i * d + j];",
+                               "W[i * d + j] -= eta * kt[i] * r[j];"),
+    "mom_gradient_point_swapped": ("const double* Wg = grad_mode ? Wc : W;",
+                                   "const double* Wg = grad_mode ? W : Wc;"),
+    "mom_initial_momentum_dropped": ("    if (m_init)\n        memcpy(M, m_init,",
+                                     "    if (0)\n        memcpy(M, m_init,"),
+    "mom_gradient_transposed": ("M[i * d + j] = beta * M[i * d + j] + kt[i] * r[j];",
+                                "M[i * d + j] = beta * M[i * d + j] + kt[j] * r[i];"),
+    "mom_chunk_start_off_by_one": ("if (t % b == 0)\n            memcpy(Wc, W,",
+                                   "if (t % b == 1 || b == 1)\n            memcpy(Wc, W,"),
 }
 
 
@@ -119,6 +133,12 @@ def _battery():
         ("pbwd_autograd", lambda: pbpins.test_matches_torch_autograd(oracle, 4, False)),
         ("pbwd_autograd_start", lambda: pbpins.test_matches_torch_autograd(oracle, 4, True)),
         ("pbwd_token_sum", lambda: pbpins.test_token_eta_gradients_sum_to_head_gradient(oracle, False)),
+        ("mom_worked", lambda: mpins.test_momentum_worked_examples_exact(oracle)),
+        ("mom_heavy_ball", lambda: mpins.test_heavy_ball_closed_form(oracle, 0.1, 0.5)),
+        ("mom_beta0_online", lambda: mpins.test_beta_zero_exact_steps_is_online_gd(oracle, 5)),
+        ("mom_beta0_minibatch", lambda: mpins.test_beta_zero_chunk_start_is_minibatch(oracle, 4)),
+        ("mom_autograd_exact", lambda: mpins.test_momentum_matches_autograd(oracle, 0, 6)),
+        ("mom_autograd_start", lambda: mpins.test_momentum_matches_autograd(oracle, 1, 6)),
     ]
     for name, fn in checks:
         try:
