@@ -373,6 +373,66 @@ int ttt_linear_decode_step_ex(const void* q, const void* k, const void* v, int q
  */
 int ttt_linear_segments(int64_t B, int64_t H, int64_t T, int d, int b, int qkv_dtype);
 
+/*
+ * TTT-Linear with momentum gradient descent.  The E2-TTT write-up
+ * (zhichai.net), sections "E2-TTT's Breakthrough: A Closed-Form Solution"
+ * and "Core Math (Simplified)": fast weights W and a momentum M of the same
+ * shape, one step per token t on the loss above,
+ *     r_t = k_t W_g - v_t,  M_t = beta_h M_{t-1} + k_t^T r_t,
+ *     W_t = W_{t-1} - eta_h M_t,  y_t = q_t W_t,
+ * with the gradient point W_g chosen by grad_mode:
+ *   0  W_g = W_{t-1}: exact token-level steps (with beta = 0, exact online
+ *      gradient descent, the same result as ttt_linear_forward with b = 1);
+ *   1  W_g = the weights at the start of the token's mini-batch of b tokens
+ *      (the chunk-start gradients of the section "The Curse of Efficiency";
+ *      with beta = 0 the result of ttt_linear_forward with the same b).
+ * The kernels run each mini-batch in a closed form: for exact steps the
+ * residuals R of the chunk solve a unit lower triangular system built from
+ * K K^T (one forward substitution per chunk), and the chunk-end W and M
+ * follow from R with geometric sums of beta.  So b sets only the work split
+ * when grad_mode = 0 (the result is the same up to rounding for every b).
+ *
+ *   Q, K, V, Y   as for ttt_linear_forward.
+ *   W0           fp32, [H][d][d] (w0_per_batch = 0) or [B][H][d][d] (= 1).
+ *   M0           fp32 [B][H][d][d] start momentum, or NULL for zero.
+ *   eta, beta    fp32 [H]: learning rate and momentum coefficient per head.
+ *   grad_mode    0 or 1 (above).
+ *   W_out, M_out fp32 [B][H][d][d]: the weights and momentum after the last
+ *                token.  W_out may be W0 when w0_per_batch = 1, and M_out may
+ *                be M0 (in-place state update); no other overlap between an
+ *                output and any argument is allowed.
+ *   B, H, T, d   as for ttt_linear_forward; T = 0 writes W_out = W0 and
+ *                M_out = M0 (or zero).
+ *   b            1 <= b <= 64.  bf16 Q/K/V with d = 64 and b = 16 run the
+ *                MFMA kernels; other shapes run a plain fp32 kernel whose
+ *                on-chip memory bounds b for d = 128 (b <= 20, else
+ *                TTT_ERR_UNSUPPORTED).
+ *   workspace    caller-owned device memory of at least
+ *                ttt_linear_momentum_workspace_bytes for these sizes (the
+ *                per-chunk triangular inverses of exact steps on the MFMA
+ *                path; 0 bytes elsewhere); must not overlap any other
+ *                argument.
+ *
+ * Errors: TTT_ERR_INVALID_ARG (null or overlapping buffers, grad_mode not 0
+ * or 1, a workspace smaller than required), TTT_ERR_UNSUPPORTED (sizes as for
+ * ttt_linear_forward, or on-chip memory), TTT_ERR_HIP.
+ */
+int ttt_linear_momentum_forward(const void* Q, const void* K, const void* V, int qkv_dtype,
+                                const float* W0, int w0_per_batch, const float* M0,
+                                const float* eta, const float* beta, int grad_mode,
+                                int64_t B, int64_t H, int64_t T, int d, int b,
+                                void* Y, float* W_out, float* M_out,
+                                void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * Workspace bytes ttt_linear_momentum_forward needs for these sizes:
+ * B*H*ceil(T/32)*1024 for exact steps on the MFMA path (one 16x16 bf16
+ * inverse per chunk of 16 tokens, stored in pairs), else 0.  Negative ttt_status for sizes the call
+ * would reject.
+ */
+int64_t ttt_linear_momentum_workspace_bytes(int64_t B, int64_t H, int64_t T, int d, int b,
+                                            int qkv_dtype, int grad_mode);
+
 /* Static, human-readable text for a status code (never NULL). */
 const char* ttt_status_string(int status);
 

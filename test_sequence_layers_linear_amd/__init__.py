@@ -81,6 +81,11 @@ def load_library():
     lib.ttt_linear_workspace_bytes.restype = L
     lib.ttt_linear_backward_workspace_bytes.argtypes = [L, L, L, I, I, I]
     lib.ttt_linear_backward_workspace_bytes.restype = L
+    lib.ttt_linear_momentum_forward.argtypes = [P, P, P, I, P, I, P, P, P, I, L, L, L, I, I,
+                                                P, P, P, P, L, P]
+    lib.ttt_linear_momentum_forward.restype = I
+    lib.ttt_linear_momentum_workspace_bytes.argtypes = [L, L, L, I, I, I, I]
+    lib.ttt_linear_momentum_workspace_bytes.restype = L
     lib.ttt_status_string.argtypes = [I]
     lib.ttt_status_string.restype = ctypes.c_char_p
     lib.ttt_abi_version.argtypes = []
@@ -456,6 +461,66 @@ def ttt_linear_decode_step_ex(q, k, v, W, eta, eta_tok=None, ln_q=None, ln_k=Non
     return y
 
 
+def ttt_linear_momentum_forward(Q, K, V, W0, eta, beta, b: int = 16, M0=None, grad_mode: int = 0,
+                                Y=None, W_out=None, M_out=None, workspace=None, stream=None):
+    """TTT-Linear with momentum gradient descent.  Q,K,V [B,H,T,d] fp32/bf16;
+    W0 fp32 [H,d,d] or [B,H,d,d]; M0 fp32 [B,H,d,d] or None (zero); eta,
+    beta fp32 [H]; grad_mode 0 (exact token steps) or 1 (chunk-start
+    gradients).  workspace: uint8 device tensor (None: one of
+    ttt_linear_momentum_workspace_bytes bytes is allocated with torch).
+    Returns (Y, W_out, M_out)."""
+    lib = load_library()
+    if Q.dim() != 4:
+        raise ValueError("Q must be [B,H,T,d]")
+    dev = Q.device
+    B, H, T, d = Q.shape
+    for t, n in ((Q, "Q"), (K, "K"), (V, "V")):
+        _need(t, n, dev, Q.dtype)
+        if t.shape != Q.shape:
+            raise ValueError(f"{n} shape {tuple(t.shape)} != Q shape {tuple(Q.shape)}")
+    for t, n in ((W0, "W0"), (eta, "eta"), (beta, "beta")):
+        _need(t, n, dev, torch.float32)
+    per_batch = W0.dim() == 4
+    if W0.shape != ((B, H, d, d) if per_batch else (H, d, d)) or eta.shape != (H,) \
+            or beta.shape != (H,):
+        raise ValueError("W0 must be [H,d,d] or [B,H,d,d], eta and beta [H]")
+    if M0 is not None:
+        _need(M0, "M0", dev, torch.float32)
+        if M0.shape != (B, H, d, d):
+            raise ValueError("M0 must be [B,H,d,d]")
+    if Y is None:
+        Y = torch.empty_like(Q)
+    if W_out is None:
+        W_out = torch.empty((B, H, d, d), device=dev, dtype=torch.float32)
+    if M_out is None:
+        M_out = torch.empty((B, H, d, d), device=dev, dtype=torch.float32)
+    _need(Y, "Y", dev, Q.dtype)
+    _need(W_out, "W_out", dev, torch.float32)
+    _need(M_out, "M_out", dev, torch.float32)
+    code = _dtype_code(Q)
+    ws = _workspace(lib.ttt_linear_momentum_workspace_bytes(B, H, T, d, int(b), code,
+                                                            int(grad_mode))
+                    if workspace is None else 0, dev, workspace)
+    _check(lib.ttt_linear_momentum_forward(Q.data_ptr(), K.data_ptr(), V.data_ptr(), code,
+                                           W0.data_ptr(), int(per_batch),
+                                           None if M0 is None else M0.data_ptr(),
+                                           eta.data_ptr(), beta.data_ptr(), int(grad_mode),
+                                           B, H, T, d, int(b), Y.data_ptr(), W_out.data_ptr(),
+                                           M_out.data_ptr(), *_ws_args(ws),
+                                           _stream_handle(dev, stream)))
+    return Y, W_out, M_out
+
+
+def ttt_linear_momentum_workspace_bytes(B: int, H: int, T: int, d: int, b: int,
+                                        dtype=torch.bfloat16, grad_mode: int = 0) -> int:
+    """Workspace bytes ttt_linear_momentum_forward needs for these sizes."""
+    code = TTT_F32 if dtype == torch.float32 else TTT_BF16
+    n = load_library().ttt_linear_momentum_workspace_bytes(int(B), int(H), int(T), int(d),
+                                                           int(b), code, int(grad_mode))
+    _check(min(n, 0))
+    return n
+
+
 def ttt_linear_segments(B: int, H: int, T: int, d: int, b: int, dtype=torch.bfloat16) -> int:
     """Sequence segments ttt_linear_forward cuts each chain into for these
     sizes on the current device (1 = unsegmented)."""
@@ -500,7 +565,8 @@ __all__ = [
     "ttt_mlp_forward", "ttt_linear_decode_step",
     "ttt_linear_decode_step_ex", "ttt_linear_backward",
     "ttt_linear_segments", "ttt_linear_backward_segments", "ttt_linear_workspace_bytes",
-    "ttt_linear_backward_workspace_bytes",
+    "ttt_linear_backward_workspace_bytes", "ttt_linear_momentum_forward",
+    "ttt_linear_momentum_workspace_bytes",
     "load_library",
     "status_string", "TTTError", "LIB_PATH", "TTT_F32", "TTT_BF16",
 ]

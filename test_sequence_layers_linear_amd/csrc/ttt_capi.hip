@@ -18,8 +18,9 @@ namespace {
 using ttt::LinearArgs;
 using ttt::MlpArgs;
 using ttt::DecodeArgs;
+using ttt::MomentumArgs;
 
-constexpr int kAbiVersion = (2 << 16) | 0;
+constexpr int kAbiVersion = (2 << 16) | 1;
 
 bool valid_dtype(int dt) { return dt == TTT_F32 || dt == TTT_BF16; }
 size_t elem_bytes(int dt) { return dt == TTT_F32 ? 4 : 2; }
@@ -652,6 +653,78 @@ int ttt_linear_decode_step_ex(const void* q, const void* k, const void* v, int q
     pro.ln_eps = ln_eps;
     pro.read_start = read_mode;
     return decode_impl(q, k, v, qkv_dtype, W, eta, B, H, d, y, stream, pro);
+}
+
+}  // extern "C"
+
+namespace {
+
+// The launch configuration a momentum forward of these sizes takes:
+// workspace bytes it needs, or a negative ttt_status.
+int64_t momentum_plan(const MomentumArgs& a)
+{
+    if (const int st = linear_sizes_status(a.B, a.H, a.T, a.d, a.b, a.dtype)) return st;
+    if (a.grad_mode != 0 && a.grad_mode != 1) return TTT_ERR_INVALID_ARG;
+    if (ttt::momentum_mfma_supports(a)) return ttt::momentum_mfma_workspace_bytes(a);
+    if (ttt::momentum_generic_lds_bytes(a.d, a.b) > static_cast<size_t>(ttt::kMaxLdsBytes))
+        return TTT_ERR_UNSUPPORTED;
+    return 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ttt_linear_momentum_forward(const void* Q, const void* K, const void* V, int qkv_dtype,
+                                const float* W0, int w0_per_batch, const float* M0,
+                                const float* eta, const float* beta, int grad_mode,
+                                int64_t B, int64_t H, int64_t T, int d, int b,
+                                void* Y, float* W_out, float* M_out,
+                                void* workspace, int64_t workspace_bytes, void* stream)
+{
+    if (w0_per_batch != 0 && w0_per_batch != 1) return TTT_ERR_INVALID_ARG;
+    if (workspace_bytes < 0 || (workspace_bytes > 0 && !workspace)) return TTT_ERR_INVALID_ARG;
+    MomentumArgs a{Q, K, V, qkv_dtype, W0, w0_per_batch, M0, eta, beta, grad_mode,
+                   B, H, T, d, b, Y, W_out, M_out, static_cast<hipStream_t>(stream)};
+    const int64_t need = momentum_plan(a);
+    if (need < 0) return static_cast<int>(need);
+    const int64_t units = B * H;
+    if (units == 0) return TTT_OK;
+    if (!W0 || !eta || !beta || !W_out || !M_out) return TTT_ERR_INVALID_ARG;
+    if (T > 0 && (!Q || !K || !V || !Y)) return TTT_ERR_INVALID_ARG;
+    if (workspace_bytes < need) return TTT_ERR_INVALID_ARG;
+
+    const int64_t n_qkv = units * T * d * static_cast<int64_t>(elem_bytes(qkv_dtype));
+    const int64_t n_state = static_cast<int64_t>(d) * d * 4;
+    const Range rQ{Q, T ? n_qkv : 0}, rK{K, T ? n_qkv : 0}, rV{V, T ? n_qkv : 0};
+    const Range rY{Y, T ? n_qkv : 0};
+    const Range rW0{W0, (w0_per_batch ? units : H) * n_state}, rM0{M0, M0 ? units * n_state : 0};
+    const Range rWo{W_out, units * n_state}, rMo{M_out, units * n_state};
+    const Range rEta{eta, H * 4}, rBeta{beta, H * 4}, rWs{workspace, workspace_bytes};
+    for (const Range& in : {rQ, rK, rV, rW0, rM0, rEta, rBeta, rWo, rMo, rWs})
+        if (overlap(rY, in)) return TTT_ERR_INVALID_ARG;
+    for (const Range& in : {rQ, rK, rV, rEta, rBeta, rMo, rWs})
+        if (overlap(rWo, in)) return TTT_ERR_INVALID_ARG;
+    for (const Range& in : {rQ, rK, rV, rEta, rBeta, rW0, rWs})
+        if (overlap(rMo, in)) return TTT_ERR_INVALID_ARG;
+    if (overlap(rWo, rW0) && !(w0_per_batch && static_cast<const void*>(W_out) == W0))
+        return TTT_ERR_INVALID_ARG;
+    if (overlap(rWo, rM0) || (overlap(rMo, rM0) && M_out != M0)) return TTT_ERR_INVALID_ARG;
+    for (const Range& in : {rQ, rK, rV, rW0, rM0, rEta, rBeta})
+        if (overlap(rWs, in)) return TTT_ERR_INVALID_ARG;
+
+    if (ttt::momentum_mfma_supports(a)) return hip_status(ttt::launch_momentum_mfma(a, workspace));
+    return hip_status(ttt::launch_momentum_generic(a));
+}
+
+int64_t ttt_linear_momentum_workspace_bytes(int64_t B, int64_t H, int64_t T, int d, int b,
+                                            int qkv_dtype, int grad_mode)
+{
+    MomentumArgs a{};
+    a.dtype = qkv_dtype;
+    a.grad_mode = grad_mode;
+    a.B = B; a.H = H; a.T = T; a.d = d; a.b = b;
+    return momentum_plan(a);
 }
 
 }  // extern "C"

@@ -296,4 +296,23 @@ hipError_t launch_linear_backward(const LinearBwdArgs& a, const SegmentPlan& p, 
 // Decode step.
 hipError_t launch_decode(const DecodeArgs& a);
 
+// TTT-Linear with momentum gradient descent (ttt_momentum.hip): grad_mode 0
+// takes each token's gradient at the current weights (exact token steps),
+// 1 at the chunk start; M0 null means a zero start momentum.
+struct MomentumArgs {
+    const void* Q; const void* K; const void* V; int dtype;
+    const float* W0; int w0_per_batch; const float* M0;
+    const float* eta; const float* beta; int grad_mode;
+    int64_t B, H, T; int d, b;
+    void* Y; float* W_out; float* M_out; hipStream_t stream;
+};
+size_t momentum_generic_lds_bytes(int d, int b);
+hipError_t launch_momentum_generic(const MomentumArgs& a);
+// bf16 d = 64, b = 16 on MFMA (ttt_momentum_mfma.hip).  Exact token steps
+// need a workspace of momentum_mfma_workspace_bytes for the per-chunk
+// triangular inverses.
+bool momentum_mfma_supports(const MomentumArgs& a);
+int64_t momentum_mfma_workspace_bytes(const MomentumArgs& a);
+hipError_t launch_momentum_mfma(const MomentumArgs& a, void* workspace);
+
 }  // namespace ttt

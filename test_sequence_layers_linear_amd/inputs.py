@@ -30,6 +30,11 @@ N(0, 0.1^2) per head for q and for k, and per-token step sizes
 eta_t ~ U[0.1/d, 0.6/d] (LayerNorm'd keys have |k|^2 about d, so eta_t |k|^2
 stays below 1 and each step contracts).
 
+Momentum (make_momentum): a momentum coefficient per head beta_h ~ U[0, 0.9]
+(the E2-TTT write-up names the coefficient but gives no value; 0.9 is the
+largest, with 1/(1 - beta) = 10 the largest step amplification), optionally
+a start momentum M0 ~ N(0, 0.02^2) per chain.
+
 Generator: numpy.random.default_rng(seed), float32 standard normals scaled in
 float32, then cast to the input dtype (bf16 by round-to-nearest-even through
 torch).  Draw order: Q, K, V, initial state (W0, or W1 then W2), eta, then the
@@ -166,6 +171,15 @@ def make_prologue(w: Workload, seed: int, device="cpu") -> dict:
     out["eta_tok"] = torch.from_numpy(rng.uniform(lo, hi, size=(w.B, w.H, w.T)).astype(np.float32))
     out["eta"] = torch.from_numpy(rng.uniform(lo, hi, size=(w.H,)).astype(np.float32))
     return {k: v.to(device) for k, v in out.items()}
+
+
+def make_momentum(w: Workload, seed: int, device="cpu", m0: bool = False) -> dict:
+    """Seeded momentum parameters for a TTT-Linear workload: beta [H] fp32
+    and, with ``m0``, a start momentum M0 [B,H,d,d] fp32 (else None)."""
+    rng = np.random.default_rng(seed)
+    out = {"beta": torch.from_numpy(rng.uniform(0.0, 0.9, size=(w.H,)).astype(np.float32))}
+    out["M0"] = torch.from_numpy(_normal(rng, (w.B, w.H, w.d, w.d), 0.02)) if m0 else None
+    return {k: (v.to(device) if v is not None else None) for k, v in out.items()}
 
 
 def default_seed(config: int) -> int:

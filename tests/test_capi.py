@@ -342,3 +342,50 @@ def test_noalloc_validation_and_limit(lib, monkeypatch):
     # 30 forced segments of 48 chains: 48 * 88 matrices of 16 KB = 69 MB > 16 MiB
     monkeypatch.setenv("TTT_LINEAR_SEGMENTS", "30")
     assert na() == UNSUPPORTED
+
+
+MOA, M0A, BETA = (0xD0_0000_0000 + 0x10_0000_0000 * i for i in range(3))
+
+
+def mom(lib, Q=QA, K=KA, V=VA, dt=1, W0=W0A, pb=0, M0=M0A, eta=ETA, beta=BETA, gm=0, B=2, H=3,
+        T=64, d=64, b=16, Y=YA, Wo=WOA, Mo=MOA, ws=WSA, wsb=1 << 20):
+    return lib.ttt_linear_momentum_forward(Q, K, V, dt, W0, pb, M0, eta, beta, gm, B, H, T, d, b,
+                                           Y, Wo, Mo, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(B=-1), INVALID), (dict(T=-1), INVALID), (dict(b=0), INVALID), (dict(pb=2), INVALID),
+    (dict(gm=2), INVALID), (dict(gm=-1), INVALID),
+    (dict(Q=None), INVALID), (dict(Y=None), INVALID), (dict(W0=None), INVALID),
+    (dict(eta=None), INVALID), (dict(beta=None), INVALID), (dict(Wo=None), INVALID),
+    (dict(Mo=None), INVALID),
+    (dict(d=48), UNSUPPORTED), (dict(b=65), UNSUPPORTED), (dict(dt=5), UNSUPPORTED),
+    (dict(d=128, b=21, dt=0), UNSUPPORTED), (dict(T=2**31), UNSUPPORTED),
+    # overlaps: outputs with inputs, the two outputs, the workspace
+    (dict(Y=QA), INVALID), (dict(Mo=KA), INVALID), (dict(Mo=WOA + 64), INVALID),
+    (dict(Wo=M0A), INVALID), (dict(Mo=BETA), INVALID), (dict(Wo=BETA - 4), INVALID),
+    (dict(ws=VA), INVALID), (dict(ws=MOA - 64), INVALID), (dict(ws=M0A), INVALID),
+    (dict(Mo=M0A + 4), INVALID), (dict(Wo=W0A), INVALID),
+    (dict(wsb=-1), INVALID), (dict(ws=None, wsb=16), INVALID),
+    # in place: W_out = W0 (per batch), M_out = M0; no start momentum
+    (dict(Wo=W0A, pb=1, B=0), OK), (dict(M0=None, B=0), OK), (dict(B=0, Q=None), OK),
+])
+def test_momentum_validation(lib, kw, expect):
+    assert mom(lib, **kw) == expect
+
+
+def test_momentum_workspace_query(lib):
+    q = lib.ttt_linear_momentum_workspace_bytes
+    assert q(-1, 3, 64, 64, 16, 1, 0) == INVALID
+    assert q(1, 3, 64, 64, 16, 1, 2) == INVALID
+    assert q(1, 3, 64, 48, 16, 1, 0) == UNSUPPORTED
+    assert q(1, 3, 64, 128, 32, 0, 0) == UNSUPPORTED
+    for args in ((1, 3, 64, 64, 16, 1, 1), (1, 3, 64, 64, 16, 0, 0), (1, 3, 64, 32, 16, 1, 0),
+                 (1, 3, 64, 64, 8, 1, 0)):
+        assert q(*args) == 0          # chunk-start gradients, or the plain fp32 kernel
+    # exact steps on the bf16 MFMA path: 512-byte inverses, one per chunk of 16
+    # tokens, stored in pairs (T = 100: 7 chunks in 4 pairs)
+    assert q(2, 3, 100, 64, 16, 1, 0) == 6 * 4 * 1024
+    assert q(0, 3, 100, 64, 16, 1, 0) == 0
+    # one byte short of that is rejected before any launch
+    assert mom(lib, B=2, H=3, T=100, ws=WSA, wsb=6 * 4 * 1024 - 1) == INVALID

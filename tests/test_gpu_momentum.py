@@ -1,0 +1,169 @@
+"""GPU parity of ttt_linear_momentum_forward against the fp64 oracle
+(oracle.linear_momentum: momentum gradient descent token by token).
+
+Relative-L2 comparison of Y, W_out and M_out on the same seeded inputs:
+within 1e-4 for fp32 Q/K/V and 2e-2 for bf16 Q/K/V (fp32 state), for both
+gradient points (exact token steps, chunk-start gradients).  Small cases span
+several chunks and a ragged tail on both kernels (MFMA: bf16, d = 64, b = 16;
+plain fp32 kernel: every other shape); the 96-chain workload runs at full
+size, every chain, in the launch configuration the benchmark times.
+"""
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import test_sequence_layers_linear_amd as ttt
+from parity_util import TOL, WORKLOADS, announce, default_seed, make_inputs, rel_l2, to_gpu
+from test_sequence_layers_linear_amd.inputs import make_momentum
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(inp, mom, b, grad_mode, dtype, tol=None):
+    tol = TOL[dtype] if tol is None else tol
+    g = to_gpu(inp)
+    M0 = None if mom["M0"] is None else mom["M0"].cuda()
+    Y, W, M = ttt.ttt_linear_momentum_forward(g["Q"], g["K"], g["V"], g["W0"], g["eta"],
+                                              mom["beta"].cuda(), b, M0, grad_mode)
+    torch.cuda.synchronize()
+    Yr, Wr, Mr = oracle.linear_momentum(inp["Q"], inp["K"], inp["V"], inp["W0"], inp["eta"],
+                                        mom["beta"], b, mom["M0"], grad_mode)
+    ey, ew, em = rel_l2(Y, Yr), rel_l2(W, Wr), rel_l2(M, Mr)
+    print(f"  rel-L2 Y {ey:.3e}  W {ew:.3e}  M {em:.3e}", flush=True)
+    assert ey <= tol and ew <= tol and em <= tol, (ey, ew, em)
+    return Y, W, M
+
+
+@pytest.mark.parametrize("grad_mode", [0, 1])
+def test_momentum_config3_full(grad_mode):
+    """B8 H12 T2048 bf16, d = 64, b = 16: all 96 chains, whole tensors."""
+    w = WORKLOADS[3]
+    announce("momentum config 3, all chains, grad_mode", grad_mode)
+    inp = make_inputs(w, default_seed(3))
+    _run(inp, make_momentum(w, 31), w.b, grad_mode, "bf16")
+
+
+@pytest.mark.parametrize("grad_mode", [0, 1])
+def test_momentum_config2_fp32(grad_mode):
+    """B1 H4 T2048 fp32 on the plain fp32 kernel, within 1e-4."""
+    w = WORKLOADS[2]
+    announce("momentum config 2 fp32, grad_mode", grad_mode)
+    _run(make_inputs(w, default_seed(2)), make_momentum(w, 32, m0=True), w.b, grad_mode, "fp32")
+
+
+@pytest.mark.parametrize("grad_mode", [0, 1])
+@pytest.mark.parametrize("B,H,T", [(1, 1, 1), (1, 1, 5), (1, 1, 16), (1, 1, 17), (2, 3, 48),
+                                   (1, 7, 257), (2, 2, 1000)])
+def test_momentum_mfma_shapes(B, H, T, grad_mode):
+    w = WORKLOADS[3].with_(B=B, H=H, T=T)
+    announce("momentum mfma", B, H, T, grad_mode)
+    _run(make_inputs(w, 40 + T), make_momentum(w, 41 + T, m0=T % 2 == 1), 16, grad_mode, "bf16")
+
+
+@pytest.mark.parametrize("grad_mode", [0, 1])
+@pytest.mark.parametrize("d,b,dtype", [(16, 16, "fp32"), (32, 7, "fp32"), (64, 16, "fp32"),
+                                       (128, 16, "fp32"), (64, 1, "fp32"), (32, 64, "fp32"),
+                                       (16, 16, "bf16"), (128, 16, "bf16"), (64, 8, "bf16"),
+                                       (64, 32, "bf16")])
+def test_momentum_generic_shapes(d, b, dtype, grad_mode):
+    w = WORKLOADS[2].with_(B=2, H=3, T=3 * b + 5, d=d, b=b, dtype=dtype,
+                           eta=("uniform", 0.01, 0.1))
+    announce("momentum generic", d, b, dtype, grad_mode)
+    _run(make_inputs(w, 200 + d + b), make_momentum(w, 201 + d, m0=True), b, grad_mode, dtype)
+
+
+@pytest.mark.parametrize("cfg", [2, 3])
+def test_beta_zero_chunk_start_matches_linear_forward(cfg):
+    """beta = 0 with chunk-start gradients is the mini-batch scan of
+    ttt_linear_forward: the two entry points agree within the tolerance."""
+    w = WORKLOADS[cfg].with_(B=2, H=3, T=300)
+    announce("momentum beta=0 vs linear forward", cfg)
+    g = to_gpu(make_inputs(w, 50 + cfg))
+    beta = torch.zeros(w.H, device="cuda")
+    Y, W, _ = ttt.ttt_linear_momentum_forward(g["Q"], g["K"], g["V"], g["W0"], g["eta"], beta,
+                                              16, None, 1)
+    Yl, Wl = ttt.ttt_linear_forward(g["Q"], g["K"], g["V"], g["W0"], g["eta"], 16)
+    torch.cuda.synchronize()
+    tol = TOL[w.dtype]
+    assert rel_l2(Y, Yl.double().cpu().numpy()) <= tol
+    assert rel_l2(W, Wl.double().cpu().numpy()) <= tol
+
+
+def test_momentum_empty_sequence_copies_state():
+    w = WORKLOADS[3].with_(B=2, H=3, T=0)
+    g = to_gpu(make_inputs(w, 5))
+    mom = make_momentum(w, 6, m0=True)
+    Y, W, M = ttt.ttt_linear_momentum_forward(g["Q"], g["K"], g["V"], g["W0"], g["eta"],
+                                              mom["beta"].cuda(), 16, mom["M0"].cuda(), 0)
+    torch.cuda.synchronize()
+    assert Y.shape == (2, 3, 0, 64)
+    assert torch.equal(W, g["W0"][None].expand(2, 3, 64, 64))
+    assert torch.equal(M.cpu(), mom["M0"])
+    _, _, Mz = ttt.ttt_linear_momentum_forward(g["Q"], g["K"], g["V"], g["W0"], g["eta"],
+                                               mom["beta"].cuda(), 16, None, 0)
+    torch.cuda.synchronize()
+    assert not Mz.any()
+
+
+@pytest.mark.parametrize("cfg,grad_mode", [(3, 0), (3, 1), (2, 0)])
+def test_momentum_chaining_in_place(cfg, grad_mode):
+    """Two calls that resume from (W_out, M_out), updated in place, continue
+    the sequence: they match one call over all the tokens."""
+    w = WORKLOADS[cfg].with_(B=2, H=3, T=320)
+    announce("momentum chaining", cfg, grad_mode)
+    inp = make_inputs(w, 60 + cfg, w0_per_batch=True)
+    g = to_gpu(inp)
+    beta = make_momentum(w, 61)["beta"].cuda()
+    Y, W, M = ttt.ttt_linear_momentum_forward(g["Q"], g["K"], g["V"], g["W0"], g["eta"], beta,
+                                              16, None, grad_mode)
+    Ws = g["W0"].clone()
+    Ms = torch.zeros_like(Ws)
+    Ys = []
+    for lo, hi in ((0, 160), (160, 320)):
+        sl = [x[:, :, lo:hi].contiguous() for x in (g["Q"], g["K"], g["V"])]
+        Yp, _, _ = ttt.ttt_linear_momentum_forward(*sl, Ws, g["eta"], beta, 16, Ms, grad_mode,
+                                                   W_out=Ws, M_out=Ms)
+        Ys.append(Yp)
+    torch.cuda.synchronize()
+    tol = TOL[w.dtype]
+    assert rel_l2(torch.cat(Ys, dim=2), Y.double().cpu().numpy()) <= tol
+    assert rel_l2(Ws, W.double().cpu().numpy()) <= tol
+    assert rel_l2(Ms, M.double().cpu().numpy()) <= tol
+
+
+@pytest.mark.parametrize("path", ["generic_fp32", "mfma_bf16"])
+def test_momentum_worked_examples_bit_exact(path):
+    """The hand-worked d = 2 examples embedded by zero padding; every value
+    is dyadic with few bits, so both kernels reproduce them exactly."""
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden",
+                                    "momentum_d2_worked.json")))
+    eta = torch.tensor([float(Fraction(g["eta"]))]).cuda()
+    beta = torch.tensor([float(Fraction(g["beta"]))]).cuda()
+    fr = lambda rows: torch.tensor([[float(Fraction(x)) for x in r] for r in rows])
+    for case in g["cases"]:
+        if path == "mfma_bf16":
+            if case["grad_mode"] == 1 and case["b"] < 2:
+                continue      # b = 16 covers both tokens in one chunk: only b >= T matches
+            d, b, dtype = 64, 16, torch.bfloat16
+        else:
+            d, b, dtype = 16, case["b"], torch.float32
+
+        def pad(rows):
+            x = torch.zeros(1, 1, 2, d)
+            x[0, 0, :, :2] = torch.tensor(rows, dtype=torch.float32)
+            return x.to(dtype).cuda()
+        M0 = torch.zeros(1, 1, d, d)
+        M0[0, 0, :2, :2] = fr(case["M0"])
+        Y, W, M = ttt.ttt_linear_momentum_forward(pad(g["q"]), pad(g["k"]), pad(g["v"]),
+                                                  torch.zeros(1, d, d).cuda(), eta, beta, b,
+                                                  M0.cuda(), case["grad_mode"])
+        torch.cuda.synchronize()
+        assert torch.equal(Y[0, 0, :, :2].float().cpu(), fr(case["Y"])), case
+        assert torch.equal(W[0, 0, :2, :2].cpu(), fr(case["W"])), case
+        assert torch.equal(M[0, 0, :2, :2].cpu(), fr(case["M"])), case
+        assert not Y[0, 0, :, 2:].float().any() and not W[0, 0, 2:].any()
