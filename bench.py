@@ -38,6 +38,10 @@ inputs run on bf16 MFMA, fp32 inputs on fp32 MFMA).  It is reported beside the f
 headline value.  "prologue" times ttt_linear_forward_ex on the same inputs
 with LayerNorm of q and k and a step size per token fused into the scan, and
 "backward_prologue" ttt_linear_backward_ex, the backward through them.
+The bf16 TTT-Linear workloads also report "momentum": ttt_linear_momentum_forward
+(momentum gradient descent, beta per head from make_momentum) on the same
+inputs, for exact token steps and for chunk-start gradients, each timed with
+the cache flushed and back to back, with its own roofline object.
 """
 from __future__ import annotations
 
@@ -77,6 +81,9 @@ KERNEL_SOURCES = {
     "mlp_generic_kernel": "ttt_generic.hip",
     "mlp_mfma_kernel": "ttt_mlp_mfma.hip",
     "decode_kernel": "ttt_decode.hip",
+    "momentum_inverse_kernel": "ttt_momentum_mfma.hip",
+    "momentum_mfma_kernel[exact]": "ttt_momentum_mfma.hip",
+    "momentum_mfma_kernel[chunk_start]": "ttt_momentum_mfma.hip",
 }
 
 
@@ -116,6 +123,21 @@ def mlp_work(w):
     d, m, units = w.d, w.m, w.B * w.H
     flops = units * sum(14 * n * d * m + 4 * n * n * d + 4 * n * n * m for n in _chunks(w.T, w.b))
     nbytes = units * w.T * 4 * d * s + (w.H + units) * 2 * d * m * 4
+    return flops, nbytes
+
+
+def momentum_work(w, exact):
+    """flops and HBM bytes of one ttt_linear_momentum_forward call.  Per chunk
+    of n tokens: K W, K M (exact steps only), Q W, Q M and the two state
+    updates -- 2 n d^2 each -- and S = Q K^T, S R, plus for exact steps K K^T
+    and P RHS -- 2 n^2 d each.  Bytes: Q, K, V read, Y written, W0 once and
+    W_out, M_out written (the per-chunk inverses that the first launch writes
+    and the scan reads are extra traffic, not algorithmic)."""
+    s = 4 if w.dtype == "fp32" else 2
+    d, units = w.d, w.B * w.H
+    nd2, n2d = (6, 4) if exact else (5, 2)
+    flops = units * sum(2 * nd2 * n * d * d + 2 * n2d * n * n * d for n in _chunks(w.T, w.b))
+    nbytes = units * w.T * 4 * d * s + w.H * d * d * 4 + 2 * units * d * d * 4
     return flops, nbytes
 
 
@@ -433,6 +455,46 @@ class Runner:
         torch.cuda.synchronize()
         return start.elapsed_time(end) / 1e3 / steps
 
+    def measure_momentum(self, steps, warmup, grad_mode, cold_reps):
+        """ttt_linear_momentum_forward: (mean back to back over `steps` calls,
+        mean with the last-level cache flushed before each of `cold_reps`
+        calls)."""
+        torch, g, w = self.torch, self.g, self.w
+        from test_sequence_layers_linear_amd.inputs import make_momentum
+        beta = make_momentum(w, 31)["beta"].cuda()
+        M = torch.empty_like(self.W)
+        ws = torch.empty(self.ttt.ttt_linear_momentum_workspace_bytes(w.B, w.H, w.T, w.d, w.b,
+                                                                      w.torch_dtype, grad_mode),
+                         dtype=torch.uint8, device="cuda")
+
+        def call():
+            self.ttt.ttt_linear_momentum_forward(g["Q"], g["K"], g["V"], g["W0"], g["eta"], beta,
+                                                 w.b, None, grad_mode, Y=self.Y, W_out=self.W,
+                                                 M_out=M, workspace=ws)
+        for _ in range(warmup):
+            call()
+        torch.cuda.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record()
+        for _ in range(steps):
+            call()
+        end.record()
+        torch.cuda.synchronize()
+        warm = start.elapsed_time(end) / 1e3 / steps
+        junk = torch.empty(512 * 1024 * 1024 // 4, device="cuda")
+        times = []
+        for _ in range(cold_reps):
+            junk.fill_(1.0)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            call()
+            b.record()
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b) / 1e3)
+        del junk, ws
+        return warm, sum(times) / len(times)
+
     def measure_cold(self, reps):
         """Forward duration with the 256 MB last-level cache flushed (a 512 MB
         buffer written) before each call: (mean, median) over `reps` calls."""
@@ -546,6 +608,16 @@ def measure_workload(cfg, steps, warmup, cold_reps, roofs=None):
         bpt = r.measure_backward(max(3, steps // 2), 2, prologue=True)
         out["backward_prologue"] = {"us": bpt * 1e6, "tokens_per_s": w.B * w.T / bpt,
                                     "vs_plain_backward": bpt / bt}
+    if w.kind == "linear" and w.d == 64 and w.b == 16 and w.dtype == "bf16":
+        out["momentum"] = {}
+        for mode, gm in (("exact", 0), ("chunk_start", 1)):
+            warm, cold = r.measure_momentum(max(3, steps // 2), 2, gm, max(3, cold_reps // 3))
+            mf, mb = momentum_work(w, gm == 0)
+            kern = (["momentum_inverse_kernel"] if gm == 0 else []) + [f"momentum_mfma_kernel[{mode}]"]
+            out["momentum"][mode] = {"us": warm * 1e6, "us_cold_llc": cold * 1e6,
+                                     "tokens_per_s": w.B * w.T / warm,
+                                     "roofline": roofline(w, mf, mb, cold, kern, roofs,
+                                                          warm_seconds=warm)}
     if w.decode_steps:
         df, db = decode_work(w)
         per = dec / w.decode_steps

@@ -9,6 +9,14 @@ reports as roofline.traffic.
 FETCH_SIZE and WRITE_SIZE are in KiB per dispatch.  Each is scaled by the
 ratio of the known bytes of the plain 256 MiB device copy in the same run to
 what the same counter reads for that copy.
+
+--sq DIR [DIR ...]: rocprofv3 --pmc runs of SQ counters (any split into
+passes); adds a table of instructions per wave and MFMA utilisation per
+kernel.  SQ_WAVE_CYCLES counts quad-cycles (4 clocks) per wave, and
+SQ_VALU_MFMA_BUSY_CYCLES clocks per SIMD, so the MFMA busy fraction of the
+chip is MFMA_BUSY / (GRBM_GUI_ACTIVE x 1024 SIMDs) (rocprofv3's own derived
+metric) and of a wave's lifetime MFMA_BUSY / (4 x SQ_WAVE_CYCLES) (one wave
+per SIMD).
 """
 from __future__ import annotations
 
@@ -48,6 +56,9 @@ KERNEL_FILES = {
     "mlp_generic_kernel": "ttt_generic.hip",
     "mlp_mfma_kernel": "ttt_mlp_mfma.hip",
     "decode_kernel": "ttt_decode.hip",
+    "momentum_inverse_kernel": "ttt_momentum_mfma.hip",
+    "momentum_mfma_kernel[exact]": "ttt_momentum_mfma.hip",
+    "momentum_mfma_kernel[chunk_start]": "ttt_momentum_mfma.hip",
 }
 COPY_NAME = "__amd_rocclr_copyBuffer"
 
@@ -57,6 +68,8 @@ def short_name(full: str) -> str:
     instantiations of the TTT-Linear forward kernels and [gmaps] / [segments]
     for the backward's cotangent maps and segment backward (+prologue for
     the instantiations with the input prologue)."""
+    if "momentum_mfma_kernel<" in full:      # kExact
+        return "momentum_mfma_kernel[exact]" if "<true>" in full else "momentum_mfma_kernel[chunk_start]"
     for base in ("linear_backward_kernel", "linear_backward_bf16_kernel"):
         if base + "<" in full:
             args = [a.strip() for a in full.split(base + "<", 1)[1].split(">", 1)[0].split(",")]
@@ -96,10 +109,49 @@ def counter_per_kernel(d: str):
     return vals
 
 
+SIMDS = 1024          # 256 CUs x 4 SIMDs
+
+
+def sq_table(dirs, command, chunks_per_wave):
+    """Per-kernel SQ counter summary: mean per dispatch over every run."""
+    per = {}
+    for d in dirs:
+        for r in csv.DictReader(open(one_csv(d, "counter_collection.csv"))):
+            name = short_name(r["Kernel_Name"])
+            if name not in KERNEL_FILES:
+                continue
+            per.setdefault(name, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    out = ["SQ counters (mean per dispatch):", "", "```", command, "```", "",
+           "| kernel | waves | VALU/wave | MFMA/wave | LDS/wave | SALU/wave | VMEM rd/wave | "
+           "wave cycles | MFMA busy, chip | MFMA busy, wave lifetime | wait-inst / wave cycles | "
+           "LDS bank conflicts / LDS inst |" + (" cycles per chunk |" if chunks_per_wave else ""),
+           "|---|" + "---|" * (11 + (1 if chunks_per_wave else 0))]
+
+    for name, c in sorted(per.items()):
+        m = {k: sum(v) / len(v) for k, v in c.items()}
+        waves = m.get("SQ_WAVES", float("nan"))
+        wc = 4 * m.get("SQ_WAVE_CYCLES", float("nan"))
+        busy = m.get("SQ_VALU_MFMA_BUSY_CYCLES", float("nan"))
+        grbm = m.get("GRBM_GUI_ACTIVE", float("nan"))
+        pw = lambda k: m.get(k, float("nan")) / waves
+        row = (f"| {name} | {waves:.0f} | {pw('SQ_INSTS_VALU'):.0f} | {pw('SQ_INSTS_MFMA'):.0f} | "
+               f"{pw('SQ_INSTS_LDS'):.0f} | {pw('SQ_INSTS_SALU'):.0f} | {pw('SQ_INSTS_VMEM_RD'):.0f} | "
+               f"{wc / waves:.0f} | {100 * busy / (grbm * SIMDS):.2f}% | {100 * busy / wc:.1f}% | "
+               f"{m.get('SQ_WAIT_INST_ANY', float('nan')) * 4 / wc:.3f} | "
+               f"{m.get('SQ_LDS_BANK_CONFLICT', float('nan')) / m.get('SQ_INSTS_LDS', float('nan')):.3f} |")
+        if chunks_per_wave:
+            # only for the scans, whose every wave walks its chain's chunks
+            scan = not any(x in name for x in ("inverse", "combine", "maps", "reduce"))
+            row += f" {wc / waves / chunks_per_wave:.0f} |" if scan else " |"
+        out.append(row)
+    out.append("")
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--config", type=int, required=True)
-    ap.add_argument("--trace", required=True)
+    ap.add_argument("--trace", help="rocprofv3 --kernel-trace --stats output (omit: counters only)")
     ap.add_argument("--fetch", help="rocprofv3 --pmc FETCH_SIZE output (omit: no byte counts)")
     ap.add_argument("--write", help="rocprofv3 --pmc WRITE_SIZE output")
     ap.add_argument("--title", help="heading (default: the workload name)")
@@ -110,6 +162,10 @@ def main():
                     help="which call the trace covers (the traffic table keys the kernels of "
                          "any call but the forward under '<workload>/<call>')")
     ap.add_argument("--out", required=True)
+    ap.add_argument("--sq", nargs="*", default=[], help="rocprofv3 --pmc runs of SQ counters")
+    ap.add_argument("--sq-command", default="", help="the commands of the --sq runs")
+    ap.add_argument("--chunks-per-wave", type=float, default=0.0,
+                    help="chunks each wave of the scan processes (for cycles per chunk)")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"))
     args = ap.parse_args()
 
@@ -118,7 +174,7 @@ def main():
     from test_sequence_layers_linear_amd.inputs import WORKLOADS
     w = WORKLOADS[args.config]
 
-    stats = list(csv.DictReader(open(one_csv(args.trace, "kernel_stats.csv"))))
+    stats = list(csv.DictReader(open(one_csv(args.trace, "kernel_stats.csv")))) if args.trace else []
     have_bytes = bool(args.fetch and args.write)
     fetch = counter_per_kernel(args.fetch) if have_bytes else {}
     write = counter_per_kernel(args.write) if have_bytes else {}
@@ -133,8 +189,9 @@ def main():
         lines += [f"Copy calibration ({args.copy_mib} MiB device copy): FETCH_SIZE reads "
                   f"{copy_fetch / 1024:.1f} KiB (scale {f_scale:.3f}), WRITE_SIZE reads "
                   f"{copy_write / 1024:.1f} KiB (scale {w_scale:.3f}).", ""]
-    lines += ["| kernel | calls | avg us | min us | max us | HBM read MB/launch | HBM write MB/launch |",
-              "|---|---|---|---|---|---|---|"]
+    if stats:
+        lines += ["| kernel | calls | avg us | min us | max us | HBM read MB/launch | HBM write MB/launch |",
+                  "|---|---|---|---|---|---|---|"]
     table = json.load(open(args.traffic)) if os.path.exists(args.traffic) else {}
     for r in stats:
         name = short_name(r["Name"])
@@ -155,6 +212,8 @@ def main():
                 "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
                 "avg_us": round(float(r["AverageNs"]) / 1e3, 3)}
     lines.append("")
+    if args.sq:
+        lines += sq_table(args.sq, args.sq_command, args.chunks_per_wave)
     with open(args.out, "w") as f:
         f.write("\n".join(lines))
     with open(args.traffic, "w") as f:

@@ -30,12 +30,15 @@ def main():
     ap.add_argument("--prologue", action="store_true",
                     help="with the input prologue (LayerNorm of q and k, per-token step sizes): "
                          "ttt_linear_forward_ex / ttt_linear_backward_ex")
+    ap.add_argument("--momentum", choices=["exact", "chunk_start"],
+                    help="run ttt_linear_momentum_forward (beta per head from make_momentum) "
+                         "instead of the forward")
     args = ap.parse_args()
 
     import torch
     import test_sequence_layers_linear_amd as ttt
     from test_sequence_layers_linear_amd.inputs import (WORKLOADS, default_seed, make_cotangents,
-                                                        make_inputs, make_prologue)
+                                                        make_inputs, make_momentum, make_prologue)
 
     w = WORKLOADS[args.config]
     g = {k: v.cuda() for k, v in make_inputs(w, default_seed(args.config)).items()}
@@ -51,7 +54,13 @@ def main():
         pro = {k: v.cuda() for k, v in make_prologue(w, 11).items()}
         pkw = {k: pro[k] for k in ("eta_tok", "ln_q", "ln_k")}
     ws = None
-    if w.kind == "linear":
+    gm = 0 if args.momentum == "exact" else 1
+    if args.momentum:
+        beta = make_momentum(w, 31)["beta"].cuda()
+        M = torch.empty_like(W)
+        nbytes = ttt.ttt_linear_momentum_workspace_bytes(w.B, w.H, w.T, w.d, w.b, w.torch_dtype, gm)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    elif w.kind == "linear":
         nbytes = (ttt.ttt_linear_backward_workspace_bytes if args.backward
                   else ttt.ttt_linear_workspace_bytes)(w.B, w.H, w.T, w.d, w.b, w.torch_dtype)
         ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
@@ -60,7 +69,10 @@ def main():
     for _ in range(args.reps):
         if junk is not None:
             junk.fill_(1.0)
-        if args.backward and args.prologue:
+        if args.momentum:
+            ttt.ttt_linear_momentum_forward(g["Q"], g["K"], g["V"], g["W0"], g["eta"], beta, w.b,
+                                            None, gm, Y=Y, W_out=W, M_out=M, workspace=ws)
+        elif args.backward and args.prologue:
             ttt.ttt_linear_backward_ex(g["Q"], g["K"], g["V"], g["W0"], pro["eta"], w.b, cot["dY"],
                                        cot["dW_out"], workspace=ws, **pkw)
         elif args.backward:
