@@ -17,8 +17,10 @@ measured too and reported under "workloads" in the same line.
 
 roofline.achieved = algorithmic bytes (HBM bound) or flops (MFMA bound) of
 one forward call / its mean duration from HIP events recorded on the launch
-stream around the call, with the 256 MB last-level cache flushed (a 512 MB
-buffer written) before every call; the same figure for back-to-back calls in
+stream around the call, with the 256 MB last-level cache flushed before every
+call (a 512 MB buffer read: the cache then holds only clean lines of that
+buffer; a buffer written instead would leave dirty lines whose write-back the
+timed call would pay for); the same figure for back-to-back calls in
 the timed region is roofline.warm.  A call is one kernel launch, except a
 segmented TTT-Linear scan: maps, start-state composition and segment scans,
 three launches back to back on the stream, or two for the fp32 column-split
@@ -239,7 +241,7 @@ def roofline(w, flops, nbytes, seconds, kernels, roofs=None, warm_seconds=None):
     out = {"bound": bound, "achieved": round(ach, 3), "peak": peak, "unit": unit,
            "frac": round(ach / peak, 5), "traffic": stored_traffic(kernels, w.name),
            "kernel": " + ".join(kernels), "mean_launch_us": round(seconds * 1e6, 3),
-           "timing": "HIP events around each call, last-level cache flushed before it",
+           "timing": "HIP events around each call, last-level cache flushed before it (512 MB read)",
            "peak_measured": round(meas, 3) if meas else None,
            "frac_of_measured": round(ach / meas, 5) if meas else None,
            "algorithmic_flops": flops, "algorithmic_bytes": nbytes,
@@ -249,6 +251,19 @@ def roofline(w, flops, nbytes, seconds, kernels, roofs=None, warm_seconds=None):
                        "mean_launch_us": round(warm_seconds * 1e6, 3),
                        "timing": "mean over the back-to-back calls of the timed region"}
     return out
+
+
+_FLUSH = {}
+
+
+def flush_llc(torch):
+    """Evict the 256 MB last-level cache by reading a 512 MB buffer (a sum over
+    it): afterwards the cache holds only clean lines of that buffer, so the
+    next call's inputs come from HBM and it pays no write-back of the flush."""
+    if "buf" not in _FLUSH:
+        _FLUSH["buf"] = torch.ones(512 * 1024 * 1024 // 4, device="cuda")
+        _FLUSH["out"] = torch.empty((), device="cuda")
+    torch.sum(_FLUSH["buf"], dim=0, out=_FLUSH["out"])
 
 
 def measure_roofs():
@@ -482,34 +497,31 @@ class Runner:
         end.record()
         torch.cuda.synchronize()
         warm = start.elapsed_time(end) / 1e3 / steps
-        junk = torch.empty(512 * 1024 * 1024 // 4, device="cuda")
         times = []
         for _ in range(cold_reps):
-            junk.fill_(1.0)
+            flush_llc(torch)
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record()
             call()
             b.record()
             torch.cuda.synchronize()
             times.append(a.elapsed_time(b) / 1e3)
-        del junk, ws
+        del ws
         return warm, sum(times) / len(times)
 
     def measure_cold(self, reps):
         """Forward duration with the 256 MB last-level cache flushed (a 512 MB
-        buffer written) before each call: (mean, median) over `reps` calls."""
+        buffer read) before each call: (mean, median) over `reps` calls."""
         torch = self.torch
-        junk = torch.empty(512 * 1024 * 1024 // 4, device="cuda")
         times = []
         for _ in range(reps):
-            junk.fill_(1.0)
+            flush_llc(torch)
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record()
             self.forward()
             b.record()
             torch.cuda.synchronize()
             times.append(a.elapsed_time(b) / 1e3)
-        del junk
         mean = sum(times) / len(times)
         times.sort()
         return mean, times[len(times) // 2]

@@ -25,7 +25,7 @@ def main():
     ap.add_argument("--backward", action="store_true",
                     help="run ttt_linear_backward (seeded cotangents) instead of the forward")
     ap.add_argument("--flush", action="store_true",
-                    help="write a 512 MB buffer before every call (the 256 MB last-level cache "
+                    help="read a 512 MB buffer before every call (the 256 MB last-level cache "
                          "flushed, as bench.py's roofline timing does)")
     ap.add_argument("--prologue", action="store_true",
                     help="with the input prologue (LayerNorm of q and k, per-token step sizes): "
@@ -64,11 +64,12 @@ def main():
         nbytes = (ttt.ttt_linear_backward_workspace_bytes if args.backward
                   else ttt.ttt_linear_workspace_bytes)(w.B, w.H, w.T, w.d, w.b, w.torch_dtype)
         ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
-    junk = torch.empty(512 * 1024 * 1024 // 4, device="cuda") if args.flush else None
+    junk = torch.ones(512 * 1024 * 1024 // 4, device="cuda") if args.flush else None
+    sink = torch.empty((), device="cuda")
     torch.cuda.synchronize()
     for _ in range(args.reps):
         if junk is not None:
-            junk.fill_(1.0)
+            torch.sum(junk, dim=0, out=sink)
         if args.momentum:
             ttt.ttt_linear_momentum_forward(g["Q"], g["K"], g["V"], g["W0"], g["eta"], beta, w.b,
                                             None, gm, Y=Y, W_out=W, M_out=M, workspace=ws)

@@ -5,8 +5,9 @@ Relative-L2 comparison of Y, W_out and M_out on the same seeded inputs:
 within 1e-4 for fp32 Q/K/V and 2e-2 for bf16 Q/K/V (fp32 state), for both
 gradient points (exact token steps, chunk-start gradients).  Small cases span
 several chunks and a ragged tail on both kernels (MFMA: bf16, d = 64, b = 16;
-plain fp32 kernel: every other shape); the 96-chain workload runs at full
-size, every chain, in the launch configuration the benchmark times.
+plain fp32 kernel: every other shape); the 96-chain and the 32768-token
+workloads run at full size, every chain, in the launch configuration the
+benchmark times.
 """
 import json
 import os
@@ -18,7 +19,8 @@ import torch
 
 import oracle
 import test_sequence_layers_linear_amd as ttt
-from parity_util import TOL, WORKLOADS, announce, default_seed, make_inputs, rel_l2, to_gpu
+from parity_util import (TOL, WORKLOADS, announce, cached_inputs, default_seed, make_inputs,
+                         rel_l2, to_gpu)
 from test_sequence_layers_linear_amd.inputs import make_momentum
 
 pytestmark = pytest.mark.gpu
@@ -45,6 +47,16 @@ def test_momentum_config3_full(grad_mode):
     w = WORKLOADS[3]
     announce("momentum config 3, all chains, grad_mode", grad_mode)
     inp = make_inputs(w, default_seed(3))
+    _run(inp, make_momentum(w, 31), w.b, grad_mode, "bf16")
+
+
+@pytest.mark.parametrize("grad_mode", [0, 1])
+def test_momentum_config4_full(grad_mode):
+    """B2 H24 T32768 bf16 in the launch configuration the benchmark times:
+    all 48 chains, relative L2 over the whole Y, W_out and M_out tensors."""
+    w = WORKLOADS[4]
+    announce("momentum config 4, all chains, grad_mode", grad_mode)
+    inp = cached_inputs(4, default_seed(4))
     _run(inp, make_momentum(w, 31), w.b, grad_mode, "bf16")
 
 
