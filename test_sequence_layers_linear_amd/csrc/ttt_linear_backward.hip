@@ -56,7 +56,7 @@
 // chunk-start read dropping A, and an epilogue in which the staging threads
 // apply the LayerNorm backward to dQ, dK of the normalised rows (through LDS),
 // store them and sum the gamma, beta gradients.  83 KB of LDS: one per CU.
-#include "ttt_internal.h"
+#include "ttt_mfma_ops.h"
 
 namespace ttt {
 namespace {
@@ -127,16 +127,6 @@ template <> struct Raw<uint16_t> {
                      __uint_as_float(x[1] << 16), __uint_as_float(x[1] & 0xffff0000u)};
     }
 };
-
-// Raw buffer resource over a chain's rows: loads past `bytes` read zero and
-// stores past it are dropped, so the tokens past T need no branch (a memory
-// operation under a branch costs the compiler's wait counts their precision,
-// and the stage loads of the chunks ahead must stay in flight).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t chain_rsrc(const void* base, int64_t bytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes),
-                                             0x00020000);
-}
 
 __device__ __forceinline__ float to_f(float x) { return x; }
 __device__ __forceinline__ float to_f(uint16_t x) { return __uint_as_float(static_cast<uint32_t>(x) << 16); }
@@ -216,16 +206,16 @@ linear_backward_kernel(const In* __restrict__ Q, const In* __restrict__ K, const
     float* st = states + (u * nseg + s) * static_cast<int64_t>(seg_chunks) * kD * kD;
     static_assert(sizeof(In) == 4, "fp32 rows (bf16 inputs run in ttt_linear_backward_bf16.hip)");
     const int64_t chain_bytes = static_cast<int64_t>(T) * kD * 4;
-    const __amdgpu_buffer_rsrc_t r_q = chain_rsrc(Q + off, chain_bytes);
-    const __amdgpu_buffer_rsrc_t r_k = chain_rsrc(K + off, chain_bytes);
-    const __amdgpu_buffer_rsrc_t r_v = chain_rsrc(V + off, kGMap ? 0 : chain_bytes);
-    const __amdgpu_buffer_rsrc_t r_dy = chain_rsrc(dY + off, chain_bytes);
-    const __amdgpu_buffer_rsrc_t r_dq = chain_rsrc(dQ + off, kGMap ? 0 : chain_bytes);
-    const __amdgpu_buffer_rsrc_t r_dk = chain_rsrc(dK + off, kGMap ? 0 : chain_bytes);
-    const __amdgpu_buffer_rsrc_t r_dv = chain_rsrc(dV + off, kGMap ? 0 : chain_bytes);
+    const __amdgpu_buffer_rsrc_t r_q = mfma::buffer_rsrc(Q + off, chain_bytes);
+    const __amdgpu_buffer_rsrc_t r_k = mfma::buffer_rsrc(K + off, chain_bytes);
+    const __amdgpu_buffer_rsrc_t r_v = mfma::buffer_rsrc(V + off, kGMap ? 0 : chain_bytes);
+    const __amdgpu_buffer_rsrc_t r_dy = mfma::buffer_rsrc(dY + off, chain_bytes);
+    const __amdgpu_buffer_rsrc_t r_dq = mfma::buffer_rsrc(dQ + off, kGMap ? 0 : chain_bytes);
+    const __amdgpu_buffer_rsrc_t r_dk = mfma::buffer_rsrc(dK + off, kGMap ? 0 : chain_bytes);
+    const __amdgpu_buffer_rsrc_t r_dv = mfma::buffer_rsrc(dV + off, kGMap ? 0 : chain_bytes);
     // this segment's chunk-start states in the workspace
     const __amdgpu_buffer_rsrc_t r_st =
-        chain_rsrc(st, kGMap ? 0 : static_cast<int64_t>(seg_chunks) * kD * kD * 4);
+        mfma::buffer_rsrc(st, kGMap ? 0 : static_cast<int64_t>(seg_chunks) * kD * kD * 4);
     // the M half of a cotangent map sees dY = 0 (a per-workgroup, uniform branch)
     const bool use_dy = !kGMap || half == 1;
 
@@ -253,10 +243,10 @@ linear_backward_kernel(const In* __restrict__ Q, const In* __restrict__ K, const
         }
     }
     const __amdgpu_buffer_rsrc_t r_eta =
-        chain_rsrc(use_tok ? pro.eta_tok + u * static_cast<int64_t>(T) : eta,
+        mfma::buffer_rsrc(use_tok ? pro.eta_tok + u * static_cast<int64_t>(T) : eta,
                    use_tok ? static_cast<int64_t>(T) * 4 : 0);
     const __amdgpu_buffer_rsrc_t r_deta =
-        chain_rsrc(use_tok && !kGMap ? deta_tok + u * static_cast<int64_t>(T) : eta,
+        mfma::buffer_rsrc(use_tok && !kGMap ? deta_tok + u * static_cast<int64_t>(T) : eta,
                    use_tok && !kGMap ? static_cast<int64_t>(T) * 4 : 0);
     auto norm = [&](f32x4 x, const float (&gm)[4], const float (&bt)[4], bool valid,
                     float (&xh)[4], float& rstd) {

@@ -41,16 +41,18 @@
 // the LayerNorm backward to their row segment, store the raw-row gradients
 // and sum the gamma, beta gradients; per-token deta_t = -<P_t, E_t> is summed
 // over the columns of each wave and then over the waves.
-#include "ttt_internal.h"
+#include "ttt_mfma_ops.h"
 
 namespace ttt {
 namespace {
+
+using namespace mfma;
 
 constexpr int kD = 64;
 constexpr int kB = 16;
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kRow = kD * 2;                    // bytes per bf16 row
+constexpr int kRow = kRowBytes;                 // bytes per bf16 row
 constexpr int kTileB = kB * kRow;               // 2048: a 16 x 64 tile
 constexpr int kMatB = kD * kRow;                // 8192: a 64 x 64 matrix
 constexpr int kSlotQ = 0;
@@ -79,72 +81,20 @@ static_assert(Lay<false>::kBytes == 32784, "plain layout");
 static_assert(2 * Lay<true>::kBytes <= kMaxLdsBytes, "two workgroups per CU");
 static_assert(kWaves * 4 * kD * 4 <= 2 * kB * kFP * 4, "the gamma/beta reduction fits the dQ, dK tiles");
 
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c)
-{
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x4 mfma16(bf16x4 a, bf16x4 b, f32x4 c)
-{
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a),
-                                                     __builtin_bit_cast(i16x4, b), c, 0, 0, 0);
-}
-
-// fp32 pairs -> one word of two bf16 (round to nearest even)
-__device__ __forceinline__ uint32_t cvt2(float a, float b)
-{
-    typedef float f32x2 __attribute__((ext_vector_type(2)));
-    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
-}
-__device__ __forceinline__ bf16x8 pack8(f32x4 lo, f32x4 hi)
-{
-    return __builtin_bit_cast(bf16x8, u32x4{cvt2(lo[0], lo[1]), cvt2(lo[2], lo[3]),
-                                            cvt2(hi[0], hi[1]), cvt2(hi[2], hi[3])});
-}
-__device__ __forceinline__ bf16x4 pack4(f32x4 x)
-{
-    return __builtin_bit_cast(bf16x4, u32x2{cvt2(x[0], x[1]), cvt2(x[2], x[3])});
-}
 __device__ __forceinline__ bf16x8 join(bf16x4 lo, bf16x4 hi)
 {
     const u32x2 a = __builtin_bit_cast(u32x2, lo), b = __builtin_bit_cast(u32x2, hi);
     return __builtin_bit_cast(bf16x8, u32x4{a[0], a[1], b[0], b[1]});
 }
 
-// Raw buffer resource over a chain's rows: loads past `bytes` read zero and
-// stores past it are dropped, so the tokens past T need no branch (a memory
-// operation under a branch costs the compiler's wait counts their precision,
-// and the stage loads of the chunks ahead must stay in flight).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t chain_rsrc(const void* base, int64_t bytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes),
-                                             0x00020000);
-}
+// (a chain's rows are read through buffer resources: loads past the end read
+// zero and stores past it are dropped, so the tokens past T need no branch;
+// a memory operation under a branch costs the compiler's wait counts their
+// precision, and the stage loads of the chunks ahead must stay in flight)
 
-__device__ __forceinline__ int rho(int mt, int m)
-{
-    return 32 * (mt >> 1) + 8 * (m >> 2) + 4 * (mt & 1) + (m & 3);
-}
-
-// byte offset of 16-byte segment `seg` of row `r` in a swizzled tile
-__device__ __forceinline__ int swz(int r, int seg) { return r * kRow + ((seg ^ (r & 7)) << 4); }
 // byte offset of element x of row r
 __device__ __forceinline__ int swz_elem(int r, int x) { return swz(r, x >> 3) + 2 * (x & 7); }
 
-__device__ __forceinline__ bf16x4 read_tr16(const unsigned char* p)
-{
-    typedef __bf16 lds_bf16x4 __attribute__((ext_vector_type(4)));
-    const auto q = (__attribute__((address_space(3))) lds_bf16x4*)(
-        (__attribute__((address_space(3))) unsigned char*)(p));
-    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(q);
-}
 // X[r0 .. r0 + 3][x0 + c] for lane (c, .) of a row-major swizzled tile
 // (x0 a multiple of 16)
 __device__ __forceinline__ bf16x4 col4(const unsigned char* tile, int r0, int x0, int c)
@@ -221,17 +171,17 @@ linear_backward_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __re
     const int c1 = min((T + kB - 1) / kB, c0 + seg_chunks);
     const int64_t off = u * static_cast<int64_t>(T) * kD;
     const int64_t chain_bytes = static_cast<int64_t>(T) * kD * 2;
-    const __amdgpu_buffer_rsrc_t r_q = chain_rsrc(Q + off, chain_bytes);
-    const __amdgpu_buffer_rsrc_t r_k = chain_rsrc(K + off, chain_bytes);
-    const __amdgpu_buffer_rsrc_t r_v = chain_rsrc(V + off, kGMap ? 0 : chain_bytes);
-    const __amdgpu_buffer_rsrc_t r_dy = chain_rsrc(dY + off, chain_bytes);
-    const __amdgpu_buffer_rsrc_t r_dq = chain_rsrc(dQ + off, kGMap ? 0 : chain_bytes);
-    const __amdgpu_buffer_rsrc_t r_dk = chain_rsrc(dK + off, kGMap ? 0 : chain_bytes);
-    const __amdgpu_buffer_rsrc_t r_dv = chain_rsrc(dV + off, kGMap ? 0 : chain_bytes);
+    const __amdgpu_buffer_rsrc_t r_q = buffer_rsrc(Q + off, chain_bytes);
+    const __amdgpu_buffer_rsrc_t r_k = buffer_rsrc(K + off, chain_bytes);
+    const __amdgpu_buffer_rsrc_t r_v = buffer_rsrc(V + off, kGMap ? 0 : chain_bytes);
+    const __amdgpu_buffer_rsrc_t r_dy = buffer_rsrc(dY + off, chain_bytes);
+    const __amdgpu_buffer_rsrc_t r_dq = buffer_rsrc(dQ + off, kGMap ? 0 : chain_bytes);
+    const __amdgpu_buffer_rsrc_t r_dk = buffer_rsrc(dK + off, kGMap ? 0 : chain_bytes);
+    const __amdgpu_buffer_rsrc_t r_dv = buffer_rsrc(dV + off, kGMap ? 0 : chain_bytes);
     uint16_t* st = states + (u * nseg + s) * static_cast<int64_t>(seg_chunks) * kD * kD;
     // this segment's chunk-start states (bf16 W^T) in the workspace
     const __amdgpu_buffer_rsrc_t r_st =
-        chain_rsrc(st, kGMap ? 0 : static_cast<int64_t>(seg_chunks) * kD * kD * 2);
+        buffer_rsrc(st, kGMap ? 0 : static_cast<int64_t>(seg_chunks) * kD * kD * 2);
     const bool use_dy = !kGMap || half == 1;     // uniform per workgroup
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 
@@ -260,10 +210,10 @@ linear_backward_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __re
         }
     }
     const __amdgpu_buffer_rsrc_t r_eta =
-        chain_rsrc(use_tok ? pro.eta_tok + u * static_cast<int64_t>(T) : eta,
+        buffer_rsrc(use_tok ? pro.eta_tok + u * static_cast<int64_t>(T) : eta,
                    use_tok ? static_cast<int64_t>(T) * 4 : 0);
     const __amdgpu_buffer_rsrc_t r_deta =
-        chain_rsrc(use_tok && !kGMap ? deta_tok + u * static_cast<int64_t>(T) : eta,
+        buffer_rsrc(use_tok && !kGMap ? deta_tok + u * static_cast<int64_t>(T) : eta,
                    use_tok && !kGMap ? static_cast<int64_t>(T) * 4 : 0);
     // LayerNorm of a staged row segment, back to bf16; keeps xh and 1/std
     auto norm = [&](u32x2 x, const float (&gm)[4], const float (&bt)[4], bool valid,

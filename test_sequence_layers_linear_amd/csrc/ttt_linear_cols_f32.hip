@@ -46,7 +46,7 @@
 // one barrier, 16 k-steps over the 64 rows), so the start states need no
 // launch of their own and never go through memory; segment s is ready after
 // s steps, the last one after nseg - 1, as with a separate composition.
-#include "ttt_internal.h"
+#include "ttt_mfma_ops.h"
 
 namespace ttt {
 namespace {
@@ -60,9 +60,7 @@ constexpr int kRing = 4;                         // register sets of staged chun
 constexpr int kSlots = 3;                        // LDS tile slots
 constexpr int kP = kD + 4;                       // padded K, Q row (floats)
 constexpr int kVP = 20;                          // padded V slice row (floats)
-constexpr int kTileFloats = 256;                 // one 16 x 16 accumulator tile, lane order
-constexpr int kBufferDword3 = 0x00020000;        // raw buffer resource word 3 (gfx9 family)
-
+constexpr int kTileFloats = 256;                 
 // LDS layout (floats): a slot holds the chunk's K, Q (scan only) and V slice
 // (and with the prologue its 16 step sizes); the partial tiles [2 parity]
 // [kinds][4 waves][256] follow the slots (the maps have only P, and no Q:
@@ -85,12 +83,6 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ f32x4 mfma(float a, float b, f32x4 c)
 {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t chain_rsrc(const void* base, int64_t bytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0,
-                                             static_cast<int>(bytes), kBufferDword3);
 }
 
 struct StageRegs {
@@ -224,10 +216,10 @@ linear_cols_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
 
     const int64_t base = (u * static_cast<int64_t>(T) + t_begin) * kD;
     const int64_t seg_bytes = static_cast<int64_t>(t_len) * kD * 4;
-    const __amdgpu_buffer_rsrc_t rq = chain_rsrc(Q + base, kMaps ? 0 : seg_bytes);
-    const __amdgpu_buffer_rsrc_t rk = chain_rsrc(K + base, seg_bytes);
-    const __amdgpu_buffer_rsrc_t rv = chain_rsrc(V + base, (kMaps && half == 0) ? 0 : seg_bytes);
-    const __amdgpu_buffer_rsrc_t ry = chain_rsrc(Y + base, kMaps ? 0 : seg_bytes);
+    const __amdgpu_buffer_rsrc_t rq = mfma::buffer_rsrc(Q + base, kMaps ? 0 : seg_bytes);
+    const __amdgpu_buffer_rsrc_t rk = mfma::buffer_rsrc(K + base, seg_bytes);
+    const __amdgpu_buffer_rsrc_t rv = mfma::buffer_rsrc(V + base, (kMaps && half == 0) ? 0 : seg_bytes);
+    const __amdgpu_buffer_rsrc_t ry = mfma::buffer_rsrc(Y + base, kMaps ? 0 : seg_bytes);
 
     // staging: thread tid moves 16 bytes of row tid / 16 of K and Q (columns
     // 4 (tid % 16) ..), and lane l of every wave loads 16 bytes of the V slice
@@ -252,7 +244,7 @@ linear_cols_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
         }
     }
     const __amdgpu_buffer_rsrc_t reta =
-        chain_rsrc(use_tok ? pro.eta_tok + u * static_cast<int64_t>(T) + t_begin : eta,
+        mfma::buffer_rsrc(use_tok ? pro.eta_tok + u * static_cast<int64_t>(T) + t_begin : eta,
                    use_tok ? static_cast<int64_t>(t_len) * 4 : 0);
     auto load_stage = [&](StageRegs& o, int chunk) {
         const int off = ((chunk * kB + st_row) * kD + st_col) * 4;

@@ -54,10 +54,12 @@
 // sized to the chain's T tokens, so rows past the end read as zero (an
 // all-zero chunk leaves W unchanged) and stores past the end are dropped:
 // there are no tail branches.
-#include "ttt_internal.h"
+#include "ttt_mfma_ops.h"
 
 namespace ttt {
 namespace {
+
+using namespace mfma;
 
 constexpr int kD = 64;
 constexpr int kB = 16;
@@ -67,11 +69,7 @@ constexpr int kStageChunks = 2;
 constexpr int kStageTokens = kB * kStageChunks;
 constexpr int kSet = 6;                 // stages per register set (two sets)
 constexpr int kSlots = 3;               // LDS ring slots (kSet * 2 % kSlots == 0)
-// word 3 of a raw buffer resource on gfx9-family GPUs (32-bit data format)
-constexpr int kBufferDword3 = 0x00020000;
-
 // LDS layout of one chunk inside a stage slot (bytes)
-constexpr int kRowBytes = kD * 2;                    // 128
 constexpr int kOffK = 0;
 constexpr int kOffQ = kOffK + kB * kRowBytes;        // 2048
 constexpr int kOffV = kOffQ + kB * kRowBytes;        // 4096
@@ -79,81 +77,6 @@ constexpr int kChunkBytes = kOffV + kB * kRowBytes;  // 6144
 constexpr int kSlotBytes = kChunkBytes * kStageChunks;
 
 static_assert((2 * kSet) % kSlots == 0, "slot index must be static inside the loop");
-
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c)
-{
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ f32x4 mfma16(bf16x4 a, bf16x4 b, f32x4 c)
-{
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a),
-                                                     __builtin_bit_cast(i16x4, b), c, 0, 0, 0);
-}
-
-// A 16x16x16 product whose result feeds a 16x16x32 product as the
-// accumulator (or the reverse) needs 5 wait states on gfx950 between the two,
-// more than the compiler inserts; such products are issued as 16x16x32 with
-// the upper four k-slots zero, so that every accumulation chain has one shape.
-__device__ __forceinline__ f32x4 mfma16_as32(bf16x4 a, bf16x4 b, f32x4 c)
-{
-    const u32x2 aw = __builtin_bit_cast(u32x2, a), bw = __builtin_bit_cast(u32x2, b);
-    return mfma32(__builtin_bit_cast(bf16x8, u32x4{aw[0], aw[1], 0u, 0u}),
-                  __builtin_bit_cast(bf16x8, u32x4{bw[0], bw[1], 0u, 0u}), c);
-}
-
-// fp32 -> bf16 (round to nearest even), two values per conversion
-// instruction.  Built from 32-bit words: element-wise conversions feeding an
-// MFMA operand otherwise compile to one conversion per value plus permutes.
-__device__ __forceinline__ uint32_t cvt2(float a, float b)
-{
-    typedef float f32x2 __attribute__((ext_vector_type(2)));
-    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
-}
-
-__device__ __forceinline__ bf16x8 pack8(f32x4 lo, f32x4 hi)
-{
-    return __builtin_bit_cast(bf16x8, u32x4{cvt2(lo[0], lo[1]), cvt2(lo[2], lo[3]),
-                                            cvt2(hi[0], hi[1]), cvt2(hi[2], hi[3])});
-}
-
-__device__ __forceinline__ bf16x4 pack4(f32x4 x)
-{
-    return __builtin_bit_cast(bf16x4, u32x2{cvt2(x[0], x[1]), cvt2(x[2], x[3])});
-}
-
-__device__ __forceinline__ int rho(int mt, int m)
-{
-    return 32 * (mt >> 1) + 8 * (m >> 2) + 4 * (mt & 1) + (m & 3);
-}
-
-// ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives, as
-// element k (k = 0..3), element i % 4 of the 8-byte block addressed by lane
-// 4k + i / 4 of its group (measured on gfx950 with an in-bounds probe).
-__device__ __forceinline__ bf16x4 read_tr16(const unsigned char* p)
-{
-    typedef __bf16 lds_bf16x4 __attribute__((ext_vector_type(4)));
-    const auto q = (__attribute__((address_space(3))) lds_bf16x4*)(
-        (__attribute__((address_space(3))) unsigned char*)(p));
-    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(q);
-}
-
-// byte offset of 16-byte segment `seg` of row `r` in a swizzled row-major tile
-__device__ __forceinline__ int swz(int r, int seg) { return r * kRowBytes + ((seg ^ (r & 7)) << 4); }
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t chain_rsrc(const void* base, int64_t bytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0,
-                                             static_cast<int>(bytes), kBufferDword3);
-}
 
 // One wave's share of one stage: rows [8w, 8w + 8) of the stage's K, Q, V;
 // lane l holds row 8w + l / 8, 16-byte segment l % 8.
@@ -250,10 +173,10 @@ linear_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
 
     const int64_t base = (u * static_cast<int64_t>(T) + t_begin) * kD;
     const int64_t seg_bytes = static_cast<int64_t>(t_len) * kD * 2;
-    const __amdgpu_buffer_rsrc_t rq = chain_rsrc(Q + base, kMaps ? 0 : seg_bytes);
-    const __amdgpu_buffer_rsrc_t rk = chain_rsrc(K + base, seg_bytes);
-    const __amdgpu_buffer_rsrc_t rv = chain_rsrc(V + base, seg_bytes);
-    const __amdgpu_buffer_rsrc_t ry = chain_rsrc(Y + base, kMaps ? 0 : seg_bytes);
+    const __amdgpu_buffer_rsrc_t rq = buffer_rsrc(Q + base, kMaps ? 0 : seg_bytes);
+    const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(K + base, seg_bytes);
+    const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(V + base, seg_bytes);
+    const __amdgpu_buffer_rsrc_t ry = buffer_rsrc(Y + base, kMaps ? 0 : seg_bytes);
 
     const int nstages = (t_len + kStageTokens - 1) / kStageTokens;
     // a slot also holds the stage's 32 step sizes when the prologue is on
@@ -282,7 +205,7 @@ linear_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
         }
     }
     const __amdgpu_buffer_rsrc_t reta =
-        chain_rsrc(use_tok ? pro.eta_tok + u * static_cast<int64_t>(T) + t_begin : eta,
+        buffer_rsrc(use_tok ? pro.eta_tok + u * static_cast<int64_t>(T) + t_begin : eta,
                    use_tok ? static_cast<int64_t>(t_len) * 4 : 0);
     auto load_stage = [&](StageRegs& o, int stage) {
         if (!stager)
@@ -434,10 +357,10 @@ linear_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
             // different buffers: x is K or Q, y is V or nothing, e the step
             // sizes or nothing (a zero-sized resource reads as zero)
             const bool kgrp = kMaps || wave < 2 * kWaves;
-            const __amdgpu_buffer_rsrc_t rx = chain_rsrc((kgrp ? K : Q) + base, seg_bytes);
-            const __amdgpu_buffer_rsrc_t ry = chain_rsrc(V + base, kgrp ? seg_bytes : 0);
+            const __amdgpu_buffer_rsrc_t rx = buffer_rsrc((kgrp ? K : Q) + base, seg_bytes);
+            const __amdgpu_buffer_rsrc_t ry = buffer_rsrc(V + base, kgrp ? seg_bytes : 0);
             const __amdgpu_buffer_rsrc_t re =
-                chain_rsrc(use_tok ? pro.eta_tok + u * static_cast<int64_t>(T) + t_begin : eta,
+                buffer_rsrc(use_tok ? pro.eta_tok + u * static_cast<int64_t>(T) + t_begin : eta,
                            use_tok && kgrp ? static_cast<int64_t>(t_len) * 4 : 0);
             const bool ln_x = kgrp ? ln_k : ln_q;
             const int off_x = kgrp ? kOffK : kOffQ;

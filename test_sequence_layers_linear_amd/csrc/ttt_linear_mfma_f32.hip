@@ -34,7 +34,7 @@
 // V^T (token-contiguous rows, segments swizzled by row group).  One barrier
 // per chunk.  Every product is a 16x16x4 fp32 MFMA, so accumulation chains
 // never mix MFMA shapes.
-#include "ttt_internal.h"
+#include "ttt_mfma_ops.h"
 
 namespace ttt {
 namespace {
@@ -45,7 +45,6 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kSet = 6;                 // chunks per register set (two sets)
 constexpr int kSlots = 3;
-constexpr int kBufferDword3 = 0x00020000;   // raw buffer resource word 3 (gfx9 family)
 
 constexpr int kRowBytes = kD * 4;                    // 256
 constexpr int kOffK = 0;
@@ -71,12 +70,6 @@ __device__ __forceinline__ int swz_row(int r, int s) { return r * kRowBytes + ((
 // reading segment s of 8 rows ρ hit 8 different bank groups.
 __device__ __forceinline__ int swz_kt(int i, int s) { return i * 64 + ((s ^ ((i >> 4) & 3)) << 4); }
 __device__ __forceinline__ int swz_vt(int j, int s) { return j * 64 + ((s ^ ((j >> 2) & 3)) << 4); }
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t chain_rsrc(const void* base, int64_t bytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0,
-                                             static_cast<int>(bytes), kBufferDword3);
-}
 
 struct StageRegs {
     u32x4 k, q, v;
@@ -157,10 +150,10 @@ linear_mfma_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
 
     const int64_t base = (u * static_cast<int64_t>(T) + t_begin) * kD;
     const int64_t seg_bytes = static_cast<int64_t>(t_len) * kD * 4;
-    const __amdgpu_buffer_rsrc_t rq = chain_rsrc(Q + base, kMaps ? 0 : seg_bytes);
-    const __amdgpu_buffer_rsrc_t rk = chain_rsrc(K + base, seg_bytes);
-    const __amdgpu_buffer_rsrc_t rv = chain_rsrc(V + base, (kMaps && half == 0) ? 0 : seg_bytes);
-    const __amdgpu_buffer_rsrc_t ry = chain_rsrc(Y + base, kMaps ? 0 : seg_bytes);
+    const __amdgpu_buffer_rsrc_t rq = mfma::buffer_rsrc(Q + base, kMaps ? 0 : seg_bytes);
+    const __amdgpu_buffer_rsrc_t rk = mfma::buffer_rsrc(K + base, seg_bytes);
+    const __amdgpu_buffer_rsrc_t rv = mfma::buffer_rsrc(V + base, (kMaps && half == 0) ? 0 : seg_bytes);
+    const __amdgpu_buffer_rsrc_t ry = mfma::buffer_rsrc(Y + base, kMaps ? 0 : seg_bytes);
 
     const int nchunks = (t_len + kB - 1) / kB;
     // a slot also holds the chunk's 16 step sizes when the prologue is on
@@ -185,7 +178,7 @@ linear_mfma_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
         bq[e] = ln_q ? pro.ln_q[(2 * h + 1) * kD + 4 * st_seg + e] : 0.f;
     }
     const __amdgpu_buffer_rsrc_t reta =
-        chain_rsrc(use_tok ? pro.eta_tok + u * static_cast<int64_t>(T) + t_begin : eta,
+        mfma::buffer_rsrc(use_tok ? pro.eta_tok + u * static_cast<int64_t>(T) + t_begin : eta,
                    use_tok ? static_cast<int64_t>(t_len) * 4 : 0);
     auto load_stage = [&](StageRegs& o, int chunk) {
         const int off = (chunk * kB + st_row) * kRowBytes + st_seg * 16;

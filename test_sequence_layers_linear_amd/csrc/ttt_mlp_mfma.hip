@@ -44,10 +44,12 @@
 //   P3  LDS: read E' both ways, K^T.  MFMA: D', Hq, Aq, Y partial -> LDS,
 //       updates of W1, W2a, W2b; stage the next chunk's inputs.    | barrier
 // Every accumulation chain uses a single MFMA shape (see mfma16_as32).
-#include "ttt_internal.h"
+#include "ttt_mfma_ops.h"
 
 namespace ttt {
 namespace {
+
+using namespace mfma;
 
 constexpr int kD = 64;
 constexpr int kM = 256;
@@ -58,10 +60,8 @@ constexpr int kHT = kHid / 16;                          // 16-unit hidden tiles 
 constexpr int kHK = kHT / 2;                            // 32-unit k-blocks per wave
 constexpr int kWork = 4;                                // waves that stage and reduce
 constexpr int kThreads = 64 * kWaves;
-constexpr int kBufferDword3 = 0x00020000;   // raw buffer resource word 3 (gfx9 family)
 
 // LDS layout (bytes)
-constexpr int kRowBytes = kD * 2;                       // 128: bf16 row of K/Q
 constexpr int kTrRow = 40;                              // E'^T rows: 16 tokens + pad
 constexpr int kOffK = 0;
 constexpr int kOffQ = kOffK + kB * kRowBytes;           // 2048
@@ -78,51 +78,6 @@ constexpr int kOffEN = kOffY + kWaves * kYWave;         // 88064
 constexpr int kOffET = kOffEN + kB * kENRow;            // 90368
 constexpr int kLdsBytes = kOffET + kD * kTrRow;         // 92928
 
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c)
-{
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x4 mfma16(bf16x4 a, bf16x4 b, f32x4 c)
-{
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a),
-                                                     __builtin_bit_cast(i16x4, b), c, 0, 0, 0);
-}
-// fp32 -> bf16 (round to nearest even), two values per conversion
-// instruction.  Built from 32-bit words: element-wise conversions feeding an
-// MFMA operand otherwise compile to one conversion per value plus permutes.
-__device__ __forceinline__ uint32_t cvt2(float a, float b)
-{
-    typedef float f32x2 __attribute__((ext_vector_type(2)));
-    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
-}
-
-__device__ __forceinline__ bf16x8 pack8(f32x4 lo, f32x4 hi)
-{
-    return __builtin_bit_cast(bf16x8, u32x4{cvt2(lo[0], lo[1]), cvt2(lo[2], lo[3]),
-                                            cvt2(hi[0], hi[1]), cvt2(hi[2], hi[3])});
-}
-__device__ __forceinline__ bf16x4 pack4(f32x4 x)
-{
-    return __builtin_bit_cast(bf16x4, u32x2{cvt2(x[0], x[1]), cvt2(x[2], x[3])});
-}
-// A 16x16x16 product accumulated onto a 16x16x32 result (or the reverse)
-// needs more wait states on gfx950 than the compiler inserts between the two;
-// such products are issued as 16x16x32 with the upper four k-slots zero, so
-// every accumulation chain uses one shape.
-__device__ __forceinline__ f32x4 mfma16_as32(bf16x4 a, bf16x4 b, f32x4 c)
-{
-    const u32x2 aw = __builtin_bit_cast(u32x2, a), bw = __builtin_bit_cast(u32x2, b);
-    return mfma32(__builtin_bit_cast(bf16x8, u32x4{aw[0], aw[1], 0u, 0u}),
-                  __builtin_bit_cast(bf16x8, u32x4{bw[0], bw[1], 0u, 0u}), c);
-}
 __device__ __forceinline__ bf16x8 cat8(bf16x4 lo, bf16x4 hi)
 {
     bf16x8 r;
@@ -133,21 +88,6 @@ __device__ __forceinline__ bf16x8 cat8(bf16x4 lo, bf16x4 hi)
     }
     return r;
 }
-__device__ __forceinline__ int rho(int mt, int m)
-{
-    return 32 * (mt >> 1) + 8 * (m >> 2) + 4 * (mt & 1) + (m & 3);
-}
-// ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives, as
-// element k (k = 0..3), element i % 4 of the 8-byte block addressed by lane
-// 4k + i / 4 of its group (measured on gfx950 with an in-bounds probe).
-__device__ __forceinline__ bf16x4 read_tr16(const unsigned char* p)
-{
-    typedef __bf16 lds_bf16x4 __attribute__((ext_vector_type(4)));
-    const auto q = (__attribute__((address_space(3))) lds_bf16x4*)(
-        (__attribute__((address_space(3))) unsigned char*)(p));
-    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(q);
-}
-__device__ __forceinline__ int swz(int r, int seg) { return r * kRowBytes + ((seg ^ (r & 7)) << 4); }
 // logistic sigmoid with the hardware exp2 and reciprocal (about 1 ulp each;
 // the products it feeds take bf16 operands)
 __device__ __forceinline__ float sigmoid_f(float x)
@@ -155,11 +95,6 @@ __device__ __forceinline__ float sigmoid_f(float x)
     return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * x));
 }
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t chain_rsrc(const void* base, int64_t bytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0,
-                                             static_cast<int>(bytes), kBufferDword3);
-}
 
 // one staging wave's share of one chunk (w < kWork): rows [4w, 4w + 4) of
 // K, Q, V; lane l holds row 4w + l / 16, 8-byte segment l % 16 (4 bf16)
@@ -220,10 +155,10 @@ mlp_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 
     const int64_t base = u * static_cast<int64_t>(T) * kD;
     const int64_t chain_bytes = static_cast<int64_t>(T) * kD * 2;
-    const __amdgpu_buffer_rsrc_t rq = chain_rsrc(Q + base, chain_bytes);
-    const __amdgpu_buffer_rsrc_t rk = chain_rsrc(K + base, chain_bytes);
-    const __amdgpu_buffer_rsrc_t rv = chain_rsrc(V + base, chain_bytes);
-    const __amdgpu_buffer_rsrc_t ry = chain_rsrc(Y + base, chain_bytes);
+    const __amdgpu_buffer_rsrc_t rq = buffer_rsrc(Q + base, chain_bytes);
+    const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(K + base, chain_bytes);
+    const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(V + base, chain_bytes);
+    const __amdgpu_buffer_rsrc_t ry = buffer_rsrc(Y + base, chain_bytes);
     const int nchunks = (T + kB - 1) / kB;
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 
