@@ -17,10 +17,11 @@ measured too and reported under "workloads" in the same line.
 
 roofline.achieved = algorithmic bytes (HBM bound) or flops (MFMA bound) of
 one forward call / its mean duration from HIP events recorded on the launch
-stream around the call, with the 256 MB last-level cache flushed before every
-call (a 512 MB buffer read: the cache then holds only clean lines of that
-buffer; a buffer written instead would leave dirty lines whose write-back the
-timed call would pay for); the same figure for back-to-back calls in
+stream, for back-to-back calls that cycle through copies of the inputs, so
+many that at least 512 MB of other inputs are read between two uses of a copy:
+the 256 MB last-level cache cannot serve them (the cold-cache protocol of
+rotated input sets; no flush kernel runs between the calls); the same figure
+for back-to-back calls on one input set in
 the timed region is roofline.warm.  A call is one kernel launch, except a
 segmented TTT-Linear scan: maps, start-state composition and segment scans,
 three launches back to back on the stream, or two for the fp32 column-split
@@ -42,8 +43,9 @@ with LayerNorm of q and k and a step size per token fused into the scan, and
 "backward_prologue" ttt_linear_backward_ex, the backward through them.
 The bf16 TTT-Linear workloads also report "momentum": ttt_linear_momentum_forward
 (momentum gradient descent, beta per head from make_momentum) on the same
-inputs, for exact token steps and for chunk-start gradients, each timed with
-the cache flushed and back to back, with its own roofline object.
+inputs, for exact token steps and for chunk-start gradients, each timed on
+cycled input copies (cold cache) and back to back on one copy, with its own
+roofline object.
 """
 from __future__ import annotations
 
@@ -224,8 +226,8 @@ def stored_traffic(kernels, workload):
 
 
 def roofline(w, flops, nbytes, seconds, kernels, roofs=None, warm_seconds=None):
-    """Roofline object of one forward call: `seconds` is its flushed-cache
-    mean duration, `warm_seconds` (optional) the back-to-back one; `roofs`
+    """Roofline object of one forward call: `seconds` is its cold-cache
+    mean duration (calls cycling through input copies), `warm_seconds` (optional) the back-to-back one; `roofs`
     the measured copy bandwidth and MFMA throughputs."""
     dt = "bf16" if w.dtype == "bf16" else "fp32"
     ridge = PEAK_FLOPS[dt] / PEAK_HBM
@@ -241,7 +243,8 @@ def roofline(w, flops, nbytes, seconds, kernels, roofs=None, warm_seconds=None):
     out = {"bound": bound, "achieved": round(ach, 3), "peak": peak, "unit": unit,
            "frac": round(ach / peak, 5), "traffic": stored_traffic(kernels, w.name),
            "kernel": " + ".join(kernels), "mean_launch_us": round(seconds * 1e6, 3),
-           "timing": "HIP events around each call, last-level cache flushed before it (512 MB read)",
+           "timing": ("HIP events around back-to-back calls cycling through copies of the "
+                      "inputs; >= 512 MB of other inputs read between two uses of a copy"),
            "peak_measured": round(meas, 3) if meas else None,
            "frac_of_measured": round(ach / meas, 5) if meas else None,
            "algorithmic_flops": flops, "algorithmic_bytes": nbytes,
@@ -253,17 +256,22 @@ def roofline(w, flops, nbytes, seconds, kernels, roofs=None, warm_seconds=None):
     return out
 
 
-_FLUSH = {}
-
-
-def flush_llc(torch):
-    """Evict the 256 MB last-level cache by reading a 512 MB buffer (a sum over
-    it): afterwards the cache holds only clean lines of that buffer, so the
-    next call's inputs come from HBM and it pays no write-back of the flush."""
-    if "buf" not in _FLUSH:
-        _FLUSH["buf"] = torch.ones(512 * 1024 * 1024 // 4, device="cuda")
-        _FLUSH["out"] = torch.empty((), device="cuda")
-    torch.sum(_FLUSH["buf"], dim=0, out=_FLUSH["out"])
+def cycle_timed(torch, call, sets, reps):
+    """Mean duration of back-to-back calls that cycle through the input sets
+    (one warm-up pass over them, then at least `reps` calls and at least two
+    passes), from HIP events at the two ends."""
+    for x in sets:
+        call(x)
+    n = max(reps, 2 * len(sets))
+    n = -(-n // len(sets)) * len(sets)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(n):
+        call(sets[i % len(sets)])
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / 1e3 / n
 
 
 def measure_roofs():
@@ -338,8 +346,21 @@ class Runner:
                                   dtype=torch.uint8, device="cuda")
         torch.cuda.synchronize()
 
-    def forward(self):
-        g, ttt = self.g, self.ttt
+    def input_sets(self):
+        """Copies of Q, K, V (the first is the original), enough that at
+        least 512 MB of other inputs are read between two uses of a copy
+        when calls cycle through them: a call then finds none of its inputs
+        in the 256 MB last-level cache."""
+        if getattr(self, "_sets", None) is None:
+            w = self.w
+            per_call = (linear_work if w.kind == "linear" else mlp_work)(w)[1]
+            n = max(3, 1 + math.ceil(512e6 / per_call))
+            self._sets = [self.g] + [dict(self.g, Q=self.g["Q"].clone(), K=self.g["K"].clone(),
+                                           V=self.g["V"].clone()) for _ in range(n - 1)]
+        return self._sets
+
+    def forward(self, g=None):
+        g, ttt = g or self.g, self.ttt
         if self.w.kind == "linear":
             ttt.ttt_linear_forward(g["Q"], g["K"], g["V"], g["W0"], g["eta"], self.w.b,
                                    Y=self.Y, W_out=self.W, workspace=self.ws)
@@ -472,8 +493,8 @@ class Runner:
 
     def measure_momentum(self, steps, warmup, grad_mode, cold_reps):
         """ttt_linear_momentum_forward: (mean back to back over `steps` calls,
-        mean with the last-level cache flushed before each of `cold_reps`
-        calls)."""
+        mean over at least `cold_reps` back-to-back calls cycling through the
+        input copies)."""
         torch, g, w = self.torch, self.g, self.w
         from test_sequence_layers_linear_amd.inputs import make_momentum
         beta = make_momentum(w, 31)["beta"].cuda()
@@ -482,8 +503,8 @@ class Runner:
                                                                       w.torch_dtype, grad_mode),
                          dtype=torch.uint8, device="cuda")
 
-        def call():
-            self.ttt.ttt_linear_momentum_forward(g["Q"], g["K"], g["V"], g["W0"], g["eta"], beta,
+        def call(x=g):
+            self.ttt.ttt_linear_momentum_forward(x["Q"], x["K"], x["V"], x["W0"], x["eta"], beta,
                                                  w.b, None, grad_mode, Y=self.Y, W_out=self.W,
                                                  M_out=M, workspace=ws)
         for _ in range(warmup):
@@ -497,34 +518,15 @@ class Runner:
         end.record()
         torch.cuda.synchronize()
         warm = start.elapsed_time(end) / 1e3 / steps
-        times = []
-        for _ in range(cold_reps):
-            flush_llc(torch)
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            call()
-            b.record()
-            torch.cuda.synchronize()
-            times.append(a.elapsed_time(b) / 1e3)
+        cold = cycle_timed(torch, call, self.input_sets(), cold_reps)
         del ws
-        return warm, sum(times) / len(times)
+        return warm, cold
 
     def measure_cold(self, reps):
-        """Forward duration with the 256 MB last-level cache flushed (a 512 MB
-        buffer read) before each call: (mean, median) over `reps` calls."""
-        torch = self.torch
-        times = []
-        for _ in range(reps):
-            flush_llc(torch)
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            self.forward()
-            b.record()
-            torch.cuda.synchronize()
-            times.append(a.elapsed_time(b) / 1e3)
-        mean = sum(times) / len(times)
-        times.sort()
-        return mean, times[len(times) // 2]
+        """Mean forward duration over at least `reps` back-to-back calls that
+        cycle through the input copies (none of a call's inputs in the
+        last-level cache)."""
+        return cycle_timed(self.torch, self.forward, self.input_sets(), reps)
 
 
 # ---------------------------------------------------------------------------
@@ -600,11 +602,11 @@ def measure_workload(cfg, steps, warmup, cold_reps, roofs=None):
     flops, nbytes = (linear_work if w.kind == "linear" else mlp_work)(w)
     nseg = segments(w)
     kern = kernel_names(w, nseg)
-    cold_mean, cold_median = r.measure_cold(cold_reps)
+    cold_mean = r.measure_cold(cold_reps)
     out = {"workload": w.name, "config": cfg, "tokens_per_s": w.B * w.T / per_step,
            "segments_per_chain": nseg,
            "ms_per_step": per_step * 1e3, "forward_us": fwd * 1e6,
-           "forward_us_cold_llc": cold_mean * 1e6, "forward_us_cold_llc_median": cold_median * 1e6,
+           "forward_us_cold_llc": cold_mean * 1e6, "input_copies": len(r.input_sets()),
            "forward_tokens_per_s": w.B * w.T / fwd,
            "roofline": roofline(w, flops, nbytes, cold_mean, kern, roofs, warm_seconds=fwd)}
     if w.kind == "linear" and w.d == 64 and w.b == 16:

@@ -24,9 +24,11 @@ def main():
     ap.add_argument("--decode", action="store_true", help="also run the workload's decode steps")
     ap.add_argument("--backward", action="store_true",
                     help="run ttt_linear_backward (seeded cotangents) instead of the forward")
-    ap.add_argument("--flush", action="store_true",
-                    help="read a 512 MB buffer before every call (the 256 MB last-level cache "
-                         "flushed, as bench.py's roofline timing does)")
+    ap.add_argument("--cold", action="store_true",
+                    help="cycle the calls through copies of the inputs, enough that at least "
+                         "512 MB of other inputs are read between two uses of a copy (the "
+                         "256 MB last-level cache cannot serve them), as bench.py's roofline "
+                         "timing does")
     ap.add_argument("--prologue", action="store_true",
                     help="with the input prologue (LayerNorm of q and k, per-token step sizes): "
                          "ttt_linear_forward_ex / ttt_linear_backward_ex")
@@ -64,12 +66,15 @@ def main():
         nbytes = (ttt.ttt_linear_backward_workspace_bytes if args.backward
                   else ttt.ttt_linear_workspace_bytes)(w.B, w.H, w.T, w.d, w.b, w.torch_dtype)
         ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
-    junk = torch.ones(512 * 1024 * 1024 // 4, device="cuda") if args.flush else None
-    sink = torch.empty((), device="cuda")
+    sets = [g]
+    if args.cold:
+        per_call = sum(g[k].numel() * g[k].element_size() for k in ("Q", "K", "V")) * 4 // 3
+        n = max(3, 1 + -(-512 * 10**6 // per_call))
+        sets += [dict(g, Q=g["Q"].clone(), K=g["K"].clone(), V=g["V"].clone())
+                 for _ in range(n - 1)]
     torch.cuda.synchronize()
-    for _ in range(args.reps):
-        if junk is not None:
-            torch.sum(junk, dim=0, out=sink)
+    for rep in range(args.reps):
+        g = sets[rep % len(sets)]
         if args.momentum:
             ttt.ttt_linear_momentum_forward(g["Q"], g["K"], g["V"], g["W0"], g["eta"], beta, w.b,
                                             None, gm, Y=Y, W_out=W, M_out=M, workspace=ws)
