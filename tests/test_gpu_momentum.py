@@ -179,3 +179,45 @@ def test_momentum_worked_examples_bit_exact(path):
         assert torch.equal(W[0, 0, :2, :2].cpu(), fr(case["W"])), case
         assert torch.equal(M[0, 0, :2, :2].cpu(), fr(case["M"])), case
         assert not Y[0, 0, :, 2:].float().any() and not W[0, 0, 2:].any()
+
+
+def test_momentum_graph_capture():
+    """Exact momentum steps (the inverse launch, then the scan) captured in a
+    HIP graph with the caller's workspace: every replay equals the eager call
+    bit for bit, with other eager work through the same workspace between
+    the replays."""
+    w = WORKLOADS[3].with_(B=2, H=6, T=1000)
+    announce("momentum graph capture")
+    g = to_gpu(make_inputs(w, 70))
+    beta = make_momentum(w, 71)["beta"].cuda()
+    nbytes = ttt.ttt_linear_momentum_workspace_bytes(w.B, w.H, w.T, 64, 16, torch.bfloat16, 0)
+    assert nbytes > 0
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    Y_e, W_e, M_e = ttt.ttt_linear_momentum_forward(g["Q"], g["K"], g["V"], g["W0"], g["eta"],
+                                                    beta, 16, None, 0, workspace=ws)
+    torch.cuda.synchronize()
+    Y, W, M = torch.empty_like(Y_e), torch.empty_like(W_e), torch.empty_like(M_e)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):          # warm the launch path off the capture
+        ttt.ttt_linear_momentum_forward(g["Q"], g["K"], g["V"], g["W0"], g["eta"], beta, 16,
+                                        None, 0, Y=Y, W_out=W, M_out=M, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        ttt.ttt_linear_momentum_forward(g["Q"], g["K"], g["V"], g["W0"], g["eta"], beta, 16,
+                                        None, 0, Y=Y, W_out=W, M_out=M, workspace=ws)
+    og = to_gpu(make_inputs(w.with_(B=1, H=4, T=700), 72))
+    obeta = make_momentum(w.with_(H=4), 73)["beta"].cuda()
+    for rep in range(3):
+        Y.zero_()
+        W.zero_()
+        M.zero_()
+        ws.fill_(0xff)
+        ttt.ttt_linear_momentum_forward(og["Q"], og["K"], og["V"], og["W0"], og["eta"], obeta,
+                                        16, None, 0, workspace=ws)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(Y, Y_e) and torch.equal(W, W_e) and torch.equal(M, M_e), rep
