@@ -405,7 +405,7 @@ int ttt_linear_segments(int64_t B, int64_t H, int64_t T, int d, int b, int qkv_d
  *                M_out = M0 (or zero).
  *   b            1 <= b <= 64.  bf16 Q/K/V with d = 64 and b = 16 run the
  *                MFMA kernels; other shapes run a plain fp32 kernel whose
- *                on-chip memory bounds b for d = 128 (b <= 20, else
+ *                on-chip memory bounds b for d = 128 (b <= 19, else
  *                TTT_ERR_UNSUPPORTED).
  *   workspace    caller-owned device memory of at least
  *                ttt_linear_momentum_workspace_bytes for these sizes (the
