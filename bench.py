@@ -395,6 +395,43 @@ class Runner:
         else:
             self.decode_eager()
 
+    def measure_decode_floor(self, reps=10):
+        """Per-step time of the decode graph replayed back to back (its
+        inputs then sit in the caches, as a projection just before would leave
+        them), and of a graph of as many empty launches of the step's grid
+        (B*H*ceil(d/32) workgroups of 64 threads): the launch floor."""
+        torch, ttt, w = self.torch, self.ttt, self.w
+        if getattr(self, "graph", None) is None:
+            return None
+        import ctypes
+        lib = ttt.load_library()
+        lib.ttt_roof_launch.argtypes = [ctypes.c_int64, ctypes.c_void_p]
+        groups = w.B * w.H * max(1, -(-w.d // 32))
+
+        def empties():
+            stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+            for _ in range(w.decode_steps):
+                ttt._check(lib.ttt_roof_launch(groups, stream))
+
+        empties()
+        torch.cuda.synchronize()
+        floor_graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(floor_graph):
+            empties()
+        torch.cuda.synchronize()
+        out = {}
+        for name, gr in (("cached_inputs", self.graph), ("empty_kernel", floor_graph)):
+            gr.replay()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(reps):
+                gr.replay()
+            b.record()
+            torch.cuda.synchronize()
+            out[name] = a.elapsed_time(b) * 1e3 / (reps * w.decode_steps)
+        return out
+
     def measure(self, steps, warmup):
         """Time exactly `steps` steps between two synchronisations.  HIP events
         on the launch stream mark the start, the end and (with decode steps)
@@ -639,6 +676,13 @@ def measure_workload(cfg, steps, warmup, cold_reps, roofs=None):
                          "hip_graph": r.graph is not None,
                          "GB_per_s": db / per / 1e9, "hbm_frac": db / per / PEAK_HBM,
                          "bytes_per_step": db}
+        floor = r.measure_decode_floor()
+        if floor:
+            # in the timed step the decode inputs come cold from HBM (the
+            # forward before them streams far more than the caches hold)
+            out["decode"]["us_per_step_cached_inputs"] = floor["cached_inputs"]
+            out["decode"]["launch_floor_us"] = floor["empty_kernel"]
+            out["decode"]["vs_launch_floor"] = per * 1e6 / floor["empty_kernel"]
     return w, r, out
 
 

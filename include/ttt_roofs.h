@@ -2,16 +2,19 @@
  * ttt_roofs.h -- measured roofs of the current device, exported by libttt.so
  * beside the TTT entry points of ttt.h.  The roofline fractions of the TTT
  * kernels are reported against the vendor's peak figures and against what
- * these two plain kernels reach on the same GPU:
+ * these plain kernels reach on the same GPU:
  *   - a streaming device-to-device copy (every byte read once and written
  *     once, 16-byte accesses, four loads in flight per thread): achievable
  *     HBM bandwidth = 2 * bytes / time;
  *   - a dense MFMA loop (each wave issues independent accumulation chains of
  *     one MFMA shape, no memory traffic): achievable matrix-core throughput
- *     = flops / time.
- * Both enqueue one kernel on `stream` and return without synchronising; the
+ *     = flops / time;
+ *   - an empty kernel: the floor of one launch, for steps as small as the
+ *     single-token decode step (timed per launch in a HIP graph of many).
+ * Each enqueues one kernel on `stream` and returns without synchronising; the
  * caller times them (e.g. with HIP events).  Errors: TTT_ERR_INVALID_ARG
- * (null pointer, negative or unaligned size, bad dtype, iters < 1),
+ * (null pointer, negative or unaligned size, bad dtype, iters < 1, fewer
+ * than one workgroup),
  * TTT_ERR_HIP (launch failed).
  */
 #ifndef TTT_ROOFS_H
@@ -39,6 +42,12 @@ int ttt_roof_copy(const void* src, void* dst, int64_t bytes, void* stream);
  * *flops when flops is not NULL (host memory).
  */
 int ttt_roof_mfma(float* out, int dtype, int64_t waves, int64_t iters, double* flops, void* stream);
+
+/*
+ * Launches an empty kernel of `workgroups` workgroups of 64 threads (1 to
+ * 2^31 - 1).  It reads and writes nothing.
+ */
+int ttt_roof_launch(int64_t workgroups, void* stream);
 
 #ifdef __cplusplus
 }

@@ -1,7 +1,8 @@
-// ttt_roofs.hip -- the two plain kernels behind include/ttt_roofs.h: a
-// streaming copy (achievable HBM bandwidth) and a dense MFMA loop (achievable
-// matrix-core throughput), so that the TTT kernels' roofline fractions can be
-// stated against this GPU's measured roofs as well as the datasheet peaks.
+// ttt_roofs.hip -- the plain kernels behind include/ttt_roofs.h: a streaming
+// copy (achievable HBM bandwidth), a dense MFMA loop (achievable matrix-core
+// throughput) and an empty kernel (the cost of one launch), so that the TTT
+// kernels' roofline fractions can be stated against this GPU's measured roofs
+// as well as the datasheet peaks.
 #include "ttt.h"
 #include "ttt_roofs.h"
 
@@ -72,6 +73,10 @@ __global__ void __launch_bounds__(256) roof_mfma_kernel(float* __restrict__ out,
     out[static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x] = s;
 }
 
+// No work: a launch of it costs only the dispatch and completion of its
+// workgroups.
+__global__ void __launch_bounds__(64) roof_launch_kernel() {}
+
 }  // namespace
 
 extern "C" {
@@ -108,6 +113,15 @@ int ttt_roof_mfma(float* out, int dtype, int64_t waves, int64_t iters, double* f
     else
         hipLaunchKernelGGL(roof_mfma_kernel<false>, grid, block, 0, static_cast<hipStream_t>(stream),
                            out, iters);
+    return hipGetLastError() == hipSuccess ? TTT_OK : TTT_ERR_HIP;
+}
+
+int ttt_roof_launch(int64_t workgroups, void* stream)
+{
+    if (workgroups < 1 || workgroups > 0x7fffffff)
+        return TTT_ERR_INVALID_ARG;
+    hipLaunchKernelGGL(roof_launch_kernel, dim3(static_cast<unsigned>(workgroups)), dim3(64), 0,
+                       static_cast<hipStream_t>(stream));
     return hipGetLastError() == hipSuccess ? TTT_OK : TTT_ERR_HIP;
 }
 

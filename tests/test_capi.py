@@ -41,7 +41,7 @@ def test_exports_every_declared_function(lib):
                           "ttt_linear_backward", "ttt_linear_forward_ex", "ttt_linear_segments",
                           "ttt_linear_backward_segments", "ttt_linear_decode_step_ex",
                           "ttt_linear_workspace_bytes", "ttt_linear_backward_workspace_bytes",
-                          "ttt_status_string", "ttt_roof_copy", "ttt_roof_mfma",
+                          "ttt_status_string", "ttt_roof_copy", "ttt_roof_mfma", "ttt_roof_launch",
                           "ttt_linear_forward_noalloc", "ttt_linear_noalloc_max_workspace_bytes",
                           "ttt_abi_version"}
     for n in names:
@@ -321,6 +321,9 @@ def test_roof_probe_validation(lib):
     assert lib.ttt_roof_mfma(YA, 2, 1024, 10, None, None) == INVALID
     assert lib.ttt_roof_mfma(YA, 1, 1022, 10, None, None) == INVALID
     assert lib.ttt_roof_mfma(YA, 0, 1024, 0, None, None) == INVALID
+    lib.ttt_roof_launch.argtypes = [ctypes.c_int64, ctypes.c_void_p]
+    assert lib.ttt_roof_launch(0, None) == INVALID
+    assert lib.ttt_roof_launch(1 << 31, None) == INVALID
 
 
 def test_noalloc_validation_and_limit(lib, monkeypatch):
