@@ -26,16 +26,19 @@ FLAGS = [
     f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}",
 ]
 
-# Per-file flags.  The TTT-Linear MFMA kernels (forward and backward) keep every MFMA accumulator in
-# ordinary VGPRs (they fit): otherwise the compiler places the results in
-# AGPRs and copies each one back to a VGPR before its VALU use, about a
-# quarter of the instructions of a chunk.  The TTT-MLP kernel needs the AGPRs
-# for its 192 registers of fast weights.
+# Per-file flags.  The MFMA kernels whose accumulators fit in VGPRs keep them
+# there: otherwise the compiler places MFMA results in AGPRs and copies each
+# one back to a VGPR before its VALU use (about a quarter of the instructions
+# of a chunk of the TTT-Linear scan, and about three thousand copies in the
+# momentum scans).  The TTT-MLP kernel's weights already sit in VGPRs without
+# the flag.
 EXTRA = {
     "ttt_linear_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "ttt_linear_mfma_f32.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "ttt_linear_backward.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "ttt_linear_cols_f32.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "ttt_linear_combine.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "ttt_momentum_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     # the MFMA loop of the measured roof: AGPR accumulators make the compiler
     # rotate them through VGPRs every iteration
     "ttt_roofs.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
