@@ -43,8 +43,9 @@ with LayerNorm of q and k and a step size per token fused into the scan, and
 "backward_prologue" ttt_linear_backward_ex, the backward through them.
 The bf16 TTT-Linear workloads also report "momentum": ttt_linear_momentum_forward
 (momentum gradient descent, beta per head from make_momentum) on the same
-inputs, for exact token steps and for chunk-start gradients, each timed on
-cycled input copies (cold cache) and back to back on one copy, with its own
+inputs, for exact token steps and for chunk-start gradients (sequence
+segments as ttt_linear_momentum_forward plans them), each timed on cycled
+input copies (cold cache) and back to back on one copy, with its own
 roofline object.
 """
 from __future__ import annotations
@@ -88,6 +89,9 @@ KERNEL_SOURCES = {
     "momentum_inverse_kernel": "ttt_momentum_mfma.hip",
     "momentum_mfma_kernel[exact]": "ttt_momentum_mfma.hip",
     "momentum_mfma_kernel[chunk_start]": "ttt_momentum_mfma.hip",
+    "momentum_mfma_kernel[exact+maps]": "ttt_momentum_mfma.hip",
+    "momentum_mfma_kernel[chunk_start+maps]": "ttt_momentum_mfma.hip",
+    "momentum_combine_kernel": "ttt_linear_combine.hip",
 }
 
 
@@ -664,8 +668,12 @@ def measure_workload(cfg, steps, warmup, cold_reps, roofs=None):
         for mode, gm in (("exact", 0), ("chunk_start", 1)):
             warm, cold = r.measure_momentum(max(3, steps // 2), 2, gm, max(3, cold_reps // 3))
             mf, mb = momentum_work(w, gm == 0)
-            kern = (["momentum_inverse_kernel"] if gm == 0 else []) + [f"momentum_mfma_kernel[{mode}]"]
+            nseg = r.ttt.ttt_linear_momentum_segments(w.B, w.H, w.T, w.d, w.b, w.torch_dtype, gm)
+            kern = ((["momentum_inverse_kernel"] if gm == 0 else []) +
+                    ([f"momentum_mfma_kernel[{mode}+maps]", "momentum_combine_kernel"]
+                     if nseg > 1 else []) + [f"momentum_mfma_kernel[{mode}]"])
             out["momentum"][mode] = {"us": warm * 1e6, "us_cold_llc": cold * 1e6,
+                                     "segments_per_chain": nseg,
                                      "tokens_per_s": w.B * w.T / warm,
                                      "roofline": roofline(w, mf, mb, cold, kern, roofs,
                                                           warm_seconds=warm)}

@@ -391,6 +391,12 @@ int ttt_linear_segments(int64_t B, int64_t H, int64_t T, int d, int b, int qkv_d
  * K K^T (one forward substitution per chunk), and the chunk-end W and M
  * follow from R with geometric sums of beta.  So b sets only the work split
  * when grad_mode = 0 (the result is the same up to rounding for every b).
+ * On the MFMA path a few long chains are split into sequence segments as in
+ * ttt_linear_forward: a chunk maps each column [W; M] of the state affinely,
+ * so each segment's map (A of 2d x 2d, N of 2d x d) is computed from the
+ * segment's inputs alone, the maps are composed into every segment's start
+ * state, and the segments then run at once
+ * (ttt_linear_momentum_segments gives the count).
  *
  *   Q, K, V, Y   as for ttt_linear_forward.
  *   W0           fp32, [H][d][d] (w0_per_batch = 0) or [B][H][d][d] (= 1).
@@ -407,11 +413,13 @@ int ttt_linear_segments(int64_t B, int64_t H, int64_t T, int d, int b, int qkv_d
  *                MFMA kernels; other shapes run a plain fp32 kernel whose
  *                on-chip memory bounds b for d = 128 (b <= 19, else
  *                TTT_ERR_UNSUPPORTED).
- *   workspace    caller-owned device memory of at least
- *                ttt_linear_momentum_workspace_bytes for these sizes (the
- *                per-chunk triangular inverses of exact steps on the MFMA
- *                path; 0 bytes elsewhere); must not overlap any other
- *                argument.
+ *   workspace    caller-owned device memory (must not overlap any other
+ *                argument): the per-chunk triangular inverses of exact steps
+ *                on the MFMA path, and with sequence segments their maps and
+ *                start states.  ttt_linear_momentum_workspace_bytes gives the
+ *                size of the planned split; less (down to what one segment
+ *                needs, 0 bytes off the MFMA path or for grad_mode 1) runs
+ *                with fewer segments.
  *
  * Errors: TTT_ERR_INVALID_ARG (null or overlapping buffers, grad_mode not 0
  * or 1, a workspace smaller than required), TTT_ERR_UNSUPPORTED (sizes as for
@@ -425,13 +433,27 @@ int ttt_linear_momentum_forward(const void* Q, const void* K, const void* V, int
                                 void* workspace, int64_t workspace_bytes, void* stream);
 
 /*
- * Workspace bytes ttt_linear_momentum_forward needs for these sizes:
- * B*H*ceil(T/32)*1024 for exact steps on the MFMA path (one 16x16 bf16
- * inverse per chunk of 16 tokens, stored in pairs), else 0.  Negative ttt_status for sizes the call
- * would reject.
+ * Workspace bytes ttt_linear_momentum_forward uses for these sizes with its
+ * planned number S of sequence segments: for exact steps on the MFMA path
+ * B*H*ceil(T/32)*1024 (one 16x16 bf16 inverse per chunk of 16 tokens, stored
+ * in pairs), rounded up to 256; with S > 1 also B*H*(S-1)*6*d*d*4 (the
+ * segments' maps, rounded up to 256) plus B*H*S*2*d*d*4 (their start
+ * states); 0 when none of these apply.  Negative ttt_status for sizes the
+ * call would reject.
  */
 int64_t ttt_linear_momentum_workspace_bytes(int64_t B, int64_t H, int64_t T, int d, int b,
                                             int qkv_dtype, int grad_mode);
+
+/*
+ * Sequence segments per (batch, head) chain that ttt_linear_momentum_forward
+ * plans for these sizes with the workspace of
+ * ttt_linear_momentum_workspace_bytes (1: no split; only the bf16 MFMA path
+ * splits), or a negative ttt_status.  The environment variable
+ * TTT_MOMENTUM_SEGMENTS=S (1 <= S <= 12) forces S segments (each a multiple
+ * of 32 tokens, so fewer for short sequences).
+ */
+int ttt_linear_momentum_segments(int64_t B, int64_t H, int64_t T, int d, int b, int qkv_dtype,
+                                 int grad_mode);
 
 /* Static, human-readable text for a status code (never NULL). */
 const char* ttt_status_string(int status);

@@ -86,6 +86,8 @@ def load_library():
     lib.ttt_linear_momentum_forward.restype = I
     lib.ttt_linear_momentum_workspace_bytes.argtypes = [L, L, L, I, I, I, I]
     lib.ttt_linear_momentum_workspace_bytes.restype = L
+    lib.ttt_linear_momentum_segments.argtypes = [L, L, L, I, I, I, I]
+    lib.ttt_linear_momentum_segments.restype = I
     lib.ttt_status_string.argtypes = [I]
     lib.ttt_status_string.restype = ctypes.c_char_p
     lib.ttt_abi_version.argtypes = []
@@ -513,10 +515,22 @@ def ttt_linear_momentum_forward(Q, K, V, W0, eta, beta, b: int = 16, M0=None, gr
 
 def ttt_linear_momentum_workspace_bytes(B: int, H: int, T: int, d: int, b: int,
                                         dtype=torch.bfloat16, grad_mode: int = 0) -> int:
-    """Workspace bytes ttt_linear_momentum_forward needs for these sizes."""
+    """Workspace bytes ttt_linear_momentum_forward uses for these sizes on the
+    current device (its planned sequence segments included)."""
     code = TTT_F32 if dtype == torch.float32 else TTT_BF16
     n = load_library().ttt_linear_momentum_workspace_bytes(int(B), int(H), int(T), int(d),
                                                            int(b), code, int(grad_mode))
+    _check(min(n, 0))
+    return n
+
+
+def ttt_linear_momentum_segments(B: int, H: int, T: int, d: int, b: int,
+                                 dtype=torch.bfloat16, grad_mode: int = 0) -> int:
+    """Sequence segments ttt_linear_momentum_forward cuts each chain into for
+    these sizes on the current device (1 = unsegmented)."""
+    code = TTT_F32 if dtype == torch.float32 else TTT_BF16
+    n = load_library().ttt_linear_momentum_segments(int(B), int(H), int(T), int(d), int(b), code,
+                                                    int(grad_mode))
     _check(min(n, 0))
     return n
 
@@ -566,7 +580,7 @@ __all__ = [
     "ttt_linear_decode_step_ex", "ttt_linear_backward",
     "ttt_linear_segments", "ttt_linear_backward_segments", "ttt_linear_workspace_bytes",
     "ttt_linear_backward_workspace_bytes", "ttt_linear_momentum_forward",
-    "ttt_linear_momentum_workspace_bytes",
+    "ttt_linear_momentum_workspace_bytes", "ttt_linear_momentum_segments",
     "load_library",
     "status_string", "TTTError", "LIB_PATH", "TTT_F32", "TTT_BF16",
 ]

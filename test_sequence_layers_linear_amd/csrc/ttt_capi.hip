@@ -20,7 +20,7 @@ using ttt::MlpArgs;
 using ttt::DecodeArgs;
 using ttt::MomentumArgs;
 
-constexpr int kAbiVersion = (2 << 16) | 1;
+constexpr int kAbiVersion = (2 << 16) | 2;
 
 bool valid_dtype(int dt) { return dt == TTT_F32 || dt == TTT_BF16; }
 size_t elem_bytes(int dt) { return dt == TTT_F32 ? 4 : 2; }
@@ -94,22 +94,22 @@ ttt::SegmentPlan with_segments(int64_t T, int chunk, int S)
     return p;
 }
 
-// Segment count for a chain-parallel scan of `units` chains of T tokens whose
-// maps and start states must fit in `ws_bytes` of workspace.  Each launch of
-// the split runs all its workgroups at once, one per CU (more would queue or
-// share CUs and stretch the slowest ones), so S is limited to what fits;
-// within that it minimises
+// Segment count for a chain-parallel scan of `units` chains of T tokens in
+// units of `chunk` tokens, whose maps and start states for S segments must
+// fit the workspace (`fits`).  Each launch of the split runs all its
+// workgroups at once, one per CU (more would queue or share CUs and stretch
+// the slowest ones), so S is limited to what fits; within that it minimises
 //   ceil(chunks / S) (map + fwd) + (S - 1) apply + launch
 // against the unsplit chunks * fwd (costs measured on MI355X).
-// TTT_LINEAR_SEGMENTS=S (1 <= S <= kMaxSegments) forces S segments (at least
-// one chunk each; fewer if the workspace is too small), for tests and tuning.
-ttt::SegmentPlan plan_segments(int64_t units, int64_t T, int chunk, int d,
-                               const ttt::SegmentCosts& cost, int64_t ws_bytes)
+// The environment variable `env_name` = S (1 <= S <= max_s) forces S
+// segments (at least one chunk each; fewer if the workspace is too small),
+// for tests and tuning.
+ttt::SegmentPlan plan_split(int64_t units, int64_t T, int chunk, const ttt::SegmentCosts& cost,
+                            const std::function<bool(int)>& fits, const char* env_name, int max_s)
 {
     const int64_t chunks = (T + chunk - 1) / chunk;
-    auto fits = [&](int S) { return forward_workspace_bytes(units, d, S) <= ws_bytes; };
-    if (const char* env = getenv("TTT_LINEAR_SEGMENTS")) {
-        long S = std::min<long>(strtol(env, nullptr, 10), ttt::kMaxSegments);
+    if (const char* env = getenv(env_name)) {
+        long S = std::min<long>(strtol(env, nullptr, 10), max_s);
         if (S >= 1 && chunks > 0) {
             S = std::min<long>(S, chunks);
             while (S > 1 && !fits(static_cast<int>(with_segments(T, chunk, static_cast<int>(S)).nseg)))
@@ -122,7 +122,7 @@ ttt::SegmentPlan plan_segments(int64_t units, int64_t T, int chunk, int d,
     if (cus <= 0 || 2 * scan_blocks > cus || chunks < 4) return with_segments(T, chunk, 1);
     double best = static_cast<double>(chunks) * cost.fwd;
     int best_s = 1;
-    for (int S = 2; S <= ttt::kMaxSegments; ++S) {
+    for (int S = 2; S <= max_s; ++S) {
         if (scan_blocks * S > cus ||
             units * (S - 1) * cost.map_blocks_per_segment > cost.map_blocks_per_cu * cus)
             break;
@@ -133,6 +133,14 @@ ttt::SegmentPlan plan_segments(int64_t units, int64_t T, int chunk, int d,
         if (t < best) { best = t; best_s = S; }
     }
     return with_segments(T, chunk, best_s);
+}
+
+ttt::SegmentPlan plan_segments(int64_t units, int64_t T, int chunk, int d,
+                               const ttt::SegmentCosts& cost, int64_t ws_bytes)
+{
+    return plan_split(units, T, chunk, cost,
+                      [&](int S) { return forward_workspace_bytes(units, d, S) <= ws_bytes; },
+                      "TTT_LINEAR_SEGMENTS", ttt::kMaxSegments);
 }
 
 // Segment count for the backward of a TTT-Linear scan: each segment pays
@@ -659,13 +667,39 @@ int ttt_linear_decode_step_ex(const void* q, const void* k, const void* v, int q
 
 namespace {
 
-// The launch configuration a momentum forward of these sizes takes:
-// workspace bytes it needs, or a negative ttt_status.
-int64_t momentum_plan(const MomentumArgs& a)
+// Tokens per unit of a momentum segment: a stage of two chunks (the chunk
+// inverses are stored per stage).
+constexpr int kMomentumStage = 32;
+
+// Segments of a momentum forward of these sizes with `ws_bytes` of
+// workspace (the bf16 MFMA scan only; one segment otherwise).
+// TTT_MOMENTUM_SEGMENTS=S forces S segments.
+ttt::SegmentPlan plan_momentum(const MomentumArgs& a, int64_t ws_bytes)
+{
+    const int64_t units = a.B * a.H;
+    if (!ttt::momentum_mfma_supports(a) || units == 0 || a.T == 0)
+        return with_segments(a.T, kMomentumStage, 1);
+    const ttt::SegmentCosts& cost =
+        a.grad_mode == 0 ? ttt::kMomentumExactCosts : ttt::kMomentumChunkStartCosts;
+    return plan_split(units, a.T, kMomentumStage, cost,
+                      [&](int S) {
+                          return S <= 1 || (S <= ttt::kMaxMomentumSegments &&
+                                            ttt::momentum_combine_lds_bytes(S) <=
+                                                static_cast<size_t>(ttt::kMaxLdsBytes) &&
+                                            ttt::momentum_mfma_workspace_bytes(a, S) <= ws_bytes);
+                      },
+                      "TTT_MOMENTUM_SEGMENTS", ttt::kMaxMomentumSegments);
+}
+
+// The launch configuration a momentum forward of these sizes takes: the
+// workspace bytes it needs with `ws_bytes` available (INT64_MAX: the planned
+// split's; the least is that of one segment), or a negative ttt_status.
+int64_t momentum_plan(const MomentumArgs& a, int64_t ws_bytes = INT64_MAX)
 {
     if (const int st = linear_sizes_status(a.B, a.H, a.T, a.d, a.b, a.dtype)) return st;
     if (a.grad_mode != 0 && a.grad_mode != 1) return TTT_ERR_INVALID_ARG;
-    if (ttt::momentum_mfma_supports(a)) return ttt::momentum_mfma_workspace_bytes(a);
+    if (ttt::momentum_mfma_supports(a))
+        return ttt::momentum_mfma_workspace_bytes(a, plan_momentum(a, ws_bytes).nseg);
     if (ttt::momentum_generic_lds_bytes(a.d, a.b) > static_cast<size_t>(ttt::kMaxLdsBytes))
         return TTT_ERR_UNSUPPORTED;
     return 0;
@@ -686,7 +720,8 @@ int ttt_linear_momentum_forward(const void* Q, const void* K, const void* V, int
     if (workspace_bytes < 0 || (workspace_bytes > 0 && !workspace)) return TTT_ERR_INVALID_ARG;
     MomentumArgs a{Q, K, V, qkv_dtype, W0, w0_per_batch, M0, eta, beta, grad_mode,
                    B, H, T, d, b, Y, W_out, M_out, static_cast<hipStream_t>(stream)};
-    const int64_t need = momentum_plan(a);
+    // the least workspace: that of one segment
+    const int64_t need = momentum_plan(a, 0);
     if (need < 0) return static_cast<int>(need);
     const int64_t units = B * H;
     if (units == 0) return TTT_OK;
@@ -713,7 +748,10 @@ int ttt_linear_momentum_forward(const void* Q, const void* K, const void* V, int
     for (const Range& in : {rQ, rK, rV, rW0, rM0, rEta, rBeta})
         if (overlap(rWs, in)) return TTT_ERR_INVALID_ARG;
 
-    if (ttt::momentum_mfma_supports(a)) return hip_status(ttt::launch_momentum_mfma(a, workspace));
+    if (ttt::momentum_mfma_supports(a)) {
+        const ttt::SegmentPlan p = plan_momentum(a, workspace_bytes);
+        return hip_status(ttt::launch_momentum_mfma(a, workspace, p.nseg, p.seg_len));
+    }
     return hip_status(ttt::launch_momentum_generic(a));
 }
 
@@ -725,6 +763,18 @@ int64_t ttt_linear_momentum_workspace_bytes(int64_t B, int64_t H, int64_t T, int
     a.grad_mode = grad_mode;
     a.B = B; a.H = H; a.T = T; a.d = d; a.b = b;
     return momentum_plan(a);
+}
+
+int ttt_linear_momentum_segments(int64_t B, int64_t H, int64_t T, int d, int b, int qkv_dtype,
+                                 int grad_mode)
+{
+    MomentumArgs a{};
+    a.dtype = qkv_dtype;
+    a.grad_mode = grad_mode;
+    a.B = B; a.H = H; a.T = T; a.d = d; a.b = b;
+    const int64_t st = momentum_plan(a);
+    if (st < 0) return static_cast<int>(st);
+    return plan_momentum(a, INT64_MAX).nseg;
 }
 
 }  // extern "C"

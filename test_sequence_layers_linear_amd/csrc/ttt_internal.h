@@ -312,7 +312,19 @@ hipError_t launch_momentum_generic(const MomentumArgs& a);
 // need a workspace of momentum_mfma_workspace_bytes for the per-chunk
 // triangular inverses.
 bool momentum_mfma_supports(const MomentumArgs& a);
-int64_t momentum_mfma_workspace_bytes(const MomentumArgs& a);
-hipError_t launch_momentum_mfma(const MomentumArgs& a, void* workspace);
+int64_t momentum_mfma_workspace_bytes(const MomentumArgs& a, int nseg);
+hipError_t launch_momentum_mfma(const MomentumArgs& a, void* workspace, int nseg, int64_t seg_len);
+// Start states [W; M] of the segments of a segmented momentum scan from the
+// segments' maps (ttt_linear_combine.hip): xstart [units][nseg][2d][d].
+hipError_t launch_momentum_combine(const MomentumArgs& a, const float* maps, int nseg,
+                                   float* xstart);
+size_t momentum_combine_lds_bytes(int nseg);
+// most segments per chain of the momentum scan (its start states, 2d rows
+// each, stay in the combine's LDS)
+constexpr int kMaxMomentumSegments = 12;
+// per-chunk latencies (us) of the bf16 momentum scan and its maps (three
+// workgroups per segment: the W and M basis columns and the V columns)
+constexpr SegmentCosts kMomentumExactCosts{0.50, 0.50, 1.2, 10.0, 3, 1, 2};
+constexpr SegmentCosts kMomentumChunkStartCosts{0.43, 0.43, 1.2, 10.0, 3, 1, 2};
 
 }  // namespace ttt

@@ -1,5 +1,5 @@
 // ttt_linear_combine.hip -- start states of the segments of a segmented
-// TTT-Linear scan.
+// TTT-Linear scan, with or without momentum.
 //
 // A chunk of the scan maps the fast weights affinely,
 //     W' = (I - eta K^T K) W + eta K^T V
@@ -7,21 +7,24 @@
 // chunk-start W: "Test-Time Training Layers: How Inner-Loop Gradient Descent
 // Replaces the Transformer KV Cache ...", sections "The Core Mechanism" and
 // "Hardware Parallelization"), so a segment of chunks does too:
-// W_end = M W_start + N.  Given the maps (M_j, N_j) of segments
-// 0 .. nseg - 2, this kernel computes
-//     W_0 = W0,   W_{j+1} = M_j W_j + N_j
-// and stores every W_j.  The segments then run their scans independently.
+// W_end = M W_start + N.  With momentum (the E2-TTT write-up on zhichai.net,
+// section "Core Math") a chunk maps the pair X = [W; M] (2d rows) affinely in
+// the same way, column by column.  Given the maps (M_j, N_j) of segments
+// 0 .. nseg - 2 (M_j of kRows x kRows, N_j of kRows x d), this kernel computes
+//     X_0 = [W0; M0],   X_{j+1} = M_j X_j + N_j
+// and stores every X_j.  The segments then run their scans independently.
 //
-// Column j of W_{j+1} depends only on column j of W_j, so one chain is split
+// Column j of X_{j+1} depends only on column j of X_j, so one chain is split
 // over 4 workgroups, one per 16-column slice J (all on the XCD of the chain's
 // maps and scans); wave I of a workgroup computes
 // the 16 x 16 output tile (I, J) of each step in fp32 on
-// v_mfma_f32_16x16x4_f32 (16 k-steps in 4 independent accumulators).  Every
-// slice W_j stays in LDS (rows padded to 17 floats, so the four rows 16 g + s
-// a wave reads per k-step fall in different banks) and goes to memory at the end, so
-// the only memory operations inside the loop are the loads of the M and N
-// operands, kDepth steps ahead in a ring of register sets: the maps were just
-// written by other CUs, so each load costs a trip to memory.
+// v_mfma_f32_16x16x4_f32 (kRows / 4 k-steps in 4 independent accumulators).
+// Every slice X_j stays in LDS (rows padded to 17 floats, so the four rows
+// kRows / 4 g + s a wave reads per k-step fall in different banks) and goes to
+// memory at the end, so the only memory operations inside the loop are the
+// loads of the M and N operands, kDepth steps ahead in a ring of register
+// sets: the maps were just written by other CUs, so each load costs a trip to
+// memory.
 #include "ttt_internal.h"
 
 namespace ttt {
@@ -29,30 +32,47 @@ namespace {
 
 constexpr int kD = 64;
 constexpr int kSlice = 16;
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
 constexpr int kPad = kSlice + 1;
-constexpr int kSliceFloats = kD * kPad;
-constexpr int kDepth = 6;                // steps of operands in flight
+
+template <int kRows>
+struct Shape {
+    static constexpr int kWaves = kRows / 16;          // one row tile each
+    static constexpr int kThreads = 64 * kWaves;
+    static constexpr int kSliceFloats = kRows * kPad;
+    static constexpr int kK = kRows / 4;               // k-steps per product (k-slot g: column kK g + s)
+    static constexpr int kDepth = kRows == 64 ? 6 : 3; // steps of operands in flight
+    static constexpr int64_t kMapFloats = static_cast<int64_t>(kRows) * kRows + kRows * kD;
+};
+
+template <int kRows>
+size_t combine_lds_bytes(int nseg)
+{
+    using S = Shape<kRows>;
+    return static_cast<size_t>(nseg + S::kDepth) * S::kSliceFloats * 4;
+}
 
 }  // namespace
 
 // LDS of one combine workgroup for a chain of nseg segments (kDepth spare
 // slots beyond the nseg start states)
-size_t linear_combine_lds_bytes(int nseg)
-{
-    return static_cast<size_t>(nseg + kDepth) * kSliceFloats * 4;
-}
+size_t linear_combine_lds_bytes(int nseg) { return combine_lds_bytes<64>(nseg); }
+size_t momentum_combine_lds_bytes(int nseg) { return combine_lds_bytes<128>(nseg); }
 
 namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-__global__ void __launch_bounds__(kThreads, 1)
-linear_combine_kernel(const float* W0, int w0_per_batch, int H, int64_t units,
-                      const float* __restrict__ maps, int nseg, float* __restrict__ wstart)
+// X_0 = [W0; M0] (rows kD .. kRows - 1 from M0 when kRows > kD; zero without
+// M0), then the composition; xstart: [units][nseg][kRows][kD]
+template <int kRows>
+__device__ __forceinline__ void combine_chain(const float* W0, int w0_per_batch, const float* M0,
+                                              int H, int64_t units, const float* __restrict__ maps,
+                                              int nseg, float* __restrict__ xstart)
 {
-    extern __shared__ float Wl[];        // [nseg][64][kPad]: slice J of W_0 .. W_{nseg-1}
+    using S = Shape<kRows>;
+    constexpr int kDepth = S::kDepth;
+    constexpr int kK = S::kK;
+    extern __shared__ float Wl[];        // [nseg][kRows][kPad]: slice J of X_0 .. X_{nseg-1}
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -77,32 +97,36 @@ linear_combine_kernel(const float* W0, int w0_per_batch, int H, int64_t units,
         return;
     const int h = static_cast<int>(u % H);
     const float* w0 = W0 + (w0_per_batch ? u : h) * kD * kD;
-    float* out = wstart + u * nseg * kD * kD;
-    const float* chain_maps = maps + u * (nseg - 1) * 2 * kD * kD;
+    const float* m0 = M0 ? M0 + u * kD * kD : nullptr;
+    float* out = xstart + u * nseg * kRows * kD;
+    const float* chain_maps = maps + u * (nseg - 1) * S::kMapFloats;
 
-    // thread tid moves rows tid / 16 + 16 q, column tid % 16 of a slice
+    // thread tid moves rows tid / 16 + (kRows / 4) q, column tid % 16 of a slice
     {
         float x[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-            x[q] = w0[(tid / 16 + 16 * q) * kD + 16 * J + tid % 16];
+        for (int q = 0; q < 4; ++q) {
+            const int row = tid / 16 + (kRows / 4) * q;
+            x[q] = row < kD ? w0[row * kD + 16 * J + tid % 16]
+                            : (m0 ? m0[(row - kD) * kD + 16 * J + tid % 16] : 0.f);
+        }
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-            Wl[(tid / 16 + 16 * q) * kPad + tid % 16] = x[q];
+            Wl[(tid / 16 + (kRows / 4) * q) * kPad + tid % 16] = x[q];
     }
 
-    // operands of step j: a[s] = M_j[16 I + c][16 g + s] (A of k-step s, whose
-    // k-slot g is row 16 g + s of W_j: one contiguous 64-byte run of M per
-    // lane) and n[r] = N_j[16 I + 4 g + r][16 J + c] (the accumulator's start
-    // value); steps past the last one reload the last map (results unused)
-    f32x4 a[kDepth][4];
+    // operands of step j: a[s] = M_j[16 I + c][kK g + s] (A of k-step s, whose
+    // k-slot g is row kK g + s of X_j: one contiguous run of M per lane) and
+    // n[r] = N_j[16 I + 4 g + r][16 J + c] (the accumulator's start value);
+    // steps past the last one reload the last map (results unused)
+    f32x4 a[kDepth][kK / 4];
     f32x4 n[kDepth];
-    auto load_ops = [&](f32x4 (&dst)[4], f32x4& ndst, int j) {
-        const float* M = chain_maps + min(j, nseg - 2) * 2 * kD * kD;
-        const float* N = M + kD * kD;
+    auto load_ops = [&](f32x4 (&dst)[kK / 4], f32x4& ndst, int j) {
+        const float* M = chain_maps + min(j, nseg - 2) * S::kMapFloats;
+        const float* N = M + kRows * kRows;
 #pragma unroll
-        for (int x = 0; x < 4; ++x)
-            dst[x] = *reinterpret_cast<const f32x4*>(M + (16 * I + c) * kD + 16 * g + 4 * x);
+        for (int x = 0; x < kK / 4; ++x)
+            dst[x] = *reinterpret_cast<const f32x4*>(M + (16 * I + c) * kRows + kK * g + 4 * x);
 #pragma unroll
         for (int r = 0; r < 4; ++r)
             ndst[r] = N[(16 * I + 4 * g + r) * kD + 16 * J + c];
@@ -112,21 +136,21 @@ linear_combine_kernel(const float* W0, int w0_per_batch, int H, int64_t units,
         load_ops(a[q], n[q], q);             // nseg >= 2 whenever this kernel runs
     __syncthreads();
 
-    // step j with the operands of ring entry q: W_{j+1} slice into LDS, then
+    // step j with the operands of ring entry q: X_{j+1} slice into LDS, then
     // the ring entry reloaded for step j + kDepth
     auto step = [&](int q, int j) {
-        const float* Wc = Wl + j * kSliceFloats;
-        float b[16];
+        const float* Wc = Wl + j * S::kSliceFloats;
+        float b[kK];
 #pragma unroll
-        for (int s = 0; s < 16; ++s)
-            b[s] = Wc[(16 * g + s) * kPad + c];
+        for (int s = 0; s < kK; ++s)
+            b[s] = Wc[(kK * g + s) * kPad + c];
         f32x4 acc[4] = {n[q], {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-        for (int s = 0; s < 16; ++s)
+        for (int s = 0; s < kK; ++s)
             acc[s & 3] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[q][s >> 2][s & 3], b[s], acc[s & 3],
                                                               0, 0, 0);
         const f32x4 res = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-        float* Wn = Wl + (j + 1) * kSliceFloats;
+        float* Wn = Wl + (j + 1) * S::kSliceFloats;
 #pragma unroll
         for (int r = 0; r < 4; ++r)
             Wn[(16 * I + 4 * g + r) * kPad + c] = res[r];
@@ -149,34 +173,65 @@ linear_combine_kernel(const float* W0, int w0_per_batch, int H, int64_t units,
     }
 
     for (int j = 0; j < nseg; ++j) {
-        const float* Ws = Wl + j * kSliceFloats;
-        float* o = out + j * kD * kD;
+        const float* Ws = Wl + j * S::kSliceFloats;
+        float* o = out + j * kRows * kD;
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-            o[(tid / 16 + 16 * q) * kD + 16 * J + tid % 16] = Ws[(tid / 16 + 16 * q) * kPad + tid % 16];
+            o[(tid / 16 + (kRows / 4) * q) * kD + 16 * J + tid % 16] =
+                Ws[(tid / 16 + (kRows / 4) * q) * kPad + tid % 16];
     }
+}
+
+__global__ void __launch_bounds__(Shape<64>::kThreads, 1)
+linear_combine_kernel(const float* W0, int w0_per_batch, int H, int64_t units,
+                      const float* __restrict__ maps, int nseg, float* __restrict__ wstart)
+{
+    combine_chain<64>(W0, w0_per_batch, nullptr, H, units, maps, nseg, wstart);
+}
+
+__global__ void __launch_bounds__(Shape<128>::kThreads, 1)
+momentum_combine_kernel(const float* W0, int w0_per_batch, const float* M0, int H, int64_t units,
+                        const float* __restrict__ maps, int nseg, float* __restrict__ xstart)
+{
+    combine_chain<128>(W0, w0_per_batch, M0, H, units, maps, nseg, xstart);
+}
+
+template <int kRows, typename Kernel, typename... Args>
+hipError_t launch_combine(Kernel kernel, int64_t units, int nseg, hipStream_t stream, Args... args)
+{
+    const size_t lds = combine_lds_bytes<kRows>(nseg);
+    if (lds > static_cast<size_t>(kMaxLdsBytes))
+        return hipErrorInvalidValue;
+    if (lds > 64 * 1024) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                 static_cast<int>(lds));
+        if (e != hipSuccess)
+            return e;
+    }
+    const int64_t blocks = units < 8 ? 4 * units : 32 * ((units + 7) / 8);
+    hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(blocks)), dim3(Shape<kRows>::kThreads),
+                       lds, stream, args...);
+    return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_linear_combine(const LinearArgs& a, const SegmentPlan& p)
 {
-    const size_t lds = linear_combine_lds_bytes(p.nseg);
-    if (lds > static_cast<size_t>(kMaxLdsBytes))
-        return hipErrorInvalidValue;
-    if (lds > 64 * 1024) {
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(linear_combine_kernel),
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                 static_cast<int>(lds));
-        if (e != hipSuccess)
-            return e;
-    }
     const int64_t units = a.B * a.H;
-    const int64_t blocks = units < 8 ? 4 * units : 32 * ((units + 7) / 8);
-    hipLaunchKernelGGL(linear_combine_kernel, dim3(static_cast<unsigned>(blocks)),
-                       dim3(kThreads), lds, a.stream, a.W0, a.w0_per_batch, static_cast<int>(a.H), units,
-                       p.maps, p.nseg, p.wstart);
-    return hipGetLastError();
+    return launch_combine<64>(linear_combine_kernel, units, p.nseg, a.stream, a.W0,
+                              a.w0_per_batch, static_cast<int>(a.H), units,
+                              static_cast<const float*>(p.maps), p.nseg, p.wstart);
+}
+
+hipError_t launch_momentum_combine(const MomentumArgs& a, const float* maps, int nseg,
+                                   float* xstart)
+{
+    const int64_t units = a.B * a.H;
+    return launch_combine<128>(momentum_combine_kernel, units, nseg, a.stream, a.W0,
+                               a.w0_per_batch, a.M0, static_cast<int>(a.H), units, maps, nseg,
+                               xstart);
 }
 
 }  // namespace ttt

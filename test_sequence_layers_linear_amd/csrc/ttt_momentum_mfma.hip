@@ -162,7 +162,17 @@ struct ScanParams {
     const float* eta; const float* beta; int H; int T;
     const unsigned char* pinv;
     uint16_t* Y; float* W_out; float* M_out;
+    int64_t units;
+    // sequence segments: nseg of seg_len tokens (a multiple of a stage; the
+    // last one shorter), the maps of segments 0 .. nseg - 2 and the start
+    // states [W; M] of every segment ([units][nseg][2][d][d])
+    int nseg; int seg_len;
+    float* maps; const float* xstart;
 };
+
+// a segment's map: A (2d x 2d, acting on a column [W; M] of the state), then
+// N (2d x d), row-major
+constexpr int64_t kMapFloats = 4 * kD * kD + 2 * kD * kD;
 
 // update weights of a chunk of n tokens, for this lane's C-tile rows
 // t = 4g + e: W gets -eta dsum_{n-1-t} R[t], M gets beta^{n-1-t} R[t]; the
@@ -187,31 +197,55 @@ __device__ __forceinline__ Coef chunk_coef(float et, float bt, int n, int g)
     return cf;
 }
 
-template <bool kExact, bool kMom>
+// One chain, or one segment `seg` of it.  kMap: the segment's affine map
+// instead of its outputs.  A segment maps each column [W; M] of the state to
+// A [W; M] + n (the recurrence treats the d columns alike, n from column j
+// of V), so the map is the segment run on 3d columns with no readout: part 0
+// starts from W = e_j, M = 0 and part 1 from W = 0, M = e_j with V = 0 (the
+// columns of A), part 2 from zero with V (N).
+template <bool kExact, bool kMom, bool kMap>
 __device__ __forceinline__ void scan_chain(const ScanParams& p, unsigned char* lds, int64_t u,
-                                           int h)
+                                           int h, int seg, int part)
 {
     const int lane = threadIdx.x & 63;
     const int w = threadIdx.x >> 6;
     const int c = lane & 15;
     const int g = lane >> 4;
     const int col = 16 * w + c;
-    const int T = p.T;
+    // the segment's tokens [t_begin, t_begin + T) of the chain
+    const int64_t t_begin = static_cast<int64_t>(seg) * p.seg_len;
+    const int T = p.nseg > 1 ? static_cast<int>(min(static_cast<int64_t>(p.seg_len), p.T - t_begin))
+                             : p.T;
     const float et = p.eta[h];
     const float bt = kMom ? p.beta[h] : 0.f;
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 
     // W and M: acc[mt][r] = X[rho(mt, 4g + r)][col]
     f32x4 Wacc[4], Macc[4];
-    const float* w0 = p.W0 + (p.w0_per_batch ? u : h) * kD * kD;
-    const float* m0 = p.M0 ? p.M0 + u * kD * kD : nullptr;
+    if constexpr (kMap) {
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+        for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            Wacc[mt][r] = w0[rho(mt, 4 * g + r) * kD + col];
-            Macc[mt][r] = m0 ? m0[rho(mt, 4 * g + r) * kD + col] : 0.f;
+            for (int r = 0; r < 4; ++r) {
+                const float e = rho(mt, 4 * g + r) == col ? 1.f : 0.f;
+                Wacc[mt][r] = part == 0 ? e : 0.f;
+                Macc[mt][r] = part == 1 ? e : 0.f;
+            }
+    } else {
+        const float* w0 = p.W0 + (p.w0_per_batch ? u : h) * kD * kD;
+        const float* m0 = p.M0 ? p.M0 + u * kD * kD : nullptr;
+        if (p.nseg > 1) {
+            w0 = p.xstart + (u * p.nseg + seg) * 2 * kD * kD;
+            m0 = w0 + kD * kD;
         }
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                Wacc[mt][r] = w0[rho(mt, 4 * g + r) * kD + col];
+                Macc[mt][r] = m0 ? m0[rho(mt, 4 * g + r) * kD + col] : 0.f;
+            }
+    }
 
     // -I as the B operand of a 16x16x16 product: B[k = 4g + r][n = c] = -(k == n)
     bf16x4 neg_eye;
@@ -236,15 +270,17 @@ __device__ __forceinline__ void scan_chain(const ScanParams& p, unsigned char* l
     const Coef full = chunk_coef(et, bt, kB, g);
     const Coef tail = chunk_coef(et, bt, T % kB, g);
 
-    const int64_t base = u * static_cast<int64_t>(T) * kD;
+    const int64_t base = (u * static_cast<int64_t>(p.T) + t_begin) * kD;
     const int64_t bytes = static_cast<int64_t>(T) * kD * 2;
     const __amdgpu_buffer_rsrc_t rq = buffer_rsrc(p.Q + base, bytes);
     const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(p.K + base, bytes);
     const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(p.V + base, bytes);
     const __amdgpu_buffer_rsrc_t ry = buffer_rsrc(p.Y + base, bytes);
     const int nstages = (T + kStageTokens - 1) / kStageTokens;
+    // the chain's P, from the segment's first stage on
+    const int64_t pstage = u * ((p.T + kStageTokens - 1) / kStageTokens) + t_begin / kStageTokens;
     const __amdgpu_buffer_rsrc_t rp =
-        buffer_rsrc(kExact ? p.pinv + u * nstages * static_cast<int64_t>(kPinvStageBytes) : p.pinv,
+        buffer_rsrc(kExact ? p.pinv + pstage * kPinvStageBytes : p.pinv,
                     kExact ? static_cast<int64_t>(nstages) * kPinvStageBytes : 0);
 
     struct StageRegs {
@@ -255,7 +291,8 @@ __device__ __forceinline__ void scan_chain(const ScanParams& p, unsigned char* l
     auto load_stage = [&](StageRegs& o, int stage) {
         const int off = (stage * kStageTokens + st_row) * kRowBytes + st_seg * 16;
         o.k = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
-        o.q = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0);
+        if constexpr (!kMap)
+            o.q = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0);
         o.v = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0);
         if (kExact)
             o.pv = __builtin_amdgcn_raw_buffer_load_b128(rp, stage * kPinvStageBytes + lane * 16, 0, 0);
@@ -264,7 +301,8 @@ __device__ __forceinline__ void scan_chain(const ScanParams& p, unsigned char* l
         unsigned char* chunk = lds + slot * kSlotBytes + (st_row >> 4) * kChunkBytes;
         const int r = st_row & 15;
         *reinterpret_cast<u32x4*>(chunk + kOffK + swz(r, st_seg)) = o.k;
-        *reinterpret_cast<u32x4*>(chunk + kOffQ + swz(r, st_seg)) = o.q;
+        if constexpr (!kMap)
+            *reinterpret_cast<u32x4*>(chunk + kOffQ + swz(r, st_seg)) = o.q;
         *reinterpret_cast<u32x4*>(chunk + kOffV + swz(r, st_seg)) = o.v;
     };
 
@@ -276,9 +314,15 @@ __device__ __forceinline__ void scan_chain(const ScanParams& p, unsigned char* l
     auto read_ops = [&](ChunkOps& o, const unsigned char* tile) {
         o.ka0 = *reinterpret_cast<const bf16x8*>(tile + kOffK + swz(c, g));
         o.ka1 = *reinterpret_cast<const bf16x8*>(tile + kOffK + swz(c, 4 + g));
-        o.qa0 = *reinterpret_cast<const bf16x8*>(tile + kOffQ + swz(c, g));
-        o.qa1 = *reinterpret_cast<const bf16x8*>(tile + kOffQ + swz(c, 4 + g));
-        o.vrow = *reinterpret_cast<const bf16x4*>(tile + kOffV + swz(c, 2 * w + (g >> 1)) + 8 * (g & 1));
+        if constexpr (!kMap) {
+            o.qa0 = *reinterpret_cast<const bf16x8*>(tile + kOffQ + swz(c, g));
+            o.qa1 = *reinterpret_cast<const bf16x8*>(tile + kOffQ + swz(c, 4 + g));
+        }
+        // the columns of A run with V = 0
+        if (!kMap || part == 2)
+            o.vrow = *reinterpret_cast<const bf16x4*>(tile + kOffV + swz(c, 2 * w + (g >> 1)) + 8 * (g & 1));
+        else
+            o.vrow = bf16x4{};
         // K^T (A operand of the updates), transposed on the way out of LDS:
         // lane (c, g) receives K[4g + r][rho(mt, c)], r = 0..3
 #pragma unroll
@@ -330,6 +374,8 @@ __device__ __forceinline__ void scan_chain(const ScanParams& p, unsigned char* l
             }
         }
 
+        if constexpr (kMap)
+            return;
         // off the chain: Y^T = W^T Q^T (+ M^T (-eta c_{t+1} Q)^T) + R^T S~^T
         f32x4 St = mfma32(o.ka0, o.qa0, zero);
         St = mfma32(o.ka1, o.qa1, St);
@@ -425,28 +471,54 @@ __device__ __forceinline__ void scan_chain(const ScanParams& p, unsigned char* l
             step(o1, p1, t0 + kB, t0 + 2 * kB <= T ? full : tail, true);
         }
     }
-    float* wo = p.W_out + u * kD * kD;
-    float* mo = p.M_out + u * kD * kD;
+    if constexpr (kMap) {
+        // A[i][64 part + col] (part 0, 1) or N[i][col] (part 2), rows i of
+        // W, then of M
+        float* m = p.maps + (u * (p.nseg - 1) + seg) * kMapFloats;
+        const int ld = part < 2 ? 2 * kD : kD;
+        float* dst = part < 2 ? m + kD * part + col : m + 4 * kD * kD + col;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+        for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            wo[rho(mt, 4 * g + r) * kD + col] = Wacc[mt][r];
-            mo[rho(mt, 4 * g + r) * kD + col] = Macc[mt][r];
-        }
+            for (int r = 0; r < 4; ++r) {
+                dst[rho(mt, 4 * g + r) * ld] = Wacc[mt][r];
+                dst[(kD + rho(mt, 4 * g + r)) * ld] = Macc[mt][r];
+            }
+    } else if (seg == p.nseg - 1) {
+        float* wo = p.W_out + u * kD * kD;
+        float* mo = p.M_out + u * kD * kD;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                wo[rho(mt, 4 * g + r) * kD + col] = Wacc[mt][r];
+                mo[rho(mt, 4 * g + r) * kD + col] = Macc[mt][r];
+            }
+    }
 }
 
-template <bool kExact>
+// kMap: the maps of segments 0 .. nseg - 2 (three workgroups per segment,
+// see scan_chain); else the scans of the chains or of their segments.  With
+// segments, the workgroups of a chain share an XCD (xcd_block).
+template <bool kExact, bool kMap>
 __global__ void __launch_bounds__(kThreads, 1)
 momentum_mfma_kernel(ScanParams p)
 {
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
-    const int64_t u = blockIdx.x;
+    int64_t u = blockIdx.x;
+    int s = 0;
+    if (p.nseg > 1) {
+        xcd_block(static_cast<int>(blockIdx.x), kMap ? 3 * (p.nseg - 1) : p.nseg, p.units, u, s);
+        if (u >= p.units)                // uniform over the workgroup
+            return;
+    }
     const int h = static_cast<int>(u % p.H);
-    if (p.beta[h] != 0.f)
-        scan_chain<kExact, true>(p, lds, u, h);
+    if constexpr (kMap)
+        scan_chain<kExact, true, true>(p, lds, u, h, s / 3, s % 3);
+    else if (p.beta[h] != 0.f)
+        scan_chain<kExact, true, false>(p, lds, u, h, s, 0);
     else
-        scan_chain<kExact, false>(p, lds, u, h);
+        scan_chain<kExact, false, false>(p, lds, u, h, s, 0);
 }
 
 int64_t pinv_stages(int64_t T) { return (T + kStageTokens - 1) / kStageTokens; }
@@ -460,18 +532,38 @@ bool momentum_mfma_supports(const MomentumArgs& a)
     return a.dtype == 1 && a.d == kD && a.b == kB && a.T <= max_tokens;
 }
 
-int64_t momentum_mfma_workspace_bytes(const MomentumArgs& a)
+namespace {
+
+int64_t pad256(int64_t n) { return (n + 255) / 256 * 256; }
+
+int64_t pinv_bytes(const MomentumArgs& a)
 {
-    if (a.grad_mode != 0) return 0;
-    return a.B * a.H * pinv_stages(a.T) * kPinvStageBytes;
+    return a.grad_mode == 0 ? pad256(a.B * a.H * pinv_stages(a.T) * kPinvStageBytes) : 0;
 }
 
-hipError_t launch_momentum_mfma(const MomentumArgs& a, void* workspace)
+}  // namespace
+
+// The chunk inverses (exact steps), then with nseg > 1 segments the maps of
+// segments 0 .. nseg - 2 and the start states of all of them.
+int64_t momentum_mfma_workspace_bytes(const MomentumArgs& a, int nseg)
+{
+    const int64_t units = a.B * a.H;
+    int64_t n = pinv_bytes(a);
+    if (nseg > 1)
+        n += pad256(units * (nseg - 1) * kMapFloats * 4) + units * nseg * 2 * kD * kD * 4;
+    return n;
+}
+
+// nseg segments of seg_len tokens (a multiple of a stage of two chunks, so
+// that each segment's chunk inverses start at a stage of the chain's).
+hipError_t launch_momentum_mfma(const MomentumArgs& a, void* workspace, int nseg, int64_t seg_len)
 {
     const int64_t units = a.B * a.H;
     const bool exact = a.grad_mode == 0;
     auto* pinv = static_cast<unsigned char*>(workspace);
     const int T = static_cast<int>(a.T);
+    if (T == 0 || nseg < 1 || (nseg > 1 && (seg_len % kStageTokens != 0 || seg_len * (nseg - 1) >= T)))
+        nseg = 1;
     if (exact && T > 0) {
         const int nchunks = (T + kB - 1) / kB;
         const int64_t total = units * nchunks;
@@ -485,15 +577,34 @@ hipError_t launch_momentum_mfma(const MomentumArgs& a, void* workspace)
         if (e != hipSuccess)
             return e;
     }
+    float* maps = nullptr;
+    float* xstart = nullptr;
+    if (nseg > 1) {
+        maps = reinterpret_cast<float*>(pinv + pinv_bytes(a));
+        xstart = maps + pad256(units * (nseg - 1) * kMapFloats * 4) / 4;
+    }
     ScanParams p{static_cast<const uint16_t*>(a.Q), static_cast<const uint16_t*>(a.K),
                  static_cast<const uint16_t*>(a.V), a.W0, a.w0_per_batch, a.M0, a.eta, a.beta,
-                 static_cast<int>(a.H), T, pinv, static_cast<uint16_t*>(a.Y), a.W_out, a.M_out};
+                 static_cast<int>(a.H), T, pinv, static_cast<uint16_t*>(a.Y), a.W_out, a.M_out,
+                 units, nseg, static_cast<int>(nseg > 1 ? seg_len : T), maps, xstart};
     const int lds = kSlots * kSlotBytes;
-    const dim3 grid(static_cast<unsigned>(units));
+    if (nseg > 1) {
+        const dim3 grid(static_cast<unsigned>(placed_grid(units, 3 * (nseg - 1))));
+        if (exact)
+            hipLaunchKernelGGL((momentum_mfma_kernel<true, true>), grid, dim3(kThreads), lds, a.stream, p);
+        else
+            hipLaunchKernelGGL((momentum_mfma_kernel<false, true>), grid, dim3(kThreads), lds, a.stream, p);
+        hipError_t e = hipGetLastError();
+        if (e == hipSuccess)
+            e = launch_momentum_combine(a, maps, nseg, xstart);
+        if (e != hipSuccess)
+            return e;
+    }
+    const dim3 grid(static_cast<unsigned>(nseg > 1 ? placed_grid(units, nseg) : units));
     if (exact)
-        hipLaunchKernelGGL(momentum_mfma_kernel<true>, grid, dim3(kThreads), lds, a.stream, p);
+        hipLaunchKernelGGL((momentum_mfma_kernel<true, false>), grid, dim3(kThreads), lds, a.stream, p);
     else
-        hipLaunchKernelGGL(momentum_mfma_kernel<false>, grid, dim3(kThreads), lds, a.stream, p);
+        hipLaunchKernelGGL((momentum_mfma_kernel<false, false>), grid, dim3(kThreads), lds, a.stream, p);
     return hipGetLastError();
 }
 

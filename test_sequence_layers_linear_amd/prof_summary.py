@@ -58,6 +58,9 @@ KERNEL_FILES = {
     "decode_kernel": "ttt_decode.hip",
     "momentum_inverse_kernel": "ttt_momentum_mfma.hip",
     "momentum_mfma_kernel[exact]": "ttt_momentum_mfma.hip",
+    "momentum_mfma_kernel[exact+maps]": "ttt_momentum_mfma.hip",
+    "momentum_mfma_kernel[chunk_start+maps]": "ttt_momentum_mfma.hip",
+    "momentum_combine_kernel": "ttt_linear_combine.hip",
     "momentum_mfma_kernel[chunk_start]": "ttt_momentum_mfma.hip",
 }
 COPY_NAME = "__amd_rocclr_copyBuffer"
@@ -68,8 +71,10 @@ def short_name(full: str) -> str:
     instantiations of the TTT-Linear forward kernels and [gmaps] / [segments]
     for the backward's cotangent maps and segment backward (+prologue for
     the instantiations with the input prologue)."""
-    if "momentum_mfma_kernel<" in full:      # kExact
-        return "momentum_mfma_kernel[exact]" if "<true>" in full else "momentum_mfma_kernel[chunk_start]"
+    if "momentum_mfma_kernel<" in full:      # kExact, kMap
+        args = [a.strip() for a in full.split("momentum_mfma_kernel<", 1)[1].split(">", 1)[0].split(",")]
+        mode = "exact" if args[0] == "true" else "chunk_start"
+        return f"momentum_mfma_kernel[{mode}{'+maps' if len(args) > 1 and args[1] == 'true' else ''}]"
     for base in ("linear_backward_kernel", "linear_backward_bf16_kernel"):
         if base + "<" in full:
             args = [a.strip() for a in full.split(base + "<", 1)[1].split(">", 1)[0].split(",")]

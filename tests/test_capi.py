@@ -43,6 +43,7 @@ def test_exports_every_declared_function(lib):
                           "ttt_linear_workspace_bytes", "ttt_linear_backward_workspace_bytes",
                           "ttt_status_string", "ttt_roof_copy", "ttt_roof_mfma", "ttt_roof_launch",
                           "ttt_linear_forward_noalloc", "ttt_linear_noalloc_max_workspace_bytes",
+                          "ttt_linear_momentum_segments",
                           "ttt_abi_version"}
     for n in names:
         assert hasattr(lib, n), f"{n} declared in ttt.h but not exported"
@@ -392,3 +393,28 @@ def test_momentum_workspace_query(lib):
     assert q(0, 3, 100, 64, 16, 1, 0) == 0
     # one byte short of that is rejected before any launch
     assert mom(lib, B=2, H=3, T=100, ws=WSA, wsb=6 * 4 * 1024 - 1) == INVALID
+
+
+def test_momentum_segments_query_and_workspace(lib, monkeypatch):
+    """Without a GPU the plan has one segment; a forced split of whole
+    stages of 32 tokens adds the maps (6 d^2 floats each) and start states
+    (2 d^2 floats each) to the documented workspace."""
+    seg = lib.ttt_linear_momentum_segments
+    q = lib.ttt_linear_momentum_workspace_bytes
+    assert seg(2, 3, 1000, 64, 16, 1, 0) == 1
+    assert seg(2, 3, 1000, 48, 16, 1, 0) == UNSUPPORTED
+    assert seg(2, 3, 1000, 64, 16, 1, 5) == INVALID
+    monkeypatch.setenv("TTT_MOMENTUM_SEGMENTS", "5")
+    pad = lambda n: (n + 255) // 256 * 256
+    units, d = 6, 64
+    for gm in (0, 1):
+        # T = 1000: 32 stages, 7 per segment, so 5 segments
+        assert seg(2, 3, 1000, 64, 16, 1, gm) == 5
+        pinv = units * 32 * 1024 if gm == 0 else 0
+        want = pinv + pad(units * 4 * 6 * d * d * 4) + units * 5 * 2 * d * d * 4
+        assert q(2, 3, 1000, 64, 16, 1, gm) == want
+    # forced beyond the stages: one segment per stage (T = 64: two)
+    assert seg(1, 1, 64, 64, 16, 1, 0) == 2
+    # only the bf16 MFMA path splits
+    assert seg(2, 3, 1000, 64, 16, 0, 0) == 1
+    assert seg(2, 3, 1000, 32, 16, 1, 0) == 1

@@ -221,3 +221,52 @@ def test_momentum_graph_capture():
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(Y, Y_e) and torch.equal(W, W_e) and torch.equal(M, M_e), rep
+
+
+@pytest.mark.parametrize("grad_mode", [0, 1])
+@pytest.mark.parametrize("S,T", [(2, 64), (2, 1000), (3, 333), (5, 1000), (12, 1000)])
+def test_momentum_forced_segments(S, T, grad_mode, monkeypatch):
+    """Sequence segments of the MFMA scan (maps of [W; M], their composition,
+    segment scans) against the oracle, forced to S segments of whole stages of
+    32 tokens, with a ragged last segment, a start momentum and one head with
+    beta = 0 (whose scan does not carry M)."""
+    monkeypatch.setenv("TTT_MOMENTUM_SEGMENTS", str(S))
+    w = WORKLOADS[3].with_(B=2, H=3, T=T)
+    announce("momentum segments", S, T, grad_mode)
+    stages = -(-T // 32)
+    want = -(-stages // -(-stages // S))       # segments of ceil(stages / S) stages
+    assert ttt.ttt_linear_momentum_segments(w.B, w.H, w.T, w.d, w.b, torch.bfloat16,
+                                            grad_mode) == want
+    mom = make_momentum(w, 50 + S, m0=True)
+    mom["beta"][1] = 0.0
+    _run(make_inputs(w, 51 + T), mom, 16, grad_mode, "bf16")
+
+
+@pytest.mark.parametrize("grad_mode", [0, 1])
+def test_momentum_segments_in_place_chaining(grad_mode, monkeypatch):
+    """Segmented calls with per-batch W0 updated in place (W_out = W0,
+    M_out = M0): two calls over halves of a sequence equal one call over the
+    whole (both segmented), up to rounding."""
+    monkeypatch.setenv("TTT_MOMENTUM_SEGMENTS", "3")
+    w = WORKLOADS[3].with_(B=1, H=2, T=512)
+    announce("momentum segments in place", grad_mode)
+    inp = make_inputs(w, 61, w0_per_batch=True)
+    mom = make_momentum(w, 62, m0=True)
+    g = to_gpu(inp)
+    beta = mom["beta"].cuda()
+    Y1, W1, M1 = ttt.ttt_linear_momentum_forward(g["Q"], g["K"], g["V"], g["W0"], g["eta"], beta,
+                                                 16, mom["M0"].cuda(), grad_mode)
+    W = g["W0"].clone()
+    M = mom["M0"].cuda().clone()
+    half = w.T // 2
+    ys = []
+    for sl in (slice(0, half), slice(half, w.T)):
+        q, k, v = (g[n][:, :, sl].contiguous() for n in ("Q", "K", "V"))
+        y, _, _ = ttt.ttt_linear_momentum_forward(q, k, v, W, g["eta"], beta, 16, M, grad_mode,
+                                                  W_out=W, M_out=M)
+        ys.append(y)
+    torch.cuda.synchronize()
+    Y2 = torch.cat(ys, dim=2)
+    for a, b in ((Y1, Y2), (W1, W), (M1, M)):
+        r = float((a.float() - b.float()).norm() / b.float().norm())
+        assert r <= 1e-2, r
