@@ -4,8 +4,8 @@
  * kernels are reported against the vendor's peak figures and against what
  * these plain kernels reach on the same GPU:
  *   - a streaming device-to-device copy (every byte read once and written
- *     once, 16-byte accesses, four loads in flight per thread): achievable
- *     HBM bandwidth = 2 * bytes / time;
+ *     once, 16-byte non-temporal accesses, four loads in flight per thread):
+ *     achievable HBM bandwidth = 2 * bytes / time;
  *   - a dense MFMA loop (each wave issues independent accumulation chains of
  *     one MFMA shape, no memory traffic): achievable matrix-core throughput
  *     = flops / time;

@@ -14,21 +14,28 @@ namespace {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
-// Grid-stride copy of n 16-byte elements, four loads in flight per thread.
-__global__ void __launch_bounds__(256) roof_copy_kernel(const uint4* __restrict__ src,
-                                                        uint4* __restrict__ dst, int64_t n)
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Grid-stride copy of n 16-byte elements, four loads in flight per thread,
+// non-temporal loads and stores (the data is touched once).  Measured on
+// MI355X for 1 GiB: 5.2 TB/s with 32 workgroups per CU, against 4.2-4.5 TB/s
+// with temporal accesses, 8 loads in flight or 4-16 workgroups per CU.
+__global__ void __launch_bounds__(256) roof_copy_kernel(const u32x4* __restrict__ src,
+                                                        u32x4* __restrict__ dst, int64_t n)
 {
     const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
     int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
     for (; i + 3 * stride < n; i += 4 * stride) {
-        const uint4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
-        dst[i] = a;
-        dst[i + stride] = b;
-        dst[i + 2 * stride] = c;
-        dst[i + 3 * stride] = d;
+        u32x4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            v[u] = __builtin_nontemporal_load(src + i + u * stride);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            __builtin_nontemporal_store(v[u], dst + i + u * stride);
     }
     for (; i < n; i += stride)
-        dst[i] = src[i];
+        __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
 }
 
 constexpr int kChains = 8;
@@ -92,10 +99,10 @@ int ttt_roof_copy(const void* src, void* dst, int64_t bytes, void* stream)
     if (bytes == 0) return TTT_OK;
     const int64_t n = bytes / 16;
     int64_t blocks = (n + 255) / 256;
-    if (blocks > 256 * 16) blocks = 256 * 16;      // 16 workgroups per CU of a 256-CU GPU
+    if (blocks > 256 * 32) blocks = 256 * 32;      // 32 workgroups per CU of a 256-CU GPU
     hipLaunchKernelGGL(roof_copy_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
-                       static_cast<hipStream_t>(stream), static_cast<const uint4*>(src),
-                       static_cast<uint4*>(dst), n);
+                       static_cast<hipStream_t>(stream), static_cast<const u32x4*>(src),
+                       static_cast<u32x4*>(dst), n);
     return hipGetLastError() == hipSuccess ? TTT_OK : TTT_ERR_HIP;
 }
 

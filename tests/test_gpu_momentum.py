@@ -224,12 +224,14 @@ def test_momentum_graph_capture():
 
 
 @pytest.mark.parametrize("grad_mode", [0, 1])
-@pytest.mark.parametrize("S,T", [(2, 64), (2, 1000), (3, 333), (5, 1000), (12, 1000)])
+@pytest.mark.parametrize("S,T", [(2, 33), (2, 48), (2, 64), (2, 1000), (3, 333), (5, 1000),
+                                 (12, 1000)])
 def test_momentum_forced_segments(S, T, grad_mode, monkeypatch):
     """Sequence segments of the MFMA scan (maps of [W; M], their composition,
     segment scans) against the oracle, forced to S segments of whole stages of
-    32 tokens, with a ragged last segment, a start momentum and one head with
-    beta = 0 (whose scan does not carry M)."""
+    32 tokens, with a ragged last segment (down to one token, T = 33, or one
+    chunk, T = 48), a start momentum and one head with beta = 0 (whose scan
+    does not carry M)."""
     monkeypatch.setenv("TTT_MOMENTUM_SEGMENTS", str(S))
     w = WORKLOADS[3].with_(B=2, H=3, T=T)
     announce("momentum segments", S, T, grad_mode)
