@@ -9,6 +9,8 @@ namespace ttt {
 
 // Maximum LDS one workgroup may use on gfx950.
 constexpr int kMaxLdsBytes = 160 * 1024;
+// MI355X's last-level (Infinity) cache
+constexpr int64_t kLastLevelCacheBytes = int64_t{256} << 20;
 
 // ---------------------------------------------------------------------------
 // element access: Q/K/V/Y are fp32 or bf16 (stored as raw 16-bit patterns)

@@ -21,6 +21,8 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kBufferDword3 = 0x00020000;
 // bytes of one 64-element bf16 row
 constexpr int kRowBytes = 128;
+// cache-policy operand of a buffer load or store on gfx950: non-temporal
+constexpr int kNonTemporal = 2;
 
 __device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c)
 {
