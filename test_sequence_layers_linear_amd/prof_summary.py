@@ -83,7 +83,7 @@ def short_name(full: str) -> str:
             return f"{base}[{role}{'+prologue' if flags[1] == 'true' else ''}]"
     for k in KERNEL_FILES:
         base = k.split("[")[0]
-        if base.startswith("linear_backward"):
+        if base in ("linear_backward_kernel", "linear_backward_bf16_kernel"):
             continue
         if base + "<true" in full or base + "<false" in full:
             args = [a.strip() for a in full.split(base + "<", 1)[1].split(">", 1)[0].split(",")]
