@@ -27,11 +27,13 @@
 // Layouts (16x16 MFMA; lane l, c = l % 16, g = l / 16; C: lane holds rows
 // 4g..4g+3 of column c; A: lane holds row c; B: lane holds column c):
 //   "T" = (lane = hidden unit, registers = tokens), "H" = (lane = token,
-//   registers = hidden units).  Hk, D', Hq come out in T; products over the
-//   hidden index need H, which a 16x16x16 product with the identity provides
-//   (an exact copy).  W1 tiles use the input-index numbering of the TTT-Linear
-//   kernel so that two accumulator tiles, rounded to bf16, are the B operand
-//   of a 16x16x32 product over i.  W2 is used contracted over the hidden index
+//   registers = hidden units).  Hk and D' come out in T; products over the
+//   hidden index need Ak in H too, which a 16x16x16 product with the identity
+//   provides (an exact copy).  Hq is formed transposed, Hq^T = W1^T Q^T +
+//   D'^T S^T, so Aq comes out in H with no copy.  W1 tiles use the input-index
+//   numbering of the TTT-Linear kernel so that two accumulator tiles, rounded
+//   to bf16, are the B operand of a 16x16x32 product over i (and the A operand
+//   of W1^T Q^T).  W2 is used contracted over the hidden index
 //   (Z, Y) and over the output index (E' W2^T), so two copies are kept: W2a
 //   with lane = output column, W2b = W2^T with lane = hidden unit; both take
 //   the same rank-16 update every chunk (from the same bf16 operands).
@@ -39,7 +41,7 @@
 // Phases of one chunk (a barrier between them):
 //   P0  LDS: finish the previous chunk's Y (sum 4 partials, store), read K, Q
 //       of this chunk.
-//   P1  MFMA: Hk, SiLU, Q W1, tril(Q K^T), Ak^H, Z partial -> LDS.   | barrier
+//   P1  MFMA: Hk, SiLU, W1^T Q^T, tril(Q K^T), Ak^H, Z partial -> LDS. | barrier
 //   P2  LDS: reduce Z for this wave's 16 output columns, E' -> LDS.  | barrier
 //   P3  LDS: read E' both ways, K^T.  MFMA: D', Hq, Aq, Y partial -> LDS,
 //       updates of W1, W2a, W2b; stage the next chunk's inputs.    | barrier
@@ -213,7 +215,10 @@ mlp_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         // ---- P1: Hk, Q W1, S, Ak, Z partial ----------------------------------
         // (bf16 copies of the chunk-start weights are packed where they are
         // used; the updates come last, so every product sees chunk-start values)
-        f32x4 Hq[kHT], dsl[kHT];
+        // Hk in layout T; Hq^T = W1^T Q^T comes out in layout H directly (the
+        // packed W1 tiles are the B operand of K W1 and the A operand of
+        // W1^T Q^T; the Q rows are both operand shapes at once)
+        f32x4 HqT[kHT], dsl[kHT];
         bf16x4 AkT[kHT], AkH[kHT];
 #pragma unroll
         for (int ht = 0; ht < kHT; ++ht) {
@@ -221,19 +226,20 @@ mlp_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
             const bf16x8 b1 = pack8(W1a[2][ht], W1a[3][ht]);
             f32x4 hk = mfma32(ka0, b0, zero);
             hk = mfma32(ka1, b1, hk);
-            Hq[ht] = mfma32(qa0, b0, zero);
-            Hq[ht] = mfma32(qa1, b1, Hq[ht]);
+            HqT[ht] = mfma32(b0, qa0, zero);
+            HqT[ht] = mfma32(b1, qa1, HqT[ht]);
             f32x4 a;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const float x = hk[r];
                 const float sg = sigmoid_f(x);
                 a[r] = x * sg;
-                dsl[ht][r] = sg * (1.0f + x * (1.0f - sg));
+                dsl[ht][r] = __builtin_fmaf(a[r], 1.0f - sg, sg);   // SiLU'(x) = sg + x sg (1 - sg)
             }
             AkT[ht] = pack4(a);
         }
-        // S = tril(Q K^T) as an A operand: lane (c = t, g) holds S[t][t' = 4g + r]
+        // S = tril(Q K^T): lane (c = t, g) holds S[t][t' = 4g + r], the B
+        // operand S^T [t'][t] of D'^T S^T
         bf16x4 sb;
         {
             f32x4 St = mfma32(ka0, qa0, zero);
@@ -313,16 +319,17 @@ mlp_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
             gg = mfma32(eA[1], pack8(W2b[2][ht], W2b[3][ht]), gg);
             DT[ht] = pack4(gg * dsl[ht]);
         }
-        // Hq = Q W1 + S D'; Aq = SiLU(Hq) -> layout H
+        // Hq^T = W1^T Q^T + D'^T S^T (D' in layout T is the A operand D'^T);
+        // Aq = SiLU(Hq), already in layout H
         bf16x4 AqH[kHT];
 #pragma unroll
         for (int ht = 0; ht < kHT; ++ht) {
-            const f32x4 hq = mfma16_as32(sb, DT[ht], Hq[ht]);
+            const f32x4 hq = mfma16_as32(DT[ht], sb, HqT[ht]);
             f32x4 a;
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 a[r] = hq[r] * sigmoid_f(hq[r]);
-            AqH[ht] = pack4(mfma16(pack4(a), eye, zero));
+            AqH[ht] = pack4(a);
         }
         bf16x8 aqh[kHK];
 #pragma unroll
@@ -340,18 +347,14 @@ mlp_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 Sa[r] = (4 * g + r <= c) ? Sa[r] : 0.f;
             sab = pack4(Sa);
         }
-        // Y^T partial of this wave: lane (c = t, g) holds Y[t][16jt + 4g + r].
-        // The W2 copies are taken through an opaque move so that the compiler
-        // repacks them here instead of keeping the phase-1 packs alive.
+        // Y^T partial of this wave: lane (c = t, g) holds Y[t][16jt + 4g + r]
+        // (the bf16 W2 tiles are the phase-1 packs, kept in registers)
 #pragma unroll
         for (int jt = 0; jt < 4; ++jt) {
             f32x4 y = zero;
 #pragma unroll
-            for (int kb = 0; kb < kHK; ++kb) {
-                f32x4 x0 = W2a[2 * kb][jt], x1 = W2a[2 * kb + 1][jt];
-                asm volatile("" : "+v"(x0), "+v"(x1));
-                y = mfma32(pack8(x0, x1), aqh[kb], y);
-            }
+            for (int kb = 0; kb < kHK; ++kb)
+                y = mfma32(pack8(W2a[2 * kb][jt], W2a[2 * kb + 1][jt]), aqh[kb], y);
             y = mfma16_as32(eT[jt], sab, y);
             *reinterpret_cast<f32x4*>(lds + kOffY + w * kYWave + c * kYRow + (16 * jt + 4 * g) * 4) = y;
         }
