@@ -53,6 +53,8 @@ namespace {
 
 using namespace mfma;
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
 constexpr int kD = 64;
 constexpr int kM = 256;
 constexpr int kB = 16;
@@ -268,27 +270,26 @@ mlp_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         __builtin_amdgcn_sched_barrier(0);
         __syncthreads();
 
-        // ---- P2: Z for columns 16w + c, E' -> LDS (waves w < kWork) ---------
-        if (w < kWork) {
-            f32x4 zs = zero;
+        // ---- P2: Z for columns 8w + (lane % 8), tokens 2 (lane / 8) .. +1, and
+        // E' -> LDS, on all waves (each sums 8 partials of 8 bytes per lane)
+        {
+            const int jz = 8 * w + (lane & 7);
+            const int tz = 2 * (lane >> 3);
+            f32x2 zs = {0.f, 0.f};
 #pragma unroll
             for (int ww = 0; ww < kWaves; ++ww)
-                zs += *reinterpret_cast<const f32x4*>(lds + kOffZ + ww * kZWave +
-                                                      (16 * w + c) * kZRow + 16 * g);
-            // V[4g + r][16w + c], transposed on the way out of LDS (lane (c, g)
-            // addresses row 4g + c / 4, columns 16w + 4 (c % 4) .. + 3)
-            const bf16x4 vt = read_tr16(sl + kOffV + swz(4 * g + (c >> 2), 2 * w + ((c & 3) >> 1)) +
-                                        8 * (c & 1));
-            f32x4 e;
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                e[r] = -et * (zs[r] - static_cast<float>(vt[r]));
-            const bf16x4 eb = pack4(e);
+                zs += *reinterpret_cast<const f32x2*>(lds + kOffZ + ww * kZWave + jz * kZRow + 4 * tz);
+            // V[tz][jz], V[tz + 1][jz] from the row-major, swizzled V tile
+            const float v0 = static_cast<float>(*reinterpret_cast<const __bf16*>(
+                sl + kOffV + swz(tz, jz >> 3) + 2 * (jz & 7)));
+            const float v1 = static_cast<float>(*reinterpret_cast<const __bf16*>(
+                sl + kOffV + swz(tz + 1, jz >> 3) + 2 * (jz & 7)));
+            const uint32_t e01 = cvt2(-et * (zs[0] - v0), -et * (zs[1] - v1));
             // E'^T [j][t] and E' [t][j]
-            *reinterpret_cast<bf16x4*>(lds + kOffET + (16 * w + c) * kTrRow + 8 * g) = eb;
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                *reinterpret_cast<__bf16*>(lds + kOffEN + (4 * g + r) * kENRow + 2 * (16 * w + c)) = eb[r];
+            *reinterpret_cast<uint32_t*>(lds + kOffET + jz * kTrRow + 2 * tz) = e01;
+            *reinterpret_cast<uint16_t*>(lds + kOffEN + tz * kENRow + 2 * jz) = static_cast<uint16_t>(e01);
+            *reinterpret_cast<uint16_t*>(lds + kOffEN + (tz + 1) * kENRow + 2 * jz) =
+                static_cast<uint16_t>(e01 >> 16);
         }
         __syncthreads();
 
