@@ -20,9 +20,11 @@
 // W1[:, slice] and W2[slice, :] live in its fp32 MFMA accumulators (ordinary
 // VGPRs) for the whole scan.  Only two quantities need all hidden units: Z
 // (needed by every wave, on the critical path) and Y; both are summed across
-// waves through LDS, waves 0-3 each reducing a quarter of the output columns
-// (reduce-scatter), and E' is then shared through LDS in the two orientations
-// the products need.  Waves 0-3 also stage the inputs.
+// waves through LDS, each summing wave a slice of the output columns
+// (reduce-scatter: Z on all 8 waves, 8 columns each; Y on waves 0-3, 16
+// each), and E' is then shared through LDS in the two orientations the
+// products need.
+// Waves 0-3 also stage the inputs.
 //
 // Layouts (16x16 MFMA; lane l, c = l % 16, g = l / 16; C: lane holds rows
 // 4g..4g+3 of column c; A: lane holds row c; B: lane holds column c):
@@ -39,10 +41,11 @@
 //   the same rank-16 update every chunk (from the same bf16 operands).
 //
 // Phases of one chunk (a barrier between them):
-//   P0  LDS: finish the previous chunk's Y (sum 4 partials, store), read K, Q
+//   P0  LDS: finish the previous chunk's Y (waves 0-3: sum the 8 partials,
+//       store; summing on all 8 waves delays 4-7 in P1), read K, Q
 //       of this chunk.
 //   P1  MFMA: Hk, SiLU, W1^T Q^T, tril(Q K^T), Ak^H, Z partial -> LDS. | barrier
-//   P2  LDS: reduce Z for this wave's 16 output columns, E' -> LDS.  | barrier
+//   P2  LDS: every wave reduces Z for 8 output columns, E' -> LDS.  | barrier
 //   P3  LDS: read E' both ways, K^T.  MFMA: D', Hq, Aq, Y partial -> LDS,
 //       updates of W1, W2a, W2b; stage the next chunk's inputs.    | barrier
 // Every accumulation chain uses a single MFMA shape (see mfma16_as32).
