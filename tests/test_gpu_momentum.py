@@ -181,13 +181,19 @@ def test_momentum_worked_examples_bit_exact(path):
         assert not Y[0, 0, :, 2:].float().any() and not W[0, 0, 2:].any()
 
 
-def test_momentum_graph_capture():
-    """Exact momentum steps (the inverse launch, then the scan) captured in a
-    HIP graph with the caller's workspace: every replay equals the eager call
-    bit for bit, with other eager work through the same workspace between
-    the replays."""
+@pytest.mark.parametrize("S", [None, 5])
+def test_momentum_graph_capture(S, monkeypatch):
+    """Exact momentum steps (the inverse launch, then the scan; with S = 5
+    forced segments also the maps and their composition) captured in a HIP
+    graph with the caller's workspace: every replay equals the eager call bit
+    for bit, with other eager work through the same workspace between the
+    replays."""
+    if S is not None:
+        monkeypatch.setenv("TTT_MOMENTUM_SEGMENTS", str(S))
     w = WORKLOADS[3].with_(B=2, H=6, T=1000)
-    announce("momentum graph capture")
+    announce("momentum graph capture, segments", S)
+    if S is not None:
+        assert ttt.ttt_linear_momentum_segments(w.B, w.H, w.T, 64, 16, torch.bfloat16, 0) == S
     g = to_gpu(make_inputs(w, 70))
     beta = make_momentum(w, 71)["beta"].cuda()
     nbytes = ttt.ttt_linear_momentum_workspace_bytes(w.B, w.H, w.T, 64, 16, torch.bfloat16, 0)
