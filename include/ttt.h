@@ -33,6 +33,9 @@
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default
  *     stream) and the call returns without synchronising; no call makes a
  *     synchronising HIP call, so every call can be captured into a HIP graph.
+ *     Segment plans and workspace sizes use the current device's
+ *     compute-unit count, as the size queries do: pass a stream of the
+ *     current device (or of a device with as many compute units).
  *   - Arguments are validated before any HIP call; on an error nothing is
  *     launched and nothing is written.  No C++ exception crosses the ABI.
  *   - Results are deterministic run to run (no atomics, fixed reduction
@@ -131,7 +134,8 @@ int ttt_linear_forward(const void* Q, const void* K, const void* V, int qkv_dtyp
  * ttt_linear_workspace_bytes of workspace, so the results are identical bit
  * for bit.  The segment maps and start states go to a static device array of
  * ttt_linear_noalloc_max_workspace_bytes() (16 MiB) that every device the
- * library runs on holds until the process ends; sizes whose plan needs more
+ * library runs on holds until the process ends (the copy of the device that
+ * `stream` belongs to is used); sizes whose plan needs more
  * return TTT_ERR_UNSUPPORTED (every planned call on a 256-CU MI355X fits:
  * at most B*H*(3 S - 2) matrices of 16 KB with B*H*S <= 256).  The call
  * allocates nothing.  Its contents need no clearing (every byte read is

@@ -272,19 +272,26 @@ int linear_sizes_status(int64_t B, int64_t H, int64_t T, int d, int b, int qkv_d
 constexpr int64_t kScratchBytes = int64_t{16} << 20;
 static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
-// Device address of the current device's copy of `scratch`, looked up once
-// per device (the array's name is not a device address in host code).
-int scratch_address(void** out)
+// Device address of `scratch` on the device that `stream` belongs to (the
+// null stream: the current device), looked up once per device with that
+// device current (the array's name is not a device address in host code,
+// and each device holds its own copy at its own address).
+int scratch_address(hipStream_t stream, void** out)
 {
     constexpr int kMaxDevices = 64;
     static std::mutex mu;
     static void* addr[kMaxDevices];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return TTT_ERR_HIP;
+    int cur = 0, dev = 0;
+    if (hipGetDevice(&cur) != hipSuccess || hipStreamGetDevice(stream, &dev) != hipSuccess ||
+        dev < 0 || dev >= kMaxDevices)
+        return TTT_ERR_HIP;
     std::lock_guard<std::mutex> lock(mu);
     if (!addr[dev]) {
+        if (dev != cur && hipSetDevice(dev) != hipSuccess) return TTT_ERR_HIP;
         void* p = nullptr;
-        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return TTT_ERR_HIP;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (dev != cur && hipSetDevice(cur) != hipSuccess) return TTT_ERR_HIP;
+        if (e != hipSuccess || !p) return TTT_ERR_HIP;
         addr[dev] = p;
     }
     *out = addr[dev];
@@ -340,7 +347,7 @@ int linear_forward_impl(const void* Q, const void* K, const void* V, int qkv_dty
         if (forward_workspace_bytes(units, d, p.nseg) > kScratchBytes) return TTT_ERR_UNSUPPORTED;
         void* sp = nullptr;
         if (p.nseg > 1)
-            if (const int st = scratch_address(&sp)) return st;
+            if (const int st = scratch_address(a.stream, &sp)) return st;
         return run_linear_segmented(a, p, sp, k.launch);
     }
     if (ttt::linear_generic_lds_bytes(d, b) > static_cast<size_t>(ttt::kMaxLdsBytes))
