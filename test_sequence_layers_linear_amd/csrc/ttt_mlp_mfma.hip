@@ -44,16 +44,21 @@
 //   P0  LDS: finish the previous chunk's Y (waves 0-3: sum the 8 partials,
 //       store; summing on all 8 waves delays 4-7 in P1), read K, Q
 //       of this chunk.
-//   P1  MFMA: the previous chunk's W2a, W2b updates; Hk, SiLU, W1^T Q^T,
-//       tril(Q K^T), Ak^H, Z partial -> LDS.                          | barrier
-//   P2  LDS: every wave reduces Z for 8 output columns, E' -> LDS.  | barrier
-//   P3  LDS: read E' both ways, K^T.  MFMA: D', Hq, Aq, Y partial -> LDS,
+//   P1  MFMA: the previous chunk's W2a, W2b updates; Hk, SiLU, Ak^H,
+//       Z partial -> LDS.                                              | barrier
+//   P2  LDS: every wave reduces Z for 8 output columns, E' -> LDS; beside
+//       it W1^T Q^T, tril(Q K^T), the K^T reads, bf16 W2^T.           | barrier
+//   P3  LDS: read E' both ways.  MFMA: D', Hq, Aq, Y partial -> LDS,
 //       update of W1; stage the next chunk's inputs.                 | barrier
-// The W2 updates (16 of a wave's products) wait for the next chunk's P1,
-// where the first use of W2a is (Z) and where they run beside the SiLU
-// arithmetic instead of after P3's own products: 1124 -> 1067 us on
-// B4 H12 T8192, bit for bit the same results.  After the last chunk they are
-// applied before W2 is written out.
+// Work sits in the first phase that has room for it, not the one that first
+// needs its result.  The W2 updates (16 of a wave's products) wait for the
+// next chunk's P1, where W2a is first used (Z) and the SiLU arithmetic
+// leaves the matrix unit idle; after the last chunk they are applied before
+// W2 is written out.  P2's reduction is mostly LDS and barrier latency, so the
+// products and packing that P3 needs but that do not wait for E' run there.
+// On B4 H12 T8192: 1124 us with all of them in their first-use phase, 1067
+// with the W2 updates deferred, 1000 with P2 filled; the results are the
+// same bit for bit.
 // Every accumulation chain uses a single MFMA shape (see mfma16_as32).
 #include "ttt_mfma_ops.h"
 
@@ -242,23 +247,22 @@ mlp_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
         __builtin_amdgcn_sched_barrier(0);
 
-        // ---- P1: Hk, Q W1, S, Ak, Z partial ----------------------------------
+        // ---- P1: W2 updates, Hk, Ak, Z partial --------------------------------
         // (bf16 copies of the chunk-start weights are packed where they are
-        // used; the updates come last, so every product sees chunk-start values)
-        // Hk in layout T; Hq^T = W1^T Q^T comes out in layout H directly (the
-        // packed W1 tiles are the B operand of K W1 and the A operand of
-        // W1^T Q^T; the Q rows are both operand shapes at once)
+        // used; the updates come after the products that read them, so every
+        // product sees chunk-start values)
+        // Hk in layout T; the packed W1 tiles are the B operand of K W1 here
+        // and the A operand of W1^T Q^T in P2
         w2_update();
         f32x4 HqT[kHT], dsl[kHT];
         bf16x4 AkT[kHT], AkH[kHT];
+        bf16x8 w1p[kHT][2];
 #pragma unroll
         for (int ht = 0; ht < kHT; ++ht) {
-            const bf16x8 b0 = pack8(W1a[0][ht], W1a[1][ht]);
-            const bf16x8 b1 = pack8(W1a[2][ht], W1a[3][ht]);
-            f32x4 hk = mfma32(ka0, b0, zero);
-            hk = mfma32(ka1, b1, hk);
-            HqT[ht] = mfma32(b0, qa0, zero);
-            HqT[ht] = mfma32(b1, qa1, HqT[ht]);
+            w1p[ht][0] = pack8(W1a[0][ht], W1a[1][ht]);
+            w1p[ht][1] = pack8(W1a[2][ht], W1a[3][ht]);
+            f32x4 hk = mfma32(ka0, w1p[ht][0], zero);
+            hk = mfma32(ka1, w1p[ht][1], hk);
             f32x4 a;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -268,17 +272,6 @@ mlp_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 dsl[ht][r] = __builtin_fmaf(a[r], 1.0f - sg, sg);   // SiLU'(x) = sg + x sg (1 - sg)
             }
             AkT[ht] = pack4(a);
-        }
-        // S = tril(Q K^T): lane (c = t, g) holds S[t][t' = 4g + r], the B
-        // operand S^T [t'][t] of D'^T S^T
-        bf16x4 sb;
-        {
-            f32x4 St = mfma32(ka0, qa0, zero);
-            St = mfma32(ka1, qa1, St);
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                St[r] = (4 * g + r <= c) ? St[r] : 0.f;
-            sb = pack4(St);
         }
 #pragma unroll
         for (int ht = 0; ht < kHT; ++ht)
@@ -300,7 +293,35 @@ mlp_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         __syncthreads();
 
         // ---- P2: Z for columns 8w + (lane % 8), tokens 2 (lane / 8) .. +1, and
-        // E' -> LDS, on all waves (each sums 8 partials of 8 bytes per lane)
+        // E' -> LDS, on all waves (each sums 8 partials of 8 bytes per lane).
+        // Beside that, the work of P3 that does not wait for E': Hq^T = W1^T
+        // Q^T (layout H directly: the Q rows are both operand shapes at once),
+        // S = tril(Q K^T) (lane (c = t, g) holds S[t][t' = 4g + r], the B
+        // operand S^T [t'][t] of D'^T S^T), the K^T rows and the bf16 W2^T tiles
+#pragma unroll
+        for (int ht = 0; ht < kHT; ++ht) {
+            HqT[ht] = mfma32(w1p[ht][0], qa0, zero);
+            HqT[ht] = mfma32(w1p[ht][1], qa1, HqT[ht]);
+        }
+        bf16x4 sb;
+        {
+            f32x4 St = mfma32(ka0, qa0, zero);
+            St = mfma32(ka1, qa1, St);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                St[r] = (4 * g + r <= c) ? St[r] : 0.f;
+            sb = pack4(St);
+        }
+        bf16x4 kt[4];            // K^T rows rho(it, c), tokens 4g .. +3
+#pragma unroll
+        for (int it = 0; it < 4; ++it)
+            kt[it] = read_tr16(sl + kOffK + swz(4 * g + (c >> 2), 4 * (it >> 1) + (c & 3)) + 8 * (it & 1));
+        bf16x8 w2bp[kHT][2];     // W2^T tiles (lane = hidden, k-slots = output)
+#pragma unroll
+        for (int ht = 0; ht < kHT; ++ht) {
+            w2bp[ht][0] = pack8(W2b[0][ht], W2b[1][ht]);
+            w2bp[ht][1] = pack8(W2b[2][ht], W2b[3][ht]);
+        }
         {
             const int jz = 8 * w + (lane & 7);
             const int tz = 2 * (lane >> 3);
@@ -325,7 +346,6 @@ mlp_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         // ---- P3 -------------------------------------------------------------
         bf16x8 eA[2];            // E' (lane = t, k-slots = output index)
         bf16x4 eT[4];            // E' (lane = output index, registers = t)
-        bf16x4 kt[4];            // K^T rows rho(it, c), tokens 4g .. +3
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
             const bf16x4 lo = *reinterpret_cast<const bf16x4*>(lds + kOffEN + c * kENRow + 2 * (32 * p + 4 * g));
@@ -335,9 +355,6 @@ mlp_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 #pragma unroll
         for (int jt = 0; jt < 4; ++jt)
             eT[jt] = *reinterpret_cast<const bf16x4*>(lds + kOffET + (16 * jt + c) * kTrRow + 8 * g);
-#pragma unroll
-        for (int it = 0; it < 4; ++it)
-            kt[it] = read_tr16(sl + kOffK + swz(4 * g + (c >> 2), 4 * (it >> 1) + (c & 3)) + 8 * (it & 1));
         __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
         __builtin_amdgcn_sched_barrier(0);
 
@@ -345,8 +362,8 @@ mlp_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         bf16x4 DT[kHT];
 #pragma unroll
         for (int ht = 0; ht < kHT; ++ht) {
-            f32x4 gg = mfma32(eA[0], pack8(W2b[0][ht], W2b[1][ht]), zero);
-            gg = mfma32(eA[1], pack8(W2b[2][ht], W2b[3][ht]), gg);
+            f32x4 gg = mfma32(eA[0], w2bp[ht][0], zero);
+            gg = mfma32(eA[1], w2bp[ht][1], gg);
             DT[ht] = pack4(gg * dsl[ht]);
         }
         // Hq^T = W1^T Q^T + D'^T S^T (D' in layout T is the A operand D'^T);
