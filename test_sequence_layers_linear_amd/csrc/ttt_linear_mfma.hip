@@ -54,6 +54,8 @@
 // sized to the chain's T tokens, so rows past the end read as zero (an
 // all-zero chunk leaves W unchanged) and stores past the end are dropped:
 // there are no tail branches.
+#include <type_traits>
+
 #include "ttt_mfma_ops.h"
 
 namespace ttt {
@@ -67,7 +69,7 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kStageChunks = 2;
 constexpr int kStageTokens = kB * kStageChunks;
-constexpr int kSet = 6;                 // stages per register set (two sets)
+constexpr int kSet = 6;                 // most stages per register set (two sets)
 constexpr int kSlots = 3;               // LDS ring slots (kSet * 2 % kSlots == 0)
 // LDS layout of one chunk inside a stage slot (bytes)
 constexpr int kOffK = 0;
@@ -187,8 +189,11 @@ linear_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     // a slot also holds the stage's 32 step sizes when the prologue is on
     constexpr int kSlotB = kPro ? kSlotBytes + kStageTokens * 4 : kSlotBytes;
     // stages per register set: the maps block runs 8 waves (half the
-    // registers per wave), so it prefetches 3-6 stages ahead instead of 6-12
-    constexpr int kSetK = kMaps ? kSet / 2 : kSet;
+    // registers per wave), so it prefetches 3-6 stages ahead; so does the
+    // plain scan (3-6 ahead was faster than 6-12: 42.6 against 48.1 us on
+    // B8 H12 T2048 with a cold cache, 258 against 269 us on B2 H24 T32768);
+    // the prologue scan's staging waves run 6-12 ahead
+    constexpr int kSetK = (kMaps || !kSplit) ? kSet / 2 : kSet;
     static_assert((2 * kSetK) % kSlots == 0, "slot index must be static inside the loop");
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 
@@ -290,8 +295,47 @@ linear_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
             o.kt[mt] = read_tr16(tile + kOffK + swz(4 * g + (c >> 2), 4 * (mt >> 1) + (c & 3)) + 8 * (mt & 1));
     };
 
-    // One chunk of the scan, tokens t0 onwards.
-    auto step = [&](const ChunkOps& o, int t0) {
+    // Readout of one chunk, rows t0 .. t0 + 15 of Y, from its K and Q
+    // operands, the bf16 chunk-start W slice (b0, b1) and E' (eb): off the
+    // chain, so the plain scan runs the second chunk of a stage at the start
+    // of the next stage, where it fills the wait for that stage's LDS reads
+    // (41.4 against 42.6 us on B8 H12 T2048, 247 against 258 us on B2 H24
+    // T32768, both with a cold cache; the same results bit for bit).
+    auto readout = [&](const bf16x8& ka0, const bf16x8& ka1, const bf16x8& qa0,
+                       const bf16x8& qa1, const bf16x8& b0, const bf16x8& b1, const bf16x4& eb,
+                       int t0) {
+        // S^T = K Q^T, Y^T partial = W_J^T Q^T
+        f32x4 St = mfma32(ka0, qa0, zero);
+        St = mfma32(ka1, qa1, St);
+        f32x4 Yt = mfma32(b0, qa0, zero);
+        Yt = mfma32(b1, qa1, Yt);
+
+        // S^T masked: lane (c = t, g) holds S[t][t' = 4g + r]; keep t' <= t
+        f32x4 Sm;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            Sm[r] = (4 * g + r <= c) ? St[r] : 0.f;
+        // (the chunk-start read drops the intra-chunk term: zero operand)
+        const bf16x4 sb = (kPro && pro.read_start) ? bf16x4{} : pack4(Sm);
+        Yt = mfma16_as32(eb, sb, Yt);
+
+        // Y[t0 + c][16w + 4g .. +3]; rows past the segment fall outside the buffer.
+        const bf16x4 yb = pack4(Yt);
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, yb), ry,
+                                              ((t0 + c) * kD + 16 * w + 4 * g) * 2, 0, 0);
+    };
+    // a readout held over to the next stage
+    struct Pending {
+        bf16x8 ka0, ka1, qa0, qa1, b0, b1;
+        bf16x4 eb;
+    };
+    Pending pend;
+    int pend_t0 = 0;
+
+    // One chunk of the scan, tokens t0 onwards; kDefer (plain scan only):
+    // keep its readout's operands in `pend` instead of reading out.
+    auto step = [&](const ChunkOps& o, int t0, auto defer) {
+        constexpr bool kDefer = decltype(defer)::value && !kSplit;
         // bf16 copy of the W slice at the chunk start: the B operand of K W_J
         // and the A operand of W_J^T Q^T (k-slot (g, e) of pair s <-> input
         // index 32s + 8g + e)
@@ -317,27 +361,15 @@ linear_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
         for (int mt = 0; mt < 4; ++mt)
             Wacc[mt] = mfma16(o.kt[mt], eb, Wacc[mt]);
 
-        if constexpr (!kMaps) {
-            // off the chain: S^T = K Q^T, Y^T partial = W_J^T Q^T
-            f32x4 St = mfma32(o.ka0, o.qa0, zero);
-            St = mfma32(o.ka1, o.qa1, St);
-            f32x4 Yt = mfma32(b0, o.qa0, zero);
-            Yt = mfma32(b1, o.qa1, Yt);
-
-            // S^T masked: lane (c = t, g) holds S[t][t' = 4g + r]; keep t' <= t
-            f32x4 Sm;
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                Sm[r] = (4 * g + r <= c) ? St[r] : 0.f;
-            // (the chunk-start read drops the intra-chunk term: zero operand)
-            const bf16x4 sb = (kPro && pro.read_start) ? bf16x4{} : pack4(Sm);
-            Yt = mfma16_as32(eb, sb, Yt);
-
-            // Y[t0 + c][16w + 4g .. +3]; rows past the segment fall outside the buffer.
-            const bf16x4 yb = pack4(Yt);
-            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, yb), ry,
-                                                  ((t0 + c) * kD + 16 * w + 4 * g) * 2, 0, 0);
+        if constexpr (kDefer) {
+            pend = Pending{o.ka0, o.ka1, o.qa0, o.qa1, b0, b1, eb};
+            pend_t0 = t0;
+        } else if constexpr (!kMaps) {
+            readout(o.ka0, o.ka1, o.qa0, o.qa1, b0, b1, eb, t0);
         }
+    };
+    auto flush = [&]() {
+        readout(pend.ka0, pend.ka1, pend.qa0, pend.qa1, pend.b0, pend.b1, pend.eb, pend_t0);
     };
 
     // Stage s: publish stage s + 1 (held in `next`), then compute stage s.
@@ -352,8 +384,11 @@ linear_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
             o0.eta4 = *reinterpret_cast<const f32x4*>(sl + kSlotBytes + 16 * g);
             o1.eta4 = *reinterpret_cast<const f32x4*>(sl + kSlotBytes + 64 + 16 * g);
         }
-        step(o0, s * kStageTokens);
-        step(o1, s * kStageTokens + kB);
+        if constexpr (!kSplit)
+            if (s > 0)                   // the previous stage's second readout
+                flush();
+        step(o0, s * kStageTokens, std::false_type{});
+        step(o1, s * kStageTokens + kB, std::true_type{});
         prep(ahead, s + 2);
     };
 
@@ -460,8 +495,8 @@ linear_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
                         o0.eta4 = *reinterpret_cast<const f32x4*>(sl + kSlotBytes + 16 * g);
                         o1.eta4 = *reinterpret_cast<const f32x4*>(sl + kSlotBytes + 64 + 16 * g);
                     }
-                    step(o0, (s0 + p) * kStageTokens);
-                    step(o1, (s0 + p) * kStageTokens + kB);
+                    step(o0, (s0 + p) * kStageTokens, std::false_type{});
+                    step(o1, (s0 + p) * kStageTokens + kB, std::false_type{});
                 }
             }
         }
@@ -505,6 +540,9 @@ linear_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
         }
     }
 done:
+    if constexpr (!kSplit)
+        if (nstages > 0)
+            flush();
     if (kSplit && stager)
         return;
 
