@@ -34,20 +34,22 @@
 //   S^T  = K Q^T        : lands in exactly the B layout of E'^T S^T
 //   E'   = -eta R (C layout) is at once the B operand of the update and the
 //        A operand of E'^T S^T
-//   W   += K^T E'       : A = K^T, read from a transposed copy in LDS
+//   W   += K^T E'       : A = K^T, transposed on its way out of LDS
+//                         (ds_read_b64_tr_b16 on the row-major K tile)
 // Y^T comes out with 4 consecutive columns of one token per lane (one 8-byte
-// store).  Only R -> E' -> update -> bf16(W) is a dependent chain per chunk.
+// store).  Only R -> E' -> update -> bf16(W) is a dependent chain per chunk;
+// the plain scan runs the second chunk's readout (S^T, Y^T, the store) at
+// the start of the next stage, while that stage's LDS reads are in flight.
 //
 // Memory.  Q, K, V stream from HBM exactly once per chain.  A stage is two
 // chunks (32 tokens); for each stage wave w loads rows [8w, 8w + 8) of the
 // stage's K, Q and V with fully coalesced 16-byte-per-lane buffer loads (one
 // 1 KB row block per instruction) into registers, and later writes them to
 // one slot of a 3-slot LDS ring: K, Q, V row-major with the 16-byte segments
-// of row r XOR-swizzled by r % 8 (conflict-free operand reads), plus K^T with
-// a padded 40-byte row (conflict-free 8-byte reads of 4 tokens of one input
-// index).  Loads run 6 to 12 stages ahead in two fixed register sets, A and
-// B (while one set is consumed the other is in flight), so the compiler can
-// wait on exactly the set it needs.  One barrier per stage: at stage s every
+// of row r XOR-swizzled by r % 8 (conflict-free operand reads).  Loads run 3
+// to 6 stages ahead in two fixed register sets, A and B (while one set is
+// consumed the other is in flight), so the compiler can wait on exactly the
+// set it needs.  One barrier per stage: at stage s every
 // wave writes stage s + 1 into slot (s + 1) % 3, meets the barrier, then
 // computes stage s from slot s % 3; the slot being written was last read at
 // stage s - 2, before the previous barrier.  Per-chain buffer resources are
@@ -69,7 +71,7 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kStageChunks = 2;
 constexpr int kStageTokens = kB * kStageChunks;
-constexpr int kSet = 6;                 // most stages per register set (two sets)
+constexpr int kSet = 6;                 // bound on the stages per register set (two sets)
 constexpr int kSlots = 3;               // LDS ring slots (kSet * 2 % kSlots == 0)
 // LDS layout of one chunk inside a stage slot (bytes)
 constexpr int kOffK = 0;
@@ -188,12 +190,12 @@ linear_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     const int nstages = (t_len + kStageTokens - 1) / kStageTokens;
     // a slot also holds the stage's 32 step sizes when the prologue is on
     constexpr int kSlotB = kPro ? kSlotBytes + kStageTokens * 4 : kSlotBytes;
-    // stages per register set: the maps block runs 8 waves (half the
-    // registers per wave), so it prefetches 3-6 stages ahead; so does the
-    // plain scan (3-6 ahead was faster than 6-12: 42.6 against 48.1 us on
-    // B8 H12 T2048 with a cold cache, 258 against 269 us on B2 H24 T32768);
-    // the prologue scan's staging waves run 6-12 ahead
-    constexpr int kSetK = (kMaps || !kSplit) ? kSet / 2 : kSet;
+    // stages per register set: every instantiation prefetches 3-6 stages
+    // ahead (the bound on T allows for 6-12).  6-12 ahead was slower: the
+    // plain scan 48.1 against 42.6 us on B8 H12 T2048 with a cold cache and
+    // 269 against 258 us on B2 H24 T32768; with the prologue 63.7 against
+    // 57.9 and 341 against 321 us.
+    constexpr int kSetK = kSet / 2;
     static_assert((2 * kSetK) % kSlots == 0, "slot index must be static inside the loop");
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 
@@ -437,9 +439,8 @@ linear_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
                             use_tok ? __uint_as_float(o.e) : et;
                 }
             };
-            // stage s + 1 goes to LDS before barrier s; loads run 6 to 12
-            // stages ahead in two register sets, as in the plain scan (3 to
-            // 6 in a maps block, whose 12 waves have fewer registers each)
+            // stage s + 1 goes to LDS before barrier s; loads run 3 to 6
+            // stages ahead in two register sets, as in the plain scan
             Rows setA[kSetK], setB[kSetK];
             {
                 Rows first;
