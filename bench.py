@@ -68,6 +68,7 @@ PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = {
     "linear_mfma_kernel[scan]": "ttt_linear_mfma.hip",
     "linear_mfma_kernel[maps]": "ttt_linear_mfma.hip",
+    "linear_fused_kernel": "ttt_linear_mfma.hip",
     "linear_mfma_f32_kernel[scan]": "ttt_linear_mfma_f32.hip",
     "linear_mfma_f32_kernel[maps]": "ttt_linear_mfma_f32.hip",
     "linear_cols_f32_kernel[scan]": "ttt_linear_cols_f32.hip",
@@ -155,9 +156,10 @@ def decode_work(w):
     return units * 6 * d * d, units * (2 * d * d * 4 + 4 * d * s)
 
 
-def kernel_names(w, nseg):
+def kernel_names(w, nseg, fused=False):
     """Kernels one forward call dispatches (segmented TTT-Linear: the maps
-    launch, the start-state composition and the segment scans)."""
+    launch, or with the fused layout segment 0's scan beside the maps, the
+    start-state composition and the segment scans)."""
     if w.kind == "mlp":
         return ["mlp_mfma_kernel" if (w.dtype == "bf16" and w.d == 64 and w.m == 256 and w.b == 16)
                 else "mlp_generic_kernel"]
@@ -167,6 +169,8 @@ def kernel_names(w, nseg):
             k = "linear_cols_f32_kernel"
             return [k + "[maps]", k + "[scan]"] if nseg > 1 else [k + "[scan]"]
         k = "linear_mfma_kernel" if w.dtype == "bf16" else "linear_mfma_f32_kernel"
+        if nseg > 1 and fused:
+            return ["linear_fused_kernel", "linear_combine_kernel", k + "[scan]"]
         return [k + "[maps]", "linear_combine_kernel", k + "[scan]"] if nseg > 1 else [k + "[scan]"]
     return ["linear_generic_kernel"]
 
@@ -193,6 +197,17 @@ def backward_kernel_names(w):
         f = "linear_mfma_kernel[maps]" if w.dtype == "bf16" else "linear_mfma_f32_kernel[maps]"
         k = [f, "linear_combine_kernel", b + "[gmaps]", "linear_combine_kernel"] + k
     return k
+
+
+def fused(w):
+    """Whether the library runs this TTT-Linear forward in the fused segment
+    layout."""
+    if w.kind != "linear":
+        return False
+    import torch
+    import test_sequence_layers_linear_amd as ttt
+    return ttt.ttt_linear_fused(w.B, w.H, w.T, w.d, w.b,
+                                torch.float32 if w.dtype == "fp32" else torch.bfloat16)
 
 
 def segments(w):
@@ -642,10 +657,10 @@ def measure_workload(cfg, steps, warmup, cold_reps, roofs=None):
     per_step, fwd, dec = r.measure(steps, warmup)
     flops, nbytes = (linear_work if w.kind == "linear" else mlp_work)(w)
     nseg = segments(w)
-    kern = kernel_names(w, nseg)
+    kern = kernel_names(w, nseg, fused(w))
     cold_mean = r.measure_cold(cold_reps)
     out = {"workload": w.name, "config": cfg, "tokens_per_s": w.B * w.T / per_step,
-           "segments_per_chain": nseg,
+           "segments_per_chain": nseg, "fused_segments": fused(w),
            "ms_per_step": per_step * 1e3, "forward_us": fwd * 1e6,
            "forward_us_cold_llc": cold_mean * 1e6, "input_copies": len(r.input_sets()),
            "forward_tokens_per_s": w.B * w.T / fwd,

@@ -104,6 +104,12 @@ typedef enum {
  * qkv_dtype); with less it uses the fastest count whose maps and states fit
  * (NULL / 0 bytes: one segment, which needs none).  The environment variable
  * TTT_LINEAR_SEGMENTS=S (1..30) forces S segments (fewer if they do not fit).
+ * bf16 at d = 64, b = 16 without the prologue may use the fused layout
+ * (ttt_linear_fused reports it): the first launch also scans segment 0,
+ * which then needs no map and is shorter than the others, and the
+ * composition starts from its end state; with S - 1 workgroups per chain in
+ * each launch, one more segment fits the GPU.  TTT_LINEAR_FUSED=0 turns it
+ * off.  Same workspace size.
  *
  * fp32 Q/K/V at d = 64, b = 16 with B*H*4 <= the GPU's compute units: each
  * chain's W is split by columns over 4 workgroups (the dual form keeps W's
@@ -376,6 +382,14 @@ int ttt_linear_decode_step_ex(const void* q, const void* k, const void* v, int q
  * count.
  */
 int ttt_linear_segments(int64_t B, int64_t H, int64_t T, int d, int b, int qkv_dtype);
+
+/*
+ * 1 if ttt_linear_forward uses the fused segment layout for these sizes on
+ * the current device (segment 0 scanned in the maps launch), 0 if not;
+ * a negative ttt_status for arguments ttt_linear_forward would reject.
+ * Needs no device memory.
+ */
+int ttt_linear_fused(int64_t B, int64_t H, int64_t T, int d, int b, int qkv_dtype);
 
 /*
  * TTT-Linear with momentum gradient descent.  The E2-TTT write-up

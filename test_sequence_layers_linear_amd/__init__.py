@@ -73,6 +73,8 @@ def load_library():
     lib.ttt_linear_backward_segments.restype = I
     lib.ttt_linear_segments.argtypes = [L, L, L, I, I, I]
     lib.ttt_linear_segments.restype = I
+    lib.ttt_linear_fused.argtypes = [L, L, L, I, I, I]
+    lib.ttt_linear_fused.restype = I
     lib.ttt_linear_forward_noalloc.argtypes = [P, P, P, I, P, I, P, L, L, L, I, I, P, P, P]
     lib.ttt_linear_forward_noalloc.restype = I
     lib.ttt_linear_noalloc_max_workspace_bytes.argtypes = []
@@ -544,6 +546,15 @@ def ttt_linear_segments(B: int, H: int, T: int, d: int, b: int, dtype=torch.bflo
     return n
 
 
+def ttt_linear_fused(B: int, H: int, T: int, d: int, b: int, dtype=torch.bfloat16) -> bool:
+    """Whether ttt_linear_forward uses the fused segment layout (segment 0
+    scanned beside the maps) for these sizes on the current device."""
+    code = TTT_F32 if dtype == torch.float32 else TTT_BF16
+    n = load_library().ttt_linear_fused(int(B), int(H), int(T), int(d), int(b), code)
+    _check(min(n, 0))
+    return bool(n)
+
+
 def ttt_linear_workspace_bytes(B: int, H: int, T: int, d: int, b: int,
                                dtype=torch.bfloat16) -> int:
     """Workspace bytes ttt_linear_forward uses for these sizes on the current
@@ -578,7 +589,7 @@ __all__ = [
     "ttt_linear_forward", "ttt_linear_forward_ex", "ttt_linear_forward_noalloc",
     "ttt_mlp_forward", "ttt_linear_decode_step",
     "ttt_linear_decode_step_ex", "ttt_linear_backward",
-    "ttt_linear_segments", "ttt_linear_backward_segments", "ttt_linear_workspace_bytes",
+    "ttt_linear_segments", "ttt_linear_fused", "ttt_linear_backward_segments", "ttt_linear_workspace_bytes",
     "ttt_linear_backward_workspace_bytes", "ttt_linear_momentum_forward",
     "ttt_linear_momentum_workspace_bytes", "ttt_linear_momentum_segments",
     "load_library",

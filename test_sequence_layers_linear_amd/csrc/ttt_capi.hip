@@ -10,6 +10,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <cmath>
 #include <functional>
 #include <mutex>
 
@@ -20,7 +21,7 @@ using ttt::MlpArgs;
 using ttt::DecodeArgs;
 using ttt::MomentumArgs;
 
-constexpr int kAbiVersion = (2 << 16) | 2;
+constexpr int kAbiVersion = (2 << 16) | 3;
 
 bool valid_dtype(int dt) { return dt == TTT_F32 || dt == TTT_BF16; }
 size_t elem_bytes(int dt) { return dt == TTT_F32 ? 4 : 2; }
@@ -246,12 +247,71 @@ LinearScan pick_scan(const LinearArgs& a)
     return {nullptr, nullptr};
 }
 
-// The plan a forward of these sizes uses with `ws_bytes` of workspace.
+// The fused layout with S segments (bf16 TTT-Linear without the prologue):
+// segment 0 of L0 chunks, scanned beside the maps of segments 1 .. S - 2 of L
+// chunks each, L0 = ratio L so that the two roles of the first launch end
+// together; the last segment takes the rest.  nseg = 1 if S does not fit.
+ttt::SegmentPlan fused_with_segments(int64_t T, int chunk, int S, double ratio)
+{
+    ttt::SegmentPlan p = with_segments(T, chunk, 1);
+    const int64_t chunks = (T + chunk - 1) / chunk;
+    if (S < 3) return p;
+    const int64_t L = static_cast<int64_t>(std::ceil(chunks / (S - 1 + ratio)));
+    const int64_t L0 = std::max<int64_t>(1, chunks - (S - 1) * L);
+    if (L0 + (S - 2) * L >= chunks) return p;       // the last segment would be empty
+    p.nseg = S;
+    p.seg_len = L * chunk;
+    p.first_len = L0 * chunk;
+    p.fused = true;
+    return p;
+}
+
+// Estimated duration (us) of a bf16 TTT-Linear plan, from the segment costs:
+// unfused, the longest segment's map and scan; fused, the longer role of the
+// first launch, then a segment's scan.
+double plan_cost(const ttt::SegmentPlan& p, int64_t T, int chunk, const ttt::SegmentCosts& cost)
+{
+    const int64_t chunks = (T + chunk - 1) / chunk;
+    if (p.nseg <= 1) return static_cast<double>(chunks) * cost.fwd;
+    const double L = static_cast<double>(p.seg_len / chunk);
+    if (!p.fused) return L * (cost.map + cost.fwd) + (p.nseg - 1) * cost.apply + cost.launch;
+    const double L0 = static_cast<double>(p.first() / chunk);
+    return std::max(L0 * cost.fwd * ttt::kStagedScanFactor, L * cost.map) +
+           (p.nseg - 2) * cost.apply + cost.launch + L * cost.fwd;
+}
+
+// The plan a forward of these sizes uses with `ws_bytes` of workspace.  The
+// bf16 MFMA scan without the prologue also weighs the fused layout (off with
+// TTT_LINEAR_FUSED=0): its two launches hold units (S - 1) workgroups each,
+// so it may use one more segment than the unfused layout on the same CUs.
 ttt::SegmentPlan plan_forward(const LinearArgs& a, int64_t ws_bytes)
 {
     const LinearScan k = pick_scan(a);
-    if (!k.cost || a.B * a.H == 0 || a.T == 0) return with_segments(a.T, a.b, 1);
-    return plan_segments(a.B * a.H, a.T, a.b, a.d, *k.cost, ws_bytes);
+    const int64_t units = a.B * a.H;
+    if (!k.cost || units == 0 || a.T == 0) return with_segments(a.T, a.b, 1);
+    const ttt::SegmentPlan unfused = plan_segments(units, a.T, a.b, a.d, *k.cost, ws_bytes);
+    const char* off = getenv("TTT_LINEAR_FUSED");
+    if (k.cost != &ttt::kLinearBf16Costs || a.pro.active() || (off && strtol(off, nullptr, 10) == 0))
+        return unfused;
+    const ttt::SegmentCosts& cost = *k.cost;
+    const double ratio = cost.map / (cost.fwd * ttt::kStagedScanFactor);
+    auto fits = [&](const ttt::SegmentPlan& p) {
+        return forward_workspace_bytes(units, a.d, p.nseg) <= ws_bytes;
+    };
+    if (getenv("TTT_LINEAR_SEGMENTS")) {         // forced: the same count, fused when it can be
+        const ttt::SegmentPlan f = fused_with_segments(a.T, a.b, unfused.nseg, ratio);
+        return f.fused && f.nseg == unfused.nseg && fits(f) ? f : unfused;
+    }
+    const int64_t cus = device_cus();
+    ttt::SegmentPlan best = unfused;
+    double best_t = plan_cost(unfused, a.T, a.b, cost);
+    for (int S = 3; S <= ttt::kMaxSegments && cus > 0 && units * (S - 1) <= cus; ++S) {
+        const ttt::SegmentPlan f = fused_with_segments(a.T, a.b, S, ratio);
+        if (!f.fused || !fits(f)) continue;
+        const double t = plan_cost(f, a.T, a.b, cost);
+        if (t < best_t) { best = f; best_t = t; }
+    }
+    return best;
 }
 
 // Size checks shared by the TTT-Linear entry points and their queries.
@@ -418,6 +478,14 @@ int ttt_linear_segments(int64_t B, int64_t H, int64_t T, int d, int b, int qkv_d
     LinearArgs a{nullptr, nullptr, nullptr, qkv_dtype, nullptr, 0, nullptr, B, H, T, d, b,
                  nullptr, nullptr, nullptr};
     return plan_forward(a, INT64_MAX).nseg;
+}
+
+int ttt_linear_fused(int64_t B, int64_t H, int64_t T, int d, int b, int qkv_dtype)
+{
+    if (const int st = linear_sizes_status(B, H, T, d, b, qkv_dtype)) return st;
+    LinearArgs a{nullptr, nullptr, nullptr, qkv_dtype, nullptr, 0, nullptr, B, H, T, d, b,
+                 nullptr, nullptr, nullptr};
+    return plan_forward(a, INT64_MAX).fused ? 1 : 0;
 }
 
 }  // extern "C"

@@ -182,10 +182,16 @@ hipError_t launch_mlp_generic(const MlpArgs& a);
 // and a third runs every segment's scan from its start state.
 struct SegmentPlan {
     int nseg = 1;
-    int64_t seg_len = 0;
+    int64_t seg_len = 0;        // tokens of segments 1 .. nseg - 1
+    int64_t first_len = 0;      // tokens of segment 0 (0: seg_len)
     float* maps = nullptr;
     float* wstart = nullptr;
     bool starts_only = false;   // maps and start states only, no segment scans
+    // segment 0 scanned beside the maps of segments 1 .. nseg - 2 (bf16
+    // TTT-Linear without the prologue): no map of segment 0, and the
+    // composition starts from its end state
+    bool fused = false;
+    int64_t first() const { return first_len > 0 ? first_len : seg_len; }
 };
 
 // Block id -> (chain u, block s of the chain) for nb blocks per chain.  With
@@ -227,7 +233,15 @@ bool linear_mfma_supports(const LinearArgs& a);
 hipError_t launch_linear_mfma(const LinearArgs& a, const SegmentPlan& p);
 bool linear_mfma_f32_supports(const LinearArgs& a);
 hipError_t launch_linear_mfma_f32(const LinearArgs& a, const SegmentPlan& p);
-constexpr SegmentCosts kLinearBf16Costs{0.35, 0.25, 0.60, 8.5, 1};
+// bf16: chunk costs of the current scan and maps on MI355X, and the fixed
+// cost of a segmented call (the extra launches, the composition's launch and
+// the launches' tails), fitted to B8 H12 T2048 (unsegmented 40 us, fused with
+// 3 segments 46 us) and B2 H24 T32768 (unfused with 5 segments 237-255 us,
+// fused with 6 segments 227-230 us)
+constexpr SegmentCosts kLinearBf16Costs{0.32, 0.25, 0.60, 18.0, 1};
+// a chunk of the 12-wave staged scan (the fused layout's segment 0) over one
+// of the plain 4-wave scan: 163 against 140 us per segment on B2 H24 T32768
+constexpr double kStagedScanFactor = 1.16;
 constexpr SegmentCosts kLinearF32Costs{1.38, 0.90, 0.60, 8.5, 2};
 // fp32 Q/K/V with each chain's W split by columns over 4 workgroups
 // (ttt_linear_cols_f32.hip, with or without the prologue): used while the chains'

@@ -63,11 +63,13 @@ namespace {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // X_0 = [W0; M0] (rows kD .. kRows - 1 from M0 when kRows > kD; zero without
-// M0), then the composition; xstart: [units][nseg][kRows][kD]
+// M0), then the composition; xstart: [units][nseg][kRows][kD].  first = 1:
+// X_1 is already in xstart (segment 0 was scanned; map 0 is not used) and
+// the composition starts there.
 template <int kRows>
 __device__ __forceinline__ void combine_chain(const float* W0, int w0_per_batch, const float* M0,
                                               int H, int64_t units, const float* __restrict__ maps,
-                                              int nseg, float* __restrict__ xstart)
+                                              int nseg, float* __restrict__ xstart, int first)
 {
     using S = Shape<kRows>;
     constexpr int kDepth = S::kDepth;
@@ -104,15 +106,17 @@ __device__ __forceinline__ void combine_chain(const float* W0, int w0_per_batch,
     // thread tid moves rows tid / 16 + (kRows / 4) q, column tid % 16 of a slice
     {
         float x[4];
+        const float* x1 = out + kRows * kD;      // X_1 when first = 1
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int row = tid / 16 + (kRows / 4) * q;
-            x[q] = row < kD ? w0[row * kD + 16 * J + tid % 16]
+            x[q] = first ? x1[row * kD + 16 * J + tid % 16]
+                 : row < kD ? w0[row * kD + 16 * J + tid % 16]
                             : (m0 ? m0[(row - kD) * kD + 16 * J + tid % 16] : 0.f);
         }
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-            Wl[(tid / 16 + (kRows / 4) * q) * kPad + tid % 16] = x[q];
+            Wl[first * S::kSliceFloats + (tid / 16 + (kRows / 4) * q) * kPad + tid % 16] = x[q];
     }
 
     // operands of step j: a[s] = M_j[16 I + c][kK g + s] (A of k-step s, whose
@@ -133,7 +137,7 @@ __device__ __forceinline__ void combine_chain(const float* W0, int w0_per_batch,
     };
 #pragma unroll
     for (int q = 0; q < kDepth; ++q)
-        load_ops(a[q], n[q], q);             // nseg >= 2 whenever this kernel runs
+        load_ops(a[q], n[q], first + q);     // nseg >= 2 whenever this kernel runs
     __syncthreads();
 
     // step j with the operands of ring entry q: X_{j+1} slice into LDS, then
@@ -159,7 +163,7 @@ __device__ __forceinline__ void combine_chain(const float* W0, int w0_per_batch,
     };
     // full rounds of kDepth steps, then the last partial round with an exit
     // (kept out of the full rounds, whose schedule it would disturb)
-    int j0 = 0;
+    int j0 = first;
     for (; j0 + kDepth + 1 <= nseg; j0 += kDepth) {
 #pragma unroll
         for (int q = 0; q < kDepth; ++q)
@@ -172,7 +176,7 @@ __device__ __forceinline__ void combine_chain(const float* W0, int w0_per_batch,
         step(q, j0 + q);
     }
 
-    for (int j = 0; j < nseg; ++j) {
+    for (int j = first; j < nseg; ++j) {
         const float* Ws = Wl + j * S::kSliceFloats;
         float* o = out + j * kRows * kD;
 #pragma unroll
@@ -184,16 +188,17 @@ __device__ __forceinline__ void combine_chain(const float* W0, int w0_per_batch,
 
 __global__ void __launch_bounds__(Shape<64>::kThreads, 1)
 linear_combine_kernel(const float* W0, int w0_per_batch, int H, int64_t units,
-                      const float* __restrict__ maps, int nseg, float* __restrict__ wstart)
+                      const float* __restrict__ maps, int nseg, float* __restrict__ wstart,
+                      int first)
 {
-    combine_chain<64>(W0, w0_per_batch, nullptr, H, units, maps, nseg, wstart);
+    combine_chain<64>(W0, w0_per_batch, nullptr, H, units, maps, nseg, wstart, first);
 }
 
 __global__ void __launch_bounds__(Shape<128>::kThreads, 1)
 momentum_combine_kernel(const float* W0, int w0_per_batch, const float* M0, int H, int64_t units,
                         const float* __restrict__ maps, int nseg, float* __restrict__ xstart)
 {
-    combine_chain<128>(W0, w0_per_batch, M0, H, units, maps, nseg, xstart);
+    combine_chain<128>(W0, w0_per_batch, M0, H, units, maps, nseg, xstart, 0);
 }
 
 template <int kRows, typename Kernel, typename... Args>
@@ -222,7 +227,8 @@ hipError_t launch_linear_combine(const LinearArgs& a, const SegmentPlan& p)
     const int64_t units = a.B * a.H;
     return launch_combine<64>(linear_combine_kernel, units, p.nseg, a.stream, a.W0,
                               a.w0_per_batch, static_cast<int>(a.H), units,
-                              static_cast<const float*>(p.maps), p.nseg, p.wstart);
+                              static_cast<const float*>(p.maps), p.nseg, p.wstart,
+                              p.fused ? 1 : 0);
 }
 
 hipError_t launch_momentum_combine(const MomentumArgs& a, const float* maps, int nseg,

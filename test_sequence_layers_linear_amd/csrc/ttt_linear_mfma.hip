@@ -119,13 +119,17 @@ struct StageRegs {
 //   lines: 278 us against 288 us per call on B2 H24 T32768 with a cold
 //   cache, where 75 MB of inputs that the cache can hold load 10% slower
 //   when they are re-read warm).
+// One workgroup's work: segment s of chain u (segment 0 holds first_len
+// tokens, the others seg_len each).  end_to_wstart: the scan of segment 0
+// writes its end state as the start state of segment 1 (the first launch of
+// the fused layout, see linear_fused_kernel).
 template <bool kMaps, bool kPro, bool kStream>
-__global__ void __launch_bounds__(kPro || kMaps ? 3 * kThreads : kThreads, 1)
-linear_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-                   const uint16_t* __restrict__ V, const float* W0, int w0_per_batch,
-                   const float* __restrict__ eta, int H, int T, int64_t units, int seg_len,
-                   int nseg, float* maps, const float* wstart, uint16_t* __restrict__ Y,
-                   float* W_out, Prologue pro)
+__device__ __forceinline__ void
+linear_body(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+            const uint16_t* __restrict__ V, const float* W0, int w0_per_batch,
+            const float* __restrict__ eta, int H, int T, int seg_len, int first_len, int nseg,
+            float* maps, float* wstart, uint16_t* __restrict__ Y, float* W_out,
+            const Prologue& pro, int64_t u, int s, bool end_to_wstart)
 {
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
 
@@ -142,17 +146,10 @@ linear_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     const int g = lane >> 4;
     const int col = 16 * w + c;          // this lane's column of W
 
-    int64_t u = blockIdx.x;
-    int s = 0;
-    if (nseg > 1) {
-        xcd_block(blockIdx.x, kMaps ? nseg - 1 : nseg, units, u, s);
-        if (u >= units)                  // padding of the XCD placement
-            return;
-    }
     const int h = static_cast<int>(u % H);
     const float et = eta[h];
-    const int t_begin = s * seg_len;
-    const int t_len = min(seg_len, T - t_begin);
+    const int t_begin = s == 0 ? 0 : first_len + (s - 1) * seg_len;
+    const int t_len = max(0, min(s == 0 ? first_len : seg_len, T - t_begin));
     // map j of chain u: M at maps + (u (nseg - 1) + j) 2 64 64, N right after
     auto map_ptr = [&](int j) { return maps + ((u * (nseg - 1) + j) * 2) * kD * kD; };
 
@@ -165,8 +162,10 @@ linear_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
             for (int r = 0; r < 4; ++r)
                 Wacc[mt][r] = (half == 0 && rho(mt, 4 * g + r) == col) ? 1.0f : 0.0f;
     } else if (!kSplit || !stager) {
-        const float* w0 = nseg > 1 ? wstart + (u * nseg + s) * kD * kD
-                                   : W0 + (w0_per_batch ? u : h) * kD * kD;
+        // segment 0 (or the only one) starts from W0, the others from the
+        // composed start states
+        const float* w0 = s > 0 ? wstart + (u * nseg + s) * kD * kD
+                                : W0 + (w0_per_batch ? u : h) * kD * kD;
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -552,6 +551,8 @@ done:
         wo = map_ptr(s) + half * kD * kD;
     else if (s == nseg - 1)
         wo = W_out + u * kD * kD;
+    else if (end_to_wstart)
+        wo = wstart + (u * nseg + 1) * kD * kD;
     else
         return;
 #pragma unroll
@@ -559,6 +560,56 @@ done:
 #pragma unroll
         for (int r = 0; r < 4; ++r)
             wo[rho(mt, 4 * g + r) * kD + col] = Wacc[mt][r];
+}
+
+// The scans or maps of the plan: segments seg_base .. of every chain (maps:
+// segments 0 .. nseg - 2), nb workgroups per chain placed by xcd_block.
+template <bool kMaps, bool kPro, bool kStream>
+__global__ void __launch_bounds__(kPro || kMaps ? 3 * kThreads : kThreads, 1)
+linear_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                   const uint16_t* __restrict__ V, const float* W0, int w0_per_batch,
+                   const float* __restrict__ eta, int H, int T, int64_t units, int seg_len,
+                   int first_len, int nseg, int seg_base, float* maps, float* wstart,
+                   uint16_t* __restrict__ Y, float* W_out, Prologue pro)
+{
+    int64_t u = blockIdx.x;
+    int s = 0;
+    if (nseg > 1) {
+        xcd_block(blockIdx.x, kMaps ? nseg - 1 : nseg - seg_base, units, u, s);
+        if (u >= units)                  // padding of the XCD placement
+            return;
+    }
+    linear_body<kMaps, kPro, kStream>(Q, K, V, W0, w0_per_batch, eta, H, T, seg_len, first_len,
+                                      nseg, maps, wstart, Y, W_out, pro, u, s + seg_base, false);
+}
+
+// First launch of the fused layout: per chain, workgroup 0 scans segment 0
+// (Y rows and its end state, the start state of segment 1) while workgroups
+// 1 .. nseg - 2 form the maps of segments 1 .. nseg - 2, so segment 0 needs no
+// map.  Both roles run 12 waves: the scan in the staged form of the prologue
+// scan with the prologue off (the same products as the plain scan, bit for
+// bit), the maps as in the unfused layout.
+template <bool kStream>
+__global__ void __launch_bounds__(3 * kThreads, 1)
+linear_fused_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                    const uint16_t* __restrict__ V, const float* W0, int w0_per_batch,
+                    const float* __restrict__ eta, int H, int T, int64_t units, int seg_len,
+                    int first_len, int nseg, float* maps, float* wstart,
+                    uint16_t* __restrict__ Y, float* W_out)
+{
+    int64_t u = blockIdx.x;
+    int s = 0;
+    xcd_block(blockIdx.x, nseg - 1, units, u, s);
+    if (u >= units)
+        return;
+    if (s == 0)
+        linear_body<false, true, kStream>(Q, K, V, W0, w0_per_batch, eta, H, T, seg_len,
+                                          first_len, nseg, maps, wstart, Y, W_out, Prologue{}, u,
+                                          0, true);
+    else
+        linear_body<true, false, kStream>(Q, K, V, W0, w0_per_batch, eta, H, T, seg_len,
+                                          first_len, nseg, maps, wstart, Y, W_out, Prologue{}, u,
+                                          s, false);
 }
 
 }  // namespace
@@ -581,25 +632,35 @@ hipError_t launch_bf16(const LinearArgs& a, const SegmentPlan& p)
     auto* y = static_cast<uint16_t*>(a.Y);
     const int H = static_cast<int>(a.H), T = static_cast<int>(a.T);
     const int seg_len = static_cast<int>(p.seg_len);
+    const int first_len = static_cast<int>(p.first());
     const int64_t units = a.B * a.H;
     const int lds = kSlots * (kPro ? kSlotBytes + kStageTokens * 4 : kSlotBytes);
+    int seg_base = 0;
     if (p.nseg > 1) {
         const dim3 grid(static_cast<unsigned>(placed_grid(units, p.nseg - 1)));
-        hipLaunchKernelGGL((linear_mfma_kernel<true, kPro, kStream>), grid, dim3(3 * kThreads), lds,
-                           a.stream, q,
-                           k, v, a.W0, a.w0_per_batch, a.eta, H, T, units, seg_len, p.nseg, p.maps,
-                           p.wstart, y, a.W_out, a.pro);
+        if (p.fused) {
+            // (the staged scan's slots also hold the step sizes)
+            hipLaunchKernelGGL((linear_fused_kernel<kStream>), grid, dim3(3 * kThreads),
+                               kSlots * (kSlotBytes + kStageTokens * 4), a.stream, q, k, v, a.W0,
+                               a.w0_per_batch, a.eta, H, T, units, seg_len, first_len, p.nseg,
+                               p.maps, p.wstart, y, a.W_out);
+            seg_base = 1;
+        } else {
+            hipLaunchKernelGGL((linear_mfma_kernel<true, kPro, kStream>), grid, dim3(3 * kThreads),
+                               lds, a.stream, q, k, v, a.W0, a.w0_per_batch, a.eta, H, T, units,
+                               seg_len, first_len, p.nseg, 0, p.maps, p.wstart, y, a.W_out, a.pro);
+        }
         hipError_t e = hipGetLastError();
         if (e == hipSuccess)
             e = launch_linear_combine(a, p);
         if (e != hipSuccess || p.starts_only)
             return e;
     }
-    const dim3 grid(static_cast<unsigned>(p.nseg > 1 ? placed_grid(units, p.nseg) : units));
+    const dim3 grid(static_cast<unsigned>(p.nseg > 1 ? placed_grid(units, p.nseg - seg_base) : units));
     hipLaunchKernelGGL((linear_mfma_kernel<false, kPro, kStream>), grid, dim3(kPro ? 3 * kThreads : kThreads), lds,
                        a.stream, q, k, v,
-                       a.W0, a.w0_per_batch, a.eta, H, T, units, seg_len, p.nseg, p.maps, p.wstart, y,
-                       a.W_out, a.pro);
+                       a.W0, a.w0_per_batch, a.eta, H, T, units, seg_len, first_len, p.nseg, seg_base,
+                       p.maps, p.wstart, y, a.W_out, a.pro);
     return hipGetLastError();
 }
 

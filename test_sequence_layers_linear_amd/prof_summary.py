@@ -32,6 +32,7 @@ CSRC = os.path.join(ROOT, "test_sequence_layers_linear_amd", "csrc")
 KERNEL_FILES = {
     "linear_mfma_kernel[scan]": "ttt_linear_mfma.hip",
     "linear_mfma_kernel[maps]": "ttt_linear_mfma.hip",
+    "linear_fused_kernel": "ttt_linear_mfma.hip",
     "linear_mfma_f32_kernel[scan]": "ttt_linear_mfma_f32.hip",
     "linear_mfma_f32_kernel[maps]": "ttt_linear_mfma_f32.hip",
     "linear_cols_f32_kernel[scan]": "ttt_linear_cols_f32.hip",
@@ -68,9 +69,12 @@ COPY_NAME = "__amd_rocclr_copyBuffer"
 
 def short_name(full: str) -> str:
     """Kernel key: the function name, with [maps] / [scan] for the two
-    instantiations of the TTT-Linear forward kernels and [gmaps] / [segments]
+    instantiations of the TTT-Linear forward kernels (the fused layout's first
+    launch, segment 0's scan beside the maps, is linear_fused_kernel) and [gmaps] / [segments]
     for the backward's cotangent maps and segment backward (+prologue for
     the instantiations with the input prologue)."""
+    if "linear_fused_kernel<" in full:       # kStream only: one key
+        return "linear_fused_kernel"
     if "momentum_mfma_kernel<" in full:      # kExact, kMap
         args = [a.strip() for a in full.split("momentum_mfma_kernel<", 1)[1].split(">", 1)[0].split(",")]
         mode = "exact" if args[0] == "true" else "chunk_start"

@@ -43,7 +43,7 @@ def test_exports_every_declared_function(lib):
                           "ttt_linear_workspace_bytes", "ttt_linear_backward_workspace_bytes",
                           "ttt_status_string", "ttt_roof_copy", "ttt_roof_mfma", "ttt_roof_launch",
                           "ttt_linear_forward_noalloc", "ttt_linear_noalloc_max_workspace_bytes",
-                          "ttt_linear_momentum_segments",
+                          "ttt_linear_momentum_segments", "ttt_linear_fused",
                           "ttt_abi_version"}
     for n in names:
         assert hasattr(lib, n), f"{n} declared in ttt.h but not exported"
@@ -258,6 +258,29 @@ def test_segment_query_validation_and_override(lib, monkeypatch):
     assert lib.ttt_linear_segments(1, 4, 30 * 16, 64, 16, 0) == 30
     monkeypatch.setenv("TTT_LINEAR_SEGMENTS", "3")
     assert lib.ttt_linear_segments(1, 4, 2048, 32, 16, 0) == 1     # generic kernel: no split
+
+
+def test_fused_layout_query(lib, monkeypatch):
+    """ttt_linear_fused validates like ttt_linear_segments; with a forced
+    segment count of 3 or more the bf16 d = 64, b = 16 forward takes the
+    fused layout (same count, same workspace), unless TTT_LINEAR_FUSED=0;
+    fp32, other shapes and two segments never do."""
+    assert lib.ttt_linear_fused(-1, 3, 64, 64, 16, 1) == INVALID
+    assert lib.ttt_linear_fused(1, 3, 64, 48, 16, 1) == UNSUPPORTED
+    assert lib.ttt_linear_fused(0, 3, 64, 64, 16, 1) == 0
+    monkeypatch.delenv("TTT_LINEAR_FUSED", raising=False)
+    monkeypatch.setenv("TTT_LINEAR_SEGMENTS", "6")
+    assert lib.ttt_linear_fused(2, 24, 32768, 64, 16, 1) == 1
+    assert lib.ttt_linear_segments(2, 24, 32768, 64, 16, 1) == 6
+    assert lib.ttt_linear_workspace_bytes(2, 24, 32768, 64, 16, 1) == 48 * (3 * 6 - 2) * 64 * 64 * 4
+    assert lib.ttt_linear_fused(2, 24, 32768, 64, 16, 0) == 0      # fp32
+    assert lib.ttt_linear_fused(2, 24, 32768, 32, 16, 1) == 0      # generic kernel
+    monkeypatch.setenv("TTT_LINEAR_SEGMENTS", "2")
+    assert lib.ttt_linear_fused(2, 24, 32768, 64, 16, 1) == 0
+    monkeypatch.setenv("TTT_LINEAR_SEGMENTS", "6")
+    monkeypatch.setenv("TTT_LINEAR_FUSED", "0")
+    assert lib.ttt_linear_fused(2, 24, 32768, 64, 16, 1) == 0
+    assert lib.ttt_linear_segments(2, 24, 32768, 64, 16, 1) == 6
 
 
 def test_backward_segment_query_validation_and_override(lib, monkeypatch):
