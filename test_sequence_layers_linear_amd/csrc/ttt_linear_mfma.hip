@@ -162,10 +162,13 @@ linear_body(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
             for (int r = 0; r < 4; ++r)
                 Wacc[mt][r] = (half == 0 && rho(mt, 4 * g + r) == col) ? 1.0f : 0.0f;
     } else if (!kSplit || !stager) {
-        // segment 0 (or the only one) starts from W0, the others from the
-        // composed start states
-        const float* w0 = s > 0 ? wstart + (u * nseg + s) * kD * kD
-                                : W0 + (w0_per_batch ? u : h) * kD * kD;
+        // W0 itself only for the only segment and for segment 0 in the fused
+        // layout's first launch, which runs before any segment writes W_out
+        // (W_out may be W0); otherwise the start states of the composition
+        // (its copy of W0 for segment 0)
+        const bool from_w0 = nseg == 1 || end_to_wstart;
+        const float* w0 = from_w0 ? W0 + (w0_per_batch ? u : h) * kD * kD
+                                  : wstart + (u * nseg + s) * kD * kD;
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll

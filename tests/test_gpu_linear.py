@@ -225,21 +225,37 @@ def test_nan_propagates():
 # chain is cut into segments whose maps are composed (forced segment counts;
 # the benchmark workloads above use the library's own choice)
 # ---------------------------------------------------------------------------
+@pytest.mark.parametrize("fused", ["1", "0"])
 @pytest.mark.parametrize("cfg", [2, 3])
 @pytest.mark.parametrize("T,S,per_batch", [(100, 2, False), (333, 3, True), (1000, 7, False),
                                            (100, 50, True), (512, 4, False), (48, 3, False)])
-def test_segmented_scan(cfg, T, S, per_batch, monkeypatch):
+def test_segmented_scan(cfg, T, S, per_batch, fused, monkeypatch):
+    """Forced segment counts against the oracle; bf16 runs S >= 3 in the
+    fused layout (segment 0 scanned beside the maps) unless
+    TTT_LINEAR_FUSED=0."""
+    if cfg == 2 and fused == "0":
+        pytest.skip("fp32 has no fused layout")
     monkeypatch.setenv("TTT_LINEAR_SEGMENTS", str(S))
+    monkeypatch.setenv("TTT_LINEAR_FUSED", fused)
     w = WORKLOADS[cfg].with_(B=2, H=3, T=T, w0=("normal", 0.3), eta=("uniform", 0.01, 0.1))
-    announce("linear segmented", cfg, T, S, per_batch)
+    announce("linear segmented", cfg, T, S, per_batch, "fused" if fused == "1" else "unfused")
+    is_fused = ttt.ttt_linear_fused(w.B, w.H, w.T, w.d, w.b, w.torch_dtype)
+    if cfg == 2 or fused == "0":
+        assert not is_fused
+    elif (T, S) == (1000, 7):                    # room for a shorter segment 0
+        assert is_fused
     _check(make_inputs(w, 400 + T + S, w0_per_batch=per_batch), 16, w.dtype)
 
 
+@pytest.mark.parametrize("fused", ["1", "0"])
 @pytest.mark.parametrize("cfg", [2, 3])
-def test_segmented_in_place_and_deterministic(cfg, monkeypatch):
+def test_segmented_in_place_and_deterministic(cfg, fused, monkeypatch):
     """W_out == W0 with several segments: the later segments still start from
-    the original W0; repeated calls agree bit for bit."""
+    the original W0 (in the unfused layout segment 0 reads the composition's
+    copy of it, since the last segment writes W_out in the same launch);
+    repeated calls agree bit for bit."""
     monkeypatch.setenv("TTT_LINEAR_SEGMENTS", "4")
+    monkeypatch.setenv("TTT_LINEAR_FUSED", fused)
     w = WORKLOADS[cfg].with_(B=2, H=3, T=300)
     g = to_gpu(make_inputs(w, 71, w0_per_batch=True))
     Y_ref, W_ref = linear_gpu(g, 16)
