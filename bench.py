@@ -20,7 +20,9 @@ one forward call / its mean duration from HIP events recorded on the launch
 stream, for back-to-back calls that cycle through copies of the inputs, so
 many that at least 512 MB of other inputs are read between two uses of a copy:
 the 256 MB last-level cache cannot serve them (the cold-cache protocol of
-rotated input sets; no flush kernel runs between the calls); the same figure
+rotated input sets; no flush kernel runs between the calls; the cycle first
+runs untimed for 50 ms of GPU time, so the timed calls see the steady state
+rather than the slower first calls after the decode graph); the same figure
 for back-to-back calls on one input set in
 the timed region is roofline.warm.  A call is one kernel launch, except a
 segmented TTT-Linear scan: maps, start-state composition and segment scans,
@@ -244,10 +246,17 @@ def stored_traffic(kernels, workload):
     return total
 
 
-def roofline(w, flops, nbytes, seconds, kernels, roofs=None, warm_seconds=None):
-    """Roofline object of one forward call: `seconds` is its cold-cache
-    mean duration (calls cycling through input copies), `warm_seconds` (optional) the back-to-back one; `roofs`
-    the measured copy bandwidth and MFMA throughputs."""
+COLD_TIMING = ("HIP events around back-to-back calls cycling through copies of the inputs; "
+               ">= 512 MB of other inputs read between two uses of a copy; the cycle warmed "
+               "for 50 ms of GPU time first")
+
+
+def roofline(w, flops, nbytes, seconds, kernels, roofs=None, warm_seconds=None,
+             timing=COLD_TIMING):
+    """Roofline object of one call: `seconds` is its mean duration as `timing`
+    states (for a forward: cold cache, calls cycling through input copies),
+    `warm_seconds` (optional) the back-to-back one; `roofs` the measured copy
+    bandwidth and MFMA throughputs."""
     dt = "bf16" if w.dtype == "bf16" else "fp32"
     ridge = PEAK_FLOPS[dt] / PEAK_HBM
     roofs = roofs or {}
@@ -262,8 +271,7 @@ def roofline(w, flops, nbytes, seconds, kernels, roofs=None, warm_seconds=None):
     out = {"bound": bound, "achieved": round(ach, 3), "peak": peak, "unit": unit,
            "frac": round(ach / peak, 5), "traffic": stored_traffic(kernels, w.name),
            "kernel": " + ".join(kernels), "mean_launch_us": round(seconds * 1e6, 3),
-           "timing": ("HIP events around back-to-back calls cycling through copies of the "
-                      "inputs; >= 512 MB of other inputs read between two uses of a copy"),
+           "timing": timing,
            "peak_measured": round(meas, 3) if meas else None,
            "frac_of_measured": round(ach / meas, 5) if meas else None,
            "algorithmic_flops": flops, "algorithmic_bytes": nbytes,
@@ -275,16 +283,30 @@ def roofline(w, flops, nbytes, seconds, kernels, roofs=None, warm_seconds=None):
     return out
 
 
-def cycle_timed(torch, call, sets, reps):
+def cycle_timed(torch, call, sets, reps, warm_seconds=0.05):
     """Mean duration of back-to-back calls that cycle through the input sets
-    (one warm-up pass over them, then at least `reps` calls and at least two
-    passes), from HIP events at the two ends."""
-    for x in sets:
-        call(x)
+    (at least `reps` calls and at least two passes), from HIP events at the
+    two ends.  Before the timed calls the cycle runs untimed passes until
+    they have kept the GPU busy for `warm_seconds`: after an idle spell or a
+    phase of short launches (decode steps), the first few dozen large calls
+    run up to 15% slower than the steady state that a serving loop sees
+    (B2 H24 T32768: 266, 246, then 228 us per call over three 30-call
+    passes, 225 us from then on)."""
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    warmed = 0.0
+    while True:
+        torch.cuda.synchronize()
+        a.record()
+        for x in sets:
+            call(x)
+        b.record()
+        torch.cuda.synchronize()
+        warmed += a.elapsed_time(b) / 1e3
+        if warmed >= warm_seconds:
+            break
     n = max(reps, 2 * len(sets))
     n = -(-n // len(sets)) * len(sets)
     torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record()
     for i in range(n):
         call(sets[i % len(sets)])
@@ -669,7 +691,9 @@ def measure_workload(cfg, steps, warmup, cold_reps, roofs=None):
         bt = r.measure_backward(max(3, steps // 2), 2)
         bf, bb = linear_backward_work(w)
         kern = backward_kernel_names(w)
-        rf = roofline(w, bf, bb, bt, kern)   # bf16 inputs run on bf16 MFMA, fp32 on fp32
+        # bf16 inputs run on bf16 MFMA, fp32 on fp32
+        rf = roofline(w, bf, bb, bt, kern,
+                      timing="HIP events around back-to-back calls on one input set")
         rf["traffic"] = stored_traffic(kern, w.name + "/backward")
         out["backward"] = {"us": bt * 1e6, "tokens_per_s": w.B * w.T / bt, "roofline": rf}
         pt = r.measure_prologue(max(3, steps // 2), 2)

@@ -27,6 +27,8 @@ namespace {
 // (batch, head) at d = 64.  Measured on MI355X for 48 heads in a HIP graph of
 // 256 steps: 2.07 us per step, against 2.36 with 64 columns per wave (one
 // wave per head: twice the loads per lane in one wave) and 2.48 with 16.
+// The other 3 lane bits number the row groups, so that every sum over the
+// input index ends inside an aligned octet of lanes.
 constexpr int kDecodeColumnGroups = 8;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -77,23 +79,34 @@ __device__ __forceinline__ void load_block(const uint16_t* p, float (&x)[R])
     }
 }
 
-// Sum over the wave's row groups: lanes that differ only in the bits at and
-// above kCG (the column-group count, a power of two).
-template <int kCG>
+// x of the lane that DPP control `ctrl` selects, within the lane's row of 16
+template <int kCtrl>
+__device__ __forceinline__ float dpp(float x)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+        0, __builtin_bit_cast(int, x), kCtrl, 0xf, 0xf, false));
+}
+
+// Sum over the wave's 8 row groups: the lanes of an aligned octet (the row
+// group is lane % 8).  Three DPP adds, no LDS round trip: swap neighbours
+// (quad_perm 1,0,3,2), swap pairs (quad_perm 2,3,0,1), after which the four
+// lanes of a quad hold its sum, then mirror the octet (lane i reads lane
+// 7 - i, in the other quad).  Each add is commutative in its two operands,
+// so every lane of the octet ends with the same bits.
 __device__ __forceinline__ float rowgroup_sum(float x)
 {
-#pragma unroll
-    for (int m = kCG; m < 64; m <<= 1)
-        x += __shfl_xor(x, m);
+    x += dpp<0xb1>(x);       // quad_perm [1, 0, 3, 2]
+    x += dpp<0x4e>(x);       // quad_perm [2, 3, 0, 1]
+    x += dpp<0x141>(x);      // row_half_mirror
     return x;
 }
 
 // One wave per (batch, head) and slice of 4 kCG columns of W.  Lane l holds
-// the four columns j = 4 kCG slice + 4 (l % kCG) .. + 3 over the R rows
-// (l / kCG) R .. + R - 1, R = d kCG / 64: each of its R float4 loads and
+// the four columns j = 4 kCG slice + 4 (l / 8) .. + 3 over the R rows
+// (l % 8) R .. + R - 1, R = d kCG / 64: each of its R float4 loads and
 // stores is one row segment.  Sums over the input index run over the lane's
-// rows, then over the 64 / kCG row groups with lane shuffles.  k and q: each
-// lane reads its R-row block.
+// rows, then over the 8 row groups of its octet (rowgroup_sum).  k and q:
+// each lane reads its R-row block.
 template <typename TIn, int kD, bool kPro, int kCG>
 __global__ void __launch_bounds__(64)
 decode_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
@@ -104,11 +117,14 @@ decode_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
     constexpr int kSlices = (kD + kCols - 1) / kCols;
     constexpr int R = kD * kCG / 64;              // rows per lane
     constexpr int kGroups = kD / 4 < kCG ? kD / 4 : kCG;   // column groups in use
+    static_assert(64 / kCG == 8, "rowgroup_sum adds the 8 row groups of a lane octet");
     const int lane = threadIdx.x;
     const int64_t u = blockIdx.x / kSlices;
-    const int cg = lane & (kCG - 1), rg = lane / kCG;
-    // d < 64: lanes past the last column group only help with the sums
-    const bool active = cg < kGroups;
+    const int cg = lane >> 3, rg = lane & 7;
+    // d < 32: the octets past the last column group repeat column group 0
+    // and store nothing (a constant true otherwise, so that no branch gives
+    // the compiler a place to sink the loads of v and eta into)
+    const bool active = kGroups == kCG || cg < kGroups;
     const int j0 = (blockIdx.x % kSlices) * kCols + 4 * (active ? cg : 0);
     const int h = static_cast<int>(u % H);
     const int i0 = rg * R;
@@ -123,10 +139,11 @@ decode_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
     load_block<R>(k + u * kD + i0, kr);
     load_block<R>(q + u * kD + i0, qr);
     float vj[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-        vj[e] = load_elem(v, u * kD + j0 + e);
+    load_block<4>(v + u * kD + j0, vj);
     const float et = (kPro && pro.eta_tok) ? pro.eta_tok[u] : eta[h];
+    // (all of them in flight before the first use: left to itself the
+    // scheduler issues the last W row only after the first rows arrive)
+    __builtin_amdgcn_sched_barrier(0);
 
     if constexpr (kPro) {
         // LayerNorm of the whole k and q rows: each row group holds R of the
@@ -136,12 +153,12 @@ decode_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
 #pragma unroll
             for (int i = 0; i < R; ++i)
                 s += x[i];
-            const float mean = rowgroup_sum<kCG>(s) * (1.0f / kD);
+            const float mean = rowgroup_sum(s) * (1.0f / kD);
             float sq = 0.f;
 #pragma unroll
             for (int i = 0; i < R; ++i)
                 sq += (x[i] - mean) * (x[i] - mean);
-            const float rstd = rsqrtf(rowgroup_sum<kCG>(sq) * (1.0f / kD) + pro.ln_eps);
+            const float rstd = rsqrtf(rowgroup_sum(sq) * (1.0f / kD) + pro.ln_eps);
 #pragma unroll
             for (int i = 0; i < R; ++i)
                 x[i] = (x[i] - mean) * rstd * prm[(2 * h) * kD + i0 + i] + prm[(2 * h + 1) * kD + i0 + i];
@@ -165,10 +182,10 @@ decode_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-        kw[e] = rowgroup_sum<kCG>(kw[e]);
-        qw[e] = rowgroup_sum<kCG>(qw[e]);
+        kw[e] = rowgroup_sum(kw[e]);
+        qw[e] = rowgroup_sum(qw[e]);
     }
-    qk = rowgroup_sum<kCG>(qk);
+    qk = rowgroup_sum(qk);
     if (!active)
         return;
     float r[4];
