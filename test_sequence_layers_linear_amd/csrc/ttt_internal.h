@@ -296,7 +296,11 @@ bool linear_backward_supports(const LinearBwdArgs& a);
 // segment-backward workgroups a CU may hold, and the slowdown of each per
 // extra workgroup per CU (measured on MI355X: the bf16 kernel's 32 KB of LDS
 // let two share a CU, each 1.7x slower at 1.9 per CU; the fp32 kernel gains
-// nothing from sharing); maps workgroups a CU may hold.
+// nothing from sharing); maps workgroups a CU may hold.  The bf16 figures
+// are a least-squares fit to forced segment counts on MI355X (B8 H12 T2048:
+// 173, 167, 176, 181, 207 us at 2-6 segments; B2 H24 T32768: 1111, 1007,
+// 906 us at 6, 8, 10), where the composition step also stands for every
+// other cost that grows with the segment count.
 struct BwdCosts {
     double bwd, fmap, gmap, apply, launch;
     int fmap_blocks_per_segment;
@@ -305,7 +309,7 @@ struct BwdCosts {
     int maps_per_cu;
 };
 constexpr BwdCosts kLinearBwdF32Costs{5.2, 0.9, 1.5, 0.6, 20.0, 2, 1, 0.0, 2};
-constexpr BwdCosts kLinearBwdBf16Costs{2.63, 0.43, 1.0, 0.6, 20.0, 1, 2, 0.7, 4};
+constexpr BwdCosts kLinearBwdBf16Costs{1.64, 0.27, 0.62, 10.0, 5.3, 1, 2, 0.88, 4};
 size_t linear_backward_workspace_bytes(const LinearBwdArgs& a, const SegmentPlan& p);
 hipError_t launch_linear_backward(const LinearBwdArgs& a, const SegmentPlan& p, void* workspace);
 

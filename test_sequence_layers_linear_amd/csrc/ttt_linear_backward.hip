@@ -828,8 +828,10 @@ BwdWorkspace carve(const LinearBwdArgs& a, const SegmentPlan& p, void* base)
         w.gmaps = take(units * (S - 1) * 2 * st);
         w.gend = take(units * S * st);
     }
-    // chunk-start states: fp32 W for fp32 inputs, bf16 W^T (half the bytes) for bf16
-    w.states = take(units * S * seg_chunks * st / (a.dtype != 0 ? 2 : 1));
+    // chunk-start states: fp32 W for fp32 inputs; for bf16 the update
+    // operands E' from which the bf16 kernel walks the states back (256
+    // threads x 8 bytes per chunk: 512 floats' worth)
+    w.states = take(units * S * seg_chunks * (a.dtype != 0 ? 512 : st));
     w.dw_chain = a.w0_per_batch ? a.dW0 : take(units * st);
     w.deta_chain = take(units * S);
     w.dln_chain = a.pro.active() ? take(units * S * kDlnRows * kD) : nullptr;

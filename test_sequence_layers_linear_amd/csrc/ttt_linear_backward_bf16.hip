@@ -30,7 +30,15 @@
 // 16-lane group, lane i receives element i % 4 of the 8-byte block addressed
 // by lane 4k + i / 4 as its element k, so lanes addressing rows r0 + j / 4 at
 // columns x0 + 4 (j % 4) hand lane i the 4 values X[r0 .. r0 + 3][x0 + i].
-// The chunk-start states go to the workspace as bf16 W^T (8 KB per chunk).
+// Chunk-start states without storing them: sweep 1 writes each chunk's
+// update operand E'_c = bf16(-eta E_c) to the workspace (8 bytes per lane, 2
+// KB per chunk) and ends with W of the segment's last chunk in registers;
+// sweep 2 walks back from there, W_c = W_{c+1} - K_c^T E'_c, the same
+// product with E'_c negated (exact in bf16), so each W_c is the one sweep 1
+// passed through up to the fp32 rounding of one add per chunk (no inverse is
+// taken and no error is amplified), and its bf16 W_c^T goes to LDS from the
+// registers.  A quarter of the 8 KB per chunk that W_c^T in bf16 would take
+// each way.
 //
 // kPro: the input prologue.  Raw Q, K rows are LayerNorm'd (per-head gamma,
 // beta over the 64-wide head dim) as they are staged into LDS, keeping the
@@ -116,7 +124,7 @@ struct Stage {
     uint32_t v[4];     // V[4g + r][16w + c] of this lane's column: the 4-byte word holding
                        // the bf16 value (a whole word: no extension after the load, so
                        // the value can stay in flight; vneg picks the half)
-    u32x4 w[2];        // W_c^T row tid / 4, segments 2 (tid % 4), +1
+    u32x2 e;           // E'_c of this lane: sweep 1's update operand of the chunk
     float eta;         // kPro: the step size of row tid / 16 (0 past T)
     bool ok;           // row tid / 16 is a token (< T)
 };
@@ -178,10 +186,10 @@ linear_backward_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __re
     const __amdgpu_buffer_rsrc_t r_dq = buffer_rsrc(dQ + off, kGMap ? 0 : chain_bytes);
     const __amdgpu_buffer_rsrc_t r_dk = buffer_rsrc(dK + off, kGMap ? 0 : chain_bytes);
     const __amdgpu_buffer_rsrc_t r_dv = buffer_rsrc(dV + off, kGMap ? 0 : chain_bytes);
-    uint16_t* st = states + (u * nseg + s) * static_cast<int64_t>(seg_chunks) * kD * kD;
-    // this segment's chunk-start states (bf16 W^T) in the workspace
+    // this segment's update operands E' in the workspace: [chunk][thread] x 8 bytes
+    uint16_t* st = states + (u * nseg + s) * static_cast<int64_t>(seg_chunks) * kThreads * 4;
     const __amdgpu_buffer_rsrc_t r_st =
-        buffer_rsrc(st, kGMap ? 0 : static_cast<int64_t>(seg_chunks) * kD * kD * 2);
+        buffer_rsrc(st, kGMap ? 0 : static_cast<int64_t>(seg_chunks) * kThreads * 8);
     const bool use_dy = !kGMap || half == 1;     // uniform per workgroup
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 
@@ -246,11 +254,9 @@ linear_backward_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __re
                     r_v, ((chunk * kB + 4 * g + r) * kD + (col & ~1)) * 2, 0, 0);
         }
         if (wst) {
-            // chunk c0 - 1 (loaded ahead of the first chunk) falls outside: zeros
-#pragma unroll
-            for (int q = 0; q < 2; ++q)
-                x.w[q] = __builtin_amdgcn_raw_buffer_load_b128(
-                    r_st, (((chunk - c0) * kD + (tid >> 2)) * kD + 8 * (2 * (tid & 3) + q)) * 2, 0, 0);
+            // chunk c0 - 1 (loaded ahead of the first chunk) falls outside:
+            // zeros; the segment's last chunk has none (unused)
+            x.e = __builtin_amdgcn_raw_buffer_load_b64(r_st, ((chunk - c0) * kThreads + tid) * 8, 0, 0);
         }
     };
     // (with the prologue: LayerNorm first, and the rows' step sizes)
@@ -278,11 +284,6 @@ linear_backward_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __re
         else
             return f32x4{et, et, et, et};
     };
-    auto store_w = [&](const Stage& x) {
-#pragma unroll
-        for (int q = 0; q < 2; ++q)
-            *reinterpret_cast<u32x4*>(lds + kOffW + swz(tid >> 2, 2 * (tid & 3) + q)) = x.w[q];
-    };
     auto vneg = [&](const uint32_t (&v)[4]) {
         f32x4 r;
 #pragma unroll
@@ -292,8 +293,8 @@ linear_backward_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __re
     };
 
     // ---------------- sweep 1: chunk-start states of the segment ----------------
+    f32x4 Wacc[4];               // W[rho(mt, 4g + r)][col]; after sweep 1 W of chunk c1 - 1
     if (!kGMap && c1 > c0) {
-        f32x4 Wacc[4];           // W[rho(mt, 4g + r)][col]
         {
             const float* w0 = nseg > 1 ? wstart + (u * nseg + s) * kD * kD
                                        : W0 + (w0_per_batch ? u : h) * kD * kD;
@@ -329,22 +330,21 @@ linear_backward_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __re
             load_stage(kring[q], c0 + 1 + q, false, false, false);
         }
         __syncthreads();
-        // (`last`: the segment's last chunk, whose state is stored and nothing
-        // more; a constant false in the full rounds)
+        // (`last`: the segment's last chunk, whose W stays in the registers
+        // for sweep 2; a constant false in the full rounds)
         auto sweep1_step = [&](int ch, Stage& knext, uint32_t (&vc)[4], bool last) {
+            if (last)
+                return;
             // W_c^T row col: 16 bytes at i = 8g .. and 32 + 8g ..
             const bf16x8 b0 = pack8(Wacc[0], Wacc[1]);
             const bf16x8 b1 = pack8(Wacc[2], Wacc[3]);
-            uint16_t* sc = st + static_cast<int64_t>(ch - c0) * kD * kD + col * kD;
-            *reinterpret_cast<bf16x8*>(sc + 8 * g) = b0;
-            *reinterpret_cast<bf16x8*>(sc + 32 + 8 * g) = b1;
-            if (last)
-                return;
             const unsigned char* sl = lds + ((ch - c0) & 1) * kSlotBytes;
-            // E = K W_J - V, W += K^T (-eta E)
+            // E = K W_J - V, W += K^T (-eta E); E' = -eta E goes to the workspace
             f32x4 R = mfma32(row8(sl + kSlotK, c, g), b0, vneg(vc));
             R = mfma32(row8(sl + kSlotK, c, 4 + g), b1, R);
             const bf16x4 eb = pack4(-(rows_eta((ch - c0) & 1) * R));
+            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, eb), r_st,
+                                                  ((ch - c0) * kThreads + tid) * 8, 0, 0);
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt)
                 Wacc[mt] = mfma16(col4_rho(sl + kSlotK, 4 * g, mt, c), eb, Wacc[mt]);
@@ -366,7 +366,7 @@ linear_backward_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __re
                 break;
             sweep1_step(ch + q, kring[q], vring[q], ch + q + 1 == c1);
         }
-        // the states just stored are read back below by other threads
+        // the operands just stored are read back below (by the threads that wrote them)
         __threadfence();
         __syncthreads();
     }
@@ -391,12 +391,12 @@ linear_backward_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __re
     float deta_acc = 0.f;
 
     uint32_t vcur[4] = {0, 0, 0, 0};
+    u32x2 ecur = {0, 0};         // E' of the chunk in hand (none for the last)
     if (c1 > c0) {
         Stage nx;
-        load_stage(nx, c1 - 1, use_dy, !kGMap);
+        load_stage(nx, c1 - 1, use_dy, false);
         store_stage(nx, 0, use_dy);
         if (!kGMap) {
-            store_w(nx);
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 vcur[r] = nx.v[r];
@@ -417,14 +417,22 @@ linear_backward_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __re
         const bf16x8 gb0 = pack8(Gacc[0], Gacc[1]);       // G'_J as a B operand
         const bf16x8 gb1 = pack8(Gacc[2], Gacc[3]);
         f32x4 E = zero;
-        bf16x8 wb[2];                                     // W[16 w + c][32 s + 8g ..] for phase B
         if (!kGMap) {
-            E = mfma32(ka0, row8(lds + kOffW, col, g), vneg(vcur));
-            E = mfma32(ka1, row8(lds + kOffW, col, 4 + g), E);
+            // W_c from W_{c+1}: undo sweep 1's update of this chunk (uniform)
+            if (ch < c1 - 1) {
+                const bf16x4 en = __builtin_bit_cast(bf16x4, ecur ^ u32x2{0x80008000u, 0x80008000u});
 #pragma unroll
-            for (int q = 0; q < 2; ++q)
-                wb[q] = join(col4(lds + kOffW, 32 * q + 8 * g, 16 * w, c),
-                             col4(lds + kOffW, 32 * q + 8 * g + 4, 16 * w, c));
+                for (int mt = 0; mt < 4; ++mt)
+                    Wacc[mt] = mfma16(col4_rho(sl + kSlotK, 4 * g, mt, c), en, Wacc[mt]);
+            }
+            // W_c^T row col (i = 8g .. and 32 + 8g ..) for this wave's E and,
+            // through LDS, for every wave's phase B
+            const bf16x8 b0 = pack8(Wacc[0], Wacc[1]);
+            const bf16x8 b1 = pack8(Wacc[2], Wacc[3]);
+            *reinterpret_cast<bf16x8*>(lds + kOffW + swz(col, g)) = b0;
+            *reinterpret_cast<bf16x8*>(lds + kOffW + swz(col, 4 + g)) = b1;
+            E = mfma32(ka0, b0, vneg(vcur));
+            E = mfma32(ka1, b1, E);
         }
         // P = A^T dY_J + K G'_J  (A = tril(Q K^T); S holds S[t = 4g + r][s = c])
         f32x4 P1 = zero;
@@ -479,10 +487,13 @@ linear_backward_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __re
 
         if (!kGMap) {
             __syncthreads();
-            // every wave has read W_c: the next chunk's W_c may replace it
-            if (ch > c0)
-                store_w(nx);
             // ---- phase B: input dims I = w ----
+            // W[16 w + c][32 q + 8g ..], written by the four waves before the barrier
+            bf16x8 wb[2];
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+                wb[q] = join(col4(lds + kOffW, 32 * q + 8 * g, 16 * w, c),
+                             col4(lds + kOffW, 32 * q + 8 * g + 4, 16 * w, c));
             const bf16x8 ya0 = row8(sl + kSlotDY, c, g), ya1 = row8(sl + kSlotDY, c, 4 + g);
             const bf16x8 ea0 = row8(lds + kOffE, c, g), ea1 = row8(lds + kOffE, c, 4 + g);
             // dA[t = 4g + r][s = c] and dA^T[s = 4g + r][t = c], masked and scaled
@@ -576,6 +587,7 @@ linear_backward_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __re
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     vcur[r] = nx.v[r];
+                ecur = nx.e;
             }
         }
         __syncthreads();

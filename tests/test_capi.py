@@ -322,12 +322,14 @@ def test_workspace_queries(lib, monkeypatch):
     units, chunks = 2, 4
     pad = lambda n: (n + 255) // 256 * 256
     small = pad(units * 4) + pad(units * 4 * 64 * 4)     # deta per segment, LayerNorm sums
-    for dt, state in ((1, st // 2), (0, st)):
+    # per chunk: fp32 W (fp32 inputs); bf16 inputs keep the update operand E',
+    # 256 threads x 8 bytes, from which the kernel walks the states back
+    for dt, state in ((1, 256 * 8), (0, st)):
         want = pad(units * chunks * state) + pad(units * st) + small
         assert lib.ttt_linear_backward_workspace_bytes(1, 2, 64, 64, 16, dt) == want
     # the plain call with shared W0 needs the states, dW0 per chain and deta
     # (no LayerNorm sums); one byte short of that is rejected before any launch
-    need = pad(units * chunks * st // 2) + pad(units * st) + pad(units * 4)
+    need = pad(units * chunks * 256 * 8) + pad(units * st) + pad(units * 4)
     assert bwd(lib, B=1, H=2, ws=WSA, wsb=need - 1) == INVALID
 
 
