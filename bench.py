@@ -37,8 +37,8 @@ this host's cores on a bounded sample of the same workload: with all host
 threads (one chain each), and with one thread (single_thread).
 
 Each TTT-Linear workload also reports "backward": ttt_linear_backward (the
-gradients of Q, K, V, W0 and eta for seeded cotangents dY, dW_out) timed the
-same way, with its own roofline (the MFMA peak of the input dtype: bf16
+gradients of Q, K, V, W0 and eta for seeded cotangents dY, dW_out), timed
+back to back on one input set after 50 ms of untimed calls, with its own roofline (the MFMA peak of the input dtype: bf16
 inputs run on bf16 MFMA, fp32 inputs on fp32 MFMA).  It is reported beside the forward, not folded into the
 headline value.  "prologue" times ttt_linear_forward_ex on the same inputs
 with LayerNorm of q and k and a step size per token fused into the scan, and
@@ -281,6 +281,21 @@ def roofline(w, flops, nbytes, seconds, kernels, roofs=None, warm_seconds=None,
                        "mean_launch_us": round(warm_seconds * 1e6, 3),
                        "timing": "mean over the back-to-back calls of the timed region"}
     return out
+
+
+def warm_up(torch, call, calls, seconds=0.05):
+    """At least `calls` untimed calls, and more until they have kept the GPU
+    busy for `seconds` (see cycle_timed for why)."""
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    done, busy = 0, 0.0
+    while done < calls or busy < seconds:
+        torch.cuda.synchronize()
+        a.record()
+        call()
+        b.record()
+        torch.cuda.synchronize()
+        busy += a.elapsed_time(b) / 1e3
+        done += 1
 
 
 def cycle_timed(torch, call, sets, reps, warm_seconds=0.05):
@@ -533,8 +548,7 @@ class Runner:
             else:
                 self.ttt.ttt_linear_backward(g["Q"], g["K"], g["V"], g["W0"], g["eta"], w.b,
                                              cot["dY"], cot["dW_out"], workspace=ws, **outs)
-        for _ in range(warmup):
-            call()
+        warm_up(torch, call, warmup)
         torch.cuda.synchronize()
         start = torch.cuda.Event(enable_timing=True)
         end = torch.cuda.Event(enable_timing=True)
@@ -557,8 +571,7 @@ class Runner:
                                            eta_tok=pro["eta_tok"], ln_q=pro["ln_q"],
                                            ln_k=pro["ln_k"], Y=self.Y, W_out=self.W,
                                            workspace=self.ws)
-        for _ in range(warmup):
-            call()
+        warm_up(torch, call, warmup)
         torch.cuda.synchronize()
         start = torch.cuda.Event(enable_timing=True)
         end = torch.cuda.Event(enable_timing=True)
@@ -585,8 +598,7 @@ class Runner:
             self.ttt.ttt_linear_momentum_forward(x["Q"], x["K"], x["V"], x["W0"], x["eta"], beta,
                                                  w.b, None, grad_mode, Y=self.Y, W_out=self.W,
                                                  M_out=M, workspace=ws)
-        for _ in range(warmup):
-            call()
+        warm_up(torch, call, warmup)
         torch.cuda.synchronize()
         start = torch.cuda.Event(enable_timing=True)
         end = torch.cuda.Event(enable_timing=True)
