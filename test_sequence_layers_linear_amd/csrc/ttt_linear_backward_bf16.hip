@@ -148,7 +148,8 @@ linear_backward_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __re
                             uint16_t* __restrict__ dK, uint16_t* __restrict__ dV,
                             float* __restrict__ dW0_chain, float* __restrict__ deta_chain,
                             uint16_t* __restrict__ states, float* __restrict__ gmaps,
-                            Prologue pro, float* __restrict__ deta_tok, float* __restrict__ dln_chain)
+                            Prologue pro, float* __restrict__ deta_tok, float* __restrict__ dln_chain,
+                            const float* __restrict__ fmaps)
 {
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
     using L = Lay<kPro>;
@@ -171,6 +172,19 @@ linear_backward_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __re
             half = s & 1;
             s = (s >> 1) + 1;
         }
+    }
+    if (kGMap && half == 0 && s < nseg - 1) {
+        // The linear part of a segment's cotangent map, the product of the
+        // chunks' I - K^T diag(eta) K from the segment's end to its start,
+        // is the transpose of the forward map's product of the same
+        // symmetric factors in the forward order, which the forward maps
+        // launch before this one has already formed (for every segment but
+        // the last): copy it transposed instead of scanning K again.
+        const float* A = fmaps + (u * (nseg - 1) + s) * 2 * kD * kD;
+        float* Lm = gmaps + ((u * (nseg - 1) + (nseg - 1 - s)) * 2) * kD * kD;
+        for (int e = threadIdx.x; e < kD * kD; e += kThreads)
+            Lm[(e % kD) * kD + e / kD] = A[e];
+        return;
     }
     const int h = static_cast<int>(u % H);
     const float et = eta[h];
@@ -653,7 +667,7 @@ void launch_bf16(const LinearBwdArgs& a, const SegmentPlan& p, const BwdBuffers&
                        static_cast<const uint16_t*>(a.dY), a.dW_out, static_cast<uint16_t*>(a.dQ),
                        static_cast<uint16_t*>(a.dK), static_cast<uint16_t*>(a.dV), b.dw_chain,
                        b.deta_chain, reinterpret_cast<uint16_t*>(b.states), b.gmaps, a.pro,
-                       a.deta_tok, b.dln_chain);
+                       a.deta_tok, b.dln_chain, b.maps);
 }
 
 }  // namespace
