@@ -247,7 +247,8 @@ LinearScan pick_scan(const LinearArgs& a)
     return {nullptr, nullptr};
 }
 
-// The fused layout with S segments (bf16 TTT-Linear without the prologue):
+// The fused layout with S segments (bf16 TTT-Linear, with or without the
+// prologue):
 // segment 0 of L0 chunks, scanned beside the maps of segments 1 .. S - 2 of L
 // chunks each, L0 = ratio L so that the two roles of the first launch end
 // together; the last segment takes the rest.  nseg = 1 if S does not fit.
@@ -281,7 +282,7 @@ double plan_cost(const ttt::SegmentPlan& p, int64_t T, int chunk, const ttt::Seg
 }
 
 // The plan a forward of these sizes uses with `ws_bytes` of workspace.  The
-// bf16 MFMA scan without the prologue also weighs the fused layout (off with
+// bf16 MFMA scan also weighs the fused layout (off with
 // TTT_LINEAR_FUSED=0): its two launches hold units (S - 1) workgroups each,
 // so it may use one more segment than the unfused layout on the same CUs.
 ttt::SegmentPlan plan_forward(const LinearArgs& a, int64_t ws_bytes)
@@ -291,7 +292,7 @@ ttt::SegmentPlan plan_forward(const LinearArgs& a, int64_t ws_bytes)
     if (!k.cost || units == 0 || a.T == 0) return with_segments(a.T, a.b, 1);
     const ttt::SegmentPlan unfused = plan_segments(units, a.T, a.b, a.d, *k.cost, ws_bytes);
     const char* off = getenv("TTT_LINEAR_FUSED");
-    if (k.cost != &ttt::kLinearBf16Costs || a.pro.active() || (off && strtol(off, nullptr, 10) == 0))
+    if (k.cost != &ttt::kLinearBf16Costs || (off && strtol(off, nullptr, 10) == 0))
         return unfused;
     const ttt::SegmentCosts& cost = *k.cost;
     const double ratio = cost.map / (cost.fwd * ttt::kStagedScanFactor);

@@ -590,15 +590,16 @@ linear_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
 // (Y rows and its end state, the start state of segment 1) while workgroups
 // 1 .. nseg - 2 form the maps of segments 1 .. nseg - 2, so segment 0 needs no
 // map.  Both roles run 12 waves: the scan in the staged form of the prologue
-// scan with the prologue off (the same products as the plain scan, bit for
-// bit), the maps as in the unfused layout.
-template <bool kStream>
+// scan (with the prologue off unless kPro: the same products as the plain
+// scan, bit for bit), the maps as in the unfused layout (kPro: with the
+// LayerNorm of K and the step sizes).
+template <bool kPro, bool kStream>
 __global__ void __launch_bounds__(3 * kThreads, 1)
 linear_fused_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                     const uint16_t* __restrict__ V, const float* W0, int w0_per_batch,
                     const float* __restrict__ eta, int H, int T, int64_t units, int seg_len,
                     int first_len, int nseg, float* maps, float* wstart,
-                    uint16_t* __restrict__ Y, float* W_out)
+                    uint16_t* __restrict__ Y, float* W_out, Prologue pro)
 {
     int64_t u = blockIdx.x;
     int s = 0;
@@ -607,12 +608,12 @@ linear_fused_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__
         return;
     if (s == 0)
         linear_body<false, true, kStream>(Q, K, V, W0, w0_per_batch, eta, H, T, seg_len,
-                                          first_len, nseg, maps, wstart, Y, W_out, Prologue{}, u,
-                                          0, true);
+                                          first_len, nseg, maps, wstart, Y, W_out,
+                                          kPro ? pro : Prologue{}, u, 0, true);
     else
-        linear_body<true, false, kStream>(Q, K, V, W0, w0_per_batch, eta, H, T, seg_len,
-                                          first_len, nseg, maps, wstart, Y, W_out, Prologue{}, u,
-                                          s, false);
+        linear_body<true, kPro, kStream>(Q, K, V, W0, w0_per_batch, eta, H, T, seg_len,
+                                         first_len, nseg, maps, wstart, Y, W_out,
+                                         kPro ? pro : Prologue{}, u, s, false);
 }
 
 }  // namespace
@@ -643,10 +644,10 @@ hipError_t launch_bf16(const LinearArgs& a, const SegmentPlan& p)
         const dim3 grid(static_cast<unsigned>(placed_grid(units, p.nseg - 1)));
         if (p.fused) {
             // (the staged scan's slots also hold the step sizes)
-            hipLaunchKernelGGL((linear_fused_kernel<kStream>), grid, dim3(3 * kThreads),
+            hipLaunchKernelGGL((linear_fused_kernel<kPro, kStream>), grid, dim3(3 * kThreads),
                                kSlots * (kSlotBytes + kStageTokens * 4), a.stream, q, k, v, a.W0,
                                a.w0_per_batch, a.eta, H, T, units, seg_len, first_len, p.nseg,
-                               p.maps, p.wstart, y, a.W_out);
+                               p.maps, p.wstart, y, a.W_out, a.pro);
             seg_base = 1;
         } else {
             hipLaunchKernelGGL((linear_mfma_kernel<true, kPro, kStream>), grid, dim3(3 * kThreads),

@@ -64,13 +64,16 @@ def test_prologue_f32_one_workgroup_kernel(part, T, S, monkeypatch):
     assert ey <= TOL["fp32"] and ew <= TOL["fp32"]
 
 
-@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("dtype,layout", [("fp32", "unfused"), ("bf16", "unfused"), ("bf16", "fused")])
 @pytest.mark.parametrize("T,S", [(100, 2), (333, 3), (480, 30)])
-def test_prologue_segmented(dtype, T, S, monkeypatch):
+def test_prologue_segmented(dtype, layout, T, S, monkeypatch):
+    """bf16 runs both segment layouts: maps then scans, and segment 0's scan
+    beside the other segments' maps (from 3 segments on)."""
     monkeypatch.setenv("TTT_LINEAR_SEGMENTS", str(S))
+    monkeypatch.setenv("TTT_LINEAR_FUSED", "1" if layout == "fused" else "0")
     w = WORKLOADS[3].with_(B=1, H=3, T=T, dtype=dtype)
     seed = 9100 + T + S
-    announce("prologue segmented", dtype, T, S, seed)
+    announce("prologue segmented", dtype, layout, T, S, seed)
     ey, ew = _run(w, seed, PARTS["all"])
     assert ey <= TOL[dtype] and ew <= TOL[dtype]
 
