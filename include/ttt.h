@@ -104,8 +104,9 @@ typedef enum {
  * qkv_dtype); with less it uses the fastest count whose maps and states fit
  * (NULL / 0 bytes: one segment, which needs none).  The environment variable
  * TTT_LINEAR_SEGMENTS=S (1..30) forces S segments (fewer if they do not fit).
- * bf16 at d = 64, b = 16 without the prologue may use the fused layout
- * (ttt_linear_fused reports it): the first launch also scans segment 0,
+ * bf16 at d = 64, b = 16 may use the fused layout (ttt_linear_fused
+ * reports it; ttt_linear_forward_ex with the prologue weighs it the same
+ * way): the first launch also scans segment 0,
  * which then needs no map and is shorter than the others, and the
  * composition starts from its end state; with S - 1 workgroups per chain in
  * each launch, one more segment fits the GPU.  TTT_LINEAR_FUSED=0 turns it
@@ -287,12 +288,15 @@ int ttt_linear_decode_step(const void* q, const void* k, const void* v, int qkv_
  * summed in a fixed order).  ttt_linear_backward_segments reports the count;
  * TTT_LINEAR_BWD_SEGMENTS=S (1..30) forces it.  Workspace, caller-owned, in
  * d*d*4-byte matrices per chain: S*ceil(ceil(T/16)/S) recomputed chunk-start
- * states (half that for bf16 inputs, which store them in bf16), with S > 1
- * another 6 S - 4 (maps, start and end states), and one more when W0 is
- * shared (per-chain dW0).  With workspace_bytes >=
+ * states (fp32 inputs; bf16 inputs keep instead each chunk's 2 KB update
+ * operand, from which the kernel walks the states back: an eighth of
+ * that), with S > 1 another 6 S - 4 (maps, start and end states), and one
+ * more when W0 is shared (per-chain dW0).  With workspace_bytes >=
  * ttt_linear_backward_workspace_bytes(...) the call uses the count
- * ttt_linear_backward_segments reports; with less, the fastest count that
- * fits; if not even one segment's states fit, TTT_ERR_INVALID_ARG.
+ * ttt_linear_backward_segments reports (the prologue call of
+ * ttt_linear_backward_ex may plan more segments; the query covers both);
+ * with less, the fastest count that fits; if not even one segment's
+ * states fit, TTT_ERR_INVALID_ARG.
  * Errors as for ttt_linear_forward.
  */
 int ttt_linear_backward(const void* Q, const void* K, const void* V, int qkv_dtype,

@@ -493,6 +493,14 @@ int ttt_linear_fused(int64_t B, int64_t H, int64_t T, int d, int b, int qkv_dtyp
 
 namespace {
 
+// Planner costs of a backward call: by input dtype, and for bf16 with or
+// without the prologue.
+const ttt::BwdCosts& bwd_costs(int qkv_dtype, bool pro)
+{
+    if (qkv_dtype != TTT_BF16) return ttt::kLinearBwdF32Costs;
+    return pro ? ttt::kLinearBwdBf16ProCosts : ttt::kLinearBwdBf16Costs;
+}
+
 int linear_backward_impl(const void* Q, const void* K, const void* V, int qkv_dtype,
                          const float* W0, int w0_per_batch, const float* eta,
                          int64_t B, int64_t H, int64_t T, int d, int b,
@@ -550,8 +558,7 @@ int linear_backward_impl(const void* Q, const void* K, const void* V, int qkv_dt
     };
     ttt::SegmentPlan p;
     if (units > 0)
-        p = plan_backward(units, T, b, qkv_dtype == TTT_BF16 ? ttt::kLinearBwdBf16Costs
-                                                              : ttt::kLinearBwdF32Costs, fits);
+        p = plan_backward(units, T, b, bwd_costs(qkv_dtype, pro.active()), fits);
     if (!fits(p)) return TTT_ERR_INVALID_ARG;   // not even one segment's states fit
     return hip_status(ttt::launch_linear_backward(a, p, ws));
 }
@@ -610,8 +617,7 @@ int ttt_linear_backward_segments(int64_t B, int64_t H, int64_t T, int d, int b, 
     if (const int st = linear_sizes_status(B, H, T, d, b, qkv_dtype)) return st;
     if (d != 64 || b != 16) return TTT_ERR_UNSUPPORTED;
     if (B * H == 0 || T == 0) return 1;
-    return plan_backward(B * H, T, b, qkv_dtype == TTT_BF16 ? ttt::kLinearBwdBf16Costs
-                                                            : ttt::kLinearBwdF32Costs,
+    return plan_backward(B * H, T, b, bwd_costs(qkv_dtype, false),
                          [](const ttt::SegmentPlan&) { return true; }).nseg;
 }
 
@@ -621,12 +627,17 @@ int64_t ttt_linear_backward_workspace_bytes(int64_t B, int64_t H, int64_t T, int
     if (const int st = linear_sizes_status(B, H, T, d, b, qkv_dtype)) return st;
     if (d != 64 || b != 16) return TTT_ERR_UNSUPPORTED;
     const ttt::LinearBwdArgs a = bwd_query_args(B, H, T, d, b, qkv_dtype);
-    ttt::SegmentPlan p;
-    if (B * H > 0 && T > 0)
-        p = plan_backward(B * H, T, b, qkv_dtype == TTT_BF16 ? ttt::kLinearBwdBf16Costs
-                                                             : ttt::kLinearBwdF32Costs,
-                          [](const ttt::SegmentPlan&) { return true; });
-    return static_cast<int64_t>(ttt::linear_backward_workspace_bytes(a, p));
+    // enough for the plain call's plan and the prologue call's, which may
+    // take more segments
+    size_t bytes = ttt::linear_backward_workspace_bytes(a, ttt::SegmentPlan{});
+    if (B * H > 0 && T > 0) {
+        for (const bool pro : {false, true}) {
+            const ttt::SegmentPlan p = plan_backward(B * H, T, b, bwd_costs(qkv_dtype, pro),
+                                                     [](const ttt::SegmentPlan&) { return true; });
+            bytes = std::max(bytes, ttt::linear_backward_workspace_bytes(a, p));
+        }
+    }
+    return static_cast<int64_t>(bytes);
 }
 
 int ttt_mlp_forward(const void* Q, const void* K, const void* V, int qkv_dtype,

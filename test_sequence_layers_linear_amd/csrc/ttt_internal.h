@@ -188,7 +188,7 @@ struct SegmentPlan {
     float* wstart = nullptr;
     bool starts_only = false;   // maps and start states only, no segment scans
     // segment 0 scanned beside the maps of segments 1 .. nseg - 2 (bf16
-    // TTT-Linear without the prologue): no map of segment 0, and the
+    // TTT-Linear, with or without the prologue): no map of segment 0, and the
     // composition starts from its end state
     bool fused = false;
     int64_t first() const { return first_len > 0 ? first_len : seg_len; }
@@ -310,6 +310,11 @@ struct BwdCosts {
 };
 constexpr BwdCosts kLinearBwdF32Costs{5.2, 0.9, 1.5, 0.6, 20.0, 2, 1, 0.0, 2};
 constexpr BwdCosts kLinearBwdBf16Costs{1.64, 0.27, 0.62, 10.0, 5.3, 1, 2, 0.88, 4};
+// the same with the input prologue (LayerNorm of q, k, per-token step sizes:
+// a dearer chunk, so more segments pay), fitted to B8 H12 T2048 at 1-6
+// segments (367, 311, 265, 247, 238, 285 us) and B2 H24 T32768 at 8 and 10
+// (1433, 1233 us)
+constexpr BwdCosts kLinearBwdBf16ProCosts{2.87, 0.47, 1.10, 16.7, 0.0, 1, 2, 0.074, 4};
 size_t linear_backward_workspace_bytes(const LinearBwdArgs& a, const SegmentPlan& p);
 hipError_t launch_linear_backward(const LinearBwdArgs& a, const SegmentPlan& p, void* workspace);
 

@@ -83,6 +83,21 @@ def test_backward_segmented(dtype, B, H, T, S, per_batch, monkeypatch):
     _compare(_gpu(inp, cot, 16), _oracle(inp, cot, 16), TOL[dtype])
 
 
+def test_backward_bf16_long_walk(monkeypatch):
+    """bf16, one segment of 2048 chunks: sweep 2 walks the chunk-start states
+    back from the last chunk through all of them (W_c = W_{c+1} - K_c^T E'_c),
+    so any drift of that walk would show most here; whole tensors against the
+    oracle."""
+    monkeypatch.setenv("TTT_LINEAR_BWD_SEGMENTS", "1")
+    w = WORKLOADS[4].with_(B=1, H=2)
+    assert ttt.ttt_linear_backward_segments(w.B, w.H, w.T, w.d, w.b, w.torch_dtype) == 1
+    seed = 7700
+    announce("backward bf16 one long segment", w.name, seed)
+    inp = make_inputs(w, seed, w0_per_batch=True)
+    cot = make_cotangents(w, seed + 1)
+    _compare(_gpu(inp, cot, w.b), _oracle(inp, cot, w.b), TOL["bf16"])
+
+
 def test_backward_segmented_close_to_single_segment(monkeypatch):
     """fp32: a segmented backward is the same arithmetic in another rounding
     order of the state and the cotangent."""
